@@ -1,0 +1,212 @@
+"""Plain fp64 CPU oracle for causal linear attention and the gated delta rule.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link this module: only the test suite, the package smoke check and the CPU
+baseline leg of the benchmark use it.  It shares no code with the HIP
+library and imports nothing from it.
+
+Everything here is deliberately slow and literal: a Python loop over tokens,
+each step written as the pages write the recurrence, in float64 NumPy.
+Inputs are upcast exactly (bf16 and fp32 values are representable in fp64),
+so the oracle evaluates the method on the very values the GPU consumes.
+
+Sources (cited by page title and section):
+  [WILA]  "What Is Linear Attention?" (xutianle.me): section 2 (kernel trick,
+          S and z), section 4 (causal recurrence), 5.1 (gamma decay),
+          5.2 (delta rule), 5.3 (gate).
+  [EAV]   "Efficient attention variants" (bailixisu.com): section 4 (kernel
+          form, elu+1), section 5 (causal prefix form, write-then-read),
+          5.1 (hand-worked example), 7.1 (RetNet decay), 7.3 (DeltaNet),
+          section 10 (NumPy self-check: dense vs recurrent).
+  [LIO3]  "LLM inference optimisation (3): Linear Attention" (wangyu.me):
+          'recurrent form of the summary', 'implementation', 'delta rule'.
+  [TAR]   "Transformers Are RNNs" (myhz0606.com): epsilon in the
+          denominator, multiplicative causal mask.
+
+Readings where the pages disagree (each is listed in the design doc):
+  * The state is read AFTER the current token is written (token attends to
+    itself), as [WILA] section 4 and [EAV] section 5 state.
+  * eps is added to the denominator: o = phi(q).S / (phi(q).z + eps).
+  * gamma decays both S and z.
+  * The delta rule uses the raw k and q (no feature map, no normaliser), the
+    prediction is S^T k with S stored [r, dv], the gate scales the write, and
+    the output is read from the updated state: o_t = S_t^T q_t.
+
+Parity pins live in tests/test_oracle.py; every function below is pinned
+there against printed values, closed forms or brute force.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+FMAP_IDENTITY = "identity"
+FMAP_ELU1 = "elu1"
+
+
+def _f64(x):
+    """Exact upcast of a NumPy / torch (CPU) array to float64."""
+    if hasattr(x, "detach"):  # torch tensor: go through float32 exactly
+        x = x.detach().to("cpu")
+        import torch
+
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def phi_elu1(x):
+    """elu(x) + 1 with alpha = 1.
+
+    [EAV] section 4 names elu(x)+1 as the positive feature map of the Linear
+    Transformer; its section-10 program evaluates it as max(x,0) +
+    exp(min(x,0)) so that no large positive exponent is formed.  For x > 0
+    this is x + 1, for x <= 0 it is e^x (so phi(0) = 1).
+    """
+    x = _f64(x)
+    return np.maximum(x, 0.0) + np.exp(np.minimum(x, 0.0))
+
+
+def feature_map(x, fmap):
+    """phi applied elementwise.  IDENTITY means the inputs already are the
+    non-negative features ([EAV] 5.1 gives its example features directly)."""
+    if fmap == FMAP_ELU1:
+        return phi_elu1(x)
+    if fmap == FMAP_IDENTITY:
+        return _f64(x)
+    raise ValueError(f"unknown feature map {fmap!r}")
+
+
+def _gamma_heads(gamma, H):
+    """Per-head decay as a float64 vector of length H (None means 1)."""
+    if gamma is None:
+        return np.ones(H, dtype=np.float64)
+    g = _f64(gamma).reshape(-1)
+    if g.shape[0] != H:
+        raise ValueError("gamma must have one value per head")
+    return g
+
+
+# ---------------------------------------------------------------------------
+# LINEAR rule (elu+1 kernel, optional per-head decay, eps-stabilised normaliser)
+# ---------------------------------------------------------------------------
+
+def linear_step(S, z, fq, fk, v, gamma_bh, eps):
+    """One token of causal linear attention, on features already mapped.
+
+    S: [..., r, dv], z: [..., r], fq, fk: [..., r], v: [..., dv],
+    gamma_bh: [...] (decay per leading index).  Returns (o, S_new, z_new).
+
+    State update ([WILA] section 4 with the decay of 5.1, applied to S and z):
+        S_t = gamma * S_{t-1} + phi(k_t) v_t^T
+        z_t = gamma * z_{t-1} + phi(k_t)
+    Read after the write ([EAV] section 5: write first, then read, so the
+    token attends to itself), with eps in the denominator ([TAR]):
+        o_t = phi(q_t)^T S_t / (phi(q_t) . z_t + eps)
+    """
+    g = gamma_bh[..., None, None]
+    S_new = g * S + fk[..., :, None] * v[..., None, :]
+    z_new = gamma_bh[..., None] * z + fk
+    num = np.einsum("...r,...rd->...d", fq, S_new)
+    den = np.einsum("...r,...r->...", fq, z_new) + eps
+    return num / den[..., None], S_new, z_new
+
+
+def linear_prefill(q, k, v, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1,
+                   S0=None, z0=None):
+    """Causal linear attention over a whole sequence, token by token.
+
+    q, k: [B, H, N, d]; v: [B, H, N, dv]; gamma: [H] or None; S0: [B, H, d, dv]
+    or None (zero state); z0: [B, H, d] or None.
+    Returns (o [B, H, N, dv], S_N [B, H, d, dv], z_N [B, H, d]) in float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    fq, fk = feature_map(q, fmap), feature_map(k, fmap)
+    gam = np.broadcast_to(_gamma_heads(gamma, H)[None, :], (B, H))
+    S = np.zeros((B, H, d, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros((B, H, d)) if z0 is None else _f64(z0).copy()
+    o = np.empty((B, H, N, dv))
+    for t in range(N):
+        o[:, :, t], S, z = linear_step(S, z, fq[:, :, t], fk[:, :, t],
+                                       v[:, :, t], gam, eps)
+    return o, S, z
+
+
+def linear_decode_step(q, k, v, S, z, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1):
+    """One decode step against a persistent state: the same token body as
+    the prefill ([LIO3] 'recurrent form': read once, add once per token).
+
+    q, k: [B, H, d]; v: [B, H, dv]; S: [B, H, d, dv]; z: [B, H, d].
+    Returns (o [B, H, dv], S_new, z_new); the inputs are not modified.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H = q.shape[:2]
+    gam = np.broadcast_to(_gamma_heads(gamma, H)[None, :], (B, H))
+    return linear_step(_f64(S), _f64(z), feature_map(q, fmap),
+                       feature_map(k, fmap), v, gam, eps)
+
+
+def linear_quadratic(q, k, v, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1):
+    """The O(N^2) masked matrix form, zero initial state.
+
+    A = (phi(Q) phi(K)^T) (.) D with D_ij = gamma^(i-j) for j <= i and 0
+    otherwise (the multiplicative causal mask of [TAR], with the unrolled
+    RetNet decay of [EAV] 7.1); O = (A V) / (A 1 + eps), as in the dense
+    function of [EAV] section 10 (which has no eps).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, _ = q.shape
+    gam = _gamma_heads(gamma, H)
+    fq, fk = feature_map(q, fmap), feature_map(k, fmap)
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    lag = np.where(i >= j, i - j, 0)
+    D = np.where(i >= j, gam[:, None, None] ** lag[None], 0.0)  # [H, N, N]
+    A = np.matmul(fq, np.swapaxes(fk, -1, -2)) * D[None]
+    return np.matmul(A, v) / (A.sum(axis=-1, keepdims=True) + eps)
+
+
+# ---------------------------------------------------------------------------
+# Gated DELTA rule (raw q, k; no normaliser)
+# ---------------------------------------------------------------------------
+
+def delta_step(S, q, k, v, g):
+    """One token of the gated delta rule.
+
+    [WILA] 5.2-5.3: predict what the state already returns for this key,
+    write only the residual, scaled by the write gate g_t:
+        v_hat_t = S_{t-1}^T k_t            (S stored [r, dv])
+        S_t     = S_{t-1} + g_t k_t (v_t - v_hat_t)^T
+    The output is read from the updated state: o_t = S_t^T q_t.
+    S: [..., d, dv]; q, k: [..., d]; v: [..., dv]; g: [...].
+    """
+    v_hat = np.einsum("...rd,...r->...d", S, k)
+    S_new = S + g[..., None, None] * k[..., :, None] * (v - v_hat)[..., None, :]
+    o = np.einsum("...rd,...r->...d", S_new, q)
+    return o, S_new
+
+
+def delta_prefill(q, k, v, g, *, S0=None):
+    """Gated delta rule over a whole sequence, token by token.
+
+    q, k: [B, H, N, d]; v: [B, H, N, dv]; g: [B, H, N]; S0: [B, H, d, dv] or
+    None.  Returns (o [B, H, N, dv], S_N [B, H, d, dv]) in float64.
+    """
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, d, dv)) if S0 is None else _f64(S0).copy()
+    o = np.empty((B, H, N, dv))
+    for t in range(N):
+        o[:, :, t], S = delta_step(S, q[:, :, t], k[:, :, t], v[:, :, t],
+                                   g[:, :, t])
+    return o, S
+
+
+def delta_decode_step(q, k, v, g, S):
+    """One decode step of the gated delta rule against a persistent state.
+
+    q, k: [B, H, d]; v: [B, H, dv]; g: [B, H]; S: [B, H, d, dv].
+    Returns (o [B, H, dv], S_new); S is not modified.
+    """
+    return delta_step(_f64(S), _f64(q), _f64(k), _f64(v), _f64(g))

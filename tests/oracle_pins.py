@@ -1,0 +1,374 @@
+"""Pins for the fp64 oracle: each check compares the oracle with something
+other than itself -- a value the pages print, a closed form, a library
+routine, finite differences, or brute force on tiny inputs.
+
+Every pin is a function of the oracle module, so tests/test_oracle.py runs
+them on the real oracle and tests/test_oracle_mutations.py runs them on
+deliberately broken copies to show that each plausible mistake is caught.
+"""
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bh(x):
+    """Add leading batch and head axes of size 1."""
+    return np.asarray(x, dtype=np.float64)[None, None]
+
+
+# --- feature map -----------------------------------------------------------
+
+def pin_phi_closed_form(orc):
+    """elu(x)+1 with alpha = 1: x+1 above zero, e^x at or below zero,
+    phi(0) = 1 (Efficient attention variants, section 4 and section 10)."""
+    xs = [-30.0, -2.5, -1.0, -1e-3, 0.0, 1e-3, 0.5, 3.0, 1000.0]
+    got = orc.phi_elu1(np.array(xs))
+    want = [x + 1.0 if x > 0 else math.exp(x) for x in xs]
+    np.testing.assert_allclose(got, want, rtol=1e-15, atol=0)
+    assert got[4] == 1.0
+
+
+def pin_phi_matches_torch(orc):
+    """Against a library routine: torch.nn.functional.elu (alpha=1) + 1."""
+    import torch
+
+    x = np.random.default_rng(7).normal(scale=3.0, size=4096)
+    ref = (torch.nn.functional.elu(torch.from_numpy(x)) + 1.0).numpy()
+    # torch forms expm1(x) + 1, which loses relative (not absolute) precision
+    # for very negative x, hence the absolute floor.
+    np.testing.assert_allclose(orc.phi_elu1(x), ref, rtol=1e-14, atol=1e-15)
+
+
+# --- LINEAR rule -----------------------------------------------------------
+
+def _handworked_inputs():
+    g = _golden("handworked_example.json")
+    fk = np.array(g["phi_k"], dtype=np.float64)
+    v = np.array(g["v"], dtype=np.float64)
+    # The page gives only phi(q3); the same query feature is used at every
+    # position (a reading: the other two outputs are then derived by hand).
+    fq = np.tile(np.array(g["phi_q3"], dtype=np.float64), (3, 1))
+    return g, fq, fk, v
+
+
+def pin_handworked_example(orc):
+    """The printed example: three keys with similarities 1, 2, 3 to phi(q3),
+    weights 1/6, 2/6, 3/6, output [10/6, 7/6]."""
+    g, fq, fk, v = _handworked_inputs()
+    o, S, z = orc.linear_prefill(_bh(fq), _bh(fk), _bh(v), eps=0.0,
+                                 fmap=orc.FMAP_IDENTITY)
+    np.testing.assert_allclose(o[0, 0, 2], g["o3"], rtol=1e-15)
+    # the same value through the quadratic form, and its normalised weights
+    oq = orc.linear_quadratic(_bh(fq), _bh(fk), _bh(v), eps=0.0,
+                              fmap=orc.FMAP_IDENTITY)
+    np.testing.assert_allclose(oq[0, 0, 2], g["o3"], rtol=1e-15)
+    sims = fk @ np.array(g["phi_q3"], dtype=np.float64)
+    np.testing.assert_allclose(sims, g["similarities_q3"])
+    np.testing.assert_allclose(sims / sims.sum(), g["weights_q3"], rtol=1e-15)
+    # With eps = 1e-6 the printed row moves by eps / den = 1e-6 / 6.
+    o_eps, _, _ = orc.linear_prefill(_bh(fq), _bh(fk), _bh(v), eps=1e-6,
+                                     fmap=orc.FMAP_IDENTITY)
+    np.testing.assert_allclose(o_eps[0, 0, 2], g["o3"], rtol=2e-7)
+
+
+def pin_handworked_derived_rows(orc):
+    """Rows 1 and 2 worked out by hand from the same table (query feature
+    [1,2] everywhere): o1 = v1 = [1,0]; o2 = (1*v1 + 2*v2)/3 = [1/3, 4/3].
+    The final state is sum_j phi(k_j) v_j^T = [[4,1],[3,3]], z = [2,2]."""
+    _, fq, fk, v = _handworked_inputs()
+    o, S, z = orc.linear_prefill(_bh(fq), _bh(fk), _bh(v), eps=0.0,
+                                 fmap=orc.FMAP_IDENTITY)
+    np.testing.assert_allclose(o[0, 0, 0], [1.0, 0.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(o[0, 0, 1], [1 / 3, 4 / 3], rtol=1e-15)
+    np.testing.assert_allclose(S[0, 0], [[4, 1], [3, 3]], rtol=0, atol=0)
+    np.testing.assert_allclose(z[0, 0], [2, 2], rtol=0, atol=0)
+
+
+def _selfcheck_inputs():
+    p = _golden("printed_values.json")["dense_vs_recurrent_selfcheck"]
+    rng = np.random.default_rng(p["seed"])
+    q = rng.normal(size=(p["N"], p["d"]))
+    k = rng.normal(size=(p["N"], p["d"]))
+    v = rng.normal(size=(p["N"], p["dv"]))
+    return p, q, k, v
+
+
+def _brute_linear(q, k, v, gamma, eps, phi):
+    """The definition written out per output: o_i is the similarity-weighted
+    average of v_j over j <= i, similarity gamma^(i-j) phi(q_i).phi(k_j),
+    with eps added to the weight sum.  Pure Python loops, tiny inputs."""
+    N, dv = v.shape
+    out = np.zeros((N, dv))
+    for i in range(N):
+        num = [0.0] * dv
+        den = 0.0
+        for j in range(i + 1):
+            s = sum(phi(q[i, a]) * phi(k[j, a]) for a in range(q.shape[1]))
+            s *= gamma ** (i - j)
+            den += s
+            for c in range(dv):
+                num[c] += s * v[j, c]
+        out[i] = [x / (den + eps) for x in num]
+    return out
+
+
+def pin_selfcheck_dense_vs_recurrent(orc):
+    """The page's own NumPy check: recurrence == masked quadratic form on
+    N=17, d=4, dv=3 normal inputs from seed 42, to 1e-12 (printed max
+    difference 4.44e-16)."""
+    p, q, k, v = _selfcheck_inputs()
+    rec, _, _ = orc.linear_prefill(_bh(q), _bh(k), _bh(v), eps=0.0)
+    den = orc.linear_quadratic(_bh(q), _bh(k), _bh(v), eps=0.0)
+    np.testing.assert_allclose(den, rec, rtol=p["rtol"], atol=p["atol"])
+    assert np.max(np.abs(den - rec)) < 1e3 * p["printed_max_abs_error"]
+
+
+def pin_brute_force_linear(orc):
+    """Recurrence against the definition written out by brute force, with a
+    per-head decay and eps, on tiny inputs with d != dv."""
+    rng = np.random.default_rng(11)
+    H, N, d, dv = 2, 9, 3, 5
+    q = rng.normal(size=(1, H, N, d))
+    k = rng.normal(size=(1, H, N, d))
+    v = rng.normal(size=(1, H, N, dv))
+    gam = np.array([1.0, 0.8])
+    eps = 0.25
+    o, _, _ = orc.linear_prefill(q, k, v, gamma=gam, eps=eps)
+    phi = lambda x: x + 1.0 if x > 0 else math.exp(x)  # noqa: E731
+    for h in range(H):
+        ref = _brute_linear(q[0, h], k[0, h], v[0, h], gam[h], eps, phi)
+        np.testing.assert_allclose(o[0, h], ref, rtol=1e-12, atol=1e-14)
+    oq = orc.linear_quadratic(q, k, v, gamma=gam, eps=eps)
+    np.testing.assert_allclose(oq, o, rtol=1e-12, atol=1e-14)
+
+
+def pin_no_future_leakage(orc):
+    """Changing k and v from token 8 on leaves outputs 0..7 unchanged and
+    changes later outputs (Efficient attention variants, section 10)."""
+    p, q, k, v = _selfcheck_inputs()
+    t0 = p["perturb_from"]
+    k2, v2 = k.copy(), v.copy()
+    k2[t0:] += p["k_shift"]
+    v2[t0:] += p["v_shift"]
+    a, _, _ = orc.linear_prefill(_bh(q), _bh(k), _bh(v), eps=0.0)
+    b, _, _ = orc.linear_prefill(_bh(q), _bh(k2), _bh(v2), eps=0.0)
+    np.testing.assert_allclose(a[..., :t0, :], b[..., :t0, :], rtol=0,
+                               atol=1e-12)
+    assert np.all(np.abs(a[..., t0:, :] - b[..., t0:, :]).max(axis=-1) > 1e-3)
+
+
+def pin_final_state_closed_form(orc):
+    """At the end of the sequence S = phi(K)^T W V and z = phi(K)^T w with
+    w_j = gamma^(N-1-j) (w = 1 without decay), computed with a library
+    matmul; and the last output equals the non-causal reassociated form
+    phi(q_N) (phi(K)^T V) / (phi(q_N) . sum_j phi(k_j))."""
+    rng = np.random.default_rng(3)
+    H, N, d, dv = 3, 40, 6, 4
+    q = rng.normal(size=(2, H, N, d))
+    k = rng.normal(size=(2, H, N, d))
+    v = rng.normal(size=(2, H, N, dv))
+    gam = np.array([1.0, 0.97, 0.5])
+    o, S, z = orc.linear_prefill(q, k, v, gamma=gam, eps=0.0)
+    fk = np.maximum(k, 0) + np.exp(np.minimum(k, 0))
+    fq = np.maximum(q, 0) + np.exp(np.minimum(q, 0))
+    for h in range(H):
+        w = gam[h] ** np.arange(N - 1, -1, -1)
+        for b in range(2):
+            np.testing.assert_allclose(S[b, h], fk[b, h].T @ (w[:, None] * v[b, h]),
+                                       rtol=1e-12)
+            np.testing.assert_allclose(z[b, h], fk[b, h].T @ w, rtol=1e-12)
+    # gamma = 1 head: the last row is the non-causal formula's last row
+    St = fk[:, 0].transpose(0, 2, 1) @ v[:, 0]
+    last = np.einsum("br,brd->bd", fq[:, 0, -1], St) / np.einsum(
+        "br,br->b", fq[:, 0, -1], fk[:, 0].sum(axis=1))[:, None]
+    np.testing.assert_allclose(o[:, 0, -1], last, rtol=1e-12)
+
+
+def pin_gamma_one_is_plain(orc):
+    """A decay of exactly 1 is the plain prefix sum."""
+    rng = np.random.default_rng(5)
+    q, k = rng.normal(size=(2, 1, 2, 12, 4))
+    v = rng.normal(size=(1, 2, 12, 3))
+    a = orc.linear_prefill(q, k, v, gamma=np.ones(2), eps=1e-6)
+    b = orc.linear_prefill(q, k, v, gamma=None, eps=1e-6)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def pin_decay_printed_value(orc):
+    """gamma = 0.99: a record written once weighs ~0.366 after 100 further
+    steps (printed to three digits); S and z both decay."""
+    p = _golden("printed_values.json")["decay_after_100_steps"]
+    n = p["steps"] + 1
+    k = np.zeros((1, 1, n, 1))
+    v = np.zeros((1, 1, n, 1))
+    k[0, 0, 0, 0] = 1.0
+    v[0, 0, 0, 0] = 1.0
+    q = np.ones((1, 1, n, 1))
+    _, S, z = orc.linear_prefill(q, k, v, gamma=np.array([p["gamma"]]),
+                                 eps=0.0, fmap=orc.FMAP_IDENTITY)
+    half_ulp = 0.5 * 10.0 ** (-p["printed_digits"])
+    assert abs(S[0, 0, 0, 0] - p["printed"]) <= half_ulp
+    assert abs(z[0, 0, 0] - p["printed"]) <= half_ulp
+    assert abs(S[0, 0, 0, 0] - 0.99 ** 100) < 1e-15
+
+
+def pin_duplicate_key_linear(orc):
+    """One unit key written with 2 then 5: unnormalised read 7, normalised
+    read 3.5 (Efficient attention variants, section 7.3)."""
+    p = _golden("printed_values.json")["duplicate_unit_key"]
+    e1 = np.array([1.0, 0.0])
+    k = np.stack([e1, e1])[None, None]
+    v = np.array(p["values"], dtype=np.float64).reshape(1, 1, 2, 1)
+    o, S, z = orc.linear_prefill(k, k, v, eps=0.0, fmap=orc.FMAP_IDENTITY)
+    assert e1 @ S[0, 0, :, 0] == p["additive_read"]
+    assert o[0, 0, 1, 0] == p["normalised_read"]
+
+
+def pin_chunk_split_and_decode(orc):
+    """Splitting the sequence and carrying (S, z) gives the same result, and
+    a decode step after a prefill equals the next row of a longer prefill."""
+    rng = np.random.default_rng(9)
+    q = rng.normal(size=(2, 3, 20, 5))
+    k = rng.normal(size=(2, 3, 20, 5))
+    v = rng.normal(size=(2, 3, 20, 2))
+    gam = np.array([0.9, 1.0, 0.6])
+    o, S, z = orc.linear_prefill(q, k, v, gamma=gam, eps=1e-3)
+    o1, S1, z1 = orc.linear_prefill(q[:, :, :7], k[:, :, :7], v[:, :, :7],
+                                    gamma=gam, eps=1e-3)
+    o2, S2, z2 = orc.linear_prefill(q[:, :, 7:19], k[:, :, 7:19], v[:, :, 7:19],
+                                    gamma=gam, eps=1e-3, S0=S1, z0=z1)
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), o[:, :, :19],
+                               rtol=1e-12)
+    od, Sd, zd = orc.linear_decode_step(q[:, :, 19], k[:, :, 19], v[:, :, 19],
+                                        S2, z2, gamma=gam, eps=1e-3)
+    np.testing.assert_allclose(od, o[:, :, 19], rtol=1e-12)
+    np.testing.assert_allclose(Sd, S, rtol=1e-12)
+    np.testing.assert_allclose(zd, z, rtol=1e-12)
+
+
+# --- gated DELTA rule ------------------------------------------------------
+
+def pin_duplicate_key_delta(orc):
+    """Delta update with step 1 on a unit key written with 2 then 5 reads 5;
+    a direction orthogonal to the key is untouched (section 7.3)."""
+    p = _golden("printed_values.json")["duplicate_unit_key"]
+    e1, e2 = np.array([1.0, 0.0]), np.array([0.0, 1.0])
+    S0 = np.array([[0.0], [4.0]])[None, None]  # something stored along e2
+    k = np.stack([e1, e1])[None, None]
+    v = np.array(p["values"], dtype=np.float64).reshape(1, 1, 2, 1)
+    g = np.ones((1, 1, 2))
+    o, S = orc.delta_prefill(k, k, v, g, S0=S0)
+    assert e1 @ S[0, 0, :, 0] == p["delta_read"]
+    assert o[0, 0, 1, 0] == p["delta_read"]
+    assert e2 @ S[0, 0, :, 0] == 4.0
+
+
+def pin_delta_gate_zero(orc):
+    """g = 0 never writes: S stays S0 and every output is S0^T q_t; from a
+    zero state every output is zero."""
+    rng = np.random.default_rng(12)
+    q = rng.normal(size=(1, 2, 10, 4))
+    k = rng.normal(size=(1, 2, 10, 4))
+    v = rng.normal(size=(1, 2, 10, 3))
+    S0 = rng.normal(size=(1, 2, 4, 3))
+    g = np.zeros((1, 2, 10))
+    o, S = orc.delta_prefill(q, k, v, g, S0=S0)
+    np.testing.assert_array_equal(S, S0)
+    np.testing.assert_allclose(o, np.matmul(q, S0), rtol=1e-14)
+    o0, S0b = orc.delta_prefill(q, k, v, g)
+    assert not np.any(o0) and not np.any(S0b)
+
+
+def pin_delta_first_token(orc):
+    """From a zero state the first output is g (k . q) v (closed form)."""
+    rng = np.random.default_rng(13)
+    q, k = rng.normal(size=(2, 1, 1, 1, 6))
+    v = rng.normal(size=(1, 1, 1, 4))
+    g = np.array([[[0.3]]])
+    o, _ = orc.delta_prefill(q, k, v, g)
+    np.testing.assert_allclose(o[0, 0, 0], 0.3 * float(k[0, 0, 0] @ q[0, 0, 0])
+                               * v[0, 0, 0], rtol=1e-14)
+
+
+def pin_delta_gradient_step(orc):
+    """One delta step is one gradient step of size g on the loss
+    L(S) = 1/2 ||S^T k - v||^2 (section 7.3); the gradient is taken by
+    central finite differences, independently of any formula."""
+    rng = np.random.default_rng(14)
+    d, dv = 5, 3
+    S = rng.normal(size=(d, dv))
+    k = rng.normal(size=d)
+    v = rng.normal(size=dv)
+    q = rng.normal(size=d)
+    g = 0.37
+
+    def loss(M):
+        r = M.T @ k - v
+        return 0.5 * float(r @ r)
+
+    grad = np.zeros_like(S)
+    h = 1e-5
+    for a in range(d):
+        for c in range(dv):
+            Sp, Sm = S.copy(), S.copy()
+            Sp[a, c] += h
+            Sm[a, c] -= h
+            grad[a, c] = (loss(Sp) - loss(Sm)) / (2 * h)
+    _, S_new = orc.delta_decode_step(q[None, None], k[None, None],
+                                     v[None, None], np.array([[g]]),
+                                     S[None, None])
+    np.testing.assert_allclose(S_new[0, 0], S - g * grad, rtol=1e-7, atol=1e-8)
+
+
+def pin_delta_brute_force(orc):
+    """Sequence against explicit matrix products S <- (I - g k k^T) S + g k v^T
+    and o = S^T q on tiny inputs with d != dv."""
+    rng = np.random.default_rng(15)
+    N, d, dv = 11, 4, 6
+    q = rng.normal(size=(N, d))
+    k = rng.normal(size=(N, d))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.normal(size=(N, dv))
+    g = 1 / (1 + np.exp(-rng.normal(size=N)))
+    S0 = rng.normal(size=(d, dv))
+    S = S0.copy()
+    ref = np.zeros((N, dv))
+    eye = np.eye(d)
+    for t in range(N):
+        S = (eye - g[t] * np.outer(k[t], k[t])) @ S + g[t] * np.outer(k[t], v[t])
+        ref[t] = S.T @ q[t]
+    o, Sf = orc.delta_prefill(_bh(q), _bh(k), _bh(v), _bh(g), S0=_bh(S0))
+    np.testing.assert_allclose(o[0, 0], ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Sf[0, 0], S, rtol=1e-12, atol=1e-13)
+
+
+def pin_delta_split_and_decode(orc):
+    """Sequence split with carried state, and decode after prefill."""
+    rng = np.random.default_rng(16)
+    q = rng.normal(size=(1, 2, 15, 4))
+    k = rng.normal(size=(1, 2, 15, 4))
+    v = rng.normal(size=(1, 2, 15, 5))
+    g = rng.uniform(size=(1, 2, 15))
+    o, S = orc.delta_prefill(q, k, v, g)
+    o1, S1 = orc.delta_prefill(q[:, :, :6], k[:, :, :6], v[:, :, :6], g[:, :, :6])
+    o2, S2 = orc.delta_prefill(q[:, :, 6:14], k[:, :, 6:14], v[:, :, 6:14],
+                               g[:, :, 6:14], S0=S1)
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), o[:, :, :14],
+                               rtol=1e-12)
+    od, Sd = orc.delta_decode_step(q[:, :, 14], k[:, :, 14], v[:, :, 14],
+                                   g[:, :, 14], S2)
+    np.testing.assert_allclose(od, o[:, :, 14], rtol=1e-12)
+    np.testing.assert_allclose(Sd, S, rtol=1e-12)
+
+
+ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

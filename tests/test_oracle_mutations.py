@@ -1,0 +1,149 @@
+"""Plant plausible mistakes in a private copy of the oracle and check that
+the pins catch every one of them (CPU only).  The real oracle module is not
+touched: each mutant is a freshly loaded copy of oracle/la_oracle.py."""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+from oracle_pins import ALL_PINS
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(
+    os.path.abspath(__file__))), "oracle", "la_oracle.py")
+
+
+def _fresh():
+    spec = importlib.util.spec_from_file_location("la_oracle_mutant", ORACLE_SRC)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _read_before_write(m):
+    def step(S, z, fq, fk, v, gam, eps):
+        num = np.einsum("...r,...rd->...d", fq, S)
+        den = np.einsum("...r,...r->...", fq, z) + eps
+        S2 = gam[..., None, None] * S + fk[..., :, None] * v[..., None, :]
+        z2 = gam[..., None] * z + fk
+        return num / den[..., None], S2, z2
+    m.linear_step = step
+
+
+def _z_not_decayed(m):
+    orig = m.linear_step
+    def step(S, z, fq, fk, v, gam, eps):
+        o, S2, _ = orig(S, z, fq, fk, v, gam, eps)
+        z2 = z + fk
+        num = np.einsum("...r,...rd->...d", fq, S2)
+        return num / (np.einsum("...r,...r->...", fq, z2) + eps)[..., None], S2, z2
+    m.linear_step = step
+
+
+def _eps_outside(m):
+    orig = m.linear_step
+    def step(S, z, fq, fk, v, gam, eps):
+        o, S2, z2 = orig(S, z, fq, fk, v, gam, 0.0)
+        return o + eps, S2, z2
+    m.linear_step = step
+
+
+def _no_plus_one(m):
+    m.phi_elu1 = lambda x: np.where(m._f64(x) > 0, m._f64(x), np.exp(m._f64(x)) - 1)
+
+
+def _exp_everywhere(m):
+    m.phi_elu1 = lambda x: np.exp(m._f64(x))
+
+
+def _decay_off_by_one(m):
+    orig = m.linear_step
+    def step(S, z, fq, fk, v, gam, eps):
+        return orig(S, z, fq, gam[..., None] * fk, v, gam, eps)
+    m.linear_step = step
+
+
+def _outer_transposed(m):
+    def step(S, z, fq, fk, v, gam, eps):
+        d, dv = S.shape[-2:]
+        upd = (v[..., :, None] * fk[..., None, :])
+        upd = upd.reshape(upd.shape[:-2] + (d, dv)) if upd.size == S.size else upd
+        S2 = gam[..., None, None] * S + upd
+        z2 = gam[..., None] * z + fk
+        num = np.einsum("...r,...rd->...d", fq, S2)
+        return num / (np.einsum("...r,...r->...", fq, z2) + eps)[..., None], S2, z2
+    m.linear_step = step
+
+
+def _quadratic_strict_mask(m):
+    orig = m.linear_quadratic
+    def quad(q, k, v, *, gamma=None, eps=1e-6, fmap=m.FMAP_ELU1):
+        qq = m._f64(q)
+        qq = np.concatenate([np.zeros_like(qq[..., :1, :]) - 50, qq[..., :-1, :]], axis=-2)
+        return orig(q, k, v, gamma=gamma, eps=eps, fmap=fmap) * 0 + orig(
+            qq, k, v, gamma=gamma, eps=eps, fmap=fmap)
+    m.linear_quadratic = quad
+
+
+def _delta_not_transposed(m):
+    def step(S, q, k, v, g):
+        d, dv = S.shape[-2:]
+        if d == dv:
+            v_hat = np.einsum("...rd,...d->...r", S, k)
+        else:
+            v_hat = np.einsum("...rd,...r->...d", S, k)[..., ::-1]
+        S2 = S + g[..., None, None] * k[..., :, None] * (v - v_hat)[..., None, :]
+        return np.einsum("...rd,...r->...d", S2, q), S2
+    m.delta_step = step
+
+
+def _delta_wrong_sign(m):
+    def step(S, q, k, v, g):
+        v_hat = np.einsum("...rd,...r->...d", S, k)
+        S2 = S + g[..., None, None] * k[..., :, None] * (v + v_hat)[..., None, :]
+        return np.einsum("...rd,...r->...d", S2, q), S2
+    m.delta_step = step
+
+
+def _delta_output_before_update(m):
+    def step(S, q, k, v, g):
+        v_hat = np.einsum("...rd,...r->...d", S, k)
+        S2 = S + g[..., None, None] * k[..., :, None] * (v - v_hat)[..., None, :]
+        return np.einsum("...rd,...r->...d", S, q), S2
+    m.delta_step = step
+
+
+def _delta_gate_on_value_only(m):
+    def step(S, q, k, v, g):
+        v_hat = np.einsum("...rd,...r->...d", S, k)
+        S2 = S + k[..., :, None] * (g[..., None] * v - v_hat)[..., None, :]
+        return np.einsum("...rd,...r->...d", S2, q), S2
+    m.delta_step = step
+
+
+def _delta_dropped_correction(m):
+    def step(S, q, k, v, g):
+        S2 = S + g[..., None, None] * k[..., :, None] * v[..., None, :]
+        return np.einsum("...rd,...r->...d", S2, q), S2
+    m.delta_step = step
+
+
+MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
+           _exp_everywhere, _decay_off_by_one, _outer_transposed,
+           _quadratic_strict_mask, _delta_not_transposed, _delta_wrong_sign,
+           _delta_output_before_update, _delta_gate_on_value_only,
+           _delta_dropped_correction]
+
+
+@pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
+def test_pins_catch_mutant(mutate):
+    mod = _fresh()
+    mutate(mod)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutant {mutate.__name__}"
