@@ -1,2 +1,159 @@
 """Causal linear attention (elu+1 kernel, per-head decay, gated delta rule)
-on MI355X: a thin Python binding over the C-ABI library liblinattn.so."""
+on MI355X: a thin Python binding over the C-ABI library liblinattn.so.
+
+Only argument marshalling happens here; every step of the computation runs
+in the HIP kernels behind include/linattn.h.  PyTorch supplies device memory
+and the current stream.  There is no fallback: if the library is missing or
+a tensor is not on a GPU, the call raises.
+
+    o, S, z = prefill(q, k, v, gamma=gamma, eps=1e-6)       # LINEAR, elu+1
+    o, S, _ = prefill(q, k, v, rule="delta", g=g)             # gated delta
+    o = decode_step(q1, k1, v1, S, z)                         # in place on S, z
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import LinattnError, LibraryMissing  # noqa: F401
+
+__all__ = ["prefill", "decode_step", "state_init", "workspace_size",
+           "LinattnError", "LibraryMissing"]
+
+_RULES = {"linear": _lib.LA_RULE_LINEAR, "delta": _lib.LA_RULE_DELTA}
+_FMAPS = {"elu1": _lib.LA_FMAP_ELU1, "identity": _lib.LA_FMAP_IDENTITY}
+_DTYPES = {torch.float32: _lib.LA_F32, torch.bfloat16: _lib.LA_BF16}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError("liblinattn works on GPU tensors only")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _need_f32(*ts):
+    for t in ts:
+        if t is not None and t.dtype != torch.float32:
+            raise ValueError("gamma, g, states must be float32")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _prefill_args(q, k, v, rule, fmap, gamma, g, eps):
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,N,d] and v [B,H,N,dv]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, H, N, d = q.shape
+    a = _lib.PrefillArgs()
+    a.B, a.H, a.N, a.d, a.dv = B, H, N, d, v.shape[3]
+    a.dtype = _DTYPES[q.dtype]
+    a.rule = _RULES[rule]
+    a.fmap = _FMAPS[fmap]
+    a.gamma = _ptr(gamma)
+    a.g = _ptr(g)
+    a.eps = float(eps)
+    return a
+
+
+def workspace_size(q, k, v, *, rule="linear", fmap="elu1", gamma=None, g=None,
+                   eps=1e-6):
+    """Workspace bytes la_prefill needs for these tensors (current device)."""
+    a = _prefill_args(q, k, v, rule, fmap, gamma, g, eps)
+    n = _lib.load().la_prefill_workspace_size(ctypes.byref(a))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes")
+    return int(n)
+
+
+def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
+            S_in=None, z_in=None, S_out=None, z_out=None, return_state=True,
+            o=None, workspace=None):
+    """Chunked prefill over [B,H,N,*] sequences (see la_prefill).
+
+    rule "linear": fmap defaults to "elu1"; gamma [H] fp32 or None; eps >= 0.
+    rule "delta":  fmap "identity"; g [B,H,N] fp32 required.
+    Returns (o, S_out, z_out); the states are None unless requested
+    (return_state) or passed in.  z_out is always None for "delta".
+    """
+    if fmap is None:
+        fmap = "elu1" if rule == "linear" else "identity"
+    _need_gpu(q, k, v, gamma, g, S_in, z_in, S_out, z_out, o, workspace)
+    _need_f32(gamma, g, S_in, z_in, S_out, z_out)
+    a = _prefill_args(q, k, v, rule, fmap, gamma, g, eps)
+    B, H, N, d = q.shape
+    dv = v.shape[3]
+    if o is None:
+        o = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
+    if return_state and S_out is None:
+        S_out = torch.empty((B, H, d, dv), dtype=torch.float32, device=q.device)
+    if return_state and z_out is None and rule == "linear":
+        z_out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    a.S_in, a.z_in = _ptr(S_in), _ptr(z_in)
+    a.S_out, a.z_out = _ptr(S_out), _ptr(z_out)
+    a.q, a.k, a.v, a.o = _ptr(q), _ptr(k), _ptr(v), _ptr(o)
+    need = lib.la_prefill_workspace_size(ctypes.byref(a))
+    if need == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes")
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _lib.check(lib.la_prefill(ctypes.byref(a), _stream()), "la_prefill")
+    return o, S_out, z_out
+
+
+def decode_step(q, k, v, S, z=None, *, rule="linear", fmap=None, gamma=None,
+                g=None, eps=1e-6, o=None):
+    """One token per sequence: q, k [B,H,d], v [B,H,dv]; S [B,H,d,dv] (and z
+    [B,H,d] for "linear") are updated in place.  Returns o [B,H,dv]."""
+    if fmap is None:
+        fmap = "elu1" if rule == "linear" else "identity"
+    _need_gpu(q, k, v, S, z, gamma, g, o)
+    _need_f32(S, z, gamma, g)
+    if q.dim() != 3 or k.shape != q.shape or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [B,H,d] and v [B,H,dv]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share dtype float32 or bfloat16")
+    B, H, d = q.shape
+    dv = v.shape[2]
+    if S.shape != (B, H, d, dv) or (z is not None and z.shape != (B, H, d)):
+        raise ValueError("state shape mismatch")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    a = _lib.DecodeArgs()
+    a.B, a.H, a.d, a.dv = B, H, d, dv
+    a.dtype = _DTYPES[q.dtype]
+    a.rule = _RULES[rule]
+    a.fmap = _FMAPS[fmap]
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.gamma, a.g = _ptr(gamma), _ptr(g)
+    a.eps = float(eps)
+    a.S, a.z, a.o = _ptr(S), _ptr(z), _ptr(o)
+    _lib.check(_lib.load().la_decode_step(ctypes.byref(a), _stream()),
+               "la_decode_step")
+    return o
+
+
+def state_init(S, z=None):
+    """Zero a state in place on the current stream (fill kernel)."""
+    _need_gpu(S, z)
+    _need_f32(S, z)
+    B, H, d, dv = S.shape
+    _lib.check(_lib.load().la_state_init(_ptr(S), _ptr(z), B, H, d, dv, _stream()),
+               "la_state_init")
+    return S, z

@@ -1,0 +1,290 @@
+// C ABI of liblinattn.so: argument validation, planning and kernel dispatch.
+// Every check runs before anything is enqueued (see include/linattn.h).
+#include <atomic>
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "../../include/linattn.h"
+#include "la_internal.hpp"
+
+namespace la {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 256;  // no device visible (e.g. a workspace query on a build host)
+  }
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess || v <= 0) {
+    (void)hipGetLastError();
+    v = 256;
+  }
+  if (dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// ---- kernel timing log -----------------------------------------------------
+namespace {
+struct ProfRec {
+  const char *name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+hipEvent_t g_pending = nullptr;
+constexpr size_t kMaxRecs = 65536;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return e;
+}
+
+void clear_log_locked() {
+  for (auto &r : g_recs) {
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  if (g_pending) g_pool.push_back(g_pending);
+  g_pending = nullptr;
+}
+}  // namespace
+
+void prof_begin(hipStream_t s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (g_recs.size() >= kMaxRecs) return;
+  if (g_pending) g_pool.push_back(g_pending);
+  g_pending = take_event();
+  if (g_pending && hipEventRecord(g_pending, s) != hipSuccess) {
+    (void)hipGetLastError();
+    g_pool.push_back(g_pending);
+    g_pending = nullptr;
+  }
+}
+
+void prof_end(const char *name, hipStream_t s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_pending) return;
+  hipEvent_t e = take_event();
+  if (!e) return;
+  if (hipEventRecord(e, s) != hipSuccess) {
+    (void)hipGetLastError();
+    g_pool.push_back(e);
+    return;
+  }
+  g_recs.push_back({name, g_pending, e});
+  g_pending = nullptr;
+}
+
+}  // namespace la
+
+namespace {
+
+constexpr int kMaxGridY = 65535;
+
+bool dims_ok(int d, int dv) {
+  return d >= 1 && d <= LA_MAX_DIM && dv >= 1 && dv <= LA_MAX_DIM;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int to_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_EHIP; }
+
+// Shape / mode checks shared by the workspace query and the prefill itself.
+int check_prefill_shape(const la_prefill_args *a) {
+  if (!a) return LA_EINVAL;
+  if (a->B < 0 || a->H < 0 || a->N < 0 || !dims_ok(a->d, a->dv)) return LA_EINVAL;
+  if (a->dtype != LA_F32 && a->dtype != LA_BF16) return LA_EINVAL;
+  if (a->rule != LA_RULE_LINEAR && a->rule != LA_RULE_DELTA) return LA_EINVAL;
+  if (a->fmap != LA_FMAP_IDENTITY && a->fmap != LA_FMAP_ELU1) return LA_EINVAL;
+  if (a->rule == LA_RULE_DELTA && a->fmap != LA_FMAP_IDENTITY) return LA_EINVAL;
+  if ((long long)a->B * a->H > kMaxGridY) return LA_EUNSUPPORTED;
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t la_abi_version(void) { return 1; }
+
+const char *la_status_str(int s) {
+  switch (s) {
+    case LA_OK: return "ok";
+    case LA_EINVAL: return "invalid argument";
+    case LA_EUNSUPPORTED: return "unsupported configuration";
+    case LA_EHIP: return "HIP launch or runtime error";
+    case LA_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+size_t la_prefill_workspace_size(const la_prefill_args *a) {
+  if (check_prefill_shape(a) != LA_OK) return (size_t)-1;
+  const int BH = a->B * a->H;
+  if (BH == 0 || a->N == 0) return 0;
+  if (a->rule == LA_RULE_LINEAR)
+    return la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16).ws_bytes;
+  return 0;
+}
+
+int la_prefill(const la_prefill_args *a, void *stream) {
+  int st = check_prefill_shape(a);
+  if (st != LA_OK) return st;
+  const int BH = a->B * a->H;
+  const bool linear = a->rule == LA_RULE_LINEAR;
+  if (linear) {
+    if (a->g || !(a->eps >= 0.f) || !std::isfinite(a->eps)) return LA_EINVAL;
+  } else {
+    if (!a->g && BH > 0 && a->N > 0) return LA_EINVAL;
+    if (a->gamma || a->z_in || a->z_out) return LA_EINVAL;
+  }
+  if (BH > 0 && a->N > 0 && (!a->q || !a->k || !a->v || !a->o)) return LA_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (BH == 0) return LA_OK;
+
+  const size_t nS = (size_t)BH * a->d * a->dv, nz = (size_t)BH * a->d;
+  if (a->N == 0) {  // no tokens: the state passes through unchanged
+    hipError_t e = hipSuccess;
+    if (a->S_out)
+      e = a->S_in ? la::launch_copy(a->S_out, a->S_in, nS, s)
+                  : la::launch_fill(a->S_out, nS, 0.f, s);
+    if (e == hipSuccess && a->z_out)
+      e = a->z_in ? la::launch_copy(a->z_out, a->z_in, nz, s)
+                  : la::launch_fill(a->z_out, nz, 0.f, s);
+    return to_status(e);
+  }
+  if (!linear) return LA_EUNSUPPORTED;
+
+  const bool bf16_io = a->dtype == LA_BF16;
+  const la::LinearPlan plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io);
+  if (plan.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < plan.ws_bytes))
+    return LA_EWORKSPACE;
+
+  la::PrefillParams p{};
+  p.BH = BH;
+  p.H = a->H;
+  p.N = a->N;
+  p.d = a->d;
+  p.dv = a->dv;
+  p.fmap = a->fmap == LA_FMAP_ELU1;
+  const int vec = bf16_io ? 8 : 4;
+  p.vec_ok = (a->d % vec == 0) && (a->dv % vec == 0) && aligned16(a->q) &&
+             aligned16(a->k) && aligned16(a->v);
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.gamma = a->gamma;
+  p.g = a->g;
+  p.eps = a->eps;
+  p.S_in = a->S_in;
+  p.z_in = a->z_in;
+  p.S_out = a->S_out;
+  p.z_out = a->z_out;
+  p.o = a->o;
+  p.ws = reinterpret_cast<float *>(a->workspace);
+  p.nseg = plan.nseg;
+  p.seg_len = plan.seg_len;
+  return to_status(la::launch_linear_prefill(p, plan, bf16_io, s));
+}
+
+int la_decode_step(const la_decode_args *a, void *stream) {
+  if (!a) return LA_EINVAL;
+  if (a->B < 0 || a->H < 0 || !dims_ok(a->d, a->dv)) return LA_EINVAL;
+  if (a->dtype != LA_F32 && a->dtype != LA_BF16) return LA_EINVAL;
+  if (a->rule != LA_RULE_LINEAR && a->rule != LA_RULE_DELTA) return LA_EINVAL;
+  if (a->fmap != LA_FMAP_IDENTITY && a->fmap != LA_FMAP_ELU1) return LA_EINVAL;
+  const bool delta = a->rule == LA_RULE_DELTA;
+  const long long BH = (long long)a->B * a->H;
+  if (BH > 0x7fffffffLL) return LA_EUNSUPPORTED;
+  if (delta) {
+    if (a->fmap != LA_FMAP_IDENTITY || a->gamma || a->z) return LA_EINVAL;
+    if (BH > 0 && !a->g) return LA_EINVAL;
+  } else {
+    if (a->g || !(a->eps >= 0.f) || !std::isfinite(a->eps)) return LA_EINVAL;
+    if (BH > 0 && !a->z) return LA_EINVAL;
+  }
+  if (BH == 0) return LA_OK;
+  if (!a->q || !a->k || !a->v || !a->o || !a->S) return LA_EINVAL;
+
+  la::DecodeParams p{};
+  p.BH = (int)BH;
+  p.H = a->H;
+  p.d = a->d;
+  p.dv = a->dv;
+  p.fmap = a->fmap == LA_FMAP_ELU1;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.gamma = a->gamma;
+  p.g = a->g;
+  p.eps = a->eps;
+  p.S = a->S;
+  p.z = a->z;
+  p.o = a->o;
+  const int vec = (a->dv % 4 == 0 && aligned16(a->S)) ? 4 : 1;
+  return to_status(la::launch_decode(p, a->dtype == LA_BF16, delta, vec,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+int la_state_init(float *S, float *z, int32_t B, int32_t H, int32_t d,
+                  int32_t dv, void *stream) {
+  if (B < 0 || H < 0 || !dims_ok(d, dv)) return LA_EINVAL;
+  const size_t BH = (size_t)B * H;
+  if (BH == 0) return LA_OK;
+  if (!S) return LA_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = la::launch_fill(S, BH * d * dv, 0.f, s);
+  if (e == hipSuccess && z) e = la::launch_fill(z, BH * d, 0.f, s);
+  return to_status(e);
+}
+
+int la_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(la::g_prof_mu);
+  la::clear_log_locked();
+  la::g_prof_on.store(on != 0, std::memory_order_relaxed);
+  return LA_OK;
+}
+
+int la_profile_collect(la_kernel_time *out, int max) {
+  std::lock_guard<std::mutex> lk(la::g_prof_mu);
+  int n = 0;
+  bool err = false;
+  for (const auto &r : la::g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess ||
+        hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      (void)hipGetLastError();
+      err = true;
+      break;
+    }
+    if (out && n < max) out[n] = la_kernel_time{r.name, ms};
+    ++n;
+  }
+  la::clear_log_locked();
+  if (err) return -1;
+  return n < max ? n : max;
+}
+
+}  // extern "C"

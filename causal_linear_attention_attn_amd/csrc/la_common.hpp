@@ -1,0 +1,106 @@
+// Device helpers shared by the linattn kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int LA_MAXD = 128;  // largest d and dv
+
+// ---------------------------------------------------------------------------
+// Element conversion.  bf16 -> f32 is exact; f32 -> bf16 rounds to nearest
+// even (v_cvt_pk_bf16_f32 on gfx950).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// elu(x)+1 with alpha 1: x+1 above zero, e^x at or below (no large positive
+// exponent is ever formed).
+__device__ __forceinline__ float phi_elu1(float x) {
+  return x > 0.f ? x + 1.f : __expf(x);
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core fragments.  One "k-step" contracts 32 values of k.  Lane l of a
+// wave holds row (A) / column (B) l%16 and the eight k values of slot group
+// l/16.  The A and B operand slots are laid out identically, so any
+// consistent assignment of logical k to the (group, element) slots gives the
+// same sum; the kernels rely on that to feed accumulator tiles back in as
+// operands without a layout change.
+// Accumulator layout (16x16 fp32): lane l holds rows 4*(l/16)+r, r=0..3, of
+// column l%16.
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x8 v; };
+
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag<bf16> &a,
+                                    const Frag<bf16> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+// fp32 inputs: eight 16x16x4 products, element e of every slot group at a time.
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag<float> &a,
+                                    const Frag<float> &b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+// 8 consecutive elements from LDS (16 B for bf16, 32 B for fp32).
+__device__ __forceinline__ void lds_frag(Frag<bf16> &f, const bf16 *p) {
+  f.v = *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ void lds_frag(Frag<float> &f, const float *p) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  f.v = (f32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+// 4 consecutive elements into slots [off, off+4) of a fragment.
+__device__ __forceinline__ void lds_half(Frag<bf16> &f, const bf16 *p, int off) {
+  const bf16x4 h = *reinterpret_cast<const bf16x4 *>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f.v[off + e] = h[e];
+}
+__device__ __forceinline__ void lds_half(Frag<float> &f, const float *p, int off) {
+  const f32x4 h = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f.v[off + e] = h[e];
+}
+template <typename T>
+__device__ __forceinline__ float frag_elem(const Frag<T> &f, int e) {
+  return to_f32(f.v[e]);
+}
+template <typename T>
+__device__ __forceinline__ void frag_set(Frag<T> &f, int e, float x) {
+  f.v[e] = from_f32<T>(x);
+}
+
+// Four consecutive T to LDS.
+__device__ __forceinline__ void lds_store4(bf16 *p, float a, float b, float c,
+                                           float d) {
+  *reinterpret_cast<bf16x4 *>(p) = (bf16x4){(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+}
+__device__ __forceinline__ void lds_store4(float *p, float a, float b, float c,
+                                           float d) {
+  *reinterpret_cast<f32x4 *>(p) = (f32x4){a, b, c, d};
+}
+
+// Sum over the four slot groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace la

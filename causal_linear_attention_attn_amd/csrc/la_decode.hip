@@ -1,0 +1,241 @@
+// Single-token decode step against a persistent fp32 state, updated in place.
+//
+// LINEAR ("What Is Linear Attention?" section 4 with the decay of 5.1;
+// "LLM inference optimisation (3)", recurrent form: read once, add once):
+//     S <- gamma S + phi(k) v^T,  z <- gamma z + phi(k)
+//     o  = S^T phi(q) / (phi(q) . z + eps)
+// DELTA ("What Is Linear Attention?" 5.2-5.3):
+//     b = S^T k,  S <- S + g k (v - b)^T,  o = S^T q  (updated state)
+//       = S_old^T q + g (k . q) (v - b)
+//
+// The step is bound by HBM: each (b,h) state block (d x dv fp32, 64 KiB at
+// d = dv = 128) is read once and written once.  One workgroup of 256 threads
+// owns one block; consecutive threads own consecutive VEC-wide column groups
+// of a row, so each wave moves whole rows (coalesced dwordx4 traffic), and
+// each thread walks rows rg, rg + RG, ... .  All of a thread's rows are
+// loaded before any is used so that every load is in flight at once.  Column
+// sums (the reads S^T phi(q), S^T k, S^T q) are reduced across the RG row
+// groups through LDS in a fixed order: no atomics, deterministic.
+#include "la_common.hpp"
+#include "la_internal.hpp"
+
+namespace la {
+namespace {
+
+constexpr int kDecThreads = 256;
+
+__device__ __forceinline__ float block_sum(float x, float *red) {
+  // all threads of a 256-thread block call this; returns the sum everywhere
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = x;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <typename T, int VEC, bool DELTA>
+__global__ void __launch_bounds__(kDecThreads)
+decode_kernel(DecodeParams p) {
+  constexpr int ROWS = 64 / VEC;  // rows per thread at most (d <= 128)
+  __shared__ float s_q[LA_MAXD], s_k[LA_MAXD], s_v[LA_MAXD];
+  __shared__ float s_part[2][kDecThreads * VEC];
+  __shared__ float s_a[LA_MAXD], s_b[LA_MAXD];
+  __shared__ float s_red[4];
+
+  const int bh = blockIdx.x;
+  const int t = threadIdx.x;
+  const int d = p.d, dv = p.dv;
+  const T *q = reinterpret_cast<const T *>(p.q) + (size_t)bh * d;
+  const T *k = reinterpret_cast<const T *>(p.k) + (size_t)bh * d;
+  const T *v = reinterpret_cast<const T *>(p.v) + (size_t)bh * dv;
+  float *S = p.S + (size_t)bh * d * dv;
+
+  if (t < d) {
+    float xq = to_f32(q[t]), xk = to_f32(k[t]);
+    if (!DELTA && p.fmap) { xq = phi_elu1(xq); xk = phi_elu1(xk); }
+    s_q[t] = xq;
+    s_k[t] = xk;
+  }
+  if (t < dv) s_v[t] = to_f32(v[t]);
+  const float gam = (!DELTA && p.gamma) ? p.gamma[bh % p.H] : 1.f;
+  const float gate = DELTA ? p.g[bh] : 0.f;
+  __syncthreads();
+
+  const int colsv = dv / VEC;        // column groups per row
+  const int RG = kDecThreads / colsv;  // row groups
+  const int cv = t % colsv, rg = t / colsv;
+  const bool active = rg < RG;
+  const int c0 = cv * VEC;
+
+  // load every row this thread owns
+  float sr[ROWS][VEC];
+#pragma unroll
+  for (int m = 0; m < ROWS; ++m) {
+    const int r = rg + RG * m;
+    if (active && r < d) {
+      const float *src = S + (size_t)r * dv + c0;
+      if constexpr (VEC == 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(src);
+        sr[m][0] = x[0]; sr[m][1] = x[1]; sr[m][2] = x[2]; sr[m][3] = x[3];
+      } else {
+        sr[m][0] = src[0];
+      }
+    }
+  }
+
+  float acc[VEC], acc2[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) { acc[e] = 0.f; acc2[e] = 0.f; }
+
+  if constexpr (!DELTA) {
+    // update in place and accumulate phi(q)^T S_new for our columns
+#pragma unroll
+    for (int m = 0; m < ROWS; ++m) {
+      const int r = rg + RG * m;
+      if (active && r < d) {
+        const float fk = s_k[r], fq = s_q[r];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float sn = fmaf(gam, sr[m][e], fk * s_v[c0 + e]);
+          sr[m][e] = sn;
+          acc[e] = fmaf(fq, sn, acc[e]);
+        }
+        float *dst = S + (size_t)r * dv + c0;
+        if constexpr (VEC == 4)
+          *reinterpret_cast<f32x4 *>(dst) =
+              (f32x4){sr[m][0], sr[m][1], sr[m][2], sr[m][3]};
+        else
+          dst[0] = sr[m][0];
+      }
+    }
+    // normaliser: z <- gamma z + phi(k); den = phi(q) . z_new
+    float dz = 0.f;
+    if (t < d) {
+      const float zn = fmaf(gam, p.z[(size_t)bh * d + t], s_k[t]);
+      p.z[(size_t)bh * d + t] = zn;
+      dz = s_q[t] * zn;
+    }
+    const float den = block_sum(dz, s_red) + p.eps;
+    if (active) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) s_part[0][rg * dv + c0 + e] = acc[e];
+    }
+    __syncthreads();
+    if (t < dv) {
+      float num = 0.f;
+      for (int r2 = 0; r2 < RG; ++r2) num += s_part[0][r2 * dv + t];
+      reinterpret_cast<T *>(p.o)[(size_t)bh * dv + t] = from_f32<T>(num / den);
+    }
+  } else {
+    // column dots of the OLD state with k and q, from the same read
+#pragma unroll
+    for (int m = 0; m < ROWS; ++m) {
+      const int r = rg + RG * m;
+      if (active && r < d) {
+        const float kr = s_k[r], qr = s_q[r];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          acc[e] = fmaf(kr, sr[m][e], acc[e]);
+          acc2[e] = fmaf(qr, sr[m][e], acc2[e]);
+        }
+      }
+    }
+    const float qk = block_sum(t < d ? s_q[t] * s_k[t] : 0.f, s_red);
+    if (active) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        s_part[0][rg * dv + c0 + e] = acc[e];
+        s_part[1][rg * dv + c0 + e] = acc2[e];
+      }
+    }
+    __syncthreads();
+    if (t < dv) {
+      float b = 0.f, a = 0.f;
+      for (int r2 = 0; r2 < RG; ++r2) {
+        b += s_part[0][r2 * dv + t];
+        a += s_part[1][r2 * dv + t];
+      }
+      const float u = s_v[t] - b;  // residual v - S_old^T k
+      s_b[t] = u;
+      s_a[t] = a;
+      reinterpret_cast<T *>(p.o)[(size_t)bh * dv + t] =
+          from_f32<T>(fmaf(gate * qk, u, a));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < ROWS; ++m) {
+      const int r = rg + RG * m;
+      if (active && r < d) {
+        const float gk = gate * s_k[r];
+        float *dst = S + (size_t)r * dv + c0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sr[m][e] = fmaf(gk, s_b[c0 + e], sr[m][e]);
+        if constexpr (VEC == 4)
+          *reinterpret_cast<f32x4 *>(dst) =
+              (f32x4){sr[m][0], sr[m][1], sr[m][2], sr[m][3]};
+        else
+          dst[0] = sr[m][0];
+      }
+    }
+  }
+}
+
+__global__ void fill_kernel(float *dst, size_t n, float value) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = value;
+}
+
+__global__ void copy_kernel(float *dst, const float *src, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+template <typename T, int VEC, bool DELTA>
+hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s) {
+  prof_begin(s);
+  hipLaunchKernelGGL((decode_kernel<T, VEC, DELTA>), dim3(p.BH),
+                     dim3(kDecThreads), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) prof_end(DELTA ? "delta_decode" : "linear_decode", s);
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams &p, bool bf16_io, bool delta,
+                         int vec, hipStream_t s) {
+  if (bf16_io) {
+    if (delta) return vec == 4 ? launch_decode_t<bf16, 4, true>(p, s)
+                               : launch_decode_t<bf16, 1, true>(p, s);
+    return vec == 4 ? launch_decode_t<bf16, 4, false>(p, s)
+                    : launch_decode_t<bf16, 1, false>(p, s);
+  }
+  if (delta) return vec == 4 ? launch_decode_t<float, 4, true>(p, s)
+                             : launch_decode_t<float, 1, true>(p, s);
+  return vec == 4 ? launch_decode_t<float, 4, false>(p, s)
+                  : launch_decode_t<float, 1, false>(p, s);
+}
+
+hipError_t launch_fill(float *dst, size_t n, float value, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dst,
+                     n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(float *dst, const float *src, size_t n, hipStream_t s) {
+  if (n == 0 || dst == src) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dst,
+                     src, n);
+  return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,170 @@
+/*
+ * linattn.h -- C ABI of liblinattn.so: causal linear attention with an
+ * elu+1 feature map, optional per-head decay, eps-stabilised normaliser,
+ * and the gated delta rule, as a chunked prefill over whole sequences and as
+ * a single-token decode step against a persistent state.  gfx950 (MI355X).
+ *
+ * Sources (web pages, cited by title and section):
+ *   "What Is Linear Attention?" (xutianle.me)                       [WILA]
+ *   "Efficient attention variants" (bailixisu.com)                   [EAV]
+ *   "LLM inference optimisation (3): Linear Attention" (wangyu.me)   [LIO3]
+ *   "Transformers Are RNNs" (myhz0606.com)                           [TAR]
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major memory
+ *     owned by the caller.  The library never allocates, frees or keeps a
+ *     pointer after the call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and runs asynchronously; the library never synchronises the
+ *     host.  The caller must keep every buffer alive until the stream has
+ *     passed the enqueued work.
+ *   - Arguments are validated before anything is enqueued: a call that
+ *     returns LA_EINVAL, LA_EUNSUPPORTED or LA_EWORKSPACE has enqueued
+ *     nothing.  LA_EHIP means a HIP launch failed; work enqueued before the
+ *     failure may still run.  The library never aborts and never throws
+ *     across this interface.
+ *   - B, H and N may be 0 (nothing to do); d and dv are 1..128.
+ *   - Thread-safe: the only shared state is a cached per-device CU count
+ *     and the (mutex-guarded) kernel timing log below.
+ *   - Results are deterministic for a given device, shape and build: no
+ *     atomics take part in any sum.
+ *   - Numerics: inputs fp32 or bf16; feature maps, decays, normaliser,
+ *     state and all accumulation in fp32.  With bf16 inputs the matrix
+ *     products take bf16 operands (the state read uses a bf16 copy of the
+ *     fp32 state; the fp32 state itself is never rounded).
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_MAX_DIM 128 /* largest d and dv */
+
+typedef enum {
+  LA_OK = 0,
+  LA_EINVAL = 1,       /* a NULL pointer where one is required, a negative
+                          size, d or dv outside 1..128, eps < 0 or not finite,
+                          or an argument the rule does not take */
+  LA_EUNSUPPORTED = 2, /* valid request this build does not implement */
+  LA_EHIP = 3,         /* a HIP call or kernel launch failed */
+  LA_EWORKSPACE = 4    /* workspace NULL or smaller than
+                          la_prefill_workspace_size() */
+} la_status;
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype; /* dtype of q, k, v, o */
+
+/* The feature map phi applied to q and k ([EAV] section 4, [LIO3] 'what is
+ * phi'): ELU1 is elu(x)+1 with alpha 1, i.e. x+1 for x > 0 and e^x
+ * otherwise; IDENTITY means q and k already are the (non-negative) features,
+ * as in the hand-worked example of [EAV] section 5.1. */
+typedef enum { LA_FMAP_IDENTITY = 0, LA_FMAP_ELU1 = 1 } la_fmap;
+
+/* LA_RULE_LINEAR ([WILA] sections 4 and 5.1; [EAV] section 5; [TAR] eps):
+ *     S_t = gamma_h S_{t-1} + phi(k_t) v_t^T,  z_t = gamma_h z_{t-1} + phi(k_t)
+ *     o_t = S_t^T phi(q_t) / (phi(q_t) . z_t + eps)
+ *   The state is read after the token is written (the token sees itself).
+ * LA_RULE_DELTA ([WILA] sections 5.2 and 5.3):
+ *     S_t = S_{t-1} + g_t k_t (v_t - S_{t-1}^T k_t)^T,   o_t = S_t^T q_t
+ *   raw q and k (fmap must be IDENTITY), no normaliser, no z. */
+typedef enum { LA_RULE_LINEAR = 0, LA_RULE_DELTA = 1 } la_rule;
+
+/* One call processes B*H independent sequences of N tokens. */
+typedef struct la_prefill_args {
+  int32_t B, H, N;   /* batch, heads, tokens per sequence (each >= 0) */
+  int32_t d, dv;     /* key/query feature dim r = d; value dim (1..128) */
+  int32_t dtype;     /* la_dtype of q, k, v and o */
+  int32_t rule;      /* la_rule */
+  int32_t fmap;      /* la_fmap (DELTA: IDENTITY only) */
+  const void *q;     /* [B,H,N,d]  */
+  const void *k;     /* [B,H,N,d]  */
+  const void *v;     /* [B,H,N,dv] */
+  const float *gamma;/* LINEAR: [H] decay per head, each in (0,1]; NULL = 1.
+                        DELTA: must be NULL.  Values are the caller's
+                        contract (not read on the host). */
+  const float *g;    /* DELTA: [B,H,N] write gate per token (required).
+                        LINEAR: must be NULL. */
+  float eps;         /* LINEAR: added to the denominator, >= 0. DELTA: ignored */
+  const float *S_in; /* [B,H,d,dv] initial state; NULL = zeros */
+  const float *z_in; /* LINEAR: [B,H,d] initial normaliser; NULL = zeros.
+                        DELTA: must be NULL. */
+  float *S_out;      /* [B,H,d,dv] state after the last token; NULL = not
+                        written.  May alias S_in exactly (in-place update). */
+  float *z_out;      /* LINEAR: [B,H,d]; NULL = not written; may alias z_in.
+                        DELTA: must be NULL. */
+  void *o;           /* [B,H,N,dv] output, dtype as q (required if N > 0) */
+  void *workspace;   /* device scratch of workspace_bytes, caller-owned;
+                        may be NULL when la_prefill_workspace_size() is 0 */
+  size_t workspace_bytes;
+} la_prefill_args;
+
+/* Bytes of device workspace la_prefill needs for these arguments on the
+ * current device (0 when none).  Reads only the sizes, dtype and rule.
+ * Returns (size_t)-1 when the sizes are invalid. */
+size_t la_prefill_workspace_size(const la_prefill_args *args);
+
+/* Chunked prefill: computes o for every token and, when S_out/z_out are
+ * given, the final state.  Equivalent (up to fp rounding order) to running
+ * the per-token recurrence of `rule` from (S_in, z_in). */
+int la_prefill(const la_prefill_args *args, void *stream);
+
+/* One token per sequence against a persistent state updated in place. */
+typedef struct la_decode_args {
+  int32_t B, H;      /* sequences and heads (each >= 0) */
+  int32_t d, dv;     /* 1..128 */
+  int32_t dtype;     /* la_dtype of q, k, v and o */
+  int32_t rule;      /* la_rule */
+  int32_t fmap;      /* la_fmap (DELTA: IDENTITY only) */
+  const void *q;     /* [B,H,d]  */
+  const void *k;     /* [B,H,d]  */
+  const void *v;     /* [B,H,dv] */
+  const float *gamma;/* LINEAR: [H] or NULL (=1).  DELTA: must be NULL. */
+  const float *g;    /* DELTA: [B,H] write gate (required). LINEAR: NULL. */
+  float eps;         /* LINEAR: >= 0 */
+  float *S;          /* [B,H,d,dv] fp32, read and overwritten in place */
+  float *z;          /* LINEAR: [B,H,d] fp32 in place (required).
+                        DELTA: must be NULL. */
+  void *o;           /* [B,H,dv] output, dtype as q */
+} la_decode_args;
+
+/* One decode step ([LIO3] 'recurrent form': one read and one write of the
+ * state per token).  S (and z) must not overlap q, k, v or o. */
+int la_decode_step(const la_decode_args *args, void *stream);
+
+/* Zero-fill a state: S [B,H,d,dv] and, if z is not NULL, z [B,H,d]
+ * ([LIO3] 'implementation': the state starts as zeros).  Uses a fill
+ * kernel (no memset node), so it may be captured in a HIP graph. */
+int la_state_init(float *S, float *z, int32_t B, int32_t H, int32_t d,
+                  int32_t dv, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *la_status_str(int status);
+
+/* Kernel timing for benchmarks and tracing (not part of the method).
+ * While enabled, every kernel the library launches is bracketed by two HIP
+ * events recorded on the launch stream (a few microseconds of overhead per
+ * launch, no host synchronisation).  la_profile_collect() waits for the
+ * recorded events, writes up to `max` records (oldest first) and clears the
+ * log; it returns the number of records written, or -1 on a HIP error.
+ * Records past an internal limit of 65536 are dropped.  Kernel names are
+ * static strings.  Enabling/disabling clears the log.  Not meant to be
+ * toggled while another thread is launching. */
+typedef struct la_kernel_time {
+  const char *name; /* kernel name (static storage) */
+  float ms;         /* elapsed time between the bracketing events */
+} la_kernel_time;
+int la_profile_enable(int on);
+int la_profile_collect(la_kernel_time *out, int max);
+
+/* ABI version: bumped whenever a struct above changes layout. */
+int32_t la_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

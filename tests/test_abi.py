@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, the ctypes structs match the C layout, and invalid
+arguments are rejected before anything touches a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from causal_linear_attention_attn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_lists_exactly_the_binding_exports():
+    assert _declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (la_\w+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    fields_p = [f for f, _ in _lib.PrefillArgs._fields_]
+    fields_d = [f for f, _ in _lib.DecodeArgs._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "linattn.h"',
+             "int main(void){"]
+    lines.append('printf("%zu\\n", sizeof(la_prefill_args));')
+    for f in fields_p:
+        lines.append(f'printf("%zu\\n", offsetof(la_prefill_args, {f}));')
+    lines.append('printf("%zu\\n", sizeof(la_decode_args));')
+    for f in fields_d:
+        lines.append(f'printf("%zu\\n", offsetof(la_decode_args, {f}));')
+    lines.append("return 0;}")
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-I", os.path.dirname(HEADER),
+                    str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True,
+                                          text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(_lib.PrefillArgs)]
+    want += [getattr(_lib.PrefillArgs, f).offset for f in fields_p]
+    want += [ctypes.sizeof(_lib.DecodeArgs)]
+    want += [getattr(_lib.DecodeArgs, f).offset for f in fields_d]
+    assert got == want
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.la_status_str(s)
+    assert lib.la_status_str(99) == b"unknown status"
+    assert lib.la_abi_version() == _lib.ABI_VERSION
+
+
+def _args(**kw):
+    a = _lib.PrefillArgs()
+    a.B, a.H, a.N, a.d, a.dv = 1, 1, 4, 8, 8
+    a.dtype, a.rule, a.fmap = _lib.LA_BF16, _lib.LA_RULE_LINEAR, _lib.LA_FMAP_ELU1
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    a.q = a.k = a.v = a.o = fake
+    a.eps = 1e-6
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("bad", [
+    dict(B=-1), dict(N=-2), dict(d=0), dict(dv=129), dict(d=200), dict(dtype=7),
+    dict(rule=5), dict(fmap=3), dict(eps=-1.0), dict(eps=float("nan")),
+    dict(eps=float("inf")), dict(q=None), dict(o=None),
+    dict(g=ctypes.c_void_p(0x2000)),                       # gate on LINEAR
+    dict(rule=_lib.LA_RULE_DELTA),                          # DELTA with elu1
+    dict(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY),  # DELTA, no g
+    dict(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY,
+         g=ctypes.c_void_p(0x2000), z_out=ctypes.c_void_p(0x3000)),
+    dict(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY,
+         g=ctypes.c_void_p(0x2000), gamma=ctypes.c_void_p(0x3000)),
+])
+def test_prefill_rejects_invalid_arguments(lib, bad):
+    a = _args(**bad)
+    assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EINVAL
+
+
+def test_prefill_null_args_and_unsupported_grid(lib):
+    assert lib.la_prefill(None, None) == _lib.LA_EINVAL
+    a = _args(B=70000, H=1)
+    assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+    assert lib.la_prefill_workspace_size(ctypes.byref(_args(d=0))) == \
+        ctypes.c_size_t(-1).value
+
+
+def test_empty_inputs_are_noops(lib):
+    for kw in (dict(B=0), dict(H=0)):
+        a = _args(**kw)
+        a.q = a.k = a.v = a.o = None
+        assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_OK
+        assert lib.la_prefill_workspace_size(ctypes.byref(a)) == 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(B=-1), dict(d=0), dict(dv=300), dict(dtype=2), dict(rule=9),
+    dict(eps=-0.5), dict(S=None), dict(z=None),
+    dict(rule=_lib.LA_RULE_DELTA),                          # elu1 + delta
+    dict(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY),  # z given, no g
+])
+def test_decode_rejects_invalid_arguments(lib, bad):
+    a = _lib.DecodeArgs()
+    a.B, a.H, a.d, a.dv = 2, 2, 8, 8
+    a.dtype, a.rule, a.fmap = _lib.LA_BF16, _lib.LA_RULE_LINEAR, _lib.LA_FMAP_ELU1
+    fake = ctypes.c_void_p(0x1000)
+    a.q = a.k = a.v = a.o = a.S = a.z = fake
+    a.eps = 1e-6
+    for k, v in bad.items():
+        setattr(a, k, v)
+    assert lib.la_decode_step(ctypes.byref(a), None) == _lib.LA_EINVAL
+
+
+def test_state_init_rejects_invalid_arguments(lib):
+    assert lib.la_state_init(None, None, 1, 1, 8, 8, None) == _lib.LA_EINVAL
+    assert lib.la_state_init(ctypes.c_void_p(0x1000), None, 1, 1, 0, 8, None) == \
+        _lib.LA_EINVAL
+    assert lib.la_state_init(None, None, 0, 4, 8, 8, None) == _lib.LA_OK

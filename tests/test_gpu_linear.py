@@ -1,0 +1,201 @@
+"""GPU parity for the LINEAR rule: chunked prefill and decode step against the
+fp64 oracle, through the C ABI, on seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import causal_linear_attention_attn_amd as la
+from causal_linear_attention_attn_amd import inputs
+import oracle
+from parity import TOL, assert_close, cpu
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _rand(shape, dtype, seed, scale=1.0):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(dtype).to(DEV)
+
+
+def _oracle_prefill(q, k, v, gamma, eps, fmap, S0=None, z0=None):
+    return oracle.linear_prefill(cpu(q), cpu(k), cpu(v),
+                                 gamma=None if gamma is None else cpu(gamma),
+                                 eps=eps, fmap=fmap, S0=cpu(S0), z0=cpu(z0))
+
+
+def test_handworked_example_on_gpu():
+    x = inputs.handworked_example(DEV)
+    o, S, z = la.prefill(x["q"], x["k"], x["v"], fmap="identity", eps=0.0)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(o[0, 0, 2].cpu().numpy(), [10 / 6, 7 / 6], rtol=1e-6)
+    np.testing.assert_allclose(o[0, 0, :2].cpu().numpy(), [[1, 0], [1 / 3, 4 / 3]],
+                               rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(S[0, 0].cpu().numpy(), [[4, 1], [3, 3]], rtol=1e-6)
+    np.testing.assert_allclose(z[0, 0].cpu().numpy(), [2, 2], rtol=1e-6)
+    # and with eps = 1e-6, as the workload runs it, against the oracle
+    o2, _, _ = la.prefill(x["q"], x["k"], x["v"], fmap="identity", eps=1e-6)
+    ref, _, _ = _oracle_prefill(x["q"], x["k"], x["v"], None, 1e-6, "identity")
+    assert_close(o2, ref, 1e-6, "hand-worked example")
+
+
+SHAPES = [  # (B, H, N, d, dv)
+    (1, 1, 1, 64, 64), (1, 2, 3, 16, 16), (2, 1, 63, 64, 64), (1, 1, 64, 64, 64),
+    (1, 2, 65, 64, 64), (2, 2, 200, 128, 128), (1, 3, 130, 64, 128),
+    (1, 2, 97, 128, 64), (1, 1, 17, 4, 3), (2, 1, 50, 100, 72), (1, 1, 70, 2, 2),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("decay", [False, True], ids=["nodecay", "decay"])
+def test_prefill_small(shape, dtype, decay):
+    B, H, N, d, dv = shape
+    seed = (B * 7919 + H * 104729 + N * 31 + d * 17 + dv * 3
+            + 1000 * (dtype == torch.bfloat16) + 5000 * decay)
+    sc = 1 / np.sqrt(d)
+    q = _rand((B, H, N, d), dtype, seed, sc)
+    k = _rand((B, H, N, d), dtype, seed + 1, sc)
+    v = _rand((B, H, N, dv), dtype, seed + 2)
+    if dv < 16:
+        # With 2 or 3 values per row, a weighted average of zero-mean values
+        # can cancel to a few percent of the values averaged, and bf16
+        # rounding of the weights (about 2^-8 each) then exceeds 2e-2 of the
+        # row itself.  A CPU emulation of the kernel's rounding points gives
+        # the same error as the GPU, so the metric, not the kernel, is what
+        # is ill-conditioned there; a nonzero mean keeps those rows away from
+        # cancellation.
+        v = v + 1.0
+    gamma = inputs.per_head_gamma(H, DEV) if decay else None
+    o, S, z = la.prefill(q, k, v, gamma=gamma, eps=1e-6)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_prefill(q, k, v, gamma, 1e-6, "elu1")
+    tol = TOL[dtype]
+    assert_close(o, ro, tol, "o")
+    assert_close(S, rS, tol, "S", axes=(-2, -1))
+    assert_close(z, rz, tol, "z")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_prefill_with_initial_state_and_identity_map(dtype):
+    B, H, N, d, dv = 2, 3, 150, 64, 64
+    q = _rand((B, H, N, d), dtype, 1).abs()
+    k = _rand((B, H, N, d), dtype, 2).abs()
+    v = _rand((B, H, N, dv), dtype, 3)
+    S0 = _rand((B, H, d, dv), torch.float32, 4).abs()
+    z0 = _rand((B, H, d), torch.float32, 5).abs()
+    gamma = torch.tensor([0.9, 1.0, 0.99], device=DEV)
+    o, S, z = la.prefill(q, k, v, fmap="identity", gamma=gamma, eps=1e-3,
+                         S_in=S0, z_in=z0)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_prefill(q, k, v, gamma, 1e-3, "identity", S0, z0)
+    assert_close(o, ro, TOL[dtype], "o")
+    assert_close(S, rS, TOL[dtype], "S", axes=(-2, -1))
+    assert_close(z, rz, TOL[dtype], "z")
+
+
+@pytest.mark.parametrize("N", [3000, 4096 + 17])
+def test_prefill_many_segments(N):
+    """Few heads and a long sequence: the two-level scan runs with many
+    segments and a ragged last chunk; S_in is given and S_out aliases it."""
+    B, H, d, dv = 1, 2, 64, 64
+    dtype = torch.bfloat16
+    q = _rand((B, H, N, d), dtype, 10, 0.125)
+    k = _rand((B, H, N, d), dtype, 11, 0.125)
+    v = _rand((B, H, N, dv), dtype, 12, 0.125)
+    gamma = torch.tensor([0.999, 1.0], device=DEV)
+    S = _rand((B, H, d, dv), torch.float32, 13).abs()
+    z = _rand((B, H, d), torch.float32, 14).abs() + 1
+    S0, z0 = S.clone(), z.clone()
+    assert la.workspace_size(q, k, v, gamma=gamma) > 0
+    o, _, _ = la.prefill(q, k, v, gamma=gamma, S_in=S, z_in=z, S_out=S, z_out=z)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_prefill(q, k, v, gamma, 1e-6, "elu1", S0, z0)
+    assert_close(o, ro, 2e-2, "o")
+    assert_close(S, rS, 2e-2, "S", axes=(-2, -1))
+    assert_close(z, rz, 2e-2, "z")
+
+
+def test_prefill_empty_sequence_passes_state_through():
+    q = torch.empty((2, 2, 0, 8), dtype=torch.bfloat16, device=DEV)
+    v = torch.empty((2, 2, 0, 4), dtype=torch.bfloat16, device=DEV)
+    S0 = _rand((2, 2, 8, 4), torch.float32, 20)
+    z0 = _rand((2, 2, 8), torch.float32, 21)
+    o, S, z = la.prefill(q, q, v, S_in=S0, z_in=z0)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 2, 0, 4)
+    assert torch.equal(S, S0) and torch.equal(z, z0)
+    _, S, z = la.prefill(q, q, v)
+    torch.cuda.synchronize()
+    assert not S.any() and not z.any()
+
+
+def test_prefill_deterministic_and_guarded():
+    """Two runs agree bit for bit, and nothing is written outside o."""
+    B, H, N, d, dv = 2, 4, 333, 128, 128
+    q = _rand((B, H, N, d), torch.bfloat16, 30, 0.09)
+    k = _rand((B, H, N, d), torch.bfloat16, 31, 0.09)
+    v = _rand((B, H, N, dv), torch.bfloat16, 32)
+    n = B * H * N * dv
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    o = buf[guard:guard + n].view(B, H, N, dv)
+    la.prefill(q, k, v, o=o, return_state=False)
+    o1 = o.clone()
+    la.prefill(q, k, v, o=o, return_state=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o)
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + n:]).all()
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("dims", [(128, 128), (64, 64), (4, 3), (100, 72), (2, 2),
+                                  (128, 66)], ids=lambda s: "x".join(map(str, s)))
+def test_decode_steps(dims, dtype):
+    d, dv = dims
+    B, H, steps = 3, 5, 6
+    S = _rand((B, H, d, dv), torch.float32, 40).abs() * 0.1
+    z = _rand((B, H, d), torch.float32, 41).abs() + 0.5
+    gamma = inputs.per_head_gamma(H, DEV)
+    rS, rz = cpu(S).double().numpy(), cpu(z).double().numpy()
+    for t in range(steps):
+        q = _rand((B, H, d), dtype, 50 + t, 1 / np.sqrt(d))
+        k = _rand((B, H, d), dtype, 60 + t, 1 / np.sqrt(d))
+        v = _rand((B, H, dv), dtype, 70 + t)
+        o = la.decode_step(q, k, v, S, z, gamma=gamma, eps=1e-6)
+        torch.cuda.synchronize()
+        ro, rS, rz = oracle.linear_decode_step(cpu(q), cpu(k), cpu(v), rS, rz,
+                                               gamma=cpu(gamma), eps=1e-6)
+        assert_close(o, ro, TOL[dtype], f"o step {t}")
+    assert_close(S, rS, 1e-5, "S", axes=(-2, -1))
+    assert_close(z, rz, 1e-5, "z")
+
+
+def test_prefill_then_decode_handoff():
+    """prefill(N) then one decode step equals row N of prefill(N+1)."""
+    B, H, N, d, dv = 2, 2, 257, 128, 128
+    sc = 1 / np.sqrt(d)
+    q = _rand((B, H, N + 1, d), torch.bfloat16, 80, sc)
+    k = _rand((B, H, N + 1, d), torch.bfloat16, 81, sc)
+    v = _rand((B, H, N + 1, dv), torch.bfloat16, 82, sc)
+    gamma = torch.tensor([0.995, 1.0], device=DEV)
+    _, S, z = la.prefill(q[:, :, :N].contiguous(), k[:, :, :N].contiguous(),
+                         v[:, :, :N].contiguous(), gamma=gamma)
+    o = la.decode_step(q[:, :, N].contiguous(), k[:, :, N].contiguous(),
+                       v[:, :, N].contiguous(), S, z, gamma=gamma)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_prefill(q, k, v, gamma, 1e-6, "elu1")
+    assert_close(o, ro[:, :, N], 2e-2, "decode after prefill")
+    assert_close(S, rS, 2e-2, "S", axes=(-2, -1))
+
+
+def test_state_init_zeroes():
+    S = torch.randn((3, 2, 16, 8), device=DEV)
+    z = torch.randn((3, 2, 16), device=DEV)
+    la.state_init(S, z)
+    torch.cuda.synchronize()
+    assert not S.any() and not z.any()
