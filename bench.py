@@ -112,7 +112,9 @@ def bench_prefill(la, lib, torch, w, steps, warmup):
         times = kt.collect()
     dt = (t1 - t0) / steps
     kern = {n: sum(v) / len(v) for n, v in times.items()}
-    return dict(x=x, o=o, S=S, z=z, dt=dt, kern=kern, ws_bytes=ws_bytes)
+    rec = d * dv + d
+    nseg = ws_bytes // (B * H * rec * 4) if ws_bytes else 1
+    return dict(x=x, o=o, S=S, z=z, dt=dt, kern=kern, ws_bytes=ws_bytes, nseg=nseg)
 
 
 def bench_decode(la, lib, torch, nsteps, warmup=8):
@@ -230,6 +232,7 @@ def main():
                    "rule": w.rule, "fmap": w.fmap, "decay": w.decay,
                    "eps": w.eps, "head_tokens_per_step": head_tokens},
         "kernels_ms": res["kern"],
+        "plan": {"segments_per_sequence": res["nseg"], "workspace_bytes": res["ws_bytes"]},
     }
     if w.rule == "linear":
         kname = "linear_chunk"

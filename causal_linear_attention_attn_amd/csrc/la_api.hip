@@ -191,7 +191,7 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   p.fmap = a->fmap == LA_FMAP_ELU1;
   const int vec = bf16_io ? 8 : 4;
   p.vec_ok = (a->d % vec == 0) && (a->dv % vec == 0) && aligned16(a->q) &&
-             aligned16(a->k) && aligned16(a->v);
+             aligned16(a->k) && aligned16(a->v) && aligned16(a->o);
   p.q = a->q;
   p.k = a->k;
   p.v = a->v;

@@ -96,6 +96,42 @@ __device__ __forceinline__ void lds_store4(float *p, float a, float b, float c,
   *reinterpret_cast<f32x4 *>(p) = (f32x4){a, b, c, d};
 }
 
+// 16-byte vector of T (8 bf16 or 4 fp32).
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> { using type = bf16x8; };
+template <> struct Vec16<float> { using type = f32x4; };
+
+// R consecutive T to LDS from fp32 values (R * sizeof(T) = 2..32 bytes).
+template <typename T, int R>
+__device__ __forceinline__ void lds_store_n(T *p, const float (&x)[R]) {
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (R == 1) {
+      p[0] = (bf16)x[0];
+    } else if constexpr (R == 2) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<bf16x2 *>(p) = (bf16x2){(bf16)x[0], (bf16)x[1]};
+    } else if constexpr (R == 4) {
+      lds_store4(p, x[0], x[1], x[2], x[3]);
+    } else {
+      static_assert(R == 8, "unsupported width");
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];
+      *reinterpret_cast<bf16x8 *>(p) = v;
+    }
+  } else if constexpr (R == 1) {
+    p[0] = x[0];
+  } else if constexpr (R == 2) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<f32x2 *>(p) = (f32x2){x[0], x[1]};
+  } else {
+    static_assert(R % 4 == 0, "unsupported width");
+#pragma unroll
+    for (int e = 0; e < R; e += 4)
+      *reinterpret_cast<f32x4 *>(p + e) = (f32x4){x[e], x[e + 1], x[e + 2], x[e + 3]};
+  }
+}
+
 // Sum over the four slot groups (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float sum_groups(float x) {
   x += __shfl_xor(x, 16);

@@ -12,6 +12,7 @@ struct LinearPlan {
   int dk, dv_pad;   // padded feature / value dims (64 or 128)
   int chunk;        // tokens per chunk
   int threads;      // workgroup size
+  int per_cu;       // resident workgroups per CU
   int nseg;         // segments per sequence (>= 1)
   int seg_len;      // tokens per segment (multiple of chunk)
   size_t ws_bytes;  // workspace bytes

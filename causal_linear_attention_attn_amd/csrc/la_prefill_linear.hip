@@ -24,32 +24,45 @@
 //            P_{s+1} = gamma^L P_s + dS_s, P_0 = (S_in, z_in);
 //   phase 3  chunk_kernel    per (segment, head): outputs from P_s, chunk by
 //            chunk; the last segment writes (S_out, z_out).
-// With one segment, phase 3 runs alone from (S_in, z_in).
+// With one segment, phase 3 runs alone from (S_in, z_in).  The planner picks
+// the segment count so that one launch fills every workgroup slot once.
 //
 // Data layout: q, k [BH, N, d], v, o [BH, N, dv] (row-major, dtype T);
 // workspace slots [nseg][BH][d*dv + d] fp32 (state then normaliser).
 //
-// Tiles live in LDS: Phi_q and Phi_k row-major (token rows), Phi_k^T scaled
-// by w and V^T (feature rows: the token contraction needs consecutive tokens
-// per lane), and a T-precision copy S^T of the fp32 state for the state read.
-// The fp32 state itself lives in matrix-core accumulators and is never
-// rounded.  All contractions run on the matrix cores (bf16 inputs: 16x16x32
-// bf16; fp32 inputs: 16x16x4 fp32).
+// Per chunk, the kernel streams q, k, v once from HBM and writes o once.
+// Global loads are issued one chunk ahead into registers (the next chunk's
+// loads are in flight while the current chunk computes); each thread owns
+// whole 16-byte column blocks of a few consecutive rows, so every wave reads
+// contiguous row segments.  Tiles live in LDS: Phi_q and Phi_k row-major
+// (token rows), Phi_k^T scaled by w and V^T (feature rows: the token
+// contraction needs consecutive tokens per lane), a T-precision copy S^T of
+// the fp32 state for the state read, and an output tile that turns the
+// matrix-core output layout into 16-byte row stores.  The fp32 state itself
+// lives in matrix-core accumulators and is never rounded.  All contractions
+// run on the matrix cores (bf16 inputs: 16x16x32 bf16; fp32 inputs: 16x16x4
+// fp32).  Powers of gamma come from a per-head table gamma^m, m = 0..C.
+#include <atomic>
+
 #include "la_common.hpp"
 #include "la_internal.hpp"
 
 namespace la {
 namespace {
 
+constexpr int kLdsBytes = 160 * 1024;
+
 template <typename T, int DK_, int DV_, int C_, int NW_>
 struct Cfg {
   using type = T;
+  using vec = typename Vec16<T>::type;
   static constexpr int DK = DK_, DV = DV_, C = C_, NW = NW_;
   static constexpr int NT = NW * kWave;
   static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte vector
   static constexpr int QLD = DK + VEC;  // row stride of Phi_q / Phi_k tiles
   static constexpr int TLD = C + VEC;   // row stride of Phi_k^T / V^T tiles
   static constexpr int SLD = DK + VEC;  // row stride of the S^T copy
+  static constexpr int OLD = DV + VEC;  // row stride of the output tile
   static constexpr int NRB = C / 16;    // 16-row blocks of a chunk
   static constexpr int NG = NW / NRB;   // waves sharing one row block
   static constexpr int NPW = (DV / 16) / NG;  // output column tiles per wave
@@ -58,8 +71,14 @@ struct Cfg {
   static constexpr int TNW = (DV / 16) / NWN; // state column tiles per wave
   static constexpr int KSD = DK / 32;   // k-steps over features
   static constexpr int KSC = C / 32;    // k-steps over tokens
+  static constexpr int QCB = DK / VEC;  // 16-byte column blocks per q/k row
+  static constexpr int VCB = DV / VEC;  // ... per v/o row
+  static constexpr int RQ = C * DK / (VEC * NT);  // q/k rows per thread
+  static constexpr int RV = C * DV / (VEC * NT);  // v/o rows per thread
   static_assert(NG >= 1 && NPW >= 1 && TFW >= 1 && TNW >= 1, "bad tiling");
   static_assert(NRB % 2 == 0, "chunk must hold an even number of row blocks");
+  static_assert(RQ >= 1 && RQ * VEC * NT == C * DK, "q/k rows per thread");
+  static_assert(RV >= 1 && RV * VEC * NT == C * DV, "v/o rows per thread");
 };
 
 template <class CF>
@@ -70,7 +89,9 @@ struct alignas(16) SmemChunk {
   T Kt[CF::DK * CF::TLD];
   T Vt[CF::DV * CF::TLD];
   T St[CF::DV * CF::SLD];
+  T Os[CF::C * CF::OLD];
   float zs[CF::DK];
+  float pw[CF::C + 4];  // gamma^m, m = 0..C
 };
 
 template <class CF>
@@ -78,111 +99,108 @@ struct alignas(16) SmemSummary {
   using T = typename CF::type;
   T Kt[CF::DK * CF::TLD];
   T Vt[CF::DV * CF::TLD];
+  float pw[CF::C + 4];
 };
 
-// VEC consecutive elements of one row as fp32; zero outside the tensor.
-template <typename T, int VEC>
-__device__ __forceinline__ void load_vec(float (&x)[VEC], const T *row, int col0,
-                                         int ncols, bool row_ok, bool vec_ok) {
-  if (!row_ok) {
+// This thread's rows of one chunk, as loaded (raw 16-byte vectors).
+template <class CF>
+struct ChunkRegs {
+  typename CF::vec q[CF::RQ], k[CF::RQ], v[CF::RV];
+};
+
+// One 16-byte vector of a row; zero outside the tensor.
+template <typename T>
+__device__ __forceinline__ typename Vec16<T>::type load16(const T *row, int col0,
+                                                          int ncols, bool row_ok,
+                                                          bool vec_ok) {
+  using V = typename Vec16<T>::type;
+  constexpr int VEC = 16 / (int)sizeof(T);
+  if (row_ok && vec_ok && col0 + VEC <= ncols)
+    return *reinterpret_cast<const V *>(row + col0);
+  V r;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) x[e] = 0.f;
-    return;
-  }
-  if (vec_ok && col0 + VEC <= ncols) {
-    if constexpr (sizeof(T) == 2) {
-      const bf16x8 r = *reinterpret_cast<const bf16x8 *>(row + col0);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) x[e] = (float)r[e];
-    } else {
-      const f32x4 r = *reinterpret_cast<const f32x4 *>(row + col0);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) x[e] = r[e];
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      x[e] = (col0 + e < ncols) ? to_f32(row[col0 + e]) : 0.f;
-  }
+  for (int e = 0; e < VEC; ++e)
+    r[e] = (row_ok && col0 + e < ncols) ? row[col0 + e] : from_f32<T>(0.f);
+  return r;
 }
 
-template <typename T, int VEC>
-__device__ __forceinline__ void store_row_vec(T *dst, const float (&x)[VEC]) {
-  if constexpr (sizeof(T) == 2) {
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) r[e] = (bf16)x[e];
-    *reinterpret_cast<bf16x8 *>(dst) = r;
-  } else {
-    *reinterpret_cast<f32x4 *>(dst) = (f32x4){x[0], x[1], x[2], x[3]};
-  }
-}
-
-// Stage one chunk into LDS.  Work unit: 4 token rows x VEC columns.
-// Feature-map padding rule: lanes outside the tensor (tokens past N, features
-// past d) are zero AFTER phi (phi(0) = 1 would be wrong).
-template <class CF, bool WITH_ROWS>
-__device__ __forceinline__ void stage_chunk(
-    typename CF::type *Qs, typename CF::type *Ks, typename CF::type *Kt,
-    typename CF::type *Vt, const PrefillParams &p, const typename CF::type *qh,
-    const typename CF::type *kh, const typename CF::type *vh, int c0, int Lc,
-    float log2g) {
-  using T = typename CF::type;
-  constexpr int VEC = CF::VEC, C = CF::C;
-  constexpr int UQ = (C / 4) * (CF::DK / VEC);
-  constexpr int UV = (C / 4) * (CF::DV / VEC);
-  const int d = p.d, dv = p.dv;
+template <class CF, bool WITH_Q>
+__device__ __forceinline__ void prefetch(ChunkRegs<CF> &R, const PrefillParams &p,
+                                         const typename CF::type *qh,
+                                         const typename CF::type *kh,
+                                         const typename CF::type *vh, int c0,
+                                         int Lc) {
   const bool vec_ok = p.vec_ok != 0;
-  const bool elu = p.fmap != 0;
+  const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
+#pragma unroll
+  for (int r = 0; r < CF::RQ; ++r) {
+    const int row = qrg * CF::RQ + r;
+    const bool ok = row < Lc;
+    const size_t off = (size_t)(c0 + row) * p.d;
+    if constexpr (WITH_Q) R.q[r] = load16(qh + off, qcb * CF::VEC, p.d, ok, vec_ok);
+    R.k[r] = load16(kh + off, qcb * CF::VEC, p.d, ok, vec_ok);
+  }
+  const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
+#pragma unroll
+  for (int r = 0; r < CF::RV; ++r) {
+    const int row = vrg * CF::RV + r;
+    R.v[r] = load16(vh + (size_t)(c0 + row) * p.dv, vcb * CF::VEC, p.dv,
+                    row < Lc, vec_ok);
+  }
+}
 
-  if constexpr (WITH_ROWS) {
-    for (int u = threadIdx.x; u < UQ; u += CF::NT) {
-      const int r0 = (u / (CF::DK / VEC)) * 4, col0 = (u % (CF::DK / VEC)) * VEC;
+// Registers -> LDS tiles.  Feature-map padding rule: lanes outside the
+// tensor (tokens past N, features past d) are zero AFTER phi (phi(0) = 1
+// would be wrong).
+template <class CF, bool WITH_Q>
+__device__ __forceinline__ void commit(const ChunkRegs<CF> &R,
+                                       typename CF::type *Qs,
+                                       typename CF::type *Ks,
+                                       typename CF::type *Kt,
+                                       typename CF::type *Vt, const float *pw,
+                                       const PrefillParams &p, int Lc) {
+  using T = typename CF::type;
+  constexpr int VEC = CF::VEC;
+  const bool elu = p.fmap != 0;
+  const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
+  const int col0 = qcb * VEC;
+  float kw[VEC][CF::RQ];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r = r0 + rr;
-        float x[VEC];
-        load_vec<T, VEC>(x, qh + (size_t)(c0 + r) * d, col0, d, r < Lc, vec_ok);
+  for (int r = 0; r < CF::RQ; ++r) {
+    const int row = qrg * CF::RQ + r;
+    const bool ok = row < Lc;
+    float x[VEC];
+    if constexpr (WITH_Q) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          x[e] = (r < Lc && col0 + e < d) ? (elu ? phi_elu1(x[e]) : x[e]) : 0.f;
-        store_row_vec<T, VEC>(Qs + r * CF::QLD + col0, x);
+      for (int e = 0; e < VEC; ++e) {
+        const float xq = to_f32(R.q[r][e]);
+        x[e] = (ok && col0 + e < p.d) ? (elu ? phi_elu1(xq) : xq) : 0.f;
       }
-    }
-  }
-  for (int u = threadIdx.x; u < UQ; u += CF::NT) {
-    const int r0 = (u / (CF::DK / VEC)) * 4, col0 = (u % (CF::DK / VEC)) * VEC;
-    float kt[4][VEC];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = r0 + rr;
-      float x[VEC];
-      load_vec<T, VEC>(x, kh + (size_t)(c0 + r) * d, col0, d, r < Lc, vec_ok);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e)
-        x[e] = (r < Lc && col0 + e < d) ? (elu ? phi_elu1(x[e]) : x[e]) : 0.f;
-      if constexpr (WITH_ROWS) store_row_vec<T, VEC>(Ks + r * CF::QLD + col0, x);
-      const float w = r < Lc ? exp2f((float)(Lc - 1 - r) * log2g) : 0.f;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) kt[rr][e] = x[e] * w;
+      lds_store_n<T, VEC>(Qs + row * CF::QLD + col0, x);
     }
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      lds_store4(Kt + (col0 + e) * CF::TLD + r0, kt[0][e], kt[1][e], kt[2][e],
-                 kt[3][e]);
-  }
-  for (int u = threadIdx.x; u < UV; u += CF::NT) {
-    const int r0 = (u / (CF::DV / VEC)) * 4, col0 = (u % (CF::DV / VEC)) * VEC;
-    float vt[4][VEC];
+    for (int e = 0; e < VEC; ++e) {
+      const float xk = to_f32(R.k[r][e]);
+      x[e] = (ok && col0 + e < p.d) ? (elu ? phi_elu1(xk) : xk) : 0.f;
+    }
+    if constexpr (WITH_Q) lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
+    const float w = ok ? pw[Lc - 1 - row] : 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      load_vec<T, VEC>(vt[rr], vh + (size_t)(c0 + r0 + rr) * dv, col0, dv,
-                       r0 + rr < Lc, vec_ok);
-#pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      lds_store4(Vt + (col0 + e) * CF::TLD + r0, vt[0][e], vt[1][e], vt[2][e],
-                 vt[3][e]);
+    for (int e = 0; e < VEC; ++e) kw[e][r] = x[e] * w;
   }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e)
+    lds_store_n<T, CF::RQ>(Kt + (col0 + e) * CF::TLD + qrg * CF::RQ, kw[e]);
+
+  const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
+  float vt[VEC][CF::RV];
+#pragma unroll
+  for (int r = 0; r < CF::RV; ++r)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) vt[e][r] = to_f32(R.v[r][e]);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e)
+    lds_store_n<T, CF::RV>(Vt + (vcb * VEC + e) * CF::TLD + vrg * CF::RV, vt[e]);
 }
 
 // S <- gamma^Lc S + Phi_k^T diag(w) V and z <- gamma^Lc z + Phi_k^T w for the
@@ -238,15 +256,20 @@ __device__ __forceinline__ void write_state_copy(
 }
 
 template <class CF>
+__device__ __forceinline__ void fill_powers(float *pw, float log2g) {
+  for (int m = threadIdx.x; m <= CF::C; m += CF::NT) pw[m] = exp2f((float)m * log2g);
+}
+
+template <class CF>
 __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
   using T = typename CF::type;
+  using V = typename CF::vec;
   __shared__ SmemChunk<CF> sm;
 
   const int seg = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int d = p.d, dv = p.dv, N = p.N;
-  const float log2g = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
   const size_t rec = (size_t)d * dv + d;
   const T *qh = reinterpret_cast<const T *>(p.q) + (size_t)bh * N * d;
   const T *kh = reinterpret_cast<const T *>(p.k) + (size_t)bh * N * d;
@@ -254,6 +277,10 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
   T *oh = reinterpret_cast<T *>(p.o) + (size_t)bh * N * dv;
   const int t_begin = seg * p.seg_len;
   const int t_end = min(N, t_begin + p.seg_len);
+
+  ChunkRegs<CF> R;
+  prefetch<CF, true>(R, p, qh, kh, vh, t_begin, min(CF::C, N - t_begin));
+  fill_powers<CF>(sm.pw, p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f);
 
   const float *S0, *z0;
   if (p.nseg > 1) {
@@ -266,6 +293,7 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
 
   const int rb = wv % CF::NRB, ng = wv / CF::NRB;  // output role
   const int wf = wv % 4, wn = wv / 4;              // state-tile role
+  const int irow = 16 * rb + li;  // chunk row this lane carries as an operand
 
   f32x4 Sacc[CF::TFW][CF::TNW];
   float zreg[CF::TFW];
@@ -285,15 +313,16 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
     zreg[a] = (z0 && fz < d) ? z0[fz] : 0.f;
   }
   write_state_copy<CF>(sm.St, sm.zs, Sacc, zreg, wf, wn, li, lg);
+  __syncthreads();
 
   for (int c0 = t_begin; c0 < t_end; c0 += CF::C) {
     const int Lc = min(CF::C, N - c0);
-    stage_chunk<CF, true>(sm.Qs, sm.Ks, sm.Kt, sm.Vt, p, qh, kh, vh, c0, Lc,
-                          log2g);
+    commit<CF, true>(R, sm.Qs, sm.Ks, sm.Kt, sm.Vt, sm.pw, p, Lc);
     __syncthreads();
+    if (c0 + CF::C < t_end)
+      prefetch<CF, true>(R, p, qh, kh, vh, c0 + CF::C, min(CF::C, N - c0 - CF::C));
 
     // ---- state read: gamma^(i+1) phi(q_i)^T S-, and phi(q_i) . z- ----
-    const int irow = 16 * rb + li;  // row this lane carries as an operand
     Frag<T> qf[CF::KSD];
     float dz = 0.f;
 #pragma unroll
@@ -315,10 +344,10 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
         mma(acc[nt], qf[ks], sf);
       }
     }
-    dz = sum_groups(dz) * exp2f((float)(irow + 1) * log2g);
+    dz = sum_groups(dz) * sm.pw[irow + 1];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float sc = exp2f((float)(16 * rb + 4 * lg + r + 1) * log2g);
+      const float sc = sm.pw[16 * rb + 4 * lg + r + 1];
 #pragma unroll
       for (int nt = 0; nt < CF::NPW; ++nt) acc[nt][r] *= sc;
     }
@@ -340,7 +369,7 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int lag = irow - (16 * tj + 4 * lg + r);
-          float x = lag >= 0 ? at[tj][r] * exp2f((float)lag * log2g) : 0.f;
+          float x = lag >= 0 ? at[tj][r] * sm.pw[lag] : 0.f;
           x = to_f32(from_f32<T>(x));  // the weight the product below uses
           at[tj][r] = x;
           dintra += x;
@@ -370,28 +399,43 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
       }
     }
 
-    // ---- normalise and store ----
+    // ---- normalise into the output tile ----
     const float den = dz + dintra + p.eps;  // for row irow
-    float dr[4];
+    float rden[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dr[r] = __shfl(den, 4 * lg + r);
+    for (int r = 0; r < 4; ++r) rden[r] = 1.f / __shfl(den, 4 * lg + r);
 #pragma unroll
     for (int nt = 0; nt < CF::NPW; ++nt) {
       const int n = 16 * (ng * CF::NPW + nt) + li;
-      if (n < dv) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * rb + 4 * lg + r;
-          if (i < Lc) oh[(size_t)(c0 + i) * dv + n] = from_f32<T>(acc[nt][r] / dr[r]);
-        }
-      }
+      for (int r = 0; r < 4; ++r)
+        sm.Os[(16 * rb + 4 * lg + r) * CF::OLD + n] = from_f32<T>(acc[nt][r] * rden[r]);
     }
 
     // ---- carry the state across the chunk ----
-    state_update<CF>(Sacc, zreg, sm.Kt, sm.Vt, exp2f((float)Lc * log2g), wf, wn,
-                     li, lg);
+    state_update<CF>(Sacc, zreg, sm.Kt, sm.Vt, sm.pw[Lc], wf, wn, li, lg);
     __syncthreads();
     write_state_copy<CF>(sm.St, sm.zs, Sacc, zreg, wf, wn, li, lg);
+    // 16-byte row stores of the output tile
+    {
+      const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
+      const int col0 = vcb * CF::VEC;
+#pragma unroll
+      for (int r = 0; r < CF::RV; ++r) {
+        const int row = vrg * CF::RV + r;
+        if (row < Lc) {
+          const V val = *reinterpret_cast<const V *>(sm.Os + row * CF::OLD + col0);
+          T *dst = oh + (size_t)(c0 + row) * dv + col0;
+          if (p.vec_ok && col0 + CF::VEC <= dv) {
+            *reinterpret_cast<V *>(dst) = val;
+          } else {
+#pragma unroll
+            for (int e = 0; e < CF::VEC; ++e)
+              if (col0 + e < dv) dst[e] = val[e];
+          }
+        }
+      }
+    }
   }
 
   if (seg == p.nseg - 1) {
@@ -429,13 +473,16 @@ __global__ void __launch_bounds__(CF::NT) summary_kernel(PrefillParams p) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int d = p.d, dv = p.dv, N = p.N;
-  const float log2g = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
   const size_t rec = (size_t)d * dv + d;
   const T *kh = reinterpret_cast<const T *>(p.k) + (size_t)bh * N * d;
   const T *vh = reinterpret_cast<const T *>(p.v) + (size_t)bh * N * dv;
   const int t_begin = seg * p.seg_len;
   const int t_end = t_begin + p.seg_len;
   const int wf = wv % 4, wn = wv / 4;
+
+  ChunkRegs<CF> R;
+  prefetch<CF, false>(R, p, nullptr, kh, vh, t_begin, CF::C);
+  fill_powers<CF>(sm.pw, p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f);
 
   f32x4 Sacc[CF::TFW][CF::TNW];
   float zreg[CF::TFW];
@@ -445,11 +492,12 @@ __global__ void __launch_bounds__(CF::NT) summary_kernel(PrefillParams p) {
 #pragma unroll
     for (int b = 0; b < CF::TNW; ++b) Sacc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
-  const float gC = exp2f((float)CF::C * log2g);
+  __syncthreads();
+  const float gC = sm.pw[CF::C];
   for (int c0 = t_begin; c0 < t_end; c0 += CF::C) {
-    stage_chunk<CF, false>(nullptr, nullptr, sm.Kt, sm.Vt, p, nullptr, kh, vh,
-                           c0, CF::C, log2g);
+    commit<CF, false>(R, nullptr, nullptr, sm.Kt, sm.Vt, sm.pw, p, CF::C);
     __syncthreads();
+    if (c0 + CF::C < t_end) prefetch<CF, false>(R, p, nullptr, kh, vh, c0 + CF::C, CF::C);
     state_update<CF>(Sacc, zreg, sm.Kt, sm.Vt, gC, wf, wn, li, lg);
     __syncthreads();
   }
@@ -496,6 +544,7 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
 
 template <class CF>
 hipError_t run(const PrefillParams &p, hipStream_t s) {
+  static_assert(sizeof(SmemChunk<CF>) <= kLdsBytes, "LDS budget");
   if (p.nseg > 1) {
     prof_begin(s);
     hipLaunchKernelGGL(summary_kernel<CF>, dim3(p.nseg - 1, p.BH), dim3(CF::NT),
@@ -518,16 +567,39 @@ hipError_t run(const PrefillParams &p, hipStream_t s) {
   return e;
 }
 
-// Instantiations: bf16 uses 64-token chunks; fp32 at 128 x 128 uses 32-token
-// chunks so that its fp32 tiles fit in LDS.
+// Workgroups of chunk_kernel<CF> that fit on one CU (queried once).
+template <class CF>
+int resident_per_cu() {
+  static std::atomic<int> cached{0};
+  int v = cached.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<CF>, CF::NT, 0) !=
+          hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 1;
+  }
+  cached.store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Instantiations: bf16 uses 64-token chunks; fp32 uses 32-token chunks
+// (64 at d = dv = 64) so that its fp32 tiles fit in LDS.
 using B64x64 = Cfg<bf16, 64, 64, 64, 4>;
 using B64x128 = Cfg<bf16, 64, 128, 64, 8>;
 using B128x64 = Cfg<bf16, 128, 64, 64, 8>;
 using B128x128 = Cfg<bf16, 128, 128, 64, 8>;
 using F64x64 = Cfg<float, 64, 64, 64, 4>;
-using F64x128 = Cfg<float, 64, 128, 64, 4>;
-using F128x64 = Cfg<float, 128, 64, 64, 4>;
+using F64x128 = Cfg<float, 64, 128, 32, 4>;
+using F128x64 = Cfg<float, 128, 64, 32, 4>;
 using F128x128 = Cfg<float, 128, 128, 32, 4>;
+
+template <class CF>
+void fill_plan(LinearPlan &pl) {
+  pl.chunk = CF::C;
+  pl.threads = CF::NT;
+  pl.per_cu = resident_per_cu<CF>();
+}
 
 }  // namespace
 
@@ -535,14 +607,19 @@ LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io) {
   LinearPlan pl{};
   pl.dk = d <= 64 ? 64 : 128;
   pl.dv_pad = dv <= 64 ? 64 : 128;
-  const bool big = pl.dk == 128 && pl.dv_pad == 128;
-  pl.chunk = (!bf16_io && big) ? 32 : 64;
-  pl.threads = bf16_io ? ((pl.dk == 64 && pl.dv_pad == 64) ? 256 : 512) : 256;
+  if (bf16_io) {
+    if (pl.dk == 64) pl.dv_pad == 64 ? fill_plan<B64x64>(pl) : fill_plan<B64x128>(pl);
+    else pl.dv_pad == 64 ? fill_plan<B128x64>(pl) : fill_plan<B128x128>(pl);
+  } else {
+    if (pl.dk == 64) pl.dv_pad == 64 ? fill_plan<F64x64>(pl) : fill_plan<F64x128>(pl);
+    else pl.dv_pad == 64 ? fill_plan<F128x64>(pl) : fill_plan<F128x128>(pl);
+  }
   const long chunks = N > 0 ? ((long)N + pl.chunk - 1) / pl.chunk : 0;
   long nseg = 1;
   if (chunks > 1 && BH > 0) {
-    const long target = 2L * device_cu_count();  // workgroups per launch
-    nseg = (target + BH - 1) / BH;
+    // one launch fills every resident workgroup slot once
+    const long slots = (long)device_cu_count() * pl.per_cu;
+    nseg = (slots + BH / 2) / BH;
     if (nseg > chunks) nseg = chunks;
     if (nseg < 1) nseg = 1;
   }
