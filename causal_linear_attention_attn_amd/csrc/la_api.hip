@@ -102,6 +102,7 @@ void prof_end(const char *name, hipStream_t s) {
 namespace {
 
 constexpr int kMaxGridY = 65535;
+constexpr size_t kMaxHeadBytes = 0x7fff0000u;
 
 bool dims_ok(int d, int dv) {
   return d >= 1 && d <= LA_MAX_DIM && dv >= 1 && dv <= LA_MAX_DIM;
@@ -120,6 +121,10 @@ int check_prefill_shape(const la_prefill_args *a) {
   if (a->fmap != LA_FMAP_IDENTITY && a->fmap != LA_FMAP_ELU1) return LA_EINVAL;
   if (a->rule == LA_RULE_DELTA && a->fmap != LA_FMAP_IDENTITY) return LA_EINVAL;
   if ((long long)a->B * a->H > kMaxGridY) return LA_EUNSUPPORTED;
+  // one head's q/k/v/o must be addressable with 32-bit byte offsets
+  const size_t esz = a->dtype == LA_BF16 ? 2 : 4;
+  const size_t dmax = a->d > a->dv ? a->d : a->dv;
+  if ((size_t)a->N * dmax * esz > kMaxHeadBytes) return LA_EUNSUPPORTED;
   return LA_OK;
 }
 

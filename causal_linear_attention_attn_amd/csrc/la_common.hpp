@@ -132,6 +132,54 @@ __device__ __forceinline__ void lds_store_n(T *p, const float (&x)[R]) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Buffer-resource loads and stores.  A raw buffer access whose byte offset
+// lies at or past the resource's size returns zeros (loads) or is dropped
+// (stores) in hardware, so bounds checks become offset selects instead of
+// branches: no divergent control flow sits between a load and its use, and
+// the compiler can keep every prefetched load in flight across the compute.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kOOB = 0x7ffffff0u;  // an offset past any resource used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base,
+                                                           uint32_t bytes) {
+  // dword 3 = 0x00020000: 32-bit data format, the gfx9-family raw-buffer setting
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Vec16<T>::type buf_load16(
+    __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return __builtin_bit_cast(typename Vec16<T>::type, x);
+}
+
+__device__ __forceinline__ float buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                           float *) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ bf16 buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                          bf16 *) {
+  return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+}
+
+template <typename T>
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                            typename Vec16<T>::type v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                           float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                           bf16 x) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, x), r, (int)off, 0, 0);
+}
+
 // Sum over the four slot groups (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float sum_groups(float x) {
   x += __shfl_xor(x, 16);

@@ -108,44 +108,68 @@ struct ChunkRegs {
   typename CF::vec q[CF::RQ], k[CF::RQ], v[CF::RV];
 };
 
-// One 16-byte vector of a row; zero outside the tensor.
+// Per-head buffer resources of q, k, v and o.  Every global access of the
+// prefill goes through them, with out-of-range lanes given an offset past
+// the resource (zero on load, dropped on store).
+struct HeadBufs {
+  __amdgpu_buffer_rsrc_t q, k, v, o;
+};
+
 template <typename T>
-__device__ __forceinline__ typename Vec16<T>::type load16(const T *row, int col0,
-                                                          int ncols, bool row_ok,
-                                                          bool vec_ok) {
-  using V = typename Vec16<T>::type;
-  constexpr int VEC = 16 / (int)sizeof(T);
-  if (row_ok && vec_ok && col0 + VEC <= ncols)
-    return *reinterpret_cast<const V *>(row + col0);
-  V r;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e)
-    r[e] = (row_ok && col0 + e < ncols) ? row[col0 + e] : from_f32<T>(0.f);
-  return r;
+__device__ __forceinline__ HeadBufs head_bufs(const PrefillParams &p, int bh) {
+  const size_t qk = (size_t)p.N * p.d, vo = (size_t)p.N * p.dv;
+  HeadBufs hb;
+  hb.q = buf_rsrc(reinterpret_cast<const T *>(p.q) + (size_t)bh * qk,
+                  (uint32_t)(qk * sizeof(T)));
+  hb.k = buf_rsrc(reinterpret_cast<const T *>(p.k) + (size_t)bh * qk,
+                  (uint32_t)(qk * sizeof(T)));
+  hb.v = buf_rsrc(reinterpret_cast<const T *>(p.v) + (size_t)bh * vo,
+                  (uint32_t)(vo * sizeof(T)));
+  hb.o = buf_rsrc(reinterpret_cast<const T *>(p.o) + (size_t)bh * vo,
+                  (uint32_t)(vo * sizeof(T)));
+  return hb;
 }
 
-template <class CF, bool WITH_Q>
+// One 16-byte column block of row `tok` of a [N, ncols] tensor (zero where
+// the row or a column is outside it).  VK: ncols is a multiple of the vector
+// width, so a block is either wholly inside or wholly outside.
+template <typename T, bool VK>
+__device__ __forceinline__ typename Vec16<T>::type load_block(
+    __amdgpu_buffer_rsrc_t r, int tok, int col0, int ncols, bool row_ok) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  if constexpr (VK) {
+    const bool ok = row_ok && col0 < ncols;
+    return buf_load16<T>(r, ok ? (uint32_t)(((size_t)tok * ncols + col0) * sizeof(T))
+                               : kOOB);
+  } else {
+    typename Vec16<T>::type x;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const bool ok = row_ok && col0 + e < ncols;
+      x[e] = buf_load1(r, ok ? (uint32_t)(((size_t)tok * ncols + col0 + e) * sizeof(T))
+                             : kOOB, (T *)nullptr);
+    }
+    return x;
+  }
+}
+
+template <class CF, bool WITH_Q, bool VK>
 __device__ __forceinline__ void prefetch(ChunkRegs<CF> &R, const PrefillParams &p,
-                                         const typename CF::type *qh,
-                                         const typename CF::type *kh,
-                                         const typename CF::type *vh, int c0,
-                                         int Lc) {
-  const bool vec_ok = p.vec_ok != 0;
+                                         const HeadBufs &hb, int c0, int Lc) {
+  using T = typename CF::type;
   const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
 #pragma unroll
   for (int r = 0; r < CF::RQ; ++r) {
     const int row = qrg * CF::RQ + r;
-    const bool ok = row < Lc;
-    const size_t off = (size_t)(c0 + row) * p.d;
-    if constexpr (WITH_Q) R.q[r] = load16(qh + off, qcb * CF::VEC, p.d, ok, vec_ok);
-    R.k[r] = load16(kh + off, qcb * CF::VEC, p.d, ok, vec_ok);
+    if constexpr (WITH_Q)
+      R.q[r] = load_block<T, VK>(hb.q, c0 + row, qcb * CF::VEC, p.d, row < Lc);
+    R.k[r] = load_block<T, VK>(hb.k, c0 + row, qcb * CF::VEC, p.d, row < Lc);
   }
   const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
 #pragma unroll
   for (int r = 0; r < CF::RV; ++r) {
     const int row = vrg * CF::RV + r;
-    R.v[r] = load16(vh + (size_t)(c0 + row) * p.dv, vcb * CF::VEC, p.dv,
-                    row < Lc, vec_ok);
+    R.v[r] = load_block<T, VK>(hb.v, c0 + row, vcb * CF::VEC, p.dv, row < Lc);
   }
 }
 
@@ -260,7 +284,7 @@ __device__ __forceinline__ void fill_powers(float *pw, float log2g) {
   for (int m = threadIdx.x; m <= CF::C; m += CF::NT) pw[m] = exp2f((float)m * log2g);
 }
 
-template <class CF>
+template <class CF, bool VK>
 __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
   using T = typename CF::type;
   using V = typename CF::vec;
@@ -271,16 +295,9 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
   const int li = lane & 15, lg = lane >> 4;
   const int d = p.d, dv = p.dv, N = p.N;
   const size_t rec = (size_t)d * dv + d;
-  const T *qh = reinterpret_cast<const T *>(p.q) + (size_t)bh * N * d;
-  const T *kh = reinterpret_cast<const T *>(p.k) + (size_t)bh * N * d;
-  const T *vh = reinterpret_cast<const T *>(p.v) + (size_t)bh * N * dv;
-  T *oh = reinterpret_cast<T *>(p.o) + (size_t)bh * N * dv;
+  const HeadBufs hb = head_bufs<T>(p, bh);
   const int t_begin = seg * p.seg_len;
   const int t_end = min(N, t_begin + p.seg_len);
-
-  ChunkRegs<CF> R;
-  prefetch<CF, true>(R, p, qh, kh, vh, t_begin, min(CF::C, N - t_begin));
-  fill_powers<CF>(sm.pw, p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f);
 
   const float *S0, *z0;
   if (p.nseg > 1) {
@@ -312,6 +329,11 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
     const int fz = 16 * tf + li;
     zreg[a] = (z0 && fz < d) ? z0[fz] : 0.f;
   }
+  // the first chunk's loads go out after the state loads (loads complete in
+  // issue order, so waiting for the state does not wait for the chunk)
+  ChunkRegs<CF> R;
+  prefetch<CF, true, VK>(R, p, hb, t_begin, min(CF::C, N - t_begin));
+  fill_powers<CF>(sm.pw, p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f);
   write_state_copy<CF>(sm.St, sm.zs, Sacc, zreg, wf, wn, li, lg);
   __syncthreads();
 
@@ -320,7 +342,7 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
     commit<CF, true>(R, sm.Qs, sm.Ks, sm.Kt, sm.Vt, sm.pw, p, Lc);
     __syncthreads();
     if (c0 + CF::C < t_end)
-      prefetch<CF, true>(R, p, qh, kh, vh, c0 + CF::C, min(CF::C, N - c0 - CF::C));
+      prefetch<CF, true, VK>(R, p, hb, c0 + CF::C, min(CF::C, N - c0 - CF::C));
 
     // ---- state read: gamma^(i+1) phi(q_i)^T S-, and phi(q_i) . z- ----
     Frag<T> qf[CF::KSD];
@@ -423,15 +445,16 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
 #pragma unroll
       for (int r = 0; r < CF::RV; ++r) {
         const int row = vrg * CF::RV + r;
-        if (row < Lc) {
-          const V val = *reinterpret_cast<const V *>(sm.Os + row * CF::OLD + col0);
-          T *dst = oh + (size_t)(c0 + row) * dv + col0;
-          if (p.vec_ok && col0 + CF::VEC <= dv) {
-            *reinterpret_cast<V *>(dst) = val;
-          } else {
+        const V val = *reinterpret_cast<const V *>(sm.Os + row * CF::OLD + col0);
+        const size_t el = (size_t)(c0 + row) * dv + col0;
+        if constexpr (VK) {
+          const bool ok = row < Lc && col0 < dv;
+          buf_store16<T>(hb.o, ok ? (uint32_t)(el * sizeof(T)) : kOOB, val);
+        } else {
 #pragma unroll
-            for (int e = 0; e < CF::VEC; ++e)
-              if (col0 + e < dv) dst[e] = val[e];
+          for (int e = 0; e < CF::VEC; ++e) {
+            const bool ok = row < Lc && col0 + e < dv;
+            buf_store1(hb.o, ok ? (uint32_t)((el + e) * sizeof(T)) : kOOB, val[e]);
           }
         }
       }
@@ -465,7 +488,7 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
 
 // Phase 1: each segment's own contribution, from a zero state (all but the
 // last segment; those are whole multiples of the chunk length).
-template <class CF>
+template <class CF, bool VK>
 __global__ void __launch_bounds__(CF::NT) summary_kernel(PrefillParams p) {
   using T = typename CF::type;
   __shared__ SmemSummary<CF> sm;
@@ -474,14 +497,13 @@ __global__ void __launch_bounds__(CF::NT) summary_kernel(PrefillParams p) {
   const int li = lane & 15, lg = lane >> 4;
   const int d = p.d, dv = p.dv, N = p.N;
   const size_t rec = (size_t)d * dv + d;
-  const T *kh = reinterpret_cast<const T *>(p.k) + (size_t)bh * N * d;
-  const T *vh = reinterpret_cast<const T *>(p.v) + (size_t)bh * N * dv;
+  const HeadBufs hb = head_bufs<T>(p, bh);
   const int t_begin = seg * p.seg_len;
   const int t_end = t_begin + p.seg_len;
   const int wf = wv % 4, wn = wv / 4;
 
   ChunkRegs<CF> R;
-  prefetch<CF, false>(R, p, nullptr, kh, vh, t_begin, CF::C);
+  prefetch<CF, false, VK>(R, p, hb, t_begin, CF::C);
   fill_powers<CF>(sm.pw, p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f);
 
   f32x4 Sacc[CF::TFW][CF::TNW];
@@ -497,7 +519,7 @@ __global__ void __launch_bounds__(CF::NT) summary_kernel(PrefillParams p) {
   for (int c0 = t_begin; c0 < t_end; c0 += CF::C) {
     commit<CF, false>(R, nullptr, nullptr, sm.Kt, sm.Vt, sm.pw, p, CF::C);
     __syncthreads();
-    if (c0 + CF::C < t_end) prefetch<CF, false>(R, p, nullptr, kh, vh, c0 + CF::C, CF::C);
+    if (c0 + CF::C < t_end) prefetch<CF, false, VK>(R, p, hb, c0 + CF::C, CF::C);
     state_update<CF>(Sacc, zreg, sm.Kt, sm.Vt, gC, wf, wn, li, lg);
     __syncthreads();
   }
@@ -542,12 +564,12 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
   }
 }
 
-template <class CF>
-hipError_t run(const PrefillParams &p, hipStream_t s) {
+template <class CF, bool VK>
+hipError_t run_vk(const PrefillParams &p, hipStream_t s) {
   static_assert(sizeof(SmemChunk<CF>) <= kLdsBytes, "LDS budget");
   if (p.nseg > 1) {
     prof_begin(s);
-    hipLaunchKernelGGL(summary_kernel<CF>, dim3(p.nseg - 1, p.BH), dim3(CF::NT),
+    hipLaunchKernelGGL((summary_kernel<CF, VK>), dim3(p.nseg - 1, p.BH), dim3(CF::NT),
                        0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -561,10 +583,15 @@ hipError_t run(const PrefillParams &p, hipStream_t s) {
     prof_end("linear_scan", s);
   }
   prof_begin(s);
-  hipLaunchKernelGGL(chunk_kernel<CF>, dim3(p.nseg, p.BH), dim3(CF::NT), 0, s, p);
+  hipLaunchKernelGGL((chunk_kernel<CF, VK>), dim3(p.nseg, p.BH), dim3(CF::NT), 0, s, p);
   const hipError_t e = hipGetLastError();
   if (e == hipSuccess) prof_end("linear_chunk", s);
   return e;
+}
+
+template <class CF>
+hipError_t run(const PrefillParams &p, hipStream_t s) {
+  return p.vec_ok ? run_vk<CF, true>(p, s) : run_vk<CF, false>(p, s);
 }
 
 // Workgroups of chunk_kernel<CF> that fit on one CU (queried once).
@@ -574,7 +601,7 @@ int resident_per_cu() {
   int v = cached.load(std::memory_order_relaxed);
   if (v > 0) return v;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<CF>, CF::NT, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<CF, true>, CF::NT, 0) !=
           hipSuccess || n < 1) {
     (void)hipGetLastError();
     n = 1;
