@@ -151,7 +151,7 @@ size_t la_prefill_workspace_size(const la_prefill_args *a) {
   if (BH == 0 || a->N == 0) return 0;
   if (a->rule == LA_RULE_LINEAR)
     return la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16).ws_bytes;
-  return 0;
+  return la::delta_workspace_bytes(BH, a->N, a->dtype == LA_BF16);
 }
 
 int la_prefill(const la_prefill_args *a, void *stream) {
@@ -180,11 +180,18 @@ int la_prefill(const la_prefill_args *a, void *stream) {
                   : la::launch_fill(a->z_out, nz, 0.f, s);
     return to_status(e);
   }
-  if (!linear) return LA_EUNSUPPORTED;
-
   const bool bf16_io = a->dtype == LA_BF16;
-  const la::LinearPlan plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io);
-  if (plan.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < plan.ws_bytes))
+  la::LinearPlan plan{};
+  size_t ws_need;
+  if (linear) {
+    plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io);
+    ws_need = plan.ws_bytes;
+  } else {
+    ws_need = la::delta_workspace_bytes(BH, a->N, bf16_io);
+    // one head's T and R tiles must be addressable with 32-bit byte offsets
+    if (ws_need / (size_t)BH > kMaxHeadBytes) return LA_EUNSUPPORTED;
+  }
+  if (ws_need > 0 && (!a->workspace || a->workspace_bytes < ws_need))
     return LA_EWORKSPACE;
 
   la::PrefillParams p{};
@@ -209,6 +216,7 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   p.z_out = a->z_out;
   p.o = a->o;
   p.ws = reinterpret_cast<float *>(a->workspace);
+  if (!linear) return to_status(la::launch_delta_prefill(p, bf16_io, s));
   p.nseg = plan.nseg;
   p.seg_len = plan.seg_len;
   return to_status(la::launch_linear_prefill(p, plan, bf16_io, s));
