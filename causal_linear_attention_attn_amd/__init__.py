@@ -68,9 +68,11 @@ def _prefill_args(q, k, v, rule, fmap, gamma, g, eps):
     return a
 
 
-def workspace_size(q, k, v, *, rule="linear", fmap="elu1", gamma=None, g=None,
+def workspace_size(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None,
                    eps=1e-6):
     """Workspace bytes la_prefill needs for these tensors (current device)."""
+    if fmap is None:
+        fmap = "elu1" if rule == "linear" else "identity"
     a = _prefill_args(q, k, v, rule, fmap, gamma, g, eps)
     n = _lib.load().la_prefill_workspace_size(ctypes.byref(a))
     if n == ctypes.c_size_t(-1).value:

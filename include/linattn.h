@@ -50,7 +50,7 @@ typedef enum {
   LA_EINVAL = 1,       /* a NULL pointer where one is required, a negative
                           size, d or dv outside 1..128, eps < 0 or not finite,
                           or an argument the rule does not take */
-  LA_EUNSUPPORTED = 2, /* valid request this build does not implement */
+  LA_EUNSUPPORTED = 2, /* valid request the library does not implement */
   LA_EHIP = 3,         /* a HIP call or kernel launch failed */
   LA_EWORKSPACE = 4    /* workspace NULL or smaller than
                           la_prefill_workspace_size() */

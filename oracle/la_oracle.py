@@ -23,7 +23,7 @@ Sources (cited by page title and section):
   [TAR]   "Transformers Are RNNs" (myhz0606.com): epsilon in the
           denominator, multiplicative causal mask.
 
-Readings where the pages disagree (each is listed in the design doc):
+Readings where the pages disagree:
   * The state is read AFTER the current token is written (token attends to
     itself), as [WILA] section 4 and [EAV] section 5 state.
   * eps is added to the denominator: o = phi(q).S / (phi(q).z + eps).
