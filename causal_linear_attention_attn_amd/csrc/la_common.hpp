@@ -86,6 +86,42 @@ __device__ __forceinline__ void frag_set(Frag<T> &f, int e, float x) {
   f.v[e] = from_f32<T>(x);
 }
 
+// Transposed fragment from a row-major LDS tile M (rows = the contraction
+// index, e.g. tokens; columns = the operand's row/column index).  Lane
+// (li, lg) receives column c0 + li; its slots 0..3 hold rows t_lo..t_lo+3 and
+// slots 4..7 rows t_hi..t_hi+3 (t_lo, t_hi may differ between slot groups).
+// bf16: two gfx950 LDS transpose reads (ds_read_b64_tr_b16): in each group
+// of 16 lanes, lane li names row t + li/4, columns c0 + 4 (li%4) .. +3, and
+// receives column c0 + li of the four rows.  fp32: eight strided reads.
+__device__ __forceinline__ void lds_frag_tr(Frag<bf16> &f, const bf16 *M, int ld,
+                                            int t_lo, int t_hi, int c0, int li) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lbf16x4;
+  typedef __attribute__((address_space(3))) lbf16x4 lds_bf16x4;
+  const int off = (li >> 2) * ld + c0 + 4 * (li & 3);
+  const lbf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4 *)(M + t_lo * ld + off));
+  const lbf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4 *)(M + t_hi * ld + off));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = a[e];
+    f.v[4 + e] = b[e];
+  }
+}
+__device__ __forceinline__ void lds_frag_tr(Frag<float> &f, const float *M, int ld,
+                                            int t_lo, int t_hi, int c0, int li) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = M[(t_lo + e) * ld + c0 + li];
+    f.v[4 + e] = M[(t_hi + e) * ld + c0 + li];
+  }
+}
+template <typename T>
+__device__ __forceinline__ void frag_fill(Frag<T> &f, float x) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = from_f32<T>(x);
+}
+
 // Four consecutive T to LDS.
 __device__ __forceinline__ void lds_store4(bf16 *p, float a, float b, float c,
                                            float d) {

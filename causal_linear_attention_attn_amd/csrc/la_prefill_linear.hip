@@ -5,43 +5,52 @@
 //     S_t = gamma S_{t-1} + phi(k_t) v_t^T,  z_t = gamma z_{t-1} + phi(k_t)
 //     o_t = phi(q_t)^T S_t / (phi(q_t) . z_t + eps)
 // evaluated chunk by chunk (the pages' chunkwise form: parallel inside a
-// chunk, state passed between chunks).  For a chunk of C tokens starting
-// from state (S-, z-), with Phi_q, Phi_k the chunk's features and chunk-local
-// indices i, j:
-//     A      = (Phi_q Phi_k^T) (.) D,  D_ij = gamma^(i-j) [j <= i]
-//     num_i  = gamma^(i+1) phi(q_i)^T S-  +  (A V)_i
-//     den_i  = gamma^(i+1) phi(q_i) . z-  +  (A 1)_i  +  eps
-//     S+     = gamma^C S-  +  Phi_k^T diag(w) V,  w_j = gamma^(C-1-j)
-//     z+     = gamma^C z-  +  Phi_k^T w
-// which is the recurrence unrolled over the chunk.
+// chunk, state passed between chunks).  For a chunk of L tokens entering with
+// state (S-, z-), chunk-local indices i, j, unrolling the recurrence gives
+//     num_i = gamma^(i+1) phi(q_i) S-  +  sum_{j<=i} gamma^(i-j) (phi(q_i).phi(k_j)) v_j
+//     den_i = gamma^(i+1) phi(q_i).z- +  sum_{j<=i} gamma^(i-j) (phi(q_i).phi(k_j))  + eps
+//     S+    = gamma^L S- + sum_j gamma^(L-1-j) phi(k_j) v_j^T   (z+ likewise)
+// With the weighted keys kw_j = gamma^(L-1-j) phi(k_j) the decay factor
+// gamma^(i-j) = gamma^(i+1-L) gamma^(L-1-j) splits into a row factor and the
+// key weight, and multiplying num_i and den_i by gamma^(L-1-i) leaves
+//     num'_i = phi(q_i) (gamma^L S-)  +  sum_{j<=i} (phi(q_i).kw_j) v_j
+//     den'_i = phi(q_i).(gamma^L z-)  +  sum_{j<=i} (phi(q_i).kw_j)  +  eps gamma^(L-1-i)
+//     S+     = gamma^L S- + KW^T V,   z+ = gamma^L z- + KW^T 1
+// so no decay factor is applied per score, and every factor is at most 1.
+// The weights underflow for gamma^(L-1) below the fp32 range, so gamma must
+// be at least 1/2 (documented in linattn.h).
+//
+// The normaliser rides along as one more 16-column tile of the value side:
+// the state is kept as [S | z z ... z] (z replicated over 16 columns) and V
+// is extended by a tile of ones, so one matrix product gives numerator and
+// denominator together.  Outputs are computed transposed (O^T = S'^T Phi_q^T
+// + V'^T A^T), which gives each lane four consecutive output columns of one
+// token and the denominator of that same token.
+//
+// LDS tiles are all row-major: Phi_q, KW and V rows as loaded (16-byte
+// stores), the scaled state copy S'^T (value columns + normaliser rows by
+// features), and an output staging tile.  Token contractions (A V and
+// KW^T V) read transposed fragments with the gfx950 LDS transpose load, so no
+// tile is ever written transposed.  Scores are computed transposed (KW as the
+// A operand, Phi_q as B), which leaves in each lane one query row and four
+// consecutive keys: two such tiles form the A^T operand of the next product
+// straight from registers.  The fp32 state lives in matrix-core accumulators
+// and is never rounded; the scaled bf16 copy feeds the next chunk's read.
 //
 // Long sequences are split into segments processed in parallel (a two-level
-// scan, "Transformers Are RNNs": the recurrence is a prefix sum, so it can be
-// scanned in parallel):
-//   phase 1  summary_kernel  per (segment, head): the segment's own decayed
-//            contribution (dS, dz) -- the chunk update from a zero state;
-//   phase 2  scan_kernel     per head: prefix over segments,
-//            P_{s+1} = gamma^L P_s + dS_s, P_0 = (S_in, z_in);
-//   phase 3  chunk_kernel    per (segment, head): outputs from P_s, chunk by
-//            chunk; the last segment writes (S_out, z_out).
-// With one segment, phase 3 runs alone from (S_in, z_in).  The planner picks
-// the segment count so that one launch fills every workgroup slot once.
+// scan, "Transformers Are RNNs": the recurrence is a prefix sum):
+//   summary_kernel  per (segment, head): the segment's own contribution
+//                   (dS, dz), i.e. the state update from a zero state;
+//   scan_kernel     per head: P_0 = (S_in, z_in), P_s = gamma^Lseg P_(s-1)
+//                   + dS_(s-1), every record loaded before the chain;
+//   chunk_kernel    per (segment, head): outputs from P_s, chunk by chunk;
+//                   the last segment writes (S_out, z_out).
+// With one segment only chunk_kernel runs, from (S_in, z_in).
 //
 // Data layout: q, k [BH, N, d], v, o [BH, N, dv] (row-major, dtype T);
 // workspace slots [nseg][BH][d*dv + d] fp32 (state then normaliser).
-//
-// Per chunk, the kernel streams q, k, v once from HBM and writes o once.
-// Global loads are issued one chunk ahead into registers (the next chunk's
-// loads are in flight while the current chunk computes); each thread owns
-// whole 16-byte column blocks of a few consecutive rows, so every wave reads
-// contiguous row segments.  Tiles live in LDS: Phi_q and Phi_k row-major
-// (token rows), Phi_k^T scaled by w and V^T (feature rows: the token
-// contraction needs consecutive tokens per lane), a T-precision copy S^T of
-// the fp32 state for the state read, and an output tile that turns the
-// matrix-core output layout into 16-byte row stores.  The fp32 state itself
-// lives in matrix-core accumulators and is never rounded.  All contractions
-// run on the matrix cores (bf16 inputs: 16x16x32 bf16; fp32 inputs: 16x16x4
-// fp32).  Powers of gamma come from a per-head table gamma^m, m = 0..C.
+// Global traffic goes through buffer resources (bounds by offset, no
+// branches between a load and its use), issued one chunk ahead.
 #include <atomic>
 
 #include "la_common.hpp"
@@ -51,6 +60,7 @@ namespace la {
 namespace {
 
 constexpr int kLdsBytes = 160 * 1024;
+constexpr int kMaxSeg = 32;  // segments per sequence the scan unrolls over
 
 template <typename T, int DK_, int DV_, int C_, int NW_>
 struct Cfg {
@@ -59,23 +69,26 @@ struct Cfg {
   static constexpr int DK = DK_, DV = DV_, C = C_, NW = NW_;
   static constexpr int NT = NW * kWave;
   static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte vector
-  static constexpr int QLD = DK + VEC;  // row stride of Phi_q / Phi_k tiles
-  static constexpr int TLD = C + VEC;   // row stride of Phi_k^T / V^T tiles
-  static constexpr int SLD = DK + VEC;  // row stride of the S^T copy
-  static constexpr int OLD = DV + VEC;  // row stride of the output tile
-  static constexpr int NRB = C / 16;    // 16-row blocks of a chunk
-  static constexpr int NG = NW / NRB;   // waves sharing one row block
-  static constexpr int NPW = (DV / 16) / NG;  // output column tiles per wave
-  static constexpr int NWN = NW / 4;    // state tiles: wave groups along dv
-  static constexpr int TFW = (DK / 16) / 4;   // state row tiles per wave
-  static constexpr int TNW = (DV / 16) / NWN; // state column tiles per wave
+  static constexpr int QLD = DK + VEC;  // row stride: Qs, Ks, St
+  static constexpr int VLD = DV + VEC;  // row stride: Vs, Os
+  static constexpr int NRB = C / 16;    // 16-token row blocks of a chunk
+  static constexpr int NG = NW / NRB;   // waves per row block (output role)
+  static constexpr int NVT = DV / 16;   // value column tiles
+  static constexpr int NPW = NVT / NG;  // value tiles per wave (output role)
+  static constexpr int NCT = NVT + 1;   // state column tiles incl. the normaliser
+  static constexpr int NFT = DK / 16;   // state row tiles
+  static constexpr int FPW = NFT >= NW ? NFT / NW : 1;  // state row tiles per wave
+  static constexpr int NWC = NFT >= NW ? 1 : NW / NFT;  // state column groups
+  static constexpr int TPW = (NCT + NWC - 1) / NWC;     // state column tiles per wave
   static constexpr int KSD = DK / 32;   // k-steps over features
   static constexpr int KSC = C / 32;    // k-steps over tokens
-  static constexpr int QCB = DK / VEC;  // 16-byte column blocks per q/k row
+  static constexpr int QCB = DK / VEC;  // 16-byte blocks per q/k row
   static constexpr int VCB = DV / VEC;  // ... per v/o row
   static constexpr int RQ = C * DK / (VEC * NT);  // q/k rows per thread
   static constexpr int RV = C * DV / (VEC * NT);  // v/o rows per thread
-  static_assert(NG >= 1 && NPW >= 1 && TFW >= 1 && TNW >= 1, "bad tiling");
+  static constexpr int SROWS = DV + 16;           // rows of the S'^T copy
+  static_assert(NG >= 1 && NPW >= 1 && NPW * NG == NVT, "output tiling");
+  static_assert(FPW * NW == NFT || NWC * NFT == NW, "state tiling");
   static_assert(NRB % 2 == 0, "chunk must hold an even number of row blocks");
   static_assert(RQ >= 1 && RQ * VEC * NT == C * DK, "q/k rows per thread");
   static_assert(RV >= 1 && RV * VEC * NT == C * DV, "v/o rows per thread");
@@ -84,21 +97,19 @@ struct Cfg {
 template <class CF>
 struct alignas(16) SmemChunk {
   using T = typename CF::type;
-  T Qs[CF::C * CF::QLD];
-  T Ks[CF::C * CF::QLD];
-  T Kt[CF::DK * CF::TLD];
-  T Vt[CF::DV * CF::TLD];
-  T St[CF::DV * CF::SLD];
-  T Os[CF::C * CF::OLD];
-  float zs[CF::DK];
-  float pw[CF::C + 4];  // gamma^m, m = 0..C
+  T Qs[CF::C * CF::QLD];      // phi(q) rows
+  T Ks[CF::C * CF::QLD];      // weighted phi(k) rows
+  T Vs[CF::C * CF::VLD];      // v rows
+  T St[CF::SROWS * CF::QLD];  // gamma^L [S | z]^T for the next state read
+  T Os[CF::C * CF::VLD];      // output staging
+  float pw[CF::C + 4];        // gamma^m, m = 0..C
 };
 
 template <class CF>
 struct alignas(16) SmemSummary {
   using T = typename CF::type;
-  T Kt[CF::DK * CF::TLD];
-  T Vt[CF::DV * CF::TLD];
+  T Ks[CF::C * CF::QLD];
+  T Vs[CF::C * CF::VLD];
   float pw[CF::C + 4];
 };
 
@@ -108,9 +119,7 @@ struct ChunkRegs {
   typename CF::vec q[CF::RQ], k[CF::RQ], v[CF::RV];
 };
 
-// Per-head buffer resources of q, k, v and o.  Every global access of the
-// prefill goes through them, with out-of-range lanes given an offset past
-// the resource (zero on load, dropped on store).
+// Per-head buffer resources of q, k, v and o.
 struct HeadBufs {
   __amdgpu_buffer_rsrc_t q, k, v, o;
 };
@@ -173,109 +182,167 @@ __device__ __forceinline__ void prefetch(ChunkRegs<CF> &R, const PrefillParams &
   }
 }
 
-// Registers -> LDS tiles.  Feature-map padding rule: lanes outside the
-// tensor (tokens past N, features past d) are zero AFTER phi (phi(0) = 1
-// would be wrong).
+// Registers -> LDS: phi(q) rows, weighted phi(k) rows, v rows.  Keys past
+// the chunk get weight 0 and feature columns past d are zeroed (phi(0) = 1
+// would otherwise count them); queries need no mask (their padded features
+// meet zero keys and zero state rows).
 template <class CF, bool WITH_Q>
-__device__ __forceinline__ void commit(const ChunkRegs<CF> &R,
-                                       typename CF::type *Qs,
-                                       typename CF::type *Ks,
-                                       typename CF::type *Kt,
-                                       typename CF::type *Vt, const float *pw,
-                                       const PrefillParams &p, int Lc) {
+__device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type *Qs,
+                                       typename CF::type *Ks, typename CF::type *Vs,
+                                       const float *pw, const PrefillParams &p, int Lc) {
   using T = typename CF::type;
+  using V = typename CF::vec;
   constexpr int VEC = CF::VEC;
   const bool elu = p.fmap != 0;
+  const bool colmask = p.d < CF::DK;
   const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
   const int col0 = qcb * VEC;
-  float kw[VEC][CF::RQ];
 #pragma unroll
   for (int r = 0; r < CF::RQ; ++r) {
     const int row = qrg * CF::RQ + r;
-    const bool ok = row < Lc;
     float x[VEC];
     if constexpr (WITH_Q) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float xq = to_f32(R.q[r][e]);
-        x[e] = (ok && col0 + e < p.d) ? (elu ? phi_elu1(xq) : xq) : 0.f;
+        x[e] = elu ? phi_elu1(xq) : xq;
       }
       lds_store_n<T, VEC>(Qs + row * CF::QLD + col0, x);
     }
+    const float w = row < Lc ? pw[Lc - 1 - row] : 0.f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       const float xk = to_f32(R.k[r][e]);
-      x[e] = (ok && col0 + e < p.d) ? (elu ? phi_elu1(xk) : xk) : 0.f;
+      x[e] = (elu ? phi_elu1(xk) : xk) * w;
     }
-    if constexpr (WITH_Q) lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
-    const float w = ok ? pw[Lc - 1 - row] : 0.f;
+    if (colmask) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) kw[e][r] = x[e] * w;
+      for (int e = 0; e < VEC; ++e) x[e] = col0 + e < p.d ? x[e] : 0.f;
+    }
+    lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
   }
-#pragma unroll
-  for (int e = 0; e < VEC; ++e)
-    lds_store_n<T, CF::RQ>(Kt + (col0 + e) * CF::TLD + qrg * CF::RQ, kw[e]);
-
   const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
-  float vt[VEC][CF::RV];
 #pragma unroll
-  for (int r = 0; r < CF::RV; ++r)
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) vt[e][r] = to_f32(R.v[r][e]);
-#pragma unroll
-  for (int e = 0; e < VEC; ++e)
-    lds_store_n<T, CF::RV>(Vt + (vcb * VEC + e) * CF::TLD + vrg * CF::RV, vt[e]);
-}
-
-// S <- gamma^Lc S + Phi_k^T diag(w) V and z <- gamma^Lc z + Phi_k^T w for the
-// state tiles this wave owns (Kt already carries the weights w).
-template <class CF>
-__device__ __forceinline__ void state_update(
-    f32x4 (&Sacc)[CF::TFW][CF::TNW], float (&zreg)[CF::TFW],
-    const typename CF::type *Kt, const typename CF::type *Vt, float gC, int wf,
-    int wn, int li, int lg) {
-  using T = typename CF::type;
-#pragma unroll
-  for (int a = 0; a < CF::TFW; ++a) {
-    const int tf = wf * CF::TFW + a;
-#pragma unroll
-    for (int b = 0; b < CF::TNW; ++b) Sacc[a][b] *= gC;
-    float zsum = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < CF::KSC; ++ks) {
-      Frag<T> kf;
-      lds_frag(kf, Kt + (16 * tf + li) * CF::TLD + 32 * ks + 8 * lg);
-      if (wn == 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zsum += frag_elem(kf, e);
-      }
-#pragma unroll
-      for (int b = 0; b < CF::TNW; ++b) {
-        const int tn = wn * CF::TNW + b;
-        Frag<T> vf;
-        lds_frag(vf, Vt + (16 * tn + li) * CF::TLD + 32 * ks + 8 * lg);
-        mma(Sacc[a][b], kf, vf);
-      }
-    }
-    if (wn == 0) zreg[a] = fmaf(gC, zreg[a], sum_groups(zsum));
+  for (int r = 0; r < CF::RV; ++r) {
+    const int row = vrg * CF::RV + r;
+    *reinterpret_cast<V *>(Vs + row * CF::VLD + vcb * VEC) = R.v[r];
   }
 }
 
-// T-precision copy of the state for the next chunk's read: St[n][f] = S[f][n].
+// State-tile ownership: row tiles tf = srow(w, a), column tiles tn = scol(w, b).
 template <class CF>
-__device__ __forceinline__ void write_state_copy(
-    typename CF::type *St, float *zs, const f32x4 (&Sacc)[CF::TFW][CF::TNW],
-    const float (&zreg)[CF::TFW], int wf, int wn, int li, int lg) {
+__device__ __forceinline__ int srow(int wv, int a) {
+  return CF::NFT >= CF::NW ? wv * CF::FPW + a : wv % CF::NFT;
+}
+template <class CF>
+__device__ __forceinline__ int scol(int wv, int b) {
+  return CF::NFT >= CF::NW ? b : wv / CF::NFT + CF::NWC * b;
+}
+
+// [S | z] <- gamma^L [S | z] + KW^T [V | 1] for this wave's tiles.
+template <class CF>
+__device__ __forceinline__ void state_update(f32x4 (&Sacc)[CF::FPW][CF::TPW],
+                                             const typename CF::type *Ks,
+                                             const typename CF::type *Vs, float gL,
+                                             bool decay, int wv, int li, int lg) {
+  using T = typename CF::type;
+  if (decay) {
 #pragma unroll
-  for (int a = 0; a < CF::TFW; ++a) {
-    const int tf = wf * CF::TFW + a;
+    for (int a = 0; a < CF::FPW; ++a)
 #pragma unroll
-    for (int b = 0; b < CF::TNW; ++b) {
-      const int tn = wn * CF::TNW + b;
-      lds_store4(St + (16 * tn + li) * CF::SLD + 16 * tf + 4 * lg, Sacc[a][b][0],
-                 Sacc[a][b][1], Sacc[a][b][2], Sacc[a][b][3]);
+      for (int b = 0; b < CF::TPW; ++b) Sacc[a][b] *= gL;
+  }
+  Frag<T> ones;
+  frag_fill(ones, 1.f);
+#pragma unroll
+  for (int ks = 0; ks < CF::KSC; ++ks) {
+    const int t0 = 32 * ks + 8 * lg;
+#pragma unroll
+    for (int a = 0; a < CF::FPW; ++a) {
+      Frag<T> kf;
+      lds_frag_tr(kf, Ks, CF::QLD, t0, t0 + 4, 16 * srow<CF>(wv, a), li);
+#pragma unroll
+      for (int b = 0; b < CF::TPW; ++b) {
+        const int tn = scol<CF>(wv, b);
+        if (tn < CF::NVT) {
+          Frag<T> vf;
+          lds_frag_tr(vf, Vs, CF::VLD, t0, t0 + 4, 16 * tn, li);
+          mma(Sacc[a][b], kf, vf);
+        } else if (tn == CF::NVT) {
+          mma(Sacc[a][b], kf, ones);
+        }
+      }
     }
-    if (wn == 0 && lg == 0) zs[16 * tf + li] = zreg[a];
+  }
+}
+
+// T-precision copy of scale * [S | z], transposed: St[n][f] = S[f][n].
+template <class CF>
+__device__ __forceinline__ void write_state_copy(typename CF::type *St,
+                                                 const f32x4 (&Sacc)[CF::FPW][CF::TPW],
+                                                 float scale, int wv, int li, int lg) {
+#pragma unroll
+  for (int a = 0; a < CF::FPW; ++a) {
+    const int tf = srow<CF>(wv, a);
+#pragma unroll
+    for (int b = 0; b < CF::TPW; ++b) {
+      const int tn = scol<CF>(wv, b);
+      if (tn < CF::NCT)
+        lds_store4(St + (16 * tn + li) * CF::QLD + 16 * tf + 4 * lg, scale * Sacc[a][b][0],
+                   scale * Sacc[a][b][1], scale * Sacc[a][b][2], scale * Sacc[a][b][3]);
+    }
+  }
+}
+
+// Load this wave's [S | z] tiles from an fp32 state (rows f < d, columns
+// n < dv; the normaliser tile repeats z in every column).
+template <class CF>
+__device__ __forceinline__ void load_state(f32x4 (&Sacc)[CF::FPW][CF::TPW], const float *S0,
+                                           const float *z0, int d, int dv, int wv, int li,
+                                           int lg) {
+#pragma unroll
+  for (int a = 0; a < CF::FPW; ++a) {
+    const int tf = srow<CF>(wv, a);
+#pragma unroll
+    for (int b = 0; b < CF::TPW; ++b) {
+      const int tn = scol<CF>(wv, b);
+      const int n = 16 * tn + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int f = 16 * tf + 4 * lg + r;
+        float x = 0.f;
+        if (tn < CF::NVT) {
+          if (S0 && f < d && n < dv) x = S0[(size_t)f * dv + n];
+        } else if (tn == CF::NVT) {
+          if (z0 && f < d) x = z0[f];
+        }
+        Sacc[a][b][r] = x;
+      }
+    }
+  }
+}
+
+// Store this wave's [S | z] tiles to an fp32 state.
+template <class CF>
+__device__ __forceinline__ void store_state(const f32x4 (&Sacc)[CF::FPW][CF::TPW], float *S1,
+                                            float *z1, int d, int dv, int wv, int li, int lg) {
+#pragma unroll
+  for (int a = 0; a < CF::FPW; ++a) {
+    const int tf = srow<CF>(wv, a);
+#pragma unroll
+    for (int b = 0; b < CF::TPW; ++b) {
+      const int tn = scol<CF>(wv, b);
+      const int n = 16 * tn + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int f = 16 * tf + 4 * lg + r;
+        if (tn < CF::NVT) {
+          if (S1 && f < d && n < dv) S1[(size_t)f * dv + n] = Sacc[a][b][r];
+        } else if (tn == CF::NVT) {
+          if (z1 && li == 0 && f < d) z1[f] = Sacc[a][b][r];
+        }
+      }
+    }
   }
 }
 
@@ -291,93 +358,50 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
   __shared__ SmemChunk<CF> sm;
 
   const int seg = blockIdx.x, bh = blockIdx.y;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const int d = p.d, dv = p.dv, N = p.N;
-  const size_t rec = (size_t)d * dv + d;
   const HeadBufs hb = head_bufs<T>(p, bh);
   const int t_begin = seg * p.seg_len;
   const int t_end = min(N, t_begin + p.seg_len);
+  const bool decay = p.gamma != nullptr;
 
   const float *S0, *z0;
   if (p.nseg > 1) {
-    S0 = p.ws + ((size_t)seg * p.BH + bh) * rec;
+    S0 = p.ws + ((size_t)seg * p.BH + bh) * ((size_t)d * dv + d);
     z0 = S0 + (size_t)d * dv;
   } else {
     S0 = p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr;
     z0 = p.z_in ? p.z_in + (size_t)bh * d : nullptr;
   }
-
-  const int rb = wv % CF::NRB, ng = wv / CF::NRB;  // output role
-  const int wf = wv % 4, wn = wv / 4;              // state-tile role
-  const int irow = 16 * rb + li;  // chunk row this lane carries as an operand
-
-  f32x4 Sacc[CF::TFW][CF::TNW];
-  float zreg[CF::TFW];
-#pragma unroll
-  for (int a = 0; a < CF::TFW; ++a) {
-    const int tf = wf * CF::TFW + a;
-#pragma unroll
-    for (int b = 0; b < CF::TNW; ++b) {
-      const int n = 16 * (wn * CF::TNW + b) + li;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int f = 16 * tf + 4 * lg + r;
-        Sacc[a][b][r] = (S0 && f < d && n < dv) ? S0[(size_t)f * dv + n] : 0.f;
-      }
-    }
-    const int fz = 16 * tf + li;
-    zreg[a] = (z0 && fz < d) ? z0[fz] : 0.f;
-  }
+  f32x4 Sacc[CF::FPW][CF::TPW];
+  load_state<CF>(Sacc, S0, z0, d, dv, wv, li, lg);
   // the first chunk's loads go out after the state loads (loads complete in
   // issue order, so waiting for the state does not wait for the chunk)
   ChunkRegs<CF> R;
   prefetch<CF, true, VK>(R, p, hb, t_begin, min(CF::C, N - t_begin));
-  fill_powers<CF>(sm.pw, p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f);
-  write_state_copy<CF>(sm.St, sm.zs, Sacc, zreg, wf, wn, li, lg);
+  fill_powers<CF>(sm.pw, decay ? log2f(p.gamma[bh % p.H]) : 0.f);
   __syncthreads();
+  write_state_copy<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - t_begin)], wv, li, lg);
+
+  const int rb = wv % CF::NRB, cg = wv / CF::NRB;  // output role
+  const int irow = 16 * rb + li;                    // this lane's query row
 
   for (int c0 = t_begin; c0 < t_end; c0 += CF::C) {
     const int Lc = min(CF::C, N - c0);
-    commit<CF, true>(R, sm.Qs, sm.Ks, sm.Kt, sm.Vt, sm.pw, p, Lc);
-    __syncthreads();
+    commit<CF, true>(R, sm.Qs, sm.Ks, sm.Vs, sm.pw, p, Lc);
     if (c0 + CF::C < t_end)
       prefetch<CF, true, VK>(R, p, hb, c0 + CF::C, min(CF::C, N - c0 - CF::C));
+    __syncthreads();
 
-    // ---- state read: gamma^(i+1) phi(q_i)^T S-, and phi(q_i) . z- ----
+    // ---- scores, transposed: at[tj][r] = phi(q_i) . kw_j, i = irow,
+    //      j = 16 tj + 4 lg + r (lower triangle only) ----
     Frag<T> qf[CF::KSD];
-    float dz = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < CF::KSD; ++ks) {
+    for (int ks = 0; ks < CF::KSD; ++ks)
       lds_frag(qf[ks], sm.Qs + irow * CF::QLD + 32 * ks + 8 * lg);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        dz = fmaf(frag_elem(qf[ks], e), sm.zs[32 * ks + 8 * lg + e], dz);
-    }
-    f32x4 acc[CF::NPW];
-#pragma unroll
-    for (int nt = 0; nt < CF::NPW; ++nt) {
-      acc[nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      const int n = 16 * (ng * CF::NPW + nt) + li;
-#pragma unroll
-      for (int ks = 0; ks < CF::KSD; ++ks) {
-        Frag<T> sf;
-        lds_frag(sf, sm.St + n * CF::SLD + 32 * ks + 8 * lg);
-        mma(acc[nt], qf[ks], sf);
-      }
-    }
-    dz = sum_groups(dz) * sm.pw[irow + 1];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float sc = sm.pw[16 * rb + 4 * lg + r + 1];
-#pragma unroll
-      for (int nt = 0; nt < CF::NPW; ++nt) acc[nt][r] *= sc;
-    }
-
-    // ---- intra-chunk: A = (Phi_q Phi_k^T) (.) D, computed as A^T tiles ----
-    // at[tj][r] = A[i = 16 rb + li][j = 16 tj + 4 lg + r]
     f32x4 at[CF::NRB];
-    float dintra = 0.f;
 #pragma unroll
     for (int tj = 0; tj < CF::NRB; ++tj) {
       at[tj] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -388,56 +412,69 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
           lds_frag(kf, sm.Ks + (16 * tj + li) * CF::QLD + 32 * ks + 8 * lg);
           mma(at[tj], kf, qf[ks]);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lag = irow - (16 * tj + 4 * lg + r);
-          float x = lag >= 0 ? at[tj][r] * sm.pw[lag] : 0.f;
-          x = to_f32(from_f32<T>(x));  // the weight the product below uses
-          at[tj][r] = x;
-          dintra += x;
-        }
       }
     }
-    dintra = sum_groups(dintra);
-    // A V: two A^T tiles form one 32-token operand (slots e < 4 from tile
-    // 2pp, e >= 4 from tile 2pp+1), matched by the same tokens of V^T.
+#pragma unroll
+    for (int tj = 0; tj < CF::NRB; ++tj)
+      if (tj == rb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) at[tj][r] = 4 * lg + r <= li ? at[tj][r] : 0.f;
+      }
+
+    // ---- O'^T = (gamma^L [S | z])^T Phi_q^T + [V | 1]^T A^T ----
+    f32x4 acc[CF::NPW], accd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int a = 0; a < CF::NPW; ++a) acc[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < CF::KSD; ++ks) {
+#pragma unroll
+      for (int a = 0; a < CF::NPW; ++a) {
+        Frag<T> sf;
+        lds_frag(sf, sm.St + (16 * (cg * CF::NPW + a) + li) * CF::QLD + 32 * ks + 8 * lg);
+        mma(acc[a], sf, qf[ks]);
+      }
+      Frag<T> zf;
+      lds_frag(zf, sm.St + (CF::DV + li) * CF::QLD + 32 * ks + 8 * lg);
+      mma(accd, zf, qf[ks]);
+    }
+    Frag<T> ones;
+    frag_fill(ones, 1.f);
 #pragma unroll
     for (int pp = 0; pp < CF::NRB / 2; ++pp) {
       if (2 * pp <= rb) {
+        // slots 0..3: keys 32 pp + 4 lg + e; slots 4..7: 32 pp + 16 + 4 lg + e
         Frag<T> af;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           frag_set(af, e, at[2 * pp][e]);
           frag_set(af, 4 + e, at[2 * pp + 1][e]);
         }
+        const int tlo = 32 * pp + 4 * lg, thi = tlo + 16;
 #pragma unroll
-        for (int nt = 0; nt < CF::NPW; ++nt) {
-          const int n = 16 * (ng * CF::NPW + nt) + li;
+        for (int a = 0; a < CF::NPW; ++a) {
           Frag<T> vf;
-          lds_half(vf, sm.Vt + n * CF::TLD + 32 * pp + 4 * lg, 0);
-          lds_half(vf, sm.Vt + n * CF::TLD + 32 * pp + 16 + 4 * lg, 4);
-          mma(acc[nt], af, vf);
+          lds_frag_tr(vf, sm.Vs, CF::VLD, tlo, thi, 16 * (cg * CF::NPW + a), li);
+          mma(acc[a], vf, af);
         }
+        mma(accd, ones, af);
       }
     }
 
-    // ---- normalise into the output tile ----
-    const float den = dz + dintra + p.eps;  // for row irow
-    float rden[4];
+    // ---- normalise: lane holds columns 16 tn + 4 lg + r of token irow ----
+    {
+      const float den = accd[0] + p.eps * sm.pw[max(Lc - 1 - irow, 0)];
+      const float rd = 1.f / den;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rden[r] = 1.f / __shfl(den, 4 * lg + r);
-#pragma unroll
-    for (int nt = 0; nt < CF::NPW; ++nt) {
-      const int n = 16 * (ng * CF::NPW + nt) + li;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sm.Os[(16 * rb + 4 * lg + r) * CF::OLD + n] = from_f32<T>(acc[nt][r] * rden[r]);
+      for (int a = 0; a < CF::NPW; ++a)
+        lds_store4(sm.Os + irow * CF::VLD + 16 * (cg * CF::NPW + a) + 4 * lg,
+                   acc[a][0] * rd, acc[a][1] * rd, acc[a][2] * rd, acc[a][3] * rd);
     }
 
     // ---- carry the state across the chunk ----
-    state_update<CF>(Sacc, zreg, sm.Kt, sm.Vt, sm.pw[Lc], wf, wn, li, lg);
+    state_update<CF>(Sacc, sm.Ks, sm.Vs, sm.pw[Lc], decay, wv, li, lg);
     __syncthreads();
-    write_state_copy<CF>(sm.St, sm.zs, Sacc, zreg, wf, wn, li, lg);
+    if (c0 + CF::C < t_end)
+      write_state_copy<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - c0 - CF::C)], wv, li, lg);
     // 16-byte row stores of the output tile
     {
       const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
@@ -445,7 +482,7 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
 #pragma unroll
       for (int r = 0; r < CF::RV; ++r) {
         const int row = vrg * CF::RV + r;
-        const V val = *reinterpret_cast<const V *>(sm.Os + row * CF::OLD + col0);
+        const V val = *reinterpret_cast<const V *>(sm.Os + row * CF::VLD + col0);
         const size_t el = (size_t)(c0 + row) * dv + col0;
         if constexpr (VK) {
           const bool ok = row < Lc && col0 < dv;
@@ -461,29 +498,9 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
     }
   }
 
-  if (seg == p.nseg - 1) {
-    if (p.S_out) {
-      float *So = p.S_out + (size_t)bh * d * dv;
-#pragma unroll
-      for (int a = 0; a < CF::TFW; ++a)
-#pragma unroll
-        for (int b = 0; b < CF::TNW; ++b) {
-          const int n = 16 * (wn * CF::TNW + b) + li;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int f = 16 * (wf * CF::TFW + a) + 4 * lg + r;
-            if (f < d && n < dv) So[(size_t)f * dv + n] = Sacc[a][b][r];
-          }
-        }
-    }
-    if (p.z_out && wn == 0 && lg == 0) {
-#pragma unroll
-      for (int a = 0; a < CF::TFW; ++a) {
-        const int f = 16 * (wf * CF::TFW + a) + li;
-        if (f < d) p.z_out[(size_t)bh * d + f] = zreg[a];
-      }
-    }
-  }
+  if (seg == p.nseg - 1)
+    store_state<CF>(Sacc, p.S_out ? p.S_out + (size_t)bh * d * dv : nullptr,
+                    p.z_out ? p.z_out + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
 }
 
 // Phase 1: each segment's own contribution, from a zero state (all but the
@@ -493,55 +510,40 @@ __global__ void __launch_bounds__(CF::NT) summary_kernel(PrefillParams p) {
   using T = typename CF::type;
   __shared__ SmemSummary<CF> sm;
   const int seg = blockIdx.x, bh = blockIdx.y;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
-  const int d = p.d, dv = p.dv, N = p.N;
-  const size_t rec = (size_t)d * dv + d;
+  const int d = p.d, dv = p.dv;
   const HeadBufs hb = head_bufs<T>(p, bh);
   const int t_begin = seg * p.seg_len;
   const int t_end = t_begin + p.seg_len;
-  const int wf = wv % 4, wn = wv / 4;
+  const bool decay = p.gamma != nullptr;
 
   ChunkRegs<CF> R;
   prefetch<CF, false, VK>(R, p, hb, t_begin, CF::C);
-  fill_powers<CF>(sm.pw, p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f);
+  fill_powers<CF>(sm.pw, decay ? log2f(p.gamma[bh % p.H]) : 0.f);
 
-  f32x4 Sacc[CF::TFW][CF::TNW];
-  float zreg[CF::TFW];
+  f32x4 Sacc[CF::FPW][CF::TPW];
 #pragma unroll
-  for (int a = 0; a < CF::TFW; ++a) {
-    zreg[a] = 0.f;
+  for (int a = 0; a < CF::FPW; ++a)
 #pragma unroll
-    for (int b = 0; b < CF::TNW; ++b) Sacc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
+    for (int b = 0; b < CF::TPW; ++b) Sacc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   const float gC = sm.pw[CF::C];
   for (int c0 = t_begin; c0 < t_end; c0 += CF::C) {
-    commit<CF, false>(R, nullptr, nullptr, sm.Kt, sm.Vt, sm.pw, p, CF::C);
-    __syncthreads();
+    commit<CF, false>(R, nullptr, sm.Ks, sm.Vs, sm.pw, p, CF::C);
     if (c0 + CF::C < t_end) prefetch<CF, false, VK>(R, p, hb, c0 + CF::C, CF::C);
-    state_update<CF>(Sacc, zreg, sm.Kt, sm.Vt, gC, wf, wn, li, lg);
+    __syncthreads();
+    state_update<CF>(Sacc, sm.Ks, sm.Vs, gC, decay, wv, li, lg);
     __syncthreads();
   }
-  float *dst = p.ws + ((size_t)(seg + 1) * p.BH + bh) * rec;
-#pragma unroll
-  for (int a = 0; a < CF::TFW; ++a) {
-#pragma unroll
-    for (int b = 0; b < CF::TNW; ++b) {
-      const int n = 16 * (wn * CF::TNW + b) + li;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int f = 16 * (wf * CF::TFW + a) + 4 * lg + r;
-        if (f < d && n < dv) dst[(size_t)f * dv + n] = Sacc[a][b][r];
-      }
-    }
-    const int f = 16 * (wf * CF::TFW + a) + li;
-    if (wn == 0 && lg == 0 && f < d) dst[(size_t)d * dv + f] = zreg[a];
-  }
+  float *dst = p.ws + ((size_t)(seg + 1) * p.BH + bh) * ((size_t)d * dv + d);
+  store_state<CF>(Sacc, dst, dst + (size_t)d * dv, d, dv, wv, li, lg);
 }
 
 // Phase 2: prefix over segments, in place: slot 0 <- (S_in, z_in),
-// slot s <- gamma^L slot (s-1) + dS_(s-1) for s >= 1.
+// slot s <- gamma^L slot (s-1) + dS_(s-1) for s >= 1.  Every record is
+// loaded before the dependent chain starts.
 __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
   const int bh = blockIdx.y;
   const size_t rec = (size_t)p.d * p.dv + p.d;
@@ -550,17 +552,23 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
   const float log2g = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
   const float gL = exp2f((float)p.seg_len * log2g);
   const size_t dd = (size_t)p.d * p.dv;
+  float *base = p.ws + (size_t)bh * rec + e;
+  const size_t stride = (size_t)p.BH * rec;
+  float dS[kMaxSeg];
+#pragma unroll
+  for (int s = 1; s < kMaxSeg; ++s) dS[s] = s < p.nseg ? base[s * stride] : 0.f;
   float acc;
   if (e < dd)
     acc = p.S_in ? p.S_in[(size_t)bh * dd + e] : 0.f;
   else
     acc = p.z_in ? p.z_in[(size_t)bh * p.d + (e - dd)] : 0.f;
-  float *base = p.ws + (size_t)bh * rec + e;
-  const size_t stride = (size_t)p.BH * rec;
   base[0] = acc;
-  for (int s = 1; s < p.nseg; ++s) {
-    acc = fmaf(gL, acc, base[s * stride]);
-    base[s * stride] = acc;
+#pragma unroll
+  for (int s = 1; s < kMaxSeg; ++s) {
+    if (s < p.nseg) {
+      acc = fmaf(gL, acc, dS[s]);
+      base[s * stride] = acc;
+    }
   }
 }
 
@@ -611,15 +619,15 @@ int resident_per_cu() {
 }
 
 // Instantiations: bf16 uses 64-token chunks; fp32 uses 32-token chunks
-// (64 at d = dv = 64) so that its fp32 tiles fit in LDS.
+// beyond d = dv = 64 so that its fp32 tiles fit in LDS.
 using B64x64 = Cfg<bf16, 64, 64, 64, 4>;
 using B64x128 = Cfg<bf16, 64, 128, 64, 8>;
 using B128x64 = Cfg<bf16, 128, 64, 64, 8>;
 using B128x128 = Cfg<bf16, 128, 128, 64, 8>;
 using F64x64 = Cfg<float, 64, 64, 64, 4>;
-using F64x128 = Cfg<float, 64, 128, 32, 4>;
-using F128x64 = Cfg<float, 128, 64, 32, 4>;
-using F128x128 = Cfg<float, 128, 128, 32, 4>;
+using F64x128 = Cfg<float, 64, 128, 32, 8>;
+using F128x64 = Cfg<float, 128, 64, 32, 8>;
+using F128x128 = Cfg<float, 128, 128, 32, 8>;
 
 template <class CF>
 void fill_plan(LinearPlan &pl) {
@@ -648,6 +656,7 @@ LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io) {
     const long slots = (long)device_cu_count() * pl.per_cu;
     nseg = (slots + BH / 2) / BH;
     if (nseg > chunks) nseg = chunks;
+    if (nseg > kMaxSeg) nseg = kMaxSeg;
     if (nseg < 1) nseg = 1;
   }
   const long cps = chunks > 0 ? (chunks + nseg - 1) / nseg : 1;

@@ -83,9 +83,11 @@ typedef struct la_prefill_args {
   const void *q;     /* [B,H,N,d]  */
   const void *k;     /* [B,H,N,d]  */
   const void *v;     /* [B,H,N,dv] */
-  const float *gamma;/* LINEAR: [H] decay per head, each in (0,1]; NULL = 1.
+  const float *gamma;/* LINEAR: [H] decay per head, each in [1/2, 1]; NULL = 1.
                         DELTA: must be NULL.  Values are the caller's
-                        contract (not read on the host). */
+                        contract (not read on the host); the chunked prefill
+                        folds gamma^(chunk-1) into the key weights, which
+                        stays far inside the fp32 range on that interval. */
   const float *g;    /* DELTA: [B,H,N] write gate per token (required).
                         LINEAR: must be NULL. */
   float eps;         /* LINEAR: added to the denominator, >= 0. DELTA: ignored */
