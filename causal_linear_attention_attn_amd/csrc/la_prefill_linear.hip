@@ -39,16 +39,17 @@
 //
 // Long sequences are split into segments processed in parallel (a two-level
 // scan, "Transformers Are RNNs": the recurrence is a prefix sum):
-//   summary_kernel  per (segment, head): the segment's own contribution
-//                   (dS, dz), i.e. the state update from a zero state;
-//   scan_kernel     per head: P_0 = (S_in, z_in), P_s = gamma^Lseg P_(s-1)
-//                   + dS_(s-1), every record loaded before the chain;
-//   chunk_kernel    per (segment, head): outputs from P_s, chunk by chunk;
-//                   the last segment writes (S_out, z_out).
+//   summary_kernel  per (segment, head), all but the last segment: the
+//                   segment's own contribution (dS, dz), i.e. the state
+//                   update from a zero state;
+//   chunk_kernel    per (segment, head): the entering state
+//                   P_s = gamma^(Lseg s) P_0 + sum_{s'<s} gamma^(Lseg (s-1-s')) dS_s'
+//                   with P_0 = (S_in, z_in), then outputs chunk by chunk; the
+//                   last segment writes (S_out, z_out).
 // With one segment only chunk_kernel runs, from (S_in, z_in).
 //
 // Data layout: q, k [BH, N, d], v, o [BH, N, dv] (row-major, dtype T);
-// workspace slots [nseg][BH][d*dv + d] fp32 (state then normaliser).
+// workspace slots [nseg - 1][BH][d*dv + d] fp32 (state then normaliser).
 // Global traffic goes through buffer resources (bounds by offset, no
 // branches between a load and its use), issued one chunk ahead.
 #include <atomic>
@@ -60,7 +61,7 @@ namespace la {
 namespace {
 
 constexpr int kLdsBytes = 160 * 1024;
-constexpr int kMaxSeg = 32;  // segments per sequence the scan unrolls over
+constexpr int kMaxSeg = 32;  // most segments per sequence
 
 template <typename T, int DK_, int DV_, int C_, int NW_>
 struct Cfg {
@@ -87,6 +88,8 @@ struct Cfg {
   static constexpr int RQ = C * DK / (VEC * NT);  // q/k rows per thread
   static constexpr int RV = C * DV / (VEC * NT);  // v/o rows per thread
   static constexpr int SROWS = DV + 16;           // rows of the S'^T copy
+  // resident waves per SIMD the register allocation must allow
+  static constexpr int WPE = sizeof(T) == 4 ? 1 : (NW <= 4 ? 3 : 2);
   static_assert(NG >= 1 && NPW >= 1 && NPW * NG == NVT, "output tiling");
   static_assert(FPW * NW == NFT || NWC * NFT == NW, "state tiling");
   static_assert(NRB % 2 == 0, "chunk must hold an even number of row blocks");
@@ -195,6 +198,9 @@ __device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type
   constexpr int VEC = CF::VEC;
   const bool elu = p.fmap != 0;
   const bool colmask = p.d < CF::DK;
+  // key weights gamma^(Lc-1-j), 0 past the chunk: all 1 for a full chunk
+  // without decay
+  const bool weighted = p.gamma != nullptr || Lc < CF::C;
   const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
   const int col0 = qcb * VEC;
 #pragma unroll
@@ -209,11 +215,15 @@ __device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type
       }
       lds_store_n<T, VEC>(Qs + row * CF::QLD + col0, x);
     }
-    const float w = row < Lc ? pw[Lc - 1 - row] : 0.f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       const float xk = to_f32(R.k[r][e]);
-      x[e] = (elu ? phi_elu1(xk) : xk) * w;
+      x[e] = elu ? phi_elu1(xk) : xk;
+    }
+    if (weighted) {
+      const float w = row < Lc ? pw[Lc - 1 - row] : 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) x[e] *= w;
     }
     if (colmask) {
 #pragma unroll
@@ -280,16 +290,22 @@ __device__ __forceinline__ void state_update(f32x4 (&Sacc)[CF::FPW][CF::TPW],
 template <class CF>
 __device__ __forceinline__ void write_state_copy(typename CF::type *St,
                                                  const f32x4 (&Sacc)[CF::FPW][CF::TPW],
-                                                 float scale, int wv, int li, int lg) {
+                                                 float scale, bool decay, int wv, int li,
+                                                 int lg) {
 #pragma unroll
   for (int a = 0; a < CF::FPW; ++a) {
     const int tf = srow<CF>(wv, a);
 #pragma unroll
     for (int b = 0; b < CF::TPW; ++b) {
       const int tn = scol<CF>(wv, b);
-      if (tn < CF::NCT)
-        lds_store4(St + (16 * tn + li) * CF::QLD + 16 * tf + 4 * lg, scale * Sacc[a][b][0],
-                   scale * Sacc[a][b][1], scale * Sacc[a][b][2], scale * Sacc[a][b][3]);
+      if (tn < CF::NCT) {
+        typename CF::type *dst = St + (16 * tn + li) * CF::QLD + 16 * tf + 4 * lg;
+        if (decay)
+          lds_store4(dst, scale * Sacc[a][b][0], scale * Sacc[a][b][1],
+                     scale * Sacc[a][b][2], scale * Sacc[a][b][3]);
+        else
+          lds_store4(dst, Sacc[a][b][0], Sacc[a][b][1], Sacc[a][b][2], Sacc[a][b][3]);
+      }
     }
   }
 }
@@ -317,6 +333,33 @@ __device__ __forceinline__ void load_state(f32x4 (&Sacc)[CF::FPW][CF::TPW], cons
           if (z0 && f < d) x = z0[f];
         }
         Sacc[a][b][r] = x;
+      }
+    }
+  }
+}
+
+// Sacc <- scale * Sacc + record, for a [S | z] record in the state layout.
+template <class CF>
+__device__ __forceinline__ void add_state(f32x4 (&Sacc)[CF::FPW][CF::TPW], const float *rec,
+                                          float scale, int d, int dv, int wv, int li, int lg) {
+  const float *zr = rec + (size_t)d * dv;
+#pragma unroll
+  for (int a = 0; a < CF::FPW; ++a) {
+    const int tf = srow<CF>(wv, a);
+#pragma unroll
+    for (int b = 0; b < CF::TPW; ++b) {
+      const int tn = scol<CF>(wv, b);
+      const int n = 16 * tn + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int f = 16 * tf + 4 * lg + r;
+        float x = 0.f;
+        if (tn < CF::NVT) {
+          if (f < d && n < dv) x = rec[(size_t)f * dv + n];
+        } else if (tn == CF::NVT) {
+          if (f < d) x = zr[f];
+        }
+        Sacc[a][b][r] = fmaf(scale, Sacc[a][b][r], x);
       }
     }
   }
@@ -352,7 +395,7 @@ __device__ __forceinline__ void fill_powers(float *pw, float log2g) {
 }
 
 template <class CF, bool VK>
-__global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
+__global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p) {
   using T = typename CF::type;
   using V = typename CF::vec;
   __shared__ SmemChunk<CF> sm;
@@ -367,23 +410,28 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
   const int t_end = min(N, t_begin + p.seg_len);
   const bool decay = p.gamma != nullptr;
 
-  const float *S0, *z0;
-  if (p.nseg > 1) {
-    S0 = p.ws + ((size_t)seg * p.BH + bh) * ((size_t)d * dv + d);
-    z0 = S0 + (size_t)d * dv;
-  } else {
-    S0 = p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr;
-    z0 = p.z_in ? p.z_in + (size_t)bh * d : nullptr;
-  }
+  // state entering this segment: P_seg = gamma^(L seg) P_0 + sum over the
+  // earlier segments s of gamma^(L (seg-1-s)) dS_s (L = segment length),
+  // with P_0 = (S_in, z_in); the summaries come from summary_kernel
   f32x4 Sacc[CF::FPW][CF::TPW];
-  load_state<CF>(Sacc, S0, z0, d, dv, wv, li, lg);
+  load_state<CF>(Sacc, p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr,
+                 p.z_in ? p.z_in + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
+  if (seg > 0) {
+    const float lgL = decay ? (float)p.seg_len * log2f(p.gamma[bh % p.H]) : 0.f;
+    const size_t rec = (size_t)d * dv + d;
+    // Horner over the summaries; every record's loads are independent of
+    // the chain, so unrolled iterations keep several in flight
+#pragma unroll 2
+    for (int s = 0; s < seg; ++s)
+      add_state<CF>(Sacc, p.ws + ((size_t)s * p.BH + bh) * rec, exp2f(lgL), d, dv, wv, li, lg);
+  }
   // the first chunk's loads go out after the state loads (loads complete in
   // issue order, so waiting for the state does not wait for the chunk)
   ChunkRegs<CF> R;
   prefetch<CF, true, VK>(R, p, hb, t_begin, min(CF::C, N - t_begin));
   fill_powers<CF>(sm.pw, decay ? log2f(p.gamma[bh % p.H]) : 0.f);
   __syncthreads();
-  write_state_copy<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - t_begin)], wv, li, lg);
+  write_state_copy<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - t_begin)], decay, wv, li, lg);
 
   const int rb = wv % CF::NRB, cg = wv / CF::NRB;  // output role
   const int irow = 16 * rb + li;                    // this lane's query row
@@ -474,7 +522,8 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
     state_update<CF>(Sacc, sm.Ks, sm.Vs, sm.pw[Lc], decay, wv, li, lg);
     __syncthreads();
     if (c0 + CF::C < t_end)
-      write_state_copy<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - c0 - CF::C)], wv, li, lg);
+      write_state_copy<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - c0 - CF::C)], decay, wv, li,
+                           lg);
     // 16-byte row stores of the output tile
     {
       const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
@@ -506,7 +555,7 @@ __global__ void __launch_bounds__(CF::NT) chunk_kernel(PrefillParams p) {
 // Phase 1: each segment's own contribution, from a zero state (all but the
 // last segment; those are whole multiples of the chunk length).
 template <class CF, bool VK>
-__global__ void __launch_bounds__(CF::NT) summary_kernel(PrefillParams p) {
+__global__ void __launch_bounds__(CF::NT, CF::WPE) summary_kernel(PrefillParams p) {
   using T = typename CF::type;
   __shared__ SmemSummary<CF> sm;
   const int seg = blockIdx.x, bh = blockIdx.y;
@@ -537,39 +586,8 @@ __global__ void __launch_bounds__(CF::NT) summary_kernel(PrefillParams p) {
     state_update<CF>(Sacc, sm.Ks, sm.Vs, gC, decay, wv, li, lg);
     __syncthreads();
   }
-  float *dst = p.ws + ((size_t)(seg + 1) * p.BH + bh) * ((size_t)d * dv + d);
+  float *dst = p.ws + ((size_t)seg * p.BH + bh) * ((size_t)d * dv + d);
   store_state<CF>(Sacc, dst, dst + (size_t)d * dv, d, dv, wv, li, lg);
-}
-
-// Phase 2: prefix over segments, in place: slot 0 <- (S_in, z_in),
-// slot s <- gamma^L slot (s-1) + dS_(s-1) for s >= 1.  Every record is
-// loaded before the dependent chain starts.
-__global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
-  const int bh = blockIdx.y;
-  const size_t rec = (size_t)p.d * p.dv + p.d;
-  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= rec) return;
-  const float log2g = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
-  const float gL = exp2f((float)p.seg_len * log2g);
-  const size_t dd = (size_t)p.d * p.dv;
-  float *base = p.ws + (size_t)bh * rec + e;
-  const size_t stride = (size_t)p.BH * rec;
-  float dS[kMaxSeg];
-#pragma unroll
-  for (int s = 1; s < kMaxSeg; ++s) dS[s] = s < p.nseg ? base[s * stride] : 0.f;
-  float acc;
-  if (e < dd)
-    acc = p.S_in ? p.S_in[(size_t)bh * dd + e] : 0.f;
-  else
-    acc = p.z_in ? p.z_in[(size_t)bh * p.d + (e - dd)] : 0.f;
-  base[0] = acc;
-#pragma unroll
-  for (int s = 1; s < kMaxSeg; ++s) {
-    if (s < p.nseg) {
-      acc = fmaf(gL, acc, dS[s]);
-      base[s * stride] = acc;
-    }
-  }
 }
 
 template <class CF, bool VK>
@@ -582,13 +600,6 @@ hipError_t run_vk(const PrefillParams &p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_end("linear_summary", s);
-    const size_t rec = (size_t)p.d * p.dv + p.d;
-    prof_begin(s);
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), p.BH),
-                       dim3(256), 0, s, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    prof_end("linear_scan", s);
   }
   prof_begin(s);
   hipLaunchKernelGGL((chunk_kernel<CF, VK>), dim3(p.nseg, p.BH), dim3(CF::NT), 0, s, p);
@@ -663,7 +674,7 @@ LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io) {
   nseg = chunks > 0 ? (chunks + cps - 1) / cps : 1;
   pl.nseg = (int)nseg;
   pl.seg_len = (int)(cps * pl.chunk);
-  pl.ws_bytes = nseg > 1 ? (size_t)nseg * BH * ((size_t)d * dv + d) * sizeof(float)
+  pl.ws_bytes = nseg > 1 ? (size_t)(nseg - 1) * BH * ((size_t)d * dv + d) * sizeof(float)
                          : 0;
   return pl;
 }
