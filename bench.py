@@ -56,7 +56,20 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five "
+                         "times (a calibration point for hardware byte counters)")
     return ap.parse_args()
+
+
+def copy_probe(torch, mib):
+    n = mib * 1024 * 1024 // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "copies": 5}), flush=True)
 
 
 class KernelTimer:
@@ -289,6 +302,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe(torch, args.copy_probe)
+        return
     lib = _lib.load()
     w = inputs.WORKLOADS[args.workload]
     res, x, o = bench_workload(la, lib, torch, w, args.steps, args.warmup)

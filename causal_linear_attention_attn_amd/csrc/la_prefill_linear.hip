@@ -42,14 +42,14 @@
 //   summary_kernel  per (segment, head), all but the last segment: the
 //                   segment's own contribution (dS, dz), i.e. the state
 //                   update from a zero state;
-//   chunk_kernel    per (segment, head): the entering state
-//                   P_s = gamma^(Lseg s) P_0 + sum_{s'<s} gamma^(Lseg (s-1-s')) dS_s'
-//                   with P_0 = (S_in, z_in), then outputs chunk by chunk; the
-//                   last segment writes (S_out, z_out).
+//   scan_kernel     per head: P_0 = (S_in, z_in), P_s = gamma^Lseg P_(s-1)
+//                   + dS_(s-1), every record loaded before the chain;
+//   chunk_kernel    per (segment, head): outputs from P_s, chunk by chunk;
+//                   the last segment writes (S_out, z_out).
 // With one segment only chunk_kernel runs, from (S_in, z_in).
 //
 // Data layout: q, k [BH, N, d], v, o [BH, N, dv] (row-major, dtype T);
-// workspace slots [nseg - 1][BH][d*dv + d] fp32 (state then normaliser).
+// workspace slots [nseg][BH][d*dv + d] fp32 (state then normaliser).
 // Global traffic goes through buffer resources (bounds by offset, no
 // branches between a load and its use), issued one chunk ahead.
 #include <atomic>
@@ -71,7 +71,10 @@ struct Cfg {
   static constexpr int NT = NW * kWave;
   static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte vector
   static constexpr int QLD = DK + VEC;  // row stride: Qs, Ks, St
-  static constexpr int VLD = DV + VEC;  // row stride: Vs, Os
+  static constexpr int VLD = DV + VEC;  // row stride: Os
+  // row stride of Vs, read only through transpose loads: 8 consecutive rows
+  // of 32 bytes then fall in distinct LDS banks
+  static constexpr int VTLD = sizeof(T) == 2 ? DV + 16 : DV + 4;
   static constexpr int NRB = C / 16;    // 16-token row blocks of a chunk
   static constexpr int NG = NW / NRB;   // waves per row block (output role)
   static constexpr int NVT = DV / 16;   // value column tiles
@@ -102,7 +105,7 @@ struct alignas(16) SmemChunk {
   using T = typename CF::type;
   T Qs[CF::C * CF::QLD];      // phi(q) rows
   T Ks[CF::C * CF::QLD];      // weighted phi(k) rows
-  T Vs[CF::C * CF::VLD];      // v rows
+  T Vs[CF::C * CF::VTLD];     // v rows
   T St[CF::SROWS * CF::QLD];  // gamma^L [S | z]^T for the next state read
   T Os[CF::C * CF::VLD];      // output staging
   float pw[CF::C + 4];        // gamma^m, m = 0..C
@@ -112,7 +115,7 @@ template <class CF>
 struct alignas(16) SmemSummary {
   using T = typename CF::type;
   T Ks[CF::C * CF::QLD];
-  T Vs[CF::C * CF::VLD];
+  T Vs[CF::C * CF::VTLD];
   float pw[CF::C + 4];
 };
 
@@ -235,7 +238,7 @@ __device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type
 #pragma unroll
   for (int r = 0; r < CF::RV; ++r) {
     const int row = vrg * CF::RV + r;
-    *reinterpret_cast<V *>(Vs + row * CF::VLD + vcb * VEC) = R.v[r];
+    *reinterpret_cast<V *>(Vs + row * CF::VTLD + vcb * VEC) = R.v[r];
   }
 }
 
@@ -266,17 +269,19 @@ __device__ __forceinline__ void state_update(f32x4 (&Sacc)[CF::FPW][CF::TPW],
   frag_fill(ones, 1.f);
 #pragma unroll
   for (int ks = 0; ks < CF::KSC; ++ks) {
-    const int t0 = 32 * ks + 8 * lg;
+    // slots 0..3: tokens 32 ks + 4 lg + e, slots 4..7: 32 ks + 16 + 4 lg + e
+    // (one transpose read then covers 8 consecutive rows per 32 lanes)
+    const int t0 = 32 * ks + 4 * lg;
 #pragma unroll
     for (int a = 0; a < CF::FPW; ++a) {
       Frag<T> kf;
-      lds_frag_tr(kf, Ks, CF::QLD, t0, t0 + 4, 16 * srow<CF>(wv, a), li);
+      lds_frag_tr(kf, Ks, CF::QLD, t0, t0 + 16, 16 * srow<CF>(wv, a), li);
 #pragma unroll
       for (int b = 0; b < CF::TPW; ++b) {
         const int tn = scol<CF>(wv, b);
         if (tn < CF::NVT) {
           Frag<T> vf;
-          lds_frag_tr(vf, Vs, CF::VLD, t0, t0 + 4, 16 * tn, li);
+          lds_frag_tr(vf, Vs, CF::VTLD, t0, t0 + 16, 16 * tn, li);
           mma(Sacc[a][b], kf, vf);
         } else if (tn == CF::NVT) {
           mma(Sacc[a][b], kf, ones);
@@ -338,33 +343,6 @@ __device__ __forceinline__ void load_state(f32x4 (&Sacc)[CF::FPW][CF::TPW], cons
   }
 }
 
-// Sacc <- scale * Sacc + record, for a [S | z] record in the state layout.
-template <class CF>
-__device__ __forceinline__ void add_state(f32x4 (&Sacc)[CF::FPW][CF::TPW], const float *rec,
-                                          float scale, int d, int dv, int wv, int li, int lg) {
-  const float *zr = rec + (size_t)d * dv;
-#pragma unroll
-  for (int a = 0; a < CF::FPW; ++a) {
-    const int tf = srow<CF>(wv, a);
-#pragma unroll
-    for (int b = 0; b < CF::TPW; ++b) {
-      const int tn = scol<CF>(wv, b);
-      const int n = 16 * tn + li;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int f = 16 * tf + 4 * lg + r;
-        float x = 0.f;
-        if (tn < CF::NVT) {
-          if (f < d && n < dv) x = rec[(size_t)f * dv + n];
-        } else if (tn == CF::NVT) {
-          if (f < d) x = zr[f];
-        }
-        Sacc[a][b][r] = fmaf(scale, Sacc[a][b][r], x);
-      }
-    }
-  }
-}
-
 // Store this wave's [S | z] tiles to an fp32 state.
 template <class CF>
 __device__ __forceinline__ void store_state(const f32x4 (&Sacc)[CF::FPW][CF::TPW], float *S1,
@@ -410,21 +388,18 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p)
   const int t_end = min(N, t_begin + p.seg_len);
   const bool decay = p.gamma != nullptr;
 
-  // state entering this segment: P_seg = gamma^(L seg) P_0 + sum over the
-  // earlier segments s of gamma^(L (seg-1-s)) dS_s (L = segment length),
-  // with P_0 = (S_in, z_in); the summaries come from summary_kernel
-  f32x4 Sacc[CF::FPW][CF::TPW];
-  load_state<CF>(Sacc, p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr,
-                 p.z_in ? p.z_in + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
-  if (seg > 0) {
-    const float lgL = decay ? (float)p.seg_len * log2f(p.gamma[bh % p.H]) : 0.f;
-    const size_t rec = (size_t)d * dv + d;
-    // Horner over the summaries; every record's loads are independent of
-    // the chain, so unrolled iterations keep several in flight
-#pragma unroll 2
-    for (int s = 0; s < seg; ++s)
-      add_state<CF>(Sacc, p.ws + ((size_t)s * p.BH + bh) * rec, exp2f(lgL), d, dv, wv, li, lg);
+  // state entering this segment: slot seg of the scanned workspace, or
+  // (S_in, z_in) with a single segment
+  const float *S0, *z0;
+  if (p.nseg > 1) {
+    S0 = p.ws + ((size_t)seg * p.BH + bh) * ((size_t)d * dv + d);
+    z0 = S0 + (size_t)d * dv;
+  } else {
+    S0 = p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr;
+    z0 = p.z_in ? p.z_in + (size_t)bh * d : nullptr;
   }
+  f32x4 Sacc[CF::FPW][CF::TPW];
+  load_state<CF>(Sacc, S0, z0, d, dv, wv, li, lg);
   // the first chunk's loads go out after the state loads (loads complete in
   // issue order, so waiting for the state does not wait for the chunk)
   ChunkRegs<CF> R;
@@ -501,7 +476,7 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p)
 #pragma unroll
         for (int a = 0; a < CF::NPW; ++a) {
           Frag<T> vf;
-          lds_frag_tr(vf, sm.Vs, CF::VLD, tlo, thi, 16 * (cg * CF::NPW + a), li);
+          lds_frag_tr(vf, sm.Vs, CF::VTLD, tlo, thi, 16 * (cg * CF::NPW + a), li);
           mma(acc[a], vf, af);
         }
         mma(accd, ones, af);
@@ -586,8 +561,39 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) summary_kernel(PrefillParams 
     state_update<CF>(Sacc, sm.Ks, sm.Vs, gC, decay, wv, li, lg);
     __syncthreads();
   }
-  float *dst = p.ws + ((size_t)seg * p.BH + bh) * ((size_t)d * dv + d);
+  float *dst = p.ws + ((size_t)(seg + 1) * p.BH + bh) * ((size_t)d * dv + d);
   store_state<CF>(Sacc, dst, dst + (size_t)d * dv, d, dv, wv, li, lg);
+}
+
+// Phase 2: prefix over segments, in place: slot 0 <- (S_in, z_in),
+// slot s <- gamma^Lseg slot (s-1) + dS_(s-1) for s >= 1 (dS_(s-1) sits in
+// slot s).  One thread per record element; every record is loaded before
+// the dependent chain starts.
+__global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
+  const int bh = blockIdx.y;
+  const size_t rec = (size_t)p.d * p.dv + p.d;
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= rec) return;
+  const float gL = p.gamma ? exp2f((float)p.seg_len * log2f(p.gamma[bh % p.H])) : 1.f;
+  const size_t dd = (size_t)p.d * p.dv;
+  float *base = p.ws + (size_t)bh * rec + e;
+  const size_t stride = (size_t)p.BH * rec;
+  float dS[kMaxSeg];
+#pragma unroll
+  for (int s = 1; s < kMaxSeg; ++s) dS[s] = s < p.nseg ? base[s * stride] : 0.f;
+  float acc;
+  if (e < dd)
+    acc = p.S_in ? p.S_in[(size_t)bh * dd + e] : 0.f;
+  else
+    acc = p.z_in ? p.z_in[(size_t)bh * p.d + (e - dd)] : 0.f;
+  base[0] = acc;
+#pragma unroll
+  for (int s = 1; s < kMaxSeg; ++s) {
+    if (s < p.nseg) {
+      acc = fmaf(gL, acc, dS[s]);
+      base[s * stride] = acc;
+    }
+  }
 }
 
 template <class CF, bool VK>
@@ -600,6 +606,13 @@ hipError_t run_vk(const PrefillParams &p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_end("linear_summary", s);
+    const size_t rec = (size_t)p.d * p.dv + p.d;
+    prof_begin(s);
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), p.BH), dim3(256), 0,
+                       s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    prof_end("linear_scan", s);
   }
   prof_begin(s);
   hipLaunchKernelGGL((chunk_kernel<CF, VK>), dim3(p.nseg, p.BH), dim3(CF::NT), 0, s, p);
@@ -674,8 +687,7 @@ LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io) {
   nseg = chunks > 0 ? (chunks + cps - 1) / cps : 1;
   pl.nseg = (int)nseg;
   pl.seg_len = (int)(cps * pl.chunk);
-  pl.ws_bytes = nseg > 1 ? (size_t)(nseg - 1) * BH * ((size_t)d * dv + d) * sizeof(float)
-                         : 0;
+  pl.ws_bytes = nseg > 1 ? (size_t)nseg * BH * ((size_t)d * dv + d) * sizeof(float) : 0;
   return pl;
 }
 
