@@ -13,7 +13,8 @@
 // owns one block; consecutive threads own consecutive VEC-wide column groups
 // of a row, so each wave moves whole rows (coalesced dwordx4 traffic), and
 // each thread walks rows rg, rg + RG, ... .  All of a thread's rows are
-// loaded before any is used so that every load is in flight at once.  Column
+// loaded before any is used so that every load is in flight at once, and the
+// block's loads are issued before the token's q, k, v are read.  Column
 // sums (the reads S^T phi(q), S^T k, S^T q) are reduced across the RG row
 // groups through LDS in a fixed order: no atomics, deterministic.
 #include "la_common.hpp"
@@ -47,73 +48,75 @@ decode_kernel(DecodeParams p) {
   const int bh = blockIdx.x;
   const int t = threadIdx.x;
   const int d = p.d, dv = p.dv;
+  const int colsv = dv / VEC;          // column groups per row
+  const int RG = kDecThreads / colsv;  // row groups
+  const int cv = t % colsv, rg = t / colsv;
+  const bool active = rg < RG;
+  const int c0 = cv * VEC;
+
+  // The state block goes out first: its loads are in flight while the
+  // token's q, k, v arrive (those are tiny, but a full memory latency).
+  const size_t blk = (size_t)d * dv;
+  const __amdgpu_buffer_rsrc_t rS = buf_rsrc(p.S + (size_t)bh * blk, (uint32_t)(blk * 4));
+  float sr[ROWS][VEC];
+#pragma unroll
+  for (int m = 0; m < ROWS; ++m) {
+    const int r = rg + RG * m;
+    const bool ok = active && r < d;
+    const uint32_t off = ok ? (uint32_t)(((size_t)r * dv + c0) * 4) : kOOB;
+    if constexpr (VEC == 4) {
+      const f32x4 x = buf_load16<float>(rS, off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sr[m][e] = x[e];
+    } else {
+      sr[m][0] = buf_load1(rS, off, (float *)nullptr);
+    }
+  }
+
   const T *q = reinterpret_cast<const T *>(p.q) + (size_t)bh * d;
   const T *k = reinterpret_cast<const T *>(p.k) + (size_t)bh * d;
   const T *v = reinterpret_cast<const T *>(p.v) + (size_t)bh * dv;
-  float *S = p.S + (size_t)bh * d * dv;
-
+  float zold = 0.f;
   if (t < d) {
     float xq = to_f32(q[t]), xk = to_f32(k[t]);
     if (!DELTA && p.fmap) { xq = phi_elu1(xq); xk = phi_elu1(xk); }
     s_q[t] = xq;
     s_k[t] = xk;
+    if (!DELTA) zold = p.z[(size_t)bh * d + t];
   }
   if (t < dv) s_v[t] = to_f32(v[t]);
   const float gam = (!DELTA && p.gamma) ? p.gamma[bh % p.H] : 1.f;
   const float gate = DELTA ? p.g[bh] : 0.f;
   __syncthreads();
 
-  const int colsv = dv / VEC;        // column groups per row
-  const int RG = kDecThreads / colsv;  // row groups
-  const int cv = t % colsv, rg = t / colsv;
-  const bool active = rg < RG;
-  const int c0 = cv * VEC;
-
-  // load every row this thread owns
-  float sr[ROWS][VEC];
-#pragma unroll
-  for (int m = 0; m < ROWS; ++m) {
-    const int r = rg + RG * m;
-    if (active && r < d) {
-      const float *src = S + (size_t)r * dv + c0;
-      if constexpr (VEC == 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(src);
-        sr[m][0] = x[0]; sr[m][1] = x[1]; sr[m][2] = x[2]; sr[m][3] = x[3];
-      } else {
-        sr[m][0] = src[0];
-      }
-    }
-  }
-
   float acc[VEC], acc2[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) { acc[e] = 0.f; acc2[e] = 0.f; }
 
   if constexpr (!DELTA) {
-    // update in place and accumulate phi(q)^T S_new for our columns
+    // update in place (each row stored as soon as it is done) and
+    // accumulate phi(q)^T S_new for this thread's columns
 #pragma unroll
     for (int m = 0; m < ROWS; ++m) {
       const int r = rg + RG * m;
-      if (active && r < d) {
-        const float fk = s_k[r], fq = s_q[r];
+      const bool ok = active && r < d;
+      const float fk = ok ? s_k[r] : 0.f, fq = ok ? s_q[r] : 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const float sn = fmaf(gam, sr[m][e], fk * s_v[c0 + e]);
-          sr[m][e] = sn;
-          acc[e] = fmaf(fq, sn, acc[e]);
-        }
-        float *dst = S + (size_t)r * dv + c0;
-        if constexpr (VEC == 4)
-          *reinterpret_cast<f32x4 *>(dst) =
-              (f32x4){sr[m][0], sr[m][1], sr[m][2], sr[m][3]};
-        else
-          dst[0] = sr[m][0];
+      for (int e = 0; e < VEC; ++e) {
+        const float sn = fmaf(gam, sr[m][e], fk * s_v[c0 + e]);
+        sr[m][e] = sn;
+        acc[e] = fmaf(fq, sn, acc[e]);
       }
+      const uint32_t off = ok ? (uint32_t)(((size_t)r * dv + c0) * 4) : kOOB;
+      if constexpr (VEC == 4)
+        buf_store16<float>(rS, off, (f32x4){sr[m][0], sr[m][1], sr[m][2], sr[m][3]});
+      else
+        buf_store1(rS, off, sr[m][0]);
     }
     // normaliser: z <- gamma z + phi(k); den = phi(q) . z_new
     float dz = 0.f;
     if (t < d) {
-      const float zn = fmaf(gam, p.z[(size_t)bh * d + t], s_k[t]);
+      const float zn = fmaf(gam, zold, s_k[t]);
       p.z[(size_t)bh * d + t] = zn;
       dz = s_q[t] * zn;
     }
@@ -133,13 +136,12 @@ decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int m = 0; m < ROWS; ++m) {
       const int r = rg + RG * m;
-      if (active && r < d) {
-        const float kr = s_k[r], qr = s_q[r];
+      const bool ok = active && r < d;
+      const float kr = ok ? s_k[r] : 0.f, qr = ok ? s_q[r] : 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          acc[e] = fmaf(kr, sr[m][e], acc[e]);
-          acc2[e] = fmaf(qr, sr[m][e], acc2[e]);
-        }
+      for (int e = 0; e < VEC; ++e) {
+        acc[e] = fmaf(kr, sr[m][e], acc[e]);
+        acc2[e] = fmaf(qr, sr[m][e], acc2[e]);
       }
     }
     const float qk = block_sum(t < d ? s_q[t] * s_k[t] : 0.f, s_red);
@@ -167,17 +169,15 @@ decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int m = 0; m < ROWS; ++m) {
       const int r = rg + RG * m;
-      if (active && r < d) {
-        const float gk = gate * s_k[r];
-        float *dst = S + (size_t)r * dv + c0;
+      const bool ok = active && r < d;
+      const float gk = ok ? gate * s_k[r] : 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) sr[m][e] = fmaf(gk, s_b[c0 + e], sr[m][e]);
-        if constexpr (VEC == 4)
-          *reinterpret_cast<f32x4 *>(dst) =
-              (f32x4){sr[m][0], sr[m][1], sr[m][2], sr[m][3]};
-        else
-          dst[0] = sr[m][0];
-      }
+      for (int e = 0; e < VEC; ++e) sr[m][e] = fmaf(gk, s_b[c0 + e], sr[m][e]);
+      const uint32_t off = ok ? (uint32_t)(((size_t)r * dv + c0) * 4) : kOOB;
+      if constexpr (VEC == 4)
+        buf_store16<float>(rS, off, (f32x4){sr[m][0], sr[m][1], sr[m][2], sr[m][3]});
+      else
+        buf_store1(rS, off, sr[m][0]);
     }
   }
 }
