@@ -207,6 +207,16 @@ __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t o
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
 }
+// Streaming store: the cache-policy operand's non-temporal bit (bit 1 in
+// the gfx94x/gfx950 encoding: bit 0 sc0, bit 1 nt, bit 4 sc1).  Used for
+// data written once and not read back by the same kernel (outputs, the
+// decode state write-back, which is larger than the last-level cache).
+template <typename T>
+__device__ __forceinline__ void buf_store16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               typename Vec16<T>::type v) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 2);
+}
 __device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                            float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, (int)off, 0, 0);

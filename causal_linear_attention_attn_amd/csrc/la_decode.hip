@@ -109,7 +109,7 @@ decode_kernel(DecodeParams p) {
       }
       const uint32_t off = ok ? (uint32_t)(((size_t)r * dv + c0) * 4) : kOOB;
       if constexpr (VEC == 4)
-        buf_store16<float>(rS, off, (f32x4){sr[m][0], sr[m][1], sr[m][2], sr[m][3]});
+        buf_store16_nt<float>(rS, off, (f32x4){sr[m][0], sr[m][1], sr[m][2], sr[m][3]});
       else
         buf_store1(rS, off, sr[m][0]);
     }
@@ -175,7 +175,7 @@ decode_kernel(DecodeParams p) {
       for (int e = 0; e < VEC; ++e) sr[m][e] = fmaf(gk, s_b[c0 + e], sr[m][e]);
       const uint32_t off = ok ? (uint32_t)(((size_t)r * dv + c0) * 4) : kOOB;
       if constexpr (VEC == 4)
-        buf_store16<float>(rS, off, (f32x4){sr[m][0], sr[m][1], sr[m][2], sr[m][3]});
+        buf_store16_nt<float>(rS, off, (f32x4){sr[m][0], sr[m][1], sr[m][2], sr[m][3]});
       else
         buf_store1(rS, off, sr[m][0]);
     }

@@ -512,7 +512,7 @@ __global__ void __launch_bounds__(CF::NT) seq_kernel(PrefillParams p, int nslice
       const size_t el = (size_t)(c0 + row) * dv + col0;
       if constexpr (VK) {
         const bool ok = row < Lc && col0 < dv;
-        buf_store16<T>(rs[4], ok ? (uint32_t)(el * sizeof(T)) : kOOB, val);
+        buf_store16_nt<T>(rs[4], ok ? (uint32_t)(el * sizeof(T)) : kOOB, val);
       } else {
 #pragma unroll
         for (int e = 0; e < CF::VEC; ++e) {

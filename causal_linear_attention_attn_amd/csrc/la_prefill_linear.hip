@@ -510,7 +510,7 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p)
         const size_t el = (size_t)(c0 + row) * dv + col0;
         if constexpr (VK) {
           const bool ok = row < Lc && col0 < dv;
-          buf_store16<T>(hb.o, ok ? (uint32_t)(el * sizeof(T)) : kOOB, val);
+          buf_store16_nt<T>(hb.o, ok ? (uint32_t)(el * sizeof(T)) : kOOB, val);
         } else {
 #pragma unroll
           for (int e = 0; e < CF::VEC; ++e) {
