@@ -151,7 +151,7 @@ size_t la_prefill_workspace_size(const la_prefill_args *a) {
   if (BH == 0 || a->N == 0) return 0;
   if (a->rule == LA_RULE_LINEAR)
     return la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16).ws_bytes;
-  return la::delta_workspace_bytes(BH, a->N, a->dtype == LA_BF16);
+  return la::delta_workspace_bytes(BH, a->N, a->d, a->dtype == LA_BF16);
 }
 
 int la_prefill(const la_prefill_args *a, void *stream) {
@@ -187,7 +187,7 @@ int la_prefill(const la_prefill_args *a, void *stream) {
     plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io);
     ws_need = plan.ws_bytes;
   } else {
-    ws_need = la::delta_workspace_bytes(BH, a->N, bf16_io);
+    ws_need = la::delta_workspace_bytes(BH, a->N, a->d, bf16_io);
     // one head's T and R tiles must be addressable with 32-bit byte offsets
     if (ws_need / (size_t)BH > kMaxHeadBytes) return LA_EUNSUPPORTED;
   }

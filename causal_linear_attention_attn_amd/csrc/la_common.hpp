@@ -201,6 +201,15 @@ __device__ __forceinline__ bf16 buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t off
   return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
 }
 
+// Four consecutive T (8 bytes bf16, 16 bytes fp32), as fp32.
+__device__ __forceinline__ f32x4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16 *) {
+  const bf16x4 h = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+  return (f32x4){(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+__device__ __forceinline__ f32x4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off, float *) {
+  return buf_load16<float>(r, off);
+}
+
 template <typename T>
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                             typename Vec16<T>::type v) {
@@ -216,6 +225,19 @@ __device__ __forceinline__ void buf_store16_nt(__amdgpu_buffer_rsrc_t r, uint32_
                                                typename Vec16<T>::type v) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 2);
+}
+// Four fp32 values as four consecutive T (8 bytes bf16, 16 bytes fp32),
+// streaming (non-temporal) store.
+__device__ __forceinline__ void buf_store4_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 a,
+                                              bf16 *) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const bf16x4 h = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r, (int)off, 0, 2);
+}
+__device__ __forceinline__ void buf_store4_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 a,
+                                              float *) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a), r, (int)off, 0, 2);
 }
 __device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                            float x) {

@@ -53,10 +53,9 @@ void prof_end(const char *name, hipStream_t s);
 LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16);
 hipError_t launch_linear_prefill(const PrefillParams &p, const LinearPlan &plan,
                                  bool bf16, hipStream_t s);
-// Gated delta rule: chunk length, workspace (T and R tiles of every chunk)
-// and the two-kernel launch (per-chunk prep, then the sequential pass).
-int delta_chunk_len(bool bf16);
-size_t delta_workspace_bytes(int BH, int N, bool bf16);
+// Gated delta rule: workspace (per-chunk Wt and R tiles) and the two-kernel
+// launch (per-chunk prep, then the sequential pass).
+size_t delta_workspace_bytes(int BH, int N, int d, bool bf16);
 hipError_t launch_delta_prefill(const PrefillParams &p, bool bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, bool bf16, bool delta, int vec,
                          hipStream_t s);

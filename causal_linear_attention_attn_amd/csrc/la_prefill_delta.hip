@@ -9,30 +9,33 @@
 // S_{j-1} = S- + sum_{i<j} k_i u_i^T gives the lower-triangular system
 //     (I + diag(g) L) U = diag(g) (V - K S-),   L = strict_lower(K K^T)
 // so with T = (I + diag(g) L)^(-1) diag(g) and Y = V - K S-:
-//     U  = T Y
-//     O  = Q S- + P U = Q S- + R Y,   P = lower_incl(Q K^T),  R = P T
-//     S+ = S- + K^T U
-// T and R depend only on the chunk's q, k and g, so they are computed for
+//     U  = T Y,   O = Q S- + P U = Q S- + R Y,   P = lower_incl(Q K^T),  R = P T
+//     S+ = S- + K^T U = S- + Wt Y,               Wt = K^T T   (d x C)
+// Wt and R depend only on the chunk's q, k and g, so they are computed for
 // every chunk in parallel (prep_kernel); the state-dependent part is a
-// sequential pass over chunks (seq_kernel).  The columns of S are
-// independent, so the sequential pass is split along dv into slices of W
-// columns, one workgroup per (head, slice).
+// sequential pass over chunks (seq_kernel) with one matrix product on the
+// chain per step: X = K S-, then S+ = S- + Wt (V - X).  The columns of S are
+// independent, so the sequential pass is split along dv into slices.
 //
 // prep_kernel, one workgroup per (chunk, head):
-//   K K^T and Q K^T on the matrix cores (lower tiles only); the unit lower
-//   triangular inverse X = (I + diag(g) L)^(-1) in fp32, 16x16 diagonal
-//   blocks by forward substitution, then the blocks below the diagonal
-//   block row by block row, X_ij = -X_ii sum_{j<=m<i} N_im X_mj with
-//   N = diag(g) L; T = X diag(g); R = P T on the fp32 matrix cores.
-//   T and R are stored in the input precision, [BH][chunk][C][C].
-// seq_kernel, one workgroup per (head, dv slice), chunk after chunk:
-//   X = K S-, Z = Q S- (S- read from a T-precision copy of the fp32 state);
-//   Y = V - X;  U = T Y;  O = Z + R Y;  S+ = S- + K^T U (fp32 accumulators,
-//   never rounded).  Global loads run one chunk ahead in registers; K^T is
-//   double-buffered so the next chunk's tiles are written while the state
-//   update of the current one still reads the old K^T.
+//   K K^T and Q K^T on the matrix cores (lower tiles; the Q K^T tiles stay
+//   in registers); X = (I + N)^(-1), N = diag(g) strict_lower(K K^T), in
+//   fp32: 16x16 diagonal blocks by forward substitution, then the blocks
+//   below, block row by block row, X_ij = -X_ii sum_{j<=m<i} N_im X_mj;
+//   T = X diag(g).  Wt = K^T T and R^T = T^T P^T on the matrix cores with T
+//   (and P) split into bf16 high and low parts, so both keep fp32-level
+//   accuracy before the final rounding.  Stored in the input precision:
+//   per chunk [Wt: DK x C][R: C x C].
+// seq_kernel, one workgroup (4 waves) per (head, slice of W value columns):
+//   per chunk, wave (row block rb, column group): X^T = S'^T K^T and
+//   Z^T = S'^T Q^T from a T-precision copy S' of the fp32 state; Y = V - X
+//   into LDS; O^T = Z^T + Y^T R^T, stored straight from registers; the
+//   state rows the wave owns: S += Wt Y (fp32 accumulators, never rounded).
+//   The chunk's k, q, Wt and R are contiguous blocks; they are loaded two
+//   chunks ahead with whole-cache-line 16-byte loads into registers and
+//   staged into a double-buffered LDS tile; a chunk costs two barriers.
 //
-// Workgroups of one head's slices read the same q, k, T, R: the launch maps
+// Workgroups of one head's slices read the same q, k, R, Wt: the launch maps
 // them onto one XCD (consecutive workgroup ids alternate XCDs) so those
 // reads hit that XCD's L2.
 #include <atomic>
@@ -44,58 +47,99 @@ namespace la {
 namespace {
 
 constexpr int kXcds = 8;
+constexpr int kThreads = 256;  // both kernels: 4 waves
+constexpr int kWaves = kThreads / kWave;
 
 template <typename T, int DK_, int C_, int W_>
 struct DCfg {
   using type = T;
   using vec = typename Vec16<T>::type;
+  static constexpr bool SPLIT = sizeof(T) == 2;  // bf16: hi/lo parts in prep
   static constexpr int DK = DK_, C = C_, W = W_;
   static constexpr int VEC = 16 / (int)sizeof(T);
-  static constexpr int NRB = C / 16;    // 16-row blocks of a chunk
+  static constexpr int NRB = C / 16;    // 16-token row blocks of a chunk
   static constexpr int NCT = W / 16;    // 16-column tiles of a value slice
-  static constexpr int NW = NRB * NCT;  // waves of the sequential pass
-  static constexpr int NT = NW * kWave;
+  static constexpr int NGRP = kWaves / NRB;  // column groups of waves
+  static constexpr int TW = NCT / NGRP;      // column tiles per wave
   static constexpr int NFT = DK / 16;   // 16-row tiles of the state
-  static constexpr int FPW = NFT / NRB; // state row tiles per wave
+  static constexpr int FPW = NFT / kWaves;   // state row tiles per wave
   static constexpr int KSD = DK / 32;   // k-steps over features
-  static constexpr int QLD = DK + VEC;  // row stride: Qs, Ks, St
-  static constexpr int CLD = C + VEC;   // row stride: Kt, Ts, Rs, Yt, Ut
-  static constexpr int VLD = W + VEC;   // row stride: Vs, Os
+  static constexpr int KSC = C / 32;    // k-steps over tokens
+  static constexpr int QLD = DK + VEC;  // row stride: Ks (prep), St (seq)
+  static constexpr int YLD = W + 16;    // row stride: Ys (transpose reads)
+  static constexpr int FLD = C + 8;     // fp32 row stride: Nm, Xm (prep)
+  static constexpr int TLD = C + VEC;   // row stride: T^T parts (prep)
   static constexpr int QCB = DK / VEC;  // 16-byte blocks per q/k row
-  static constexpr int RQ = C * DK / (VEC * NT);  // q/k rows per thread
-  static constexpr int TCB = C / VEC;   // 16-byte blocks per T/R row
-  static constexpr int RT = C * C / (VEC * NT);   // T/R rows per thread
-  static constexpr int WCB = W / VEC;   // 16-byte blocks per value-slice row
-  static constexpr int NVB = C * WCB;   // 16-byte blocks of a value slice
-  static_assert(NRB >= 1 && NCT >= 1 && FPW >= 1 && NFT % NRB == 0, "tiling");
-  static_assert(RQ >= 1 && RQ * VEC * NT == C * DK, "q/k rows per thread");
-  static_assert(RT >= 1 && RT * VEC * NT == C * C, "T/R rows per thread");
-  static_assert(NVB <= NT, "one value block per thread at most");
+  static constexpr size_t WT = (size_t)DK * C;     // Wt elements per chunk
+  static constexpr size_t REC = WT + (size_t)C * C;  // workspace elements per chunk
+  static_assert(NRB >= 1 && NGRP >= 1 && NGRP * NRB == kWaves, "row blocks");
+  static_assert(TW >= 1 && TW * NGRP == NCT, "column tiles");
+  static_assert(FPW >= 1 && FPW * kWaves == NFT, "state tiles");
+  static_assert(KSC >= 1, "chunk of at least 32 tokens");
 };
+
+// 8 consecutive elements of row `row` (columns col0..col0+7) of a row-major
+// [rows, ncols] tensor as an operand fragment; zero outside it.
+template <typename T, bool VK>
+__device__ __forceinline__ void load_frag8(Frag<T> &f, __amdgpu_buffer_rsrc_t r, int row,
+                                           int col0, int ncols, bool row_ok) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+#pragma unroll
+  for (int h = 0; h < 8 / VEC; ++h) {
+    const int c = col0 + h * VEC;
+    typename Vec16<T>::type x;
+    if constexpr (VK) {
+      const bool ok = row_ok && c < ncols;
+      x = buf_load16<T>(r, ok ? (uint32_t)(((size_t)row * ncols + c) * sizeof(T)) : kOOB);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const bool ok = row_ok && c + e < ncols;
+        x[e] = buf_load1(r, ok ? (uint32_t)(((size_t)row * ncols + c + e) * sizeof(T)) : kOOB,
+                         (T *)nullptr);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) f.v[h * VEC + e] = x[e];
+  }
+}
+
+// Four fp32 values to four consecutive T in global memory (8 or 16 bytes).
+__device__ __forceinline__ void store4_t(bf16 *dst, f32x4 a) {
+  *reinterpret_cast<bf16x4 *>(dst) = (bf16x4){(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+}
+__device__ __forceinline__ void store4_t(float *dst, f32x4 a) {
+  *reinterpret_cast<f32x4 *>(dst) = a;
+}
+
+// High and low parts of an fp32 value in T (exact split for bf16; fp32
+// keeps the whole value in the high part).
+template <typename T>
+__device__ __forceinline__ void split2(float x, T &hi, T &lo) {
+  hi = from_f32<T>(x);
+  lo = from_f32<T>(x - to_f32(hi));
+}
 
 // ---------------------------------------------------------------------------
 // prep_kernel
 // ---------------------------------------------------------------------------
-constexpr int kPrepThreads = 256;
-
 template <class CF>
 struct alignas(16) SmemPrep {
   using T = typename CF::type;
-  static constexpr int FLD = CF::C + 4;  // fp32 row stride (16-byte rows)
-  T Ks[CF::C * CF::QLD];
-  T Qs[CF::C * CF::QLD];
-  float Nm[CF::C * FLD];  // diag(g) strict_lower(K K^T); later T^T
-  float Pm[CF::C * FLD];  // lower_incl(Q K^T)
-  float Xm[CF::C * FLD];  // (I + N)^(-1); later T
-  float Ym[CF::C * 16];   // partial products of the block solve
+  T Ks[CF::C * CF::QLD];     // k rows
+  union {
+    float Nm[CF::C * CF::FLD];             // N = diag(g) strict_lower(K K^T)
+    T Tt[2][CF::C * CF::TLD];              // T^T high / low parts (after the solve)
+  };
+  float Xm[CF::C * CF::FLD];  // (I + N)^(-1)
+  float Ym[CF::C * 16];       // partial products of the block solve
   float gs[CF::C];
 };
 
 template <class CF, bool VK>
-__global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrefillParams p) {
+__global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
   using T = typename CF::type;
-  constexpr int C = CF::C, VEC = CF::VEC, FLD = SmemPrep<CF>::FLD;
-  constexpr int NRB = CF::NRB;
+  constexpr int C = CF::C, FLD = CF::FLD, TLD = CF::TLD, NRB = CF::NRB;
   __shared__ SmemPrep<CF> sm;
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x;
@@ -104,77 +148,78 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrefillParams p) {
   const int N = p.N, d = p.d;
   const int c0 = chunk * C;
   const int Lc = min(C, N - c0);
+  const size_t qk = (size_t)N * d;
+  const __amdgpu_buffer_rsrc_t rq =
+      buf_rsrc(reinterpret_cast<const T *>(p.q) + (size_t)bh * qk, (uint32_t)(qk * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t rk =
+      buf_rsrc(reinterpret_cast<const T *>(p.k) + (size_t)bh * qk, (uint32_t)(qk * sizeof(T)));
 
-  // ---- q, k rows and gates into LDS (zero past the sequence) ----
-  {
-    const size_t qk = (size_t)N * d;
-    const __amdgpu_buffer_rsrc_t rq =
-        buf_rsrc(reinterpret_cast<const T *>(p.q) + (size_t)bh * qk, (uint32_t)(qk * sizeof(T)));
-    const __amdgpu_buffer_rsrc_t rk =
-        buf_rsrc(reinterpret_cast<const T *>(p.k) + (size_t)bh * qk, (uint32_t)(qk * sizeof(T)));
-    constexpr int NB = C * CF::QCB;  // 16-byte blocks per tile
-    for (int b = tid; b < NB; b += kPrepThreads) {
-      const int row = b / CF::QCB, col0 = (b % CF::QCB) * VEC;
-      const bool ok = row < Lc;
-      typename CF::vec xq, xk;
-      if constexpr (VK) {
-        const uint32_t off = (ok && col0 < d)
-                                 ? (uint32_t)(((size_t)(c0 + row) * d + col0) * sizeof(T))
-                                 : kOOB;
-        xq = buf_load16<T>(rq, off);
-        xk = buf_load16<T>(rk, off);
-      } else {
+  // ---- k rows and gates into LDS; this wave's q rows into registers ----
+  for (int b = tid; b < C * CF::QCB; b += kThreads) {
+    const int row = b / CF::QCB, col0 = (b % CF::QCB) * CF::VEC;
+    typename CF::vec x;
+    if constexpr (VK) {
+      const bool ok = row < Lc && col0 < d;
+      x = buf_load16<T>(rk, ok ? (uint32_t)(((size_t)(c0 + row) * d + col0) * sizeof(T)) : kOOB);
+    } else {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          const uint32_t off = (ok && col0 + e < d)
-                                   ? (uint32_t)(((size_t)(c0 + row) * d + col0 + e) * sizeof(T))
-                                   : kOOB;
-          xq[e] = buf_load1(rq, off, (T *)nullptr);
-          xk[e] = buf_load1(rk, off, (T *)nullptr);
-        }
+      for (int e = 0; e < CF::VEC; ++e) {
+        const bool ok = row < Lc && col0 + e < d;
+        x[e] = buf_load1(rk, ok ? (uint32_t)(((size_t)(c0 + row) * d + col0 + e) * sizeof(T))
+                                : kOOB, (T *)nullptr);
       }
-      *reinterpret_cast<typename CF::vec *>(sm.Qs + row * CF::QLD + col0) = xq;
-      *reinterpret_cast<typename CF::vec *>(sm.Ks + row * CF::QLD + col0) = xk;
     }
-    if (tid < C) sm.gs[tid] = tid < Lc ? p.g[(size_t)bh * N + c0 + tid] : 0.f;
+    *reinterpret_cast<typename CF::vec *>(sm.Ks + row * CF::QLD + col0) = x;
+  }
+  if (tid < C) sm.gs[tid] = tid < Lc ? p.g[(size_t)bh * N + c0 + tid] : 0.f;
+  const int rb = wv;  // row block of this wave (waves >= NRB idle in row-block work)
+  Frag<T> qf[CF::KSD];
+  if (rb < NRB) {
+#pragma unroll
+    for (int ks = 0; ks < CF::KSD; ++ks)
+      load_frag8<T, VK>(qf[ks], rq, c0 + 16 * rb + li, 32 * ks + 8 * lg, d,
+                        16 * rb + li < Lc);
   }
   __syncthreads();
 
-  // ---- K K^T and Q K^T, lower tiles, on the matrix cores ----
-  // Wave w handles row block w (and w + 4 when the chunk has more blocks).
-  for (int rb = wv; rb < NRB; rb += kPrepThreads / kWave) {
-    Frag<T> kr[CF::KSD], qr[CF::KSD];
+  // ---- K K^T (-> N in LDS) and Q K^T (-> registers), lower tiles ----
+  // Tiles are computed transposed: pq[tj][r] = q_i . k_j with i = 16 rb + li,
+  // j = 16 tj + 4 lg + r (lane keeps one query row, four keys).
+  f32x4 pq[NRB];
 #pragma unroll
-    for (int ks = 0; ks < CF::KSD; ++ks) {
+  for (int tj = 0; tj < NRB; ++tj) pq[tj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (rb < NRB) {
+    Frag<T> kr[CF::KSD];
+#pragma unroll
+    for (int ks = 0; ks < CF::KSD; ++ks)
       lds_frag(kr[ks], sm.Ks + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
-      lds_frag(qr[ks], sm.Qs + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
-    }
+    const int i = 16 * rb + li;
+    const float gi = sm.gs[i];
+#pragma unroll
     for (int tj = 0; tj < NRB; ++tj) {
-      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = {0.f, 0.f, 0.f, 0.f};
       if (tj <= rb) {
+        f32x4 kk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < CF::KSD; ++ks) {
           Frag<T> kc;
           lds_frag(kc, sm.Ks + (16 * tj + li) * CF::QLD + 32 * ks + 8 * lg);
-          // output tile rows = keys j of block tj, column = row i of block rb
           mma(kk, kc, kr[ks]);
-          mma(qk, kc, qr[ks]);
+          mma(pq[tj], kc, qf[ks]);
         }
-      }
-      // lane holds (i = 16 rb + li, j = 16 tj + 4 lg + r)
-      const int i = 16 * rb + li;
-      const float gi = sm.gs[i];
+        float n4[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * tj + 4 * lg + r;
-        sm.Nm[i * FLD + j] = j < i ? gi * kk[r] : 0.f;
-        sm.Pm[i * FLD + j] = j <= i ? qk[r] : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * tj + 4 * lg + r;
+          n4[r] = j < i ? gi * kk[r] : 0.f;
+          if (j > i) pq[tj][r] = 0.f;
+        }
+        lds_store4(sm.Nm + i * FLD + 16 * tj + 4 * lg, n4[0], n4[1], n4[2], n4[3]);
       }
     }
   }
   __syncthreads();
 
-  // ---- inverse of the unit lower triangular I + N ----
+  // ---- X = (I + N)^(-1), unit lower triangular ----
   // Diagonal 16x16 blocks: lane 16 b + c solves column c of block b by
   // forward substitution (x_c = 1; x_i = -sum_{m<i} N_im x_m for i > c).
   if (wv == 0 && lane < 16 * NRB) {
@@ -191,14 +236,11 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sm.Xm[(16 * b + i) * FLD + 16 * b + c] = x[i];
   }
-  // zero the strictly upper blocks
-  for (int e = tid; e < C * C; e += kPrepThreads) {
+  for (int e = tid; e < C * C; e += kThreads) {  // strictly upper blocks
     const int i = e / C, j = e % C;
     if ((j >> 4) > (i >> 4)) sm.Xm[i * FLD + j] = 0.f;
   }
   __syncthreads();
-  // Blocks below the diagonal, one block row at a time:
-  //   Y_ij = sum_{j<=m<i} N_im X_mj,   X_ij = -X_ii Y_ij.
   {
     const int r = tid >> 4, c = tid & 15;  // one element of a 16x16 block
     for (int bi = 1; bi < NRB; ++bi) {
@@ -224,182 +266,189 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(PrefillParams p) {
     }
   }
 
-  // ---- T = X diag(g): kept row-major in Xm and transposed (fp32) in Nm ----
-  for (int e = tid; e < C * C; e += kPrepThreads) {
-    const int i = e / C, j = e % C;
-    const float t = sm.Xm[i * FLD + j] * sm.gs[j];
-    sm.Xm[i * FLD + j] = t;
-    sm.Nm[j * FLD + i] = t;
+  // ---- T^T (T = X diag(g)) as high and low parts, over N's storage ----
+  for (int e = tid; e < C * C; e += kThreads) {
+    const int i = e / C, j = e % C;  // T^T[i][j] = T[j][i] = X[j][i] g_i
+    T hi, lo;
+    split2<T>(sm.Xm[j * FLD + i] * sm.gs[i], hi, lo);
+    sm.Tt[0][i * TLD + j] = hi;
+    sm.Tt[1][i * TLD + j] = lo;
   }
   __syncthreads();
 
-  // ---- R = P T (lower tiles) on the fp32 matrix cores; stores ----
-  const size_t slot = ((size_t)bh * gridDim.x + chunk) * C * C;
-  T *Tw = reinterpret_cast<T *>(p.ws) + 2 * slot;
-  T *Rw = Tw + (size_t)C * C;
-  for (int t = wv; t < NRB * NRB; t += kPrepThreads / kWave) {
-    const int ti = t / NRB, tj = t % NRB;  // output tile (rows ti, columns tj)
+  T *out = reinterpret_cast<T *>(p.ws) + ((size_t)bh * gridDim.x + chunk) * CF::REC;
+  // ---- Wt = K^T T, computed as W = T^T K (rows i, columns f) ----
+  // stored transposed, Wt[f][i]: the lane's four rows i are contiguous.
+  for (int t = wv; t < NRB * CF::NFT; t += kWaves) {
+    const int ti = t / CF::NFT, tf = t % CF::NFT;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (tj <= ti) {
-      // m runs over [16 tj, 16 ti + 16); P and T are zero outside their
-      // triangles, so whole 32-wide steps covering that range are exact.
-      for (int ks = (16 * tj) / 32; ks <= (16 * ti + 15) / 32; ++ks) {
-        Frag<float> a, b;
-        lds_frag(a, sm.Pm + (16 * ti + li) * FLD + 32 * ks + 8 * lg);
-        lds_frag(b, sm.Nm + (16 * tj + li) * FLD + 32 * ks + 8 * lg);
-        mma(acc, a, b);
+#pragma unroll
+    for (int ks = 0; ks < CF::KSC; ++ks) {
+      if (32 * ks + 31 < 16 * ti) continue;  // T^T[i][j] = 0 for j < i
+      Frag<T> kf;
+      lds_frag_tr(kf, sm.Ks, CF::QLD, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * tf, li);
+#pragma unroll
+      for (int h = 0; h < (CF::SPLIT ? 2 : 1); ++h) {
+        Frag<T> a;
+        lds_frag(a, sm.Tt[h] + (16 * ti + li) * TLD + 32 * ks + 8 * lg);
+        mma(acc, a, kf);
       }
     }
-    // lane holds R[16 ti + 4 lg + r][16 tj + li]
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      Rw[(size_t)(16 * ti + 4 * lg + r) * C + 16 * tj + li] = from_f32<T>(acc[r]);
+    // lane holds W[i = 16 ti + 4 lg + r][f = 16 tf + li]
+    store4_t(out + (size_t)(16 * tf + li) * C + 16 * ti + 4 * lg, acc);
   }
-  for (int e = tid; e < C * C; e += kPrepThreads)
-    Tw[e] = from_f32<T>(sm.Xm[(e / C) * FLD + e % C]);
+  // ---- R^T = T^T P^T (rows m, columns i = this wave's row block) ----
+  // stored as R[i][m]: the lane's four rows m are contiguous.
+  if (rb < NRB) {
+    T *Rw = out + CF::WT;
+    const int i = 16 * rb + li;
+    for (int tm = 0; tm <= rb; ++tm) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pp = 0; pp < NRB / 2; ++pp) {
+        if (2 * pp > rb || 32 * pp + 31 < 16 * tm) continue;
+        // k slots: 0..3 -> keys 32 pp + 4 lg + e, 4..7 -> 32 pp + 16 + 4 lg + e
+        Frag<T> bh_, bl_;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          T h0, l0, h1, l1;
+          split2<T>(pq[2 * pp][e], h0, l0);
+          split2<T>(2 * pp + 1 < NRB ? pq[2 * pp + 1][e] : 0.f, h1, l1);
+          bh_.v[e] = h0; bh_.v[4 + e] = h1;
+          bl_.v[e] = l0; bl_.v[4 + e] = l1;
+        }
+        Frag<T> ah, al;
+        lds_half(ah, sm.Tt[0] + (16 * tm + li) * TLD + 32 * pp + 4 * lg, 0);
+        lds_half(ah, sm.Tt[0] + (16 * tm + li) * TLD + 32 * pp + 16 + 4 * lg, 4);
+        mma(acc, ah, bh_);
+        if constexpr (CF::SPLIT) {
+          lds_half(al, sm.Tt[1] + (16 * tm + li) * TLD + 32 * pp + 4 * lg, 0);
+          lds_half(al, sm.Tt[1] + (16 * tm + li) * TLD + 32 * pp + 16 + 4 * lg, 4);
+          mma(acc, ah, bl_);
+          mma(acc, al, bh_);
+        }
+      }
+      // lane holds R^T[m = 16 tm + 4 lg + r][i]
+      store4_t(Rw + (size_t)i * C + 16 * tm + 4 * lg, acc);
+    }
+    // tiles of R above the diagonal are zero
+    for (int tm = rb + 1; tm < NRB; ++tm)
+      store4_t(Rw + (size_t)i * C + 16 * tm + 4 * lg, (f32x4){0.f, 0.f, 0.f, 0.f});
+  }
 }
 
 // ---------------------------------------------------------------------------
 // seq_kernel
 // ---------------------------------------------------------------------------
+// A chunk's operands as LDS tiles (row strides padded so that 16-lane
+// fragment reads of 16 rows hit distinct banks).
+template <class CF>
+struct alignas(16) SeqTiles {
+  using T = typename CF::type;
+  T K[CF::C * CF::QLD];    // k rows
+  T Q[CF::C * CF::QLD];    // q rows
+  T Wt[CF::DK * CF::TLD];  // Wt rows (features f, tokens contiguous)
+  T R[CF::C * CF::TLD];    // R rows
+};
+
 template <class CF>
 struct alignas(16) SmemSeq {
   using T = typename CF::type;
-  T Qs[CF::C * CF::QLD];
-  T Ks[CF::C * CF::QLD];
-  T Kt[2][CF::DK * CF::CLD];  // K^T, double-buffered
-  T Ts[CF::C * CF::CLD];
-  T Rs[CF::C * CF::CLD];
-  T Vs[CF::C * CF::VLD];
-  T Yt[CF::W * CF::CLD];      // (V - K S)^T
-  T Ut[CF::W * CF::CLD];      // U^T
-  T St[CF::W * CF::QLD];      // S^T, T-precision copy of the fp32 state
-  T Os[CF::C * CF::VLD];
+  SeqTiles<CF> tile[2];    // double buffer: chunk c and chunk c + 1
+  T Ys[CF::C * CF::YLD];   // Y = V - K S- rows (this slice's columns)
+  T St[CF::W * CF::QLD];   // S'^T: T-precision copy of the fp32 state slice
 };
 
+// One chunk's k, q, Wt and R as 16-byte blocks, this thread's share; the
+// blocks are contiguous in memory, so every load instruction of a wave
+// covers whole cache lines.
 template <class CF>
 struct SeqRegs {
-  typename CF::vec q[CF::RQ], k[CF::RQ], t[CF::RT], r[CF::RT], v;
+  static constexpr int NQ = CF::C * CF::QCB / kThreads;              // q (and k) blocks
+  static constexpr int NW = CF::DK * (CF::C / CF::VEC) / kThreads;   // Wt blocks
+  static constexpr int NR = CF::C * (CF::C / CF::VEC) / kThreads;    // R blocks
+  static_assert(NQ * kThreads == CF::C * CF::QCB && NW * kThreads == CF::DK * CF::C / CF::VEC &&
+                    NR * kThreads == CF::C * CF::C / CF::VEC,
+                "blocks per thread");
+  typename CF::vec k[NQ], q[NQ], w[NW], r[NR];
 };
 
 template <class CF, bool VK>
-__device__ __forceinline__ void seq_prefetch(SeqRegs<CF> &R, const PrefillParams &p,
-                                             const __amdgpu_buffer_rsrc_t (&rs)[5],
-                                             int c0, int chunk, int n0) {
+__device__ __forceinline__ void seq_load(SeqRegs<CF> &R, const PrefillParams &p,
+                                         const __amdgpu_buffer_rsrc_t (&rs)[5], int chunk) {
   using T = typename CF::type;
-  constexpr int VEC = CF::VEC;
+  using Reg = SeqRegs<CF>;
+  constexpr int C = CF::C, VEC = CF::VEC;
   const int tid = threadIdx.x;
-  const int Lc = min(CF::C, p.N - c0);
-  {
-    const int cb = tid % CF::QCB, rg = tid / CF::QCB;
+  const int c0 = chunk * C;
 #pragma unroll
-    for (int r = 0; r < CF::RQ; ++r) {
-      const int row = rg * CF::RQ + r;
-      R.q[r] = [&] {
-        if constexpr (VK) {
-          const bool ok = row < Lc && cb * VEC < p.d;
-          return buf_load16<T>(rs[0], ok ? (uint32_t)(((size_t)(c0 + row) * p.d + cb * VEC) * sizeof(T)) : kOOB);
-        } else {
-          typename CF::vec x;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const bool ok = row < Lc && cb * VEC + e < p.d;
-            x[e] = buf_load1(rs[0], ok ? (uint32_t)(((size_t)(c0 + row) * p.d + cb * VEC + e) * sizeof(T)) : kOOB, (T *)nullptr);
-          }
-          return x;
-        }
-      }();
-      R.k[r] = [&] {
-        if constexpr (VK) {
-          const bool ok = row < Lc && cb * VEC < p.d;
-          return buf_load16<T>(rs[1], ok ? (uint32_t)(((size_t)(c0 + row) * p.d + cb * VEC) * sizeof(T)) : kOOB);
-        } else {
-          typename CF::vec x;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const bool ok = row < Lc && cb * VEC + e < p.d;
-            x[e] = buf_load1(rs[1], ok ? (uint32_t)(((size_t)(c0 + row) * p.d + cb * VEC + e) * sizeof(T)) : kOOB, (T *)nullptr);
-          }
-          return x;
-        }
-      }();
-    }
-  }
-  {
-    // T and R of this chunk: contiguous C x C tiles
-    const uint32_t base = (uint32_t)chunk * (uint32_t)(2 * CF::C * CF::C) * sizeof(T);
-#pragma unroll
-    for (int r = 0; r < CF::RT; ++r) {
-      const uint32_t e = (uint32_t)(tid + r * CF::NT) * VEC;  // element in the tile
-      R.t[r] = buf_load16<T>(rs[2], base + e * sizeof(T));
-      R.r[r] = buf_load16<T>(rs[2], base + (e + CF::C * CF::C) * sizeof(T));
-    }
-  }
-  {
-    const int row = tid / CF::WCB, cb = tid % CF::WCB;
-    const int col0 = n0 + cb * VEC;
-    const bool in = tid < CF::NVB && row < Lc;
+  for (int m = 0; m < Reg::NQ; ++m) {
+    const int b = tid + m * kThreads;
+    const int row = b / CF::QCB, col0 = (b % CF::QCB) * VEC;
+    const int t = c0 + row;
     if constexpr (VK) {
-      const bool ok = in && col0 < p.dv;
-      R.v = buf_load16<T>(rs[3], ok ? (uint32_t)(((size_t)(c0 + row) * p.dv + col0) * sizeof(T)) : kOOB);
+      const uint32_t off = (t < p.N && col0 < p.d)
+                               ? (uint32_t)(((size_t)t * p.d + col0) * sizeof(T)) : kOOB;
+      R.k[m] = buf_load16<T>(rs[1], off);
+      R.q[m] = buf_load16<T>(rs[0], off);
     } else {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const bool ok = in && col0 + e < p.dv;
-        R.v[e] = buf_load1(rs[3], ok ? (uint32_t)(((size_t)(c0 + row) * p.dv + col0 + e) * sizeof(T)) : kOOB, (T *)nullptr);
+        const uint32_t off = (t < p.N && col0 + e < p.d)
+                                 ? (uint32_t)(((size_t)t * p.d + col0 + e) * sizeof(T)) : kOOB;
+        R.k[m][e] = buf_load1(rs[1], off, (T *)nullptr);
+        R.q[m][e] = buf_load1(rs[0], off, (T *)nullptr);
       }
     }
   }
+  // chunk record [Wt: DK x C][R: C x C], contiguous and always whole (a
+  // chunk past the end reads as zeros: offsets past the resource)
+  const uint32_t base = (uint32_t)((size_t)chunk * CF::REC * sizeof(T));
+#pragma unroll
+  for (int m = 0; m < Reg::NW; ++m)
+    R.w[m] = buf_load16<T>(rs[2], base + (uint32_t)(tid + m * kThreads) * 16u);
+#pragma unroll
+  for (int m = 0; m < Reg::NR; ++m)
+    R.r[m] = buf_load16<T>(rs[2], base + (uint32_t)(CF::WT * sizeof(T)) +
+                                      (uint32_t)(tid + m * kThreads) * 16u);
 }
 
-// Registers -> LDS tiles for one chunk (K^T into buffer `kb`).
 template <class CF>
-__device__ __forceinline__ void seq_commit(const SeqRegs<CF> &R, SmemSeq<CF> &sm, int kb) {
-  using T = typename CF::type;
+__device__ __forceinline__ void seq_commit(const SeqRegs<CF> &R, SeqTiles<CF> &tl) {
   using V = typename CF::vec;
-  constexpr int VEC = CF::VEC;
+  using Reg = SeqRegs<CF>;
+  constexpr int C = CF::C, VEC = CF::VEC;
   const int tid = threadIdx.x;
-  {
-    const int cb = tid % CF::QCB, rg = tid / CF::QCB;
-    const int col0 = cb * VEC;
 #pragma unroll
-    for (int r = 0; r < CF::RQ; ++r) {
-      const int row = rg * CF::RQ + r;
-      *reinterpret_cast<V *>(sm.Qs + row * CF::QLD + col0) = R.q[r];
-      *reinterpret_cast<V *>(sm.Ks + row * CF::QLD + col0) = R.k[r];
-    }
-    // K^T: this thread's RQ consecutive rows, column by column
+  for (int m = 0; m < Reg::NQ; ++m) {
+    const int b = tid + m * kThreads;
+    const int row = b / CF::QCB, col0 = (b % CF::QCB) * VEC;
+    *reinterpret_cast<V *>(tl.K + row * CF::QLD + col0) = R.k[m];
+    *reinterpret_cast<V *>(tl.Q + row * CF::QLD + col0) = R.q[m];
+  }
+  constexpr int CB = C / VEC;  // 16-byte blocks per Wt / R row
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      float x[CF::RQ];
-#pragma unroll
-      for (int r = 0; r < CF::RQ; ++r) x[r] = to_f32(R.k[r][e]);
-      lds_store_n<T, CF::RQ>(sm.Kt[kb] + (col0 + e) * CF::CLD + rg * CF::RQ, x);
-    }
+  for (int m = 0; m < Reg::NW; ++m) {
+    const int b = tid + m * kThreads;
+    *reinterpret_cast<V *>(tl.Wt + (b / CB) * CF::TLD + (b % CB) * VEC) = R.w[m];
   }
 #pragma unroll
-  for (int r = 0; r < CF::RT; ++r) {
-    const int e = (tid + r * CF::NT) * VEC;
-    const int row = e / CF::C, col = e % CF::C;
-    *reinterpret_cast<V *>(sm.Ts + row * CF::CLD + col) = R.t[r];
-    *reinterpret_cast<V *>(sm.Rs + row * CF::CLD + col) = R.r[r];
-  }
-  if (tid < CF::NVB) {
-    const int row = tid / CF::WCB, cb = tid % CF::WCB;
-    *reinterpret_cast<V *>(sm.Vs + row * CF::VLD + cb * VEC) = R.v;
+  for (int m = 0; m < Reg::NR; ++m) {
+    const int b = tid + m * kThreads;
+    *reinterpret_cast<V *>(tl.R + (b / CB) * CF::TLD + (b % CB) * VEC) = R.r[m];
   }
 }
 
 template <class CF, bool VK>
-__global__ void __launch_bounds__(CF::NT) seq_kernel(PrefillParams p, int nslices,
-                                                     int xcd_map) {
+__global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nslices,
+                                                       int xcd_map) {
   using T = typename CF::type;
   constexpr int C = CF::C, W = CF::W;
   __shared__ SmemSeq<CF> sm;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int rb = wv % CF::NRB, ct = wv / CF::NRB;
+  const int rb = wv % CF::NRB, ct0 = (wv / CF::NRB) * CF::TW;
 
   // workgroup -> (head, slice); with xcd_map the slices of one head share
   // an XCD (workgroup b runs on XCD b % 8)
@@ -422,150 +471,190 @@ __global__ void __launch_bounds__(CF::NT) seq_kernel(PrefillParams p, int nslice
     const size_t qk = (size_t)N * d, vo = (size_t)N * dv;
     rs[0] = buf_rsrc(reinterpret_cast<const T *>(p.q) + (size_t)bh * qk, (uint32_t)(qk * sizeof(T)));
     rs[1] = buf_rsrc(reinterpret_cast<const T *>(p.k) + (size_t)bh * qk, (uint32_t)(qk * sizeof(T)));
-    const size_t tr = (size_t)nch * 2 * C * C;
+    const size_t tr = (size_t)nch * CF::REC;
     rs[2] = buf_rsrc(reinterpret_cast<const T *>(p.ws) + (size_t)bh * tr, (uint32_t)(tr * sizeof(T)));
     rs[3] = buf_rsrc(reinterpret_cast<const T *>(p.v) + (size_t)bh * vo, (uint32_t)(vo * sizeof(T)));
     rs[4] = buf_rsrc(reinterpret_cast<const T *>(p.o) + (size_t)bh * vo, (uint32_t)(vo * sizeof(T)));
   }
 
-  // fp32 state slice: wave holds row tiles tf = rb * FPW + a, column tile ct
-  f32x4 Sacc[CF::FPW];
+  // fp32 state slice: wave holds row tiles tf = wv * FPW + a, every column tile
+  f32x4 Sacc[CF::FPW][CF::NCT];
   const float *S0 = p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr;
-  const int ncol = n0 + 16 * ct + li;
 #pragma unroll
-  for (int a = 0; a < CF::FPW; ++a) {
-    const int tf = rb * CF::FPW + a;
+  for (int a = 0; a < CF::FPW; ++a)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int f = 16 * tf + 4 * lg + r;
-      Sacc[a][r] = (S0 && f < d && ncol < dv) ? S0[(size_t)f * dv + ncol] : 0.f;
-    }
-  }
-  SeqRegs<CF> R;
-  seq_prefetch<CF, VK>(R, p, rs, 0, 0, n0);
+    for (int c = 0; c < CF::NCT; ++c) {
+      const int n = n0 + 16 * c + li;
 #pragma unroll
-  for (int a = 0; a < CF::FPW; ++a) {
-    const int tf = rb * CF::FPW + a;
-    lds_store4(sm.St + (16 * ct + li) * CF::QLD + 16 * tf + 4 * lg, Sacc[a][0], Sacc[a][1],
-               Sacc[a][2], Sacc[a][3]);
-  }
-  seq_commit<CF>(R, sm, 0);
-  if (nch > 1) seq_prefetch<CF, VK>(R, p, rs, C, 1, n0);
-  __syncthreads();
-
-  for (int c = 0; c < nch; ++c) {
-    const int c0 = c * C;
-    const int Lc = min(C, N - c0);
-    const int kb = c & 1;
-    // ---- X = K S-, Z = Q S- (tile rb, ct) ----
-    f32x4 X = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < CF::KSD; ++ks) {
-      Frag<T> kf, qf, sf;
-      lds_frag(sf, sm.St + (16 * ct + li) * CF::QLD + 32 * ks + 8 * lg);
-      lds_frag(kf, sm.Ks + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
-      lds_frag(qf, sm.Qs + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
-      mma(X, kf, sf);
-      mma(Z, qf, sf);
-    }
-    // ---- Y = V - X, stored transposed (tokens contiguous) ----
-    // lane holds rows 16 rb + 4 lg + r, column 16 ct + li
-    {
-      float y[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        y[r] = to_f32(sm.Vs[(16 * rb + 4 * lg + r) * CF::VLD + 16 * ct + li]) - X[r];
-      lds_store4(sm.Yt + (16 * ct + li) * CF::CLD + 16 * rb + 4 * lg, y[0], y[1], y[2], y[3]);
-    }
-    __syncthreads();
-    // ---- U = T Y, O = Z + R Y (T and R are lower triangular) ----
-    {
-      f32x4 U = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < C / 32; ++ks) {
-        if (32 * ks <= 16 * rb + 15) {
-          Frag<T> tf, rf, yf;
-          lds_frag(yf, sm.Yt + (16 * ct + li) * CF::CLD + 32 * ks + 8 * lg);
-          lds_frag(tf, sm.Ts + (16 * rb + li) * CF::CLD + 32 * ks + 8 * lg);
-          lds_frag(rf, sm.Rs + (16 * rb + li) * CF::CLD + 32 * ks + 8 * lg);
-          mma(U, tf, yf);
-          mma(Z, rf, yf);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int f = 16 * (wv * CF::FPW + a) + 4 * lg + r;
+        Sacc[a][c][r] = (S0 && f < d && n < dv) ? S0[(size_t)f * dv + n] : 0.f;
       }
-      lds_store4(sm.Ut + (16 * ct + li) * CF::CLD + 16 * rb + 4 * lg, U[0], U[1], U[2], U[3]);
+    }
+  // Operands run two chunks ahead: register set u holds the k, q, Wt, R
+  // blocks of chunk c + 2 while LDS tile u holds chunk c (the loop is
+  // unrolled by two so every buffer index is static).  The v values a lane
+  // needs (four consecutive columns of its token) ride along in registers.
+  // No branch guards a load: chunks past the end read as zeros, and a step
+  // on zeros leaves the state unchanged and stores nothing.
+  SeqRegs<CF> set[2];
+  f32x4 vset[2][CF::TW];
+  auto load_v = [&](f32x4 (&vv)[CF::TW], int chunk) {
+    const int t = chunk * C + 16 * rb + li;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sm.Os[(16 * rb + 4 * lg + r) * CF::VLD + 16 * ct + li] = from_f32<T>(Z[r]);
-    }
-    __syncthreads();
-    // ---- next chunk's tiles (K^T into the other buffer), next loads ----
-    if (c + 1 < nch) {
-      seq_commit<CF>(R, sm, kb ^ 1);
-      if (c + 2 < nch) seq_prefetch<CF, VK>(R, p, rs, c0 + 2 * C, c + 2, n0);
-    }
-    // ---- output rows of the slice ----
-    if (tid < CF::NVB) {
-      const int row = tid / CF::WCB, cb = tid % CF::WCB;
-      const int col0 = n0 + cb * CF::VEC;
-      const typename CF::vec val =
-          *reinterpret_cast<const typename CF::vec *>(sm.Os + row * CF::VLD + cb * CF::VEC);
-      const size_t el = (size_t)(c0 + row) * dv + col0;
+    for (int b2 = 0; b2 < CF::TW; ++b2) {
+      const int col = n0 + 16 * (ct0 + b2) + 4 * lg;
       if constexpr (VK) {
-        const bool ok = row < Lc && col0 < dv;
-        buf_store16_nt<T>(rs[4], ok ? (uint32_t)(el * sizeof(T)) : kOOB, val);
+        vv[b2] = buf_load4(rs[3], t < N && col < dv ? (uint32_t)(((size_t)t * dv + col) * sizeof(T))
+                                                     : kOOB, (T *)nullptr);
       } else {
 #pragma unroll
-        for (int e = 0; e < CF::VEC; ++e) {
-          const bool ok = row < Lc && col0 + e < dv;
-          buf_store1(rs[4], ok ? (uint32_t)((el + e) * sizeof(T)) : kOOB, val[e]);
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = t < N && col + e < dv;
+          vv[b2][e] = to_f32(buf_load1(
+              rs[3], ok ? (uint32_t)(((size_t)t * dv + col + e) * sizeof(T)) : kOOB, (T *)nullptr));
         }
       }
     }
-    // ---- S+ = S- + K^T U, and its T-precision copy ----
+  };
+  seq_load<CF, VK>(set[0], p, rs, 0);
+  seq_commit<CF>(set[0], sm.tile[0]);
+  load_v(vset[0], 0);
+  seq_load<CF, VK>(set[1], p, rs, 1);
+  load_v(vset[1], 1);
 #pragma unroll
-    for (int a = 0; a < CF::FPW; ++a) {
-      const int tf = rb * CF::FPW + a;
+  for (int a = 0; a < CF::FPW; ++a)
 #pragma unroll
-      for (int ks = 0; ks < C / 32; ++ks) {
-        Frag<T> kf, uf;
-        lds_frag(kf, sm.Kt[kb] + (16 * tf + li) * CF::CLD + 32 * ks + 8 * lg);
-        lds_frag(uf, sm.Ut + (16 * ct + li) * CF::CLD + 32 * ks + 8 * lg);
-        mma(Sacc[a], kf, uf);
+    for (int c = 0; c < CF::NCT; ++c)
+      lds_store4(sm.St + (16 * c + li) * CF::QLD + 16 * (wv * CF::FPW + a) + 4 * lg,
+                 Sacc[a][c][0], Sacc[a][c][1], Sacc[a][c][2], Sacc[a][c][3]);
+  __syncthreads();
+
+  for (int cb = 0; cb < nch; cb += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = cb + u;
+      const SeqTiles<CF> &tl = sm.tile[u];
+      seq_load<CF, VK>(set[u], p, rs, c + 2);
+      const int t = c * C + 16 * rb + li;  // this lane's token
+      const bool tok_ok = t < N;
+
+      // ---- X^T = S'^T K^T, Z^T = S'^T Q^T (rows n, columns: this row block) ----
+      f32x4 X[CF::TW], Z[CF::TW];
+#pragma unroll
+      for (int b2 = 0; b2 < CF::TW; ++b2) {
+        X[b2] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        Z[b2] = (f32x4){0.f, 0.f, 0.f, 0.f};
       }
-      lds_store4(sm.St + (16 * ct + li) * CF::QLD + 16 * tf + 4 * lg, Sacc[a][0],
-                 Sacc[a][1], Sacc[a][2], Sacc[a][3]);
+#pragma unroll
+      for (int ks = 0; ks < CF::KSD; ++ks) {
+        Frag<T> kf, qf;
+        lds_frag(kf, tl.K + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
+        lds_frag(qf, tl.Q + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
+#pragma unroll
+        for (int b2 = 0; b2 < CF::TW; ++b2) {
+          Frag<T> sf;
+          lds_frag(sf, sm.St + (16 * (ct0 + b2) + li) * CF::QLD + 32 * ks + 8 * lg);
+          mma(X[b2], sf, kf);
+          mma(Z[b2], sf, qf);
+        }
+      }
+      // ---- Y = V - X: lane holds columns 16 ct + 4 lg + r of token t ----
+#pragma unroll
+      for (int b2 = 0; b2 < CF::TW; ++b2)
+        lds_store4(sm.Ys + (16 * rb + li) * CF::YLD + 16 * (ct0 + b2) + 4 * lg,
+                   vset[u][b2][0] - X[b2][0], vset[u][b2][1] - X[b2][1],
+                   vset[u][b2][2] - X[b2][2], vset[u][b2][3] - X[b2][3]);
+      load_v(vset[u], c + 2);
+      __syncthreads();
+
+      // ---- O^T = Z^T + Y^T R^T (keys j <= this row block) ----
+#pragma unroll
+      for (int ks = 0; ks < CF::KSC; ++ks) {
+        if (32 * ks > 16 * rb + 15) continue;
+        Frag<T> rf;
+        lds_frag(rf, tl.R + (16 * rb + li) * CF::TLD + 32 * ks + 8 * lg);
+#pragma unroll
+        for (int b2 = 0; b2 < CF::TW; ++b2) {
+          Frag<T> yf;
+          lds_frag_tr(yf, sm.Ys, CF::YLD, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4,
+                      16 * (ct0 + b2), li);
+          mma(Z[b2], yf, rf);
+        }
+      }
+#pragma unroll
+      for (int b2 = 0; b2 < CF::TW; ++b2) {
+        const int col = n0 + 16 * (ct0 + b2) + 4 * lg;
+        if constexpr (VK) {
+          buf_store4_nt(rs[4],
+                        tok_ok && col < dv ? (uint32_t)(((size_t)t * dv + col) * sizeof(T)) : kOOB,
+                        Z[b2], (T *)nullptr);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool oke = tok_ok && col + e < dv;
+            buf_store1(rs[4], oke ? (uint32_t)(((size_t)t * dv + col + e) * sizeof(T)) : kOOB,
+                       from_f32<T>(Z[b2][e]));
+          }
+        }
+      }
+      // ---- S+ = S- + Wt Y for this wave's state rows; T-precision copy ----
+#pragma unroll
+      for (int ks = 0; ks < CF::KSC; ++ks) {
+        Frag<T> wf[CF::FPW];
+#pragma unroll
+        for (int a = 0; a < CF::FPW; ++a)
+          lds_frag(wf[a], tl.Wt + (16 * (wv * CF::FPW + a) + li) * CF::TLD + 32 * ks + 8 * lg);
+#pragma unroll
+        for (int c2 = 0; c2 < CF::NCT; ++c2) {
+          Frag<T> yf;
+          lds_frag_tr(yf, sm.Ys, CF::YLD, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * c2, li);
+#pragma unroll
+          for (int a = 0; a < CF::FPW; ++a) mma(Sacc[a][c2], wf[a], yf);
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < CF::FPW; ++a)
+#pragma unroll
+        for (int c2 = 0; c2 < CF::NCT; ++c2)
+          lds_store4(sm.St + (16 * c2 + li) * CF::QLD + 16 * (wv * CF::FPW + a) + 4 * lg,
+                     Sacc[a][c2][0], Sacc[a][c2][1], Sacc[a][c2][2], Sacc[a][c2][3]);
+      // chunk c + 1's tiles into the other buffer (last read in chunk c - 1)
+      seq_commit<CF>(set[u ^ 1], sm.tile[u ^ 1]);
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   if (p.S_out) {
     float *So = p.S_out + (size_t)bh * d * dv;
 #pragma unroll
-    for (int a = 0; a < CF::FPW; ++a) {
-      const int tf = rb * CF::FPW + a;
+    for (int a = 0; a < CF::FPW; ++a)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int f = 16 * tf + 4 * lg + r;
-        if (f < d && ncol < dv) So[(size_t)f * dv + ncol] = Sacc[a][r];
+      for (int c = 0; c < CF::NCT; ++c) {
+        const int n = n0 + 16 * c + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int f = 16 * (wv * CF::FPW + a) + 4 * lg + r;
+          if (f < d && n < dv) So[(size_t)f * dv + n] = Sacc[a][c][r];
+        }
       }
-    }
   }
 }
 
 template <class CF, bool VK>
 hipError_t run_vk(const PrefillParams &p, hipStream_t s) {
-  static_assert(sizeof(SmemPrep<CF>) <= 160 * 1024, "LDS budget (prep)");
+  static_assert(sizeof(SmemPrep<CF>) <= 64 * 1024, "LDS budget (prep)");
   static_assert(sizeof(SmemSeq<CF>) <= 160 * 1024, "LDS budget (seq)");
   const int nch = (p.N + CF::C - 1) / CF::C;
   prof_begin(s);
-  hipLaunchKernelGGL((prep_kernel<CF, VK>), dim3(nch, p.BH), dim3(kPrepThreads), 0, s, p);
+  hipLaunchKernelGGL((prep_kernel<CF, VK>), dim3(nch, p.BH), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   prof_end("delta_prep", s);
   const int nsl = (p.dv + CF::W - 1) / CF::W;
   const int xcd_map = (p.BH % kXcds) == 0;
   prof_begin(s);
-  hipLaunchKernelGGL((seq_kernel<CF, VK>), dim3(p.BH * nsl), dim3(CF::NT), 0, s, p, nsl,
+  hipLaunchKernelGGL((seq_kernel<CF, VK>), dim3(p.BH * nsl), dim3(kThreads), 0, s, p, nsl,
                      xcd_map);
   e = hipGetLastError();
   if (e == hipSuccess) prof_end("delta_seq", s);
@@ -577,8 +666,8 @@ hipError_t run(const PrefillParams &p, hipStream_t s) {
   return p.vec_ok ? run_vk<CF, true>(p, s) : run_vk<CF, false>(p, s);
 }
 
-// bf16: 64-token chunks, 16-column slices (4 waves); fp32: 32-token chunks,
-// 32-column slices (4 waves), so that the fp32 tiles fit in LDS.
+// bf16: 64-token chunks, 16-column slices; fp32: 32-token chunks,
+// 32-column slices.
 using DB64 = DCfg<bf16, 64, 64, 16>;
 using DB128 = DCfg<bf16, 128, 64, 16>;
 using DF64 = DCfg<float, 64, 32, 32>;
@@ -586,12 +675,11 @@ using DF128 = DCfg<float, 128, 32, 32>;
 
 }  // namespace
 
-int delta_chunk_len(bool bf16_io) { return bf16_io ? DB64::C : DF64::C; }
-
-size_t delta_workspace_bytes(int BH, int N, bool bf16_io) {
-  const int C = delta_chunk_len(bf16_io);
+size_t delta_workspace_bytes(int BH, int N, int d, bool bf16_io) {
+  const int C = bf16_io ? DB64::C : DF64::C;
+  const size_t DK = d <= 64 ? 64 : 128;
   const size_t nch = ((size_t)N + C - 1) / C;
-  return (size_t)BH * nch * 2 * C * C * (bf16_io ? 2 : 4);
+  return (size_t)BH * nch * (DK * C + (size_t)C * C) * (bf16_io ? 2 : 4);
 }
 
 hipError_t launch_delta_prefill(const PrefillParams &p, bool bf16_io, hipStream_t s) {
