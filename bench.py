@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5],
+                    help="3 runs the decode-step loop alone")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -59,17 +60,215 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five "
                          "times (a calibration point for hardware byte counters)")
+    ap.add_argument("--pmc-summary", metavar="DIR", default=None,
+                    help="only summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs "
+                         "kept under DIR/{fetch,write,copy_fetch,copy_write} for "
+                         "--workload as markdown (no GPU needed)")
+    ap.add_argument("--stats-summary", metavar="DIR", default=None,
+                    help="only summarise a rocprofv3 --kernel-trace --stats run "
+                         "kept under DIR as markdown (no GPU needed)")
     return ap.parse_args()
 
 
 def copy_probe(torch, mib):
+    """Five device copies of MIB MiB (runtime blit kernel) and five
+    elementwise passes b = a * 1 (16-byte vector loads and stores): each
+    reads and writes exactly MIB MiB, a known size for scaling counters."""
     n = mib * 1024 * 1024 // 4
     a = torch.ones(n, device="cuda")
     b = torch.empty_like(a)
     for _ in range(5):
         b.copy_(a)
+    for _ in range(5):
+        torch.mul(a, 1.0, out=b)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n * 4, "copies": 5}), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Hardware byte counters.  rocprofv3 runs of this script under
+# --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch), one counter per
+# run, plus the same two counters over --copy-probe, are condensed by
+# --pmc-summary into a markdown table whose last lines are machine-readable
+# records.  A record is tied to a hash of the kernel's source files; the
+# benchmark reports a kernel's traffic only while that hash still matches.
+
+CSRC = os.path.join(ROOT, "causal_linear_attention_attn_amd", "csrc")
+KERNEL_SRC = {
+    "linear_chunk": "la_prefill_linear.hip", "linear_summary": "la_prefill_linear.hip",
+    "linear_scan": "la_prefill_linear.hip", "delta_prep": "la_prefill_delta.hip",
+    "delta_seq": "la_prefill_delta.hip", "linear_decode": "la_decode.hip",
+    "delta_decode": "la_decode.hip",
+}
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_PROBE_MIB = 256
+
+
+def kernel_src_hash(kname):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in (KERNEL_SRC[kname], "la_common.hpp", "la_internal.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def library_kernel_name(raw):
+    """Name the library's own timer uses for a rocprofv3 kernel name
+    (mangled or demangled), or None for kernels that are not ours."""
+    if "la" not in raw:
+        return None
+    for fn, name in (("chunk_kernel", "linear_chunk"), ("summary_kernel", "linear_summary"),
+                     ("scan_kernel", "linear_scan"), ("prep_kernel", "delta_prep"),
+                     ("seq_kernel", "delta_seq")):
+        if fn in raw:
+            return name
+    if "decode_kernel" in raw:
+        delta = "Lb1E" in raw or ", true>" in raw
+        return "delta_decode" if delta else "linear_decode"
+    return None
+
+
+def _counter_rows(path):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, counter, keyfn):
+    """Average KiB per dispatch of COUNTER for each key."""
+    tot, disp = {}, {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        k = keyfn(r["Kernel_Name"])
+        if k is None:
+            continue
+        tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+        disp.setdefault(k, set()).add(r["Dispatch_Id"])
+    return {k: (tot[k] / len(disp[k]), len(disp[k])) for k in tot}
+
+
+def pmc_commands(d, wid):
+    run = f"python3 bench.py {bench_args_for_counters(wid)}"
+    cp = f"python3 bench.py --copy-probe {COPY_PROBE_MIB}"
+    return [
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o fetch -- {run}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o write -- {run}",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/copy_fetch -o cf -- {cp}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/copy_write -o cw -- {cp}",
+        f"python3 bench.py --pmc-summary {d} --workload {wid}",
+    ]
+
+
+def bench_args_for_counters(wid):
+    if wid == 3:
+        return "--workload 3 --decode-steps 16"
+    return f"--workload {wid} --steps 5 --warmup 2 --no-decode --no-extra --no-cpu-baseline"
+
+
+def pmc_summary(d, wid):
+    """Markdown table of HBM bytes per dispatch for the library's kernels of
+    one workload, scaled by the counters' reading of a copy of known size."""
+    from causal_linear_attention_attn_amd import inputs
+
+    w = inputs.WORKLOADS[wid]
+    probe = COPY_PROBE_MIB * 1024.0  # KiB read and written by each copy
+
+    def copy_key(raw):
+        if "copyBuffer" in raw:
+            return "blit copy"
+        if "MulFunctor" in raw:
+            return "elementwise b = a * 1"
+        return None
+
+    cf = _per_dispatch(_counter_rows(os.path.join(d, "copy_fetch")), "FETCH_SIZE", copy_key)
+    cw = _per_dispatch(_counter_rows(os.path.join(d, "copy_write")), "WRITE_SIZE", copy_key)
+    ref = "elementwise b = a * 1" if "elementwise b = a * 1" in cf else "blit copy"
+    f_fac, w_fac = probe / cf[ref][0], probe / cw[ref][0]
+    kf = _per_dispatch(_counter_rows(os.path.join(d, "fetch")), "FETCH_SIZE",
+                       library_kernel_name)
+    kw = _per_dispatch(_counter_rows(os.path.join(d, "write")), "WRITE_SIZE",
+                       library_kernel_name)
+    alg = None
+    if wid != 3:
+        alg = w.B * w.H * w.N * bytes_per_head_token(w)
+    out = [f"# HBM traffic per dispatch: {w.name}", "",
+           "Commands (repository root, TMPDIR=/tmp, one counter per run):", ""]
+    out += ["    " + c for c in pmc_commands(d, wid)]
+    out += ["", f"Calibration: each probe copy reads and writes {COPY_PROBE_MIB} MiB "
+            f"({probe:.0f} KiB).", "",
+            "| probe kernel | FETCH_SIZE KiB | WRITE_SIZE KiB |", "|---|---|---|"]
+    for k in sorted(cf):
+        out.append(f"| {k} | {cf[k][0]:.0f} | {cw.get(k, (float('nan'),))[0]:.0f} |")
+    out += ["", f"Scale factors (from the {ref} probe): FETCH_SIZE x {f_fac:.3f}, "
+            f"WRITE_SIZE x {w_fac:.3f}.", "",
+            "| kernel | dispatches | FETCH KiB | WRITE KiB | scaled read MB | "
+            "scaled write MB | scaled total MB | algorithmic MB |",
+            "|---|---|---|---|---|---|---|---|"]
+    recs = []
+    for k in sorted(kf):
+        fk, n = kf[k]
+        wk = kw.get(k, (float("nan"), 0))[0]
+        rd, wr = fk * 1024 * f_fac, wk * 1024 * w_fac
+        a = alg if k in ("linear_chunk", "delta_seq") else None
+        if wid == 3 and k == "linear_decode":
+            a = decode_step_bytes(w)
+        out.append(f"| {k} | {n} | {fk:.0f} | {wk:.0f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
+                   f"{(rd + wr) / 1e6:.1f} | {'' if a is None else f'{a / 1e6:.1f}'} |")
+        recs.append({"workload": w.name, "kernel": k, "src": kernel_src_hash(k),
+                     "read_bytes": rd, "write_bytes": wr, "traffic_bytes": rd + wr})
+    out += ["", "Machine-readable records (bench.py reports `traffic` from these while "
+            "the kernel source hash matches):", ""]
+    out += [f"<!-- traffic {json.dumps(r)} -->" for r in recs]
+    print("\n".join(out))
+
+
+def stats_summary(d):
+    """Markdown table of the library's kernels from a rocprofv3 --stats run."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    out = ["| kernel (library name) | rocprofv3 name | calls | average us | min us | "
+           "max us |", "|---|---|---|---|---|---|"]
+    with open(files[0], newline="") as fh:
+        for r in csv.DictReader(fh):
+            k = library_kernel_name(r["Name"])
+            if k is None:
+                continue
+            out.append(f"| {k} | `{r['Name'][:90]}` | {r['Calls']} | "
+                       f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                       f"{float(r['MaxNs']) / 1e3:.2f} |")
+    print("\n".join(out))
+
+
+def traffic_record(wname, kname):
+    """HBM bytes per launch for KNAME on workload WNAME from the committed
+    counter summaries, or None when there is none for the current source."""
+    import glob
+
+    want = kernel_src_hash(kname)
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(f) as fh:
+            for line in fh:
+                if not line.startswith("<!-- traffic "):
+                    continue
+                r = json.loads(line[len("<!-- traffic "):line.rindex("-->")])
+                if r["workload"] == wname and r["kernel"] == kname and r["src"] == want:
+                    return r["traffic_bytes"], os.path.basename(f)
+    return None, None
 
 
 class KernelTimer:
@@ -186,13 +385,15 @@ def prefill_summary(w, kern, dt):
     kname, kms = dominant(kern)
     achieved = bpl / (kms * 1e-3) / 1e9
     tflops = fpl / (kms * 1e-3) / 1e12
+    traffic, tsrc = traffic_record(w.name, kname)
     return {
         "tokens_per_s": w.B * w.N / dt, "ms_per_step": dt * 1e3,
         "kernels_ms": kern,
         "roofline": {"kernel": kname, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "bytes_per_launch": bpl, "kernel_ms": kms},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_profile": tsrc, "bytes_per_launch": bpl,
+                     "kernel_ms": kms},
         "mfma": {"kernel": kname, "flops_per_launch": fpl,
                  "achieved_tflops": tflops, "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac": tflops / BF16_PEAK_TFLOPS},
@@ -214,6 +415,14 @@ def bench_workload(la, lib, torch, w, steps, warmup):
     out["workload"] = w.name
     out["workspace_bytes"] = ws_bytes
     return out, x, o
+
+
+def decode_step_bytes(w):
+    """Algorithmic bytes of one decode step: state S and z read and written
+    once; q, k, v read and o written once."""
+    e = w.dtype.itemsize
+    nbh = w.B * w.H
+    return 2 * nbh * (w.d * w.dv + w.d) * 4 + nbh * (2 * w.d + 2 * w.dv) * e
 
 
 def bench_decode(la, lib, torch, nsteps, warmup=8):
@@ -240,9 +449,9 @@ def bench_decode(la, lib, torch, nsteps, warmup=8):
         times = kt.collect()
     ks = times.get("linear_decode", [])
     kavg = sum(ks) / len(ks) if ks else float("nan")
-    # state S and z read and written once; q, k, v read, o written (bf16)
-    step_bytes = 2 * (S.numel() + z.numel()) * 4 + (3 * B * H * d + B * H * dv) * 2
+    step_bytes = decode_step_bytes(w)
     dt = (t1 - t0) / nsteps
+    traffic, tsrc = traffic_record(w.name, "linear_decode")
     return {
         "workload": w.name, "steps": nsteps,
         "steps_per_s": 1.0 / dt, "tokens_per_s": B / dt, "ms_per_step": dt * 1e3,
@@ -251,7 +460,7 @@ def bench_decode(la, lib, torch, nsteps, warmup=8):
                      "achieved": step_bytes / (kavg * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": step_bytes / (kavg * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": traffic, "traffic_profile": tsrc},
         "loop_GBs": step_bytes / dt / 1e9,
     }
 
@@ -294,6 +503,12 @@ def main():
               "heads shard across GPUs with no communication, so each GPU "
               "would run this same single-GPU step on its share.", file=sys.stderr)
         sys.exit(2)
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.workload)
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary)
+        return
     import torch
 
     import causal_linear_attention_attn_amd as la
@@ -306,6 +521,17 @@ def main():
         copy_probe(torch, args.copy_probe)
         return
     lib = _lib.load()
+    if args.workload == 3:
+        dec = bench_decode(la, lib, torch, args.decode_steps)
+        print(json.dumps({
+            "metric": "decode state GB/s vs HBM peak", "value": dec["tokens_per_s"],
+            "unit": "tokens/s", "n_gpus": 1, "steps": dec["steps"], "warmup": 8,
+            "ms_per_step": dec["ms_per_step"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded normal draws; see inputs.py)",
+            "config": {"workload": dec["workload"]}, "roofline": dec["roofline"],
+            "decode": dec}), flush=True)
+        return
     w = inputs.WORKLOADS[args.workload]
     res, x, o = bench_workload(la, lib, torch, w, args.steps, args.warmup)
     line = {

@@ -25,10 +25,13 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
-// elu(x)+1 with alpha 1: x+1 above zero, e^x at or below (no large positive
-// exponent is ever formed).
+// elu(x)+1 with alpha 1: x+1 above zero, e^x at or below, written as
+// max(x + 1, e^-|x|).  The two agree exactly in real arithmetic: for x <= 0,
+// e^x >= 1 + x; for x > 0, e^-x < 1 < 1 + x.  No positive exponent is
+// formed, and the form needs no compare-and-select (the sign and absolute
+// value fold into the multiply ahead of the exponential).
 __device__ __forceinline__ float phi_elu1(float x) {
-  return x > 0.f ? x + 1.f : __expf(x);
+  return fmaxf(x + 1.f, __expf(-fabsf(x)));
 }
 
 // ---------------------------------------------------------------------------

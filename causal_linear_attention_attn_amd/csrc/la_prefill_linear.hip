@@ -191,19 +191,17 @@ __device__ __forceinline__ void prefetch(ChunkRegs<CF> &R, const PrefillParams &
 // Registers -> LDS: phi(q) rows, weighted phi(k) rows, v rows.  Keys past
 // the chunk get weight 0 and feature columns past d are zeroed (phi(0) = 1
 // would otherwise count them); queries need no mask (their padded features
-// meet zero keys and zero state rows).
-template <class CF, bool WITH_Q>
-__device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type *Qs,
-                                       typename CF::type *Ks, typename CF::type *Vs,
-                                       const float *pw, const PrefillParams &p, int Lc) {
+// meet zero keys and zero state rows).  The feature map and the column mask
+// are uniform per launch and taken as branches, so the common case carries
+// no per-element selects; key weights are 1 for a full chunk without decay.
+template <class CF, bool WITH_Q, bool ELU>
+__device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R, typename CF::type *Qs,
+                                            typename CF::type *Ks, const float *pw,
+                                            const PrefillParams &p, int Lc) {
   using T = typename CF::type;
-  using V = typename CF::vec;
   constexpr int VEC = CF::VEC;
-  const bool elu = p.fmap != 0;
-  const bool colmask = p.d < CF::DK;
-  // key weights gamma^(Lc-1-j), 0 past the chunk: all 1 for a full chunk
-  // without decay
   const bool weighted = p.gamma != nullptr || Lc < CF::C;
+  const bool colmask = p.d < CF::DK;  // feature columns past d
   const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
   const int col0 = qcb * VEC;
 #pragma unroll
@@ -214,31 +212,43 @@ __device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float xq = to_f32(R.q[r][e]);
-        x[e] = elu ? phi_elu1(xq) : xq;
+        x[e] = ELU ? phi_elu1(xq) : xq;
       }
       lds_store_n<T, VEC>(Qs + row * CF::QLD + col0, x);
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       const float xk = to_f32(R.k[r][e]);
-      x[e] = elu ? phi_elu1(xk) : xk;
+      x[e] = ELU ? phi_elu1(xk) : xk;
     }
-    if (weighted) {
-      const float w = row < Lc ? pw[Lc - 1 - row] : 0.f;
+    // key weights gamma^(Lc-1-j), 0 past the chunk
+    const float w = !weighted ? 1.f : row < Lc ? pw[Lc - 1 - row] : 0.f;
+    if (__builtin_expect(colmask, 0)) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) x[e] = col0 + e < p.d ? x[e] * w : 0.f;
+      lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
+    } else {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) x[e] *= w;
+      lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
     }
-    if (colmask) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) x[e] = col0 + e < p.d ? x[e] : 0.f;
-    }
-    lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
   }
+}
+
+template <class CF, bool WITH_Q>
+__device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type *Qs,
+                                       typename CF::type *Ks, typename CF::type *Vs,
+                                       const float *pw, const PrefillParams &p, int Lc) {
+  using V = typename CF::vec;
+  if (p.fmap != 0)
+    commit_rows<CF, WITH_Q, true>(R, Qs, Ks, pw, p, Lc);
+  else
+    commit_rows<CF, WITH_Q, false>(R, Qs, Ks, pw, p, Lc);
   const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
 #pragma unroll
   for (int r = 0; r < CF::RV; ++r) {
     const int row = vrg * CF::RV + r;
-    *reinterpret_cast<V *>(Vs + row * CF::VTLD + vcb * VEC) = R.v[r];
+    *reinterpret_cast<V *>(Vs + row * CF::VTLD + vcb * CF::VEC) = R.v[r];
   }
 }
 
@@ -291,26 +301,29 @@ __device__ __forceinline__ void state_update(f32x4 (&Sacc)[CF::FPW][CF::TPW],
   }
 }
 
-// T-precision copy of scale * [S | z], transposed: St[n][f] = S[f][n].
+// Scale the state by gamma^L of the chunk about to be read (decay only) and
+// write its T-precision copy, transposed: St[n][f] = S[f][n].  Scaling the
+// accumulator itself means the chunk's state update then only adds KW^T V.
 template <class CF>
-__device__ __forceinline__ void write_state_copy(typename CF::type *St,
-                                                 const f32x4 (&Sacc)[CF::FPW][CF::TPW],
-                                                 float scale, bool decay, int wv, int li,
-                                                 int lg) {
+__device__ __forceinline__ void rescale_and_copy_state(typename CF::type *St,
+                                                       f32x4 (&Sacc)[CF::FPW][CF::TPW],
+                                                       float scale, bool decay, int wv,
+                                                       int li, int lg) {
+  if (decay) {
+#pragma unroll
+    for (int a = 0; a < CF::FPW; ++a)
+#pragma unroll
+      for (int b = 0; b < CF::TPW; ++b) Sacc[a][b] *= scale;
+  }
 #pragma unroll
   for (int a = 0; a < CF::FPW; ++a) {
     const int tf = srow<CF>(wv, a);
 #pragma unroll
     for (int b = 0; b < CF::TPW; ++b) {
       const int tn = scol<CF>(wv, b);
-      if (tn < CF::NCT) {
-        typename CF::type *dst = St + (16 * tn + li) * CF::QLD + 16 * tf + 4 * lg;
-        if (decay)
-          lds_store4(dst, scale * Sacc[a][b][0], scale * Sacc[a][b][1],
-                     scale * Sacc[a][b][2], scale * Sacc[a][b][3]);
-        else
-          lds_store4(dst, Sacc[a][b][0], Sacc[a][b][1], Sacc[a][b][2], Sacc[a][b][3]);
-      }
+      if (tn < CF::NCT)
+        lds_store4(St + (16 * tn + li) * CF::QLD + 16 * tf + 4 * lg, Sacc[a][b][0],
+                   Sacc[a][b][1], Sacc[a][b][2], Sacc[a][b][3]);
     }
   }
 }
@@ -372,6 +385,88 @@ __device__ __forceinline__ void fill_powers(float *pw, float log2g) {
   for (int m = threadIdx.x; m <= CF::C; m += CF::NT) pw[m] = exp2f((float)m * log2g);
 }
 
+// Outputs of one chunk for one output role: query row block RB (compile-time,
+// so the causal structure of the score tiles costs no branches or selects)
+// and column group cg of the value tiles; normalised rows go to the staging
+// tile Os.
+template <class CF, int RB>
+__device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillParams &p, int Lc,
+                                              int cg, int li, int lg) {
+  using T = typename CF::type;
+  const int irow = 16 * RB + li;  // this lane's query row
+  // ---- scores, transposed: at[tj][r] = phi(q_i) . kw_j, i = irow,
+  //      j = 16 tj + 4 lg + r (lower triangle only) ----
+  Frag<T> qf[CF::KSD];
+#pragma unroll
+  for (int ks = 0; ks < CF::KSD; ++ks)
+    lds_frag(qf[ks], sm.Qs + irow * CF::QLD + 32 * ks + 8 * lg);
+  f32x4 at[CF::NRB];
+#pragma unroll
+  for (int tj = 0; tj < CF::NRB; ++tj) {
+    at[tj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (tj <= RB) {
+#pragma unroll
+      for (int ks = 0; ks < CF::KSD; ++ks) {
+        Frag<T> kf;
+        lds_frag(kf, sm.Ks + (16 * tj + li) * CF::QLD + 32 * ks + 8 * lg);
+        mma(at[tj], kf, qf[ks]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) at[RB][r] = 4 * lg + r <= li ? at[RB][r] : 0.f;
+
+  // ---- O'^T = (gamma^L [S | z])^T Phi_q^T + [V | 1]^T A^T ----
+  f32x4 acc[CF::NPW], accd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int a = 0; a < CF::NPW; ++a) acc[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < CF::KSD; ++ks) {
+#pragma unroll
+    for (int a = 0; a < CF::NPW; ++a) {
+      Frag<T> sf;
+      lds_frag(sf, sm.St + (16 * (cg * CF::NPW + a) + li) * CF::QLD + 32 * ks + 8 * lg);
+      mma(acc[a], sf, qf[ks]);
+    }
+    Frag<T> zf;
+    lds_frag(zf, sm.St + (CF::DV + li) * CF::QLD + 32 * ks + 8 * lg);
+    mma(accd, zf, qf[ks]);
+  }
+  Frag<T> ones;
+  frag_fill(ones, 1.f);
+#pragma unroll
+  for (int pp = 0; pp < CF::NRB / 2; ++pp) {
+    if (2 * pp <= RB) {
+      // slots 0..3: keys 32 pp + 4 lg + e; slots 4..7: 32 pp + 16 + 4 lg + e
+      Frag<T> af;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        frag_set(af, e, at[2 * pp][e]);
+        frag_set(af, 4 + e, at[2 * pp + 1][e]);
+      }
+      const int tlo = 32 * pp + 4 * lg, thi = tlo + 16;
+#pragma unroll
+      for (int a = 0; a < CF::NPW; ++a) {
+        Frag<T> vf;
+        lds_frag_tr(vf, sm.Vs, CF::VTLD, tlo, thi, 16 * (cg * CF::NPW + a), li);
+        mma(acc[a], vf, af);
+      }
+      mma(accd, ones, af);
+    }
+  }
+
+  // ---- normalise: lane holds columns 16 tn + 4 lg + r of token irow ----
+  {
+    const float den = accd[0] + p.eps * sm.pw[max(Lc - 1 - irow, 0)];
+    const float rd = __builtin_amdgcn_rcpf(den);
+#pragma unroll
+    for (int a = 0; a < CF::NPW; ++a)
+      lds_store4(sm.Os + irow * CF::VLD + 16 * (cg * CF::NPW + a) + 4 * lg,
+                 acc[a][0] * rd, acc[a][1] * rd, acc[a][2] * rd, acc[a][3] * rd);
+  }
+
+}
+
 template <class CF, bool VK>
 __global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p) {
   using T = typename CF::type;
@@ -406,11 +501,10 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p)
   prefetch<CF, true, VK>(R, p, hb, t_begin, min(CF::C, N - t_begin));
   fill_powers<CF>(sm.pw, decay ? log2f(p.gamma[bh % p.H]) : 0.f);
   __syncthreads();
-  write_state_copy<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - t_begin)], decay, wv, li, lg);
+  rescale_and_copy_state<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - t_begin)], decay, wv, li,
+                             lg);
 
   const int rb = wv % CF::NRB, cg = wv / CF::NRB;  // output role
-  const int irow = 16 * rb + li;                    // this lane's query row
-
   for (int c0 = t_begin; c0 < t_end; c0 += CF::C) {
     const int Lc = min(CF::C, N - c0);
     commit<CF, true>(R, sm.Qs, sm.Ks, sm.Vs, sm.pw, p, Lc);
@@ -418,87 +512,26 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p)
       prefetch<CF, true, VK>(R, p, hb, c0 + CF::C, min(CF::C, N - c0 - CF::C));
     __syncthreads();
 
-    // ---- scores, transposed: at[tj][r] = phi(q_i) . kw_j, i = irow,
-    //      j = 16 tj + 4 lg + r (lower triangle only) ----
-    Frag<T> qf[CF::KSD];
-#pragma unroll
-    for (int ks = 0; ks < CF::KSD; ++ks)
-      lds_frag(qf[ks], sm.Qs + irow * CF::QLD + 32 * ks + 8 * lg);
-    f32x4 at[CF::NRB];
-#pragma unroll
-    for (int tj = 0; tj < CF::NRB; ++tj) {
-      at[tj] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (tj <= rb) {
-#pragma unroll
-        for (int ks = 0; ks < CF::KSD; ++ks) {
-          Frag<T> kf;
-          lds_frag(kf, sm.Ks + (16 * tj + li) * CF::QLD + 32 * ks + 8 * lg);
-          mma(at[tj], kf, qf[ks]);
-        }
+    if constexpr (CF::NRB == 2) {
+      if (rb == 0) chunk_outputs<CF, 0>(sm, p, Lc, cg, li, lg);
+      else chunk_outputs<CF, 1>(sm, p, Lc, cg, li, lg);
+    } else {
+      static_assert(CF::NRB == 4, "row blocks per chunk");
+      switch (rb) {
+        case 0: chunk_outputs<CF, 0>(sm, p, Lc, cg, li, lg); break;
+        case 1: chunk_outputs<CF, 1>(sm, p, Lc, cg, li, lg); break;
+        case 2: chunk_outputs<CF, 2>(sm, p, Lc, cg, li, lg); break;
+        default: chunk_outputs<CF, 3>(sm, p, Lc, cg, li, lg); break;
       }
-    }
-#pragma unroll
-    for (int tj = 0; tj < CF::NRB; ++tj)
-      if (tj == rb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) at[tj][r] = 4 * lg + r <= li ? at[tj][r] : 0.f;
-      }
-
-    // ---- O'^T = (gamma^L [S | z])^T Phi_q^T + [V | 1]^T A^T ----
-    f32x4 acc[CF::NPW], accd = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int a = 0; a < CF::NPW; ++a) acc[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < CF::KSD; ++ks) {
-#pragma unroll
-      for (int a = 0; a < CF::NPW; ++a) {
-        Frag<T> sf;
-        lds_frag(sf, sm.St + (16 * (cg * CF::NPW + a) + li) * CF::QLD + 32 * ks + 8 * lg);
-        mma(acc[a], sf, qf[ks]);
-      }
-      Frag<T> zf;
-      lds_frag(zf, sm.St + (CF::DV + li) * CF::QLD + 32 * ks + 8 * lg);
-      mma(accd, zf, qf[ks]);
-    }
-    Frag<T> ones;
-    frag_fill(ones, 1.f);
-#pragma unroll
-    for (int pp = 0; pp < CF::NRB / 2; ++pp) {
-      if (2 * pp <= rb) {
-        // slots 0..3: keys 32 pp + 4 lg + e; slots 4..7: 32 pp + 16 + 4 lg + e
-        Frag<T> af;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          frag_set(af, e, at[2 * pp][e]);
-          frag_set(af, 4 + e, at[2 * pp + 1][e]);
-        }
-        const int tlo = 32 * pp + 4 * lg, thi = tlo + 16;
-#pragma unroll
-        for (int a = 0; a < CF::NPW; ++a) {
-          Frag<T> vf;
-          lds_frag_tr(vf, sm.Vs, CF::VTLD, tlo, thi, 16 * (cg * CF::NPW + a), li);
-          mma(acc[a], vf, af);
-        }
-        mma(accd, ones, af);
-      }
-    }
-
-    // ---- normalise: lane holds columns 16 tn + 4 lg + r of token irow ----
-    {
-      const float den = accd[0] + p.eps * sm.pw[max(Lc - 1 - irow, 0)];
-      const float rd = 1.f / den;
-#pragma unroll
-      for (int a = 0; a < CF::NPW; ++a)
-        lds_store4(sm.Os + irow * CF::VLD + 16 * (cg * CF::NPW + a) + 4 * lg,
-                   acc[a][0] * rd, acc[a][1] * rd, acc[a][2] * rd, acc[a][3] * rd);
     }
 
     // ---- carry the state across the chunk ----
-    state_update<CF>(Sacc, sm.Ks, sm.Vs, sm.pw[Lc], decay, wv, li, lg);
+    // (the accumulator already carries gamma^Lc: scaled before the copy)
+    state_update<CF>(Sacc, sm.Ks, sm.Vs, 1.f, false, wv, li, lg);
     __syncthreads();
     if (c0 + CF::C < t_end)
-      write_state_copy<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - c0 - CF::C)], decay, wv, li,
-                           lg);
+      rescale_and_copy_state<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - c0 - CF::C)], decay, wv,
+                                 li, lg);
     // 16-byte row stores of the output tile
     {
       const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
