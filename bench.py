@@ -12,8 +12,11 @@ argument marshalling is not timed); `value` is prefill tokens/s, B*N tokens
 per step.  Alongside:
   roofline      the dominant kernel against HBM peak: algorithmic bytes per
                 launch (q, k, v read once, o written once) over its average
-                duration, from HIP events the library records around each of
-                its kernels on the launch stream (eager run of the same step);
+                duration, from the HIP event pair the library hands to each
+                of its kernel dispatches (stamped at kernel start and end on
+                the launch stream; eager run of the same step); `traffic` is
+                the HBM bytes per launch from committed rocprofv3 byte-counter
+                summaries of the same kernel source, else null;
   mfma          the same kernel's chunk-form matrix flops against the bf16
                 dense matrix peak;
   decode        the decode-step loop (B=256 H=32 d=dv=128, state built by a
@@ -272,7 +275,8 @@ def traffic_record(wname, kname):
 
 
 class KernelTimer:
-    """HIP-event kernel durations recorded by the library itself."""
+    """Kernel durations from the HIP events the library hands to each of its
+    dispatches (start and end of the kernel itself)."""
 
     def __init__(self, lib):
         from causal_linear_attention_attn_amd import _lib

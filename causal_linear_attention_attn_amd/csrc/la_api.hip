@@ -41,7 +41,6 @@ std::mutex g_prof_mu;
 std::atomic<bool> g_prof_on{false};
 std::vector<ProfRec> g_recs;
 std::vector<hipEvent_t> g_pool;
-hipEvent_t g_pending = nullptr;
 constexpr size_t kMaxRecs = 65536;
 
 hipEvent_t take_event() {
@@ -64,37 +63,32 @@ void clear_log_locked() {
     g_pool.push_back(r.b);
   }
   g_recs.clear();
-  if (g_pending) g_pool.push_back(g_pending);
-  g_pending = nullptr;
 }
 }  // namespace
 
-void prof_begin(hipStream_t s) {
-  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+ProfSlot prof_slot() {
+  ProfSlot ps;
+  if (!g_prof_on.load(std::memory_order_relaxed)) return ps;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (g_recs.size() >= kMaxRecs) return;
-  if (g_pending) g_pool.push_back(g_pending);
-  g_pending = take_event();
-  if (g_pending && hipEventRecord(g_pending, s) != hipSuccess) {
-    (void)hipGetLastError();
-    g_pool.push_back(g_pending);
-    g_pending = nullptr;
+  if (g_recs.size() >= kMaxRecs) return ps;
+  ps.start = take_event();
+  ps.stop = ps.start ? take_event() : nullptr;
+  if (!ps.stop) {
+    if (ps.start) g_pool.push_back(ps.start);
+    ps.start = nullptr;
   }
+  return ps;
 }
 
-void prof_end(const char *name, hipStream_t s) {
-  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+void prof_commit(const char *name, ProfSlot ps, hipError_t launch_status) {
+  if (!ps.start) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_pending) return;
-  hipEvent_t e = take_event();
-  if (!e) return;
-  if (hipEventRecord(e, s) != hipSuccess) {
-    (void)hipGetLastError();
-    g_pool.push_back(e);
-    return;
+  if (launch_status == hipSuccess && g_prof_on.load(std::memory_order_relaxed)) {
+    g_recs.push_back({name, ps.start, ps.stop});
+  } else {
+    g_pool.push_back(ps.start);
+    g_pool.push_back(ps.stop);
   }
-  g_recs.push_back({name, g_pending, e});
-  g_pending = nullptr;
 }
 
 }  // namespace la

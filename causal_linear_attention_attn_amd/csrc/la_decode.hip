@@ -196,12 +196,8 @@ __global__ void copy_kernel(float *dst, const float *src, size_t n) {
 
 template <typename T, int VEC, bool DELTA>
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s) {
-  prof_begin(s);
-  hipLaunchKernelGGL((decode_kernel<T, VEC, DELTA>), dim3(p.BH),
-                     dim3(kDecThreads), 0, s, p);
-  const hipError_t e = hipGetLastError();
-  if (e == hipSuccess) prof_end(DELTA ? "delta_decode" : "linear_decode", s);
-  return e;
+  return launch_kernel(DELTA ? "delta_decode" : "linear_decode", decode_kernel<T, VEC, DELTA>,
+                       dim3(p.BH), dim3(kDecThreads), s, p);
 }
 
 }  // namespace

@@ -1,6 +1,7 @@
 // Host-side interface between the C ABI (la_api.hip) and the kernel files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -45,10 +46,30 @@ struct DecodeParams {
 
 int device_cu_count();  // cached per device
 
-// Kernel timing hooks (no-ops unless profiling is enabled): call prof_begin
-// before and prof_end after each kernel launch.
-void prof_begin(hipStream_t s);
-void prof_end(const char *name, hipStream_t s);
+// Kernel timing (off unless la_profile_enable turned it on).  A launch
+// through launch_kernel takes a pair of events from prof_slot and hands them
+// to the dispatch itself (hipExtLaunchKernel stamps them when the kernel
+// starts and ends, so launch latency is not counted); prof_commit files the
+// record under `name` if the launch succeeded.  Off, the slot is empty and
+// the launch is a plain hipLaunchKernelGGL.
+struct ProfSlot {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfSlot prof_slot();
+void prof_commit(const char *name, ProfSlot slot, hipError_t launch_status);
+
+template <typename... Args, typename F = void (*)(Args...)>
+hipError_t launch_kernel(const char *name, F kernel, dim3 grid, dim3 block, hipStream_t s,
+                         Args... args) {
+  const ProfSlot ps = prof_slot();
+  if (ps.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ps.start, ps.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  const hipError_t e = hipGetLastError();
+  prof_commit(name, ps, e);
+  return e;
+}
 
 LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16);
 hipError_t launch_linear_prefill(const PrefillParams &p, const LinearPlan &plan,

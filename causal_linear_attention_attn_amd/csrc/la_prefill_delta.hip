@@ -646,19 +646,13 @@ hipError_t run_vk(const PrefillParams &p, hipStream_t s) {
   static_assert(sizeof(SmemPrep<CF>) <= 64 * 1024, "LDS budget (prep)");
   static_assert(sizeof(SmemSeq<CF>) <= 160 * 1024, "LDS budget (seq)");
   const int nch = (p.N + CF::C - 1) / CF::C;
-  prof_begin(s);
-  hipLaunchKernelGGL((prep_kernel<CF, VK>), dim3(nch, p.BH), dim3(kThreads), 0, s, p);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_kernel("delta_prep", prep_kernel<CF, VK>, dim3(nch, p.BH),
+                               dim3(kThreads), s, p);
   if (e != hipSuccess) return e;
-  prof_end("delta_prep", s);
   const int nsl = (p.dv + CF::W - 1) / CF::W;
   const int xcd_map = (p.BH % kXcds) == 0;
-  prof_begin(s);
-  hipLaunchKernelGGL((seq_kernel<CF, VK>), dim3(p.BH * nsl), dim3(kThreads), 0, s, p, nsl,
-                     xcd_map);
-  e = hipGetLastError();
-  if (e == hipSuccess) prof_end("delta_seq", s);
-  return e;
+  return launch_kernel("delta_seq", seq_kernel<CF, VK>, dim3(p.BH * nsl), dim3(kThreads), s,
+                       p, nsl, xcd_map);
 }
 
 template <class CF>

@@ -633,25 +633,16 @@ template <class CF, bool VK>
 hipError_t run_vk(const PrefillParams &p, hipStream_t s) {
   static_assert(sizeof(SmemChunk<CF>) <= kLdsBytes, "LDS budget");
   if (p.nseg > 1) {
-    prof_begin(s);
-    hipLaunchKernelGGL((summary_kernel<CF, VK>), dim3(p.nseg - 1, p.BH), dim3(CF::NT),
-                       0, s, p);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_kernel("linear_summary", summary_kernel<CF, VK>,
+                                 dim3(p.nseg - 1, p.BH), dim3(CF::NT), s, p);
     if (e != hipSuccess) return e;
-    prof_end("linear_summary", s);
     const size_t rec = (size_t)p.d * p.dv + p.d;
-    prof_begin(s);
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)((rec + 255) / 256), p.BH), dim3(256), 0,
-                       s, p);
-    e = hipGetLastError();
+    e = launch_kernel("linear_scan", scan_kernel, dim3((unsigned)((rec + 255) / 256), p.BH),
+                      dim3(256), s, p);
     if (e != hipSuccess) return e;
-    prof_end("linear_scan", s);
   }
-  prof_begin(s);
-  hipLaunchKernelGGL((chunk_kernel<CF, VK>), dim3(p.nseg, p.BH), dim3(CF::NT), 0, s, p);
-  const hipError_t e = hipGetLastError();
-  if (e == hipSuccess) prof_end("linear_chunk", s);
-  return e;
+  return launch_kernel("linear_chunk", chunk_kernel<CF, VK>, dim3(p.nseg, p.BH), dim3(CF::NT),
+                       s, p);
 }
 
 template <class CF>
