@@ -17,9 +17,11 @@ Sources (cited by page title and section):
   [EAV]   "Efficient attention variants" (bailixisu.com): section 4 (kernel
           form, elu+1), section 5 (causal prefix form, write-then-read),
           5.1 (hand-worked example), 7.1 (RetNet decay), 7.3 (DeltaNet),
+          7.4 (Gated DeltaNet: scalar decay before the delta correction),
           section 10 (NumPy self-check: dense vs recurrent).
   [LIO3]  "LLM inference optimisation (3): Linear Attention" (wangyu.me):
-          'recurrent form of the summary', 'implementation', 'delta rule'.
+          'recurrent form of the summary', 'implementation', 'delta rule'
+          (with its gating variant).
   [TAR]   "Transformers Are RNNs" (myhz0606.com): epsilon in the
           denominator, multiplicative causal mask.
 
@@ -31,6 +33,9 @@ Readings where the pages disagree:
   * The delta rule uses the raw k and q (no feature map, no normaliser), the
     prediction is S^T k with S stored [r, dv], the gate scales the write, and
     the output is read from the updated state: o_t = S_t^T q_t.
+  * The optional decay alpha_t of the delta rule is a scalar per token and
+    head, applied to the old state before the prediction ([EAV] 7.4 warns
+    that the error must be taken on the decayed state).
 
 Parity pins live in tests/test_oracle.py; every function below is pinned
 there against printed values, closed forms or brute force.
@@ -170,7 +175,7 @@ def linear_quadratic(q, k, v, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1):
 # Gated DELTA rule (raw q, k; no normaliser)
 # ---------------------------------------------------------------------------
 
-def delta_step(S, q, k, v, g):
+def delta_step(S, q, k, v, g, alpha=None):
     """One token of the gated delta rule.
 
     [WILA] 5.2-5.3: predict what the state already returns for this key,
@@ -178,35 +183,45 @@ def delta_step(S, q, k, v, g):
         v_hat_t = S_{t-1}^T k_t            (S stored [r, dv])
         S_t     = S_{t-1} + g_t k_t (v_t - v_hat_t)^T
     The output is read from the updated state: o_t = S_t^T q_t.
-    S: [..., d, dv]; q, k: [..., d]; v: [..., dv]; g: [...].
+    With a scalar decay alpha_t ([EAV] 7.4, Gated DeltaNet; [LIO3] 'delta
+    rule', gating): the old state is decayed first and the prediction is
+    taken from the decayed state,
+        S_t = alpha_t S_{t-1} + g_t k_t (v_t - alpha_t S_{t-1}^T k_t)^T.
+    alpha None means alpha_t = 1 (the plain gated delta rule).
+    S: [..., d, dv]; q, k: [..., d]; v: [..., dv]; g, alpha: [...].
     """
+    if alpha is not None:
+        S = alpha[..., None, None] * S
     v_hat = np.einsum("...rd,...r->...d", S, k)
     S_new = S + g[..., None, None] * k[..., :, None] * (v - v_hat)[..., None, :]
     o = np.einsum("...rd,...r->...d", S_new, q)
     return o, S_new
 
 
-def delta_prefill(q, k, v, g, *, S0=None):
+def delta_prefill(q, k, v, g, *, S0=None, alpha=None):
     """Gated delta rule over a whole sequence, token by token.
 
-    q, k: [B, H, N, d]; v: [B, H, N, dv]; g: [B, H, N]; S0: [B, H, d, dv] or
-    None.  Returns (o [B, H, N, dv], S_N [B, H, d, dv]) in float64.
+    q, k: [B, H, N, d]; v: [B, H, N, dv]; g: [B, H, N]; alpha: [B, H, N] or
+    None (no decay); S0: [B, H, d, dv] or None.  Returns (o [B, H, N, dv],
+    S_N [B, H, d, dv]) in float64.
     """
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    al = None if alpha is None else _f64(alpha)
     B, H, N, d = q.shape
     dv = v.shape[-1]
     S = np.zeros((B, H, d, dv)) if S0 is None else _f64(S0).copy()
     o = np.empty((B, H, N, dv))
     for t in range(N):
         o[:, :, t], S = delta_step(S, q[:, :, t], k[:, :, t], v[:, :, t],
-                                   g[:, :, t])
+                                   g[:, :, t], None if al is None else al[:, :, t])
     return o, S
 
 
-def delta_decode_step(q, k, v, g, S):
+def delta_decode_step(q, k, v, g, S, alpha=None):
     """One decode step of the gated delta rule against a persistent state.
 
-    q, k: [B, H, d]; v: [B, H, dv]; g: [B, H]; S: [B, H, d, dv].
-    Returns (o [B, H, dv], S_new); S is not modified.
+    q, k: [B, H, d]; v: [B, H, dv]; g, alpha: [B, H] (alpha None: no decay);
+    S: [B, H, d, dv].  Returns (o [B, H, dv], S_new); S is not modified.
     """
-    return delta_step(_f64(S), _f64(q), _f64(k), _f64(v), _f64(g))
+    return delta_step(_f64(S), _f64(q), _f64(k), _f64(v), _f64(g),
+                      None if alpha is None else _f64(alpha))

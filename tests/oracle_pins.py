@@ -371,4 +371,90 @@ def pin_delta_split_and_decode(orc):
     np.testing.assert_allclose(Sd, S, rtol=1e-12)
 
 
+# --- gated delta rule with a scalar decay (Gated DeltaNet) -----------------
+
+def pin_gdn_matrix_form(orc):
+    """Efficient attention variants 7.4 writes the decayed rule as
+    S_t = alpha_t (I - g_t k_t k_t^T) S_{t-1} + g_t k_t v_t^T; explicit matrix
+    products on tiny inputs (d != dv, alpha well away from 1) must match,
+    outputs read from the updated state."""
+    rng = np.random.default_rng(21)
+    N, d, dv = 12, 4, 5
+    q = rng.normal(size=(N, d))
+    k = rng.normal(size=(N, d))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.normal(size=(N, dv))
+    g = 1 / (1 + np.exp(-rng.normal(size=N)))
+    al = rng.uniform(0.3, 0.95, size=N)
+    S0 = rng.normal(size=(d, dv))
+    S = S0.copy()
+    ref = np.zeros((N, dv))
+    eye = np.eye(d)
+    for t in range(N):
+        S = al[t] * (eye - g[t] * np.outer(k[t], k[t])) @ S + g[t] * np.outer(k[t], v[t])
+        ref[t] = S.T @ q[t]
+    o, Sf = orc.delta_prefill(_bh(q), _bh(k), _bh(v), _bh(g), S0=_bh(S0), alpha=_bh(al))
+    np.testing.assert_allclose(o[0, 0], ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(Sf[0, 0], S, rtol=1e-12, atol=1e-13)
+
+
+def pin_gdn_pure_decay(orc):
+    """With g = 0 nothing is written: S_t = (alpha_1 ... alpha_t) S_0, so
+    o_t = (prod alpha) S_0^T q_t (closed form)."""
+    rng = np.random.default_rng(22)
+    N, d, dv = 9, 3, 4
+    q = rng.normal(size=(N, d))
+    k = rng.normal(size=(N, d))
+    v = rng.normal(size=(N, dv))
+    al = rng.uniform(0.5, 1.0, size=N)
+    S0 = rng.normal(size=(d, dv))
+    o, Sf = orc.delta_prefill(_bh(q), _bh(k), _bh(v), _bh(np.zeros(N)), S0=_bh(S0),
+                              alpha=_bh(al))
+    cum = np.cumprod(al)
+    np.testing.assert_allclose(o[0, 0], cum[:, None] * (q @ S0), rtol=1e-13)
+    np.testing.assert_allclose(Sf[0, 0], cum[-1] * S0, rtol=1e-13)
+
+
+def pin_gdn_unit_key_overwrite(orc):
+    """A unit key with g = 1 replaces what the decayed state holds for that
+    key (the error is taken on the decayed state, Efficient attention
+    variants 7.4): row 0 of S_t becomes v_t, the other rows only decay."""
+    d, dv = 3, 2
+    S0 = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0]])
+    k = np.array([[1.0, 0.0, 0.0], [1.0, 0.0, 0.0]])
+    v = np.array([[7.0, -1.0], [0.5, 8.0]])
+    al = np.array([0.5, 0.25])
+    o, Sf = orc.delta_prefill(_bh(k), _bh(k), _bh(v), _bh(np.ones(2)), S0=_bh(S0),
+                              alpha=_bh(al))
+    want = np.array([[0.5, 8.0], [3.0 * 0.125, 4.0 * 0.125], [5.0 * 0.125, 6.0 * 0.125]])
+    np.testing.assert_allclose(Sf[0, 0], want, rtol=1e-15)
+    np.testing.assert_allclose(o[0, 0], v, rtol=1e-15)  # q = e_1 reads row 0
+
+
+def pin_gdn_alpha_one_and_split(orc):
+    """alpha = 1 is the plain gated delta rule; with decay, a split sequence
+    with carried state and a decode step after prefill give the same
+    outputs and state."""
+    rng = np.random.default_rng(23)
+    q = rng.normal(size=(1, 2, 13, 4))
+    k = rng.normal(size=(1, 2, 13, 4))
+    v = rng.normal(size=(1, 2, 13, 3))
+    g = rng.uniform(size=(1, 2, 13))
+    al = rng.uniform(0.6, 1.0, size=(1, 2, 13))
+    o_plain, S_plain = orc.delta_prefill(q, k, v, g)
+    o_one, S_one = orc.delta_prefill(q, k, v, g, alpha=np.ones((1, 2, 13)))
+    np.testing.assert_allclose(o_one, o_plain, rtol=1e-14)
+    np.testing.assert_allclose(S_one, S_plain, rtol=1e-14)
+    o, S = orc.delta_prefill(q, k, v, g, alpha=al)
+    o1, S1 = orc.delta_prefill(q[:, :, :5], k[:, :, :5], v[:, :, :5], g[:, :, :5],
+                               alpha=al[:, :, :5])
+    o2, S2 = orc.delta_prefill(q[:, :, 5:12], k[:, :, 5:12], v[:, :, 5:12], g[:, :, 5:12],
+                               S0=S1, alpha=al[:, :, 5:12])
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), o[:, :, :12], rtol=1e-12)
+    od, Sd = orc.delta_decode_step(q[:, :, 12], k[:, :, 12], v[:, :, 12], g[:, :, 12], S2,
+                                   alpha=al[:, :, 12])
+    np.testing.assert_allclose(od, o[:, :, 12], rtol=1e-12)
+    np.testing.assert_allclose(Sd, S, rtol=1e-12)
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]
