@@ -8,6 +8,7 @@ a tensor is not on a GPU, the call raises.
 
     o, S, z = prefill(q, k, v, gamma=gamma, eps=1e-6)       # LINEAR, elu+1
     o, S, _ = prefill(q, k, v, rule="delta", g=g)             # gated delta
+    o, S, _ = prefill(q, k, v, rule="delta", g=g, alpha=a)    # with decay
     o = decode_step(q1, k1, v1, S, z)                         # in place on S, z
 """
 from __future__ import annotations
@@ -44,14 +45,14 @@ def _need_gpu(*ts):
 def _need_f32(*ts):
     for t in ts:
         if t is not None and t.dtype != torch.float32:
-            raise ValueError("gamma, g, states must be float32")
+            raise ValueError("gamma, g, alpha, states must be float32")
 
 
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _prefill_args(q, k, v, rule, fmap, gamma, g, eps):
+def _prefill_args(q, k, v, rule, fmap, gamma, g, eps, alpha=None):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,H,N,d] and v [B,H,N,dv]")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
@@ -64,6 +65,7 @@ def _prefill_args(q, k, v, rule, fmap, gamma, g, eps):
     a.fmap = _FMAPS[fmap]
     a.gamma = _ptr(gamma)
     a.g = _ptr(g)
+    a.alpha = _ptr(alpha)
     a.eps = float(eps)
     return a
 
@@ -82,19 +84,22 @@ def workspace_size(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None,
 
 def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
             S_in=None, z_in=None, S_out=None, z_out=None, return_state=True,
-            o=None, workspace=None):
+            o=None, workspace=None, alpha=None):
     """Chunked prefill over [B,H,N,*] sequences (see la_prefill).
 
     rule "linear": fmap defaults to "elu1"; gamma [H] fp32 or None; eps >= 0.
-    rule "delta":  fmap "identity"; g [B,H,N] fp32 required.
+    rule "delta":  fmap "identity"; g [B,H,N] fp32 required; alpha [B,H,N]
+                   fp32 state decay in (0, 1] or None.
     Returns (o, S_out, z_out); the states are None unless requested
     (return_state) or passed in.  z_out is always None for "delta".
     """
     if fmap is None:
         fmap = "elu1" if rule == "linear" else "identity"
-    _need_gpu(q, k, v, gamma, g, S_in, z_in, S_out, z_out, o, workspace)
-    _need_f32(gamma, g, S_in, z_in, S_out, z_out)
-    a = _prefill_args(q, k, v, rule, fmap, gamma, g, eps)
+    _need_gpu(q, k, v, gamma, g, alpha, S_in, z_in, S_out, z_out, o, workspace)
+    _need_f32(gamma, g, alpha, S_in, z_in, S_out, z_out)
+    if alpha is not None and alpha.shape != q.shape[:3]:
+        raise ValueError("alpha must be [B,H,N]")
+    a = _prefill_args(q, k, v, rule, fmap, gamma, g, eps, alpha)
     B, H, N, d = q.shape
     dv = v.shape[3]
     if o is None:
@@ -120,13 +125,14 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
 
 
 def decode_step(q, k, v, S, z=None, *, rule="linear", fmap=None, gamma=None,
-                g=None, eps=1e-6, o=None):
+                g=None, eps=1e-6, o=None, alpha=None):
     """One token per sequence: q, k [B,H,d], v [B,H,dv]; S [B,H,d,dv] (and z
-    [B,H,d] for "linear") are updated in place.  Returns o [B,H,dv]."""
+    [B,H,d] for "linear") are updated in place; "delta" takes g [B,H] and
+    an optional decay alpha [B,H].  Returns o [B,H,dv]."""
     if fmap is None:
         fmap = "elu1" if rule == "linear" else "identity"
-    _need_gpu(q, k, v, S, z, gamma, g, o)
-    _need_f32(S, z, gamma, g)
+    _need_gpu(q, k, v, S, z, gamma, g, alpha, o)
+    _need_f32(S, z, gamma, g, alpha)
     if q.dim() != 3 or k.shape != q.shape or v.shape[:2] != q.shape[:2]:
         raise ValueError("q, k must be [B,H,d] and v [B,H,dv]")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
@@ -143,7 +149,7 @@ def decode_step(q, k, v, S, z=None, *, rule="linear", fmap=None, gamma=None,
     a.rule = _RULES[rule]
     a.fmap = _FMAPS[fmap]
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
-    a.gamma, a.g = _ptr(gamma), _ptr(g)
+    a.gamma, a.g, a.alpha = _ptr(gamma), _ptr(g), _ptr(alpha)
     a.eps = float(eps)
     a.S, a.z, a.o = _ptr(S), _ptr(z), _ptr(o)
     _lib.check(_lib.load().la_decode_step(ctypes.byref(a), _stream()),

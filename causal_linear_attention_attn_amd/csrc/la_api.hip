@@ -126,7 +126,7 @@ int check_prefill_shape(const la_prefill_args *a) {
 
 extern "C" {
 
-int32_t la_abi_version(void) { return 1; }
+int32_t la_abi_version(void) { return 2; }
 
 const char *la_status_str(int s) {
   switch (s) {
@@ -154,7 +154,7 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   const int BH = a->B * a->H;
   const bool linear = a->rule == LA_RULE_LINEAR;
   if (linear) {
-    if (a->g || !(a->eps >= 0.f) || !std::isfinite(a->eps)) return LA_EINVAL;
+    if (a->g || a->alpha || !(a->eps >= 0.f) || !std::isfinite(a->eps)) return LA_EINVAL;
   } else {
     if (!a->g && BH > 0 && a->N > 0) return LA_EINVAL;
     if (a->gamma || a->z_in || a->z_out) return LA_EINVAL;
@@ -203,6 +203,7 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   p.v = a->v;
   p.gamma = a->gamma;
   p.g = a->g;
+  p.alpha = a->alpha;
   p.eps = a->eps;
   p.S_in = a->S_in;
   p.z_in = a->z_in;
@@ -229,7 +230,7 @@ int la_decode_step(const la_decode_args *a, void *stream) {
     if (a->fmap != LA_FMAP_IDENTITY || a->gamma || a->z) return LA_EINVAL;
     if (BH > 0 && !a->g) return LA_EINVAL;
   } else {
-    if (a->g || !(a->eps >= 0.f) || !std::isfinite(a->eps)) return LA_EINVAL;
+    if (a->g || a->alpha || !(a->eps >= 0.f) || !std::isfinite(a->eps)) return LA_EINVAL;
     if (BH > 0 && !a->z) return LA_EINVAL;
   }
   if (BH == 0) return LA_OK;
@@ -246,6 +247,7 @@ int la_decode_step(const la_decode_args *a, void *stream) {
   p.v = a->v;
   p.gamma = a->gamma;
   p.g = a->g;
+  p.alpha = a->alpha;
   p.eps = a->eps;
   p.S = a->S;
   p.z = a->z;

@@ -4,9 +4,11 @@
 // "LLM inference optimisation (3)", recurrent form: read once, add once):
 //     S <- gamma S + phi(k) v^T,  z <- gamma z + phi(k)
 //     o  = S^T phi(q) / (phi(q) . z + eps)
-// DELTA ("What Is Linear Attention?" 5.2-5.3):
-//     b = S^T k,  S <- S + g k (v - b)^T,  o = S^T q  (updated state)
-//       = S_old^T q + g (k . q) (v - b)
+// DELTA ("What Is Linear Attention?" 5.2-5.3), with the optional scalar
+// decay alpha of Gated DeltaNet ("Efficient attention variants" 7.4: decay
+// first, the error is taken on the decayed state):
+//     b = S^T k,  u = v - alpha b,  S <- alpha S + g k u^T,
+//     o = S_new^T q = alpha S_old^T q + g (k . q) u
 //
 // The step is bound by HBM: each (b,h) state block (d x dv fp32, 64 KiB at
 // d = dv = 128) is read once and written once.  One workgroup of 256 threads
@@ -87,6 +89,7 @@ decode_kernel(DecodeParams p) {
   if (t < dv) s_v[t] = to_f32(v[t]);
   const float gam = (!DELTA && p.gamma) ? p.gamma[bh % p.H] : 1.f;
   const float gate = DELTA ? p.g[bh] : 0.f;
+  const float al = (DELTA && p.alpha) ? p.alpha[bh] : 1.f;
   __syncthreads();
 
   float acc[VEC], acc2[VEC];
@@ -159,11 +162,11 @@ decode_kernel(DecodeParams p) {
         b += s_part[0][r2 * dv + t];
         a += s_part[1][r2 * dv + t];
       }
-      const float u = s_v[t] - b;  // residual v - S_old^T k
+      const float u = fmaf(-al, b, s_v[t]);  // residual v - alpha S_old^T k
       s_b[t] = u;
       s_a[t] = a;
       reinterpret_cast<T *>(p.o)[(size_t)bh * dv + t] =
-          from_f32<T>(fmaf(gate * qk, u, a));
+          from_f32<T>(fmaf(gate * qk, u, al * a));
     }
     __syncthreads();
 #pragma unroll
@@ -172,7 +175,7 @@ decode_kernel(DecodeParams p) {
       const bool ok = active && r < d;
       const float gk = ok ? gate * s_k[r] : 0.f;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) sr[m][e] = fmaf(gk, s_b[c0 + e], sr[m][e]);
+      for (int e = 0; e < VEC; ++e) sr[m][e] = fmaf(gk, s_b[c0 + e], al * sr[m][e]);
       const uint32_t off = ok ? (uint32_t)(((size_t)r * dv + c0) * 4) : kOOB;
       if constexpr (VEC == 4)
         buf_store16_nt<float>(rS, off, (f32x4){sr[m][0], sr[m][1], sr[m][2], sr[m][3]});

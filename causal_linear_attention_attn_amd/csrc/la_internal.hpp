@@ -26,6 +26,7 @@ struct PrefillParams {
   const void *q, *k, *v;
   const float *gamma;  // [H] or nullptr
   const float *g;      // delta gate [BH, N]
+  const float *alpha;  // delta decay [BH, N] or nullptr
   float eps;
   const float *S_in, *z_in;
   float *S_out, *z_out;
@@ -39,6 +40,7 @@ struct DecodeParams {
   int fmap;
   const void *q, *k, *v;
   const float *gamma, *g;
+  const float *alpha;  // delta decay [BH] or nullptr
   float eps;
   float *S, *z;
   void *o;

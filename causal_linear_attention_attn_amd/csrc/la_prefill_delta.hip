@@ -11,6 +11,15 @@
 // so with T = (I + diag(g) L)^(-1) diag(g) and Y = V - K S-:
 //     U  = T Y,   O = Q S- + P U = Q S- + R Y,   P = lower_incl(Q K^T),  R = P T
 //     S+ = S- + K^T U = S- + Wt Y,               Wt = K^T T   (d x C)
+// With the scalar decay alpha of Gated DeltaNet ("Efficient attention
+// variants" 7.4: S_t = alpha_t S_{t-1} + g_t k_t (v_t - alpha_t S_{t-1}^T
+// k_t)^T), let b_j = alpha_0 ... alpha_j within the chunk.  Unrolling the
+// same way puts b_j / b_i on every pair j > i:
+//     L = strict_lower(K K^T) (.) [b_j / b_i],  P = lower_incl(Q K^T) (.) [b_j / b_i]
+//     Y = V - diag(b) K S-,  O = diag(b) Q S- + R Y,  R = P T,
+//     S+ = b_L S- + Wt Y,    Wt = K^T diag(b_L / b) T   (b_L = b of the last token)
+// prep forms the ratios from log-cumulative decays (a prefix sum of log
+// alpha over the chunk), so every factor is exp of a non-positive number.
 // Wt and R depend only on the chunk's q, k and g, so they are computed for
 // every chunk in parallel (prep_kernel); the state-dependent part is a
 // sequential pass over chunks (seq_kernel) with one matrix product on the
@@ -134,9 +143,10 @@ struct alignas(16) SmemPrep {
   float Xm[CF::C * CF::FLD];  // (I + N)^(-1)
   float Ym[CF::C * 16];       // partial products of the block solve
   float gs[CF::C];
+  float lb[CF::C];            // log b_j: prefix sums of log alpha
 };
 
-template <class CF, bool VK>
+template <class CF, bool VK, bool DECAY>
 __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
   using T = typename CF::type;
   constexpr int C = CF::C, FLD = CF::FLD, TLD = CF::TLD, NRB = CF::NRB;
@@ -172,6 +182,18 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
     *reinterpret_cast<typename CF::vec *>(sm.Ks + row * CF::QLD + col0) = x;
   }
   if (tid < C) sm.gs[tid] = tid < Lc ? p.g[(size_t)bh * N + c0 + tid] : 0.f;
+  // log-cumulative decay over the chunk (alpha = 1 past the end): an
+  // inclusive prefix sum across the lanes of wave 0
+  constexpr bool decay = DECAY;  // a decay alpha was given
+  if (decay && wv == 0) {
+    float x = lane < Lc ? logf(p.alpha[(size_t)bh * N + c0 + lane]) : 0.f;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane < C) sm.lb[lane] = x;
+  }
   const int rb = wv;  // row block of this wave (waves >= NRB idle in row-block work)
   Frag<T> qf[CF::KSD];
   if (rb < NRB) {
@@ -195,6 +217,7 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
       lds_frag(kr[ks], sm.Ks + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
     const int i = 16 * rb + li;
     const float gi = sm.gs[i];
+    const float lbi = decay ? sm.lb[i] : 0.f;
 #pragma unroll
     for (int tj = 0; tj < NRB; ++tj) {
       if (tj <= rb) {
@@ -210,14 +233,21 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * tj + 4 * lg + r;
-          n4[r] = j < i ? gi * kk[r] : 0.f;
-          if (j > i) pq[tj][r] = 0.f;
+          const float dec = decay ? expf(lbi - sm.lb[min(j, i)]) : 1.f;  // b_i / b_j
+          n4[r] = j < i ? gi * kk[r] * dec : 0.f;
+          pq[tj][r] = j <= i ? pq[tj][r] * dec : 0.f;
         }
         lds_store4(sm.Nm + i * FLD + 16 * tj + 4 * lg, n4[0], n4[1], n4[2], n4[3]);
       }
     }
   }
   __syncthreads();
+  if (decay && tid < C) {  // b_j for the sequential pass
+    float *bdst = reinterpret_cast<float *>(reinterpret_cast<T *>(p.ws) +
+                                            (size_t)p.BH * gridDim.x * CF::REC) +
+                  ((size_t)bh * gridDim.x + chunk) * C;
+    bdst[tid] = expf(sm.lb[tid]);
+  }
 
   // ---- X = (I + N)^(-1), unit lower triangular ----
   // Diagonal 16x16 blocks: lane 16 b + c solves column c of block b by
@@ -266,14 +296,21 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
     }
   }
 
-  // ---- T^T (T = X diag(g)) as high and low parts, over N's storage ----
-  for (int e = tid; e < C * C; e += kThreads) {
-    const int i = e / C, j = e % C;  // T^T[i][j] = T[j][i] = X[j][i] g_i
-    T hi, lo;
-    split2<T>(sm.Xm[j * FLD + i] * sm.gs[i], hi, lo);
-    sm.Tt[0][i * TLD + j] = hi;
-    sm.Tt[1][i * TLD + j] = lo;
-  }
+  // ---- T^T (T = X diag(g)) as high and low parts, over N's storage; for
+  //      Wt with decay, column j carries w_j = b_L / b_j ----
+  const float lbL = decay ? sm.lb[C - 1] : 0.f;
+  auto split_t = [&](bool weighted) {
+    for (int e = tid; e < C * C; e += kThreads) {
+      const int i = e / C, j = e % C;  // T^T[i][j] = T[j][i] = X[j][i] g_i
+      float x = sm.Xm[j * FLD + i] * sm.gs[i];
+      if (weighted) x *= expf(lbL - sm.lb[j]);
+      T hi, lo;
+      split2<T>(x, hi, lo);
+      sm.Tt[0][i * TLD + j] = hi;
+      sm.Tt[1][i * TLD + j] = lo;
+    }
+  };
+  split_t(decay);
   __syncthreads();
 
   T *out = reinterpret_cast<T *>(p.ws) + ((size_t)bh * gridDim.x + chunk) * CF::REC;
@@ -296,6 +333,11 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
     }
     // lane holds W[i = 16 ti + 4 lg + r][f = 16 tf + li]
     store4_t(out + (size_t)(16 * tf + li) * C + 16 * ti + 4 * lg, acc);
+  }
+  if (decay) {  // R takes T itself
+    __syncthreads();
+    split_t(false);
+    __syncthreads();
   }
   // ---- R^T = T^T P^T (rows m, columns i = this wave's row block) ----
   // stored as R[i][m]: the lane's four rows m are contiguous.
@@ -439,7 +481,7 @@ __device__ __forceinline__ void seq_commit(const SeqRegs<CF> &R, SeqTiles<CF> &t
   }
 }
 
-template <class CF, bool VK>
+template <class CF, bool VK, bool DECAY>
 __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nslices,
                                                        int xcd_map) {
   using T = typename CF::type;
@@ -476,6 +518,12 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
     rs[3] = buf_rsrc(reinterpret_cast<const T *>(p.v) + (size_t)bh * vo, (uint32_t)(vo * sizeof(T)));
     rs[4] = buf_rsrc(reinterpret_cast<const T *>(p.o) + (size_t)bh * vo, (uint32_t)(vo * sizeof(T)));
   }
+  // decay products b_j of every chunk of this head (written by prep)
+  constexpr bool decay = DECAY;  // a decay alpha was given
+  const __amdgpu_buffer_rsrc_t rdec = buf_rsrc(
+      reinterpret_cast<const float *>(reinterpret_cast<const T *>(p.ws) +
+                                      (size_t)p.BH * nch * CF::REC) + (size_t)bh * nch * C,
+      (uint32_t)((size_t)nch * C * sizeof(float)));
 
   // fp32 state slice: wave holds row tiles tf = wv * FPW + a, every column tile
   f32x4 Sacc[CF::FPW][CF::NCT];
@@ -522,6 +570,17 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
   load_v(vset[0], 0);
   seq_load<CF, VK>(set[1], p, rs, 1);
   load_v(vset[1], 1);
+  // b of this lane's token and of the chunk's last token, two chunks ahead
+  // like v (past the end they read as zero and are not used)
+  float bset[2][2] = {{1.f, 1.f}, {1.f, 1.f}};
+  auto load_b = [&](float (&bb)[2], int chunk) {
+    if (decay) {
+      bb[0] = buf_load1(rdec, (uint32_t)((chunk * C + 16 * rb + li) * 4), (float *)nullptr);
+      bb[1] = buf_load1(rdec, (uint32_t)((chunk * C + C - 1) * 4), (float *)nullptr);
+    }
+  };
+  load_b(bset[0], 0);
+  load_b(bset[1], 1);
 #pragma unroll
   for (int a = 0; a < CF::FPW; ++a)
 #pragma unroll
@@ -536,6 +595,8 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
       const int c = cb + u;
       const SeqTiles<CF> &tl = sm.tile[u];
       seq_load<CF, VK>(set[u], p, rs, c + 2);
+      const float b_tok = bset[u][0], b_last = bset[u][1];
+      load_b(bset[u], c + 2);
       const int t = c * C + 16 * rb + li;  // this lane's token
       const bool tok_ok = t < N;
 
@@ -557,6 +618,13 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
           lds_frag(sf, sm.St + (16 * (ct0 + b2) + li) * CF::QLD + 32 * ks + 8 * lg);
           mma(X[b2], sf, kf);
           mma(Z[b2], sf, qf);
+        }
+      }
+      if (decay) {  // X and Q S- rows carry b of their token
+#pragma unroll
+        for (int b2 = 0; b2 < CF::TW; ++b2) {
+          X[b2] *= b_tok;
+          Z[b2] *= b_tok;
         }
       }
       // ---- Y = V - X: lane holds columns 16 ct + 4 lg + r of token t ----
@@ -598,7 +666,13 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
           }
         }
       }
-      // ---- S+ = S- + Wt Y for this wave's state rows; T-precision copy ----
+      // ---- S+ = b_L S- + Wt Y for this wave's state rows; T-precision copy ----
+      if (decay && c < nch) {
+#pragma unroll
+        for (int a = 0; a < CF::FPW; ++a)
+#pragma unroll
+          for (int c2 = 0; c2 < CF::NCT; ++c2) Sacc[a][c2] *= b_last;
+      }
 #pragma unroll
       for (int ks = 0; ks < CF::KSC; ++ks) {
         Frag<T> wf[CF::FPW];
@@ -641,18 +715,24 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
   }
 }
 
-template <class CF, bool VK>
-hipError_t run_vk(const PrefillParams &p, hipStream_t s) {
+template <class CF, bool VK, bool DECAY>
+hipError_t run_vkd(const PrefillParams &p, hipStream_t s) {
   static_assert(sizeof(SmemPrep<CF>) <= 64 * 1024, "LDS budget (prep)");
   static_assert(sizeof(SmemSeq<CF>) <= 160 * 1024, "LDS budget (seq)");
   const int nch = (p.N + CF::C - 1) / CF::C;
-  hipError_t e = launch_kernel("delta_prep", prep_kernel<CF, VK>, dim3(nch, p.BH),
+  hipError_t e = launch_kernel("delta_prep", prep_kernel<CF, VK, DECAY>, dim3(nch, p.BH),
                                dim3(kThreads), s, p);
   if (e != hipSuccess) return e;
   const int nsl = (p.dv + CF::W - 1) / CF::W;
   const int xcd_map = (p.BH % kXcds) == 0;
-  return launch_kernel("delta_seq", seq_kernel<CF, VK>, dim3(p.BH * nsl), dim3(kThreads), s,
-                       p, nsl, xcd_map);
+  return launch_kernel("delta_seq", seq_kernel<CF, VK, DECAY>, dim3(p.BH * nsl),
+                       dim3(kThreads), s, p, nsl, xcd_map);
+}
+
+// the decay-free rule gets its own instantiation (no decay work compiled in)
+template <class CF, bool VK>
+hipError_t run_vk(const PrefillParams &p, hipStream_t s) {
+  return p.alpha ? run_vkd<CF, VK, true>(p, s) : run_vkd<CF, VK, false>(p, s);
 }
 
 template <class CF>
@@ -673,7 +753,9 @@ size_t delta_workspace_bytes(int BH, int N, int d, bool bf16_io) {
   const int C = bf16_io ? DB64::C : DF64::C;
   const size_t DK = d <= 64 ? 64 : 128;
   const size_t nch = ((size_t)N + C - 1) / C;
-  return (size_t)BH * nch * (DK * C + (size_t)C * C) * (bf16_io ? 2 : 4);
+  // per chunk: the [Wt | R] record in the input precision, then (after all
+  // records) C fp32 decay products b_j, used when a decay is given
+  return (size_t)BH * nch * ((DK * C + (size_t)C * C) * (bf16_io ? 2 : 4) + (size_t)C * 4);
 }
 
 hipError_t launch_delta_prefill(const PrefillParams &p, bool bf16_io, hipStream_t s) {

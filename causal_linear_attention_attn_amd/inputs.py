@@ -89,6 +89,14 @@ def sigmoid_gate(shape, wid, tid, device):
     return torch.sigmoid(x)
 
 
+def decay_gate(shape, wid, tid, device, lo):
+    """alpha = lo + (1 - lo) sigmoid(N(0,1)) in fp32: a per-token state decay
+    in (lo, 1)."""
+    x = torch.randn(shape, generator=_gen(wid, tid, device), device=device,
+                    dtype=torch.float32)
+    return lo + (1.0 - lo) * torch.sigmoid(x)
+
+
 def per_head_gamma(H, device="cpu"):
     """gamma_h = 1 - 2^(-5 - h/4), h = 0..H-1, as fp32."""
     h = torch.arange(H, dtype=torch.float64)

@@ -70,7 +70,10 @@ typedef enum { LA_FMAP_IDENTITY = 0, LA_FMAP_ELU1 = 1 } la_fmap;
  *   The state is read after the token is written (the token sees itself).
  * LA_RULE_DELTA ([WILA] sections 5.2 and 5.3):
  *     S_t = S_{t-1} + g_t k_t (v_t - S_{t-1}^T k_t)^T,   o_t = S_t^T q_t
- *   raw q and k (fmap must be IDENTITY), no normaliser, no z. */
+ *   raw q and k (fmap must be IDENTITY), no normaliser, no z.  With the
+ *   optional scalar decay alpha_t (Gated DeltaNet, [EAV] section 7.4; the
+ *   error is taken on the decayed state):
+ *     S_t = alpha_t S_{t-1} + g_t k_t (v_t - alpha_t S_{t-1}^T k_t)^T */
 typedef enum { LA_RULE_LINEAR = 0, LA_RULE_DELTA = 1 } la_rule;
 
 /* One call processes B*H independent sequences of N tokens. */
@@ -90,6 +93,11 @@ typedef struct la_prefill_args {
                         stays far inside the fp32 range on that interval. */
   const float *g;    /* DELTA: [B,H,N] write gate per token (required).
                         LINEAR: must be NULL. */
+  const float *alpha;/* DELTA: [B,H,N] state decay per token, each in (0, 1],
+                        or NULL (= 1, no decay).  LINEAR: must be NULL.
+                        Values are the caller's contract (not read on the
+                        host); a zero or negative value makes the chunk's
+                        decay products undefined. */
   float eps;         /* LINEAR: added to the denominator, >= 0. DELTA: ignored */
   const float *S_in; /* [B,H,d,dv] initial state; NULL = zeros */
   const float *z_in; /* LINEAR: [B,H,d] initial normaliser; NULL = zeros.
@@ -126,6 +134,8 @@ typedef struct la_decode_args {
   const void *v;     /* [B,H,dv] */
   const float *gamma;/* LINEAR: [H] or NULL (=1).  DELTA: must be NULL. */
   const float *g;    /* DELTA: [B,H] write gate (required). LINEAR: NULL. */
+  const float *alpha;/* DELTA: [B,H] state decay, or NULL (= 1).
+                        LINEAR: must be NULL. */
   float eps;         /* LINEAR: >= 0 */
   float *S;          /* [B,H,d,dv] fp32, read and overwritten in place */
   float *z;          /* LINEAR: [B,H,d] fp32 in place (required).
@@ -147,9 +157,9 @@ int la_state_init(float *S, float *z, int32_t B, int32_t H, int32_t d,
 const char *la_status_str(int status);
 
 /* Kernel timing for benchmarks and tracing (not part of the method).
- * While enabled, every kernel the library launches is bracketed by two HIP
- * events recorded on the launch stream (a few microseconds of overhead per
- * launch, no host synchronisation).  la_profile_collect() waits for the
+ * While enabled, every kernel the library launches gets a pair of HIP
+ * events that the dispatch itself stamps when the kernel starts and ends
+ * (hipExtLaunchKernel; no host synchronisation).  la_profile_collect() waits for the
  * recorded events, writes up to `max` records (oldest first) and clears the
  * log; it returns the number of records written, or -1 on a HIP error.
  * Records past an internal limit of 65536 are dropped.  Kernel names are
@@ -157,7 +167,7 @@ const char *la_status_str(int status);
  * toggled while another thread is launching. */
 typedef struct la_kernel_time {
   const char *name; /* kernel name (static storage) */
-  float ms;         /* elapsed time between the bracketing events */
+  float ms;         /* kernel duration (start to end of the dispatch) */
 } la_kernel_time;
 int la_profile_enable(int on);
 int la_profile_collect(la_kernel_time *out, int max);
