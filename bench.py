@@ -22,9 +22,10 @@ per step.  Alongside:
   decode        the decode-step loop (B=256 H=32 d=dv=128, state built by a
                 1024-token prefill, then 1024 single-token steps with fresh
                 q, k, v): steps/s and state GB/s against HBM peak;
-  workloads     the long-context decay prefill (B=1 H=32 N=131072 d=128) and
-                the gated delta-rule prefill (B=2 H=16 N=8192 d=128), each
-                with its kernels' times and HBM fraction;
+  workloads     the long-context decay prefill (B=1 H=32 N=131072 d=128), the
+                gated delta-rule prefill (B=2 H=16 N=8192 d=128) and the same
+                with a per-token state decay alpha in (0.9, 1), each with its
+                kernels' times and HBM fraction;
   cpu_baseline  the fp64 oracle on the host (one thread) over the same
                 inputs of the main workload (a reported baseline, not a
                 target), with its parity error against the GPU output.
@@ -54,7 +55,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5],
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6],
                     help="3 runs the decode-step loop alone")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -303,10 +304,12 @@ class KernelTimer:
 
 def bytes_per_head_token(w):
     """Algorithmic HBM bytes: q, k, v read once, o written once (plus the
-    fp32 gate for the delta rule)."""
+    fp32 gate, and the fp32 decay when given, for the delta rule)."""
     e = w.dtype.itemsize
     b = (2 * w.d + w.dv) * e + w.dv * e
-    return b + (4 if w.rule == "delta" else 0)
+    if w.rule == "delta":
+        b += 4 + (4 if w.decay == "alpha" else 0)
+    return b
 
 
 def flops_per_head_token(w):
@@ -329,12 +332,12 @@ def make_step(la, torch, w, x):
     o = torch.empty((B, H, N, dv), dtype=w.dtype, device="cuda")
     S = torch.empty((B, H, d, dv), dtype=torch.float32, device="cuda")
     if w.rule == "delta":
-        g = x["g"]
+        g, al = x["g"], x.get("alpha")
         ws_bytes = la.workspace_size(q, k, v, rule="delta", g=g)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
         def step():
-            la.prefill(q, k, v, rule="delta", g=g, o=o, S_out=S, workspace=ws)
+            la.prefill(q, k, v, rule="delta", g=g, alpha=al, o=o, S_out=S, workspace=ws)
     else:
         z = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
         ws_bytes = la.workspace_size(q, k, v, gamma=gamma, eps=w.eps)
@@ -484,7 +487,9 @@ def cpu_baseline(w, x, o_gpu):
     with threadpool_limits(1):
         t0 = time.perf_counter()
         if w.rule == "delta":
-            ro, _ = oracle.delta_prefill(q, k, v, x["g"].cpu())
+            al = x.get("alpha")
+            ro, _ = oracle.delta_prefill(q, k, v, x["g"].cpu(),
+                                         alpha=None if al is None else al.cpu())
         else:
             ro, _, _ = oracle.linear_prefill(q, k, v, eps=w.eps, gamma=gamma)
         el = time.perf_counter() - t0
@@ -559,7 +564,7 @@ def main():
         line["decode"] = bench_decode(la, lib, torch, args.decode_steps)
     if not args.no_extra:
         extra = {}
-        for wid in (4, 5):
+        for wid in (4, 5, 6):
             if wid == args.workload:
                 continue
             r, xx, oo = bench_workload(la, lib, torch, inputs.WORKLOADS[wid],

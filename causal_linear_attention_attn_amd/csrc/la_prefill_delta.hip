@@ -144,6 +144,7 @@ struct alignas(16) SmemPrep {
   float Ym[CF::C * 16];       // partial products of the block solve
   float gs[CF::C];
   float lb[CF::C];            // log b_j: prefix sums of log alpha
+  float wl[CF::C];            // b_L / b_j (Wt's token weights)
 };
 
 template <class CF, bool VK, bool DECAY>
@@ -242,11 +243,12 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
     }
   }
   __syncthreads();
-  if (decay && tid < C) {  // b_j for the sequential pass
+  if (decay && tid < C) {  // b_j for the sequential pass, b_L / b_j for Wt
     float *bdst = reinterpret_cast<float *>(reinterpret_cast<T *>(p.ws) +
                                             (size_t)p.BH * gridDim.x * CF::REC) +
                   ((size_t)bh * gridDim.x + chunk) * C;
     bdst[tid] = expf(sm.lb[tid]);
+    sm.wl[tid] = expf(sm.lb[C - 1] - sm.lb[tid]);
   }
 
   // ---- X = (I + N)^(-1), unit lower triangular ----
@@ -298,12 +300,11 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
 
   // ---- T^T (T = X diag(g)) as high and low parts, over N's storage; for
   //      Wt with decay, column j carries w_j = b_L / b_j ----
-  const float lbL = decay ? sm.lb[C - 1] : 0.f;
   auto split_t = [&](bool weighted) {
     for (int e = tid; e < C * C; e += kThreads) {
       const int i = e / C, j = e % C;  // T^T[i][j] = T[j][i] = X[j][i] g_i
       float x = sm.Xm[j * FLD + i] * sm.gs[i];
-      if (weighted) x *= expf(lbL - sm.lb[j]);
+      if (weighted) x *= sm.wl[j];
       T hi, lo;
       split2<T>(x, hi, lo);
       sm.Tt[0][i * TLD + j] = hi;

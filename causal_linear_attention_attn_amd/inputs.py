@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 import torch
 
 # tensor ids inside one workload
-_Q, _K, _V, _G = 1, 2, 3, 4
+_Q, _K, _V, _G, _A = 1, 2, 3, 4, 5
 _DEC_Q, _DEC_K, _DEC_V = 11, 12, 13
 
 
@@ -37,7 +37,8 @@ class Workload:
     fmap: str              # "elu1" or "identity"
     scale: float           # std of the q, k, v draws
     eps: float = 1e-6
-    decay: str = "none"    # "none" or "per_head" (gamma_h = 1 - 2^(-5 - h/4))
+    decay: str = "none"    # "none", "per_head" (gamma_h = 1 - 2^(-5 - h/4)) or
+                           # "alpha" (delta rule: per-token state decay in (0.9, 1))
     decode_steps: int = 0  # > 0: a decode loop follows the prefill
     extra: dict = field(default_factory=dict)
 
@@ -55,6 +56,9 @@ WORKLOADS = {
                 1.0 / math.sqrt(128), decay="per_head"),
     5: Workload(5, "delta_bf16_prefill_B2H16N8192d128", 2, 16, 8192, 128, 128,
                 torch.bfloat16, "delta", "identity", 1.0),
+    # the gated delta workload with Gated DeltaNet's scalar decay added
+    6: Workload(6, "delta_decay_bf16_prefill_B2H16N8192d128", 2, 16, 8192, 128, 128,
+                torch.bfloat16, "delta", "identity", 1.0, decay="alpha"),
 }
 
 
@@ -116,6 +120,8 @@ def make_prefill(w: Workload, device, *, B=None, H=None, N=None):
         out["k"] = unit_rows((B, H, N, w.d), w.wid, _K, device, w.dtype)
         out["v"] = normal((B, H, N, w.dv), w.wid, _V, device, w.scale, w.dtype)
         out["g"] = sigmoid_gate((B, H, N), w.wid, _G, device)
+        if w.decay == "alpha":
+            out["alpha"] = decay_gate((B, H, N), w.wid, _A, device, 0.9)
     else:
         out["q"] = normal((B, H, N, w.d), w.wid, _Q, device, w.scale, w.dtype)
         out["k"] = normal((B, H, N, w.d), w.wid, _K, device, w.scale, w.dtype)
