@@ -76,7 +76,7 @@ struct DCfg {
   static constexpr int KSC = C / 32;    // k-steps over tokens
   static constexpr int QLD = DK + VEC;  // row stride: Ks (prep), St (seq)
   static constexpr int YLD = W + 16;    // row stride: Ys (transpose reads)
-  static constexpr int FLD = C + 8;     // fp32 row stride: Nm, Xm (prep)
+  static constexpr int FLD = C + 8;     // fp32 row stride: Nm (prep)
   static constexpr int TLD = C + VEC;   // row stride: T^T parts (prep)
   static constexpr int QCB = DK / VEC;  // 16-byte blocks per q/k row
   static constexpr size_t WT = (size_t)DK * C;     // Wt elements per chunk
@@ -137,10 +137,10 @@ struct alignas(16) SmemPrep {
   using T = typename CF::type;
   T Ks[CF::C * CF::QLD];     // k rows
   union {
-    float Nm[CF::C * CF::FLD];             // N = diag(g) strict_lower(K K^T)
-    T Tt[2][CF::C * CF::TLD];              // T^T high / low parts (after the solve)
+    float Nm[CF::C * CF::FLD];  // N = diag(g) strict_lower(K K^T), then in
+                                // place X = (I + N)^(-1)
+    T Tt[2][CF::C * CF::TLD];   // T^T high / low parts (after the solve)
   };
-  float Xm[CF::C * CF::FLD];  // (I + N)^(-1)
   float Ym[CF::C * 16];       // partial products of the block solve
   float gs[CF::C];
   float lb[CF::C];            // log b_j: prefix sums of log alpha
@@ -251,12 +251,15 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
     sm.wl[tid] = expf(sm.lb[C - 1] - sm.lb[tid]);
   }
 
-  // ---- X = (I + N)^(-1), unit lower triangular ----
+  // ---- X = (I + N)^(-1), unit lower triangular, in place over N ----
   // Diagonal 16x16 blocks: lane 16 b + c solves column c of block b by
-  // forward substitution (x_c = 1; x_i = -sum_{m<i} N_im x_m for i > c).
+  // forward substitution (x_c = 1; x_i = -sum_{m<i} N_im x_m for i > c);
+  // a block's N is read in full before its X is written (one wave, in
+  // order), and nothing else needs it.  Blocks above the diagonal are
+  // zeroed meanwhile (N never wrote them).
   if (wv == 0 && lane < 16 * NRB) {
     const int b = lane >> 4, c = lane & 15;
-    const float *Nb = sm.Nm + (16 * b) * FLD + 16 * b;
+    float *Nb = sm.Nm + (16 * b) * FLD + 16 * b;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -266,13 +269,16 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
       x[i] = i == c ? 1.f : (i < c ? 0.f : -s);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sm.Xm[(16 * b + i) * FLD + 16 * b + c] = x[i];
+    for (int i = 0; i < 16; ++i) Nb[i * FLD + c] = x[i];
   }
   for (int e = tid; e < C * C; e += kThreads) {  // strictly upper blocks
     const int i = e / C, j = e % C;
-    if ((j >> 4) > (i >> 4)) sm.Xm[i * FLD + j] = 0.f;
+    if ((j >> 4) > (i >> 4)) sm.Nm[i * FLD + j] = 0.f;
   }
   __syncthreads();
+  // Blocks below, block row by block row: Y_j = sum_{m=j}^{i-1} N_im X_mj
+  // reads row i of N (and finished rows of X); after a barrier, X_ij =
+  // -X_ii Y_j replaces N_ij.
   {
     const int r = tid >> 4, c = tid & 15;  // one element of a 16x16 block
     for (int bi = 1; bi < NRB; ++bi) {
@@ -280,7 +286,7 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
         float s = 0.f;
         for (int bm = bj; bm < bi; ++bm) {
           const float *Nr = sm.Nm + (16 * bi + r) * FLD + 16 * bm;
-          const float *Xc = sm.Xm + (16 * bm) * FLD + 16 * bj + c;
+          const float *Xc = sm.Nm + (16 * bm) * FLD + 16 * bj + c;
 #pragma unroll
           for (int m = 0; m < 16; ++m) s = fmaf(Nr[m], Xc[m * FLD], s);
         }
@@ -288,22 +294,33 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
       }
       __syncthreads();
       for (int bj = 0; bj < bi; ++bj) {
-        const float *Xr = sm.Xm + (16 * bi + r) * FLD + 16 * bi;
+        const float *Xr = sm.Nm + (16 * bi + r) * FLD + 16 * bi;
         float s = 0.f;
 #pragma unroll
         for (int m = 0; m < 16; ++m) s = fmaf(Xr[m], sm.Ym[(bj * 16 + m) * 16 + c], s);
-        sm.Xm[(16 * bi + r) * FLD + 16 * bj + c] = -s;
+        sm.Nm[(16 * bi + r) * FLD + 16 * bj + c] = -s;
       }
       __syncthreads();
     }
   }
 
-  // ---- T^T (T = X diag(g)) as high and low parts, over N's storage; for
-  //      Wt with decay, column j carries w_j = b_L / b_j ----
+  // ---- T^T (T = X diag(g)) as high and low parts, over X's storage (so X
+  //      is first taken into registers); for Wt with decay, column j
+  //      carries w_j = b_L / b_j ----
+  constexpr int NE = C * C / kThreads;
+  static_assert(NE * kThreads == C * C, "T elements per thread");
+  float xt[NE];  // T^T[i][j] = T[j][i] = X[j][i] g_i, element e = tid + m * kThreads
+#pragma unroll
+  for (int m = 0; m < NE; ++m) {
+    const int e = tid + m * kThreads, i = e / C, j = e % C;
+    xt[m] = sm.Nm[j * FLD + i] * sm.gs[i];
+  }
+  __syncthreads();
   auto split_t = [&](bool weighted) {
-    for (int e = tid; e < C * C; e += kThreads) {
-      const int i = e / C, j = e % C;  // T^T[i][j] = T[j][i] = X[j][i] g_i
-      float x = sm.Xm[j * FLD + i] * sm.gs[i];
+#pragma unroll
+    for (int m = 0; m < NE; ++m) {
+      const int e = tid + m * kThreads, i = e / C, j = e % C;
+      float x = xt[m];
       if (weighted) x *= sm.wl[j];
       T hi, lo;
       split2<T>(x, hi, lo);
