@@ -94,35 +94,48 @@ def _gamma_heads(gamma, H):
 # LINEAR rule (elu+1 kernel, optional per-head decay, eps-stabilised normaliser)
 # ---------------------------------------------------------------------------
 
+def _row_decay(dec, S):
+    """A decay as one factor per state row: [...] (per head) is broadcast
+    over the r rows; [..., r] (per key channel) is used as is."""
+    return dec[..., None] if dec.ndim == S.ndim - 2 else dec
+
+
 def linear_step(S, z, fq, fk, v, gamma_bh, eps):
     """One token of causal linear attention, on features already mapped.
 
     S: [..., r, dv], z: [..., r], fq, fk: [..., r], v: [..., dv],
-    gamma_bh: [...] (decay per leading index).  Returns (o, S_new, z_new).
+    gamma_bh: [...] (decay per leading index) or [..., r] (one decay per key
+    channel, GLA).  Returns (o, S_new, z_new).
 
     State update ([WILA] section 4 with the decay of 5.1, applied to S and z):
         S_t = gamma * S_{t-1} + phi(k_t) v_t^T
         z_t = gamma * z_{t-1} + phi(k_t)
+    With a per-channel decay alpha_t ([EAV] 7.2, GLA: each entry keeps its
+    own state row, broadcast along the value axis) gamma becomes diag(alpha_t)
+    on the rows of S and elementwise on z.
     Read after the write ([EAV] section 5: write first, then read, so the
     token attends to itself), with eps in the denominator ([TAR]):
         o_t = phi(q_t)^T S_t / (phi(q_t) . z_t + eps)
     """
-    g = gamma_bh[..., None, None]
-    S_new = g * S + fk[..., :, None] * v[..., None, :]
-    z_new = gamma_bh[..., None] * z + fk
+    dec = _row_decay(gamma_bh, S)
+    S_new = dec[..., :, None] * S + fk[..., :, None] * v[..., None, :]
+    z_new = dec * z + fk
     num = np.einsum("...r,...rd->...d", fq, S_new)
     den = np.einsum("...r,...r->...", fq, z_new) + eps
     return num / den[..., None], S_new, z_new
 
 
 def linear_prefill(q, k, v, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1,
-                   S0=None, z0=None):
+                   S0=None, z0=None, alpha=None):
     """Causal linear attention over a whole sequence, token by token.
 
-    q, k: [B, H, N, d]; v: [B, H, N, dv]; gamma: [H] or None; S0: [B, H, d, dv]
-    or None (zero state); z0: [B, H, d] or None.
+    q, k: [B, H, N, d]; v: [B, H, N, dv]; gamma: [H] or None; alpha: [B, H,
+    N, d] per-channel decay or None (not together with gamma); S0: [B, H, d,
+    dv] or None (zero state); z0: [B, H, d] or None.
     Returns (o [B, H, N, dv], S_N [B, H, d, dv], z_N [B, H, d]) in float64.
     """
+    if alpha is not None and gamma is not None:
+        raise ValueError("gamma and alpha are alternatives")
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
     dv = v.shape[-1]
@@ -131,22 +144,30 @@ def linear_prefill(q, k, v, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1,
     S = np.zeros((B, H, d, dv)) if S0 is None else _f64(S0).copy()
     z = np.zeros((B, H, d)) if z0 is None else _f64(z0).copy()
     o = np.empty((B, H, N, dv))
+    al = None if alpha is None else _f64(alpha)
     for t in range(N):
         o[:, :, t], S, z = linear_step(S, z, fq[:, :, t], fk[:, :, t],
-                                       v[:, :, t], gam, eps)
+                                       v[:, :, t], gam if al is None else al[:, :, t],
+                                       eps)
     return o, S, z
 
 
-def linear_decode_step(q, k, v, S, z, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1):
+def linear_decode_step(q, k, v, S, z, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1,
+                       alpha=None):
     """One decode step against a persistent state: the same token body as
     the prefill ([LIO3] 'recurrent form': read once, add once per token).
 
-    q, k: [B, H, d]; v: [B, H, dv]; S: [B, H, d, dv]; z: [B, H, d].
+    q, k: [B, H, d]; v: [B, H, dv]; S: [B, H, d, dv]; z: [B, H, d];
+    alpha: [B, H, d] per-channel decay or None (not together with gamma).
     Returns (o [B, H, dv], S_new, z_new); the inputs are not modified.
     """
+    if alpha is not None and gamma is not None:
+        raise ValueError("gamma and alpha are alternatives")
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H = q.shape[:2]
     gam = np.broadcast_to(_gamma_heads(gamma, H)[None, :], (B, H))
+    if alpha is not None:
+        gam = _f64(alpha)
     return linear_step(_f64(S), _f64(z), feature_map(q, fmap),
                        feature_map(k, fmap), v, gam, eps)
 

@@ -457,4 +457,87 @@ def pin_gdn_alpha_one_and_split(orc):
     np.testing.assert_allclose(Sd, S, rtol=1e-12)
 
 
+# --- linear rule with a per-channel decay (GLA) ----------------------------
+
+def pin_gla_quadratic_form(orc):
+    """Unrolling S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T gives the score
+    A_ti = sum_f phi(q_t)_f phi(k_i)_f prod_{m=i+1..t} alpha_m,f for i <= t
+    (Efficient attention variants 7.2: each key channel keeps its own row);
+    brute force on tiny inputs with d != dv, from a nonzero initial state."""
+    rng = np.random.default_rng(31)
+    N, d, dv, eps = 9, 3, 5, 1e-3
+    q = rng.normal(size=(N, d))
+    k = rng.normal(size=(N, d))
+    v = rng.normal(size=(N, dv))
+    al = rng.uniform(0.4, 1.0, size=(N, d))
+    S0 = rng.uniform(0.0, 1.0, size=(d, dv))
+    z0 = rng.uniform(0.5, 1.0, size=d)
+    fq, fk = orc.phi_elu1(q), orc.phi_elu1(k)
+    ref = np.zeros((N, dv))
+    for t in range(N):
+        dec0 = np.prod(al[:t + 1], axis=0)          # decay of the initial state
+        num = (fq[t] * dec0) @ S0
+        den = (fq[t] * dec0) @ z0
+        for i in range(t + 1):
+            a = np.sum(fq[t] * fk[i] * np.prod(al[i + 1:t + 1], axis=0))
+            num = num + a * v[i]
+            den = den + a
+        ref[t] = num / (den + eps)
+    o, _, _ = orc.linear_prefill(_bh(q), _bh(k), _bh(v), eps=eps, S0=_bh(S0), z0=_bh(z0),
+                                 alpha=_bh(al))
+    np.testing.assert_allclose(o[0, 0], ref, rtol=1e-12, atol=1e-14)
+
+
+def pin_gla_one_hot_keys(orc):
+    """Identity features and one-hot keys: each state row only decays by its
+    own channel's alpha and receives the values written to it (closed form
+    per row), z likewise."""
+    d, dv = 3, 2
+    k = np.array([[1, 0, 0], [0, 0, 1], [1, 0, 0], [0, 1, 0]], dtype=np.float64)
+    v = np.array([[1.0, 2.0], [3.0, -1.0], [0.5, 0.25], [4.0, 4.0]])
+    al = np.array([[0.5, 0.9, 0.8], [0.25, 0.5, 0.5], [1.0, 0.75, 0.5], [0.5, 0.5, 0.25]])
+    S0 = np.ones((d, dv))
+    _, S, z = orc.linear_prefill(_bh(k), _bh(k), _bh(v), fmap=orc.FMAP_IDENTITY, S0=_bh(S0),
+                                 z0=_bh(np.ones(d)), alpha=_bh(al))
+    want_S = np.empty((d, dv))
+    want_z = np.empty(d)
+    for f in range(d):
+        row, zz = S0[f].copy(), 1.0
+        for t in range(4):
+            row = al[t, f] * row + k[t, f] * v[t]
+            zz = al[t, f] * zz + k[t, f]
+        want_S[f], want_z[f] = row, zz
+    np.testing.assert_allclose(S[0, 0], want_S, rtol=1e-15)
+    np.testing.assert_allclose(z[0, 0], want_z, rtol=1e-15)
+    assert abs(S[0, 0][1, 0] - (0.9 * 0.5 * 0.75 * 1.0 * 0.5 + 4.0)) < 1e-15
+
+
+def pin_gla_uniform_is_gamma_and_split(orc):
+    """A per-channel decay equal to gamma_h on every channel and token is the
+    per-head decay; with varying alpha, a split sequence with carried state
+    and a decode step after prefill give the same result."""
+    rng = np.random.default_rng(32)
+    B, H, N, d, dv = 1, 2, 11, 4, 3
+    q = rng.normal(size=(B, H, N, d))
+    k = rng.normal(size=(B, H, N, d))
+    v = rng.normal(size=(B, H, N, dv))
+    gamma = np.array([0.9, 0.6])
+    al_u = np.broadcast_to(gamma[None, :, None, None], (B, H, N, d)).copy()
+    og, Sg, zg = orc.linear_prefill(q, k, v, gamma=gamma)
+    oa, Sa, za = orc.linear_prefill(q, k, v, alpha=al_u)
+    np.testing.assert_allclose(oa, og, rtol=1e-14)
+    np.testing.assert_allclose(Sa, Sg, rtol=1e-14)
+    al = rng.uniform(0.5, 1.0, size=(B, H, N, d))
+    o, S, z = orc.linear_prefill(q, k, v, alpha=al)
+    o1, S1, z1 = orc.linear_prefill(q[:, :, :4], k[:, :, :4], v[:, :, :4], alpha=al[:, :, :4])
+    o2, S2, z2 = orc.linear_prefill(q[:, :, 4:10], k[:, :, 4:10], v[:, :, 4:10], S0=S1, z0=z1,
+                                    alpha=al[:, :, 4:10])
+    np.testing.assert_allclose(np.concatenate([o1, o2], axis=2), o[:, :, :10], rtol=1e-12)
+    od, Sd, zd = orc.linear_decode_step(q[:, :, 10], k[:, :, 10], v[:, :, 10], S2, z2,
+                                        alpha=al[:, :, 10])
+    np.testing.assert_allclose(od, o[:, :, 10], rtol=1e-12)
+    np.testing.assert_allclose(Sd, S, rtol=1e-12)
+    np.testing.assert_allclose(zd, z, rtol=1e-12)
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

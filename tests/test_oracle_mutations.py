@@ -20,12 +20,16 @@ def _fresh():
     return mod
 
 
+def _rows(gam, S):
+    return gam[..., None] if gam.ndim == S.ndim - 2 else gam
+
+
 def _read_before_write(m):
     def step(S, z, fq, fk, v, gam, eps):
         num = np.einsum("...r,...rd->...d", fq, S)
         den = np.einsum("...r,...r->...", fq, z) + eps
-        S2 = gam[..., None, None] * S + fk[..., :, None] * v[..., None, :]
-        z2 = gam[..., None] * z + fk
+        S2 = _rows(gam, S)[..., :, None] * S + fk[..., :, None] * v[..., None, :]
+        z2 = _rows(gam, S) * z + fk
         return num / den[..., None], S2, z2
     m.linear_step = step
 
@@ -59,7 +63,7 @@ def _exp_everywhere(m):
 def _decay_off_by_one(m):
     orig = m.linear_step
     def step(S, z, fq, fk, v, gam, eps):
-        return orig(S, z, fq, gam[..., None] * fk, v, gam, eps)
+        return orig(S, z, fq, _rows(gam, S) * fk, v, gam, eps)
     m.linear_step = step
 
 
@@ -68,8 +72,8 @@ def _outer_transposed(m):
         d, dv = S.shape[-2:]
         upd = (v[..., :, None] * fk[..., None, :])
         upd = upd.reshape(upd.shape[:-2] + (d, dv)) if upd.size == S.size else upd
-        S2 = gam[..., None, None] * S + upd
-        z2 = gam[..., None] * z + fk
+        S2 = _rows(gam, S)[..., :, None] * S + upd
+        z2 = _rows(gam, S) * z + fk
         num = np.einsum("...r,...rd->...d", fq, S2)
         return num / (np.einsum("...r,...r->...", fq, z2) + eps)[..., None], S2, z2
     m.linear_step = step
@@ -163,12 +167,39 @@ def _gdn_decay_on_write_too(m):
     m.delta_step = step
 
 
+def _gla_decay_on_value_axis(m):
+    def step(S, z, fq, fk, v, gam, eps):
+        if gam.ndim == S.ndim - 1 and S.shape[-1] != S.shape[-2]:
+            dv = S.shape[-1]
+            g = np.resize(gam, gam.shape[:-1] + (dv,))
+            S2 = g[..., None, :] * S + fk[..., :, None] * v[..., None, :]
+        else:
+            S2 = _rows(gam, S)[..., :, None] * S + fk[..., :, None] * v[..., None, :]
+        z2 = _rows(gam, S) * z + fk
+        num = np.einsum("...r,...rd->...d", fq, S2)
+        den = np.einsum("...r,...r->...", fq, z2) + eps
+        return num / den[..., None], S2, z2
+    m.linear_step = step
+
+
+def _gla_decay_after_write(m):
+    def step(S, z, fq, fk, v, gam, eps):
+        r = _rows(gam, S)
+        S2 = r[..., :, None] * (S + fk[..., :, None] * v[..., None, :])
+        z2 = r * (z + fk)
+        num = np.einsum("...r,...rd->...d", fq, S2)
+        den = np.einsum("...r,...r->...", fq, z2) + eps
+        return num / den[..., None], S2, z2
+    m.linear_step = step
+
+
 MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _exp_everywhere, _decay_off_by_one, _outer_transposed,
            _quadratic_strict_mask, _delta_not_transposed, _delta_wrong_sign,
            _delta_output_before_update, _delta_gate_on_value_only,
            _delta_dropped_correction, _gdn_error_on_undecayed_state,
-           _gdn_decay_after_write, _gdn_decay_on_write_too]
+           _gdn_decay_after_write, _gdn_decay_on_write_too, _gla_decay_on_value_axis,
+           _gla_decay_after_write]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
