@@ -87,7 +87,9 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
             o=None, workspace=None, alpha=None):
     """Chunked prefill over [B,H,N,*] sequences (see la_prefill).
 
-    rule "linear": fmap defaults to "elu1"; gamma [H] fp32 or None; eps >= 0.
+    rule "linear": fmap defaults to "elu1"; gamma [H] fp32 or None; eps >= 0;
+                   or, instead of gamma, alpha [B,H,N,d] fp32: a decay per key
+                   channel and token in [0.1, 1].
     rule "delta":  fmap "identity"; g [B,H,N] fp32 required; alpha [B,H,N]
                    fp32 state decay in (0, 1] or None.
     Returns (o, S_out, z_out); the states are None unless requested
@@ -97,8 +99,10 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
         fmap = "elu1" if rule == "linear" else "identity"
     _need_gpu(q, k, v, gamma, g, alpha, S_in, z_in, S_out, z_out, o, workspace)
     _need_f32(gamma, g, alpha, S_in, z_in, S_out, z_out)
-    if alpha is not None and alpha.shape != q.shape[:3]:
-        raise ValueError("alpha must be [B,H,N]")
+    if alpha is not None:
+        want = q.shape if rule == "linear" else q.shape[:3]
+        if tuple(alpha.shape) != tuple(want):
+            raise ValueError(f"alpha must be {list(want)} for rule {rule!r}")
     a = _prefill_args(q, k, v, rule, fmap, gamma, g, eps, alpha)
     B, H, N, d = q.shape
     dv = v.shape[3]
@@ -128,7 +132,8 @@ def decode_step(q, k, v, S, z=None, *, rule="linear", fmap=None, gamma=None,
                 g=None, eps=1e-6, o=None, alpha=None):
     """One token per sequence: q, k [B,H,d], v [B,H,dv]; S [B,H,d,dv] (and z
     [B,H,d] for "linear") are updated in place; "delta" takes g [B,H] and
-    an optional decay alpha [B,H].  Returns o [B,H,dv]."""
+    an optional decay alpha [B,H]; "linear" an optional per-channel decay
+    alpha [B,H,d] instead of gamma.  Returns o [B,H,dv]."""
     if fmap is None:
         fmap = "elu1" if rule == "linear" else "identity"
     _need_gpu(q, k, v, S, z, gamma, g, alpha, o)
@@ -141,6 +146,10 @@ def decode_step(q, k, v, S, z=None, *, rule="linear", fmap=None, gamma=None,
     dv = v.shape[2]
     if S.shape != (B, H, d, dv) or (z is not None and z.shape != (B, H, d)):
         raise ValueError("state shape mismatch")
+    if alpha is not None:
+        want = (B, H, d) if rule == "linear" else (B, H)
+        if tuple(alpha.shape) != want:
+            raise ValueError(f"alpha must be {list(want)} for rule {rule!r}")
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
     a = _lib.DecodeArgs()

@@ -154,7 +154,10 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   const int BH = a->B * a->H;
   const bool linear = a->rule == LA_RULE_LINEAR;
   if (linear) {
-    if (a->g || a->alpha || !(a->eps >= 0.f) || !std::isfinite(a->eps)) return LA_EINVAL;
+    if (a->g || (a->alpha && a->gamma) || !(a->eps >= 0.f) || !std::isfinite(a->eps))
+      return LA_EINVAL;
+    // one head's per-channel decay (fp32) must be addressable with 32-bit offsets
+    if (a->alpha && (size_t)a->N * a->d * 4 > kMaxHeadBytes) return LA_EUNSUPPORTED;
   } else {
     if (!a->g && BH > 0 && a->N > 0) return LA_EINVAL;
     if (a->gamma || a->z_in || a->z_out) return LA_EINVAL;
@@ -230,7 +233,8 @@ int la_decode_step(const la_decode_args *a, void *stream) {
     if (a->fmap != LA_FMAP_IDENTITY || a->gamma || a->z) return LA_EINVAL;
     if (BH > 0 && !a->g) return LA_EINVAL;
   } else {
-    if (a->g || a->alpha || !(a->eps >= 0.f) || !std::isfinite(a->eps)) return LA_EINVAL;
+    if (a->g || (a->alpha && a->gamma) || !(a->eps >= 0.f) || !std::isfinite(a->eps))
+      return LA_EINVAL;
     if (BH > 0 && !a->z) return LA_EINVAL;
   }
   if (BH == 0) return LA_OK;

@@ -4,6 +4,8 @@
 // "LLM inference optimisation (3)", recurrent form: read once, add once):
 //     S <- gamma S + phi(k) v^T,  z <- gamma z + phi(k)
 //     o  = S^T phi(q) / (phi(q) . z + eps)
+//   or, with a per-key-channel decay ("Efficient attention variants" 7.2,
+//   GLA), gamma replaced by alpha_r on row r of S and entry r of z.
 // DELTA ("What Is Linear Attention?" 5.2-5.3), with the optional scalar
 // decay alpha of Gated DeltaNet ("Efficient attention variants" 7.4: decay
 // first, the error is taken on the decayed state):
@@ -42,7 +44,7 @@ template <typename T, int VEC, bool DELTA>
 __global__ void __launch_bounds__(kDecThreads)
 decode_kernel(DecodeParams p) {
   constexpr int ROWS = 64 / VEC;  // rows per thread at most (d <= 128)
-  __shared__ float s_q[LA_MAXD], s_k[LA_MAXD], s_v[LA_MAXD];
+  __shared__ float s_q[LA_MAXD], s_k[LA_MAXD], s_v[LA_MAXD], s_al[LA_MAXD];
   __shared__ float s_part[2][kDecThreads * VEC];
   __shared__ float s_a[LA_MAXD], s_b[LA_MAXD];
   __shared__ float s_red[4];
@@ -85,9 +87,11 @@ decode_kernel(DecodeParams p) {
     s_q[t] = xq;
     s_k[t] = xk;
     if (!DELTA) zold = p.z[(size_t)bh * d + t];
+    if (!DELTA) s_al[t] = p.alpha ? p.alpha[(size_t)bh * d + t] : 1.f;
   }
   if (t < dv) s_v[t] = to_f32(v[t]);
   const float gam = (!DELTA && p.gamma) ? p.gamma[bh % p.H] : 1.f;
+  const bool chan = !DELTA && p.alpha != nullptr;  // per-channel decay
   const float gate = DELTA ? p.g[bh] : 0.f;
   const float al = (DELTA && p.alpha) ? p.alpha[bh] : 1.f;
   __syncthreads();
@@ -104,9 +108,10 @@ decode_kernel(DecodeParams p) {
       const int r = rg + RG * m;
       const bool ok = active && r < d;
       const float fk = ok ? s_k[r] : 0.f, fq = ok ? s_q[r] : 0.f;
+      const float gr = chan ? (ok ? s_al[r] : 1.f) : gam;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const float sn = fmaf(gam, sr[m][e], fk * s_v[c0 + e]);
+        const float sn = fmaf(gr, sr[m][e], fk * s_v[c0 + e]);
         sr[m][e] = sn;
         acc[e] = fmaf(fq, sn, acc[e]);
       }
@@ -119,7 +124,7 @@ decode_kernel(DecodeParams p) {
     // normaliser: z <- gamma z + phi(k); den = phi(q) . z_new
     float dz = 0.f;
     if (t < d) {
-      const float zn = fmaf(gam, zold, s_k[t]);
+      const float zn = fmaf(chan ? s_al[t] : gam, zold, s_k[t]);
       p.z[(size_t)bh * d + t] = zn;
       dz = s_q[t] * zn;
     }

@@ -48,11 +48,26 @@
 //                   the last segment writes (S_out, z_out).
 // With one segment only chunk_kernel runs, from (S_in, z_in).
 //
+// Per-key-channel decay (GLA, "Efficient attention variants" 7.2; the CH
+// instantiations): S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T, z alike.
+// With lb_j = sum_{t<=j} log alpha_t (chunk-local, per channel) and a
+// reference token m in the middle of the chunk, the score of query j and key
+// i <= j is sum_f phi(q_j)_f phi(k_i)_f exp(lb_j - lb_i)_f = q^_j . k^_i with
+//     q^_j = phi(q_j) (.) exp(lb_j - lb_m),   k^_i = phi(k_i) (.) exp(lb_m - lb_i)
+// (every factor within alpha^(-C/2) of 1, so alpha >= 0.1 keeps them inside
+// the fp32/bf16 range), the state read is q^_j . (diag(exp(lb_m)) S-), and
+//     S+ = diag(exp(lb_L - lb_m)) (diag(exp(lb_m)) S- + K^^T V)   (z alike).
+// The prefix sums are taken per chunk in LDS (one thread per channel); a
+// segment summary also carries the segment's total log decay per channel,
+// which the scan applies row by row.
+//
 // Data layout: q, k [BH, N, d], v, o [BH, N, dv] (row-major, dtype T);
-// workspace slots [nseg][BH][d*dv + d] fp32 (state then normaliser).
+// alpha [BH, N, d] fp32 (CH); workspace slots [nseg][BH][d*dv + 2d] fp32
+// (state, normaliser, then the segment's log decay per channel for CH).
 // Global traffic goes through buffer resources (bounds by offset, no
 // branches between a load and its use), issued one chunk ahead.
 #include <atomic>
+#include <type_traits>
 
 #include "la_common.hpp"
 #include "la_internal.hpp"
@@ -62,6 +77,12 @@ namespace {
 
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kMaxSeg = 32;  // most segments per sequence
+
+// fp32 elements of one workspace slot record: S (d x dv), z (d), and the
+// segment's log decay per channel (d; used with a per-channel decay).
+__host__ __device__ inline size_t ws_rec(int d, int dv) {
+  return (size_t)d * dv + 2 * (size_t)d;
+}
 
 template <typename T, int DK_, int DV_, int C_, int NW_>
 struct Cfg {
@@ -125,6 +146,33 @@ struct ChunkRegs {
   typename CF::vec q[CF::RQ], k[CF::RQ], v[CF::RV];
 };
 
+// Per-key-channel decay (CH): this thread's alpha values for its q/k rows
+// (VEC channels per row), and the LDS of one chunk's prefix sums.
+template <class CF>
+struct ChanRegs {
+  f32x4 a[CF::RQ][CF::VEC / 4];
+};
+
+template <class CF>
+struct alignas(16) SmemChan {
+  static constexpr int LDL = CF::DK + 4;  // row stride of lb
+  float lb[CF::C * LDL];  // lb[j][f] = sum_{t<=j} log alpha_t,f within the chunk
+  float bm[CF::DK];       // exp(lb[m][f]) for the reference token m
+  float bl[CF::DK];       // exp(lb[L-1][f] - lb[m][f])
+  float tot[CF::DK];      // segment summaries: log decay of the segment so far
+};
+struct NoChan {};
+template <class CF>
+__device__ __forceinline__ const SmemChan<CF> *chan_ptr(const SmemChan<CF> &s) {
+  return &s;
+}
+template <class CF>
+__device__ __forceinline__ const SmemChan<CF> *chan_ptr(const NoChan &) {
+  return nullptr;
+}
+template <class CF, bool CH>
+using ChanSmem = typename std::conditional<CH, SmemChan<CF>, NoChan>::type;
+
 // Per-head buffer resources of q, k, v and o.
 struct HeadBufs {
   __amdgpu_buffer_rsrc_t q, k, v, o;
@@ -168,6 +216,78 @@ __device__ __forceinline__ typename Vec16<T>::type load_block(
   }
 }
 
+// alpha rows of a chunk for this thread's q/k rows (zeros outside; they
+// become factors of 1 in chan_logs).
+template <class CF, bool VK>
+__device__ __forceinline__ void chan_prefetch(ChanRegs<CF> &A, __amdgpu_buffer_rsrc_t ra,
+                                              const PrefillParams &p, int c0, int Lc) {
+  const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
+#pragma unroll
+  for (int r = 0; r < CF::RQ; ++r) {
+    const int row = qrg * CF::RQ + r;
+    const size_t t = (size_t)(c0 + row);
+#pragma unroll
+    for (int h = 0; h < CF::VEC / 4; ++h) {
+      const int col = qcb * CF::VEC + 4 * h;
+      if constexpr (VK) {
+        A.a[r][h] = buf_load16<float>(
+            ra, row < Lc && col < p.d ? (uint32_t)((t * p.d + col) * 4) : kOOB);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          A.a[r][h][e] = buf_load1(
+              ra, row < Lc && col + e < p.d ? (uint32_t)((t * p.d + col + e) * 4) : kOOB,
+              (float *)nullptr);
+      }
+    }
+  }
+}
+
+// log alpha of this thread's elements into lb (0 for rows past the chunk and
+// columns past d, i.e. a factor of 1).
+template <class CF>
+__device__ __forceinline__ void chan_logs(const ChanRegs<CF> &A, SmemChan<CF> &sc, int d,
+                                          int Lc) {
+  const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
+#pragma unroll
+  for (int r = 0; r < CF::RQ; ++r) {
+    const int row = qrg * CF::RQ + r;
+#pragma unroll
+    for (int h = 0; h < CF::VEC / 4; ++h) {
+      const int col = qcb * CF::VEC + 4 * h;
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        x[e] = row < Lc && col + e < d ? __logf(A.a[r][h][e]) : 0.f;
+      *reinterpret_cast<f32x4 *>(sc.lb + row * SmemChan<CF>::LDL + col) = x;
+    }
+  }
+}
+
+// Prefix sums of lb down each column (one thread per channel), the state
+// factors bm and bl, and (segment summaries) the running total.
+template <class CF>
+__device__ __forceinline__ int chan_ref(int Lc) {
+  return min(CF::C / 2, Lc) - 1;
+}
+template <class CF>
+__device__ __forceinline__ void chan_prefix(SmemChan<CF> &sc, int Lc, bool total) {
+  constexpr int LDL = SmemChan<CF>::LDL;
+  const int t = threadIdx.x;
+  if (t < CF::DK) {
+    float x = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < CF::C; ++j) {
+      x += sc.lb[j * LDL + t];
+      sc.lb[j * LDL + t] = x;
+    }
+    const float lm = sc.lb[chan_ref<CF>(Lc) * LDL + t];
+    sc.bm[t] = __expf(lm);
+    sc.bl[t] = __expf(x - lm);  // x = lb[C-1] = lb[Lc-1] (factors of 1 past Lc)
+    if (total) sc.tot[t] += x;
+  }
+}
+
 template <class CF, bool WITH_Q, bool VK>
 __device__ __forceinline__ void prefetch(ChunkRegs<CF> &R, const PrefillParams &p,
                                          const HeadBufs &hb, int c0, int Lc) {
@@ -194,25 +314,31 @@ __device__ __forceinline__ void prefetch(ChunkRegs<CF> &R, const PrefillParams &
 // meet zero keys and zero state rows).  The feature map and the column mask
 // are uniform per launch and taken as branches, so the common case carries
 // no per-element selects; key weights are 1 for a full chunk without decay.
-template <class CF, bool WITH_Q, bool ELU>
+template <class CF, bool WITH_Q, bool ELU, bool CH>
 __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R, typename CF::type *Qs,
                                             typename CF::type *Ks, const float *pw,
-                                            const PrefillParams &p, int Lc) {
+                                            const PrefillParams &p, int Lc,
+                                            const SmemChan<CF> *sc) {
   using T = typename CF::type;
   constexpr int VEC = CF::VEC;
   const bool weighted = p.gamma != nullptr || Lc < CF::C;
   const bool colmask = p.d < CF::DK;  // feature columns past d
   const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
   const int col0 = qcb * VEC;
+  // per-channel decay: q^ = phi(q) exp(lb_row - lb_m), k^ = phi(k) exp(lb_m - lb_row)
+  constexpr int LDL = SmemChan<CF>::LDL;
+  const float *lbm = CH ? sc->lb + chan_ref<CF>(Lc) * LDL + col0 : nullptr;
 #pragma unroll
   for (int r = 0; r < CF::RQ; ++r) {
     const int row = qrg * CF::RQ + r;
+    const float *lbr = CH ? sc->lb + row * LDL + col0 : nullptr;
     float x[VEC];
     if constexpr (WITH_Q) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const float xq = to_f32(R.q[r][e]);
         x[e] = ELU ? phi_elu1(xq) : xq;
+        if constexpr (CH) x[e] *= __expf(lbr[e] - lbm[e]);
       }
       lds_store_n<T, VEC>(Qs + row * CF::QLD + col0, x);
     }
@@ -220,6 +346,7 @@ __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R, typename CF:
     for (int e = 0; e < VEC; ++e) {
       const float xk = to_f32(R.k[r][e]);
       x[e] = ELU ? phi_elu1(xk) : xk;
+      if constexpr (CH) x[e] *= __expf(lbm[e] - lbr[e]);
     }
     // key weights gamma^(Lc-1-j), 0 past the chunk
     const float w = !weighted ? 1.f : row < Lc ? pw[Lc - 1 - row] : 0.f;
@@ -235,15 +362,16 @@ __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R, typename CF:
   }
 }
 
-template <class CF, bool WITH_Q>
+template <class CF, bool WITH_Q, bool CH = false>
 __device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type *Qs,
                                        typename CF::type *Ks, typename CF::type *Vs,
-                                       const float *pw, const PrefillParams &p, int Lc) {
+                                       const float *pw, const PrefillParams &p, int Lc,
+                                       const SmemChan<CF> *sc = nullptr) {
   using V = typename CF::vec;
   if (p.fmap != 0)
-    commit_rows<CF, WITH_Q, true>(R, Qs, Ks, pw, p, Lc);
+    commit_rows<CF, WITH_Q, true, CH>(R, Qs, Ks, pw, p, Lc, sc);
   else
-    commit_rows<CF, WITH_Q, false>(R, Qs, Ks, pw, p, Lc);
+    commit_rows<CF, WITH_Q, false, CH>(R, Qs, Ks, pw, p, Lc, sc);
   const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
 #pragma unroll
   for (int r = 0; r < CF::RV; ++r) {
@@ -324,6 +452,22 @@ __device__ __forceinline__ void rescale_and_copy_state(typename CF::type *St,
       if (tn < CF::NCT)
         lds_store4(St + (16 * tn + li) * CF::QLD + 16 * tf + 4 * lg, Sacc[a][b][0],
                    Sacc[a][b][1], Sacc[a][b][2], Sacc[a][b][3]);
+    }
+  }
+}
+
+// Per-row factors on this wave's [S | z] tiles (per-channel decay).
+template <class CF>
+__device__ __forceinline__ void chan_scale(f32x4 (&Sacc)[CF::FPW][CF::TPW], const float *fac,
+                                           int wv, int lg) {
+#pragma unroll
+  for (int a = 0; a < CF::FPW; ++a) {
+    const int tf = srow<CF>(wv, a);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float f = fac[16 * tf + 4 * lg + r];
+#pragma unroll
+      for (int b = 0; b < CF::TPW; ++b) Sacc[a][b][r] *= f;
     }
   }
 }
@@ -467,11 +611,13 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillPa
 
 }
 
-template <class CF, bool VK>
-__global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p) {
+template <class CF, bool VK, bool CH>
+__global__ void __launch_bounds__(CF::NT, CH ? (CF::WPE < 2 ? CF::WPE : 2) : CF::WPE)
+    chunk_kernel(PrefillParams p) {
   using T = typename CF::type;
   using V = typename CF::vec;
   __shared__ SmemChunk<CF> sm;
+  __shared__ ChanSmem<CF, CH> sc;  // per-channel decay (CH) only
 
   const int seg = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -487,7 +633,7 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p)
   // (S_in, z_in) with a single segment
   const float *S0, *z0;
   if (p.nseg > 1) {
-    S0 = p.ws + ((size_t)seg * p.BH + bh) * ((size_t)d * dv + d);
+    S0 = p.ws + ((size_t)seg * p.BH + bh) * ws_rec(d, dv);
     z0 = S0 + (size_t)d * dv;
   } else {
     S0 = p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr;
@@ -499,15 +645,32 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p)
   // issue order, so waiting for the state does not wait for the chunk)
   ChunkRegs<CF> R;
   prefetch<CF, true, VK>(R, p, hb, t_begin, min(CF::C, N - t_begin));
+  [[maybe_unused]] ChanRegs<CF> A;
+  [[maybe_unused]] const __amdgpu_buffer_rsrc_t ra =
+      CH ? buf_rsrc(p.alpha + (size_t)bh * N * d, (uint32_t)((size_t)N * d * 4)) : hb.q;
+  if constexpr (CH) chan_prefetch<CF, VK>(A, ra, p, t_begin, min(CF::C, N - t_begin));
   fill_powers<CF>(sm.pw, decay ? log2f(p.gamma[bh % p.H]) : 0.f);
   __syncthreads();
-  rescale_and_copy_state<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - t_begin)], decay, wv, li,
-                             lg);
+  if constexpr (!CH)
+    rescale_and_copy_state<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - t_begin)], decay, wv, li,
+                               lg);
 
   const int rb = wv % CF::NRB, cg = wv / CF::NRB;  // output role
   for (int c0 = t_begin; c0 < t_end; c0 += CF::C) {
     const int Lc = min(CF::C, N - c0);
-    commit<CF, true>(R, sm.Qs, sm.Ks, sm.Vs, sm.pw, p, Lc);
+    if constexpr (CH) {  // the chunk's per-channel decay prefix sums
+      chan_logs<CF>(A, sc, d, Lc);
+      __syncthreads();
+      chan_prefix<CF>(sc, Lc, false);
+      __syncthreads();
+    }
+    commit<CF, true, CH>(R, sm.Qs, sm.Ks, sm.Vs, sm.pw, p, Lc, chan_ptr<CF>(sc));
+    if constexpr (CH) {  // state read from diag(exp(lb_m)) S-
+      chan_scale<CF>(Sacc, sc.bm, wv, lg);
+      rescale_and_copy_state<CF>(sm.St, Sacc, 1.f, false, wv, li, lg);
+      if (c0 + CF::C < t_end)
+        chan_prefetch<CF, VK>(A, ra, p, c0 + CF::C, min(CF::C, N - c0 - CF::C));
+    }
     if (c0 + CF::C < t_end)
       prefetch<CF, true, VK>(R, p, hb, c0 + CF::C, min(CF::C, N - c0 - CF::C));
     __syncthreads();
@@ -526,12 +689,16 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p)
     }
 
     // ---- carry the state across the chunk ----
-    // (the accumulator already carries gamma^Lc: scaled before the copy)
+    // (the accumulator already carries gamma^Lc, or diag(exp(lb_m)) with a
+    // per-channel decay: scaled before the copy)
     state_update<CF>(Sacc, sm.Ks, sm.Vs, 1.f, false, wv, li, lg);
+    if constexpr (CH) chan_scale<CF>(Sacc, sc.bl, wv, lg);
     __syncthreads();
-    if (c0 + CF::C < t_end)
-      rescale_and_copy_state<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - c0 - CF::C)], decay, wv,
-                                 li, lg);
+    if constexpr (!CH) {
+      if (c0 + CF::C < t_end)
+        rescale_and_copy_state<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - c0 - CF::C)], decay,
+                                   wv, li, lg);
+    }
     // 16-byte row stores of the output tile
     {
       const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
@@ -562,10 +729,11 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) chunk_kernel(PrefillParams p)
 
 // Phase 1: each segment's own contribution, from a zero state (all but the
 // last segment; those are whole multiples of the chunk length).
-template <class CF, bool VK>
+template <class CF, bool VK, bool CH>
 __global__ void __launch_bounds__(CF::NT, CF::WPE) summary_kernel(PrefillParams p) {
   using T = typename CF::type;
   __shared__ SmemSummary<CF> sm;
+  __shared__ ChanSmem<CF, CH> sc;  // per-channel decay (CH) only
   const int seg = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -578,6 +746,13 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) summary_kernel(PrefillParams 
 
   ChunkRegs<CF> R;
   prefetch<CF, false, VK>(R, p, hb, t_begin, CF::C);
+  [[maybe_unused]] ChanRegs<CF> A;
+  [[maybe_unused]] const __amdgpu_buffer_rsrc_t ra =
+      CH ? buf_rsrc(p.alpha + (size_t)bh * p.N * d, (uint32_t)((size_t)p.N * d * 4)) : hb.q;
+  if constexpr (CH) {
+    chan_prefetch<CF, VK>(A, ra, p, t_begin, CF::C);
+    if (threadIdx.x < CF::DK) sc.tot[threadIdx.x] = 0.f;
+  }
   fill_powers<CF>(sm.pw, decay ? log2f(p.gamma[bh % p.H]) : 0.f);
 
   f32x4 Sacc[CF::FPW][CF::TPW];
@@ -588,32 +763,56 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) summary_kernel(PrefillParams 
   __syncthreads();
   const float gC = sm.pw[CF::C];
   for (int c0 = t_begin; c0 < t_end; c0 += CF::C) {
-    commit<CF, false>(R, nullptr, sm.Ks, sm.Vs, sm.pw, p, CF::C);
+    if constexpr (CH) {
+      chan_logs<CF>(A, sc, d, CF::C);
+      __syncthreads();
+      chan_prefix<CF>(sc, CF::C, true);
+      __syncthreads();
+    }
+    commit<CF, false, CH>(R, nullptr, sm.Ks, sm.Vs, sm.pw, p, CF::C, chan_ptr<CF>(sc));
+    if constexpr (CH) {
+      chan_scale<CF>(Sacc, sc.bm, wv, lg);
+      if (c0 + CF::C < t_end) chan_prefetch<CF, VK>(A, ra, p, c0 + CF::C, CF::C);
+    }
     if (c0 + CF::C < t_end) prefetch<CF, false, VK>(R, p, hb, c0 + CF::C, CF::C);
     __syncthreads();
     state_update<CF>(Sacc, sm.Ks, sm.Vs, gC, decay, wv, li, lg);
+    if constexpr (CH) chan_scale<CF>(Sacc, sc.bl, wv, lg);
     __syncthreads();
   }
-  float *dst = p.ws + ((size_t)(seg + 1) * p.BH + bh) * ((size_t)d * dv + d);
+  float *dst = p.ws + ((size_t)(seg + 1) * p.BH + bh) * ws_rec(d, dv);
   store_state<CF>(Sacc, dst, dst + (size_t)d * dv, d, dv, wv, li, lg);
+  if constexpr (CH) {  // the segment's log decay per channel (own thread's sum)
+    if (threadIdx.x < d) dst[(size_t)d * dv + d + threadIdx.x] = sc.tot[threadIdx.x];
+  }
 }
 
 // Phase 2: prefix over segments, in place: slot 0 <- (S_in, z_in),
 // slot s <- gamma^Lseg slot (s-1) + dS_(s-1) for s >= 1 (dS_(s-1) sits in
-// slot s).  One thread per record element; every record is loaded before
-// the dependent chain starts.
+// slot s; with a per-channel decay the factor of row f is exp of the
+// segment's log decay of channel f, stored with dS).  One thread per record
+// element; every record is loaded before the dependent chain starts.
+template <bool CH>
 __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
   const int bh = blockIdx.y;
-  const size_t rec = (size_t)p.d * p.dv + p.d;
+  const size_t dd = (size_t)p.d * p.dv;
+  const size_t rec = dd + p.d;               // scanned elements: S then z
+  const size_t wr = ws_rec(p.d, p.dv);       // slot record stride
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= rec) return;
   const float gL = p.gamma ? exp2f((float)p.seg_len * log2f(p.gamma[bh % p.H])) : 1.f;
-  const size_t dd = (size_t)p.d * p.dv;
-  float *base = p.ws + (size_t)bh * rec + e;
-  const size_t stride = (size_t)p.BH * rec;
+  float *base = p.ws + (size_t)bh * wr + e;
+  const size_t stride = (size_t)p.BH * wr;
   float dS[kMaxSeg];
 #pragma unroll
   for (int s = 1; s < kMaxSeg; ++s) dS[s] = s < p.nseg ? base[s * stride] : 0.f;
+  [[maybe_unused]] float lgd[kMaxSeg];
+  if constexpr (CH) {
+    const size_t f = e < dd ? e / p.dv : e - dd;  // the element's state row
+    const float *ld = p.ws + (size_t)bh * wr + dd + p.d + f;
+#pragma unroll
+    for (int s = 1; s < kMaxSeg; ++s) lgd[s] = s < p.nseg ? ld[s * stride] : 0.f;
+  }
   float acc;
   if (e < dd)
     acc = p.S_in ? p.S_in[(size_t)bh * dd + e] : 0.f;
@@ -623,26 +822,36 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
 #pragma unroll
   for (int s = 1; s < kMaxSeg; ++s) {
     if (s < p.nseg) {
-      acc = fmaf(gL, acc, dS[s]);
+      float g = gL;
+      if constexpr (CH) g = __expf(lgd[s]);
+      acc = fmaf(g, acc, dS[s]);
       base[s * stride] = acc;
     }
   }
 }
 
-template <class CF, bool VK>
-hipError_t run_vk(const PrefillParams &p, hipStream_t s) {
-  static_assert(sizeof(SmemChunk<CF>) <= kLdsBytes, "LDS budget");
+template <class CF, bool VK, bool CH>
+hipError_t run_vkc(const PrefillParams &p, hipStream_t s) {
+  static_assert(sizeof(SmemChunk<CF>) + (CH ? sizeof(SmemChan<CF>) : 0) <= kLdsBytes,
+                "LDS budget");
   if (p.nseg > 1) {
-    hipError_t e = launch_kernel("linear_summary", summary_kernel<CF, VK>,
+    hipError_t e = launch_kernel("linear_summary", summary_kernel<CF, VK, CH>,
                                  dim3(p.nseg - 1, p.BH), dim3(CF::NT), s, p);
     if (e != hipSuccess) return e;
     const size_t rec = (size_t)p.d * p.dv + p.d;
-    e = launch_kernel("linear_scan", scan_kernel, dim3((unsigned)((rec + 255) / 256), p.BH),
+    e = launch_kernel("linear_scan", scan_kernel<CH>, dim3((unsigned)((rec + 255) / 256), p.BH),
                       dim3(256), s, p);
     if (e != hipSuccess) return e;
   }
-  return launch_kernel("linear_chunk", chunk_kernel<CF, VK>, dim3(p.nseg, p.BH), dim3(CF::NT),
-                       s, p);
+  return launch_kernel("linear_chunk", chunk_kernel<CF, VK, CH>, dim3(p.nseg, p.BH),
+                       dim3(CF::NT), s, p);
+}
+
+// a per-key-channel decay gets its own instantiations (none of its work is
+// compiled into the others)
+template <class CF, bool VK>
+hipError_t run_vk(const PrefillParams &p, hipStream_t s) {
+  return p.alpha ? run_vkc<CF, VK, true>(p, s) : run_vkc<CF, VK, false>(p, s);
 }
 
 template <class CF>
@@ -657,7 +866,7 @@ int resident_per_cu() {
   int v = cached.load(std::memory_order_relaxed);
   if (v > 0) return v;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<CF, true>, CF::NT, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<CF, true, false>, CF::NT, 0) !=
           hipSuccess || n < 1) {
     (void)hipGetLastError();
     n = 1;
@@ -711,7 +920,7 @@ LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io) {
   nseg = chunks > 0 ? (chunks + cps - 1) / cps : 1;
   pl.nseg = (int)nseg;
   pl.seg_len = (int)(cps * pl.chunk);
-  pl.ws_bytes = nseg > 1 ? (size_t)nseg * BH * ((size_t)d * dv + d) * sizeof(float) : 0;
+  pl.ws_bytes = nseg > 1 ? (size_t)nseg * BH * ws_rec(d, dv) * sizeof(float) : 0;
   return pl;
 }
 

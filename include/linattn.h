@@ -68,6 +68,9 @@ typedef enum { LA_FMAP_IDENTITY = 0, LA_FMAP_ELU1 = 1 } la_fmap;
  *     S_t = gamma_h S_{t-1} + phi(k_t) v_t^T,  z_t = gamma_h z_{t-1} + phi(k_t)
  *     o_t = S_t^T phi(q_t) / (phi(q_t) . z_t + eps)
  *   The state is read after the token is written (the token sees itself).
+ *   Instead of gamma, a per-key-channel decay alpha_t (GLA, [EAV] section
+ *   7.2) scales each state row and z entry by its own factor:
+ *     S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T,  z_t = alpha_t . z_{t-1} + phi(k_t)
  * LA_RULE_DELTA ([WILA] sections 5.2 and 5.3):
  *     S_t = S_{t-1} + g_t k_t (v_t - S_{t-1}^T k_t)^T,   o_t = S_t^T q_t
  *   raw q and k (fmap must be IDENTITY), no normaliser, no z.  With the
@@ -93,11 +96,13 @@ typedef struct la_prefill_args {
                         stays far inside the fp32 range on that interval. */
   const float *g;    /* DELTA: [B,H,N] write gate per token (required).
                         LINEAR: must be NULL. */
-  const float *alpha;/* DELTA: [B,H,N] state decay per token, each in (0, 1],
-                        or NULL (= 1, no decay).  LINEAR: must be NULL.
+  const float *alpha;/* State decay per token, or NULL (= 1, no decay).
+                        DELTA: [B,H,N], each in (0, 1].
+                        LINEAR: [B,H,N,d], one factor per key channel, each
+                        in [0.1, 1]; not together with gamma.
                         Values are the caller's contract (not read on the
-                        host); a zero or negative value makes the chunk's
-                        decay products undefined. */
+                        host); values outside the range make the chunk's
+                        decay products inaccurate or undefined. */
   float eps;         /* LINEAR: added to the denominator, >= 0. DELTA: ignored */
   const float *S_in; /* [B,H,d,dv] initial state; NULL = zeros */
   const float *z_in; /* LINEAR: [B,H,d] initial normaliser; NULL = zeros.
@@ -134,8 +139,8 @@ typedef struct la_decode_args {
   const void *v;     /* [B,H,dv] */
   const float *gamma;/* LINEAR: [H] or NULL (=1).  DELTA: must be NULL. */
   const float *g;    /* DELTA: [B,H] write gate (required). LINEAR: NULL. */
-  const float *alpha;/* DELTA: [B,H] state decay, or NULL (= 1).
-                        LINEAR: must be NULL. */
+  const float *alpha;/* State decay, or NULL (= 1).  DELTA: [B,H].
+                        LINEAR: [B,H,d] per key channel (not with gamma). */
   float eps;         /* LINEAR: >= 0 */
   float *S;          /* [B,H,d,dv] fp32, read and overwritten in place */
   float *z;          /* LINEAR: [B,H,d] fp32 in place (required).

@@ -94,7 +94,7 @@ def _args(**kw):
          g=ctypes.c_void_p(0x2000), z_out=ctypes.c_void_p(0x3000)),
     dict(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY,
          g=ctypes.c_void_p(0x2000), gamma=ctypes.c_void_p(0x3000)),
-    dict(alpha=ctypes.c_void_p(0x2000)),                   # decay on LINEAR
+    dict(alpha=ctypes.c_void_p(0x2000), gamma=ctypes.c_void_p(0x3000)),  # both decays
 ])
 def test_prefill_rejects_invalid_arguments(lib, bad):
     a = _args(**bad)
@@ -122,7 +122,7 @@ def test_empty_inputs_are_noops(lib):
     dict(eps=-0.5), dict(S=None), dict(z=None),
     dict(rule=_lib.LA_RULE_DELTA),                          # elu1 + delta
     dict(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY),  # z given, no g
-    dict(alpha=ctypes.c_void_p(0x2000)),                   # decay on LINEAR
+    dict(alpha=ctypes.c_void_p(0x2000), gamma=ctypes.c_void_p(0x3000)),  # both decays
 ])
 def test_decode_rejects_invalid_arguments(lib, bad):
     a = _lib.DecodeArgs()

@@ -199,3 +199,117 @@ def test_state_init_zeroes():
     la.state_init(S, z)
     torch.cuda.synchronize()
     assert not S.any() and not z.any()
+
+
+# --- per-key-channel decay (GLA) --------------------------------------------
+
+def _alpha(shape, seed, lo):
+    """Decay per key channel in (lo, 1): lo + (1 - lo) sigmoid(N(0,1))."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return (lo + (1.0 - lo) * torch.sigmoid(torch.randn(shape, generator=g))).to(DEV)
+
+
+def _oracle_gla(q, k, v, al, eps=1e-6, fmap="elu1", S0=None, z0=None):
+    return oracle.linear_prefill(cpu(q), cpu(k), cpu(v), eps=eps, fmap=fmap,
+                                 S0=cpu(S0), z0=cpu(z0), alpha=cpu(al))
+
+
+GLA_SHAPES = [  # (B, H, N, d, dv)
+    (1, 1, 1, 64, 64), (1, 2, 3, 16, 16), (2, 1, 63, 64, 64), (1, 2, 65, 64, 64),
+    (2, 2, 200, 128, 128), (1, 3, 130, 64, 128), (1, 2, 97, 128, 64), (1, 1, 17, 4, 3),
+    (2, 1, 50, 100, 72), (1, 1, 333, 64, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("shape", GLA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gla_prefill_small(shape, dtype):
+    B, H, N, d, dv = shape
+    seed = 900 + B * 7 + H * 11 + N * 13 + d * 17 + dv * 19 + 3 * (dtype == torch.bfloat16)
+    sc = 1 / np.sqrt(d)
+    q = _rand((B, H, N, d), dtype, seed, sc)
+    k = _rand((B, H, N, d), dtype, seed + 1, sc)
+    v = _rand((B, H, N, dv), dtype, seed + 2)
+    al = _alpha((B, H, N, d), seed + 3, 0.9)
+    o, S, z = la.prefill(q, k, v, alpha=al, eps=1e-6)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_gla(q, k, v, al)
+    assert_close(o, ro, TOL[dtype], "o")
+    assert_close(S, rS, TOL[dtype], "S", axes=(-2, -1))
+    assert_close(z, rz, TOL[dtype], "z")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("lo", [0.9, 0.3], ids=["mild", "strong"])
+def test_gla_prefill_segments_and_initial_state(dtype, lo):
+    """Long enough for several segments (summary + scan + chunk kernels), an
+    initial state updated in place, decays down to 0.3."""
+    B, H, N, d, dv = 1, 4, 4099, 64, 64
+    seed = 950 + int(lo * 10) + (dtype == torch.bfloat16)
+    q = _rand((B, H, N, d), dtype, seed, 0.125)
+    k = _rand((B, H, N, d), dtype, seed + 1, 0.125)
+    v = _rand((B, H, N, dv), dtype, seed + 2)
+    al = _alpha((B, H, N, d), seed + 3, lo)
+    S = _rand((B, H, d, dv), torch.float32, seed + 4, 0.3)
+    z = _rand((B, H, d), torch.float32, seed + 5, 0.3).abs() + 1.0
+    S0, z0 = S.clone(), z.clone()
+    o, _, _ = la.prefill(q, k, v, alpha=al, eps=1e-6, S_in=S, z_in=z, S_out=S, z_out=z)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_gla(q, k, v, al, S0=S0, z0=z0)
+    assert_close(o, ro, TOL[dtype], "o")
+    assert_close(S, rS, TOL[dtype], "S", axes=(-2, -1))
+    assert_close(z, rz, TOL[dtype], "z")
+
+
+def test_gla_uniform_alpha_matches_gamma():
+    """alpha = gamma_h on every channel and token reproduces the per-head decay
+    path (to bf16 resolution: different kernel instantiations)."""
+    B, H, N, d, dv = 1, 4, 700, 128, 128
+    q = _rand((B, H, N, d), torch.bfloat16, 960, d ** -0.5)
+    k = _rand((B, H, N, d), torch.bfloat16, 961, d ** -0.5)
+    v = _rand((B, H, N, dv), torch.bfloat16, 962)
+    gamma = torch.tensor([0.9, 0.97, 0.99, 1.0], device=DEV)
+    al = gamma[None, :, None, None].expand(B, H, N, d).contiguous()
+    o1, S1, z1 = la.prefill(q, k, v, gamma=gamma, eps=1e-6)
+    o2, S2, z2 = la.prefill(q, k, v, alpha=al, eps=1e-6)
+    torch.cuda.synchronize()
+    assert_close(o2, cpu(o1).double().numpy(), 1e-2, "o vs gamma path")
+    assert_close(S2, cpu(S1).double().numpy(), 1e-2, "S vs gamma path", axes=(-2, -1))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("dims", [(128, 128), (4, 3), (100, 72)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gla_decode_steps(dims, dtype):
+    d, dv = dims
+    B, H, steps = 3, 5, 6
+    S = _rand((B, H, d, dv), torch.float32, 970, 0.3)
+    z = _rand((B, H, d), torch.float32, 971, 0.3).abs() + 1.0
+    rS, rz = cpu(S).double().numpy(), cpu(z).double().numpy()
+    for t in range(steps):
+        q = _rand((B, H, d), dtype, 972 + 5 * t, d ** -0.5)
+        k = _rand((B, H, d), dtype, 973 + 5 * t, d ** -0.5)
+        v = _rand((B, H, dv), dtype, 974 + 5 * t)
+        al = _alpha((B, H, d), 975 + 5 * t, 0.5)
+        o = la.decode_step(q, k, v, S, z, alpha=al, eps=1e-6)
+        torch.cuda.synchronize()
+        ro, rS, rz = oracle.linear_decode_step(cpu(q), cpu(k), cpu(v), rS, rz, eps=1e-6,
+                                               alpha=cpu(al))
+        assert_close(o, ro, TOL[dtype], f"o step {t}")
+    assert_close(S, rS, 1e-5, "S", axes=(-2, -1))
+    assert_close(z, rz, 1e-5, "z")
+
+
+def test_gla_prefill_then_decode_handoff():
+    B, H, N, d, dv = 2, 2, 257, 64, 64
+    q = _rand((B, H, N + 1, d), torch.bfloat16, 980, 0.125)
+    k = _rand((B, H, N + 1, d), torch.bfloat16, 981, 0.125)
+    v = _rand((B, H, N + 1, dv), torch.bfloat16, 982)
+    al = _alpha((B, H, N + 1, d), 983, 0.8)
+    sl = lambda x: x[:, :, :N].contiguous()  # noqa: E731
+    at = lambda x: x[:, :, N].contiguous()  # noqa: E731
+    _, S, z = la.prefill(sl(q), sl(k), sl(v), alpha=sl(al), eps=1e-6)
+    o = la.decode_step(at(q), at(k), at(v), S, z, alpha=at(al), eps=1e-6)
+    torch.cuda.synchronize()
+    ro, _, _ = _oracle_gla(q, k, v, al)
+    assert_close(o, ro[:, :, N], TOL[torch.bfloat16], "o")
