@@ -23,8 +23,9 @@ per step.  Alongside:
                 1024-token prefill, then 1024 single-token steps with fresh
                 q, k, v): steps/s and state GB/s against HBM peak;
   workloads     the long-context decay prefill (B=1 H=32 N=131072 d=128), the
-                gated delta-rule prefill (B=2 H=16 N=8192 d=128) and the same
-                with a per-token state decay alpha in (0.9, 1), each with its
+                gated delta-rule prefill (B=2 H=16 N=8192 d=128), the same
+                with a per-token state decay alpha in (0.9, 1), and the main
+                workload with a per-key-channel decay (GLA), each with its
                 kernels' times and HBM fraction;
   cpu_baseline  the fp64 oracle on the host (one thread) over the same
                 inputs of the main workload (a reported baseline, not a
@@ -55,7 +56,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6],
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7],
                     help="3 runs the decode-step loop alone")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -309,6 +310,8 @@ def bytes_per_head_token(w):
     b = (2 * w.d + w.dv) * e + w.dv * e
     if w.rule == "delta":
         b += 4 + (4 if w.decay == "alpha" else 0)
+    elif w.decay == "channel":
+        b += 4 * w.d  # fp32 decay per key channel
     return b
 
 
@@ -340,11 +343,12 @@ def make_step(la, torch, w, x):
             la.prefill(q, k, v, rule="delta", g=g, alpha=al, o=o, S_out=S, workspace=ws)
     else:
         z = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+        al = x.get("alpha")
         ws_bytes = la.workspace_size(q, k, v, gamma=gamma, eps=w.eps)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
         def step():
-            la.prefill(q, k, v, gamma=gamma, eps=w.eps, o=o, S_out=S, z_out=z,
+            la.prefill(q, k, v, gamma=gamma, alpha=al, eps=w.eps, o=o, S_out=S, z_out=z,
                        workspace=ws)
     return step, o, ws_bytes
 
@@ -491,7 +495,9 @@ def cpu_baseline(w, x, o_gpu):
             ro, _ = oracle.delta_prefill(q, k, v, x["g"].cpu(),
                                          alpha=None if al is None else al.cpu())
         else:
-            ro, _, _ = oracle.linear_prefill(q, k, v, eps=w.eps, gamma=gamma)
+            al = x.get("alpha")
+            ro, _, _ = oracle.linear_prefill(q, k, v, eps=w.eps, gamma=gamma,
+                                             alpha=None if al is None else al.cpu())
         el = time.perf_counter() - t0
     got = o_gpu.detach().cpu().double().numpy()
     diff = np.abs(got - ro).max(axis=-1)
@@ -564,7 +570,7 @@ def main():
         line["decode"] = bench_decode(la, lib, torch, args.decode_steps)
     if not args.no_extra:
         extra = {}
-        for wid in (4, 5, 6):
+        for wid in (4, 5, 6, 7):
             if wid == args.workload:
                 continue
             r, xx, oo = bench_workload(la, lib, torch, inputs.WORKLOADS[wid],

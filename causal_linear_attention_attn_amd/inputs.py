@@ -37,8 +37,9 @@ class Workload:
     fmap: str              # "elu1" or "identity"
     scale: float           # std of the q, k, v draws
     eps: float = 1e-6
-    decay: str = "none"    # "none", "per_head" (gamma_h = 1 - 2^(-5 - h/4)) or
+    decay: str = "none"    # "none", "per_head" (gamma_h = 1 - 2^(-5 - h/4)),
                            # "alpha" (delta rule: per-token state decay in (0.9, 1))
+                           # or "channel" (linear rule: per-key-channel decay in (0.9, 1))
     decode_steps: int = 0  # > 0: a decode loop follows the prefill
     extra: dict = field(default_factory=dict)
 
@@ -59,6 +60,9 @@ WORKLOADS = {
     # the gated delta workload with Gated DeltaNet's scalar decay added
     6: Workload(6, "delta_decay_bf16_prefill_B2H16N8192d128", 2, 16, 8192, 128, 128,
                 torch.bfloat16, "delta", "identity", 1.0, decay="alpha"),
+    # the B4 H16 N4096 d64 prefill with GLA's per-key-channel decay
+    7: Workload(7, "linear_gla_bf16_prefill_B4H16N4096d64", 4, 16, 4096, 64, 64,
+                torch.bfloat16, "linear", "elu1", 1.0 / math.sqrt(64), decay="channel"),
 }
 
 
@@ -126,6 +130,8 @@ def make_prefill(w: Workload, device, *, B=None, H=None, N=None):
         out["q"] = normal((B, H, N, w.d), w.wid, _Q, device, w.scale, w.dtype)
         out["k"] = normal((B, H, N, w.d), w.wid, _K, device, w.scale, w.dtype)
         out["v"] = normal((B, H, N, w.dv), w.wid, _V, device, w.scale, w.dtype)
+        if w.decay == "channel":
+            out["alpha"] = decay_gate((B, H, N, w.d), w.wid, _A, device, 0.9)
     out["gamma"] = per_head_gamma(H, device) if w.decay == "per_head" else None
     return out
 
