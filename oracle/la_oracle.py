@@ -13,7 +13,8 @@ so the oracle evaluates the method on the very values the GPU consumes.
 Sources (cited by page title and section):
   [WILA]  "What Is Linear Attention?" (xutianle.me): section 2 (kernel trick,
           S and z), section 4 (causal recurrence), 5.1 (gamma decay),
-          5.2 (delta rule), 5.3 (gate).
+          5.2 (delta rule), 5.3 (gate), 5.4 (short convolution, conv
+          cache).
   [EAV]   "Efficient attention variants" (bailixisu.com): section 4 (kernel
           form, elu+1), section 5 (causal prefix form, write-then-read),
           5.1 (hand-worked example), 7.1 (RetNet decay), 7.3 (DeltaNet),
@@ -36,6 +37,11 @@ Readings where the pages disagree:
   * The optional decay alpha_t of the delta rule is a scalar per token and
     head, applied to the old state before the prediction ([EAV] 7.4 warns
     that the error must be taken on the decayed state).
+  * The short convolution of [WILA] 5.4 is depthwise (one filter per head
+    and channel), causal, over the w most recent tokens including the
+    current one, with no bias and no activation; it is applied to the raw
+    q, k and v before the feature map, and its cache holds the last w-1
+    raw tokens.
 
 Parity pins live in tests/test_oracle.py; every function below is pinned
 there against printed values, closed forms or brute force.
@@ -190,6 +196,80 @@ def linear_quadratic(q, k, v, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1):
     D = np.where(i >= j, gam[:, None, None] ** lag[None], 0.0)  # [H, N, N]
     A = np.matmul(fq, np.swapaxes(fk, -1, -2)) * D[None]
     return np.matmul(A, v) / (A.sum(axis=-1, keepdims=True) + eps)
+
+
+# ---------------------------------------------------------------------------
+# Short causal convolution before the attention ([WILA] 5.4)
+# ---------------------------------------------------------------------------
+
+def short_conv(x, weight, cache=None):
+    """Depthwise causal convolution along the token axis.
+
+    [WILA] 5.4 adds a short convolution over a window of the last w tokens in
+    front of the linear state, and splits the inference cache into the
+    recurrent state and a conv cache of the most recent tokens.  Read here as
+    one length-w filter per head and channel, tap w-1 on the current token
+    and tap j on the token w-1-j places back:
+        y_t[c] = sum_{j=0..w-1} weight[h, j, c] * x_{t-(w-1)+j}[c]
+    Tokens before the sequence come from the cache (oldest first), or are
+    zero without one.
+
+    x: [B, H, N, c]; weight: [H, w, c]; cache: [B, H, w-1, c] or None.
+    Returns (y [B, H, N, c], cache after the last token [B, H, w-1, c]: the
+    last w-1 raw tokens of cache followed by x), in float64.
+    """
+    x, W = _f64(x), _f64(weight)
+    B, H, N, c = x.shape
+    w = W.shape[1]
+    hist = np.zeros((B, H, w - 1, c)) if cache is None else _f64(cache).copy()
+    y = np.empty((B, H, N, c))
+    for t in range(N):
+        window = np.concatenate([hist, x[:, :, t:t + 1]], axis=2)  # oldest first
+        y[:, :, t] = np.sum(window * W[None], axis=2)
+        hist = window[:, :, 1:]
+    return y, hist
+
+
+def _conv_split(a, d):
+    """Channels [q | k | v] of a conv weight or cache: d, d and the rest."""
+    a = _f64(a)
+    return a[..., :d], a[..., d:2 * d], a[..., 2 * d:]
+
+
+def linear_prefill_conv(q, k, v, conv_weight, *, conv_cache=None, **kw):
+    """Short convolution of q, k and v ([WILA] 5.4), then linear_prefill.
+
+    conv_weight: [H, w, 2d + dv], channels [q | k | v]; conv_cache:
+    [B, H, w-1, 2d + dv] raw tokens before the sequence, or None (zeros).
+    Other keywords as linear_prefill.  Returns (o, S_N, z_N, conv cache
+    after the last token [B, H, w-1, 2d + dv]).
+    """
+    d = q.shape[-1]
+    wq, wk, wv = _conv_split(conv_weight, d)
+    cq = ck = cv = None
+    if conv_cache is not None:
+        cq, ck, cv = _conv_split(conv_cache, d)
+    yq, hq = short_conv(q, wq, cq)
+    yk, hk = short_conv(k, wk, ck)
+    yv, hv = short_conv(v, wv, cv)
+    o, S, z = linear_prefill(yq, yk, yv, **kw)
+    return o, S, z, np.concatenate([hq, hk, hv], axis=-1)
+
+
+def linear_decode_step_conv(q, k, v, S, z, conv_weight, conv_cache, **kw):
+    """One decode step with the short convolution: the new token joins the
+    conv cache's window, the convolved q, k, v go through
+    linear_decode_step.  q, k: [B, H, d]; v: [B, H, dv]; conv_cache:
+    [B, H, w-1, 2d + dv].  Returns (o, S_new, z_new, conv cache after the
+    token); the inputs are not modified."""
+    d = q.shape[-1]
+    wq, wk, wv = _conv_split(conv_weight, d)
+    cq, ck, cv = _conv_split(conv_cache, d)
+    yq, hq = short_conv(_f64(q)[:, :, None], wq, cq)
+    yk, hk = short_conv(_f64(k)[:, :, None], wk, ck)
+    yv, hv = short_conv(_f64(v)[:, :, None], wv, cv)
+    o, S_new, z_new = linear_decode_step(yq[:, :, 0], yk[:, :, 0], yv[:, :, 0], S, z, **kw)
+    return o, S_new, z_new, np.concatenate([hq, hk, hv], axis=-1)
 
 
 # ---------------------------------------------------------------------------

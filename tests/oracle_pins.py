@@ -540,4 +540,117 @@ def pin_gla_uniform_is_gamma_and_split(orc):
     np.testing.assert_allclose(zd, z, rtol=1e-12)
 
 
+# --- short causal convolution (What Is Linear Attention? 5.4) ---------------
+
+def _correlate_conv(x, W, cache):
+    """Per head and channel: numpy's 'valid' correlation of the cache
+    followed by the sequence with the filter (tap w-1 on the current token).
+    x: [H, N, c], W: [H, w, c], cache: [H, w-1, c]."""
+    H, N, c = x.shape
+    full = np.concatenate([cache, x], axis=1)
+    y = np.empty((H, N, c))
+    for h in range(H):
+        for ch in range(c):
+            y[h, :, ch] = np.correlate(full[h, :, ch], W[h, :, ch], mode="valid")
+    return y, full[:, full.shape[1] - (W.shape[1] - 1):]
+
+
+def pin_conv_matches_numpy_correlate(orc):
+    """The depthwise causal convolution equals numpy's correlation of the
+    cached tokens followed by the sequence, per channel; the new cache is
+    the last w-1 raw tokens; widths 1..4, sequences shorter than the cache."""
+    rng = np.random.default_rng(41)
+    for w in (1, 2, 3, 4):
+        for N in (1, 2, 7):
+            H, c = 2, 3
+            x = rng.normal(size=(1, H, N, c))
+            W = rng.normal(size=(H, w, c))
+            cache = rng.normal(size=(1, H, w - 1, c))
+            y, hist = orc.short_conv(x, W, cache)
+            ry, rh = _correlate_conv(x[0], W, cache[0])
+            np.testing.assert_allclose(y[0], ry, rtol=1e-13, atol=1e-14)
+            np.testing.assert_array_equal(hist[0], rh)
+            y0, _ = orc.short_conv(x, W)  # no cache: zeros before the sequence
+            ry0, _ = _correlate_conv(x[0], W, np.zeros_like(cache[0]))
+            np.testing.assert_allclose(y0[0], ry0, rtol=1e-13, atol=1e-14)
+
+
+def pin_conv_then_attention_brute_force(orc):
+    """linear_prefill_conv on channels [q | k | v] (distinct filters, d != dv)
+    equals the O(N^2) masked form on inputs convolved by numpy's correlation,
+    and returns the raw last tokens as the cache."""
+    rng = np.random.default_rng(42)
+    H, N, d, dv, w, eps = 2, 9, 3, 4, 4, 1e-3
+    q = rng.normal(size=(1, H, N, d))
+    k = rng.normal(size=(1, H, N, d))
+    v = rng.normal(size=(1, H, N, dv))
+    W = rng.normal(size=(H, w, 2 * d + dv))
+    cache = rng.normal(size=(1, H, w - 1, 2 * d + dv))
+    o, _, _, hist = orc.linear_prefill_conv(q, k, v, W, conv_cache=cache, eps=eps)
+    cq, _ = _correlate_conv(q[0], W[..., :d], cache[0][..., :d])
+    ck, _ = _correlate_conv(k[0], W[..., d:2 * d], cache[0][..., d:2 * d])
+    cv, _ = _correlate_conv(v[0], W[..., 2 * d:], cache[0][..., 2 * d:])
+    fq, fk = orc.phi_elu1(cq), orc.phi_elu1(ck)
+    ref = np.empty((H, N, dv))
+    for h in range(H):
+        for t in range(N):
+            a = np.array([fq[h, t] @ fk[h, i] for i in range(t + 1)])
+            ref[h, t] = (a @ cv[h, :t + 1]) / (a.sum() + eps)
+    np.testing.assert_allclose(o[0], ref, rtol=1e-11, atol=1e-13)
+    raw = np.concatenate([q, k, v], axis=-1)[0]
+    np.testing.assert_array_equal(hist[0], raw[:, N - (w - 1):])
+
+
+def pin_conv_identity_and_shift_filters(orc):
+    """The unit filter on the current token leaves q, k, v unchanged; the
+    unit filter on the oldest tap delays the sequence by w-1 tokens, the
+    cache supplying the first ones."""
+    rng = np.random.default_rng(43)
+    B, H, N, d, dv, w = 1, 2, 6, 3, 2, 3
+    q = rng.normal(size=(B, H, N, d))
+    k = rng.normal(size=(B, H, N, d))
+    v = rng.normal(size=(B, H, N, dv))
+    cache = rng.normal(size=(B, H, w - 1, 2 * d + dv))
+    ident = np.zeros((H, w, 2 * d + dv))
+    ident[:, w - 1] = 1.0
+    o, S, z, _ = orc.linear_prefill_conv(q, k, v, ident, conv_cache=cache, gamma=[0.9, 0.8])
+    o0, S0, z0 = orc.linear_prefill(q, k, v, gamma=[0.9, 0.8])
+    np.testing.assert_allclose(o, o0, rtol=1e-14)
+    np.testing.assert_allclose(S, S0, rtol=1e-14)
+    shift = np.zeros((H, w, 2 * d + dv))
+    shift[:, 0] = 1.0
+    o, _, _, _ = orc.linear_prefill_conv(q, k, v, shift, conv_cache=cache)
+    full = np.concatenate([cache, np.concatenate([q, k, v], axis=-1)], axis=2)[:, :, :N]
+    o1, _, _ = orc.linear_prefill(full[..., :d], full[..., d:2 * d], full[..., 2 * d:])
+    np.testing.assert_allclose(o, o1, rtol=1e-14)
+
+
+def pin_conv_split_and_decode(orc):
+    """Prefill in pieces (one shorter than the conv window) carrying S, z and
+    the conv cache, then decode steps, equals one prefill of the whole
+    sequence."""
+    rng = np.random.default_rng(44)
+    B, H, N, d, dv, w = 2, 1, 12, 3, 2, 4
+    q = rng.normal(size=(B, H, N, d))
+    k = rng.normal(size=(B, H, N, d))
+    v = rng.normal(size=(B, H, N, dv))
+    W = rng.normal(size=(H, w, 2 * d + dv))
+    al = rng.uniform(0.5, 1.0, size=(B, H, N, d))
+    o, S, z, C = orc.linear_prefill_conv(q, k, v, W, alpha=al)
+    parts, S1, z1, C1 = [], None, None, None
+    for a, b in ((0, 5), (5, 7), (7, 10)):
+        oi, S1, z1, C1 = orc.linear_prefill_conv(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], W,
+                                                 conv_cache=C1, S0=S1, z0=z1,
+                                                 alpha=al[:, :, a:b])
+        parts.append(oi)
+    np.testing.assert_allclose(np.concatenate(parts, axis=2), o[:, :, :10], rtol=1e-12)
+    for t in (10, 11):
+        od, S1, z1, C1 = orc.linear_decode_step_conv(q[:, :, t], k[:, :, t], v[:, :, t], S1,
+                                                     z1, W, C1, alpha=al[:, :, t])
+        np.testing.assert_allclose(od, o[:, :, t], rtol=1e-12)
+    np.testing.assert_allclose(S1, S, rtol=1e-12)
+    np.testing.assert_allclose(z1, z, rtol=1e-12)
+    np.testing.assert_array_equal(C1, C)
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

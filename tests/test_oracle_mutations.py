@@ -193,13 +193,59 @@ def _gla_decay_after_write(m):
     m.linear_step = step
 
 
+def _conv_taps_reversed(m):
+    orig = m.short_conv
+    m.short_conv = lambda x, W, cache=None: orig(x, m._f64(W)[:, ::-1], cache)
+
+
+def _conv_cache_newest_first(m):
+    orig = m.short_conv
+    def conv(x, W, cache=None):
+        return orig(x, W, None if cache is None else m._f64(cache)[:, :, ::-1])
+    m.short_conv = conv
+
+
+def _conv_cache_ignored(m):
+    orig = m.short_conv
+    def conv(x, W, cache=None):
+        y, _ = orig(x, W, None)
+        _, hist = orig(x, W, cache)
+        return y, hist
+    m.short_conv = conv
+
+
+def _conv_excludes_current_token(m):
+    def conv(x, W, cache=None):
+        x, W = m._f64(x), m._f64(W)
+        B, H, N, c = x.shape
+        w = W.shape[1]
+        hist = np.zeros((B, H, w, c))
+        if cache is not None:
+            hist[:, :, 1:] = m._f64(cache)
+        y = np.empty((B, H, N, c))
+        for t in range(N):
+            y[:, :, t] = np.sum(hist * W[None], axis=2)
+            hist = np.concatenate([hist[:, :, 1:], x[:, :, t:t + 1]], axis=2)
+        return y, hist[:, :, 1:]
+    m.short_conv = conv
+
+
+def _conv_qk_filters_swapped(m):
+    orig = m._conv_split
+    def split(a, d):
+        a0, a1, a2 = orig(a, d)
+        return a1, a0, a2
+    m._conv_split = split
+
+
 MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _exp_everywhere, _decay_off_by_one, _outer_transposed,
            _quadratic_strict_mask, _delta_not_transposed, _delta_wrong_sign,
            _delta_output_before_update, _delta_gate_on_value_only,
            _delta_dropped_correction, _gdn_error_on_undecayed_state,
            _gdn_decay_after_write, _gdn_decay_on_write_too, _gla_decay_on_value_axis,
-           _gla_decay_after_write]
+           _gla_decay_after_write, _conv_taps_reversed, _conv_cache_newest_first,
+           _conv_cache_ignored, _conv_excludes_current_token, _conv_qk_filters_swapped]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
