@@ -10,6 +10,8 @@ a tensor is not on a GPU, the call raises.
     o, S, _ = prefill(q, k, v, rule="delta", g=g)             # gated delta
     o, S, _ = prefill(q, k, v, rule="delta", g=g, alpha=a)    # with decay
     o = decode_step(q1, k1, v1, S, z)                         # in place on S, z
+    o, S, z = prefill(q, k, v, conv_weight=W, conv_cache=C)   # short conv; C in place
+    o = decode_step(q1, k1, v1, S, z, conv_weight=W, conv_cache=C)
 """
 from __future__ import annotations
 
@@ -52,6 +54,23 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _conv_check(conv_weight, conv_cache, q, H, d, dv, cache_lead):
+    """Shapes of the short-convolution filters [H, w, 2d+dv] and the conv
+    cache [*cache_lead, w-1, 2d+dv]; returns w (0 without filters)."""
+    if conv_weight is None:
+        if conv_cache is not None:
+            raise ValueError("conv_cache needs conv_weight")
+        return 0
+    if conv_weight.dim() != 3 or tuple(conv_weight.shape[::2]) != (H, 2 * d + dv):
+        raise ValueError(f"conv_weight must be [H, w, 2d+dv] = [{H}, w, {2 * d + dv}]")
+    w = conv_weight.shape[1]
+    if conv_cache is not None:
+        want = (*cache_lead, w - 1, 2 * d + dv)
+        if tuple(conv_cache.shape) != want or conv_cache.dtype != q.dtype:
+            raise ValueError(f"conv_cache must be {list(want)} of dtype {q.dtype}")
+    return w
+
+
 def _prefill_args(q, k, v, rule, fmap, gamma, g, eps, alpha=None):
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,H,N,d] and v [B,H,N,dv]")
@@ -71,11 +90,13 @@ def _prefill_args(q, k, v, rule, fmap, gamma, g, eps, alpha=None):
 
 
 def workspace_size(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None,
-                   eps=1e-6):
+                   eps=1e-6, alpha=None, conv_weight=None):
     """Workspace bytes la_prefill needs for these tensors (current device)."""
     if fmap is None:
         fmap = "elu1" if rule == "linear" else "identity"
-    a = _prefill_args(q, k, v, rule, fmap, gamma, g, eps)
+    a = _prefill_args(q, k, v, rule, fmap, gamma, g, eps, alpha)
+    if conv_weight is not None:
+        a.conv_weight, a.conv_width = _ptr(conv_weight), conv_weight.shape[1]
     n = _lib.load().la_prefill_workspace_size(ctypes.byref(a))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes")
@@ -84,12 +105,16 @@ def workspace_size(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None,
 
 def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
             S_in=None, z_in=None, S_out=None, z_out=None, return_state=True,
-            o=None, workspace=None, alpha=None):
+            o=None, workspace=None, alpha=None, conv_weight=None, conv_cache=None):
     """Chunked prefill over [B,H,N,*] sequences (see la_prefill).
 
     rule "linear": fmap defaults to "elu1"; gamma [H] fp32 or None; eps >= 0;
                    or, instead of gamma, alpha [B,H,N,d] fp32: a decay per key
-                   channel and token in [0.1, 1].
+                   channel and token in [0.1, 1].  Optionally a short causal
+                   convolution of q, k, v: conv_weight [H, w, 2d+dv] fp32
+                   (w <= 4) and conv_cache [B,H,w-1,2d+dv] (dtype of q), read
+                   as the tokens before the sequence and overwritten in place
+                   with the last w-1 tokens (None: zeros before, not kept).
     rule "delta":  fmap "identity"; g [B,H,N] fp32 required; alpha [B,H,N]
                    fp32 state decay in (0, 1] or None.
     Returns (o, S_out, z_out); the states are None unless requested
@@ -97,8 +122,9 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
     """
     if fmap is None:
         fmap = "elu1" if rule == "linear" else "identity"
-    _need_gpu(q, k, v, gamma, g, alpha, S_in, z_in, S_out, z_out, o, workspace)
-    _need_f32(gamma, g, alpha, S_in, z_in, S_out, z_out)
+    _need_gpu(q, k, v, gamma, g, alpha, S_in, z_in, S_out, z_out, o, workspace,
+              conv_weight, conv_cache)
+    _need_f32(gamma, g, alpha, S_in, z_in, S_out, z_out, conv_weight)
     if alpha is not None:
         want = q.shape if rule == "linear" else q.shape[:3]
         if tuple(alpha.shape) != tuple(want):
@@ -106,6 +132,10 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
     a = _prefill_args(q, k, v, rule, fmap, gamma, g, eps, alpha)
     B, H, N, d = q.shape
     dv = v.shape[3]
+    w = _conv_check(conv_weight, conv_cache, q, H, d, dv, (B, H))
+    if w:
+        a.conv_weight, a.conv_width = _ptr(conv_weight), w
+        a.conv_in = a.conv_out = _ptr(conv_cache)
     if o is None:
         o = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
     if return_state and S_out is None:
@@ -129,15 +159,17 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
 
 
 def decode_step(q, k, v, S, z=None, *, rule="linear", fmap=None, gamma=None,
-                g=None, eps=1e-6, o=None, alpha=None):
+                g=None, eps=1e-6, o=None, alpha=None, conv_weight=None, conv_cache=None):
     """One token per sequence: q, k [B,H,d], v [B,H,dv]; S [B,H,d,dv] (and z
     [B,H,d] for "linear") are updated in place; "delta" takes g [B,H] and
     an optional decay alpha [B,H]; "linear" an optional per-channel decay
-    alpha [B,H,d] instead of gamma.  Returns o [B,H,dv]."""
+    alpha [B,H,d] instead of gamma, and an optional short convolution
+    (conv_weight [H, w, 2d+dv], conv_cache [B,H,w-1,2d+dv] shifted in
+    place).  Returns o [B,H,dv]."""
     if fmap is None:
         fmap = "elu1" if rule == "linear" else "identity"
-    _need_gpu(q, k, v, S, z, gamma, g, alpha, o)
-    _need_f32(S, z, gamma, g, alpha)
+    _need_gpu(q, k, v, S, z, gamma, g, alpha, o, conv_weight, conv_cache)
+    _need_f32(S, z, gamma, g, alpha, conv_weight)
     if q.dim() != 3 or k.shape != q.shape or v.shape[:2] != q.shape[:2]:
         raise ValueError("q, k must be [B,H,d] and v [B,H,dv]")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
@@ -161,6 +193,9 @@ def decode_step(q, k, v, S, z=None, *, rule="linear", fmap=None, gamma=None,
     a.gamma, a.g, a.alpha = _ptr(gamma), _ptr(g), _ptr(alpha)
     a.eps = float(eps)
     a.S, a.z, a.o = _ptr(S), _ptr(z), _ptr(o)
+    w = _conv_check(conv_weight, conv_cache, q, H, d, dv, (B, H))
+    if w:
+        a.conv_weight, a.conv_width, a.conv_cache = _ptr(conv_weight), w, _ptr(conv_cache)
     _lib.check(_lib.load().la_decode_step(ctypes.byref(a), _stream()),
                "la_decode_step")
     return o

@@ -11,7 +11,7 @@ LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP, LA_EWORKSPACE = 0, 1, 2, 3, 4
 LA_F32, LA_BF16 = 0, 1
 LA_FMAP_IDENTITY, LA_FMAP_ELU1 = 0, 1
 LA_RULE_LINEAR, LA_RULE_DELTA = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # Every symbol include/linattn.h declares.
 EXPORTS = ("la_prefill_workspace_size", "la_prefill", "la_decode_step",
@@ -26,8 +26,9 @@ class PrefillArgs(ctypes.Structure):
         ("B", _i32), ("H", _i32), ("N", _i32), ("d", _i32), ("dv", _i32),
         ("dtype", _i32), ("rule", _i32), ("fmap", _i32),
         ("q", _ptr), ("k", _ptr), ("v", _ptr),
-        ("gamma", _ptr), ("g", _ptr), ("alpha", _ptr), ("eps", _f32),
-        ("S_in", _ptr), ("z_in", _ptr), ("S_out", _ptr), ("z_out", _ptr),
+        ("gamma", _ptr), ("g", _ptr), ("alpha", _ptr),
+        ("conv_weight", _ptr), ("conv_width", _i32), ("conv_in", _ptr), ("conv_out", _ptr),
+        ("eps", _f32), ("S_in", _ptr), ("z_in", _ptr), ("S_out", _ptr), ("z_out", _ptr),
         ("o", _ptr), ("workspace", _ptr), ("workspace_bytes", _size),
     ]
 
@@ -37,8 +38,9 @@ class DecodeArgs(ctypes.Structure):
         ("B", _i32), ("H", _i32), ("d", _i32), ("dv", _i32),
         ("dtype", _i32), ("rule", _i32), ("fmap", _i32),
         ("q", _ptr), ("k", _ptr), ("v", _ptr),
-        ("gamma", _ptr), ("g", _ptr), ("alpha", _ptr), ("eps", _f32),
-        ("S", _ptr), ("z", _ptr), ("o", _ptr),
+        ("gamma", _ptr), ("g", _ptr), ("alpha", _ptr),
+        ("conv_weight", _ptr), ("conv_width", _i32), ("conv_cache", _ptr),
+        ("eps", _f32), ("S", _ptr), ("z", _ptr), ("o", _ptr),
     ]
 
 

@@ -97,6 +97,7 @@ namespace {
 
 constexpr int kMaxGridY = 65535;
 constexpr size_t kMaxHeadBytes = 0x7fff0000u;
+constexpr int kMaxConvWidth = 4;
 
 bool dims_ok(int d, int dv) {
   return d >= 1 && d <= LA_MAX_DIM && dv >= 1 && dv <= LA_MAX_DIM;
@@ -119,14 +120,33 @@ int check_prefill_shape(const la_prefill_args *a) {
   const size_t esz = a->dtype == LA_BF16 ? 2 : 4;
   const size_t dmax = a->d > a->dv ? a->d : a->dv;
   if ((size_t)a->N * dmax * esz > kMaxHeadBytes) return LA_EUNSUPPORTED;
+  if (a->conv_weight) {
+    if (a->conv_width < 1 || a->conv_width > kMaxConvWidth) return LA_EINVAL;
+    if (a->rule != LA_RULE_LINEAR) return LA_EUNSUPPORTED;
+    if (!la::linear_combo_supported(a->d, a->dv, a->dtype == LA_BF16, a->alpha != nullptr,
+                                    true))
+      return LA_EUNSUPPORTED;
+  } else if (a->conv_width != 0 || a->conv_in || a->conv_out) {
+    return LA_EINVAL;
+  }
   return LA_OK;
+}
+
+// Bytes of one conv cache [B,H,w-1,2d+dv] (0 without a convolution).
+size_t conv_cache_bytes(size_t BH, int d, int dv, int width, bool bf16_io) {
+  return width > 1 ? BH * (size_t)(width - 1) * (2 * (size_t)d + dv) * (bf16_io ? 2 : 4) : 0;
+}
+
+bool overlap(const void *a, const void *b, size_t n) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return n > 0 && x < y + n && y < x + n;
 }
 
 }  // namespace
 
 extern "C" {
 
-int32_t la_abi_version(void) { return 2; }
+int32_t la_abi_version(void) { return 3; }
 
 const char *la_status_str(int s) {
   switch (s) {
@@ -144,7 +164,9 @@ size_t la_prefill_workspace_size(const la_prefill_args *a) {
   const int BH = a->B * a->H;
   if (BH == 0 || a->N == 0) return 0;
   if (a->rule == LA_RULE_LINEAR)
-    return la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16).ws_bytes;
+    return la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16,
+                           a->conv_weight ? a->conv_width : 0)
+        .ws_bytes;
   return la::delta_workspace_bytes(BH, a->N, a->d, a->dtype == LA_BF16);
 }
 
@@ -163,6 +185,12 @@ int la_prefill(const la_prefill_args *a, void *stream) {
     if (a->gamma || a->z_in || a->z_out) return LA_EINVAL;
   }
   if (BH > 0 && a->N > 0 && (!a->q || !a->k || !a->v || !a->o)) return LA_EINVAL;
+  const bool bf16_io = a->dtype == LA_BF16;
+  const int cw = a->conv_weight ? a->conv_width : 0;
+  const size_t ncache = conv_cache_bytes((size_t)BH, a->d, a->dv, cw, bf16_io);
+  if (a->conv_in && a->conv_out && a->conv_in != a->conv_out &&
+      overlap(a->conv_in, a->conv_out, ncache))
+    return LA_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (BH == 0) return LA_OK;
 
@@ -175,13 +203,15 @@ int la_prefill(const la_prefill_args *a, void *stream) {
     if (e == hipSuccess && a->z_out)
       e = a->z_in ? la::launch_copy(a->z_out, a->z_in, nz, s)
                   : la::launch_fill(a->z_out, nz, 0.f, s);
+    if (e == hipSuccess && a->conv_out)  // and so does the conv cache
+      e = a->conv_in ? la::launch_copy_bytes(a->conv_out, a->conv_in, ncache, s)
+                     : la::launch_zero_bytes(a->conv_out, ncache, s);
     return to_status(e);
   }
-  const bool bf16_io = a->dtype == LA_BF16;
   la::LinearPlan plan{};
   size_t ws_need;
   if (linear) {
-    plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io);
+    plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io, cw);
     ws_need = plan.ws_bytes;
   } else {
     ws_need = la::delta_workspace_bytes(BH, a->N, a->d, bf16_io);
@@ -217,6 +247,18 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   if (!linear) return to_status(la::launch_delta_prefill(p, bf16_io, s));
   p.nseg = plan.nseg;
   p.seg_len = plan.seg_len;
+  p.conv_w = a->conv_weight;
+  p.conv_width = cw;
+  if (cw > 1) {
+    p.conv_in = a->conv_in;
+    p.conv_out = a->conv_out;
+    // over several segments chunk_kernel reads the summary kernel's copy of
+    // the cache, so that conv_out may alias conv_in
+    const bool copy = plan.nseg > 1 && a->conv_in;
+    void *cp = copy ? static_cast<char *>(a->workspace) + plan.conv_off : nullptr;
+    p.conv_copy = cp;
+    p.conv_src = copy ? cp : a->conv_in;
+  }
   return to_status(la::launch_linear_prefill(p, plan, bf16_io, s));
 }
 
@@ -237,6 +279,13 @@ int la_decode_step(const la_decode_args *a, void *stream) {
       return LA_EINVAL;
     if (BH > 0 && !a->z) return LA_EINVAL;
   }
+  if (a->conv_weight) {
+    if (a->conv_width < 1 || a->conv_width > kMaxConvWidth) return LA_EINVAL;
+    if (delta) return LA_EUNSUPPORTED;
+    if (BH > 0 && a->conv_width > 1 && !a->conv_cache) return LA_EINVAL;
+  } else if (a->conv_width != 0 || a->conv_cache) {
+    return LA_EINVAL;
+  }
   if (BH == 0) return LA_OK;
   if (!a->q || !a->k || !a->v || !a->o || !a->S) return LA_EINVAL;
 
@@ -256,6 +305,9 @@ int la_decode_step(const la_decode_args *a, void *stream) {
   p.S = a->S;
   p.z = a->z;
   p.o = a->o;
+  p.conv_w = a->conv_weight;
+  p.conv_width = a->conv_weight ? a->conv_width : 0;
+  p.conv_cache = a->conv_cache;
   const int vec = (a->dv % 4 == 0 && aligned16(a->S)) ? 4 : 1;
   return to_status(la::launch_decode(p, a->dtype == LA_BF16, delta, vec,
                                      reinterpret_cast<hipStream_t>(stream)));

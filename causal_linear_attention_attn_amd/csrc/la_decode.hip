@@ -12,6 +12,12 @@
 //     b = S^T k,  u = v - alpha b,  S <- alpha S + g k u^T,
 //     o = S_new^T q = alpha S_old^T q + g (k . q) u
 //
+// With a short causal convolution ("What Is Linear Attention?" 5.4; LINEAR
+// rule, the CV instantiations) q, k and v are first convolved with the w-1
+// raw tokens of the conv cache, which then shifts by one token: thread t
+// owns channel t of q, k and v in every cache row, so the in-place update
+// needs no synchronisation.
+//
 // The step is bound by HBM: each (b,h) state block (d x dv fp32, 64 KiB at
 // d = dv = 128) is read once and written once.  One workgroup of 256 threads
 // owns one block; consecutive threads own consecutive VEC-wide column groups
@@ -40,7 +46,29 @@ __device__ __forceinline__ float block_sum(float x, float *red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-template <typename T, int VEC, bool DELTA>
+// Channel c of one token through the short convolution: the filter's taps
+// run over the cache rows (oldest first) and then x; the cache moves up one
+// row and x becomes its last row.  Same fp32 chain as the prefill.
+template <typename T>
+__device__ __forceinline__ float conv_channel(T *cache, const float *W, int w, int wc,
+                                              int c, T x) {
+  constexpr int kHalo = 3;  // widest filter minus one
+  T old[kHalo];
+#pragma unroll
+  for (int j = 0; j < kHalo; ++j) old[j] = j < w - 1 ? cache[(size_t)j * wc + c] : T{};
+  float y = 0.f;
+#pragma unroll
+  for (int j = 0; j < kHalo; ++j)
+    if (j < w - 1) y = fmaf(W[(size_t)j * wc + c], to_f32(old[j]), y);
+  y = fmaf(W[(size_t)(w - 1) * wc + c], to_f32(x), y);
+#pragma unroll
+  for (int j = 0; j + 1 < kHalo; ++j)
+    if (j + 1 < w - 1) cache[(size_t)j * wc + c] = old[j + 1];
+  if (w > 1) cache[(size_t)(w - 2) * wc + c] = x;
+  return y;
+}
+
+template <typename T, int VEC, bool DELTA, bool CV>
 __global__ void __launch_bounds__(kDecThreads)
 decode_kernel(DecodeParams p) {
   constexpr int ROWS = 64 / VEC;  // rows per thread at most (d <= 128)
@@ -80,16 +108,33 @@ decode_kernel(DecodeParams p) {
   const T *q = reinterpret_cast<const T *>(p.q) + (size_t)bh * d;
   const T *k = reinterpret_cast<const T *>(p.k) + (size_t)bh * d;
   const T *v = reinterpret_cast<const T *>(p.v) + (size_t)bh * dv;
+  [[maybe_unused]] const int wc = 2 * d + dv;
+  [[maybe_unused]] T *ccache = nullptr;
+  [[maybe_unused]] const float *cw = nullptr;
+  if constexpr (CV) {
+    ccache = reinterpret_cast<T *>(p.conv_cache) + (size_t)bh * (p.conv_width - 1) * wc;
+    cw = p.conv_w + (size_t)(bh % p.H) * p.conv_width * wc;
+  }
   float zold = 0.f;
   if (t < d) {
-    float xq = to_f32(q[t]), xk = to_f32(k[t]);
+    float xq, xk;
+    if constexpr (CV) {
+      xq = conv_channel<T>(ccache, cw, p.conv_width, wc, t, q[t]);
+      xk = conv_channel<T>(ccache, cw, p.conv_width, wc, d + t, k[t]);
+    } else {
+      xq = to_f32(q[t]);
+      xk = to_f32(k[t]);
+    }
     if (!DELTA && p.fmap) { xq = phi_elu1(xq); xk = phi_elu1(xk); }
     s_q[t] = xq;
     s_k[t] = xk;
     if (!DELTA) zold = p.z[(size_t)bh * d + t];
     if (!DELTA) s_al[t] = p.alpha ? p.alpha[(size_t)bh * d + t] : 1.f;
   }
-  if (t < dv) s_v[t] = to_f32(v[t]);
+  if (t < dv) {
+    if constexpr (CV) s_v[t] = conv_channel<T>(ccache, cw, p.conv_width, wc, 2 * d + t, v[t]);
+    else s_v[t] = to_f32(v[t]);
+  }
   const float gam = (!DELTA && p.gamma) ? p.gamma[bh % p.H] : 1.f;
   const bool chan = !DELTA && p.alpha != nullptr;  // per-channel decay
   const float gate = DELTA ? p.g[bh] : 0.f;
@@ -196,6 +241,18 @@ __global__ void fill_kernel(float *dst, size_t n, float value) {
     dst[i] = value;
 }
 
+__global__ void zero_bytes_kernel(unsigned char *dst, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = 0;
+}
+
+__global__ void copy_bytes_kernel(unsigned char *dst, const unsigned char *src, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
 __global__ void copy_kernel(float *dst, const float *src, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -204,8 +261,13 @@ __global__ void copy_kernel(float *dst, const float *src, size_t n) {
 
 template <typename T, int VEC, bool DELTA>
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s) {
-  return launch_kernel(DELTA ? "delta_decode" : "linear_decode", decode_kernel<T, VEC, DELTA>,
-                       dim3(p.BH), dim3(kDecThreads), s, p);
+  if constexpr (!DELTA) {
+    if (p.conv_w)
+      return launch_kernel("linear_decode", decode_kernel<T, VEC, false, true>, dim3(p.BH),
+                           dim3(kDecThreads), s, p);
+  }
+  return launch_kernel(DELTA ? "delta_decode" : "linear_decode",
+                       decode_kernel<T, VEC, DELTA, false>, dim3(p.BH), dim3(kDecThreads), s, p);
 }
 
 }  // namespace
@@ -230,6 +292,25 @@ hipError_t launch_fill(float *dst, size_t n, float value, hipStream_t s) {
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dst,
                      n, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_bytes(void *dst, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_bytes_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<unsigned char *>(dst), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_bytes(void *dst, const void *src, size_t n, hipStream_t s) {
+  if (n == 0 || dst == src) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(copy_bytes_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<unsigned char *>(dst), static_cast<const unsigned char *>(src),
+                     n);
   return hipGetLastError();
 }
 

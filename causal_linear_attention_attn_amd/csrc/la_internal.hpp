@@ -17,6 +17,8 @@ struct LinearPlan {
   int nseg;         // segments per sequence (>= 1)
   int seg_len;      // tokens per segment (multiple of chunk)
   size_t ws_bytes;  // workspace bytes
+  size_t conv_off;  // byte offset of the conv cache copy (with a convolution
+                    // over several segments; it ends the workspace)
 };
 
 struct PrefillParams {
@@ -33,6 +35,15 @@ struct PrefillParams {
   void *o;
   float *ws;
   int nseg, seg_len;
+  // short causal convolution of q, k, v (LINEAR rule): filters [H, w, 2d+dv]
+  // fp32, or nullptr; cache rows [BH, w-1, 2d+dv] of dtype T
+  const float *conv_w;
+  int conv_width;
+  const void *conv_in;   // tokens before the sequence (nullptr = zeros)
+  void *conv_out;        // last w-1 raw tokens after it (nullptr = not written)
+  const void *conv_src;  // where the chunk kernel reads the tokens before
+                         // segment 0: conv_in, or the summary kernel's copy
+  void *conv_copy;       // summary kernel: copy conv_in here (nullptr = no)
 };
 
 struct DecodeParams {
@@ -44,6 +55,9 @@ struct DecodeParams {
   float eps;
   float *S, *z;
   void *o;
+  const float *conv_w;  // [H, w, 2d+dv] or nullptr
+  int conv_width;
+  void *conv_cache;     // [BH, w-1, 2d+dv], dtype T, updated in place
 };
 
 int device_cu_count();  // cached per device
@@ -73,7 +87,9 @@ hipError_t launch_kernel(const char *name, F kernel, dim3 grid, dim3 block, hipS
   return e;
 }
 
-LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16);
+// conv_width > 0: a short convolution runs in front of q, k, v
+LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16, int conv_width);
+bool linear_combo_supported(int d, int dv, bool bf16, bool chan_decay, bool conv);
 hipError_t launch_linear_prefill(const PrefillParams &p, const LinearPlan &plan,
                                  bool bf16, hipStream_t s);
 // Gated delta rule: workspace (per-chunk Wt and R tiles) and the two-kernel
@@ -82,6 +98,8 @@ size_t delta_workspace_bytes(int BH, int N, int d, bool bf16);
 hipError_t launch_delta_prefill(const PrefillParams &p, bool bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, bool bf16, bool delta, int vec,
                          hipStream_t s);
+hipError_t launch_zero_bytes(void *dst, size_t bytes, hipStream_t s);
+hipError_t launch_copy_bytes(void *dst, const void *src, size_t bytes, hipStream_t s);
 hipError_t launch_fill(float *dst, size_t n, float value, hipStream_t s);
 hipError_t launch_copy(float *dst, const float *src, size_t n, hipStream_t s);
 

@@ -288,6 +288,234 @@ __device__ __forceinline__ void chan_prefix(SmemChan<CF> &sc, int Lc, bool total
   }
 }
 
+// ---- short causal convolution of q, k, v (the CV instantiations) ----------
+// y_t = sum_j w_j x_(t-j') over the last w tokens, per head and channel
+// ("What Is Linear Attention?" 5.4).  Fused into the row commit: a chunk's
+// raw rows go to LDS, each thread reads the kConvHalo rows before its own
+// (the first rows of a chunk find them in a small halo buffer that holds the
+// previous chunk's last raw rows), convolves in fp32 and continues with the
+// feature map as before.  Filters sit in LDS as a table of kConvTaps rows,
+// aligned so that the last row multiplies the current token; rows for taps
+// past the filter width and columns past d / dv are zero.
+constexpr int kConvTaps = 4;              // widest filter
+constexpr int kConvHalo = kConvTaps - 1;  // raw rows a chunk needs from before it
+
+template <class CF>
+struct alignas(16) SmemConv {
+  using T = typename CF::type;
+  static constexpr int WLD = 2 * CF::DK + CF::DV;  // table row: [q | k | v] columns
+  float w[kConvTaps * WLD];
+  T hq[kConvHalo * CF::QLD];  // the raw rows before the chunk, oldest first
+  T hk[kConvHalo * CF::QLD];
+  T hv[kConvHalo * CF::VLD];
+};
+struct NoConv {};
+template <class CF, bool CV>
+using ConvSmem = typename std::conditional<CV, SmemConv<CF>, NoConv>::type;
+template <class CF>
+__device__ __forceinline__ SmemConv<CF> *conv_ptr(SmemConv<CF> &s) {
+  return &s;
+}
+template <class CF>
+__device__ __forceinline__ SmemConv<CF> *conv_ptr(NoConv &) {
+  return nullptr;
+}
+
+// Filter table, and the kConvHalo raw rows before token t0: from q, k, v,
+// or, before the sequence, from the cache `src` (this head's w-1 rows of
+// [q | k | v], oldest first; zeros if null).  `copy`, if set, receives the
+// cache rows read (so that a later kernel may read them while the cache
+// itself is overwritten).
+template <class CF>
+__device__ void conv_init(SmemConv<CF> &cs, const PrefillParams &p, int bh, int t0,
+                          const typename CF::type *src, typename CF::type *copy) {
+  using T = typename CF::type;
+  constexpr int WLD = SmemConv<CF>::WLD;
+  const int d = p.d, dv = p.dv, w = p.conv_width, wc = 2 * d + dv;
+  const float *W = p.conv_w + (size_t)(bh % p.H) * w * wc;
+  const T *x[3] = {reinterpret_cast<const T *>(p.q) + (size_t)bh * p.N * d,
+                   reinterpret_cast<const T *>(p.k) + (size_t)bh * p.N * d,
+                   reinterpret_cast<const T *>(p.v) + (size_t)bh * p.N * dv};
+  for (int i = threadIdx.x; i < kConvHalo * WLD + kConvTaps * WLD; i += CF::NT) {
+    const bool is_w = i >= kConvHalo * WLD;
+    const int i2 = is_w ? i - kConvHalo * WLD : i;
+    const int row = i2 / WLD, c = i2 % WLD;
+    // tensor (0 q, 1 k, 2 v), its column and width, and the channel in [q | k | v]
+    const int tsr = c < CF::DK ? 0 : c < 2 * CF::DK ? 1 : 2;
+    const int col = c - tsr * CF::DK;
+    const int width = tsr == 2 ? dv : d;
+    const int ch = tsr * d + col;
+    if (is_w) {
+      const int tap = row - (kConvTaps - w);
+      cs.w[i2] = (col < width && tap >= 0) ? W[(size_t)tap * wc + ch] : 0.f;
+      continue;
+    }
+    const int tok = t0 - kConvHalo + row;
+    T val = from_f32<T>(0.f);
+    if (col < width) {
+      if (tok >= 0) {
+        val = x[tsr][(size_t)tok * width + col];
+      } else if (src && tok >= 1 - w) {
+        val = src[(size_t)(tok + w - 1) * wc + ch];
+        if (copy) copy[(size_t)(tok + w - 1) * wc + ch] = val;
+      }
+    }
+    T *h = tsr == 0 ? cs.hq : tsr == 1 ? cs.hk : cs.hv;
+    h[row * (tsr == 2 ? CF::VLD : CF::QLD) + col] = val;
+  }
+}
+
+// Convolved rows row0 .. row0+NR-1 at columns col0 .. col0+VEC-1 of one
+// tensor: the NR rows this thread loaded (`own`) and the kConvHalo rows
+// before them, read from the raw rows in LDS (`raw`, stride ld) or, before
+// the chunk, from the halo buffer (stride hld).
+template <class CF, int NR>
+__device__ __forceinline__ void conv_rows(float (&y)[NR][CF::VEC],
+                                          const typename CF::vec (&own)[NR],
+                                          const typename CF::type *raw, int ld,
+                                          const typename CF::type *halo, int hld, int row0,
+                                          int col0, const float *wt) {
+  using T = typename CF::type;
+  using V = typename CF::vec;
+  constexpr int VEC = CF::VEC;
+  float win[NR + kConvHalo][VEC];
+#pragma unroll
+  for (int h = 0; h < kConvHalo; ++h) {
+    const int r = row0 - kConvHalo + h;
+    const T *src = r >= 0 ? raw + r * ld + col0 : halo + (r + kConvHalo) * hld + col0;
+    const V x = *reinterpret_cast<const V *>(src);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) win[h][e] = to_f32(x[e]);
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) win[kConvHalo + i][e] = to_f32(own[i][e]);
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) y[i][e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kConvTaps; ++j) {
+    float wj[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) wj[e] = wt[j * SmemConv<CF>::WLD + col0 + e];
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) y[i][e] = fmaf(wj[e], win[i + j][e], y[i][e]);
+  }
+}
+
+// This thread's convolved rows (fp32), and its final rows as they go to LDS
+// once every thread has read its window.
+template <class CF, bool WITH_Q>
+struct ConvOut {
+  float q[WITH_Q ? CF::RQ : 1][CF::VEC];
+  float k[CF::RQ][CF::VEC];
+  float v[CF::RV][CF::VEC];
+};
+template <class CF, bool WITH_Q>
+struct ConvRows {
+  typename CF::vec q[WITH_Q ? CF::RQ : 1], k[CF::RQ], v[CF::RV];
+};
+template <class CF>
+__device__ __forceinline__ typename CF::vec pack_vec(const float (&x)[CF::VEC]) {
+  typename CF::vec v;
+#pragma unroll
+  for (int e = 0; e < CF::VEC; ++e) v[e] = from_f32<typename CF::type>(x[e]);
+  return v;
+}
+
+// Convolve this thread's rows of the chunk.  The raw rows are staged in
+// Qs / Ks / Vs (a barrier, then each thread reads its window); the caller
+// overwrites them with the final rows after a second barrier.
+template <class CF, bool WITH_Q>
+__device__ __forceinline__ void conv_gather(ConvOut<CF, WITH_Q> &Y, const ChunkRegs<CF> &R,
+                                            typename CF::type *Qs, typename CF::type *Ks,
+                                            typename CF::type *Vs, const SmemConv<CF> &cs) {
+  using V = typename CF::vec;
+  const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
+  const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
+  const int qc0 = qcb * CF::VEC, vc0 = vcb * CF::VEC;
+#pragma unroll
+  for (int r = 0; r < CF::RQ; ++r) {
+    const int row = qrg * CF::RQ + r;
+    if constexpr (WITH_Q) *reinterpret_cast<V *>(Qs + row * CF::QLD + qc0) = R.q[r];
+    *reinterpret_cast<V *>(Ks + row * CF::QLD + qc0) = R.k[r];
+  }
+#pragma unroll
+  for (int r = 0; r < CF::RV; ++r)
+    *reinterpret_cast<V *>(Vs + (vrg * CF::RV + r) * CF::VTLD + vc0) = R.v[r];
+  __syncthreads();
+  if constexpr (WITH_Q)
+    conv_rows<CF, CF::RQ>(Y.q, R.q, Qs, CF::QLD, cs.hq, CF::QLD, qrg * CF::RQ, qc0, cs.w);
+  conv_rows<CF, CF::RQ>(Y.k, R.k, Ks, CF::QLD, cs.hk, CF::QLD, qrg * CF::RQ, qc0,
+                        cs.w + CF::DK);
+  conv_rows<CF, CF::RV>(Y.v, R.v, Vs, CF::VTLD, cs.hv, CF::VLD, vrg * CF::RV, vc0,
+                        cs.w + 2 * CF::DK);
+}
+
+// After the second barrier: the chunk's last kConvHalo raw rows become the
+// next chunk's halo.
+template <class CF>
+__device__ __forceinline__ void conv_halo(const ChunkRegs<CF> &R, SmemConv<CF> &cs,
+                                          bool with_q) {
+  using V = typename CF::vec;
+  const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
+  const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
+  const int qc0 = qcb * CF::VEC, vc0 = vcb * CF::VEC;
+#pragma unroll
+  for (int r = 0; r < CF::RQ; ++r) {
+    const int h = qrg * CF::RQ + r - (CF::C - kConvHalo);
+    if (h >= 0) {
+      if (with_q) *reinterpret_cast<V *>(cs.hq + h * CF::QLD + qc0) = R.q[r];
+      *reinterpret_cast<V *>(cs.hk + h * CF::QLD + qc0) = R.k[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < CF::RV; ++r) {
+    const int h = vrg * CF::RV + r - (CF::C - kConvHalo);
+    if (h >= 0) *reinterpret_cast<V *>(cs.hv + h * CF::VLD + vc0) = R.v[r];
+  }
+}
+
+// The cache after the sequence: its last w-1 raw tokens (from the cache
+// before it when the sequence is shorter).  Every value is loaded before
+// the barrier and stored after it, so conv_out may alias conv_in.
+template <class CF>
+__device__ void conv_final(const PrefillParams &p, int bh) {
+  using T = typename CF::type;
+  const int d = p.d, dv = p.dv, N = p.N, w = p.conv_width, wc = 2 * d + dv;
+  const int n = (w - 1) * wc;
+  constexpr int MAXE = (kConvHalo * 3 * LA_MAXD + CF::NT - 1) / CF::NT;
+  const T *in = p.conv_in ? reinterpret_cast<const T *>(p.conv_in) + (size_t)bh * n : nullptr;
+  const T *x[3] = {reinterpret_cast<const T *>(p.q) + (size_t)bh * N * d,
+                   reinterpret_cast<const T *>(p.k) + (size_t)bh * N * d,
+                   reinterpret_cast<const T *>(p.v) + (size_t)bh * N * dv};
+  T val[MAXE];
+#pragma unroll
+  for (int m = 0; m < MAXE; ++m) {
+    const int i = threadIdx.x + m * CF::NT;
+    val[m] = from_f32<T>(0.f);
+    if (i < n) {
+      const int row = i / wc, ch = i % wc;
+      const int tok = N - (w - 1) + row;
+      const int tsr = ch < d ? 0 : ch < 2 * d ? 1 : 2;
+      const int col = ch - tsr * d, width = tsr == 2 ? dv : d;
+      if (tok >= 0) val[m] = x[tsr][(size_t)tok * width + col];
+      else if (in) val[m] = in[(size_t)(tok + w - 1) * wc + ch];
+    }
+  }
+  __syncthreads();
+  T *out = reinterpret_cast<T *>(p.conv_out) + (size_t)bh * n;
+#pragma unroll
+  for (int m = 0; m < MAXE; ++m) {
+    const int i = threadIdx.x + m * CF::NT;
+    if (i < n) out[i] = val[m];
+  }
+}
+
 template <class CF, bool WITH_Q, bool VK>
 __device__ __forceinline__ void prefetch(ChunkRegs<CF> &R, const PrefillParams &p,
                                          const HeadBufs &hb, int c0, int Lc) {
@@ -314,8 +542,11 @@ __device__ __forceinline__ void prefetch(ChunkRegs<CF> &R, const PrefillParams &
 // meet zero keys and zero state rows).  The feature map and the column mask
 // are uniform per launch and taken as branches, so the common case carries
 // no per-element selects; key weights are 1 for a full chunk without decay.
-template <class CF, bool WITH_Q, bool ELU, bool CH>
-__device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R, typename CF::type *Qs,
+template <class CF, bool WITH_Q, bool ELU, bool CH, bool CV>
+__device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R,
+                                            const ConvOut<CF, WITH_Q> *Y,
+                                            ConvRows<CF, WITH_Q> *P,
+                                            typename CF::type *Qs,
                                             typename CF::type *Ks, const float *pw,
                                             const PrefillParams &p, int Lc,
                                             const SmemChan<CF> *sc) {
@@ -336,15 +567,20 @@ __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R, typename CF:
     if constexpr (WITH_Q) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const float xq = to_f32(R.q[r][e]);
+        float xq;
+        if constexpr (CV) xq = Y->q[r][e];
+        else xq = to_f32(R.q[r][e]);
         x[e] = ELU ? phi_elu1(xq) : xq;
         if constexpr (CH) x[e] *= __expf(lbr[e] - lbm[e]);
       }
-      lds_store_n<T, VEC>(Qs + row * CF::QLD + col0, x);
+      if constexpr (CV) P->q[r] = pack_vec<CF>(x);
+      else lds_store_n<T, VEC>(Qs + row * CF::QLD + col0, x);
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      const float xk = to_f32(R.k[r][e]);
+      float xk;
+      if constexpr (CV) xk = Y->k[r][e];
+      else xk = to_f32(R.k[r][e]);
       x[e] = ELU ? phi_elu1(xk) : xk;
       if constexpr (CH) x[e] *= __expf(lbm[e] - lbr[e]);
     }
@@ -353,30 +589,63 @@ __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R, typename CF:
     if (__builtin_expect(colmask, 0)) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) x[e] = col0 + e < p.d ? x[e] * w : 0.f;
-      lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
+      if constexpr (CV) P->k[r] = pack_vec<CF>(x);
+      else lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
     } else {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) x[e] *= w;
-      lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
+      if constexpr (CV) P->k[r] = pack_vec<CF>(x);
+      else lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
     }
   }
 }
 
-template <class CF, bool WITH_Q, bool CH = false>
+template <class CF, bool WITH_Q, bool CH = false, bool CV = false>
 __device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type *Qs,
                                        typename CF::type *Ks, typename CF::type *Vs,
                                        const float *pw, const PrefillParams &p, int Lc,
-                                       const SmemChan<CF> *sc = nullptr) {
+                                       const SmemChan<CF> *sc = nullptr,
+                                       SmemConv<CF> *cs = nullptr) {
+  using T = typename CF::type;
   using V = typename CF::vec;
-  if (p.fmap != 0)
-    commit_rows<CF, WITH_Q, true, CH>(R, Qs, Ks, pw, p, Lc, sc);
-  else
-    commit_rows<CF, WITH_Q, false, CH>(R, Qs, Ks, pw, p, Lc, sc);
   const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
+  if constexpr (CV) {
+    // final rows computed in registers while the raw rows are still staged
+    ConvRows<CF, WITH_Q> P;
+    {
+      ConvOut<CF, WITH_Q> Y;
+      conv_gather<CF, WITH_Q>(Y, R, Qs, Ks, Vs, *cs);
+      if (p.fmap != 0)
+        commit_rows<CF, WITH_Q, true, CH, true>(R, &Y, &P, Qs, Ks, pw, p, Lc, sc);
+      else
+        commit_rows<CF, WITH_Q, false, CH, true>(R, &Y, &P, Qs, Ks, pw, p, Lc, sc);
 #pragma unroll
-  for (int r = 0; r < CF::RV; ++r) {
-    const int row = vrg * CF::RV + r;
-    *reinterpret_cast<V *>(Vs + row * CF::VTLD + vcb * CF::VEC) = R.v[r];
+      for (int r = 0; r < CF::RV; ++r) P.v[r] = pack_vec<CF>(Y.v[r]);
+    }
+    __syncthreads();
+    conv_halo<CF>(R, *cs, WITH_Q);
+    const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
+#pragma unroll
+    for (int r = 0; r < CF::RQ; ++r) {
+      const int row = qrg * CF::RQ + r;
+      if constexpr (WITH_Q) *reinterpret_cast<V *>(Qs + row * CF::QLD + qcb * CF::VEC) = P.q[r];
+      *reinterpret_cast<V *>(Ks + row * CF::QLD + qcb * CF::VEC) = P.k[r];
+    }
+#pragma unroll
+    for (int r = 0; r < CF::RV; ++r) {
+      const int row = vrg * CF::RV + r;
+      *reinterpret_cast<V *>(Vs + row * CF::VTLD + vcb * CF::VEC) = P.v[r];
+    }
+  } else {
+    if (p.fmap != 0)
+      commit_rows<CF, WITH_Q, true, CH, false>(R, nullptr, nullptr, Qs, Ks, pw, p, Lc, sc);
+    else
+      commit_rows<CF, WITH_Q, false, CH, false>(R, nullptr, nullptr, Qs, Ks, pw, p, Lc, sc);
+#pragma unroll
+    for (int r = 0; r < CF::RV; ++r) {
+      const int row = vrg * CF::RV + r;
+      *reinterpret_cast<V *>(Vs + row * CF::VTLD + vcb * CF::VEC) = R.v[r];
+    }
   }
 }
 
@@ -611,13 +880,22 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillPa
 
 }
 
-template <class CF, bool VK, bool CH>
-__global__ void __launch_bounds__(CF::NT, CH ? (CF::WPE < 2 ? CF::WPE : 2) : CF::WPE)
+// Resident waves per SIMD the register allocation must allow: the
+// per-channel decay and the convolution need more registers than three
+// waves leave.
+template <class CF>
+constexpr int wpe_at_most_2() {
+  return CF::WPE < 2 ? CF::WPE : 2;
+}
+
+template <class CF, bool VK, bool CH, bool CV>
+__global__ void __launch_bounds__(CF::NT, (CH || CV) ? wpe_at_most_2<CF>() : CF::WPE)
     chunk_kernel(PrefillParams p) {
   using T = typename CF::type;
   using V = typename CF::vec;
   __shared__ SmemChunk<CF> sm;
   __shared__ ChanSmem<CF, CH> sc;  // per-channel decay (CH) only
+  __shared__ ConvSmem<CF, CV> cs;  // short convolution (CV) only
 
   const int seg = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -649,6 +927,12 @@ __global__ void __launch_bounds__(CF::NT, CH ? (CF::WPE < 2 ? CF::WPE : 2) : CF:
   [[maybe_unused]] const __amdgpu_buffer_rsrc_t ra =
       CH ? buf_rsrc(p.alpha + (size_t)bh * N * d, (uint32_t)((size_t)N * d * 4)) : hb.q;
   if constexpr (CH) chan_prefetch<CF, VK>(A, ra, p, t_begin, min(CF::C, N - t_begin));
+  if constexpr (CV)  // the tokens before segment 0 come from the cache (or its copy)
+    conv_init<CF>(cs, p, bh, t_begin,
+                  p.conv_src ? reinterpret_cast<const T *>(p.conv_src) +
+                                   (size_t)bh * (p.conv_width - 1) * (2 * d + dv)
+                             : nullptr,
+                  nullptr);
   fill_powers<CF>(sm.pw, decay ? log2f(p.gamma[bh % p.H]) : 0.f);
   __syncthreads();
   if constexpr (!CH)
@@ -664,7 +948,8 @@ __global__ void __launch_bounds__(CF::NT, CH ? (CF::WPE < 2 ? CF::WPE : 2) : CF:
       chan_prefix<CF>(sc, Lc, false);
       __syncthreads();
     }
-    commit<CF, true, CH>(R, sm.Qs, sm.Ks, sm.Vs, sm.pw, p, Lc, chan_ptr<CF>(sc));
+    commit<CF, true, CH, CV>(R, sm.Qs, sm.Ks, sm.Vs, sm.pw, p, Lc, chan_ptr<CF>(sc),
+                             conv_ptr<CF>(cs));
     if constexpr (CH) {  // state read from diag(exp(lb_m)) S-
       chan_scale<CF>(Sacc, sc.bm, wv, lg);
       rescale_and_copy_state<CF>(sm.St, Sacc, 1.f, false, wv, li, lg);
@@ -722,18 +1007,24 @@ __global__ void __launch_bounds__(CF::NT, CH ? (CF::WPE < 2 ? CF::WPE : 2) : CF:
     }
   }
 
-  if (seg == p.nseg - 1)
+  if (seg == p.nseg - 1) {
     store_state<CF>(Sacc, p.S_out ? p.S_out + (size_t)bh * d * dv : nullptr,
                     p.z_out ? p.z_out + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
+    if constexpr (CV) {
+      if (p.conv_out) conv_final<CF>(p, bh);
+    }
+  }
 }
 
 // Phase 1: each segment's own contribution, from a zero state (all but the
 // last segment; those are whole multiples of the chunk length).
-template <class CF, bool VK, bool CH>
-__global__ void __launch_bounds__(CF::NT, CF::WPE) summary_kernel(PrefillParams p) {
+template <class CF, bool VK, bool CH, bool CV>
+__global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF::WPE)
+    summary_kernel(PrefillParams p) {
   using T = typename CF::type;
   __shared__ SmemSummary<CF> sm;
   __shared__ ChanSmem<CF, CH> sc;  // per-channel decay (CH) only
+  __shared__ ConvSmem<CF, CV> cs;  // short convolution (CV) only
   const int seg = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -753,6 +1044,12 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) summary_kernel(PrefillParams 
     chan_prefetch<CF, VK>(A, ra, p, t_begin, CF::C);
     if (threadIdx.x < CF::DK) sc.tot[threadIdx.x] = 0.f;
   }
+  if constexpr (CV) {  // segment 0 reads the cache and leaves a copy for chunk_kernel
+    const size_t crow = (size_t)bh * (p.conv_width - 1) * (2 * d + dv);
+    conv_init<CF>(cs, p, bh, t_begin,
+                  p.conv_in ? reinterpret_cast<const T *>(p.conv_in) + crow : nullptr,
+                  p.conv_copy ? reinterpret_cast<T *>(p.conv_copy) + crow : nullptr);
+  }
   fill_powers<CF>(sm.pw, decay ? log2f(p.gamma[bh % p.H]) : 0.f);
 
   f32x4 Sacc[CF::FPW][CF::TPW];
@@ -769,7 +1066,8 @@ __global__ void __launch_bounds__(CF::NT, CF::WPE) summary_kernel(PrefillParams 
       chan_prefix<CF>(sc, CF::C, true);
       __syncthreads();
     }
-    commit<CF, false, CH>(R, nullptr, sm.Ks, sm.Vs, sm.pw, p, CF::C, chan_ptr<CF>(sc));
+    commit<CF, false, CH, CV>(R, nullptr, sm.Ks, sm.Vs, sm.pw, p, CF::C, chan_ptr<CF>(sc),
+                              conv_ptr<CF>(cs));
     if constexpr (CH) {
       chan_scale<CF>(Sacc, sc.bm, wv, lg);
       if (c0 + CF::C < t_end) chan_prefetch<CF, VK>(A, ra, p, c0 + CF::C, CF::C);
@@ -830,12 +1128,20 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
   }
 }
 
-template <class CF, bool VK, bool CH>
-hipError_t run_vkc(const PrefillParams &p, hipStream_t s) {
-  static_assert(sizeof(SmemChunk<CF>) + (CH ? sizeof(SmemChan<CF>) : 0) <= kLdsBytes,
-                "LDS budget");
+// LDS of one chunk_kernel workgroup
+template <class CF, bool CH, bool CV>
+constexpr size_t chunk_lds() {
+  return sizeof(SmemChunk<CF>) + (CH ? sizeof(SmemChan<CF>) : 0) +
+         (CV ? sizeof(SmemConv<CF>) : 0);
+}
+
+template <class CF, bool VK, bool CH, bool CV>
+hipError_t run_vkcc(const PrefillParams &p, hipStream_t s) {
+  if constexpr (chunk_lds<CF, CH, CV>() > kLdsBytes) {
+    return hipErrorNotSupported;  // refused on the host before any launch
+  } else {
   if (p.nseg > 1) {
-    hipError_t e = launch_kernel("linear_summary", summary_kernel<CF, VK, CH>,
+    hipError_t e = launch_kernel("linear_summary", summary_kernel<CF, VK, CH, CV>,
                                  dim3(p.nseg - 1, p.BH), dim3(CF::NT), s, p);
     if (e != hipSuccess) return e;
     const size_t rec = (size_t)p.d * p.dv + p.d;
@@ -843,12 +1149,18 @@ hipError_t run_vkc(const PrefillParams &p, hipStream_t s) {
                       dim3(256), s, p);
     if (e != hipSuccess) return e;
   }
-  return launch_kernel("linear_chunk", chunk_kernel<CF, VK, CH>, dim3(p.nseg, p.BH),
+  return launch_kernel("linear_chunk", chunk_kernel<CF, VK, CH, CV>, dim3(p.nseg, p.BH),
                        dim3(CF::NT), s, p);
+  }
 }
 
-// a per-key-channel decay gets its own instantiations (none of its work is
-// compiled into the others)
+// a per-key-channel decay and a short convolution get their own
+// instantiations (none of their work is compiled into the others)
+template <class CF, bool VK, bool CH>
+hipError_t run_vkc(const PrefillParams &p, hipStream_t s) {
+  return p.conv_w ? run_vkcc<CF, VK, CH, true>(p, s) : run_vkcc<CF, VK, CH, false>(p, s);
+}
+
 template <class CF, bool VK>
 hipError_t run_vk(const PrefillParams &p, hipStream_t s) {
   return p.alpha ? run_vkc<CF, VK, true>(p, s) : run_vkc<CF, VK, false>(p, s);
@@ -860,14 +1172,15 @@ hipError_t run(const PrefillParams &p, hipStream_t s) {
 }
 
 // Workgroups of chunk_kernel<CF> that fit on one CU (queried once).
-template <class CF>
+template <class CF, bool CV>
 int resident_per_cu() {
   static std::atomic<int> cached{0};
   int v = cached.load(std::memory_order_relaxed);
   if (v > 0) return v;
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<CF, true, false>, CF::NT, 0) !=
-          hipSuccess || n < 1) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<CF, true, false, CV>,
+                                                   CF::NT, 0) != hipSuccess ||
+      n < 1) {
     (void)hipGetLastError();
     n = 1;
   }
@@ -887,24 +1200,25 @@ using F128x64 = Cfg<float, 128, 64, 32, 8>;
 using F128x128 = Cfg<float, 128, 128, 32, 8>;
 
 template <class CF>
-void fill_plan(LinearPlan &pl) {
+void fill_plan(LinearPlan &pl, bool conv) {
   pl.chunk = CF::C;
   pl.threads = CF::NT;
-  pl.per_cu = resident_per_cu<CF>();
+  pl.per_cu = conv ? resident_per_cu<CF, true>() : resident_per_cu<CF, false>();
 }
 
 }  // namespace
 
-LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io) {
+LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io, int conv_width) {
   LinearPlan pl{};
   pl.dk = d <= 64 ? 64 : 128;
   pl.dv_pad = dv <= 64 ? 64 : 128;
+  const bool cv = conv_width > 0;
   if (bf16_io) {
-    if (pl.dk == 64) pl.dv_pad == 64 ? fill_plan<B64x64>(pl) : fill_plan<B64x128>(pl);
-    else pl.dv_pad == 64 ? fill_plan<B128x64>(pl) : fill_plan<B128x128>(pl);
+    if (pl.dk == 64) pl.dv_pad == 64 ? fill_plan<B64x64>(pl, cv) : fill_plan<B64x128>(pl, cv);
+    else pl.dv_pad == 64 ? fill_plan<B128x64>(pl, cv) : fill_plan<B128x128>(pl, cv);
   } else {
-    if (pl.dk == 64) pl.dv_pad == 64 ? fill_plan<F64x64>(pl) : fill_plan<F64x128>(pl);
-    else pl.dv_pad == 64 ? fill_plan<F128x64>(pl) : fill_plan<F128x128>(pl);
+    if (pl.dk == 64) pl.dv_pad == 64 ? fill_plan<F64x64>(pl, cv) : fill_plan<F64x128>(pl, cv);
+    else pl.dv_pad == 64 ? fill_plan<F128x64>(pl, cv) : fill_plan<F128x128>(pl, cv);
   }
   const long chunks = N > 0 ? ((long)N + pl.chunk - 1) / pl.chunk : 0;
   long nseg = 1;
@@ -921,7 +1235,17 @@ LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io) {
   pl.nseg = (int)nseg;
   pl.seg_len = (int)(cps * pl.chunk);
   pl.ws_bytes = nseg > 1 ? (size_t)nseg * BH * ws_rec(d, dv) * sizeof(float) : 0;
+  pl.conv_off = pl.ws_bytes;
+  if (nseg > 1 && conv_width > 1)  // room for the summary kernel's copy of the cache
+    pl.ws_bytes += (size_t)BH * (conv_width - 1) * (2 * d + dv) * (bf16_io ? 2 : 4);
   return pl;
+}
+
+// A short convolution together with a per-key-channel decay does not fit
+// the LDS of the fp32 instantiation with d and dv above 64.
+bool linear_combo_supported(int d, int dv, bool bf16_io, bool chan, bool conv) {
+  if (bf16_io || !chan || !conv || d <= 64 || dv <= 64) return true;
+  return chunk_lds<F128x128, true, true>() <= kLdsBytes;
 }
 
 hipError_t launch_linear_prefill(const PrefillParams &p, const LinearPlan &pl,

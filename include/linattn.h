@@ -76,7 +76,17 @@ typedef enum { LA_FMAP_IDENTITY = 0, LA_FMAP_ELU1 = 1 } la_fmap;
  *   raw q and k (fmap must be IDENTITY), no normaliser, no z.  With the
  *   optional scalar decay alpha_t (Gated DeltaNet, [EAV] section 7.4; the
  *   error is taken on the decayed state):
- *     S_t = alpha_t S_{t-1} + g_t k_t (v_t - alpha_t S_{t-1}^T k_t)^T */
+ *     S_t = alpha_t S_{t-1} + g_t k_t (v_t - alpha_t S_{t-1}^T k_t)^T
+ *
+ * Short causal convolution (LINEAR rule only; [WILA] section 5.4: a short
+ * convolution over the most recent tokens in front of the state, with a
+ * conv cache of those tokens kept beside the state for decoding): with
+ * filters W [H, w, 2d+dv] (fp32, channels [q | k | v]) each raw q, k and v
+ * channel is replaced, before the feature map, by
+ *     x'_t[c] = sum_{j=0..w-1} W[h, j, c] * x_{t-(w-1)+j}[c]
+ * (tap w-1 on the current token; depthwise, no bias, no activation).  The
+ * conv cache [B, H, w-1, 2d+dv] (dtype of q, rows oldest first) holds the
+ * raw tokens before the current one: [q | k | v] of each token. */
 typedef enum { LA_RULE_LINEAR = 0, LA_RULE_DELTA = 1 } la_rule;
 
 /* One call processes B*H independent sequences of N tokens. */
@@ -103,6 +113,17 @@ typedef struct la_prefill_args {
                         Values are the caller's contract (not read on the
                         host); values outside the range make the chunk's
                         decay products inaccurate or undefined. */
+  const float *conv_weight; /* LINEAR: [H, w, 2d+dv] short-convolution
+                        filters (see above), or NULL (no convolution; then
+                        conv_width is 0 and conv_in, conv_out are NULL).
+                        DELTA: must be NULL (LA_EUNSUPPORTED). */
+  int32_t conv_width;/* w, 1..4 with conv_weight */
+  const void *conv_in;/* [B,H,w-1,2d+dv] conv cache before the sequence,
+                        dtype as q; NULL = zeros */
+  void *conv_out;    /* [B,H,w-1,2d+dv] the last w-1 raw tokens after the
+                        sequence (from conv_in where N < w-1); NULL = not
+                        written.  May alias conv_in exactly; no other
+                        overlap. */
   float eps;         /* LINEAR: added to the denominator, >= 0. DELTA: ignored */
   const float *S_in; /* [B,H,d,dv] initial state; NULL = zeros */
   const float *z_in; /* LINEAR: [B,H,d] initial normaliser; NULL = zeros.
@@ -118,7 +139,8 @@ typedef struct la_prefill_args {
 } la_prefill_args;
 
 /* Bytes of device workspace la_prefill needs for these arguments on the
- * current device (0 when none).  Reads only the sizes, dtype and rule.
+ * current device (0 when none).  Reads only the sizes, dtype, rule,
+ * conv_width and whether conv_weight and alpha are set.
  * Returns (size_t)-1 when the sizes are invalid. */
 size_t la_prefill_workspace_size(const la_prefill_args *args);
 
@@ -141,6 +163,11 @@ typedef struct la_decode_args {
   const float *g;    /* DELTA: [B,H] write gate (required). LINEAR: NULL. */
   const float *alpha;/* State decay, or NULL (= 1).  DELTA: [B,H].
                         LINEAR: [B,H,d] per key channel (not with gamma). */
+  const float *conv_weight; /* LINEAR: [H, w, 2d+dv] short-convolution
+                        filters, or NULL.  DELTA: must be NULL. */
+  int32_t conv_width;/* w, 1..4 with conv_weight; 0 without */
+  void *conv_cache;  /* [B,H,w-1,2d+dv] conv cache, dtype as q, read and
+                        shifted in place by one token (required for w > 1) */
   float eps;         /* LINEAR: >= 0 */
   float *S;          /* [B,H,d,dv] fp32, read and overwritten in place */
   float *z;          /* LINEAR: [B,H,d] fp32 in place (required).
@@ -149,7 +176,8 @@ typedef struct la_decode_args {
 } la_decode_args;
 
 /* One decode step ([LIO3] 'recurrent form': one read and one write of the
- * state per token).  S (and z) must not overlap q, k, v or o. */
+ * state per token).  S (and z, conv_cache) must not overlap q, k, v or o,
+ * or one another. */
 int la_decode_step(const la_decode_args *args, void *stream);
 
 /* Zero-fill a state: S [B,H,d,dv] and, if z is not NULL, z [B,H,d]

@@ -7,8 +7,11 @@ from .la_oracle import (  # noqa: F401
     delta_step,
     feature_map,
     linear_decode_step,
+    linear_decode_step_conv,
     linear_prefill,
+    linear_prefill_conv,
     linear_quadratic,
     linear_step,
     phi_elu1,
+    short_conv,
 )

@@ -95,6 +95,13 @@ def _args(**kw):
     dict(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY,
          g=ctypes.c_void_p(0x2000), gamma=ctypes.c_void_p(0x3000)),
     dict(alpha=ctypes.c_void_p(0x2000), gamma=ctypes.c_void_p(0x3000)),  # both decays
+    dict(conv_weight=ctypes.c_void_p(0x2000), conv_width=0),  # conv width 1..4
+    dict(conv_weight=ctypes.c_void_p(0x2000), conv_width=5),
+    dict(conv_width=2),                                     # width without filters
+    dict(conv_in=ctypes.c_void_p(0x2000)),                  # cache without filters
+    dict(conv_out=ctypes.c_void_p(0x2000)),
+    dict(conv_weight=ctypes.c_void_p(0x2000), conv_width=4,  # caches overlap partly
+         conv_in=ctypes.c_void_p(0x4000), conv_out=ctypes.c_void_p(0x4002)),
 ])
 def test_prefill_rejects_invalid_arguments(lib, bad):
     a = _args(**bad)
@@ -104,6 +111,14 @@ def test_prefill_rejects_invalid_arguments(lib, bad):
 def test_prefill_null_args_and_unsupported_grid(lib):
     assert lib.la_prefill(None, None) == _lib.LA_EINVAL
     a = _args(B=70000, H=1)
+    assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+    fake = ctypes.c_void_p(0x2000)
+    # the short convolution is built for the LINEAR rule only
+    a = _args(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY, g=fake,
+              conv_weight=fake, conv_width=4)
+    assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+    # fp32, d = dv = 128: convolution and per-channel decay exceed the LDS together
+    a = _args(dtype=_lib.LA_F32, d=128, dv=128, alpha=fake, conv_weight=fake, conv_width=4)
     assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
     assert lib.la_prefill_workspace_size(ctypes.byref(_args(d=0))) == \
         ctypes.c_size_t(-1).value
@@ -123,6 +138,12 @@ def test_empty_inputs_are_noops(lib):
     dict(rule=_lib.LA_RULE_DELTA),                          # elu1 + delta
     dict(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY),  # z given, no g
     dict(alpha=ctypes.c_void_p(0x2000), gamma=ctypes.c_void_p(0x3000)),  # both decays
+    dict(conv_weight=ctypes.c_void_p(0x2000), conv_width=0,
+         conv_cache=ctypes.c_void_p(0x3000)),
+    dict(conv_weight=ctypes.c_void_p(0x2000), conv_width=5,
+         conv_cache=ctypes.c_void_p(0x3000)),
+    dict(conv_weight=ctypes.c_void_p(0x2000), conv_width=3),   # no cache
+    dict(conv_width=2), dict(conv_cache=ctypes.c_void_p(0x3000)),  # no filters
 ])
 def test_decode_rejects_invalid_arguments(lib, bad):
     a = _lib.DecodeArgs()
@@ -134,6 +155,16 @@ def test_decode_rejects_invalid_arguments(lib, bad):
     for k, v in bad.items():
         setattr(a, k, v)
     assert lib.la_decode_step(ctypes.byref(a), None) == _lib.LA_EINVAL
+
+
+def test_decode_conv_on_delta_is_unsupported(lib):
+    a = _lib.DecodeArgs()
+    a.B, a.H, a.d, a.dv = 2, 2, 8, 8
+    a.dtype, a.rule, a.fmap = _lib.LA_BF16, _lib.LA_RULE_DELTA, _lib.LA_FMAP_IDENTITY
+    fake = ctypes.c_void_p(0x1000)
+    a.q = a.k = a.v = a.o = a.S = a.g = fake
+    a.conv_weight, a.conv_width, a.conv_cache = fake, 4, fake
+    assert lib.la_decode_step(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
 
 
 def test_state_init_rejects_invalid_arguments(lib):
