@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the causal linear attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|4|5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2..8]
                     [--no-decode] [--no-extra] [--no-cpu-baseline]
 
 Prints ONE JSON line.  A "step" is one la_prefill call over the whole batch
@@ -24,9 +24,11 @@ per step.  Alongside:
                 q, k, v): steps/s and state GB/s against HBM peak;
   workloads     the long-context decay prefill (B=1 H=32 N=131072 d=128), the
                 gated delta-rule prefill (B=2 H=16 N=8192 d=128), the same
-                with a per-token state decay alpha in (0.9, 1), and the main
-                workload with a per-key-channel decay (GLA), each with its
-                kernels' times and HBM fraction;
+                with a per-token state decay alpha in (0.9, 1), the main
+                workload with a per-key-channel decay (GLA), and the main
+                workload behind a width-4 short convolution of q, k, v (conv
+                cache in and out), each with its kernels' times and HBM
+                fraction;
   cpu_baseline  the fp64 oracle on the host (one thread) over the same
                 inputs of the main workload (a reported baseline, not a
                 target), with its parity error against the GPU output.
@@ -56,7 +58,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7],
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5, 6, 7, 8],
                     help="3 runs the decode-step loop alone")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -344,12 +346,15 @@ def make_step(la, torch, w, x):
     else:
         z = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
         al = x.get("alpha")
-        ws_bytes = la.workspace_size(q, k, v, gamma=gamma, eps=w.eps)
+        cw, cin = x.get("conv_weight"), x.get("conv_cache")
+        cout = None if cin is None else torch.empty_like(cin)
+        ws_bytes = la.workspace_size(q, k, v, gamma=gamma, eps=w.eps, alpha=al,
+                                     conv_weight=cw)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
         def step():
             la.prefill(q, k, v, gamma=gamma, alpha=al, eps=w.eps, o=o, S_out=S, z_out=z,
-                       workspace=ws)
+                       workspace=ws, conv_weight=cw, conv_cache=cin, conv_cache_out=cout)
     return step, o, ws_bytes
 
 
@@ -494,6 +499,12 @@ def cpu_baseline(w, x, o_gpu):
             al = x.get("alpha")
             ro, _ = oracle.delta_prefill(q, k, v, x["g"].cpu(),
                                          alpha=None if al is None else al.cpu())
+        elif x.get("conv_weight") is not None:
+            al = x.get("alpha")
+            ro = oracle.linear_prefill_conv(q, k, v, x["conv_weight"].cpu(),
+                                            conv_cache=x["conv_cache"].cpu(), eps=w.eps,
+                                            gamma=gamma,
+                                            alpha=None if al is None else al.cpu())[0]
         else:
             al = x.get("alpha")
             ro, _, _ = oracle.linear_prefill(q, k, v, eps=w.eps, gamma=gamma,
@@ -558,7 +569,8 @@ def main():
         "data": "synthetic (seeded normal draws; see inputs.py)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "dv": w.dv, "rule": w.rule, "fmap": w.fmap, "decay": w.decay,
-                   "eps": w.eps, "head_tokens_per_step": w.B * w.H * w.N},
+                   "conv": w.conv, "eps": w.eps,
+                   "head_tokens_per_step": w.B * w.H * w.N},
         "roofline": res["roofline"], "mfma": res["mfma"],
         "step_hbm_frac": res["step_hbm_frac"], "kernels_ms": res["kernels_ms"],
         "workspace_bytes": res["workspace_bytes"],
@@ -570,7 +582,7 @@ def main():
         line["decode"] = bench_decode(la, lib, torch, args.decode_steps)
     if not args.no_extra:
         extra = {}
-        for wid in (4, 5, 6, 7):
+        for wid in (4, 5, 6, 7, 8):
             if wid == args.workload:
                 continue
             r, xx, oo = bench_workload(la, lib, torch, inputs.WORKLOADS[wid],

@@ -105,7 +105,8 @@ def workspace_size(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None,
 
 def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
             S_in=None, z_in=None, S_out=None, z_out=None, return_state=True,
-            o=None, workspace=None, alpha=None, conv_weight=None, conv_cache=None):
+            o=None, workspace=None, alpha=None, conv_weight=None, conv_cache=None,
+            conv_cache_out=None):
     """Chunked prefill over [B,H,N,*] sequences (see la_prefill).
 
     rule "linear": fmap defaults to "elu1"; gamma [H] fp32 or None; eps >= 0;
@@ -114,7 +115,8 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
                    convolution of q, k, v: conv_weight [H, w, 2d+dv] fp32
                    (w <= 4) and conv_cache [B,H,w-1,2d+dv] (dtype of q), read
                    as the tokens before the sequence and overwritten in place
-                   with the last w-1 tokens (None: zeros before, not kept).
+                   with the last w-1 tokens (None: zeros before, not kept),
+                   or, with conv_cache_out, written there instead.
     rule "delta":  fmap "identity"; g [B,H,N] fp32 required; alpha [B,H,N]
                    fp32 state decay in (0, 1] or None.
     Returns (o, S_out, z_out); the states are None unless requested
@@ -123,7 +125,7 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
     if fmap is None:
         fmap = "elu1" if rule == "linear" else "identity"
     _need_gpu(q, k, v, gamma, g, alpha, S_in, z_in, S_out, z_out, o, workspace,
-              conv_weight, conv_cache)
+              conv_weight, conv_cache, conv_cache_out)
     _need_f32(gamma, g, alpha, S_in, z_in, S_out, z_out, conv_weight)
     if alpha is not None:
         want = q.shape if rule == "linear" else q.shape[:3]
@@ -133,9 +135,12 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
     B, H, N, d = q.shape
     dv = v.shape[3]
     w = _conv_check(conv_weight, conv_cache, q, H, d, dv, (B, H))
+    if conv_cache_out is not None:
+        _conv_check(conv_weight, conv_cache_out, q, H, d, dv, (B, H))
     if w:
         a.conv_weight, a.conv_width = _ptr(conv_weight), w
-        a.conv_in = a.conv_out = _ptr(conv_cache)
+        a.conv_in = _ptr(conv_cache)
+        a.conv_out = _ptr(conv_cache if conv_cache_out is None else conv_cache_out)
     if o is None:
         o = torch.empty((B, H, N, dv), dtype=q.dtype, device=q.device)
     if return_state and S_out is None:

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the five workloads.
+"""Seeded synthetic inputs for the benchmark and test workloads.
 
 This module only draws random tensors and rounds them to the storage dtype;
 it holds none of the method's arithmetic.  Both the HIP path and the fp64
@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 import torch
 
 # tensor ids inside one workload
-_Q, _K, _V, _G, _A = 1, 2, 3, 4, 5
+_Q, _K, _V, _G, _A, _W = 1, 2, 3, 4, 5, 6
 _DEC_Q, _DEC_K, _DEC_V = 11, 12, 13
 
 
@@ -41,6 +41,8 @@ class Workload:
                            # "alpha" (delta rule: per-token state decay in (0.9, 1))
                            # or "channel" (linear rule: per-key-channel decay in (0.9, 1))
     decode_steps: int = 0  # > 0: a decode loop follows the prefill
+    conv: int = 0          # > 0: short causal convolution of this width in
+                           # front of q, k, v (filters N(0, 1/w), zero cache)
     extra: dict = field(default_factory=dict)
 
 
@@ -63,6 +65,9 @@ WORKLOADS = {
     # the B4 H16 N4096 d64 prefill with GLA's per-key-channel decay
     7: Workload(7, "linear_gla_bf16_prefill_B4H16N4096d64", 4, 16, 4096, 64, 64,
                 torch.bfloat16, "linear", "elu1", 1.0 / math.sqrt(64), decay="channel"),
+    # the same prefill behind a width-4 short convolution of q, k, v
+    8: Workload(8, "linear_conv_bf16_prefill_B4H16N4096d64", 4, 16, 4096, 64, 64,
+                torch.bfloat16, "linear", "elu1", 1.0 / math.sqrt(64), conv=4),
 }
 
 
@@ -132,6 +137,11 @@ def make_prefill(w: Workload, device, *, B=None, H=None, N=None):
         out["v"] = normal((B, H, N, w.dv), w.wid, _V, device, w.scale, w.dtype)
         if w.decay == "channel":
             out["alpha"] = decay_gate((B, H, N, w.d), w.wid, _A, device, 0.9)
+        if w.conv:
+            out["conv_weight"] = normal((H, w.conv, 2 * w.d + w.dv), w.wid, _W, device,
+                                        w.conv ** -0.5)
+            out["conv_cache"] = torch.zeros((B, H, w.conv - 1, 2 * w.d + w.dv),
+                                            dtype=w.dtype, device=device)
     out["gamma"] = per_head_gamma(H, device) if w.decay == "per_head" else None
     return out
 
