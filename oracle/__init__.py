@@ -7,6 +7,7 @@ from .la_oracle import (  # noqa: F401
     delta_step,
     feature_map,
     linear_decode_step,
+    linear_backward,
     linear_decode_step_conv,
     linear_prefill,
     linear_prefill_conv,

@@ -199,6 +199,82 @@ def linear_quadratic(q, k, v, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1):
 
 
 # ---------------------------------------------------------------------------
+# Backward pass of the LINEAR rule (training)
+# ---------------------------------------------------------------------------
+
+def phi_elu1_grad(x):
+    """Derivative of elu(x)+1: 1 above zero, e^x at or below (1 at 0 from
+    both sides)."""
+    x = _f64(x)
+    return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def feature_map_grad(x, fmap):
+    if fmap == FMAP_ELU1:
+        return phi_elu1_grad(x)
+    if fmap == FMAP_IDENTITY:
+        return np.ones_like(_f64(x))
+    raise ValueError(f"unknown feature map {fmap!r}")
+
+
+def linear_backward(q, k, v, do, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1,
+                    S0=None, z0=None, dS_N=None, dz_N=None):
+    """Gradients of the LINEAR rule's prefill, token by token in reverse.
+
+    The pages motivate parallel training ([WILA] 8, [EAV] 8 and 10) but give
+    no gradient formulas; this is reverse-mode differentiation of the
+    recurrence of linear_step, written out.  With S_t, z_t the state after
+    token t, den_t = phi(q_t).z_t + eps and g_t = dL/do_t:
+        dnum_t = g_t / den_t,   dden_t = -(g_t . o_t) / den_t
+        dphi(q_t) = S_t dnum_t + z_t dden_t
+    and, with the adjoints Sh_t = dL/dS_t, zh_t = dL/dz_t (all later tokens
+    and the final-state gradient included),
+        Sh_t = phi(q_t) dnum_t^T + gamma Sh_(t+1),   zh_t = phi(q_t) dden_t + gamma zh_(t+1)
+        dphi(k_t) = Sh_t v_t + zh_t,   dv_t = Sh_t^T phi(k_t)
+        dS_in = gamma Sh_0 (the gradient of the initial state; tokens count
+        from 0), dz_in likewise,
+    then dq = dphi(q) * phi'(q), dk = dphi(k) * phi'(k).
+
+    q, k: [B, H, N, d]; v, do: [B, H, N, dv]; gamma [H] or None; S0, z0 the
+    initial state or None; dS_N [B, H, d, dv], dz_N [B, H, d] the gradient of
+    the loss with respect to the final state, or None.
+    Returns (dq, dk, dv, dS_0, dz_0) in float64.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, d = q.shape
+    dv_ = v.shape[-1]
+    fq, fk = feature_map(q, fmap), feature_map(k, fmap)
+    gam = np.broadcast_to(_gamma_heads(gamma, H)[None, :], (B, H))
+    S = np.zeros((B, H, d, dv_)) if S0 is None else _f64(S0).copy()
+    z = np.zeros((B, H, d)) if z0 is None else _f64(z0).copy()
+    Ss, zs = [], []
+    for t in range(N):  # forward pass, keeping every state
+        _, S, z = linear_step(S, z, fq[:, :, t], fk[:, :, t], v[:, :, t], gam, eps)
+        Ss.append(S)
+        zs.append(z)
+    Sh = np.zeros((B, H, d, dv_)) if dS_N is None else _f64(dS_N).copy()
+    zh = np.zeros((B, H, d)) if dz_N is None else _f64(dz_N).copy()
+    dfq = np.empty((B, H, N, d))
+    dfk = np.empty((B, H, N, d))
+    dvv = np.empty((B, H, N, dv_))
+    for t in range(N - 1, -1, -1):
+        St, zt, fqt = Ss[t], zs[t], fq[:, :, t]
+        num = np.einsum("...r,...rd->...d", fqt, St)
+        den = np.einsum("...r,...r->...", fqt, zt) + eps
+        g = do[:, :, t]
+        dnum = g / den[..., None]
+        dden = -np.einsum("...d,...d->...", g, num) / den ** 2
+        dfq[:, :, t] = np.einsum("...rd,...d->...r", St, dnum) + zt * dden[..., None]
+        Sh = Sh + fqt[..., :, None] * dnum[..., None, :]
+        zh = zh + fqt * dden[..., None]
+        dfk[:, :, t] = np.einsum("...rd,...d->...r", Sh, v[:, :, t]) + zh
+        dvv[:, :, t] = np.einsum("...rd,...r->...d", Sh, fk[:, :, t])
+        Sh = gam[..., None, None] * Sh
+        zh = gam[..., None] * zh
+    return (dfq * feature_map_grad(q, fmap), dfk * feature_map_grad(k, fmap), dvv, Sh, zh)
+
+
+# ---------------------------------------------------------------------------
 # Short causal convolution before the attention ([WILA] 5.4)
 # ---------------------------------------------------------------------------
 

@@ -653,4 +653,82 @@ def pin_conv_split_and_decode(orc):
     np.testing.assert_array_equal(C1, C)
 
 
+# --- backward of the LINEAR rule (derived; the pages give no formulas) ------
+
+def _torch_linear_loss(q, k, v, do, gamma, eps, S0, z0, dS, dz, elu):
+    """Loss sum(o * do) + sum(S_N * dS) + sum(z_N * dz) of the recurrence,
+    built from torch ops so that autograd differentiates it."""
+    import torch
+    phi = (lambda x: torch.nn.functional.elu(x) + 1.0) if elu else (lambda x: x)
+    fq, fk = phi(q), phi(k)
+    S, z = S0, z0
+    loss = 0.0
+    for t in range(q.shape[-2]):
+        S = gamma[:, None, None] * S + fk[:, t, :, None] * v[:, t, None, :]
+        z = gamma[:, None] * z + fk[:, t]
+        num = torch.einsum("hr,hrd->hd", fq[:, t], S)
+        den = (fq[:, t] * z).sum(-1) + eps
+        loss = loss + ((num / den[:, None]) * do[:, t]).sum()
+    return loss + (S * dS).sum() + (z * dz).sum()
+
+
+def pin_backward_matches_autograd(orc):
+    """dq, dk, dv and the initial-state gradients equal torch autograd's
+    through the recurrence, with decay, eps, an initial state, a final-state
+    gradient, d != dv, for both feature maps."""
+    import torch
+    rng = np.random.default_rng(51)
+    H, N, d, dv, eps = 2, 9, 3, 4, 1e-2
+    for elu in (True, False):
+        q = rng.normal(size=(H, N, d)) * (1.0 if elu else 0.0) + (0.0 if elu else 1.0)
+        k = rng.normal(size=(H, N, d)) * (1.0 if elu else 0.0) + (0.0 if elu else 1.0)
+        if not elu:  # non-negative features for the identity map
+            q, k = rng.uniform(0.1, 1.0, size=(H, N, d)), rng.uniform(0.1, 1.0, size=(H, N, d))
+        v = rng.normal(size=(H, N, dv))
+        do = rng.normal(size=(H, N, dv))
+        S0 = rng.normal(size=(H, d, dv)) * 0.3
+        z0 = rng.uniform(0.5, 1.0, size=(H, d))
+        dS = rng.normal(size=(H, d, dv))
+        dz = rng.normal(size=(H, d))
+        gamma = np.array([0.9, 0.7])
+        T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)  # noqa: E731
+        tq, tk, tv, tS0, tz0 = T(q), T(k), T(v), T(S0), T(z0)
+        loss = _torch_linear_loss(tq, tk, tv, torch.tensor(do), torch.tensor(gamma), eps, tS0,
+                                  tz0, torch.tensor(dS), torch.tensor(dz), elu)
+        loss.backward()
+        fmap = orc.FMAP_ELU1 if elu else orc.FMAP_IDENTITY
+        got = orc.linear_backward(q[None], k[None], v[None], do[None], gamma=gamma, eps=eps,
+                                  fmap=fmap, S0=S0[None], z0=z0[None], dS_N=dS[None],
+                                  dz_N=dz[None])
+        for g, t in zip(got, (tq, tk, tv, tS0, tz0)):
+            np.testing.assert_allclose(g[0], t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def pin_backward_finite_differences(orc):
+    """Central differences of the oracle's own forward (loss sum(o * do))
+    agree with the backward on every entry of q, k and v."""
+    rng = np.random.default_rng(52)
+    B, H, N, d, dv, eps, h = 1, 1, 5, 3, 2, 1e-3, 1e-6
+    q = rng.normal(size=(B, H, N, d))
+    k = rng.normal(size=(B, H, N, d))
+    v = rng.normal(size=(B, H, N, dv))
+    do = rng.normal(size=(B, H, N, dv))
+    gamma = [0.8]
+    dq, dk, dvv, _, _ = orc.linear_backward(q, k, v, do, gamma=gamma, eps=eps)
+
+    def loss(q_, k_, v_):
+        o, _, _ = orc.linear_prefill(q_, k_, v_, gamma=gamma, eps=eps)
+        return float(np.sum(o * do))
+    for x, g in ((q, dq), (k, dk), (v, dvv)):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if a is x else a for a in (q, k, v)]
+            args_m = [xm if a is x else a for a in (q, k, v)]
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

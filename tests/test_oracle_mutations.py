@@ -238,6 +238,32 @@ def _conv_qk_filters_swapped(m):
     m._conv_split = split
 
 
+def _patched(old, new):
+    """A mutant made by editing one line of the oracle's source text."""
+    def mutate(m):
+        src = open(ORACLE_SRC).read()
+        assert src.count(old) == 1, old
+        exec(compile(src.replace(old, new), ORACLE_SRC, "exec"), m.__dict__)
+    mutate.__name__ = "_patch"
+    return mutate
+
+
+_bwd_dden_dropped = _patched(
+    'dden = -np.einsum("...d,...d->...", g, num) / den ** 2', "dden = 0.0 * den")
+_bwd_dden_sign = _patched(
+    'dden = -np.einsum("...d,...d->...", g, num) / den ** 2',
+    'dden = np.einsum("...d,...d->...", g, num) / den ** 2')
+_bwd_phi_grad_one = _patched("        return phi_elu1_grad(x)\n",
+                             "        return np.ones_like(_f64(x))\n")
+_bwd_adjoint_not_decayed = _patched("Sh = gam[..., None, None] * Sh", "Sh = 1.0 * Sh")
+_bwd_dv_from_query = _patched('np.einsum("...rd,...r->...d", Sh, fk[:, :, t])',
+                              'np.einsum("...rd,...r->...d", Sh, fq[:, :, t])')
+_bwd_dk_without_z = _patched("v[:, :, t]) + zh", "v[:, :, t])")
+for _n in ("_bwd_dden_dropped", "_bwd_dden_sign", "_bwd_phi_grad_one",
+           "_bwd_adjoint_not_decayed", "_bwd_dv_from_query", "_bwd_dk_without_z"):
+    globals()[_n].__name__ = _n
+
+
 MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _exp_everywhere, _decay_off_by_one, _outer_transposed,
            _quadratic_strict_mask, _delta_not_transposed, _delta_wrong_sign,
@@ -245,7 +271,9 @@ MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _delta_dropped_correction, _gdn_error_on_undecayed_state,
            _gdn_decay_after_write, _gdn_decay_on_write_too, _gla_decay_on_value_axis,
            _gla_decay_after_write, _conv_taps_reversed, _conv_cache_newest_first,
-           _conv_cache_ignored, _conv_excludes_current_token, _conv_qk_filters_swapped]
+           _conv_cache_ignored, _conv_excludes_current_token, _conv_qk_filters_swapped,
+           _bwd_dden_dropped, _bwd_dden_sign, _bwd_phi_grad_one, _bwd_adjoint_not_decayed,
+           _bwd_dv_from_query, _bwd_dk_without_z]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
