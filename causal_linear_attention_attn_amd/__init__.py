@@ -12,6 +12,8 @@ a tensor is not on a GPU, the call raises.
     o = decode_step(q1, k1, v1, S, z)                         # in place on S, z
     o, S, z = prefill(q, k, v, conv_weight=W, conv_cache=C)   # short conv; C in place
     o = decode_step(q1, k1, v1, S, z, conv_weight=W, conv_cache=C)
+    o, S, z = prefill(q, k, v, den_out=den)                   # keep den for training
+    dq, dk, dv, dS0, dz0 = backward(q, k, v, o, den, do)      # gradients
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ import torch
 from . import _lib
 from ._lib import LinattnError, LibraryMissing  # noqa: F401
 
-__all__ = ["prefill", "decode_step", "state_init", "workspace_size",
+__all__ = ["prefill", "decode_step", "backward", "state_init", "workspace_size",
            "LinattnError", "LibraryMissing"]
 
 _RULES = {"linear": _lib.LA_RULE_LINEAR, "delta": _lib.LA_RULE_DELTA}
@@ -106,7 +108,7 @@ def workspace_size(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None,
 def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
             S_in=None, z_in=None, S_out=None, z_out=None, return_state=True,
             o=None, workspace=None, alpha=None, conv_weight=None, conv_cache=None,
-            conv_cache_out=None):
+            conv_cache_out=None, den_out=None):
     """Chunked prefill over [B,H,N,*] sequences (see la_prefill).
 
     rule "linear": fmap defaults to "elu1"; gamma [H] fp32 or None; eps >= 0;
@@ -117,6 +119,8 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
                    as the tokens before the sequence and overwritten in place
                    with the last w-1 tokens (None: zeros before, not kept),
                    or, with conv_cache_out, written there instead.
+                   den_out [B,H,N] fp32 receives each token's denominator
+                   (the input of backward()).
     rule "delta":  fmap "identity"; g [B,H,N] fp32 required; alpha [B,H,N]
                    fp32 state decay in (0, 1] or None.
     Returns (o, S_out, z_out); the states are None unless requested
@@ -125,8 +129,10 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
     if fmap is None:
         fmap = "elu1" if rule == "linear" else "identity"
     _need_gpu(q, k, v, gamma, g, alpha, S_in, z_in, S_out, z_out, o, workspace,
-              conv_weight, conv_cache, conv_cache_out)
-    _need_f32(gamma, g, alpha, S_in, z_in, S_out, z_out, conv_weight)
+              conv_weight, conv_cache, conv_cache_out, den_out)
+    _need_f32(gamma, g, alpha, S_in, z_in, S_out, z_out, conv_weight, den_out)
+    if den_out is not None and tuple(den_out.shape) != tuple(q.shape[:3]):
+        raise ValueError("den_out must be [B,H,N]")
     if alpha is not None:
         want = q.shape if rule == "linear" else q.shape[:3]
         if tuple(alpha.shape) != tuple(want):
@@ -151,6 +157,7 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
     a.S_in, a.z_in = _ptr(S_in), _ptr(z_in)
     a.S_out, a.z_out = _ptr(S_out), _ptr(z_out)
     a.q, a.k, a.v, a.o = _ptr(q), _ptr(k), _ptr(v), _ptr(o)
+    a.den_out = _ptr(den_out)
     need = lib.la_prefill_workspace_size(ctypes.byref(a))
     if need == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes")
@@ -161,6 +168,51 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
         a.workspace_bytes = workspace.numel() * workspace.element_size()
     _lib.check(lib.la_prefill(ctypes.byref(a), _stream()), "la_prefill")
     return o, S_out, z_out
+
+
+def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=None,
+             dS_out=None, dz_out=None, state_grad=True, workspace=None):
+    """Gradients of a LINEAR prefill (see la_backward): q, k [B,H,N,d], v, o,
+    do [B,H,N,dv] (dtype of q), den [B,H,N] fp32 from prefill(den_out=...);
+    gamma, S_in, z_in as in the forward; dS_out [B,H,d,dv], dz_out [B,H,d]
+    the gradient with respect to the final state, or None.
+    Returns (dq, dk, dv, dS_in, dz_in); the last two are None unless
+    state_grad."""
+    _need_gpu(q, k, v, o, den, do, gamma, S_in, z_in, dS_out, dz_out, workspace)
+    _need_f32(den, gamma, S_in, z_in, dS_out, dz_out)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,N,d] and v [B,H,N,dv]")
+    if o.shape != v.shape or do.shape != v.shape or tuple(den.shape) != tuple(q.shape[:3]):
+        raise ValueError("o, do must be [B,H,N,dv] and den [B,H,N]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == do.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v, o, do must share dtype float32 or bfloat16")
+    B, H, N, d = q.shape
+    dv = v.shape[3]
+    a = _lib.BackwardArgs()
+    a.B, a.H, a.N, a.d, a.dv = B, H, N, d, dv
+    a.dtype = _DTYPES[q.dtype]
+    a.fmap = _FMAPS[fmap]
+    dq, dk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dS_in = dz_in = None
+    if state_grad:
+        dS_in = torch.empty((B, H, d, dv), dtype=torch.float32, device=q.device)
+        dz_in = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    a.q, a.k, a.v, a.o, a.den, a.grad_o = (_ptr(t) for t in (q, k, v, o, den, do))
+    a.gamma, a.S_in, a.z_in = _ptr(gamma), _ptr(S_in), _ptr(z_in)
+    a.grad_S_out, a.grad_z_out = _ptr(dS_out), _ptr(dz_out)
+    a.grad_q, a.grad_k, a.grad_v = _ptr(dq), _ptr(dk), _ptr(dvv)
+    a.grad_S_in, a.grad_z_in = _ptr(dS_in), _ptr(dz_in)
+    lib = _lib.load()
+    need = lib.la_backward_workspace_size(ctypes.byref(a))
+    if need == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes")
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _lib.check(lib.la_backward(ctypes.byref(a), _stream()), "la_backward")
+    return dq, dk, dvv, dS_in, dz_in
 
 
 def decode_step(q, k, v, S, z=None, *, rule="linear", fmap=None, gamma=None,

@@ -11,10 +11,11 @@ LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP, LA_EWORKSPACE = 0, 1, 2, 3, 4
 LA_F32, LA_BF16 = 0, 1
 LA_FMAP_IDENTITY, LA_FMAP_ELU1 = 0, 1
 LA_RULE_LINEAR, LA_RULE_DELTA = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # Every symbol include/linattn.h declares.
 EXPORTS = ("la_prefill_workspace_size", "la_prefill", "la_decode_step",
+           "la_backward_workspace_size", "la_backward",
            "la_state_init", "la_status_str", "la_abi_version",
            "la_profile_enable", "la_profile_collect")
 
@@ -29,7 +30,20 @@ class PrefillArgs(ctypes.Structure):
         ("gamma", _ptr), ("g", _ptr), ("alpha", _ptr),
         ("conv_weight", _ptr), ("conv_width", _i32), ("conv_in", _ptr), ("conv_out", _ptr),
         ("eps", _f32), ("S_in", _ptr), ("z_in", _ptr), ("S_out", _ptr), ("z_out", _ptr),
-        ("o", _ptr), ("workspace", _ptr), ("workspace_bytes", _size),
+        ("o", _ptr), ("den_out", _ptr), ("workspace", _ptr), ("workspace_bytes", _size),
+    ]
+
+
+class BackwardArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", _i32), ("H", _i32), ("N", _i32), ("d", _i32), ("dv", _i32),
+        ("dtype", _i32), ("fmap", _i32),
+        ("q", _ptr), ("k", _ptr), ("v", _ptr), ("o", _ptr), ("den", _ptr), ("grad_o", _ptr),
+        ("gamma", _ptr), ("S_in", _ptr), ("z_in", _ptr),
+        ("grad_S_out", _ptr), ("grad_z_out", _ptr),
+        ("grad_q", _ptr), ("grad_k", _ptr), ("grad_v", _ptr),
+        ("grad_S_in", _ptr), ("grad_z_in", _ptr),
+        ("workspace", _ptr), ("workspace_bytes", _size),
     ]
 
 
@@ -72,6 +86,10 @@ def load(path: str | None = None):
         lib.la_prefill_workspace_size.restype = _size
         lib.la_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _ptr]
         lib.la_prefill.restype = ctypes.c_int
+        lib.la_backward_workspace_size.argtypes = [ctypes.POINTER(BackwardArgs)]
+        lib.la_backward_workspace_size.restype = _size
+        lib.la_backward.argtypes = [ctypes.POINTER(BackwardArgs), _ptr]
+        lib.la_backward.restype = ctypes.c_int
         lib.la_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _ptr]
         lib.la_decode_step.restype = ctypes.c_int
         lib.la_state_init.argtypes = [_ptr, _ptr, _i32, _i32, _i32, _i32, _ptr]

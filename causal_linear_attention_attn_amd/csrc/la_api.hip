@@ -146,7 +146,7 @@ bool overlap(const void *a, const void *b, size_t n) {
 
 extern "C" {
 
-int32_t la_abi_version(void) { return 3; }
+int32_t la_abi_version(void) { return 4; }
 
 const char *la_status_str(int s) {
   switch (s) {
@@ -182,7 +182,7 @@ int la_prefill(const la_prefill_args *a, void *stream) {
     if (a->alpha && (size_t)a->N * a->d * 4 > kMaxHeadBytes) return LA_EUNSUPPORTED;
   } else {
     if (!a->g && BH > 0 && a->N > 0) return LA_EINVAL;
-    if (a->gamma || a->z_in || a->z_out) return LA_EINVAL;
+    if (a->gamma || a->z_in || a->z_out || a->den_out) return LA_EINVAL;
   }
   if (BH > 0 && a->N > 0 && (!a->q || !a->k || !a->v || !a->o)) return LA_EINVAL;
   const bool bf16_io = a->dtype == LA_BF16;
@@ -243,6 +243,7 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   p.S_out = a->S_out;
   p.z_out = a->z_out;
   p.o = a->o;
+  p.den_out = a->den_out;
   p.ws = reinterpret_cast<float *>(a->workspace);
   if (!linear) return to_status(la::launch_delta_prefill(p, bf16_io, s));
   p.nseg = plan.nseg;
@@ -260,6 +261,118 @@ int la_prefill(const la_prefill_args *a, void *stream) {
     p.conv_src = copy ? cp : a->conv_in;
   }
   return to_status(la::launch_linear_prefill(p, plan, bf16_io, s));
+}
+
+namespace {
+
+int check_backward_shape(const la_backward_args *a) {
+  if (!a) return LA_EINVAL;
+  if (a->B < 0 || a->H < 0 || a->N < 0 || !dims_ok(a->d, a->dv)) return LA_EINVAL;
+  if (a->dtype != LA_F32 && a->dtype != LA_BF16) return LA_EINVAL;
+  if (a->fmap != LA_FMAP_IDENTITY && a->fmap != LA_FMAP_ELU1) return LA_EINVAL;
+  if ((long long)a->B * a->H > kMaxGridY) return LA_EUNSUPPORTED;
+  const size_t esz = a->dtype == LA_BF16 ? 2 : 4;
+  const size_t dmax = a->d > a->dv ? a->d : a->dv;
+  if ((size_t)a->N * dmax * esz > kMaxHeadBytes) return LA_EUNSUPPORTED;
+  if (!la::linear_backward_supported(a->d, a->dv, a->dtype == LA_BF16)) return LA_EUNSUPPORTED;
+  return LA_OK;
+}
+
+// Forward-state and adjoint slots: two copies of the forward's segment slots.
+size_t backward_ws_bytes(const la::LinearPlan &pl) { return 2 * pl.ws_bytes; }
+
+}  // namespace
+
+size_t la_backward_workspace_size(const la_backward_args *a) {
+  if (check_backward_shape(a) != LA_OK) return (size_t)-1;
+  const int BH = a->B * a->H;
+  if (BH == 0 || a->N == 0) return 0;
+  return backward_ws_bytes(la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16, 0));
+}
+
+int la_backward(const la_backward_args *a, void *stream) {
+  int st = check_backward_shape(a);
+  if (st != LA_OK) return st;
+  const int BH = a->B * a->H;
+  if (BH > 0 && a->N > 0 &&
+      (!a->q || !a->k || !a->v || !a->o || !a->den || !a->grad_o || !a->grad_q ||
+       !a->grad_k || !a->grad_v))
+    return LA_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (BH == 0) return LA_OK;
+  const size_t nS = (size_t)BH * a->d * a->dv, nz = (size_t)BH * a->d;
+  if (a->N == 0) {  // no tokens: the final state is the initial state
+    hipError_t e = hipSuccess;
+    if (a->grad_S_in)
+      e = a->grad_S_out ? la::launch_copy(a->grad_S_in, a->grad_S_out, nS, s)
+                        : la::launch_fill(a->grad_S_in, nS, 0.f, s);
+    if (e == hipSuccess && a->grad_z_in)
+      e = a->grad_z_out ? la::launch_copy(a->grad_z_in, a->grad_z_out, nz, s)
+                        : la::launch_fill(a->grad_z_in, nz, 0.f, s);
+    return to_status(e);
+  }
+  const bool bf16_io = a->dtype == LA_BF16;
+  const la::LinearPlan plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io, 0);
+  const size_t need = plan.nseg > 1 ? backward_ws_bytes(plan) : 0;
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return LA_EWORKSPACE;
+  const int vec = bf16_io ? 8 : 4;
+  const bool vec_ok = (a->d % vec == 0) && (a->dv % vec == 0) && aligned16(a->q) &&
+                      aligned16(a->k) && aligned16(a->v) && aligned16(a->o) &&
+                      aligned16(a->grad_o) && aligned16(a->grad_q) && aligned16(a->grad_k) &&
+                      aligned16(a->grad_v);
+  float *ws_f = reinterpret_cast<float *>(a->workspace);
+  float *ws_r = ws_f ? ws_f + plan.ws_bytes / sizeof(float) : nullptr;
+  if (plan.nseg > 1) {  // the forward state entering each segment
+    la::PrefillParams fp{};
+    fp.BH = BH;
+    fp.H = a->H;
+    fp.N = a->N;
+    fp.d = a->d;
+    fp.dv = a->dv;
+    fp.fmap = a->fmap == LA_FMAP_ELU1;
+    fp.vec_ok = vec_ok;
+    fp.q = a->q;
+    fp.k = a->k;
+    fp.v = a->v;
+    fp.gamma = a->gamma;
+    fp.S_in = a->S_in;
+    fp.z_in = a->z_in;
+    fp.ws = ws_f;
+    fp.nseg = plan.nseg;
+    fp.seg_len = plan.seg_len;
+    const hipError_t e = la::launch_linear_state_prefix(fp, plan, bf16_io, s);
+    if (e != hipSuccess) return LA_EHIP;
+  }
+  la::BwdParams p{};
+  p.BH = BH;
+  p.H = a->H;
+  p.N = a->N;
+  p.d = a->d;
+  p.dv = a->dv;
+  p.fmap = a->fmap == LA_FMAP_ELU1;
+  p.vec_ok = vec_ok;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.dout = a->grad_o;
+  p.den = a->den;
+  p.gamma = a->gamma;
+  p.S_in = a->S_in;
+  p.z_in = a->z_in;
+  p.dS_out = a->grad_S_out;
+  p.dz_out = a->grad_z_out;
+  p.dq = a->grad_q;
+  p.dk = a->grad_k;
+  p.dv_ = a->grad_v;
+  p.dS_in = a->grad_S_in;
+  p.dz_in = a->grad_z_in;
+  p.ws_f = ws_f;
+  p.ws_r = ws_r;
+  p.wrec = plan.nseg > 1 ? plan.ws_bytes / sizeof(float) / ((size_t)plan.nseg * BH) : 0;
+  p.nseg = plan.nseg;
+  p.seg_len = plan.seg_len;
+  return to_status(la::launch_linear_backward(p, bf16_io, s));
 }
 
 int la_decode_step(const la_decode_args *a, void *stream) {

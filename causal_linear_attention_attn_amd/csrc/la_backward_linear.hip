@@ -1,0 +1,670 @@
+// Backward of the LINEAR rule's chunked prefill (training): dq, dk, dv and
+// the gradient of the initial state, from the forward's inputs, its output
+// o, its per-token denominators and the gradient of the loss with respect
+// to o (and, optionally, to the final state).
+//
+// The pages motivate parallel training ("What Is Linear Attention?" 8,
+// "Efficient attention variants" 8 and 10) but give no gradient formulas;
+// these are derived from the recurrence.  The normaliser rides along as an
+// extra value column, as in the forward: with v'_t = [v_t | 1] and the
+// state S'_t = [S_t | z_t],
+//     num'_t = S'_t^T phi(q_t),  o_t = num_t / den_t,  den_t = phi(q_t).z_t + eps,
+// so dL/dnum'_t = dn_t = [g_t / den_t | -(g_t . o_t) / den_t] (g_t = dL/do_t),
+// and the rest is the gradient of unnormalised linear attention with values
+// v' and output gradients dn.  For a chunk of L tokens (local indices
+// t, j), entering state S'_in, decay D_tj = gamma^(t-j) for j <= t else 0,
+// A = phi(Q) phi(K)^T . D and dA = (dN V'^T) . D:
+//     dphi(q_t) = gamma^(t+1) S'_in dn_t + sum_j dA_tj phi(k_j)
+//     dphi(k_j) = sum_t dA_tj phi(q_t) + gamma^(L-1-j) Sh v'_j
+//     dv'_j     = sum_t A_tj dn_t      + gamma^(L-1-j) Sh^T phi(k_j)
+// where Sh is the adjoint of the state after the chunk (gradient from all
+// later tokens and the final-state gradient), carried backward as
+//     Sh <- gamma^L Sh + sum_t gamma^(t+1) phi(q_t) dn_t^T,
+// and the forward state is carried as in the forward pass.  Every decay
+// factor is at most 1.  dq = dphi(q) phi'(q), dk = dphi(k) phi'(k), with
+// phi'(x) = min(phi(x), 1) for elu+1.
+//
+// Kernels (per (segment, head); segments as in the forward):
+//   the forward's summary and scan kernels   forward state entering each segment
+//   bwd_dkv_kernel<SUMMARY>                  each segment's own adjoint, from zero
+//   bwd_rscan_kernel                         adjoint entering each segment from the right
+//   bwd_dq_kernel                            dq, chunks left to right, forward state
+//   bwd_dkv_kernel                           dk, dv, chunks right to left, adjoint state;
+//                                            segment 0 writes the initial-state gradient
+// Every product runs on the matrix cores from LDS tiles (bf16 operands,
+// fp32 accumulation; fp32 inputs use fp32 operands); the carried states
+// stay in fp32 accumulators.
+#include "la_common.hpp"
+#include "la_internal.hpp"
+
+namespace la {
+namespace {
+
+constexpr int kMaxSegB = 32;  // the forward's most segments per sequence
+
+template <typename T, int DK_, int DV_, int C_, int NW_>
+struct BCfg {
+  using type = T;
+  using vec = typename Vec16<T>::type;
+  static constexpr int DK = DK_, DV = DV_, C = C_, NW = NW_;
+  static constexpr int NT = NW * kWave;
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int PAD = sizeof(T) == 2 ? 16 : 4;
+  static constexpr int DVK = DV + 32;    // value side as a contraction: values,
+                                         // the normaliser column, zeros
+  static constexpr int NVP = DV / 16 + 1;  // value-side tiles incl. the normaliser tile
+  static constexpr int LDK = DK + PAD;     // row strides of the LDS tiles
+  static constexpr int LDV = DVK + PAD;
+  static constexpr int LDO = DV + PAD;
+  static constexpr int LDC = C + PAD;
+  static constexpr int NTB = C / 16;   // token blocks
+  static constexpr int NFB = DK / 16;  // feature blocks
+  static constexpr int NST = NFB * NVP;               // state tiles
+  static constexpr int SPW = (NST + NW - 1) / NW;     // state tiles per wave
+  static constexpr int QCB = DK / VEC, VCB = DV / VEC;  // 16-byte blocks per row
+  static constexpr int XCB = 32 / VEC;                 // blocks of the extra columns
+  static_assert(C % 32 == 0 && DK % 32 == 0 && DV % 16 == 0, "tile sizes");
+  // row loops run whole waves (the dn row reduction shuffles within a wave)
+  static_assert((C * QCB) % kWave == 0 && (C * VCB) % kWave == 0, "whole-wave row loops");
+  static_assert(VCB >= XCB && VCB <= kWave, "row groups within a wave");
+};
+
+template <class BC>
+struct alignas(16) SmemDq {
+  using T = typename BC::type;
+  T Fq[BC::C * BC::LDK];  // phi(q)
+  T Fk[BC::C * BC::LDK];  // phi(k)
+  T KW[BC::C * BC::LDK];  // gamma^(L-1-j) phi(k_j)
+  T Vp[BC::C * BC::LDV];  // [v | 1 | 0]
+  T dN[BC::C * BC::LDV];  // [g / den | -(g.o) / den | 0]
+  T dA[BC::C * BC::LDC];  // (dN V'^T) . D
+  T St[BC::DK * BC::LDV]; // the forward state [S | z | 0], rows = features
+  T Os[BC::C * BC::LDK];  // dq staging
+  float pw[BC::C + 4];    // gamma^m
+};
+
+template <class BC>
+struct alignas(16) SmemDkv {
+  using T = typename BC::type;
+  T Fq[BC::C * BC::LDK];
+  T QW[BC::C * BC::LDK];  // gamma^(t+1) phi(q_t)
+  T Fk[BC::C * BC::LDK];
+  T Vp[BC::C * BC::LDV];
+  T dN[BC::C * BC::LDV];
+  T Ad[BC::C * BC::LDC];  // A . D
+  T dA[BC::C * BC::LDC];  // dA . D
+  T Sh[BC::DK * BC::LDV]; // the adjoint [Sh | zh | 0], rows = features
+  T Ok[BC::C * BC::LDK];  // dk staging
+  T Ov[BC::C * BC::LDO];  // dv staging
+  float pw[BC::C + 4];
+};
+
+// ---- operands -------------------------------------------------------------
+// frag_rk: M[i][k] (k contiguous); frag_kr: M[k][i] (transposed read).  Lane
+// (li, lg) gets index i0 + li and k slots k0 + 8 lg .. + 7 either way.
+template <typename T>
+__device__ __forceinline__ void frag_rk(Frag<T> &f, const T *M, int ld, int i0, int k0, int li,
+                                        int lg) {
+  lds_frag(f, M + (i0 + li) * ld + k0 + 8 * lg);
+}
+template <typename T>
+__device__ __forceinline__ void frag_kr(Frag<T> &f, const T *M, int ld, int i0, int k0, int li,
+                                        int lg) {
+  lds_frag_tr(f, M, ld, k0 + 8 * lg, k0 + 8 * lg + 4, i0, li);
+}
+
+// One 16-byte block of row `tok` of a [N, ncols] tensor, zero outside.
+template <typename T, bool VK>
+__device__ __forceinline__ typename Vec16<T>::type load_vec(__amdgpu_buffer_rsrc_t r, int tok,
+                                                            int col0, int ncols, bool row_ok) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  if constexpr (VK) {
+    const bool ok = row_ok && col0 < ncols;
+    return buf_load16<T>(r, ok ? (uint32_t)(((size_t)tok * ncols + col0) * sizeof(T)) : kOOB);
+  } else {
+    typename Vec16<T>::type x;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const bool ok = row_ok && col0 + e < ncols;
+      x[e] = buf_load1(r, ok ? (uint32_t)(((size_t)tok * ncols + col0 + e) * sizeof(T)) : kOOB,
+                       (T *)nullptr);
+    }
+    return x;
+  }
+}
+
+template <typename T, bool VK>
+__device__ __forceinline__ void store_vec(__amdgpu_buffer_rsrc_t r, int tok, int col0, int ncols,
+                                          bool row_ok, typename Vec16<T>::type x) {
+  constexpr int VEC = 16 / (int)sizeof(T);
+  if constexpr (VK) {
+    const bool ok = row_ok && col0 < ncols;
+    buf_store16_nt<T>(r, ok ? (uint32_t)(((size_t)tok * ncols + col0) * sizeof(T)) : kOOB, x);
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const bool ok = row_ok && col0 + e < ncols;
+      buf_store1(r, ok ? (uint32_t)(((size_t)tok * ncols + col0 + e) * sizeof(T)) : kOOB, x[e]);
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void *base, int bh, int N,
+                                                            int ncols) {
+  const size_t n = (size_t)N * ncols;
+  return buf_rsrc(reinterpret_cast<const T *>(base) + (size_t)bh * n, (uint32_t)(n * sizeof(T)));
+}
+
+__device__ __forceinline__ float feat(float x, int fmap) {
+  return fmap ? phi_elu1(x) : x;
+}
+
+// ---- staging of one chunk ---------------------------------------------------
+// phi(q) rows (and, if QW, gamma^(t+1) phi(q_t)); rows past the chunk and
+// feature columns past d are zero.
+template <class BC, bool VK>
+__device__ __forceinline__ void stage_feat(typename BC::type *F, typename BC::type *W,
+                                           const float *wt, __amdgpu_buffer_rsrc_t r, int c0,
+                                           int Lc, int d, int fmap) {
+  using T = typename BC::type;
+  using V = typename BC::vec;
+  for (int i = threadIdx.x; i < BC::C * BC::QCB; i += BC::NT) {
+    const int row = i / BC::QCB, col0 = (i % BC::QCB) * BC::VEC;
+    const V x = load_vec<T, VK>(r, c0 + row, col0, d, row < Lc);
+    V f, w;
+    const float s = W ? wt[row] : 0.f;
+#pragma unroll
+    for (int e = 0; e < BC::VEC; ++e) {
+      const float y = (row < Lc && col0 + e < d) ? feat(to_f32(x[e]), fmap) : 0.f;
+      f[e] = from_f32<T>(y);
+      w[e] = from_f32<T>(y * s);
+    }
+    *reinterpret_cast<V *>(F + row * BC::LDK + col0) = f;
+    if (W) *reinterpret_cast<V *>(W + row * BC::LDK + col0) = w;
+  }
+}
+
+// [v | 1 | 0] rows (the ones column only for tokens of the chunk).
+template <class BC, bool VK>
+__device__ __forceinline__ void stage_values(typename BC::type *Vp, __amdgpu_buffer_rsrc_t r,
+                                             int c0, int Lc, int dv) {
+  using T = typename BC::type;
+  using V = typename BC::vec;
+  for (int i = threadIdx.x; i < BC::C * BC::VCB; i += BC::NT) {
+    const int row = i / BC::VCB, cb = i % BC::VCB, col0 = cb * BC::VEC;
+    *reinterpret_cast<V *>(Vp + row * BC::LDV + col0) =
+        load_vec<T, VK>(r, c0 + row, col0, dv, row < Lc);
+    if (cb < BC::XCB) {
+      V x;
+#pragma unroll
+      for (int e = 0; e < BC::VEC; ++e) x[e] = from_f32<T>(0.f);
+      if (cb == 0 && row < Lc) x[0] = from_f32<T>(1.f);
+      *reinterpret_cast<V *>(Vp + row * BC::LDV + BC::DV + col0) = x;
+    }
+  }
+}
+
+// [g / den | -(g . o) / den | 0] rows; zero past the chunk.  The threads of
+// one row are VCB consecutive lanes, so the row's dot product is a shuffle
+// reduction.
+template <class BC, bool VK>
+__device__ __forceinline__ void stage_dn(typename BC::type *dN, __amdgpu_buffer_rsrc_t ro,
+                                         __amdgpu_buffer_rsrc_t rg, const float *den, int c0,
+                                         int Lc, int dv) {
+  using T = typename BC::type;
+  using V = typename BC::vec;
+  for (int i = threadIdx.x; i < BC::C * BC::VCB; i += BC::NT) {
+    const int row = i / BC::VCB, cb = i % BC::VCB, col0 = cb * BC::VEC;
+    const bool ok = row < Lc;
+    const V o = load_vec<T, VK>(ro, c0 + row, col0, dv, ok);
+    const V g = load_vec<T, VK>(rg, c0 + row, col0, dv, ok);
+    const float rd = ok ? 1.f / den[c0 + row] : 0.f;
+    float dot = 0.f;
+    V x;
+#pragma unroll
+    for (int e = 0; e < BC::VEC; ++e) {
+      const float ge = to_f32(g[e]);
+      dot = fmaf(ge, to_f32(o[e]), dot);
+      x[e] = from_f32<T>(ge * rd);
+    }
+#pragma unroll
+    for (int m = 1; m < BC::VCB; m <<= 1) dot += __shfl_xor(dot, m);
+    *reinterpret_cast<V *>(dN + row * BC::LDV + col0) = x;
+    if (cb < BC::XCB) {
+      V y;
+#pragma unroll
+      for (int e = 0; e < BC::VEC; ++e) y[e] = from_f32<T>(0.f);
+      if (cb == 0) y[0] = from_f32<T>(-dot * rd);
+      *reinterpret_cast<V *>(dN + row * BC::LDV + BC::DV + col0) = y;
+    }
+  }
+}
+
+// ---- carried state: fp32 accumulator tiles st = wv + NW i ---------------------
+// tile st covers features 16 (st / NVP) .. and value columns 16 (st % NVP) ..;
+// the last value tile is the normaliser's ([z | 0 ... 0]).
+template <class BC>
+__device__ __forceinline__ void state_load(f32x4 (&Sa)[BC::SPW], const float *S, const float *z,
+                                           int d, int dv, int wv, int li, int lg) {
+#pragma unroll
+  for (int i = 0; i < BC::SPW; ++i) {
+    const int st = wv + BC::NW * i;
+    const int fb = st / BC::NVP, vb = st % BC::NVP;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int f = 16 * fb + 4 * lg + r;
+      float x = 0.f;
+      if (st < BC::NST && f < d) {
+        if (vb < BC::NVP - 1) {
+          const int c = 16 * vb + li;
+          if (S && c < dv) x = S[(size_t)f * dv + c];
+        } else if (li == 0 && z) {
+          x = z[f];
+        }
+      }
+      Sa[i][r] = x;
+    }
+  }
+}
+
+template <class BC>
+__device__ __forceinline__ void state_store(const f32x4 (&Sa)[BC::SPW], float *S, float *z, int d,
+                                            int dv, int wv, int li, int lg) {
+#pragma unroll
+  for (int i = 0; i < BC::SPW; ++i) {
+    const int st = wv + BC::NW * i;
+    const int fb = st / BC::NVP, vb = st % BC::NVP;
+    if (st >= BC::NST) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int f = 16 * fb + 4 * lg + r;
+      if (f >= d) continue;
+      if (vb < BC::NVP - 1) {
+        const int c = 16 * vb + li;
+        if (S && c < dv) S[(size_t)f * dv + c] = Sa[i][r];
+      } else if (li == 0 && z) {
+        z[f] = Sa[i][r];
+      }
+    }
+  }
+}
+
+// bf16 (or fp32) copy of the state into an LDS tile [DK][LDV], columns
+// 0 .. DV+15 (the zero columns past them are written once at the start).
+template <class BC>
+__device__ __forceinline__ void state_copy(typename BC::type *M, const f32x4 (&Sa)[BC::SPW],
+                                           int wv, int li, int lg) {
+  using T = typename BC::type;
+#pragma unroll
+  for (int i = 0; i < BC::SPW; ++i) {
+    const int st = wv + BC::NW * i;
+    if (st >= BC::NST) continue;
+    const int fb = st / BC::NVP, vb = st % BC::NVP;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      M[(16 * fb + 4 * lg + r) * BC::LDV + 16 * vb + li] = from_f32<T>(Sa[i][r]);
+  }
+}
+
+template <class BC>
+__device__ __forceinline__ void zero_tail_columns(typename BC::type *M) {
+  using T = typename BC::type;
+  for (int i = threadIdx.x; i < BC::DK * 16; i += BC::NT)
+    M[(i / 16) * BC::LDV + BC::DV + 16 + (i % 16)] = from_f32<T>(0.f);
+}
+
+// S += sum_t X[t][f] Y[t][c] over the chunk's tokens (both operands
+// token-major), after S *= scale.
+template <class BC>
+__device__ __forceinline__ void state_update(f32x4 (&Sa)[BC::SPW], const typename BC::type *X,
+                                             const typename BC::type *Y, float scale, int wv,
+                                             int li, int lg) {
+  using T = typename BC::type;
+#pragma unroll
+  for (int i = 0; i < BC::SPW; ++i) {
+    const int st = wv + BC::NW * i;
+    if (st >= BC::NST) continue;
+    const int fb = st / BC::NVP, vb = st % BC::NVP;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Sa[i][r] *= scale;
+#pragma unroll
+    for (int ks = 0; ks < BC::C / 32; ++ks) {
+      Frag<T> a, b;
+      frag_kr(a, X, BC::LDK, 16 * fb, 32 * ks, li, lg);
+      frag_kr(b, Y, BC::LDV, 16 * vb, 32 * ks, li, lg);
+      mma(Sa[i], a, b);
+    }
+  }
+}
+
+// Masked, decayed C x C product tiles: M[t][j] = D_tj sum_k X[t][k] Y[j][k]
+// (K = KS k-steps, both operands k-contiguous); tiles above the diagonal
+// are written as zeros.
+template <class BC, int KS, int LDX>
+__device__ __forceinline__ void tri_tiles(typename BC::type *M, const typename BC::type *X,
+                                          const typename BC::type *Y, const float *pw, int wv,
+                                          int li, int lg) {
+  using T = typename BC::type;
+  for (int ti = wv; ti < BC::NTB * BC::NTB; ti += BC::NW) {
+    const int tt = ti / BC::NTB, jt = ti % BC::NTB;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= tt) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        Frag<T> a, b;
+        frag_rk(a, X, LDX, 16 * tt, 32 * ks, li, lg);
+        frag_rk(b, Y, LDX, 16 * jt, 32 * ks, li, lg);
+        mma(acc, a, b);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tt + 4 * lg + r, j = 16 * jt + li;
+      M[t * BC::LDC + j] = from_f32<T>(j <= t ? acc[r] * pw[t - j] : 0.f);
+    }
+  }
+}
+
+// Rows of an LDS staging tile to global memory (rows past the chunk and
+// columns past ncols are dropped).
+template <class BC, bool VK>
+__device__ __forceinline__ void store_rows(__amdgpu_buffer_rsrc_t r, const typename BC::type *M,
+                                           int ld, int NCB, int c0, int Lc, int ncols) {
+  using V = typename BC::vec;
+  for (int i = threadIdx.x; i < BC::C * NCB; i += BC::NT) {
+    const int row = i / NCB, col0 = (i % NCB) * BC::VEC;
+    store_vec<typename BC::type, VK>(r, c0 + row, col0, ncols, row < Lc,
+                                     *reinterpret_cast<const V *>(M + row * ld + col0));
+  }
+}
+
+// ---- dq: chunks left to right, forward state --------------------------------
+template <class BC, bool VK>
+__global__ void __launch_bounds__(BC::NT) bwd_dq_kernel(BwdParams p) {
+  using T = typename BC::type;
+  __shared__ SmemDq<BC> sm;
+  const int seg = blockIdx.x, bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int d = p.d, dv = p.dv, N = p.N;
+  const int t_begin = seg * p.seg_len, t_end = min(N, t_begin + p.seg_len);
+  const __amdgpu_buffer_rsrc_t rq = head_rsrc<T>(p.q, bh, N, d), rk = head_rsrc<T>(p.k, bh, N, d),
+                               rv = head_rsrc<T>(p.v, bh, N, dv),
+                               ro = head_rsrc<T>(p.o, bh, N, dv),
+                               rg = head_rsrc<T>(p.dout, bh, N, dv),
+                               rdq = head_rsrc<T>(p.dq, bh, N, d);
+  const float *den = p.den + (size_t)bh * N;
+  const float lg2 = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
+  for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
+  zero_tail_columns<BC>(sm.St);
+
+  const float *S0, *z0;
+  if (p.nseg > 1) {
+    S0 = p.ws_f + ((size_t)seg * p.BH + bh) * p.wrec;
+    z0 = S0 + (size_t)d * dv;
+  } else {
+    S0 = p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr;
+    z0 = p.z_in ? p.z_in + (size_t)bh * d : nullptr;
+  }
+  f32x4 Sa[BC::SPW];
+  state_load<BC>(Sa, S0, z0, d, dv, wv, li, lg);
+  __syncthreads();
+
+  for (int c0 = t_begin; c0 < t_end; c0 += BC::C) {
+    const int Lc = min(BC::C, N - c0);
+    // key weights gamma^(L-1-j) (0 past the chunk) sit in Os until it is used
+    float *kw = reinterpret_cast<float *>(sm.Os);
+    for (int j = threadIdx.x; j < BC::C; j += BC::NT) kw[j] = j < Lc ? sm.pw[Lc - 1 - j] : 0.f;
+    __syncthreads();
+    stage_feat<BC, VK>(sm.Fq, nullptr, nullptr, rq, c0, Lc, d, p.fmap);
+    stage_feat<BC, VK>(sm.Fk, sm.KW, kw, rk, c0, Lc, d, p.fmap);
+    stage_values<BC, VK>(sm.Vp, rv, c0, Lc, dv);
+    stage_dn<BC, VK>(sm.dN, ro, rg, den, c0, Lc, dv);
+    state_copy<BC>(sm.St, Sa, wv, li, lg);
+    __syncthreads();
+
+    tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, wv, li, lg);
+    __syncthreads();
+
+    // dphi(q) = gamma^(t+1) dN S'_in^T + dA phi(K), then phi'(q)
+    for (int ti = wv; ti < BC::NTB * BC::NFB; ti += BC::NW) {
+      const int tt = ti / BC::NFB, fb = ti % BC::NFB;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < BC::DVK / 32; ++ks) {
+        Frag<T> a, b;
+        frag_rk(a, sm.dN, BC::LDV, 16 * tt, 32 * ks, li, lg);
+        frag_rk(b, sm.St, BC::LDV, 16 * fb, 32 * ks, li, lg);
+        mma(acc, a, b);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[16 * tt + 4 * lg + r + 1];
+      const int kend = (16 * tt + 16 + 31) / 32;
+      for (int ks = 0; ks < kend; ++ks) {
+        Frag<T> a, b;
+        frag_rk(a, sm.dA, BC::LDC, 16 * tt, 32 * ks, li, lg);
+        frag_kr(b, sm.Fk, BC::LDK, 16 * fb, 32 * ks, li, lg);
+        mma(acc, a, b);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tt + 4 * lg + r, f = 16 * fb + li;
+        const float dphi = p.fmap ? fminf(to_f32(sm.Fq[t * BC::LDK + f]), 1.f) : 1.f;
+        sm.Os[t * BC::LDK + f] = from_f32<T>(acc[r] * dphi);
+      }
+    }
+    // forward state across the chunk
+    state_update<BC>(Sa, sm.KW, sm.Vp, sm.pw[Lc], wv, li, lg);
+    __syncthreads();
+    store_rows<BC, VK>(rdq, sm.Os, BC::LDK, BC::QCB, c0, Lc, d);
+    __syncthreads();
+  }
+}
+
+// ---- dk, dv: chunks right to left, adjoint state ------------------------------
+// SUMMARY: only the adjoint, from zero at the segment's end, of segment
+// blockIdx.x + 1, into reverse slot blockIdx.x.
+template <class BC, bool VK, bool SUMMARY>
+__global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
+  using T = typename BC::type;
+  __shared__ SmemDkv<BC> sm;
+  const int seg = SUMMARY ? blockIdx.x + 1 : blockIdx.x, bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int d = p.d, dv = p.dv, N = p.N;
+  const int t_begin = seg * p.seg_len, t_end = min(N, t_begin + p.seg_len);
+  const __amdgpu_buffer_rsrc_t rq = head_rsrc<T>(p.q, bh, N, d), rk = head_rsrc<T>(p.k, bh, N, d),
+                               rv = head_rsrc<T>(p.v, bh, N, dv),
+                               ro = head_rsrc<T>(p.o, bh, N, dv),
+                               rg = head_rsrc<T>(p.dout, bh, N, dv),
+                               rdk = head_rsrc<T>(p.dk, bh, N, d),
+                               rdv = head_rsrc<T>(p.dv_, bh, N, dv);
+  const float *den = p.den + (size_t)bh * N;
+  const float lg2 = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
+  for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
+  zero_tail_columns<BC>(sm.Sh);
+
+  f32x4 Sa[BC::SPW];
+  {
+    const float *S1 = nullptr, *z1 = nullptr;
+    if (!SUMMARY) {
+      if (p.nseg > 1) {
+        S1 = p.ws_r + ((size_t)seg * p.BH + bh) * p.wrec;
+        z1 = S1 + (size_t)d * dv;
+      } else {
+        S1 = p.dS_out ? p.dS_out + (size_t)bh * d * dv : nullptr;
+        z1 = p.dz_out ? p.dz_out + (size_t)bh * d : nullptr;
+      }
+    }
+    state_load<BC>(Sa, S1, z1, d, dv, wv, li, lg);
+  }
+  __syncthreads();
+
+  const int last = t_begin + ((t_end - t_begin - 1) / BC::C) * BC::C;
+  for (int c0 = last; c0 >= t_begin; c0 -= BC::C) {
+    const int Lc = min(BC::C, N - c0);
+    stage_feat<BC, VK>(sm.Fq, sm.QW, sm.pw + 1, rq, c0, Lc, d, p.fmap);
+    stage_dn<BC, VK>(sm.dN, ro, rg, den, c0, Lc, dv);
+    if constexpr (!SUMMARY) {
+      stage_feat<BC, VK>(sm.Fk, nullptr, nullptr, rk, c0, Lc, d, p.fmap);
+      stage_values<BC, VK>(sm.Vp, rv, c0, Lc, dv);
+      state_copy<BC>(sm.Sh, Sa, wv, li, lg);
+    }
+    __syncthreads();
+
+    if constexpr (!SUMMARY) {
+      tri_tiles<BC, BC::DK / 32, BC::LDK>(sm.Ad, sm.Fq, sm.Fk, sm.pw, wv, li, lg);
+      tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, wv, li, lg);
+      __syncthreads();
+      // dphi(k) = gamma^(L-1-j) V' Sh^T + dA^T phi(Q), then phi'(k)
+      for (int ti = wv; ti < BC::NTB * BC::NFB; ti += BC::NW) {
+        const int jt = ti / BC::NFB, fb = ti % BC::NFB;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < BC::DVK / 32; ++ks) {
+          Frag<T> a, b;
+          frag_rk(a, sm.Vp, BC::LDV, 16 * jt, 32 * ks, li, lg);
+          frag_rk(b, sm.Sh, BC::LDV, 16 * fb, 32 * ks, li, lg);
+          mma(acc, a, b);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
+        for (int ks = (16 * jt) / 32; ks < BC::C / 32; ++ks) {
+          Frag<T> a, b;
+          frag_kr(a, sm.dA, BC::LDC, 16 * jt, 32 * ks, li, lg);
+          frag_kr(b, sm.Fq, BC::LDK, 16 * fb, 32 * ks, li, lg);
+          mma(acc, a, b);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * jt + 4 * lg + r, f = 16 * fb + li;
+          const float dphi = p.fmap ? fminf(to_f32(sm.Fk[j * BC::LDK + f]), 1.f) : 1.f;
+          sm.Ok[j * BC::LDK + f] = from_f32<T>(acc[r] * dphi);
+        }
+      }
+      // dv' = gamma^(L-1-j) phi(K) Sh + (A . D)^T dN  (value columns only)
+      for (int ti = wv; ti < BC::NTB * (BC::NVP - 1); ti += BC::NW) {
+        const int jt = ti / (BC::NVP - 1), vb = ti % (BC::NVP - 1);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < BC::DK / 32; ++ks) {
+          Frag<T> a, b;
+          frag_rk(a, sm.Fk, BC::LDK, 16 * jt, 32 * ks, li, lg);
+          frag_kr(b, sm.Sh, BC::LDV, 16 * vb, 32 * ks, li, lg);
+          mma(acc, a, b);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
+        for (int ks = (16 * jt) / 32; ks < BC::C / 32; ++ks) {
+          Frag<T> a, b;
+          frag_kr(a, sm.Ad, BC::LDC, 16 * jt, 32 * ks, li, lg);
+          frag_kr(b, sm.dN, BC::LDV, 16 * vb, 32 * ks, li, lg);
+          mma(acc, a, b);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sm.Ov[(16 * jt + 4 * lg + r) * BC::LDO + 16 * vb + li] = from_f32<T>(acc[r]);
+      }
+    }
+    // adjoint across the chunk: Sh <- gamma^L Sh + (gamma^(t+1) phi(Q))^T dN
+    state_update<BC>(Sa, sm.QW, sm.dN, sm.pw[Lc], wv, li, lg);
+    __syncthreads();
+    if constexpr (!SUMMARY) {
+      store_rows<BC, VK>(rdk, sm.Ok, BC::LDK, BC::QCB, c0, Lc, d);
+      store_rows<BC, VK>(rdv, sm.Ov, BC::LDO, BC::VCB, c0, Lc, dv);
+      __syncthreads();
+    }
+  }
+
+  if constexpr (SUMMARY) {
+    float *dst = p.ws_r + ((size_t)(seg - 1) * p.BH + bh) * p.wrec;
+    state_store<BC>(Sa, dst, dst + (size_t)d * dv, d, dv, wv, li, lg);
+  } else if (seg == 0) {
+    state_store<BC>(Sa, p.dS_in ? p.dS_in + (size_t)bh * d * dv : nullptr,
+                    p.dz_in ? p.dz_in + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
+  }
+}
+
+// Adjoint entering each segment from the right, in place: slot nseg-1 <-
+// (dS_out, dz_out); slot s <- gamma^len(s+1) slot (s+1) + dSh_(s+1) (which the
+// reverse summary left in slot s).  One thread per record element; every
+// record is loaded before the chain.
+__global__ void __launch_bounds__(256) bwd_rscan_kernel(BwdParams p) {
+  const int bh = blockIdx.y;
+  const size_t dd = (size_t)p.d * p.dv;
+  const size_t rec = dd + p.d;
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= rec) return;
+  const int nseg = p.nseg;
+  const float lg2 = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
+  const float gfull = exp2f((float)p.seg_len * lg2);
+  const float glast = exp2f((float)(p.N - (nseg - 1) * p.seg_len) * lg2);
+  float *base = p.ws_r + (size_t)bh * p.wrec + e;
+  const size_t stride = (size_t)p.BH * p.wrec;
+  float dS[kMaxSegB];
+#pragma unroll
+  for (int s = 0; s < kMaxSegB - 1; ++s) dS[s] = s < nseg - 1 ? base[s * stride] : 0.f;
+  float acc;
+  if (e < dd)
+    acc = p.dS_out ? p.dS_out[(size_t)bh * dd + e] : 0.f;
+  else
+    acc = p.dz_out ? p.dz_out[(size_t)bh * p.d + (e - dd)] : 0.f;
+  base[(size_t)(nseg - 1) * stride] = acc;
+#pragma unroll
+  for (int s = kMaxSegB - 2; s >= 0; --s) {
+    if (s < nseg - 1) {
+      acc = fmaf(s + 1 == nseg - 1 ? glast : gfull, acc, dS[s]);
+      base[s * stride] = acc;
+    }
+  }
+}
+
+template <class BC, bool VK>
+hipError_t run_bwd(const BwdParams &p, hipStream_t s) {
+  static_assert(sizeof(SmemDq<BC>) <= 160 * 1024 && sizeof(SmemDkv<BC>) <= 160 * 1024,
+                "LDS budget");
+  if (p.nseg > 1) {
+    hipError_t e = launch_kernel("linear_bwd_rsummary", bwd_dkv_kernel<BC, VK, true>,
+                                 dim3(p.nseg - 1, p.BH), dim3(BC::NT), s, p);
+    if (e != hipSuccess) return e;
+    const size_t rec = (size_t)p.d * p.dv + p.d;
+    e = launch_kernel("linear_bwd_rscan", bwd_rscan_kernel,
+                      dim3((unsigned)((rec + 255) / 256), p.BH), dim3(256), s, p);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch_kernel("linear_bwd_dq", bwd_dq_kernel<BC, VK>, dim3(p.nseg, p.BH),
+                               dim3(BC::NT), s, p);
+  if (e != hipSuccess) return e;
+  return launch_kernel("linear_bwd_dkv", bwd_dkv_kernel<BC, VK, false>, dim3(p.nseg, p.BH),
+                       dim3(BC::NT), s, p);
+}
+
+template <class BC>
+hipError_t run_bwd_vk(const BwdParams &p, hipStream_t s) {
+  return p.vec_ok ? run_bwd<BC, true>(p, s) : run_bwd<BC, false>(p, s);
+}
+
+// bf16: 64-token chunks at d = dv = 64, 32-token chunks (and eight waves)
+// with 128-wide tiles; fp32 up to 64-wide tiles, 32-token chunks.
+using BB64x64 = BCfg<bf16, 64, 64, 64, 4>;
+using BB64x128 = BCfg<bf16, 64, 128, 32, 8>;
+using BB128x64 = BCfg<bf16, 128, 64, 32, 8>;
+using BB128x128 = BCfg<bf16, 128, 128, 32, 8>;
+using BF64x64 = BCfg<float, 64, 64, 32, 4>;
+
+}  // namespace
+
+bool linear_backward_supported(int d, int dv, bool bf16_io) {
+  return bf16_io || (d <= 64 && dv <= 64);
+}
+
+hipError_t launch_linear_backward(const BwdParams &p, bool bf16_io, hipStream_t s) {
+  if (!bf16_io) return run_bwd_vk<BF64x64>(p, s);
+  if (p.d <= 64) return p.dv <= 64 ? run_bwd_vk<BB64x64>(p, s) : run_bwd_vk<BB64x128>(p, s);
+  return p.dv <= 64 ? run_bwd_vk<BB128x64>(p, s) : run_bwd_vk<BB128x128>(p, s);
+}
+
+}  // namespace la

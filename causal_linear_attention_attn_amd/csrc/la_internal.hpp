@@ -44,6 +44,24 @@ struct PrefillParams {
   const void *conv_src;  // where the chunk kernel reads the tokens before
                          // segment 0: conv_in, or the summary kernel's copy
   void *conv_copy;       // summary kernel: copy conv_in here (nullptr = no)
+  float *den_out;        // [BH, N] per-token denominators, or nullptr
+};
+
+// Backward of the LINEAR rule's prefill.
+struct BwdParams {
+  int BH, H, N, d, dv;
+  int fmap;
+  int vec_ok;
+  const void *q, *k, *v, *o, *dout;  // forward inputs and output, dL/do
+  const float *den;                  // [BH, N] forward denominators
+  const float *gamma;                // [H] or nullptr
+  const float *S_in, *z_in;          // forward initial state or nullptr
+  const float *dS_out, *dz_out;      // dL/d(final state) or nullptr
+  void *dq, *dk, *dv_;
+  float *dS_in, *dz_in;              // dL/d(initial state) or nullptr
+  float *ws_f, *ws_r;                // forward-state and adjoint slots
+  size_t wrec;                       // floats per slot record
+  int nseg, seg_len;
 };
 
 struct DecodeParams {
@@ -90,6 +108,12 @@ hipError_t launch_kernel(const char *name, F kernel, dim3 grid, dim3 block, hipS
 // conv_width > 0: a short convolution runs in front of q, k, v
 LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16, int conv_width);
 bool linear_combo_supported(int d, int dv, bool bf16, bool chan_decay, bool conv);
+// The forward's summary and scan kernels only: the state entering each
+// segment, in the workspace slots (nothing to do with one segment).
+hipError_t launch_linear_state_prefix(const PrefillParams &p, const LinearPlan &plan,
+                                      bool bf16, hipStream_t s);
+bool linear_backward_supported(int d, int dv, bool bf16);
+hipError_t launch_linear_backward(const BwdParams &p, bool bf16, hipStream_t s);
 hipError_t launch_linear_prefill(const PrefillParams &p, const LinearPlan &plan,
                                  bool bf16, hipStream_t s);
 // Gated delta rule: workspace (per-chunk Wt and R tiles) and the two-kernel

@@ -804,7 +804,7 @@ __device__ __forceinline__ void fill_powers(float *pw, float log2g) {
 // tile Os.
 template <class CF, int RB>
 __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillParams &p, int Lc,
-                                              int cg, int li, int lg) {
+                                              int cg, int li, int lg, float *den_row) {
   using T = typename CF::type;
   const int irow = 16 * RB + li;  // this lane's query row
   // ---- scores, transposed: at[tj][r] = phi(q_i) . kw_j, i = irow,
@@ -872,6 +872,9 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillPa
   {
     const float den = accd[0] + p.eps * sm.pw[max(Lc - 1 - irow, 0)];
     const float rd = __builtin_amdgcn_rcpf(den);
+    // the token's own denominator phi(q).z + eps (den carries gamma^(L-1-i))
+    if (den_row && cg == 0 && lg == 0 && irow < Lc)
+      den_row[irow] = accd[0] / sm.pw[Lc - 1 - irow] + p.eps;
 #pragma unroll
     for (int a = 0; a < CF::NPW; ++a)
       lds_store4(sm.Os + irow * CF::VLD + 16 * (cg * CF::NPW + a) + 4 * lg,
@@ -960,16 +963,17 @@ __global__ void __launch_bounds__(CF::NT, (CH || CV) ? wpe_at_most_2<CF>() : CF:
       prefetch<CF, true, VK>(R, p, hb, c0 + CF::C, min(CF::C, N - c0 - CF::C));
     __syncthreads();
 
+    float *dno = p.den_out ? p.den_out + (size_t)bh * N + c0 : nullptr;
     if constexpr (CF::NRB == 2) {
-      if (rb == 0) chunk_outputs<CF, 0>(sm, p, Lc, cg, li, lg);
-      else chunk_outputs<CF, 1>(sm, p, Lc, cg, li, lg);
+      if (rb == 0) chunk_outputs<CF, 0>(sm, p, Lc, cg, li, lg, dno);
+      else chunk_outputs<CF, 1>(sm, p, Lc, cg, li, lg, dno);
     } else {
       static_assert(CF::NRB == 4, "row blocks per chunk");
       switch (rb) {
-        case 0: chunk_outputs<CF, 0>(sm, p, Lc, cg, li, lg); break;
-        case 1: chunk_outputs<CF, 1>(sm, p, Lc, cg, li, lg); break;
-        case 2: chunk_outputs<CF, 2>(sm, p, Lc, cg, li, lg); break;
-        default: chunk_outputs<CF, 3>(sm, p, Lc, cg, li, lg); break;
+        case 0: chunk_outputs<CF, 0>(sm, p, Lc, cg, li, lg, dno); break;
+        case 1: chunk_outputs<CF, 1>(sm, p, Lc, cg, li, lg, dno); break;
+        case 2: chunk_outputs<CF, 2>(sm, p, Lc, cg, li, lg, dno); break;
+        default: chunk_outputs<CF, 3>(sm, p, Lc, cg, li, lg, dno); break;
       }
     }
 
@@ -1171,6 +1175,20 @@ hipError_t run(const PrefillParams &p, hipStream_t s) {
   return p.vec_ok ? run_vk<CF, true>(p, s) : run_vk<CF, false>(p, s);
 }
 
+// summary + scan only (the segment-entering states), no decay variants
+template <class CF>
+hipError_t run_prefix(const PrefillParams &p, hipStream_t s) {
+  if (p.nseg <= 1) return hipSuccess;
+  hipError_t e = p.vec_ok ? launch_kernel("linear_summary", summary_kernel<CF, true, false, false>,
+                                          dim3(p.nseg - 1, p.BH), dim3(CF::NT), s, p)
+                          : launch_kernel("linear_summary", summary_kernel<CF, false, false, false>,
+                                          dim3(p.nseg - 1, p.BH), dim3(CF::NT), s, p);
+  if (e != hipSuccess) return e;
+  const size_t rec = (size_t)p.d * p.dv + p.d;
+  return launch_kernel("linear_scan", scan_kernel<false>,
+                       dim3((unsigned)((rec + 255) / 256), p.BH), dim3(256), s, p);
+}
+
 // Workgroups of chunk_kernel<CF> that fit on one CU (queried once).
 template <class CF, bool CV>
 int resident_per_cu() {
@@ -1246,6 +1264,16 @@ LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io, int conv_widt
 bool linear_combo_supported(int d, int dv, bool bf16_io, bool chan, bool conv) {
   if (bf16_io || !chan || !conv || d <= 64 || dv <= 64) return true;
   return chunk_lds<F128x128, true, true>() <= kLdsBytes;
+}
+
+hipError_t launch_linear_state_prefix(const PrefillParams &p, const LinearPlan &pl,
+                                      bool bf16_io, hipStream_t s) {
+  if (bf16_io) {
+    if (pl.dk == 64) return pl.dv_pad == 64 ? run_prefix<B64x64>(p, s) : run_prefix<B64x128>(p, s);
+    return pl.dv_pad == 64 ? run_prefix<B128x64>(p, s) : run_prefix<B128x128>(p, s);
+  }
+  if (pl.dk == 64) return pl.dv_pad == 64 ? run_prefix<F64x64>(p, s) : run_prefix<F64x128>(p, s);
+  return pl.dv_pad == 64 ? run_prefix<F128x64>(p, s) : run_prefix<F128x128>(p, s);
 }
 
 hipError_t launch_linear_prefill(const PrefillParams &p, const LinearPlan &pl,

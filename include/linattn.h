@@ -133,6 +133,9 @@ typedef struct la_prefill_args {
   float *z_out;      /* LINEAR: [B,H,d]; NULL = not written; may alias z_in.
                         DELTA: must be NULL. */
   void *o;           /* [B,H,N,dv] output, dtype as q (required if N > 0) */
+  float *den_out;    /* LINEAR: [B,H,N] each token's denominator
+                        phi(q_t).z_t + eps (what la_backward needs), or NULL
+                        (not written).  DELTA: must be NULL. */
   void *workspace;   /* device scratch of workspace_bytes, caller-owned;
                         may be NULL when la_prefill_workspace_size() is 0 */
   size_t workspace_bytes;
@@ -148,6 +151,52 @@ size_t la_prefill_workspace_size(const la_prefill_args *args);
  * given, the final state.  Equivalent (up to fp rounding order) to running
  * the per-token recurrence of `rule` from (S_in, z_in). */
 int la_prefill(const la_prefill_args *args, void *stream);
+
+/* Backward of a LINEAR-rule prefill (training).  The pages motivate
+ * parallel training ([WILA] section 8; [EAV] sections 8 and 10) but give no
+ * gradient formulas; these are the reverse-mode derivatives of the
+ * recurrence above:
+ *   dn_t = [g_t / den_t | -(g_t . o_t) / den_t]   (g_t = dL/do_t)
+ *   adjoint state (backward in time), with the final-state gradient:
+ *     Sh_t = phi(q_t) dn_t^T + gamma Sh_(t+1)   ([S | z] stacked, as dn)
+ *   dphi(q_t) = [S_t | z_t] dn_t,  dphi(k_t) = Sh_t [v_t | 1],
+ *   dv_t = (Sh_t^T phi(k_t)) without its last entry,
+ *   dq = dphi(q) phi'(q), dk = dphi(k) phi'(k); dL/d(initial state) = gamma Sh_0.
+ * Inputs are the forward's q, k, v, gamma, initial state, its output o and
+ * its denominators den (la_prefill's den_out); no per-key-channel decay
+ * (alpha) or convolution.  fp32 inputs take d, dv <= 64 (LA_EUNSUPPORTED
+ * above); bf16 any d, dv up to 128. */
+typedef struct la_backward_args {
+  int32_t B, H, N;   /* as the forward */
+  int32_t d, dv;
+  int32_t dtype;     /* la_dtype of q, k, v, o, grad_o and the gradients */
+  int32_t fmap;      /* la_fmap of the forward */
+  const void *q;     /* [B,H,N,d]  forward inputs */
+  const void *k;     /* [B,H,N,d]  */
+  const void *v;     /* [B,H,N,dv] */
+  const void *o;     /* [B,H,N,dv] forward output */
+  const float *den;  /* [B,H,N] forward denominators */
+  const void *grad_o;/* [B,H,N,dv] dL/do */
+  const float *gamma;/* [H] or NULL, as in the forward */
+  const float *S_in; /* [B,H,d,dv] forward initial state; NULL = zeros */
+  const float *z_in; /* [B,H,d]; NULL = zeros */
+  const float *grad_S_out; /* [B,H,d,dv] dL/d(final state); NULL = zero */
+  const float *grad_z_out; /* [B,H,d]; NULL = zero */
+  void *grad_q;      /* [B,H,N,d]  outputs, dtype as q (required if N > 0) */
+  void *grad_k;      /* [B,H,N,d]  */
+  void *grad_v;      /* [B,H,N,dv] */
+  float *grad_S_in;  /* [B,H,d,dv] dL/d(initial state); NULL = not written */
+  float *grad_z_in;  /* [B,H,d]; NULL = not written */
+  void *workspace;   /* device scratch of workspace_bytes, caller-owned */
+  size_t workspace_bytes;
+} la_backward_args;
+
+/* Workspace bytes la_backward needs (0 when none); (size_t)-1 for invalid
+ * sizes.  Reads only the sizes and dtype. */
+size_t la_backward_workspace_size(const la_backward_args *args);
+
+/* dq, dk, dv (and the initial-state gradient) of one LINEAR prefill. */
+int la_backward(const la_backward_args *args, void *stream);
 
 /* One token per sequence against a persistent state updated in place. */
 typedef struct la_decode_args {

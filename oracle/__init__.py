@@ -9,6 +9,7 @@ from .la_oracle import (  # noqa: F401
     linear_decode_step,
     linear_backward,
     linear_decode_step_conv,
+    linear_denominators,
     linear_prefill,
     linear_prefill_conv,
     linear_quadratic,

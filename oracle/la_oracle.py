@@ -217,6 +217,22 @@ def feature_map_grad(x, fmap):
     raise ValueError(f"unknown feature map {fmap!r}")
 
 
+def linear_denominators(q, k, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1, z0=None):
+    """den_t = phi(q_t) . z_t + eps of every token (what the output of the
+    LINEAR rule divides by), with z_t = gamma z_(t-1) + phi(k_t).
+    q, k: [B, H, N, d].  Returns [B, H, N] in float64."""
+    q, k = _f64(q), _f64(k)
+    B, H, N, d = q.shape
+    fq, fk = feature_map(q, fmap), feature_map(k, fmap)
+    gam = np.broadcast_to(_gamma_heads(gamma, H)[None, :], (B, H))
+    z = np.zeros((B, H, d)) if z0 is None else _f64(z0).copy()
+    den = np.empty((B, H, N))
+    for t in range(N):
+        z = gam[..., None] * z + fk[:, :, t]
+        den[:, :, t] = np.einsum("...r,...r->...", fq[:, :, t], z) + eps
+    return den
+
+
 def linear_backward(q, k, v, do, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1,
                     S0=None, z0=None, dS_N=None, dz_N=None):
     """Gradients of the LINEAR rule's prefill, token by token in reverse.

@@ -731,4 +731,28 @@ def pin_backward_finite_differences(orc):
         np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
 
 
+def pin_denominators_brute_force(orc):
+    """den_t = sum_{j<=t} gamma^(t-j) phi(q_t).phi(k_j) + gamma^(t+1) phi(q_t).z0
+    + eps, by explicit double loop; and den_t o_t equals the numerator of
+    the quadratic form."""
+    rng = np.random.default_rng(53)
+    N, d, dv, eps, g = 7, 3, 2, 1e-2, 0.85
+    q = rng.normal(size=(N, d))
+    k = rng.normal(size=(N, d))
+    v = rng.normal(size=(N, dv))
+    z0 = rng.uniform(0.1, 1.0, size=d)
+    fq, fk = orc.phi_elu1(q), orc.phi_elu1(k)
+    den = orc.linear_denominators(_bh(q), _bh(k), gamma=[g], eps=eps, z0=_bh(z0))[0, 0]
+    for t in range(N):
+        want = eps + g ** (t + 1) * fq[t] @ z0
+        for j in range(t + 1):
+            want += g ** (t - j) * fq[t] @ fk[j]
+        assert abs(den[t] - want) < 1e-12 * want
+    o, _, _ = orc.linear_prefill(_bh(q), _bh(k), _bh(v), gamma=[g], eps=eps)
+    den0 = orc.linear_denominators(_bh(q), _bh(k), gamma=[g], eps=eps)[0, 0]
+    for t in range(N):
+        num = sum(g ** (t - j) * (fq[t] @ fk[j]) * v[j] for j in range(t + 1))
+        np.testing.assert_allclose(o[0, 0, t] * den0[t], num, rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

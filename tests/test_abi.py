@@ -42,6 +42,7 @@ def test_struct_layout_matches_header(tmp_path):
     src = tmp_path / "layout.c"
     fields_p = [f for f, _ in _lib.PrefillArgs._fields_]
     fields_d = [f for f, _ in _lib.DecodeArgs._fields_]
+    fields_b = [f for f, _ in _lib.BackwardArgs._fields_]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "linattn.h"',
              "int main(void){"]
     lines.append('printf("%zu\\n", sizeof(la_prefill_args));')
@@ -50,6 +51,9 @@ def test_struct_layout_matches_header(tmp_path):
     lines.append('printf("%zu\\n", sizeof(la_decode_args));')
     for f in fields_d:
         lines.append(f'printf("%zu\\n", offsetof(la_decode_args, {f}));')
+    lines.append('printf("%zu\\n", sizeof(la_backward_args));')
+    for f in fields_b:
+        lines.append(f'printf("%zu\\n", offsetof(la_backward_args, {f}));')
     lines.append("return 0;}")
     src.write_text("\n".join(lines))
     exe = tmp_path / "layout"
@@ -61,6 +65,8 @@ def test_struct_layout_matches_header(tmp_path):
     want += [getattr(_lib.PrefillArgs, f).offset for f in fields_p]
     want += [ctypes.sizeof(_lib.DecodeArgs)]
     want += [getattr(_lib.DecodeArgs, f).offset for f in fields_d]
+    want += [ctypes.sizeof(_lib.BackwardArgs)]
+    want += [getattr(_lib.BackwardArgs, f).offset for f in fields_b]
     assert got == want
 
 
@@ -165,6 +171,42 @@ def test_decode_conv_on_delta_is_unsupported(lib):
     a.q = a.k = a.v = a.o = a.S = a.g = fake
     a.conv_weight, a.conv_width, a.conv_cache = fake, 4, fake
     assert lib.la_decode_step(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+
+
+def _bargs(**kw):
+    a = _lib.BackwardArgs()
+    a.B, a.H, a.N, a.d, a.dv = 1, 2, 4, 8, 8
+    a.dtype, a.fmap = _lib.LA_BF16, _lib.LA_FMAP_ELU1
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    a.q = a.k = a.v = a.o = a.den = a.grad_o = a.grad_q = a.grad_k = a.grad_v = fake
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("bad", [
+    dict(B=-1), dict(N=-1), dict(d=0), dict(dv=129), dict(dtype=5), dict(fmap=7),
+    dict(q=None), dict(den=None), dict(grad_o=None), dict(grad_v=None),
+])
+def test_backward_rejects_invalid_arguments(lib, bad):
+    a = _bargs(**bad)
+    assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EINVAL
+
+
+def test_backward_unsupported_and_sizes(lib):
+    assert lib.la_backward(None, None) == _lib.LA_EINVAL
+    a = _bargs(dtype=_lib.LA_F32, d=128)  # fp32 backward takes d, dv <= 64
+    assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+    assert lib.la_backward_workspace_size(ctypes.byref(a)) == ctypes.c_size_t(-1).value
+    a = _bargs(B=0)
+    assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_OK
+    assert lib.la_backward_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_prefill_den_out_only_for_linear(lib):
+    a = _args(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY, g=ctypes.c_void_p(0x2000),
+              den_out=ctypes.c_void_p(0x3000))
+    assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EINVAL
 
 
 def test_state_init_rejects_invalid_arguments(lib):
