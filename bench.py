@@ -2,7 +2,7 @@
 """Benchmark of the causal linear attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2..8]
-                    [--no-decode] [--no-extra] [--no-cpu-baseline]
+                    [--no-decode] [--no-extra] [--no-train] [--no-cpu-baseline]
 
 Prints ONE JSON line.  A "step" is one la_prefill call over the whole batch
 of the workload (default: B=4 H=16 N=4096 d=dv=64 bf16 q, k, v, elu+1,
@@ -29,6 +29,12 @@ per step.  Alongside:
                 workload behind a width-4 short convolution of q, k, v (conv
                 cache in and out), each with its kernels' times and HBM
                 fraction;
+  train         a training step of the main workload: the prefill keeping
+                each token's denominator, then la_backward (dq, dk, dv) for a
+                seeded dL/do; tokens/s of the forward+backward step, the
+                backward kernels' times, and the dominant backward kernel
+                against HBM peak (its algorithmic bytes: q, k, v, o, dL/do
+                and the denominators read once, its gradients written once);
   cpu_baseline  the fp64 oracle on the host (one thread) over the same
                 inputs of the main workload (a reported baseline, not a
                 target), with its parity error against the GPU output.
@@ -62,6 +68,7 @@ def parse():
                     help="3 runs the decode-step loop alone")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -105,7 +112,9 @@ KERNEL_SRC = {
     "linear_chunk": "la_prefill_linear.hip", "linear_summary": "la_prefill_linear.hip",
     "linear_scan": "la_prefill_linear.hip", "delta_prep": "la_prefill_delta.hip",
     "delta_seq": "la_prefill_delta.hip", "linear_decode": "la_decode.hip",
-    "delta_decode": "la_decode.hip",
+    "delta_decode": "la_decode.hip", "linear_bwd_dq": "la_backward_linear.hip",
+    "linear_bwd_dkv": "la_backward_linear.hip", "linear_bwd_rsummary": "la_backward_linear.hip",
+    "linear_bwd_rscan": "la_backward_linear.hip",
 }
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_MIB = 256
@@ -126,6 +135,13 @@ def library_kernel_name(raw):
     (mangled or demangled), or None for kernels that are not ours."""
     if "la" not in raw:
         return None
+    if "bwd_rscan_kernel" in raw:
+        return "linear_bwd_rscan"
+    if "bwd_dq_kernel" in raw:
+        return "linear_bwd_dq"
+    if "bwd_dkv_kernel" in raw:  # the last template flag marks the reverse summary
+        summary = "Lb1EEEvNS_9Bwd" in raw or raw.rstrip().endswith("true>(la::BwdParams)")
+        return "linear_bwd_rsummary" if summary else "linear_bwd_dkv"
     for fn, name in (("chunk_kernel", "linear_chunk"), ("summary_kernel", "linear_summary"),
                      ("scan_kernel", "linear_scan"), ("prep_kernel", "delta_prep"),
                      ("seq_kernel", "delta_seq")):
@@ -433,6 +449,61 @@ def bench_workload(la, lib, torch, w, steps, warmup):
     return out, x, o
 
 
+def bwd_bytes_per_head_token(w, kname):
+    """Algorithmic bytes of one backward kernel per head-token: q, k, v, o,
+    dL/do and den read once; its gradients written once."""
+    e = w.dtype.itemsize
+    rd = (2 * w.d + 3 * w.dv) * e + 4
+    return rd + (w.d * e if kname == "linear_bwd_dq" else (w.d + w.dv) * e)
+
+
+def bench_train(la, lib, torch, w, steps, warmup):
+    """Training step of the main workload: prefill keeping the per-token
+    denominators, then the backward (dq, dk, dv) for a seeded dL/do."""
+    from causal_linear_attention_attn_amd import inputs
+
+    x = inputs.make_prefill(w, "cuda")
+    do = inputs.make_grad_out(w, "cuda")
+    q, k, v, gamma = x["q"], x["k"], x["v"], x["gamma"]
+    B, H, N, d, dv = w.B, w.H, w.N, w.d, w.dv
+    o = torch.empty((B, H, N, dv), dtype=w.dtype, device="cuda")
+    den = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    wsf = torch.empty(max(la.workspace_size(q, k, v, gamma=gamma, eps=w.eps), 1),
+                      dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        la.prefill(q, k, v, gamma=gamma, eps=w.eps, o=o, den_out=den, workspace=wsf,
+                   return_state=False)
+
+    def bwd():
+        return la.backward(q, k, v, o, den, do, gamma=gamma, state_grad=False)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(max(1, warmup // 4)):
+        step()
+    torch.cuda.synchronize()
+    kern = time_kernels(lib, torch, bwd, max(3, steps // 4))
+    dt = time_graph(torch, step, steps, warmup)
+    head_tokens = B * H * N
+    bk = {n: t for n, t in kern.items() if n.startswith("linear_bwd")}
+    kname, kms = dominant(bk)
+    bpl = head_tokens * bwd_bytes_per_head_token(w, kname)
+    achieved = bpl / (kms * 1e-3) / 1e9
+    traffic, tsrc = traffic_record(w.name + "_backward", kname)
+    return {
+        "workload": w.name + "_forward_backward", "tokens_per_s": B * N / dt,
+        "ms_per_step": dt * 1e3, "backward_kernels_ms": kern,
+        "backward_ms": sum(kern.values()),
+        "roofline": {"kernel": kname, "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "traffic_profile": tsrc, "bytes_per_launch": bpl,
+                     "kernel_ms": kms},
+    }
+
+
 def decode_step_bytes(w):
     """Algorithmic bytes of one decode step: state S and z read and written
     once; q, k, v read and o written once."""
@@ -580,6 +651,9 @@ def main():
     del x, o
     if not args.no_decode:
         line["decode"] = bench_decode(la, lib, torch, args.decode_steps)
+    if not args.no_train and w.rule == "linear" and w.decay in ("none", "per_head") \
+            and not w.conv:
+        line["train"] = bench_train(la, lib, torch, w, max(10, args.steps // 4), 5)
     if not args.no_extra:
         extra = {}
         for wid in (4, 5, 6, 7, 8):

@@ -20,6 +20,7 @@ import torch
 # tensor ids inside one workload
 _Q, _K, _V, _G, _A, _W = 1, 2, 3, 4, 5, 6
 _DEC_Q, _DEC_K, _DEC_V = 11, 12, 13
+_DO = 21  # gradient of the loss with respect to o (training step)
 
 
 @dataclass(frozen=True)
@@ -144,6 +145,11 @@ def make_prefill(w: Workload, device, *, B=None, H=None, N=None):
                                             dtype=w.dtype, device=device)
     out["gamma"] = per_head_gamma(H, device) if w.decay == "per_head" else None
     return out
+
+
+def make_grad_out(w: Workload, device):
+    """dL/do for a training step: N(0,1) draws of o's shape, in w.dtype."""
+    return normal((w.B, w.H, w.N, w.dv), w.wid, _DO, device, 1.0, w.dtype)
 
 
 def make_decode(w: Workload, device, *, B=None, H=None, steps=None):
