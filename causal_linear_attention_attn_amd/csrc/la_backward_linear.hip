@@ -26,7 +26,7 @@
 //
 // Kernels (per (segment, head); segments as in the forward):
 //   the forward's summary and scan kernels   forward state entering each segment
-//   bwd_dkv_kernel<SUMMARY>                  each segment's own adjoint, from zero
+//   bwd_rsum_kernel                          each segment's own adjoint, from zero
 //   bwd_rscan_kernel                         adjoint entering each segment from the right
 //   bwd_dq_kernel                            dq, chunks left to right, forward state
 //   bwd_dkv_kernel                           dk, dv, chunks right to left, adjoint state;
@@ -41,6 +41,10 @@ namespace la {
 namespace {
 
 constexpr int kMaxSegB = 32;  // the forward's most segments per sequence
+// Gradient rows leave through an LDS staging tile as whole 16-byte row
+// blocks (written out after the chunk's last barrier, so no barrier of their
+// own), not as 2-byte stores straight from the accumulators.
+constexpr bool kStageOut = true;
 
 template <typename T, int DK_, int DV_, int C_, int NW_>
 struct BCfg {
@@ -79,8 +83,9 @@ struct alignas(16) SmemDq {
   T dN[BC::C * BC::LDV];  // [g / den | -(g.o) / den | 0]
   T dA[BC::C * BC::LDC];  // (dN V'^T) . D
   T St[BC::DK * BC::LDV]; // the forward state [S | z | 0], rows = features
-  T Os[BC::C * BC::LDK];  // dq staging
   float pw[BC::C + 4];    // gamma^m
+  float kw[BC::C];        // gamma^(L-1-j), 0 past the chunk
+  T Os[kStageOut ? BC::C * BC::LDK : 1];  // dq staging
 };
 
 template <class BC>
@@ -94,8 +99,17 @@ struct alignas(16) SmemDkv {
   T Ad[BC::C * BC::LDC];  // A . D
   T dA[BC::C * BC::LDC];  // dA . D
   T Sh[BC::DK * BC::LDV]; // the adjoint [Sh | zh | 0], rows = features
-  T Ok[BC::C * BC::LDK];  // dk staging
-  T Ov[BC::C * BC::LDO];  // dv staging
+  float pw[BC::C + 4];
+  T Ok[kStageOut ? BC::C * BC::LDK : 1];  // dk staging
+  T Ov[kStageOut ? BC::C * BC::LDO : 1];  // dv staging
+};
+
+// The reverse summary needs the weighted queries and dN only.
+template <class BC>
+struct alignas(16) SmemRsum {
+  using T = typename BC::type;
+  T QW[BC::C * BC::LDK];
+  T dN[BC::C * BC::LDV];
   float pw[BC::C + 4];
 };
 
@@ -160,41 +174,87 @@ __device__ __forceinline__ float feat(float x, int fmap) {
   return fmap ? phi_elu1(x) : x;
 }
 
-// ---- staging of one chunk ---------------------------------------------------
-// phi(q) rows (and, if QW, gamma^(t+1) phi(q_t)); rows past the chunk and
-// feature columns past d are zero.
-template <class BC, bool VK>
-__device__ __forceinline__ void stage_feat(typename BC::type *F, typename BC::type *W,
-                                           const float *wt, __amdgpu_buffer_rsrc_t r, int c0,
-                                           int Lc, int d, int fmap) {
+// ---- one chunk: loads into registers (issued a chunk ahead), then LDS -------
+// Thread i handles blocks i, i + NT, ... of the chunk's rows (QCB or VCB
+// 16-byte blocks per row); NQ / NV such blocks at most.
+template <class BC>
+struct BRegs {
+  static constexpr int NQ = (BC::C * BC::QCB + BC::NT - 1) / BC::NT;
+  static constexpr int NV = (BC::C * BC::VCB + BC::NT - 1) / BC::NT;
+  typename BC::vec q[NQ], k[NQ], v[NV], o[NV], g[NV];
+  float den[NV];
+};
+
+struct HeadRsrc {
+  __amdgpu_buffer_rsrc_t q, k, v, o, g, den;
+};
+
+// LQ, LK, LV: load q, k, v; LOG: load o, dL/do and the denominators.
+template <class BC, bool VK, bool LQ, bool LK, bool LV, bool LOG>
+__device__ __forceinline__ void load_chunk(BRegs<BC> &R, const HeadRsrc &hr, int c0, int Lc,
+                                           int d, int dv) {
+  using T = typename BC::type;
+#pragma unroll
+  for (int n = 0; n < BRegs<BC>::NQ; ++n) {
+    const int i = threadIdx.x + n * BC::NT;
+    const int row = i / BC::QCB, col0 = (i % BC::QCB) * BC::VEC;
+    const bool ok = i < BC::C * BC::QCB && row < Lc;
+    if constexpr (LQ) R.q[n] = load_vec<T, VK>(hr.q, c0 + row, col0, d, ok);
+    if constexpr (LK) R.k[n] = load_vec<T, VK>(hr.k, c0 + row, col0, d, ok);
+  }
+#pragma unroll
+  for (int n = 0; n < BRegs<BC>::NV; ++n) {
+    const int i = threadIdx.x + n * BC::NT;
+    const int row = i / BC::VCB, col0 = (i % BC::VCB) * BC::VEC;
+    const bool ok = i < BC::C * BC::VCB && row < Lc;
+    if constexpr (LV) R.v[n] = load_vec<T, VK>(hr.v, c0 + row, col0, dv, ok);
+    if constexpr (LOG) {
+      R.o[n] = load_vec<T, VK>(hr.o, c0 + row, col0, dv, ok);
+      R.g[n] = load_vec<T, VK>(hr.g, c0 + row, col0, dv, ok);
+      R.den[n] = buf_load1(hr.den, ok ? (uint32_t)((c0 + row) * 4) : kOOB, (float *)nullptr);
+    }
+  }
+}
+
+// phi(q) or phi(k) rows into F (if set) and weighted rows wt[row] phi(.)
+// into W (if set); rows past the chunk and feature columns past d are zero.
+template <class BC>
+__device__ __forceinline__ void commit_feat(typename BC::type *F, typename BC::type *W,
+                                            const float *wt,
+                                            const typename BC::vec (&X)[BRegs<BC>::NQ], int Lc,
+                                            int d, int fmap) {
   using T = typename BC::type;
   using V = typename BC::vec;
-  for (int i = threadIdx.x; i < BC::C * BC::QCB; i += BC::NT) {
+#pragma unroll
+  for (int n = 0; n < BRegs<BC>::NQ; ++n) {
+    const int i = threadIdx.x + n * BC::NT;
+    if (i >= BC::C * BC::QCB) break;
     const int row = i / BC::QCB, col0 = (i % BC::QCB) * BC::VEC;
-    const V x = load_vec<T, VK>(r, c0 + row, col0, d, row < Lc);
     V f, w;
     const float s = W ? wt[row] : 0.f;
 #pragma unroll
     for (int e = 0; e < BC::VEC; ++e) {
-      const float y = (row < Lc && col0 + e < d) ? feat(to_f32(x[e]), fmap) : 0.f;
+      const float y = (row < Lc && col0 + e < d) ? feat(to_f32(X[n][e]), fmap) : 0.f;
       f[e] = from_f32<T>(y);
       w[e] = from_f32<T>(y * s);
     }
-    *reinterpret_cast<V *>(F + row * BC::LDK + col0) = f;
+    if (F) *reinterpret_cast<V *>(F + row * BC::LDK + col0) = f;
     if (W) *reinterpret_cast<V *>(W + row * BC::LDK + col0) = w;
   }
 }
 
 // [v | 1 | 0] rows (the ones column only for tokens of the chunk).
-template <class BC, bool VK>
-__device__ __forceinline__ void stage_values(typename BC::type *Vp, __amdgpu_buffer_rsrc_t r,
-                                             int c0, int Lc, int dv) {
+template <class BC>
+__device__ __forceinline__ void commit_values(typename BC::type *Vp, const BRegs<BC> &R,
+                                              int Lc) {
   using T = typename BC::type;
   using V = typename BC::vec;
-  for (int i = threadIdx.x; i < BC::C * BC::VCB; i += BC::NT) {
+#pragma unroll
+  for (int n = 0; n < BRegs<BC>::NV; ++n) {
+    const int i = threadIdx.x + n * BC::NT;
+    if (i >= BC::C * BC::VCB) break;
     const int row = i / BC::VCB, cb = i % BC::VCB, col0 = cb * BC::VEC;
-    *reinterpret_cast<V *>(Vp + row * BC::LDV + col0) =
-        load_vec<T, VK>(r, c0 + row, col0, dv, row < Lc);
+    *reinterpret_cast<V *>(Vp + row * BC::LDV + col0) = R.v[n];
     if (cb < BC::XCB) {
       V x;
 #pragma unroll
@@ -206,26 +266,24 @@ __device__ __forceinline__ void stage_values(typename BC::type *Vp, __amdgpu_buf
 }
 
 // [g / den | -(g . o) / den | 0] rows; zero past the chunk.  The threads of
-// one row are VCB consecutive lanes, so the row's dot product is a shuffle
-// reduction.
-template <class BC, bool VK>
-__device__ __forceinline__ void stage_dn(typename BC::type *dN, __amdgpu_buffer_rsrc_t ro,
-                                         __amdgpu_buffer_rsrc_t rg, const float *den, int c0,
-                                         int Lc, int dv) {
+// one row are VCB consecutive lanes and every iteration runs whole waves, so
+// the row's dot product is a shuffle reduction.
+template <class BC>
+__device__ __forceinline__ void commit_dn(typename BC::type *dN, const BRegs<BC> &R, int Lc) {
   using T = typename BC::type;
   using V = typename BC::vec;
-  for (int i = threadIdx.x; i < BC::C * BC::VCB; i += BC::NT) {
+#pragma unroll
+  for (int n = 0; n < BRegs<BC>::NV; ++n) {
+    const int i = threadIdx.x + n * BC::NT;
+    if (i >= BC::C * BC::VCB) break;
     const int row = i / BC::VCB, cb = i % BC::VCB, col0 = cb * BC::VEC;
-    const bool ok = row < Lc;
-    const V o = load_vec<T, VK>(ro, c0 + row, col0, dv, ok);
-    const V g = load_vec<T, VK>(rg, c0 + row, col0, dv, ok);
-    const float rd = ok ? 1.f / den[c0 + row] : 0.f;
+    const float rd = row < Lc ? 1.f / R.den[n] : 0.f;
     float dot = 0.f;
     V x;
 #pragma unroll
     for (int e = 0; e < BC::VEC; ++e) {
-      const float ge = to_f32(g[e]);
-      dot = fmaf(ge, to_f32(o[e]), dot);
+      const float ge = to_f32(R.g[n][e]);
+      dot = fmaf(ge, to_f32(R.o[n][e]), dot);
       x[e] = from_f32<T>(ge * rd);
     }
 #pragma unroll
@@ -238,6 +296,22 @@ __device__ __forceinline__ void stage_dn(typename BC::type *dN, __amdgpu_buffer_
       if (cb == 0) y[0] = from_f32<T>(-dot * rd);
       *reinterpret_cast<V *>(dN + row * BC::LDV + BC::DV + col0) = y;
     }
+  }
+}
+
+// One accumulator tile (rows 16 t0 + 4 lg + r, column 16 c0 + li) straight
+// to global memory: rows past the chunk and columns past ncols are dropped.
+// The tile's 16 x 16 elements are written by one wave together, so its
+// partial lines merge in the cache before they reach memory.
+template <typename T>
+__device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t r, const f32x4 &acc, int c0,
+                                           int row0, int col, int Lc, int ncols, int lg) {
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int row = row0 + 4 * lg + rr;
+    const bool ok = row < Lc && col < ncols;
+    buf_store1(r, ok ? (uint32_t)(((size_t)(c0 + row) * ncols + col) * sizeof(T)) : kOOB,
+               from_f32<T>(acc[rr]));
   }
 }
 
@@ -366,8 +440,22 @@ __device__ __forceinline__ void tri_tiles(typename BC::type *M, const typename B
   }
 }
 
-// Rows of an LDS staging tile to global memory (rows past the chunk and
-// columns past ncols are dropped).
+// A tile into an LDS staging tile (row stride ld), or straight to memory.
+template <class BC>
+__device__ __forceinline__ void out_tile(typename BC::type *M, int ld,
+                                         __amdgpu_buffer_rsrc_t r, const f32x4 &acc, int c0,
+                                         int row0, int col, int Lc, int ncols, int lg) {
+  if constexpr (kStageOut) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      M[(row0 + 4 * lg + rr) * ld + col] = from_f32<typename BC::type>(acc[rr]);
+  } else {
+    store_tile<typename BC::type>(r, acc, c0, row0, col, Lc, ncols, lg);
+  }
+}
+
+// Rows of a staging tile to memory (rows past the chunk, columns past ncols
+// dropped).
 template <class BC, bool VK>
 __device__ __forceinline__ void store_rows(__amdgpu_buffer_rsrc_t r, const typename BC::type *M,
                                            int ld, int NCB, int c0, int Lc, int ncols) {
@@ -390,12 +478,14 @@ __global__ void __launch_bounds__(BC::NT) bwd_dq_kernel(BwdParams p) {
   const int li = lane & 15, lg = lane >> 4;
   const int d = p.d, dv = p.dv, N = p.N;
   const int t_begin = seg * p.seg_len, t_end = min(N, t_begin + p.seg_len);
-  const __amdgpu_buffer_rsrc_t rq = head_rsrc<T>(p.q, bh, N, d), rk = head_rsrc<T>(p.k, bh, N, d),
-                               rv = head_rsrc<T>(p.v, bh, N, dv),
-                               ro = head_rsrc<T>(p.o, bh, N, dv),
-                               rg = head_rsrc<T>(p.dout, bh, N, dv),
-                               rdq = head_rsrc<T>(p.dq, bh, N, d);
-  const float *den = p.den + (size_t)bh * N;
+  HeadRsrc hr;
+  hr.q = head_rsrc<T>(p.q, bh, N, d);
+  hr.k = head_rsrc<T>(p.k, bh, N, d);
+  hr.v = head_rsrc<T>(p.v, bh, N, dv);
+  hr.o = head_rsrc<T>(p.o, bh, N, dv);
+  hr.g = head_rsrc<T>(p.dout, bh, N, dv);
+  hr.den = head_rsrc<float>(p.den, bh, N, 1);
+  const __amdgpu_buffer_rsrc_t rdq = head_rsrc<T>(p.dq, bh, N, d);
   const float lg2 = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
   for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
   zero_tail_columns<BC>(sm.St);
@@ -410,19 +500,22 @@ __global__ void __launch_bounds__(BC::NT) bwd_dq_kernel(BwdParams p) {
   }
   f32x4 Sa[BC::SPW];
   state_load<BC>(Sa, S0, z0, d, dv, wv, li, lg);
+  BRegs<BC> R;
+  load_chunk<BC, VK, true, true, true, true>(R, hr, t_begin, min(BC::C, N - t_begin), d, dv);
   __syncthreads();
 
   for (int c0 = t_begin; c0 < t_end; c0 += BC::C) {
     const int Lc = min(BC::C, N - c0);
-    // key weights gamma^(L-1-j) (0 past the chunk) sit in Os until it is used
-    float *kw = reinterpret_cast<float *>(sm.Os);
-    for (int j = threadIdx.x; j < BC::C; j += BC::NT) kw[j] = j < Lc ? sm.pw[Lc - 1 - j] : 0.f;
+    for (int j = threadIdx.x; j < BC::C; j += BC::NT) sm.kw[j] = j < Lc ? sm.pw[Lc - 1 - j] : 0.f;
     __syncthreads();
-    stage_feat<BC, VK>(sm.Fq, nullptr, nullptr, rq, c0, Lc, d, p.fmap);
-    stage_feat<BC, VK>(sm.Fk, sm.KW, kw, rk, c0, Lc, d, p.fmap);
-    stage_values<BC, VK>(sm.Vp, rv, c0, Lc, dv);
-    stage_dn<BC, VK>(sm.dN, ro, rg, den, c0, Lc, dv);
+    commit_feat<BC>(sm.Fq, nullptr, nullptr, R.q, Lc, d, p.fmap);
+    commit_feat<BC>(sm.Fk, sm.KW, sm.kw, R.k, Lc, d, p.fmap);
+    commit_values<BC>(sm.Vp, R, Lc);
+    commit_dn<BC>(sm.dN, R, Lc);
     state_copy<BC>(sm.St, Sa, wv, li, lg);
+    if (c0 + BC::C < t_end)  // the next chunk's rows are in flight during this one
+      load_chunk<BC, VK, true, true, true, true>(R, hr, c0 + BC::C, min(BC::C, N - c0 - BC::C),
+                                                 d, dv);
     __syncthreads();
 
     tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, wv, li, lg);
@@ -451,141 +544,172 @@ __global__ void __launch_bounds__(BC::NT) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tt + 4 * lg + r, f = 16 * fb + li;
-        const float dphi = p.fmap ? fminf(to_f32(sm.Fq[t * BC::LDK + f]), 1.f) : 1.f;
-        sm.Os[t * BC::LDK + f] = from_f32<T>(acc[r] * dphi);
+        acc[r] *= p.fmap ? fminf(to_f32(sm.Fq[t * BC::LDK + f]), 1.f) : 1.f;
       }
+      out_tile<BC>(sm.Os, BC::LDK, rdq, acc, c0, 16 * tt, 16 * fb + li, Lc, d, lg);
     }
     // forward state across the chunk
     state_update<BC>(Sa, sm.KW, sm.Vp, sm.pw[Lc], wv, li, lg);
     __syncthreads();
-    store_rows<BC, VK>(rdq, sm.Os, BC::LDK, BC::QCB, c0, Lc, d);
-    __syncthreads();
+    if constexpr (kStageOut) store_rows<BC, VK>(rdq, sm.Os, BC::LDK, BC::QCB, c0, Lc, d);
   }
 }
 
 // ---- dk, dv: chunks right to left, adjoint state ------------------------------
-// SUMMARY: only the adjoint, from zero at the segment's end, of segment
-// blockIdx.x + 1, into reverse slot blockIdx.x.
-template <class BC, bool VK, bool SUMMARY>
+template <class BC, bool VK>
 __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
   using T = typename BC::type;
   __shared__ SmemDkv<BC> sm;
-  const int seg = SUMMARY ? blockIdx.x + 1 : blockIdx.x, bh = blockIdx.y;
+  const int seg = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const int d = p.d, dv = p.dv, N = p.N;
   const int t_begin = seg * p.seg_len, t_end = min(N, t_begin + p.seg_len);
-  const __amdgpu_buffer_rsrc_t rq = head_rsrc<T>(p.q, bh, N, d), rk = head_rsrc<T>(p.k, bh, N, d),
-                               rv = head_rsrc<T>(p.v, bh, N, dv),
-                               ro = head_rsrc<T>(p.o, bh, N, dv),
-                               rg = head_rsrc<T>(p.dout, bh, N, dv),
-                               rdk = head_rsrc<T>(p.dk, bh, N, d),
+  HeadRsrc hr;
+  hr.q = head_rsrc<T>(p.q, bh, N, d);
+  hr.k = head_rsrc<T>(p.k, bh, N, d);
+  hr.v = head_rsrc<T>(p.v, bh, N, dv);
+  hr.o = head_rsrc<T>(p.o, bh, N, dv);
+  hr.g = head_rsrc<T>(p.dout, bh, N, dv);
+  hr.den = head_rsrc<float>(p.den, bh, N, 1);
+  const __amdgpu_buffer_rsrc_t rdk = head_rsrc<T>(p.dk, bh, N, d),
                                rdv = head_rsrc<T>(p.dv_, bh, N, dv);
-  const float *den = p.den + (size_t)bh * N;
   const float lg2 = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
   for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
   zero_tail_columns<BC>(sm.Sh);
 
   f32x4 Sa[BC::SPW];
   {
-    const float *S1 = nullptr, *z1 = nullptr;
-    if (!SUMMARY) {
-      if (p.nseg > 1) {
-        S1 = p.ws_r + ((size_t)seg * p.BH + bh) * p.wrec;
-        z1 = S1 + (size_t)d * dv;
-      } else {
-        S1 = p.dS_out ? p.dS_out + (size_t)bh * d * dv : nullptr;
-        z1 = p.dz_out ? p.dz_out + (size_t)bh * d : nullptr;
-      }
+    const float *S1, *z1;
+    if (p.nseg > 1) {
+      S1 = p.ws_r + ((size_t)seg * p.BH + bh) * p.wrec;
+      z1 = S1 + (size_t)d * dv;
+    } else {
+      S1 = p.dS_out ? p.dS_out + (size_t)bh * d * dv : nullptr;
+      z1 = p.dz_out ? p.dz_out + (size_t)bh * d : nullptr;
     }
     state_load<BC>(Sa, S1, z1, d, dv, wv, li, lg);
   }
+  const int last = t_begin + ((t_end - t_begin - 1) / BC::C) * BC::C;
+  BRegs<BC> R;
+  load_chunk<BC, VK, true, true, true, true>(R, hr, last, min(BC::C, N - last), d, dv);
   __syncthreads();
 
-  const int last = t_begin + ((t_end - t_begin - 1) / BC::C) * BC::C;
   for (int c0 = last; c0 >= t_begin; c0 -= BC::C) {
     const int Lc = min(BC::C, N - c0);
-    stage_feat<BC, VK>(sm.Fq, sm.QW, sm.pw + 1, rq, c0, Lc, d, p.fmap);
-    stage_dn<BC, VK>(sm.dN, ro, rg, den, c0, Lc, dv);
-    if constexpr (!SUMMARY) {
-      stage_feat<BC, VK>(sm.Fk, nullptr, nullptr, rk, c0, Lc, d, p.fmap);
-      stage_values<BC, VK>(sm.Vp, rv, c0, Lc, dv);
-      state_copy<BC>(sm.Sh, Sa, wv, li, lg);
-    }
+    commit_feat<BC>(sm.Fq, sm.QW, sm.pw + 1, R.q, Lc, d, p.fmap);
+    commit_feat<BC>(sm.Fk, nullptr, nullptr, R.k, Lc, d, p.fmap);
+    commit_values<BC>(sm.Vp, R, Lc);
+    commit_dn<BC>(sm.dN, R, Lc);
+    state_copy<BC>(sm.Sh, Sa, wv, li, lg);
+    if (c0 > t_begin)  // the previous chunk's rows are in flight during this one
+      load_chunk<BC, VK, true, true, true, true>(R, hr, c0 - BC::C, BC::C, d, dv);
     __syncthreads();
 
-    if constexpr (!SUMMARY) {
-      tri_tiles<BC, BC::DK / 32, BC::LDK>(sm.Ad, sm.Fq, sm.Fk, sm.pw, wv, li, lg);
-      tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, wv, li, lg);
-      __syncthreads();
-      // dphi(k) = gamma^(L-1-j) V' Sh^T + dA^T phi(Q), then phi'(k)
-      for (int ti = wv; ti < BC::NTB * BC::NFB; ti += BC::NW) {
-        const int jt = ti / BC::NFB, fb = ti % BC::NFB;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    tri_tiles<BC, BC::DK / 32, BC::LDK>(sm.Ad, sm.Fq, sm.Fk, sm.pw, wv, li, lg);
+    tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, wv, li, lg);
+    __syncthreads();
+    // dphi(k) = gamma^(L-1-j) V' Sh^T + dA^T phi(Q), then phi'(k)
+    for (int ti = wv; ti < BC::NTB * BC::NFB; ti += BC::NW) {
+      const int jt = ti / BC::NFB, fb = ti % BC::NFB;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < BC::DVK / 32; ++ks) {
-          Frag<T> a, b;
-          frag_rk(a, sm.Vp, BC::LDV, 16 * jt, 32 * ks, li, lg);
-          frag_rk(b, sm.Sh, BC::LDV, 16 * fb, 32 * ks, li, lg);
-          mma(acc, a, b);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
-        for (int ks = (16 * jt) / 32; ks < BC::C / 32; ++ks) {
-          Frag<T> a, b;
-          frag_kr(a, sm.dA, BC::LDC, 16 * jt, 32 * ks, li, lg);
-          frag_kr(b, sm.Fq, BC::LDK, 16 * fb, 32 * ks, li, lg);
-          mma(acc, a, b);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * jt + 4 * lg + r, f = 16 * fb + li;
-          const float dphi = p.fmap ? fminf(to_f32(sm.Fk[j * BC::LDK + f]), 1.f) : 1.f;
-          sm.Ok[j * BC::LDK + f] = from_f32<T>(acc[r] * dphi);
-        }
+      for (int ks = 0; ks < BC::DVK / 32; ++ks) {
+        Frag<T> a, b;
+        frag_rk(a, sm.Vp, BC::LDV, 16 * jt, 32 * ks, li, lg);
+        frag_rk(b, sm.Sh, BC::LDV, 16 * fb, 32 * ks, li, lg);
+        mma(acc, a, b);
       }
-      // dv' = gamma^(L-1-j) phi(K) Sh + (A . D)^T dN  (value columns only)
-      for (int ti = wv; ti < BC::NTB * (BC::NVP - 1); ti += BC::NW) {
-        const int jt = ti / (BC::NVP - 1), vb = ti % (BC::NVP - 1);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < BC::DK / 32; ++ks) {
-          Frag<T> a, b;
-          frag_rk(a, sm.Fk, BC::LDK, 16 * jt, 32 * ks, li, lg);
-          frag_kr(b, sm.Sh, BC::LDV, 16 * vb, 32 * ks, li, lg);
-          mma(acc, a, b);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
-        for (int ks = (16 * jt) / 32; ks < BC::C / 32; ++ks) {
-          Frag<T> a, b;
-          frag_kr(a, sm.Ad, BC::LDC, 16 * jt, 32 * ks, li, lg);
-          frag_kr(b, sm.dN, BC::LDV, 16 * vb, 32 * ks, li, lg);
-          mma(acc, a, b);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sm.Ov[(16 * jt + 4 * lg + r) * BC::LDO + 16 * vb + li] = from_f32<T>(acc[r]);
+      for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
+      for (int ks = (16 * jt) / 32; ks < BC::C / 32; ++ks) {
+        Frag<T> a, b;
+        frag_kr(a, sm.dA, BC::LDC, 16 * jt, 32 * ks, li, lg);
+        frag_kr(b, sm.Fq, BC::LDK, 16 * fb, 32 * ks, li, lg);
+        mma(acc, a, b);
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * jt + 4 * lg + r, f = 16 * fb + li;
+        acc[r] *= p.fmap ? fminf(to_f32(sm.Fk[j * BC::LDK + f]), 1.f) : 1.f;
+      }
+      out_tile<BC>(sm.Ok, BC::LDK, rdk, acc, c0, 16 * jt, 16 * fb + li, Lc, d, lg);
+    }
+    // dv' = gamma^(L-1-j) phi(K) Sh + (A . D)^T dN  (value columns only)
+    for (int ti = wv; ti < BC::NTB * (BC::NVP - 1); ti += BC::NW) {
+      const int jt = ti / (BC::NVP - 1), vb = ti % (BC::NVP - 1);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < BC::DK / 32; ++ks) {
+        Frag<T> a, b;
+        frag_rk(a, sm.Fk, BC::LDK, 16 * jt, 32 * ks, li, lg);
+        frag_kr(b, sm.Sh, BC::LDV, 16 * vb, 32 * ks, li, lg);
+        mma(acc, a, b);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
+      for (int ks = (16 * jt) / 32; ks < BC::C / 32; ++ks) {
+        Frag<T> a, b;
+        frag_kr(a, sm.Ad, BC::LDC, 16 * jt, 32 * ks, li, lg);
+        frag_kr(b, sm.dN, BC::LDV, 16 * vb, 32 * ks, li, lg);
+        mma(acc, a, b);
+      }
+      out_tile<BC>(sm.Ov, BC::LDO, rdv, acc, c0, 16 * jt, 16 * vb + li, Lc, dv, lg);
     }
     // adjoint across the chunk: Sh <- gamma^L Sh + (gamma^(t+1) phi(Q))^T dN
     state_update<BC>(Sa, sm.QW, sm.dN, sm.pw[Lc], wv, li, lg);
     __syncthreads();
-    if constexpr (!SUMMARY) {
+    if constexpr (kStageOut) {
       store_rows<BC, VK>(rdk, sm.Ok, BC::LDK, BC::QCB, c0, Lc, d);
       store_rows<BC, VK>(rdv, sm.Ov, BC::LDO, BC::VCB, c0, Lc, dv);
-      __syncthreads();
     }
   }
 
-  if constexpr (SUMMARY) {
-    float *dst = p.ws_r + ((size_t)(seg - 1) * p.BH + bh) * p.wrec;
-    state_store<BC>(Sa, dst, dst + (size_t)d * dv, d, dv, wv, li, lg);
-  } else if (seg == 0) {
+  if (seg == 0)
     state_store<BC>(Sa, p.dS_in ? p.dS_in + (size_t)bh * d * dv : nullptr,
                     p.dz_in ? p.dz_in + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
+}
+
+// Reverse summary: the adjoint, from zero at its end, of segment
+// blockIdx.x + 1 (every segment but the first), into reverse slot blockIdx.x.
+template <class BC, bool VK>
+__global__ void __launch_bounds__(BC::NT) bwd_rsum_kernel(BwdParams p) {
+  using T = typename BC::type;
+  __shared__ SmemRsum<BC> sm;
+  const int seg = blockIdx.x + 1, bh = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int d = p.d, dv = p.dv, N = p.N;
+  const int t_begin = seg * p.seg_len, t_end = min(N, t_begin + p.seg_len);
+  HeadRsrc hr;
+  hr.q = head_rsrc<T>(p.q, bh, N, d);
+  hr.k = hr.q;
+  hr.v = head_rsrc<T>(p.v, bh, N, dv);
+  hr.o = head_rsrc<T>(p.o, bh, N, dv);
+  hr.g = head_rsrc<T>(p.dout, bh, N, dv);
+  hr.den = head_rsrc<float>(p.den, bh, N, 1);
+  const float lg2 = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
+  for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
+  f32x4 Sa[BC::SPW];
+  state_load<BC>(Sa, nullptr, nullptr, d, dv, wv, li, lg);
+  const int last = t_begin + ((t_end - t_begin - 1) / BC::C) * BC::C;
+  BRegs<BC> R;
+  load_chunk<BC, VK, true, false, false, true>(R, hr, last, min(BC::C, N - last), d, dv);
+  __syncthreads();
+  for (int c0 = last; c0 >= t_begin; c0 -= BC::C) {
+    const int Lc = min(BC::C, N - c0);
+    commit_feat<BC>(nullptr, sm.QW, sm.pw + 1, R.q, Lc, d, p.fmap);
+    commit_dn<BC>(sm.dN, R, Lc);
+    if (c0 > t_begin)
+      load_chunk<BC, VK, true, false, false, true>(R, hr, c0 - BC::C, BC::C, d, dv);
+    __syncthreads();
+    state_update<BC>(Sa, sm.QW, sm.dN, sm.pw[Lc], wv, li, lg);
+    __syncthreads();
   }
+  float *dst = p.ws_r + ((size_t)(seg - 1) * p.BH + bh) * p.wrec;
+  state_store<BC>(Sa, dst, dst + (size_t)d * dv, d, dv, wv, li, lg);
 }
 
 // Adjoint entering each segment from the right, in place: slot nseg-1 <-
@@ -627,7 +751,7 @@ hipError_t run_bwd(const BwdParams &p, hipStream_t s) {
   static_assert(sizeof(SmemDq<BC>) <= 160 * 1024 && sizeof(SmemDkv<BC>) <= 160 * 1024,
                 "LDS budget");
   if (p.nseg > 1) {
-    hipError_t e = launch_kernel("linear_bwd_rsummary", bwd_dkv_kernel<BC, VK, true>,
+    hipError_t e = launch_kernel("linear_bwd_rsummary", bwd_rsum_kernel<BC, VK>,
                                  dim3(p.nseg - 1, p.BH), dim3(BC::NT), s, p);
     if (e != hipSuccess) return e;
     const size_t rec = (size_t)p.d * p.dv + p.d;
@@ -638,7 +762,7 @@ hipError_t run_bwd(const BwdParams &p, hipStream_t s) {
   hipError_t e = launch_kernel("linear_bwd_dq", bwd_dq_kernel<BC, VK>, dim3(p.nseg, p.BH),
                                dim3(BC::NT), s, p);
   if (e != hipSuccess) return e;
-  return launch_kernel("linear_bwd_dkv", bwd_dkv_kernel<BC, VK, false>, dim3(p.nseg, p.BH),
+  return launch_kernel("linear_bwd_dkv", bwd_dkv_kernel<BC, VK>, dim3(p.nseg, p.BH),
                        dim3(BC::NT), s, p);
 }
 
@@ -649,7 +773,7 @@ hipError_t run_bwd_vk(const BwdParams &p, hipStream_t s) {
 
 // bf16: 64-token chunks at d = dv = 64, 32-token chunks (and eight waves)
 // with 128-wide tiles; fp32 up to 64-wide tiles, 32-token chunks.
-using BB64x64 = BCfg<bf16, 64, 64, 64, 4>;
+using BB64x64 = BCfg<bf16, 64, 64, 32, 4>;
 using BB64x128 = BCfg<bf16, 64, 128, 32, 8>;
 using BB128x64 = BCfg<bf16, 128, 64, 32, 8>;
 using BB128x128 = BCfg<bf16, 128, 128, 32, 8>;
