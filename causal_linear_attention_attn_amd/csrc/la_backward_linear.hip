@@ -67,6 +67,9 @@ struct BCfg {
   static constexpr int SPW = (NST + NW - 1) / NW;     // state tiles per wave
   static constexpr int QCB = DK / VEC, VCB = DV / VEC;  // 16-byte blocks per row
   static constexpr int XCB = 32 / VEC;                 // blocks of the extra columns
+  // resident waves per SIMD the dq kernel's registers must allow (its LDS
+  // admits three four-wave workgroups per CU)
+  static constexpr int WPE_DQ = NW == 4 ? 3 : 2;
   static_assert(C % 32 == 0 && DK % 32 == 0 && DV % 16 == 0, "tile sizes");
   // row loops run whole waves (the dn row reduction shuffles within a wave)
   static_assert((C * QCB) % kWave == 0 && (C * VCB) % kWave == 0, "whole-wave row loops");
@@ -420,7 +423,11 @@ __device__ __forceinline__ void tri_tiles(typename BC::type *M, const typename B
                                           const typename BC::type *Y, const float *pw, int wv,
                                           int li, int lg) {
   using T = typename BC::type;
-  for (int ti = wv; ti < BC::NTB * BC::NTB; ti += BC::NW) {
+  constexpr int NTI = BC::NTB * BC::NTB;
+#pragma unroll
+  for (int n = 0; n < (NTI + BC::NW - 1) / BC::NW; ++n) {
+    const int ti = wv + BC::NW * n;
+    if (ti >= NTI) break;
     const int tt = ti / BC::NTB, jt = ti % BC::NTB;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (jt <= tt) {
@@ -469,7 +476,7 @@ __device__ __forceinline__ void store_rows(__amdgpu_buffer_rsrc_t r, const typen
 
 // ---- dq: chunks left to right, forward state --------------------------------
 template <class BC, bool VK>
-__global__ void __launch_bounds__(BC::NT) bwd_dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p) {
   using T = typename BC::type;
   __shared__ SmemDq<BC> sm;
   const int seg = blockIdx.x, bh = blockIdx.y;
@@ -522,7 +529,11 @@ __global__ void __launch_bounds__(BC::NT) bwd_dq_kernel(BwdParams p) {
     __syncthreads();
 
     // dphi(q) = gamma^(t+1) dN S'_in^T + dA phi(K), then phi'(q)
-    for (int ti = wv; ti < BC::NTB * BC::NFB; ti += BC::NW) {
+    constexpr int NQT = BC::NTB * BC::NFB;
+#pragma unroll
+    for (int n = 0; n < (NQT + BC::NW - 1) / BC::NW; ++n) {
+      const int ti = wv + BC::NW * n;
+      if (ti >= NQT) break;
       const int tt = ti / BC::NFB, fb = ti % BC::NFB;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -535,7 +546,9 @@ __global__ void __launch_bounds__(BC::NT) bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[16 * tt + 4 * lg + r + 1];
       const int kend = (16 * tt + 16 + 31) / 32;
-      for (int ks = 0; ks < kend; ++ks) {
+#pragma unroll
+      for (int ks = 0; ks < BC::C / 32; ++ks) {
+        if (ks >= kend) break;
         Frag<T> a, b;
         frag_rk(a, sm.dA, BC::LDC, 16 * tt, 32 * ks, li, lg);
         frag_kr(b, sm.Fk, BC::LDK, 16 * fb, 32 * ks, li, lg);
@@ -611,7 +624,11 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
     tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, wv, li, lg);
     __syncthreads();
     // dphi(k) = gamma^(L-1-j) V' Sh^T + dA^T phi(Q), then phi'(k)
-    for (int ti = wv; ti < BC::NTB * BC::NFB; ti += BC::NW) {
+    constexpr int NKT = BC::NTB * BC::NFB;
+#pragma unroll
+    for (int n = 0; n < (NKT + BC::NW - 1) / BC::NW; ++n) {
+      const int ti = wv + BC::NW * n;
+      if (ti >= NKT) break;
       const int jt = ti / BC::NFB, fb = ti % BC::NFB;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -623,7 +640,9 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
-      for (int ks = (16 * jt) / 32; ks < BC::C / 32; ++ks) {
+#pragma unroll
+      for (int ks = 0; ks < BC::C / 32; ++ks) {
+        if (ks < (16 * jt) / 32) continue;
         Frag<T> a, b;
         frag_kr(a, sm.dA, BC::LDC, 16 * jt, 32 * ks, li, lg);
         frag_kr(b, sm.Fq, BC::LDK, 16 * fb, 32 * ks, li, lg);
@@ -637,7 +656,11 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
       out_tile<BC>(sm.Ok, BC::LDK, rdk, acc, c0, 16 * jt, 16 * fb + li, Lc, d, lg);
     }
     // dv' = gamma^(L-1-j) phi(K) Sh + (A . D)^T dN  (value columns only)
-    for (int ti = wv; ti < BC::NTB * (BC::NVP - 1); ti += BC::NW) {
+    constexpr int NVT = BC::NTB * (BC::NVP - 1);
+#pragma unroll
+    for (int n = 0; n < (NVT + BC::NW - 1) / BC::NW; ++n) {
+      const int ti = wv + BC::NW * n;
+      if (ti >= NVT) break;
       const int jt = ti / (BC::NVP - 1), vb = ti % (BC::NVP - 1);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -649,7 +672,9 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
-      for (int ks = (16 * jt) / 32; ks < BC::C / 32; ++ks) {
+#pragma unroll
+      for (int ks = 0; ks < BC::C / 32; ++ks) {
+        if (ks < (16 * jt) / 32) continue;
         Frag<T> a, b;
         frag_kr(a, sm.Ad, BC::LDC, 16 * jt, 32 * ks, li, lg);
         frag_kr(b, sm.dN, BC::LDV, 16 * vb, 32 * ks, li, lg);
