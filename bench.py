@@ -246,6 +246,8 @@ def pmc_summary(d, wid):
         a = alg if k in ("linear_chunk", "delta_seq") else None
         if wid == 3 and k == "linear_decode":
             a = decode_step_bytes(w)
+        if k in ("linear_bwd_dq", "linear_bwd_dkv"):
+            a = w.B * w.H * w.N * bwd_bytes_per_head_token(w, k)
         out.append(f"| {k} | {n} | {fk:.0f} | {wk:.0f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
                    f"{(rd + wr) / 1e6:.1f} | {'' if a is None else f'{a / 1e6:.1f}'} |")
         recs.append({"workload": w.name, "kernel": k, "src": kernel_src_hash(k),
@@ -492,7 +494,7 @@ def bench_train(la, lib, torch, w, steps, warmup):
     kname, kms = dominant(bk)
     bpl = head_tokens * bwd_bytes_per_head_token(w, kname)
     achieved = bpl / (kms * 1e-3) / 1e9
-    traffic, tsrc = traffic_record(w.name + "_backward", kname)
+    traffic, tsrc = traffic_record(w.name, kname)
     return {
         "workload": w.name + "_forward_backward", "tokens_per_s": B * N / dt,
         "ms_per_step": dt * 1e3, "backward_kernels_ms": kern,
