@@ -139,9 +139,10 @@ def library_kernel_name(raw):
         return "linear_bwd_rscan"
     if "bwd_dq_kernel" in raw:
         return "linear_bwd_dq"
-    if "bwd_dkv_kernel" in raw:  # the last template flag marks the reverse summary
-        summary = "Lb1EEEvNS_9Bwd" in raw or raw.rstrip().endswith("true>(la::BwdParams)")
-        return "linear_bwd_rsummary" if summary else "linear_bwd_dkv"
+    if "bwd_rsum_kernel" in raw:
+        return "linear_bwd_rsummary"
+    if "bwd_dkv_kernel" in raw:
+        return "linear_bwd_dkv"
     for fn, name in (("chunk_kernel", "linear_chunk"), ("summary_kernel", "linear_summary"),
                      ("scan_kernel", "linear_scan"), ("prep_kernel", "delta_prep"),
                      ("seq_kernel", "delta_seq")):

@@ -46,7 +46,7 @@ constexpr int kMaxSegB = 32;  // the forward's most segments per sequence
 // own), not as 2-byte stores straight from the accumulators.
 constexpr bool kStageOut = true;
 
-template <typename T, int DK_, int DV_, int C_, int NW_>
+template <typename T, int DK_, int DV_, int C_, int NW_, int WPE_DQ_>
 struct BCfg {
   using type = T;
   using vec = typename Vec16<T>::type;
@@ -67,9 +67,9 @@ struct BCfg {
   static constexpr int SPW = (NST + NW - 1) / NW;     // state tiles per wave
   static constexpr int QCB = DK / VEC, VCB = DV / VEC;  // 16-byte blocks per row
   static constexpr int XCB = 32 / VEC;                 // blocks of the extra columns
-  // resident waves per SIMD the dq kernel's registers must allow (its LDS
-  // admits three four-wave workgroups per CU)
-  static constexpr int WPE_DQ = NW == 4 ? 3 : 2;
+  // resident waves per SIMD the dq kernel's registers must allow (what its
+  // LDS admits)
+  static constexpr int WPE_DQ = WPE_DQ_;
   static_assert(C % 32 == 0 && DK % 32 == 0 && DV % 16 == 0, "tile sizes");
   // row loops run whole waves (the dn row reduction shuffles within a wave)
   static_assert((C * QCB) % kWave == 0 && (C * VCB) % kWave == 0, "whole-wave row loops");
@@ -798,11 +798,11 @@ hipError_t run_bwd_vk(const BwdParams &p, hipStream_t s) {
 
 // bf16: 64-token chunks at d = dv = 64, 32-token chunks (and eight waves)
 // with 128-wide tiles; fp32 up to 64-wide tiles, 32-token chunks.
-using BB64x64 = BCfg<bf16, 64, 64, 32, 4>;
-using BB64x128 = BCfg<bf16, 64, 128, 32, 8>;
-using BB128x64 = BCfg<bf16, 128, 64, 32, 8>;
-using BB128x128 = BCfg<bf16, 128, 128, 32, 8>;
-using BF64x64 = BCfg<float, 64, 64, 32, 4>;
+using BB64x64 = BCfg<bf16, 64, 64, 32, 4, 3>;
+using BB64x128 = BCfg<bf16, 64, 128, 32, 8, 2>;
+using BB128x64 = BCfg<bf16, 128, 64, 32, 8, 2>;
+using BB128x128 = BCfg<bf16, 128, 128, 32, 8, 2>;
+using BF64x64 = BCfg<float, 64, 64, 32, 4, 1>;
 
 }  // namespace
 
