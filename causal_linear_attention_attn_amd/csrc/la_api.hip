@@ -180,6 +180,8 @@ int la_prefill(const la_prefill_args *a, void *stream) {
       return LA_EINVAL;
     // one head's per-channel decay (fp32) must be addressable with 32-bit offsets
     if (a->alpha && (size_t)a->N * a->d * 4 > kMaxHeadBytes) return LA_EUNSUPPORTED;
+    // denominators are written for the rule the backward covers
+    if (a->den_out && (a->alpha || a->conv_weight)) return LA_EUNSUPPORTED;
   } else {
     if (!a->g && BH > 0 && a->N > 0) return LA_EINVAL;
     if (a->gamma || a->z_in || a->z_out || a->den_out) return LA_EINVAL;

@@ -802,7 +802,7 @@ __device__ __forceinline__ void fill_powers(float *pw, float log2g) {
 // so the causal structure of the score tiles costs no branches or selects)
 // and column group cg of the value tiles; normalised rows go to the staging
 // tile Os.
-template <class CF, int RB>
+template <class CF, int RB, bool DN>
 __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillParams &p, int Lc,
                                               int cg, int li, int lg, float *den_row) {
   using T = typename CF::type;
@@ -873,8 +873,9 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillPa
     const float den = accd[0] + p.eps * sm.pw[max(Lc - 1 - irow, 0)];
     const float rd = __builtin_amdgcn_rcpf(den);
     // the token's own denominator phi(q).z + eps (den carries gamma^(L-1-i))
-    if (den_row && cg == 0 && lg == 0 && irow < Lc)
-      den_row[irow] = accd[0] / sm.pw[Lc - 1 - irow] + p.eps;
+    if constexpr (DN) {
+      if (cg == 0 && lg == 0 && irow < Lc) den_row[irow] = accd[0] / sm.pw[Lc - 1 - irow] + p.eps;
+    }
 #pragma unroll
     for (int a = 0; a < CF::NPW; ++a)
       lds_store4(sm.Os + irow * CF::VLD + 16 * (cg * CF::NPW + a) + 4 * lg,
@@ -891,7 +892,8 @@ constexpr int wpe_at_most_2() {
   return CF::WPE < 2 ? CF::WPE : 2;
 }
 
-template <class CF, bool VK, bool CH, bool CV>
+// DN: also write each token's denominator (den_out; no decay variants)
+template <class CF, bool VK, bool CH, bool CV, bool DN = false>
 __global__ void __launch_bounds__(CF::NT, (CH || CV) ? wpe_at_most_2<CF>() : CF::WPE)
     chunk_kernel(PrefillParams p) {
   using T = typename CF::type;
@@ -963,17 +965,17 @@ __global__ void __launch_bounds__(CF::NT, (CH || CV) ? wpe_at_most_2<CF>() : CF:
       prefetch<CF, true, VK>(R, p, hb, c0 + CF::C, min(CF::C, N - c0 - CF::C));
     __syncthreads();
 
-    float *dno = p.den_out ? p.den_out + (size_t)bh * N + c0 : nullptr;
+    float *dno = DN ? p.den_out + (size_t)bh * N + c0 : nullptr;
     if constexpr (CF::NRB == 2) {
-      if (rb == 0) chunk_outputs<CF, 0>(sm, p, Lc, cg, li, lg, dno);
-      else chunk_outputs<CF, 1>(sm, p, Lc, cg, li, lg, dno);
+      if (rb == 0) chunk_outputs<CF, 0, DN>(sm, p, Lc, cg, li, lg, dno);
+      else chunk_outputs<CF, 1, DN>(sm, p, Lc, cg, li, lg, dno);
     } else {
       static_assert(CF::NRB == 4, "row blocks per chunk");
       switch (rb) {
-        case 0: chunk_outputs<CF, 0>(sm, p, Lc, cg, li, lg, dno); break;
-        case 1: chunk_outputs<CF, 1>(sm, p, Lc, cg, li, lg, dno); break;
-        case 2: chunk_outputs<CF, 2>(sm, p, Lc, cg, li, lg, dno); break;
-        default: chunk_outputs<CF, 3>(sm, p, Lc, cg, li, lg, dno); break;
+        case 0: chunk_outputs<CF, 0, DN>(sm, p, Lc, cg, li, lg, dno); break;
+        case 1: chunk_outputs<CF, 1, DN>(sm, p, Lc, cg, li, lg, dno); break;
+        case 2: chunk_outputs<CF, 2, DN>(sm, p, Lc, cg, li, lg, dno); break;
+        default: chunk_outputs<CF, 3, DN>(sm, p, Lc, cg, li, lg, dno); break;
       }
     }
 
@@ -1152,6 +1154,11 @@ hipError_t run_vkcc(const PrefillParams &p, hipStream_t s) {
     e = launch_kernel("linear_scan", scan_kernel<CH>, dim3((unsigned)((rec + 255) / 256), p.BH),
                       dim3(256), s, p);
     if (e != hipSuccess) return e;
+  }
+  if constexpr (!CH && !CV) {
+    if (p.den_out)
+      return launch_kernel("linear_chunk", chunk_kernel<CF, VK, false, false, true>,
+                           dim3(p.nseg, p.BH), dim3(CF::NT), s, p);
   }
   return launch_kernel("linear_chunk", chunk_kernel<CF, VK, CH, CV>, dim3(p.nseg, p.BH),
                        dim3(CF::NT), s, p);

@@ -135,7 +135,8 @@ typedef struct la_prefill_args {
   void *o;           /* [B,H,N,dv] output, dtype as q (required if N > 0) */
   float *den_out;    /* LINEAR: [B,H,N] each token's denominator
                         phi(q_t).z_t + eps (what la_backward needs), or NULL
-                        (not written).  DELTA: must be NULL. */
+                        (not written).  Not with alpha or conv_weight
+                        (LA_EUNSUPPORTED).  DELTA: must be NULL. */
   void *workspace;   /* device scratch of workspace_bytes, caller-owned;
                         may be NULL when la_prefill_workspace_size() is 0 */
   size_t workspace_bytes;

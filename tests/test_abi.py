@@ -207,6 +207,10 @@ def test_prefill_den_out_only_for_linear(lib):
     a = _args(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY, g=ctypes.c_void_p(0x2000),
               den_out=ctypes.c_void_p(0x3000))
     assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EINVAL
+    for extra in (dict(alpha=ctypes.c_void_p(0x2000)),
+                  dict(conv_weight=ctypes.c_void_p(0x2000), conv_width=4)):
+        a = _args(den_out=ctypes.c_void_p(0x3000), **extra)
+        assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
 
 
 def test_state_init_rejects_invalid_arguments(lib):
