@@ -34,15 +34,17 @@
 //   T = X diag(g).  Wt = K^T T and R^T = T^T P^T on the matrix cores with T
 //   (and P) split into bf16 high and low parts, so both keep fp32-level
 //   accuracy before the final rounding.  Stored in the input precision:
-//   per chunk [Wt: DK x C][R: C x C].
+//   per chunk [Wt: DK x C][R: C x C], each in operand-fragment order
+//   (frag_off), so a wave's fragment is one contiguous 1 KiB block.
 // seq_kernel, one workgroup (4 waves) per (head, slice of W value columns):
 //   per chunk, wave (row block rb, column group): X^T = S'^T K^T and
 //   Z^T = S'^T Q^T from a T-precision copy S' of the fp32 state; Y = V - X
 //   into LDS; O^T = Z^T + Y^T R^T, stored straight from registers; the
 //   state rows the wave owns: S += Wt Y (fp32 accumulators, never rounded).
-//   The chunk's k, q, Wt and R are contiguous blocks; they are loaded two
-//   chunks ahead with whole-cache-line 16-byte loads into registers and
-//   staged into a double-buffered LDS tile; a chunk costs two barriers.
+//   No wave reads another's k, q, R or Wt rows, so these go from memory
+//   straight into operand registers, two chunks ahead (three register
+//   sets); LDS carries only what the waves exchange, Y and S'.  A chunk
+//   costs two barriers.
 //
 // Workgroups of one head's slices read the same q, k, R, Wt: the launch maps
 // them onto one XCD (consecutive workgroup ids alternate XCDs) so those
@@ -81,6 +83,8 @@ struct DCfg {
   static constexpr int QCB = DK / VEC;  // 16-byte blocks per q/k row
   static constexpr size_t WT = (size_t)DK * C;     // Wt elements per chunk
   static constexpr size_t REC = WT + (size_t)C * C;  // workspace elements per chunk
+  // register sets of seq_kernel operands (chunks in flight + 1)
+  static constexpr int NSET = sizeof(T) == 2 ? 3 : 2;
   static_assert(NRB >= 1 && NGRP >= 1 && NGRP * NRB == kWaves, "row blocks");
   static_assert(TW >= 1 && TW * NGRP == NCT, "column tiles");
   static_assert(FPW >= 1 && FPW * kWaves == NFT, "state tiles");
@@ -127,6 +131,19 @@ template <typename T>
 __device__ __forceinline__ void split2(float x, T &hi, T &lo) {
   hi = from_f32<T>(x);
   lo = from_f32<T>(x - to_f32(hi));
+}
+
+// Element offset of entry (row, col) of a chunk's Wt [DK x C] or R [C x C]
+// within its part of the record, in operand-fragment order: 16-row tile,
+// then 32-column k-step, then lane (lg * 16 + li holds row 16 tile + li,
+// columns 32 ks + 8 lg .. +7), then those 8 elements.  A wave's fragment of
+// one (tile, k-step) is then 64 lanes x 8 contiguous elements, which
+// seq_kernel loads straight into registers with whole-line loads.
+template <class CF>
+__device__ __forceinline__ size_t frag_off(int row, int col) {
+  const int w = col & 31;
+  return ((((size_t)(row >> 4) * CF::KSC + (col >> 5)) * 64 + (w >> 3) * 16 + (row & 15))
+          << 3) + (w & 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -349,8 +366,8 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
         mma(acc, a, kf);
       }
     }
-    // lane holds W[i = 16 ti + 4 lg + r][f = 16 tf + li]
-    store4_t(out + (size_t)(16 * tf + li) * C + 16 * ti + 4 * lg, acc);
+    // lane holds W[i = 16 ti + 4 lg + r][f = 16 tf + li], i.e. Wt[f][i..i+3]
+    store4_t(out + frag_off<CF>(16 * tf + li, 16 * ti + 4 * lg), acc);
   }
   if (decay) {  // R takes T itself
     __syncthreads();
@@ -388,114 +405,121 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
           mma(acc, al, bh_);
         }
       }
-      // lane holds R^T[m = 16 tm + 4 lg + r][i]
-      store4_t(Rw + (size_t)i * C + 16 * tm + 4 * lg, acc);
+      // lane holds R^T[m = 16 tm + 4 lg + r][i], i.e. R[i][m..m+3]
+      store4_t(Rw + frag_off<CF>(i, 16 * tm + 4 * lg), acc);
     }
     // tiles of R above the diagonal are zero
     for (int tm = rb + 1; tm < NRB; ++tm)
-      store4_t(Rw + (size_t)i * C + 16 * tm + 4 * lg, (f32x4){0.f, 0.f, 0.f, 0.f});
+      store4_t(Rw + frag_off<CF>(i, 16 * tm + 4 * lg), (f32x4){0.f, 0.f, 0.f, 0.f});
   }
 }
 
 // ---------------------------------------------------------------------------
 // seq_kernel
 // ---------------------------------------------------------------------------
-// A chunk's operands as LDS tiles (row strides padded so that 16-lane
-// fragment reads of 16 rows hit distinct banks).
-template <class CF>
-struct alignas(16) SeqTiles {
-  using T = typename CF::type;
-  T K[CF::C * CF::QLD];    // k rows
-  T Q[CF::C * CF::QLD];    // q rows
-  T Wt[CF::DK * CF::TLD];  // Wt rows (features f, tokens contiguous)
-  T R[CF::C * CF::TLD];    // R rows
-};
-
+// LDS of seq_kernel: only what the waves exchange each chunk (row strides
+// padded so that 16-lane fragment reads of 16 rows hit distinct banks).
 template <class CF>
 struct alignas(16) SmemSeq {
   using T = typename CF::type;
-  SeqTiles<CF> tile[2];    // double buffer: chunk c and chunk c + 1
   T Ys[CF::C * CF::YLD];   // Y = V - K S- rows (this slice's columns)
   T St[CF::W * CF::QLD];   // S'^T: T-precision copy of the fp32 state slice
 };
 
-// One chunk's k, q, Wt and R as 16-byte blocks, this thread's share; the
-// blocks are contiguous in memory, so every load instruction of a wave
-// covers whole cache lines.
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> { using type = bf16x4; };
+template <> struct Vec4<float> { using type = f32x4; };
+
+// One chunk's operands of one wave, in registers.  No wave reads another's
+// k, q, R or Wt rows, so they go from memory straight into operand
+// fragments: k and q of the wave's 16 tokens (features 32 ks + 8 lg .. +7 of
+// token 16 rb + li, the B operand of S'^T K^T and S'^T Q^T), the R rows of
+// those tokens (record blocks (rb, ks)), the Wt rows of the wave's state row
+// tiles (blocks (tf, ks)), the four v values of the lane's token, and the
+// decay products b of the lane's token and of the chunk's last token.
 template <class CF>
-struct SeqRegs {
-  static constexpr int NQ = CF::C * CF::QCB / kThreads;              // q (and k) blocks
-  static constexpr int NW = CF::DK * (CF::C / CF::VEC) / kThreads;   // Wt blocks
-  static constexpr int NR = CF::C * (CF::C / CF::VEC) / kThreads;    // R blocks
-  static_assert(NQ * kThreads == CF::C * CF::QCB && NW * kThreads == CF::DK * CF::C / CF::VEC &&
-                    NR * kThreads == CF::C * CF::C / CF::VEC,
-                "blocks per thread");
-  typename CF::vec k[NQ], q[NQ], w[NW], r[NR];
+struct SeqOps {
+  using T = typename CF::type;
+  Frag<T> k[CF::KSD], q[CF::KSD], r[CF::KSC], w[CF::FPW][CF::KSC];
+  typename Vec4<T>::type v[CF::TW];  // as loaded: converted where used, so
+                                     // no instruction touches it in flight
+  float b_tok, b_last;
 };
 
-template <class CF, bool VK>
-__device__ __forceinline__ void seq_load(SeqRegs<CF> &R, const PrefillParams &p,
-                                         const __amdgpu_buffer_rsrc_t (&rs)[5], int chunk) {
+// Four consecutive T (8 bytes bf16, 16 bytes fp32) as loaded.
+__device__ __forceinline__ bf16x4 buf_load4_raw(__amdgpu_buffer_rsrc_t r, uint32_t off, bf16 *) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ f32x4 buf_load4_raw(__amdgpu_buffer_rsrc_t r, uint32_t off, float *) {
+  return buf_load16<float>(r, off);
+}
+
+// 8 contiguous record elements at byte offset `off` as a fragment (zero
+// past the resource).
+__device__ __forceinline__ void load_rec_frag(Frag<bf16> &f, __amdgpu_buffer_rsrc_t r,
+                                              uint32_t off) {
+  f.v = buf_load16<bf16>(r, off);
+}
+__device__ __forceinline__ void load_rec_frag(Frag<float> &f, __amdgpu_buffer_rsrc_t r,
+                                              uint32_t off) {
+  const f32x4 a = buf_load16<float>(r, off), b = buf_load16<float>(r, off + 16u);
+  f.v = (f32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Issue the loads of chunk `chunk`'s operands for this wave (nothing waits
+// here).  Chunks past the end read as zeros: tokens past N fail the bounds,
+// records past the last chunk lie past the workspace resource.
+template <class CF, bool VK, bool DECAY>
+__device__ __forceinline__ void seq_fetch(SeqOps<CF> &o, const PrefillParams &p,
+                                          const __amdgpu_buffer_rsrc_t (&rs)[5],
+                                          __amdgpu_buffer_rsrc_t rdec, int chunk, int n0,
+                                          int wv, int rb, int ct0, int lane) {
   using T = typename CF::type;
-  using Reg = SeqRegs<CF>;
-  constexpr int C = CF::C, VEC = CF::VEC;
-  const int tid = threadIdx.x;
-  const int c0 = chunk * C;
+  constexpr int C = CF::C;
+  const int li = lane & 15, lg = lane >> 4;
+  const int t = chunk * C + 16 * rb + li;
+  const bool tok_ok = t < p.N;
 #pragma unroll
-  for (int m = 0; m < Reg::NQ; ++m) {
-    const int b = tid + m * kThreads;
-    const int row = b / CF::QCB, col0 = (b % CF::QCB) * VEC;
-    const int t = c0 + row;
+  for (int ks = 0; ks < CF::KSD; ++ks) {
+    load_frag8<T, VK>(o.k[ks], rs[1], t, 32 * ks + 8 * lg, p.d, tok_ok);
+    load_frag8<T, VK>(o.q[ks], rs[0], t, 32 * ks + 8 * lg, p.d, tok_ok);
+  }
+  const uint32_t base = (uint32_t)((size_t)chunk * CF::REC * sizeof(T));
+#pragma unroll
+  for (int ks = 0; ks < CF::KSC; ++ks) {
+    // (blocks of keys past the row block are zero; loaded anyway, so the
+    // number of loads in flight does not depend on the wave)
+    load_rec_frag(o.r[ks], rs[2],
+                    base + (uint32_t)((CF::WT + ((size_t)(rb * CF::KSC + ks) * 64 + lane) * 8) *
+                                      sizeof(T)));
+#pragma unroll
+    for (int a = 0; a < CF::FPW; ++a)
+      load_rec_frag(o.w[a][ks], rs[2],
+                    base + (uint32_t)((((size_t)((wv * CF::FPW + a) * CF::KSC + ks) * 64 + lane) *
+                                       8) * sizeof(T)));
+  }
+#pragma unroll
+  for (int b2 = 0; b2 < CF::TW; ++b2) {
+    const int col = n0 + 16 * (ct0 + b2) + 4 * lg;
     if constexpr (VK) {
-      const uint32_t off = (t < p.N && col0 < p.d)
-                               ? (uint32_t)(((size_t)t * p.d + col0) * sizeof(T)) : kOOB;
-      R.k[m] = buf_load16<T>(rs[1], off);
-      R.q[m] = buf_load16<T>(rs[0], off);
+      o.v[b2] = buf_load4_raw(rs[3], tok_ok && col < p.dv
+                                         ? (uint32_t)(((size_t)t * p.dv + col) * sizeof(T))
+                                         : kOOB,
+                              (T *)nullptr);
     } else {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const uint32_t off = (t < p.N && col0 + e < p.d)
-                                 ? (uint32_t)(((size_t)t * p.d + col0 + e) * sizeof(T)) : kOOB;
-        R.k[m][e] = buf_load1(rs[1], off, (T *)nullptr);
-        R.q[m][e] = buf_load1(rs[0], off, (T *)nullptr);
+      for (int e = 0; e < 4; ++e) {
+        const bool ok = tok_ok && col + e < p.dv;
+        o.v[b2][e] = buf_load1(
+            rs[3], ok ? (uint32_t)(((size_t)t * p.dv + col + e) * sizeof(T)) : kOOB, (T *)nullptr);
       }
     }
   }
-  // chunk record [Wt: DK x C][R: C x C], contiguous and always whole (a
-  // chunk past the end reads as zeros: offsets past the resource)
-  const uint32_t base = (uint32_t)((size_t)chunk * CF::REC * sizeof(T));
-#pragma unroll
-  for (int m = 0; m < Reg::NW; ++m)
-    R.w[m] = buf_load16<T>(rs[2], base + (uint32_t)(tid + m * kThreads) * 16u);
-#pragma unroll
-  for (int m = 0; m < Reg::NR; ++m)
-    R.r[m] = buf_load16<T>(rs[2], base + (uint32_t)(CF::WT * sizeof(T)) +
-                                      (uint32_t)(tid + m * kThreads) * 16u);
-}
-
-template <class CF>
-__device__ __forceinline__ void seq_commit(const SeqRegs<CF> &R, SeqTiles<CF> &tl) {
-  using V = typename CF::vec;
-  using Reg = SeqRegs<CF>;
-  constexpr int C = CF::C, VEC = CF::VEC;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int m = 0; m < Reg::NQ; ++m) {
-    const int b = tid + m * kThreads;
-    const int row = b / CF::QCB, col0 = (b % CF::QCB) * VEC;
-    *reinterpret_cast<V *>(tl.K + row * CF::QLD + col0) = R.k[m];
-    *reinterpret_cast<V *>(tl.Q + row * CF::QLD + col0) = R.q[m];
-  }
-  constexpr int CB = C / VEC;  // 16-byte blocks per Wt / R row
-#pragma unroll
-  for (int m = 0; m < Reg::NW; ++m) {
-    const int b = tid + m * kThreads;
-    *reinterpret_cast<V *>(tl.Wt + (b / CB) * CF::TLD + (b % CB) * VEC) = R.w[m];
-  }
-#pragma unroll
-  for (int m = 0; m < Reg::NR; ++m) {
-    const int b = tid + m * kThreads;
-    *reinterpret_cast<V *>(tl.R + (b / CB) * CF::TLD + (b % CB) * VEC) = R.r[m];
+  if constexpr (DECAY) {
+    o.b_tok = buf_load1(rdec, (uint32_t)((chunk * C + 16 * rb + li) * 4), (float *)nullptr);
+    o.b_last = buf_load1(rdec, (uint32_t)((chunk * C + C - 1) * 4), (float *)nullptr);
+  } else {
+    o.b_tok = o.b_last = 1.f;
   }
 }
 
@@ -503,7 +527,7 @@ template <class CF, bool VK, bool DECAY>
 __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nslices,
                                                        int xcd_map) {
   using T = typename CF::type;
-  constexpr int C = CF::C, W = CF::W;
+  constexpr int C = CF::C, W = CF::W, NS = CF::NSET;
   __shared__ SmemSeq<CF> sm;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -537,11 +561,18 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
     rs[4] = buf_rsrc(reinterpret_cast<const T *>(p.o) + (size_t)bh * vo, (uint32_t)(vo * sizeof(T)));
   }
   // decay products b_j of every chunk of this head (written by prep)
-  constexpr bool decay = DECAY;  // a decay alpha was given
   const __amdgpu_buffer_rsrc_t rdec = buf_rsrc(
       reinterpret_cast<const float *>(reinterpret_cast<const T *>(p.ws) +
                                       (size_t)p.BH * nch * CF::REC) + (size_t)bh * nch * C,
       (uint32_t)((size_t)nch * C * sizeof(float)));
+
+  // Operands run NS - 1 chunks ahead: register set u serves chunks
+  // u, u + NS, u + 2 NS, ... (the loop is unrolled by NS so every set index
+  // is static) and is refilled with chunk c + NS as soon as chunk c is done.
+  SeqOps<CF> set[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u)
+    seq_fetch<CF, VK, DECAY>(set[u], p, rs, rdec, u, n0, wv, rb, ct0, lane);
 
   // fp32 state slice: wave holds row tiles tf = wv * FPW + a, every column tile
   f32x4 Sacc[CF::FPW][CF::NCT];
@@ -557,48 +588,6 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
         Sacc[a][c][r] = (S0 && f < d && n < dv) ? S0[(size_t)f * dv + n] : 0.f;
       }
     }
-  // Operands run two chunks ahead: register set u holds the k, q, Wt, R
-  // blocks of chunk c + 2 while LDS tile u holds chunk c (the loop is
-  // unrolled by two so every buffer index is static).  The v values a lane
-  // needs (four consecutive columns of its token) ride along in registers.
-  // No branch guards a load: chunks past the end read as zeros, and a step
-  // on zeros leaves the state unchanged and stores nothing.
-  SeqRegs<CF> set[2];
-  f32x4 vset[2][CF::TW];
-  auto load_v = [&](f32x4 (&vv)[CF::TW], int chunk) {
-    const int t = chunk * C + 16 * rb + li;
-#pragma unroll
-    for (int b2 = 0; b2 < CF::TW; ++b2) {
-      const int col = n0 + 16 * (ct0 + b2) + 4 * lg;
-      if constexpr (VK) {
-        vv[b2] = buf_load4(rs[3], t < N && col < dv ? (uint32_t)(((size_t)t * dv + col) * sizeof(T))
-                                                     : kOOB, (T *)nullptr);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = t < N && col + e < dv;
-          vv[b2][e] = to_f32(buf_load1(
-              rs[3], ok ? (uint32_t)(((size_t)t * dv + col + e) * sizeof(T)) : kOOB, (T *)nullptr));
-        }
-      }
-    }
-  };
-  seq_load<CF, VK>(set[0], p, rs, 0);
-  seq_commit<CF>(set[0], sm.tile[0]);
-  load_v(vset[0], 0);
-  seq_load<CF, VK>(set[1], p, rs, 1);
-  load_v(vset[1], 1);
-  // b of this lane's token and of the chunk's last token, two chunks ahead
-  // like v (past the end they read as zero and are not used)
-  float bset[2][2] = {{1.f, 1.f}, {1.f, 1.f}};
-  auto load_b = [&](float (&bb)[2], int chunk) {
-    if (decay) {
-      bb[0] = buf_load1(rdec, (uint32_t)((chunk * C + 16 * rb + li) * 4), (float *)nullptr);
-      bb[1] = buf_load1(rdec, (uint32_t)((chunk * C + C - 1) * 4), (float *)nullptr);
-    }
-  };
-  load_b(bset[0], 0);
-  load_b(bset[1], 1);
 #pragma unroll
   for (int a = 0; a < CF::FPW; ++a)
 #pragma unroll
@@ -607,115 +596,107 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
                  Sacc[a][c][0], Sacc[a][c][1], Sacc[a][c][2], Sacc[a][c][3]);
   __syncthreads();
 
-  for (int cb = 0; cb < nch; cb += 2) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = cb + u;
-      const SeqTiles<CF> &tl = sm.tile[u];
-      seq_load<CF, VK>(set[u], p, rs, c + 2);
-      const float b_tok = bset[u][0], b_last = bset[u][1];
-      load_b(bset[u], c + 2);
-      const int t = c * C + 16 * rb + li;  // this lane's token
-      const bool tok_ok = t < N;
+  auto step = [&](SeqOps<CF> &op, const int c) {
+    const int t = c * C + 16 * rb + li;  // this lane's token
+    const bool tok_ok = t < N;
 
-      // ---- X^T = S'^T K^T, Z^T = S'^T Q^T (rows n, columns: this row block) ----
-      f32x4 X[CF::TW], Z[CF::TW];
+    // ---- X^T = S'^T K^T, Z^T = S'^T Q^T (rows n, columns: this row block) ----
+    f32x4 X[CF::TW], Z[CF::TW];
+#pragma unroll
+    for (int b2 = 0; b2 < CF::TW; ++b2) {
+      X[b2] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      Z[b2] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < CF::KSD; ++ks) {
 #pragma unroll
       for (int b2 = 0; b2 < CF::TW; ++b2) {
-        X[b2] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        Z[b2] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        Frag<T> sf;
+        lds_frag(sf, sm.St + (16 * (ct0 + b2) + li) * CF::QLD + 32 * ks + 8 * lg);
+        mma(X[b2], sf, op.k[ks]);
+        mma(Z[b2], sf, op.q[ks]);
       }
-#pragma unroll
-      for (int ks = 0; ks < CF::KSD; ++ks) {
-        Frag<T> kf, qf;
-        lds_frag(kf, tl.K + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
-        lds_frag(qf, tl.Q + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
-#pragma unroll
-        for (int b2 = 0; b2 < CF::TW; ++b2) {
-          Frag<T> sf;
-          lds_frag(sf, sm.St + (16 * (ct0 + b2) + li) * CF::QLD + 32 * ks + 8 * lg);
-          mma(X[b2], sf, kf);
-          mma(Z[b2], sf, qf);
-        }
-      }
-      if (decay) {  // X and Q S- rows carry b of their token
-#pragma unroll
-        for (int b2 = 0; b2 < CF::TW; ++b2) {
-          X[b2] *= b_tok;
-          Z[b2] *= b_tok;
-        }
-      }
-      // ---- Y = V - X: lane holds columns 16 ct + 4 lg + r of token t ----
-#pragma unroll
-      for (int b2 = 0; b2 < CF::TW; ++b2)
-        lds_store4(sm.Ys + (16 * rb + li) * CF::YLD + 16 * (ct0 + b2) + 4 * lg,
-                   vset[u][b2][0] - X[b2][0], vset[u][b2][1] - X[b2][1],
-                   vset[u][b2][2] - X[b2][2], vset[u][b2][3] - X[b2][3]);
-      load_v(vset[u], c + 2);
-      __syncthreads();
-
-      // ---- O^T = Z^T + Y^T R^T (keys j <= this row block) ----
-#pragma unroll
-      for (int ks = 0; ks < CF::KSC; ++ks) {
-        if (32 * ks > 16 * rb + 15) continue;
-        Frag<T> rf;
-        lds_frag(rf, tl.R + (16 * rb + li) * CF::TLD + 32 * ks + 8 * lg);
-#pragma unroll
-        for (int b2 = 0; b2 < CF::TW; ++b2) {
-          Frag<T> yf;
-          lds_frag_tr(yf, sm.Ys, CF::YLD, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4,
-                      16 * (ct0 + b2), li);
-          mma(Z[b2], yf, rf);
-        }
-      }
+    }
+    if (DECAY) {  // X and Q S- rows carry b of their token
 #pragma unroll
       for (int b2 = 0; b2 < CF::TW; ++b2) {
-        const int col = n0 + 16 * (ct0 + b2) + 4 * lg;
-        if constexpr (VK) {
-          buf_store4_nt(rs[4],
-                        tok_ok && col < dv ? (uint32_t)(((size_t)t * dv + col) * sizeof(T)) : kOOB,
-                        Z[b2], (T *)nullptr);
-        } else {
+        X[b2] *= op.b_tok;
+        Z[b2] *= op.b_tok;
+      }
+    }
+    // ---- Y = V - X: lane holds columns 16 ct + 4 lg + r of token t ----
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool oke = tok_ok && col + e < dv;
-            buf_store1(rs[4], oke ? (uint32_t)(((size_t)t * dv + col + e) * sizeof(T)) : kOOB,
-                       from_f32<T>(Z[b2][e]));
-          }
+    for (int b2 = 0; b2 < CF::TW; ++b2)
+      lds_store4(sm.Ys + (16 * rb + li) * CF::YLD + 16 * (ct0 + b2) + 4 * lg,
+                 to_f32(op.v[b2][0]) - X[b2][0], to_f32(op.v[b2][1]) - X[b2][1],
+                 to_f32(op.v[b2][2]) - X[b2][2], to_f32(op.v[b2][3]) - X[b2][3]);
+    __syncthreads();
+
+    // ---- O^T = Z^T + Y^T R^T (keys j <= this row block) ----
+#pragma unroll
+    for (int ks = 0; ks < CF::KSC; ++ks) {
+      if (32 * ks > 16 * rb + 15) continue;
+#pragma unroll
+      for (int b2 = 0; b2 < CF::TW; ++b2) {
+        Frag<T> yf;
+        lds_frag_tr(yf, sm.Ys, CF::YLD, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4,
+                    16 * (ct0 + b2), li);
+        mma(Z[b2], yf, op.r[ks]);
+      }
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < CF::TW; ++b2) {
+      const int col = n0 + 16 * (ct0 + b2) + 4 * lg;
+      if constexpr (VK) {
+        buf_store4_nt(rs[4],
+                      tok_ok && col < dv ? (uint32_t)(((size_t)t * dv + col) * sizeof(T)) : kOOB,
+                      Z[b2], (T *)nullptr);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool oke = tok_ok && col + e < dv;
+          buf_store1(rs[4], oke ? (uint32_t)(((size_t)t * dv + col + e) * sizeof(T)) : kOOB,
+                     from_f32<T>(Z[b2][e]));
         }
       }
-      // ---- S+ = b_L S- + Wt Y for this wave's state rows; T-precision copy ----
-      if (decay && c < nch) {
-#pragma unroll
-        for (int a = 0; a < CF::FPW; ++a)
-#pragma unroll
-          for (int c2 = 0; c2 < CF::NCT; ++c2) Sacc[a][c2] *= b_last;
-      }
-#pragma unroll
-      for (int ks = 0; ks < CF::KSC; ++ks) {
-        Frag<T> wf[CF::FPW];
-#pragma unroll
-        for (int a = 0; a < CF::FPW; ++a)
-          lds_frag(wf[a], tl.Wt + (16 * (wv * CF::FPW + a) + li) * CF::TLD + 32 * ks + 8 * lg);
-#pragma unroll
-        for (int c2 = 0; c2 < CF::NCT; ++c2) {
-          Frag<T> yf;
-          lds_frag_tr(yf, sm.Ys, CF::YLD, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * c2, li);
-#pragma unroll
-          for (int a = 0; a < CF::FPW; ++a) mma(Sacc[a][c2], wf[a], yf);
-        }
-      }
+    }
+    // ---- S+ = b_L S- + Wt Y for this wave's state rows; T-precision copy ----
+    if (DECAY) {
 #pragma unroll
       for (int a = 0; a < CF::FPW; ++a)
 #pragma unroll
-        for (int c2 = 0; c2 < CF::NCT; ++c2)
-          lds_store4(sm.St + (16 * c2 + li) * CF::QLD + 16 * (wv * CF::FPW + a) + 4 * lg,
-                     Sacc[a][c2][0], Sacc[a][c2][1], Sacc[a][c2][2], Sacc[a][c2][3]);
-      // chunk c + 1's tiles into the other buffer (last read in chunk c - 1)
-      seq_commit<CF>(set[u ^ 1], sm.tile[u ^ 1]);
-      __syncthreads();
+        for (int c2 = 0; c2 < CF::NCT; ++c2) Sacc[a][c2] *= op.b_last;
     }
+#pragma unroll
+    for (int ks = 0; ks < CF::KSC; ++ks) {
+#pragma unroll
+      for (int c2 = 0; c2 < CF::NCT; ++c2) {
+        Frag<T> yf;
+        lds_frag_tr(yf, sm.Ys, CF::YLD, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * c2, li);
+#pragma unroll
+        for (int a = 0; a < CF::FPW; ++a) mma(Sacc[a][c2], op.w[a][ks], yf);
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < CF::FPW; ++a)
+#pragma unroll
+      for (int c2 = 0; c2 < CF::NCT; ++c2)
+        lds_store4(sm.St + (16 * c2 + li) * CF::QLD + 16 * (wv * CF::FPW + a) + 4 * lg,
+                   Sacc[a][c2][0], Sacc[a][c2][1], Sacc[a][c2][2], Sacc[a][c2][3]);
+    seq_fetch<CF, VK, DECAY>(op, p, rs, rdec, c + NS, n0, wv, rb, ct0, lane);
+    __syncthreads();
+  };
+  // Whole groups of NS chunks without a branch between them: every load of
+  // a register set is then followed by the loads of the other NS - 1 sets
+  // before its use, and the compiler's wait counts let those stay in flight.
+  int cb = 0;
+  for (; cb + NS <= nch; cb += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) step(set[u], cb + u);
   }
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u)
+    if (cb + u < nch) step(set[u], cb + u);
 
   if (p.S_out) {
     float *So = p.S_out + (size_t)bh * d * dv;

@@ -114,6 +114,11 @@ struct Cfg {
   static constexpr int SROWS = DV + 16;           // rows of the S'^T copy
   // resident waves per SIMD the register allocation must allow
   static constexpr int WPE = sizeof(T) == 4 ? 1 : (NW <= 4 ? 3 : 2);
+  // chunks whose k, v rows summary_kernel keeps in flight: eight-wave bf16
+  // workgroups (d or dv of 128) run at most one per CU on long sequences,
+  // where a second chunk in flight measured 6% faster; four-wave ones keep
+  // one (a deeper prefetch measured slower there).
+  static constexpr int PD = (sizeof(T) == 2 && NW == 8) ? 2 : 1;
   static_assert(NG >= 1 && NPW >= 1 && NPW * NG == NVT, "output tiling");
   static_assert(FPW * NW == NFT || NWC * NFT == NW, "state tiling");
   static_assert(NRB % 2 == 0, "chunk must hold an even number of row blocks");
@@ -1041,8 +1046,14 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
   const int t_end = t_begin + p.seg_len;
   const bool decay = p.gamma != nullptr;
 
-  ChunkRegs<CF> R;
-  prefetch<CF, false, VK>(R, p, hb, t_begin, CF::C);
+  // k and v rows of the next PD chunks are in flight while one is reduced
+  // (CF::PD; the per-channel decay and the convolution keep one chunk).
+  constexpr int PD = (CH || CV) ? 1 : CF::PD;
+  ChunkRegs<CF> R[PD];
+#pragma unroll
+  for (int u = 0; u < PD; ++u)
+    if (t_begin + u * CF::C < t_end)
+      prefetch<CF, false, VK>(R[u], p, hb, t_begin + u * CF::C, CF::C);
   [[maybe_unused]] ChanRegs<CF> A;
   [[maybe_unused]] const __amdgpu_buffer_rsrc_t ra =
       CH ? buf_rsrc(p.alpha + (size_t)bh * p.N * d, (uint32_t)((size_t)p.N * d * 4)) : hb.q;
@@ -1065,24 +1076,30 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
     for (int b = 0; b < CF::TPW; ++b) Sacc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   const float gC = sm.pw[CF::C];
-  for (int c0 = t_begin; c0 < t_end; c0 += CF::C) {
-    if constexpr (CH) {
-      chan_logs<CF>(A, sc, d, CF::C);
+  for (int c0 = t_begin; c0 < t_end; c0 += PD * CF::C) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {  // register set u holds chunk c0 + u C
+      const int cc = c0 + u * CF::C;
+      if (cc >= t_end) break;
+      if constexpr (CH) {
+        chan_logs<CF>(A, sc, d, CF::C);
+        __syncthreads();
+        chan_prefix<CF>(sc, CF::C, true);
+        __syncthreads();
+      }
+      commit<CF, false, CH, CV>(R[u], nullptr, sm.Ks, sm.Vs, sm.pw, p, CF::C,
+                                chan_ptr<CF>(sc), conv_ptr<CF>(cs));
+      if constexpr (CH) {
+        chan_scale<CF>(Sacc, sc.bm, wv, lg);
+        if (cc + CF::C < t_end) chan_prefetch<CF, VK>(A, ra, p, cc + CF::C, CF::C);
+      }
+      if (cc + PD * CF::C < t_end)
+        prefetch<CF, false, VK>(R[u], p, hb, cc + PD * CF::C, CF::C);
       __syncthreads();
-      chan_prefix<CF>(sc, CF::C, true);
+      state_update<CF>(Sacc, sm.Ks, sm.Vs, gC, decay, wv, li, lg);
+      if constexpr (CH) chan_scale<CF>(Sacc, sc.bl, wv, lg);
       __syncthreads();
     }
-    commit<CF, false, CH, CV>(R, nullptr, sm.Ks, sm.Vs, sm.pw, p, CF::C, chan_ptr<CF>(sc),
-                              conv_ptr<CF>(cs));
-    if constexpr (CH) {
-      chan_scale<CF>(Sacc, sc.bm, wv, lg);
-      if (c0 + CF::C < t_end) chan_prefetch<CF, VK>(A, ra, p, c0 + CF::C, CF::C);
-    }
-    if (c0 + CF::C < t_end) prefetch<CF, false, VK>(R, p, hb, c0 + CF::C, CF::C);
-    __syncthreads();
-    state_update<CF>(Sacc, sm.Ks, sm.Vs, gC, decay, wv, li, lg);
-    if constexpr (CH) chan_scale<CF>(Sacc, sc.bl, wv, lg);
-    __syncthreads();
   }
   float *dst = p.ws + ((size_t)(seg + 1) * p.BH + bh) * ws_rec(d, dv);
   store_state<CF>(Sacc, dst, dst + (size_t)d * dv, d, dv, wv, li, lg);
