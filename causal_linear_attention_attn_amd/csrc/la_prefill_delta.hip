@@ -41,10 +41,10 @@
 //   Z^T = S'^T Q^T from a T-precision copy S' of the fp32 state; Y = V - X
 //   into LDS; O^T = Z^T + Y^T R^T, stored straight from registers; the
 //   state rows the wave owns: S += Wt Y (fp32 accumulators, never rounded).
-//   No wave reads another's k, q, R or Wt rows, so these go from memory
-//   straight into operand registers, two chunks ahead (three register
-//   sets); LDS carries only what the waves exchange, Y and S'.  A chunk
-//   costs two barriers.
+//   No wave reads another's R or Wt rows, so these go from memory straight
+//   into operand registers, two chunks ahead (three register sets); k and
+//   q are loaded as whole-line blocks with them and staged through LDS (a
+//   k/q fragment would span 16 rows per load).  A chunk costs two barriers.
 //
 // Workgroups of one head's slices read the same q, k, R, Wt: the launch maps
 // them onto one XCD (consecutive workgroup ids alternate XCDs) so those
@@ -422,6 +422,8 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
 template <class CF>
 struct alignas(16) SmemSeq {
   using T = typename CF::type;
+  T K[CF::NSET][CF::C * CF::QLD];  // k rows of the chunk of register set u
+  T Q[CF::NSET][CF::C * CF::QLD];  // q rows
   T Ys[CF::C * CF::YLD];   // Y = V - K S- rows (this slice's columns)
   T St[CF::W * CF::QLD];   // S'^T: T-precision copy of the fp32 state slice
 };
@@ -430,17 +432,21 @@ template <typename T> struct Vec4;
 template <> struct Vec4<bf16> { using type = bf16x4; };
 template <> struct Vec4<float> { using type = f32x4; };
 
-// One chunk's operands of one wave, in registers.  No wave reads another's
-// k, q, R or Wt rows, so they go from memory straight into operand
-// fragments: k and q of the wave's 16 tokens (features 32 ks + 8 lg .. +7 of
-// token 16 rb + li, the B operand of S'^T K^T and S'^T Q^T), the R rows of
-// those tokens (record blocks (rb, ks)), the Wt rows of the wave's state row
-// tiles (blocks (tf, ks)), the four v values of the lane's token, and the
-// decay products b of the lane's token and of the chunk's last token.
+// One chunk's operands, in registers.  No wave reads another's R or Wt
+// rows, so those go from memory straight into operand fragments: the R rows
+// of the wave's 16 tokens (record blocks (rb, ks)) and the Wt rows of its
+// state row tiles (blocks (tf, ks)); likewise the four v values of the
+// lane's token and the decay products b of that token and of the chunk's
+// last token.  k and q are loaded as whole-line 16-byte blocks (this
+// thread's share of the workgroup's) and staged through LDS: an operand
+// fragment of them would span 16 rows per load.
 template <class CF>
 struct SeqOps {
   using T = typename CF::type;
-  Frag<T> k[CF::KSD], q[CF::KSD], r[CF::KSC], w[CF::FPW][CF::KSC];
+  static constexpr int NQ = CF::C * CF::QCB / kThreads;  // k (and q) blocks per thread
+  static_assert(NQ * kThreads == CF::C * CF::QCB, "k/q blocks per thread");
+  typename CF::vec kb[NQ], qb[NQ];  // whole-line blocks, staged to LDS
+  Frag<T> r[CF::KSC], w[CF::FPW][CF::KSC];
   typename Vec4<T>::type v[CF::TW];  // as loaded: converted where used, so
                                      // no instruction touches it in flight
   float b_tok, b_last;
@@ -479,10 +485,25 @@ __device__ __forceinline__ void seq_fetch(SeqOps<CF> &o, const PrefillParams &p,
   const int li = lane & 15, lg = lane >> 4;
   const int t = chunk * C + 16 * rb + li;
   const bool tok_ok = t < p.N;
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int ks = 0; ks < CF::KSD; ++ks) {
-    load_frag8<T, VK>(o.k[ks], rs[1], t, 32 * ks + 8 * lg, p.d, tok_ok);
-    load_frag8<T, VK>(o.q[ks], rs[0], t, 32 * ks + 8 * lg, p.d, tok_ok);
+  for (int m = 0; m < SeqOps<CF>::NQ; ++m) {
+    const int b = tid + m * kThreads;
+    const int row = chunk * C + b / CF::QCB, col0 = (b % CF::QCB) * CF::VEC;
+    if constexpr (VK) {
+      const uint32_t off = (row < p.N && col0 < p.d)
+                               ? (uint32_t)(((size_t)row * p.d + col0) * sizeof(T)) : kOOB;
+      o.kb[m] = buf_load16<T>(rs[1], off);
+      o.qb[m] = buf_load16<T>(rs[0], off);
+    } else {
+#pragma unroll
+      for (int e = 0; e < CF::VEC; ++e) {
+        const uint32_t off = (row < p.N && col0 + e < p.d)
+                                 ? (uint32_t)(((size_t)row * p.d + col0 + e) * sizeof(T)) : kOOB;
+        o.kb[m][e] = buf_load1(rs[1], off, (T *)nullptr);
+        o.qb[m][e] = buf_load1(rs[0], off, (T *)nullptr);
+      }
+    }
   }
   const uint32_t base = (uint32_t)((size_t)chunk * CF::REC * sizeof(T));
 #pragma unroll
@@ -520,6 +541,20 @@ __device__ __forceinline__ void seq_fetch(SeqOps<CF> &o, const PrefillParams &p,
     o.b_last = buf_load1(rdec, (uint32_t)((chunk * C + C - 1) * 4), (float *)nullptr);
   } else {
     o.b_tok = o.b_last = 1.f;
+  }
+}
+
+// This thread's k and q blocks of a register set into LDS tiles.
+template <class CF>
+__device__ __forceinline__ void seq_stage(const SeqOps<CF> &o, typename CF::type *K,
+                                          typename CF::type *Q) {
+  using V = typename CF::vec;
+#pragma unroll
+  for (int m = 0; m < SeqOps<CF>::NQ; ++m) {
+    const int b = threadIdx.x + m * kThreads;
+    const int row = b / CF::QCB, col0 = (b % CF::QCB) * CF::VEC;
+    *reinterpret_cast<V *>(K + row * CF::QLD + col0) = o.kb[m];
+    *reinterpret_cast<V *>(Q + row * CF::QLD + col0) = o.qb[m];
   }
 }
 
@@ -594,9 +629,14 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
     for (int c = 0; c < CF::NCT; ++c)
       lds_store4(sm.St + (16 * c + li) * CF::QLD + 16 * (wv * CF::FPW + a) + 4 * lg,
                  Sacc[a][c][0], Sacc[a][c][1], Sacc[a][c][2], Sacc[a][c][3]);
+  seq_stage<CF>(set[0], sm.K[0], sm.Q[0]);
   __syncthreads();
 
-  auto step = [&](SeqOps<CF> &op, const int c) {
+  // chunk c = (group) + u: k, q in LDS tile u; its other operands in set u.
+  // At the end of the chunk the next chunk's k, q (set u1) go to tile u1,
+  // last read two chunks earlier, and set u is refilled with chunk c + NS.
+  auto step = [&](SeqOps<CF> &op, const SeqOps<CF> &opn, const T *Kt, const T *Qt, T *Kn,
+                  T *Qn, const int c) {
     const int t = c * C + 16 * rb + li;  // this lane's token
     const bool tok_ok = t < N;
 
@@ -611,10 +651,12 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
     for (int ks = 0; ks < CF::KSD; ++ks) {
 #pragma unroll
       for (int b2 = 0; b2 < CF::TW; ++b2) {
-        Frag<T> sf;
+        Frag<T> sf, kf, qf;
+        lds_frag(kf, Kt + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
+        lds_frag(qf, Qt + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
         lds_frag(sf, sm.St + (16 * (ct0 + b2) + li) * CF::QLD + 32 * ks + 8 * lg);
-        mma(X[b2], sf, op.k[ks]);
-        mma(Z[b2], sf, op.q[ks]);
+        mma(X[b2], sf, kf);
+        mma(Z[b2], sf, qf);
       }
     }
     if (DECAY) {  // X and Q S- rows carry b of their token
@@ -683,6 +725,7 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
       for (int c2 = 0; c2 < CF::NCT; ++c2)
         lds_store4(sm.St + (16 * c2 + li) * CF::QLD + 16 * (wv * CF::FPW + a) + 4 * lg,
                    Sacc[a][c2][0], Sacc[a][c2][1], Sacc[a][c2][2], Sacc[a][c2][3]);
+    seq_stage<CF>(opn, Kn, Qn);
     seq_fetch<CF, VK, DECAY>(op, p, rs, rdec, c + NS, n0, wv, rb, ct0, lane);
     __syncthreads();
   };
@@ -692,11 +735,16 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
   int cb = 0;
   for (; cb + NS <= nch; cb += NS) {
 #pragma unroll
-    for (int u = 0; u < NS; ++u) step(set[u], cb + u);
+    for (int u = 0; u < NS; ++u) {
+      const int u1 = (u + 1) % NS;
+      step(set[u], set[u1], sm.K[u], sm.Q[u], sm.K[u1], sm.Q[u1], cb + u);
+    }
   }
 #pragma unroll
-  for (int u = 0; u < NS - 1; ++u)
-    if (cb + u < nch) step(set[u], cb + u);
+  for (int u = 0; u < NS - 1; ++u) {
+    const int u1 = (u + 1) % NS;
+    if (cb + u < nch) step(set[u], set[u1], sm.K[u], sm.Q[u], sm.K[u1], sm.Q[u1], cb + u);
+  }
 
   if (p.S_out) {
     float *So = p.S_out + (size_t)bh * d * dv;
