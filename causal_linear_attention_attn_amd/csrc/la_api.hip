@@ -250,6 +250,7 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   if (!linear) return to_status(la::launch_delta_prefill(p, bf16_io, s));
   p.nseg = plan.nseg;
   p.seg_len = plan.seg_len;
+  p.slot_vec = (a->d % 4 == 0) && aligned16(a->workspace);
   p.conv_w = a->conv_weight;
   p.conv_width = cw;
   if (cw > 1) {
@@ -341,6 +342,7 @@ int la_backward(const la_backward_args *a, void *stream) {
     fp.z_in = a->z_in;
     fp.ws = ws_f;
     fp.nseg = plan.nseg;
+    fp.slot_vec = (a->d % 4 == 0) && aligned16(ws_f);
     fp.seg_len = plan.seg_len;
     const hipError_t e = la::launch_linear_state_prefix(fp, plan, bf16_io, s);
     if (e != hipSuccess) return LA_EHIP;
@@ -374,6 +376,7 @@ int la_backward(const la_backward_args *a, void *stream) {
   p.wrec = plan.nseg > 1 ? plan.ws_bytes / sizeof(float) / ((size_t)plan.nseg * BH) : 0;
   p.nseg = plan.nseg;
   p.seg_len = plan.seg_len;
+  p.slot_vec = (a->d % 4 == 0) && aligned16(ws_f);
   return to_status(la::launch_linear_backward(p, bf16_io, s));
 }
 

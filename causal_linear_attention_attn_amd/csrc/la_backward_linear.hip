@@ -345,6 +345,33 @@ __device__ __forceinline__ void state_load(f32x4 (&Sa)[BC::SPW], const float *S,
   }
 }
 
+// The same tiles from a forward workspace slot, where S is stored
+// transposed (element (f, n) at n d + f, then z at d dv + f): a lane's four
+// rows of one column are 16 contiguous bytes (vec: d % 4 == 0 and the slot
+// is 16-byte aligned; the four rows are then all inside or all past d).
+template <class BC>
+__device__ __forceinline__ void slot_load(f32x4 (&Sa)[BC::SPW], const float *slot, int d,
+                                          int dv, bool vec, int wv, int li, int lg) {
+#pragma unroll
+  for (int i = 0; i < BC::SPW; ++i) {
+    const int st = wv + BC::NW * i;
+    const int fb = st / BC::NVP, vb = st % BC::NVP;
+    const int f = 16 * fb + 4 * lg;
+    const int c = 16 * vb + li;
+    const bool val = vb < BC::NVP - 1;
+    const bool ok = st < BC::NST && (val ? c < dv : li == 0);
+    const float *src = slot + (val ? (size_t)c * d : (size_t)d * dv) + f;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (vec) {
+      if (ok && f < d) x = *reinterpret_cast<const f32x4 *>(src);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = ok && f + r < d ? src[r] : 0.f;
+    }
+    Sa[i] = x;
+  }
+}
+
 template <class BC>
 __device__ __forceinline__ void state_store(const f32x4 (&Sa)[BC::SPW], float *S, float *z, int d,
                                             int dv, int wv, int li, int lg) {
@@ -497,16 +524,13 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
   for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
   zero_tail_columns<BC>(sm.St);
 
-  const float *S0, *z0;
-  if (p.nseg > 1) {
-    S0 = p.ws_f + ((size_t)seg * p.BH + bh) * p.wrec;
-    z0 = S0 + (size_t)d * dv;
-  } else {
-    S0 = p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr;
-    z0 = p.z_in ? p.z_in + (size_t)bh * d : nullptr;
-  }
   f32x4 Sa[BC::SPW];
-  state_load<BC>(Sa, S0, z0, d, dv, wv, li, lg);
+  if (p.nseg > 1)
+    slot_load<BC>(Sa, p.ws_f + ((size_t)seg * p.BH + bh) * p.wrec, d, dv, p.slot_vec, wv, li,
+                  lg);
+  else
+    state_load<BC>(Sa, p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr,
+                   p.z_in ? p.z_in + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
   BRegs<BC> R;
   load_chunk<BC, VK, true, true, true, true>(R, hr, t_begin, min(BC::C, N - t_begin), d, dv);
   __syncthreads();

@@ -35,6 +35,7 @@ struct PrefillParams {
   void *o;
   float *ws;
   int nseg, seg_len;
+  int slot_vec;  // workspace slots take 16-byte accesses (d % 4 == 0, ws aligned)
   // short causal convolution of q, k, v (LINEAR rule): filters [H, w, 2d+dv]
   // fp32, or nullptr; cache rows [BH, w-1, 2d+dv] of dtype T
   const float *conv_w;
@@ -62,6 +63,7 @@ struct BwdParams {
   float *ws_f, *ws_r;                // forward-state and adjoint slots
   size_t wrec;                       // floats per slot record
   int nseg, seg_len;
+  int slot_vec;                      // forward slots take 16-byte accesses
 };
 
 struct DecodeParams {

@@ -63,7 +63,8 @@
 //
 // Data layout: q, k [BH, N, d], v, o [BH, N, dv] (row-major, dtype T);
 // alpha [BH, N, d] fp32 (CH); workspace slots [nseg][BH][d*dv + 2d] fp32
-// (state, normaliser, then the segment's log decay per channel for CH).
+// (state transposed, element (f, n) at n d + f; normaliser; then the
+// segment's log decay per channel for CH).
 // Global traffic goes through buffer resources (bounds by offset, no
 // branches between a load and its use), issued one chunk ahead.
 #include <atomic>
@@ -774,6 +775,60 @@ __device__ __forceinline__ void load_state(f32x4 (&Sacc)[CF::FPW][CF::TPW], cons
   }
 }
 
+// Workspace slots hold S transposed, element (f, n) at n d + f, then z at
+// d dv + f: a lane's four rows f..f+3 of one column are then 16 contiguous
+// bytes, one vector access (vec: d % 4 == 0 and the workspace is 16-byte
+// aligned; f is a multiple of 4, so the four rows are all inside or all
+// past d).  Load this wave's [S | z] tiles from a slot.
+template <class CF>
+__device__ __forceinline__ void load_slot(f32x4 (&Sacc)[CF::FPW][CF::TPW], const float *slot,
+                                          int d, int dv, bool vec, int wv, int li, int lg) {
+#pragma unroll
+  for (int a = 0; a < CF::FPW; ++a) {
+    const int f = 16 * srow<CF>(wv, a) + 4 * lg;
+#pragma unroll
+    for (int b = 0; b < CF::TPW; ++b) {
+      const int tn = scol<CF>(wv, b);
+      const int n = 16 * tn + li;
+      // source of the lane's four values (the normaliser tile repeats z)
+      const bool ok = tn < CF::NVT ? n < dv : tn == CF::NVT;
+      const float *src = slot + (tn < CF::NVT ? (size_t)n * d : (size_t)d * dv) + f;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (vec) {
+        if (ok && f < d) x = *reinterpret_cast<const f32x4 *>(src);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = ok && f + r < d ? src[r] : 0.f;
+      }
+      Sacc[a][b] = x;
+    }
+  }
+}
+
+// Store this wave's [S | z] tiles to a slot (layout above).
+template <class CF>
+__device__ __forceinline__ void store_slot(const f32x4 (&Sacc)[CF::FPW][CF::TPW], float *slot,
+                                           int d, int dv, bool vec, int wv, int li, int lg) {
+#pragma unroll
+  for (int a = 0; a < CF::FPW; ++a) {
+    const int f = 16 * srow<CF>(wv, a) + 4 * lg;
+#pragma unroll
+    for (int b = 0; b < CF::TPW; ++b) {
+      const int tn = scol<CF>(wv, b);
+      const int n = 16 * tn + li;
+      const bool ok = tn < CF::NVT ? n < dv : (tn == CF::NVT && li == 0);
+      float *dst = slot + (tn < CF::NVT ? (size_t)n * d : (size_t)d * dv) + f;
+      if (vec) {
+        if (ok && f < d) *reinterpret_cast<f32x4 *>(dst) = Sacc[a][b];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (ok && f + r < d) dst[r] = Sacc[a][b][r];
+      }
+    }
+  }
+}
+
 // Store this wave's [S | z] tiles to an fp32 state.
 template <class CF>
 __device__ __forceinline__ void store_state(const f32x4 (&Sacc)[CF::FPW][CF::TPW], float *S1,
@@ -919,16 +974,13 @@ __global__ void __launch_bounds__(CF::NT, (CH || CV) ? wpe_at_most_2<CF>() : CF:
 
   // state entering this segment: slot seg of the scanned workspace, or
   // (S_in, z_in) with a single segment
-  const float *S0, *z0;
-  if (p.nseg > 1) {
-    S0 = p.ws + ((size_t)seg * p.BH + bh) * ws_rec(d, dv);
-    z0 = S0 + (size_t)d * dv;
-  } else {
-    S0 = p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr;
-    z0 = p.z_in ? p.z_in + (size_t)bh * d : nullptr;
-  }
   f32x4 Sacc[CF::FPW][CF::TPW];
-  load_state<CF>(Sacc, S0, z0, d, dv, wv, li, lg);
+  if (p.nseg > 1)
+    load_slot<CF>(Sacc, p.ws + ((size_t)seg * p.BH + bh) * ws_rec(d, dv), d, dv, p.slot_vec,
+                  wv, li, lg);
+  else
+    load_state<CF>(Sacc, p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr,
+                   p.z_in ? p.z_in + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
   // the first chunk's loads go out after the state loads (loads complete in
   // issue order, so waiting for the state does not wait for the chunk)
   ChunkRegs<CF> R;
@@ -1102,7 +1154,7 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
     }
   }
   float *dst = p.ws + ((size_t)(seg + 1) * p.BH + bh) * ws_rec(d, dv);
-  store_state<CF>(Sacc, dst, dst + (size_t)d * dv, d, dv, wv, li, lg);
+  store_slot<CF>(Sacc, dst, d, dv, p.slot_vec, wv, li, lg);
   if constexpr (CH) {  // the segment's log decay per channel (own thread's sum)
     if (threadIdx.x < d) dst[(size_t)d * dv + d + threadIdx.x] = sc.tot[threadIdx.x];
   }
@@ -1129,14 +1181,14 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
   for (int s = 1; s < kMaxSeg; ++s) dS[s] = s < p.nseg ? base[s * stride] : 0.f;
   [[maybe_unused]] float lgd[kMaxSeg];
   if constexpr (CH) {
-    const size_t f = e < dd ? e / p.dv : e - dd;  // the element's state row
+    const size_t f = e < dd ? e % p.d : e - dd;  // the element's state row
     const float *ld = p.ws + (size_t)bh * wr + dd + p.d + f;
 #pragma unroll
     for (int s = 1; s < kMaxSeg; ++s) lgd[s] = s < p.nseg ? ld[s * stride] : 0.f;
   }
   float acc;
-  if (e < dd)
-    acc = p.S_in ? p.S_in[(size_t)bh * dd + e] : 0.f;
+  if (e < dd)  // slot element e is S[f][n] with n = e / d, f = e % d
+    acc = p.S_in ? p.S_in[(size_t)bh * dd + (e % p.d) * p.dv + e / p.d] : 0.f;
   else
     acc = p.z_in ? p.z_in[(size_t)bh * p.d + (e - dd)] : 0.f;
   base[0] = acc;
