@@ -372,6 +372,29 @@ __device__ __forceinline__ void slot_load(f32x4 (&Sa)[BC::SPW], const float *slo
   }
 }
 
+// ... and into a slot in that layout (the adjoint's reverse slots use it too).
+template <class BC>
+__device__ __forceinline__ void slot_store(const f32x4 (&Sa)[BC::SPW], float *slot, int d,
+                                           int dv, bool vec, int wv, int li, int lg) {
+#pragma unroll
+  for (int i = 0; i < BC::SPW; ++i) {
+    const int st = wv + BC::NW * i;
+    const int fb = st / BC::NVP, vb = st % BC::NVP;
+    const int f = 16 * fb + 4 * lg;
+    const int c = 16 * vb + li;
+    const bool val = vb < BC::NVP - 1;
+    const bool ok = st < BC::NST && (val ? c < dv : li == 0);
+    float *dst = slot + (val ? (size_t)c * d : (size_t)d * dv) + f;
+    if (vec) {
+      if (ok && f < d) *reinterpret_cast<f32x4 *>(dst) = Sa[i];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (ok && f + r < d) dst[r] = Sa[i][r];
+    }
+  }
+}
+
 template <class BC>
 __device__ __forceinline__ void state_store(const f32x4 (&Sa)[BC::SPW], float *S, float *z, int d,
                                             int dv, int wv, int li, int lg) {
@@ -617,17 +640,12 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
   zero_tail_columns<BC>(sm.Sh);
 
   f32x4 Sa[BC::SPW];
-  {
-    const float *S1, *z1;
-    if (p.nseg > 1) {
-      S1 = p.ws_r + ((size_t)seg * p.BH + bh) * p.wrec;
-      z1 = S1 + (size_t)d * dv;
-    } else {
-      S1 = p.dS_out ? p.dS_out + (size_t)bh * d * dv : nullptr;
-      z1 = p.dz_out ? p.dz_out + (size_t)bh * d : nullptr;
-    }
-    state_load<BC>(Sa, S1, z1, d, dv, wv, li, lg);
-  }
+  if (p.nseg > 1)
+    slot_load<BC>(Sa, p.ws_r + ((size_t)seg * p.BH + bh) * p.wrec, d, dv, p.slot_vec, wv, li,
+                  lg);
+  else
+    state_load<BC>(Sa, p.dS_out ? p.dS_out + (size_t)bh * d * dv : nullptr,
+                   p.dz_out ? p.dz_out + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
   const int last = t_begin + ((t_end - t_begin - 1) / BC::C) * BC::C;
   BRegs<BC> R;
   load_chunk<BC, VK, true, true, true, true>(R, hr, last, min(BC::C, N - last), d, dv);
@@ -757,8 +775,8 @@ __global__ void __launch_bounds__(BC::NT) bwd_rsum_kernel(BwdParams p) {
     state_update<BC>(Sa, sm.QW, sm.dN, sm.pw[Lc], wv, li, lg);
     __syncthreads();
   }
-  float *dst = p.ws_r + ((size_t)(seg - 1) * p.BH + bh) * p.wrec;
-  state_store<BC>(Sa, dst, dst + (size_t)d * dv, d, dv, wv, li, lg);
+  slot_store<BC>(Sa, p.ws_r + ((size_t)(seg - 1) * p.BH + bh) * p.wrec, d, dv, p.slot_vec, wv,
+                 li, lg);
 }
 
 // Adjoint entering each segment from the right, in place: slot nseg-1 <-
@@ -781,8 +799,8 @@ __global__ void __launch_bounds__(256) bwd_rscan_kernel(BwdParams p) {
 #pragma unroll
   for (int s = 0; s < kMaxSegB - 1; ++s) dS[s] = s < nseg - 1 ? base[s * stride] : 0.f;
   float acc;
-  if (e < dd)
-    acc = p.dS_out ? p.dS_out[(size_t)bh * dd + e] : 0.f;
+  if (e < dd)  // slot element e is S[f][n] with n = e / d, f = e % d
+    acc = p.dS_out ? p.dS_out[(size_t)bh * dd + (e % p.d) * p.dv + e / p.d] : 0.f;
   else
     acc = p.dz_out ? p.dz_out[(size_t)bh * p.d + (e - dd)] : 0.f;
   base[(size_t)(nseg - 1) * stride] = acc;
