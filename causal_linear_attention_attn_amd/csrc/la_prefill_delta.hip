@@ -30,7 +30,8 @@
 //   K K^T and Q K^T on the matrix cores (lower tiles; the Q K^T tiles stay
 //   in registers); X = (I + N)^(-1), N = diag(g) strict_lower(K K^T), in
 //   fp32: 16x16 diagonal blocks by forward substitution, then the blocks
-//   below, block row by block row, X_ij = -X_ii sum_{j<=m<i} N_im X_mj;
+//   below, block row by block row, X_ij = -X_ii sum_{j<=m<i} N_im X_mj
+//   (fp32 matrix-core products);
 //   T = X diag(g).  Wt = K^T T and R^T = T^T P^T on the matrix cores with T
 //   (and P) split into bf16 high and low parts, so both keep fp32-level
 //   accuracy before the final rounding.  Stored in the input precision:
@@ -158,7 +159,6 @@ struct alignas(16) SmemPrep {
                                 // place X = (I + N)^(-1)
     T Tt[2][CF::C * CF::TLD];   // T^T high / low parts (after the solve)
   };
-  float Ym[CF::C * 16];       // partial products of the block solve
   float gs[CF::C];
   float lb[CF::C];            // log b_j: prefix sums of log alpha
   float wl[CF::C];            // b_L / b_j (Wt's token weights)
@@ -293,32 +293,39 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
     if ((j >> 4) > (i >> 4)) sm.Nm[i * FLD + j] = 0.f;
   }
   __syncthreads();
-  // Blocks below, block row by block row: Y_j = sum_{m=j}^{i-1} N_im X_mj
-  // reads row i of N (and finished rows of X); after a barrier, X_ij =
-  // -X_ii Y_j replaces N_ij.
-  {
-    const int r = tid >> 4, c = tid & 15;  // one element of a 16x16 block
-    for (int bi = 1; bi < NRB; ++bi) {
-      for (int bj = 0; bj < bi; ++bj) {
-        float s = 0.f;
-        for (int bm = bj; bm < bi; ++bm) {
-          const float *Nr = sm.Nm + (16 * bi + r) * FLD + 16 * bm;
-          const float *Xc = sm.Nm + (16 * bm) * FLD + 16 * bj + c;
+  // Blocks below, block row by block row, on the matrix cores in fp32
+  // (16x16x4 products, so X keeps full fp32 accuracy): wave w takes column
+  // block j = w < i; Y_j = sum_{m=j}^{i-1} N_im X_mj stays in its registers
+  // (the accumulator layout, lane (li, lg) holding rows 4 lg + r of column
+  // li, is the B operand layout of the second product); after a barrier
+  // (every read of block row i of N is done), X_ij = -X_ii Y_j replaces N_ij.
+  // A operands take the lane's four consecutive columns 4 lg .. 4 lg + 3 of
+  // row li as its k slots (one 16-byte LDS read); B operands the same k rows.
+  for (int bi = 1; bi < NRB; ++bi) {
+    const int bj = wv;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    if (bj < bi) {
+      for (int bm = bj; bm < bi; ++bm) {
+        const f32x4 a =
+            *reinterpret_cast<const f32x4 *>(sm.Nm + (16 * bi + li) * FLD + 16 * bm + 4 * lg);
 #pragma unroll
-          for (int m = 0; m < 16; ++m) s = fmaf(Nr[m], Xc[m * FLD], s);
+        for (int kk = 0; kk < 4; ++kk) {
+          const float bk = sm.Nm[(16 * bm + 4 * lg + kk) * FLD + 16 * bj + li];
+          y = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk], bk, y, 0, 0, 0);
         }
-        sm.Ym[(bj * 16 + r) * 16 + c] = s;
       }
-      __syncthreads();
-      for (int bj = 0; bj < bi; ++bj) {
-        const float *Xr = sm.Nm + (16 * bi + r) * FLD + 16 * bi;
-        float s = 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) s = fmaf(Xr[m], sm.Ym[(bj * 16 + m) * 16 + c], s);
-        sm.Nm[(16 * bi + r) * FLD + 16 * bj + c] = -s;
-      }
-      __syncthreads();
     }
+    __syncthreads();
+    if (bj < bi) {
+      const f32x4 a =
+          *reinterpret_cast<const f32x4 *>(sm.Nm + (16 * bi + li) * FLD + 16 * bi + 4 * lg);
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) x = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk], y[kk], x, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.Nm[(16 * bi + 4 * lg + r) * FLD + 16 * bj + li] = -x[r];
+    }
+    __syncthreads();
   }
 
   // ---- T^T (T = X diag(g)) as high and low parts, over X's storage (so X
