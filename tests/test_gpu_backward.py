@@ -82,6 +82,7 @@ SHAPES = [  # (B, H, N, d, dv)
     (1, 1, 1, 64, 64), (1, 2, 3, 16, 16), (2, 1, 63, 64, 64), (1, 1, 64, 64, 64),
     (1, 2, 65, 64, 64), (2, 2, 200, 128, 128), (1, 3, 130, 64, 128), (1, 2, 97, 128, 64),
     (1, 1, 17, 4, 3), (2, 1, 50, 100, 72), (1, 1, 70, 24, 40),
+    (1, 1, 130, 6, 5),  # several segments, d not a multiple of 4 (scalar slot moves)
 ]
 
 

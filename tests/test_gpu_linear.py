@@ -116,6 +116,55 @@ def test_prefill_many_segments(N):
     assert_close(z, rz, 2e-2, "z")
 
 
+@pytest.mark.parametrize("case", ["d6", "misaligned_ws"])
+def test_prefill_segments_scalar_slots(case):
+    """Several segments where the workspace slots cannot take 16-byte
+    accesses: d not a multiple of 4, or a workspace that starts 4 bytes past
+    a 16-byte boundary (the summary, scan and chunk kernels then move the
+    transposed slots element by element)."""
+    B, H, N = 1, 2, 1000
+    d, dv = (6, 5) if case == "d6" else (64, 64)
+    dtype = torch.bfloat16
+    q = _rand((B, H, N, d), dtype, 20, 0.5)
+    k = _rand((B, H, N, d), dtype, 21, 0.5)
+    v = _rand((B, H, N, dv), dtype, 22)
+    gamma = torch.tensor([0.995, 1.0], device=DEV)
+    S = _rand((B, H, d, dv), torch.float32, 23, 0.3)
+    z = _rand((B, H, d), torch.float32, 24, 0.3).abs() + 1.0
+    need = la.workspace_size(q, k, v, gamma=gamma)
+    assert need > 0
+    ws = None
+    if case == "misaligned_ws":
+        ws = torch.empty(need + 16, dtype=torch.uint8, device=DEV)[4:4 + need]
+        assert ws.data_ptr() % 16 == 4
+    o, S1, z1 = la.prefill(q, k, v, gamma=gamma, S_in=S, z_in=z, workspace=ws)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_prefill(q, k, v, gamma, 1e-6, "elu1", S, z)
+    assert_close(o, ro, 2e-2, "o")
+    assert_close(S1, rS, 2e-2, "S", axes=(-2, -1))
+    assert_close(z1, rz, 2e-2, "z")
+
+
+def test_gla_segments_scalar_slots():
+    """Per-channel decay over several segments with d not a multiple of 4:
+    the scan reads each element's row log decay from the transposed slot."""
+    B, H, N, d, dv = 1, 2, 1000, 6, 5
+    dtype = torch.bfloat16
+    q = _rand((B, H, N, d), dtype, 30, 0.5)
+    k = _rand((B, H, N, d), dtype, 31, 0.5)
+    v = _rand((B, H, N, dv), dtype, 32)
+    al = _alpha((B, H, N, d), 33, 0.9)
+    S = _rand((B, H, d, dv), torch.float32, 34, 0.3)
+    z = _rand((B, H, d), torch.float32, 35, 0.3).abs() + 1.0
+    assert la.workspace_size(q, k, v, alpha=al) > 0
+    o, S1, z1 = la.prefill(q, k, v, alpha=al, eps=1e-6, S_in=S, z_in=z)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_gla(q, k, v, al, S0=S, z0=z)
+    assert_close(o, ro, 2e-2, "o")
+    assert_close(S1, rS, 2e-2, "S", axes=(-2, -1))
+    assert_close(z1, rz, 2e-2, "z")
+
+
 def test_prefill_empty_sequence_passes_state_through():
     q = torch.empty((2, 2, 0, 8), dtype=torch.bfloat16, device=DEV)
     v = torch.empty((2, 2, 0, 4), dtype=torch.bfloat16, device=DEV)
