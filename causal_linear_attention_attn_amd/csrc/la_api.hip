@@ -222,6 +222,8 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   }
   if (ws_need > 0 && (!a->workspace || a->workspace_bytes < ws_need))
     return LA_EWORKSPACE;
+  // the delta rule moves its per-chunk records with 16-byte accesses
+  if (!linear && ws_need > 0 && !aligned16(a->workspace)) return LA_EINVAL;
 
   la::PrefillParams p{};
   p.BH = BH;

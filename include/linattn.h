@@ -138,7 +138,10 @@ typedef struct la_prefill_args {
                         (not written).  Not with alpha or conv_weight
                         (LA_EUNSUPPORTED).  DELTA: must be NULL. */
   void *workspace;   /* device scratch of workspace_bytes, caller-owned;
-                        may be NULL when la_prefill_workspace_size() is 0 */
+                        may be NULL when la_prefill_workspace_size() is 0.
+                        DELTA: 16-byte aligned (else LA_EINVAL).  LINEAR:
+                        4-byte aligned; 16-byte alignment with d % 4 == 0
+                        lets the kernels move it with vector accesses. */
   size_t workspace_bytes;
 } la_prefill_args;
 

@@ -130,6 +130,17 @@ def test_prefill_null_args_and_unsupported_grid(lib):
         ctypes.c_size_t(-1).value
 
 
+def test_delta_workspace_must_be_16_byte_aligned(lib):
+    fake = ctypes.c_void_p(0x2000)
+    a = _args(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY, g=fake)
+    need = lib.la_prefill_workspace_size(ctypes.byref(a))
+    assert 0 < need < 1 << 30
+    a.workspace, a.workspace_bytes = ctypes.c_void_p(0x4004), need
+    assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EINVAL
+    a.workspace, a.workspace_bytes = ctypes.c_void_p(0x4000), need - 1
+    assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EWORKSPACE
+
+
 def test_empty_inputs_are_noops(lib):
     for kw in (dict(B=0), dict(H=0)):
         a = _args(**kw)
