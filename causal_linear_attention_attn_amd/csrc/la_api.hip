@@ -252,6 +252,8 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   if (!linear) return to_status(la::launch_delta_prefill(p, bf16_io, s));
   p.nseg = plan.nseg;
   p.seg_len = plan.seg_len;
+  p.nsplit = plan.nsplit;
+  p.split_len = plan.split_len;
   p.slot_vec = (a->d % 4 == 0) && aligned16(a->workspace);
   p.conv_w = a->conv_weight;
   p.conv_width = cw;
@@ -344,6 +346,8 @@ int la_backward(const la_backward_args *a, void *stream) {
     fp.z_in = a->z_in;
     fp.ws = ws_f;
     fp.nseg = plan.nseg;
+    fp.nsplit = plan.nsplit;
+    fp.split_len = plan.split_len;
     fp.slot_vec = (a->d % 4 == 0) && aligned16(ws_f);
     fp.seg_len = plan.seg_len;
     const hipError_t e = la::launch_linear_state_prefix(fp, plan, bf16_io, s);
@@ -375,7 +379,7 @@ int la_backward(const la_backward_args *a, void *stream) {
   p.dz_in = a->grad_z_in;
   p.ws_f = ws_f;
   p.ws_r = ws_r;
-  p.wrec = plan.nseg > 1 ? plan.ws_bytes / sizeof(float) / ((size_t)plan.nseg * BH) : 0;
+  p.wrec = plan.nseg > 1 ? plan.wrec : 0;
   p.nseg = plan.nseg;
   p.seg_len = plan.seg_len;
   p.slot_vec = (a->d % 4 == 0) && aligned16(ws_f);

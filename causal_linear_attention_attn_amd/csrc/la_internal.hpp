@@ -16,6 +16,9 @@ struct LinearPlan {
   int per_cu;       // resident workgroups per CU
   int nseg;         // segments per sequence (>= 1)
   int seg_len;      // tokens per segment (multiple of chunk)
+  int nsplit;       // summary workgroups per segment (1 or 2)
+  int split_len;    // tokens in a segment's first summary part (nsplit 2)
+  size_t wrec;      // floats per workspace slot record
   size_t ws_bytes;  // workspace bytes
   size_t conv_off;  // byte offset of the conv cache copy (with a convolution
                     // over several segments; it ends the workspace)
@@ -35,6 +38,7 @@ struct PrefillParams {
   void *o;
   float *ws;
   int nseg, seg_len;
+  int nsplit, split_len;  // summary parts per segment, tokens in the first
   int slot_vec;  // workspace slots take 16-byte accesses (d % 4 == 0, ws aligned)
   // short causal convolution of q, k, v (LINEAR rule): filters [H, w, 2d+dv]
   // fp32, or nullptr; cache rows [BH, w-1, 2d+dv] of dtype T

@@ -1088,14 +1088,16 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
   __shared__ SmemSummary<CF> sm;
   __shared__ ChanSmem<CF, CH> sc;  // per-channel decay (CH) only
   __shared__ ConvSmem<CF, CV> cs;  // short convolution (CV) only
-  const int seg = blockIdx.x, bh = blockIdx.y;
+  // part `part` of segment `seg`: with two parts per segment the first
+  // covers split_len tokens, the second the rest (whole chunks both)
+  const int seg = blockIdx.x / p.nsplit, part = blockIdx.x % p.nsplit, bh = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const int d = p.d, dv = p.dv;
   const HeadBufs hb = head_bufs<T>(p, bh);
-  const int t_begin = seg * p.seg_len;
-  const int t_end = t_begin + p.seg_len;
+  const int t_begin = seg * p.seg_len + part * p.split_len;
+  const int t_end = part + 1 == p.nsplit ? (seg + 1) * p.seg_len : t_begin + p.split_len;
   const bool decay = p.gamma != nullptr;
 
   // k and v rows of the next PD chunks are in flight while one is reduced
@@ -1153,7 +1155,9 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
       __syncthreads();
     }
   }
-  float *dst = p.ws + ((size_t)(seg + 1) * p.BH + bh) * ws_rec(d, dv);
+  // the first part's record in slot seg + 1, the second's in slot nseg + seg
+  const int slot = part == 0 ? seg + 1 : p.nseg + seg;
+  float *dst = p.ws + ((size_t)slot * p.BH + bh) * ws_rec(d, dv);
   store_slot<CF>(Sacc, dst, d, dv, p.slot_vec, wv, li, lg);
   if constexpr (CH) {  // the segment's log decay per channel (own thread's sum)
     if (threadIdx.x < d) dst[(size_t)d * dv + d + threadIdx.x] = sc.tot[threadIdx.x];
@@ -1161,11 +1165,13 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
 }
 
 // Phase 2: prefix over segments, in place: slot 0 <- (S_in, z_in),
-// slot s <- gamma^Lseg slot (s-1) + dS_(s-1) for s >= 1 (dS_(s-1) sits in
-// slot s; with a per-channel decay the factor of row f is exp of the
-// segment's log decay of channel f, stored with dS).  One thread per record
-// element; every record is loaded before the dependent chain starts.
-template <bool CH>
+// slot s <- gamma^Lseg slot (s-1) + dS_(s-1) for s >= 1, where dS_(s-1) is
+// the contribution of segment s-1: its summary record (slot s), or with two
+// summary parts gamma^Lb A + B (A in slot s, B, the last Lb tokens, in slot
+// nseg + s - 1).  With a per-channel decay the factors of row f are exp of
+// the parts' log decays of channel f, stored with the records.  One thread
+// per record element; every record is loaded before the dependent chain.
+template <bool CH, bool TWO>
 __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
   const int bh = blockIdx.y;
   const size_t dd = (size_t)p.d * p.dv;
@@ -1173,18 +1179,31 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
   const size_t wr = ws_rec(p.d, p.dv);       // slot record stride
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= rec) return;
-  const float gL = p.gamma ? exp2f((float)p.seg_len * log2f(p.gamma[bh % p.H])) : 1.f;
+  constexpr bool two = TWO;  // two summary parts per segment (nsplit 2)
+  const float lgam = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
+  const float gL = exp2f((float)p.seg_len * lgam);
+  const float gB = exp2f((float)(p.seg_len - p.split_len) * lgam);
   float *base = p.ws + (size_t)bh * wr + e;
+  const float *bsec = p.ws + ((size_t)p.nseg * p.BH + bh) * wr + e;  // second parts
   const size_t stride = (size_t)p.BH * wr;
   float dS[kMaxSeg];
+  [[maybe_unused]] float dB[TWO ? kMaxSeg : 1];
 #pragma unroll
-  for (int s = 1; s < kMaxSeg; ++s) dS[s] = s < p.nseg ? base[s * stride] : 0.f;
+  for (int s = 1; s < kMaxSeg; ++s) {
+    dS[s] = s < p.nseg ? base[s * stride] : 0.f;
+    if constexpr (TWO) dB[s] = s < p.nseg ? bsec[(s - 1) * stride] : 0.f;
+  }
   [[maybe_unused]] float lgd[kMaxSeg];
+  [[maybe_unused]] float lgb[TWO ? kMaxSeg : 1];
   if constexpr (CH) {
     const size_t f = e < dd ? e % p.d : e - dd;  // the element's state row
     const float *ld = p.ws + (size_t)bh * wr + dd + p.d + f;
+    const float *lb = p.ws + ((size_t)p.nseg * p.BH + bh) * wr + dd + p.d + f;
 #pragma unroll
-    for (int s = 1; s < kMaxSeg; ++s) lgd[s] = s < p.nseg ? ld[s * stride] : 0.f;
+    for (int s = 1; s < kMaxSeg; ++s) {
+      lgd[s] = s < p.nseg ? ld[s * stride] : 0.f;
+      if constexpr (TWO) lgb[s] = s < p.nseg ? lb[(s - 1) * stride] : 0.f;
+    }
   }
   float acc;
   if (e < dd)  // slot element e is S[f][n] with n = e / d, f = e % d
@@ -1195,12 +1214,29 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
 #pragma unroll
   for (int s = 1; s < kMaxSeg; ++s) {
     if (s < p.nseg) {
-      float g = gL;
-      if constexpr (CH) g = __expf(lgd[s]);
-      acc = fmaf(g, acc, dS[s]);
+      float g = gL, seg_part = dS[s];
+      if constexpr (TWO) {
+        float gb = gB;
+        if constexpr (CH) {
+          g = __expf(lgd[s] + lgb[s]);
+          gb = __expf(lgb[s]);
+        }
+        seg_part = fmaf(gb, seg_part, dB[s]);
+      } else if constexpr (CH) {
+        g = __expf(lgd[s]);
+      }
+      acc = fmaf(g, acc, seg_part);
       base[s * stride] = acc;
     }
   }
+}
+
+template <bool CH>
+hipError_t launch_scan(const PrefillParams &p, hipStream_t s) {
+  const size_t rec = (size_t)p.d * p.dv + p.d;
+  const dim3 grid((unsigned)((rec + 255) / 256), p.BH);
+  return p.nsplit == 2 ? launch_kernel("linear_scan", scan_kernel<CH, true>, grid, dim3(256), s, p)
+                       : launch_kernel("linear_scan", scan_kernel<CH, false>, grid, dim3(256), s, p);
 }
 
 // LDS of one chunk_kernel workgroup
@@ -1217,11 +1253,9 @@ hipError_t run_vkcc(const PrefillParams &p, hipStream_t s) {
   } else {
   if (p.nseg > 1) {
     hipError_t e = launch_kernel("linear_summary", summary_kernel<CF, VK, CH, CV>,
-                                 dim3(p.nseg - 1, p.BH), dim3(CF::NT), s, p);
+                                 dim3((p.nseg - 1) * p.nsplit, p.BH), dim3(CF::NT), s, p);
     if (e != hipSuccess) return e;
-    const size_t rec = (size_t)p.d * p.dv + p.d;
-    e = launch_kernel("linear_scan", scan_kernel<CH>, dim3((unsigned)((rec + 255) / 256), p.BH),
-                      dim3(256), s, p);
+    e = launch_scan<CH>(p, s);
     if (e != hipSuccess) return e;
   }
   if constexpr (!CH && !CV) {
@@ -1255,14 +1289,13 @@ hipError_t run(const PrefillParams &p, hipStream_t s) {
 template <class CF>
 hipError_t run_prefix(const PrefillParams &p, hipStream_t s) {
   if (p.nseg <= 1) return hipSuccess;
+  const dim3 grid((p.nseg - 1) * p.nsplit, p.BH);
   hipError_t e = p.vec_ok ? launch_kernel("linear_summary", summary_kernel<CF, true, false, false>,
-                                          dim3(p.nseg - 1, p.BH), dim3(CF::NT), s, p)
+                                          grid, dim3(CF::NT), s, p)
                           : launch_kernel("linear_summary", summary_kernel<CF, false, false, false>,
-                                          dim3(p.nseg - 1, p.BH), dim3(CF::NT), s, p);
+                                          grid, dim3(CF::NT), s, p);
   if (e != hipSuccess) return e;
-  const size_t rec = (size_t)p.d * p.dv + p.d;
-  return launch_kernel("linear_scan", scan_kernel<false>,
-                       dim3((unsigned)((rec + 255) / 256), p.BH), dim3(256), s, p);
+  return launch_scan<false>(p, s);
 }
 
 // Workgroups of chunk_kernel<CF> that fit on one CU (queried once).
@@ -1328,7 +1361,17 @@ LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io, int conv_widt
   nseg = chunks > 0 ? (chunks + cps - 1) / cps : 1;
   pl.nseg = (int)nseg;
   pl.seg_len = (int)(cps * pl.chunk);
-  pl.ws_bytes = nseg > 1 ? (size_t)nseg * BH * ws_rec(d, dv) * sizeof(float) : 0;
+  // When its workgroups would not cover the CUs (few heads, long segments),
+  // the summary kernel splits each segment in two parts of whole chunks (its
+  // workgroups then walk half as many chunks each, and twice as many run);
+  // the scan combines the parts.  Records: nseg slots, then one more per
+  // summarised segment for the second parts.  With enough workgroups the
+  // split measured slower (more records to write and scan).
+  pl.nsplit = nseg > 1 && cps >= 2 && (nseg - 1) * (long)BH < device_cu_count() ? 2 : 1;
+  pl.split_len = (int)(((cps + 1) / 2) * pl.chunk);
+  pl.wrec = ws_rec(d, dv);
+  const size_t nrec = nseg > 1 ? (size_t)nseg + (size_t)(pl.nsplit - 1) * (nseg - 1) : 0;
+  pl.ws_bytes = nrec * BH * pl.wrec * sizeof(float);
   pl.conv_off = pl.ws_bytes;
   if (nseg > 1 && conv_width > 1)  // room for the summary kernel's copy of the cache
     pl.ws_bytes += (size_t)BH * (conv_width - 1) * (2 * d + dv) * (bf16_io ? 2 : 4);
