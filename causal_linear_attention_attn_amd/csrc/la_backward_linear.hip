@@ -470,8 +470,8 @@ __device__ __forceinline__ void state_update(f32x4 (&Sa)[BC::SPW], const typenam
 // are written as zeros.
 template <class BC, int KS, int LDX>
 __device__ __forceinline__ void tri_tiles(typename BC::type *M, const typename BC::type *X,
-                                          const typename BC::type *Y, const float *pw, int wv,
-                                          int li, int lg) {
+                                          const typename BC::type *Y, const float *pw,
+                                          bool decay, int wv, int li, int lg) {
   using T = typename BC::type;
   constexpr int NTI = BC::NTB * BC::NTB;
 #pragma unroll
@@ -492,7 +492,7 @@ __device__ __forceinline__ void tri_tiles(typename BC::type *M, const typename B
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = 16 * tt + 4 * lg + r, j = 16 * jt + li;
-      M[t * BC::LDC + j] = from_f32<T>(j <= t ? acc[r] * pw[t - j] : 0.f);
+      M[t * BC::LDC + j] = from_f32<T>(j <= t ? (decay ? acc[r] * pw[t - j] : acc[r]) : 0.f);
     }
   }
 }
@@ -544,6 +544,7 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
   hr.den = head_rsrc<float>(p.den, bh, N, 1);
   const __amdgpu_buffer_rsrc_t rdq = head_rsrc<T>(p.dq, bh, N, d);
   const float lg2 = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
+  const bool decay = p.gamma != nullptr;  // uniform: no decay skips its factors
   for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
   zero_tail_columns<BC>(sm.St);
 
@@ -560,10 +561,13 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
 
   for (int c0 = t_begin; c0 < t_end; c0 += BC::C) {
     const int Lc = min(BC::C, N - c0);
-    for (int j = threadIdx.x; j < BC::C; j += BC::NT) sm.kw[j] = j < Lc ? sm.pw[Lc - 1 - j] : 0.f;
-    __syncthreads();
+    if (decay) {
+      for (int j = threadIdx.x; j < BC::C; j += BC::NT) sm.kw[j] = j < Lc ? sm.pw[Lc - 1 - j] : 0.f;
+      __syncthreads();
+    }
     commit_feat<BC>(sm.Fq, nullptr, nullptr, R.q, Lc, d, p.fmap);
-    commit_feat<BC>(sm.Fk, sm.KW, sm.kw, R.k, Lc, d, p.fmap);
+    // without decay the weighted keys are phi(k) itself (zero past the chunk)
+    commit_feat<BC>(sm.Fk, decay ? sm.KW : nullptr, sm.kw, R.k, Lc, d, p.fmap);
     commit_values<BC>(sm.Vp, R, Lc);
     commit_dn<BC>(sm.dN, R, Lc);
     state_copy<BC>(sm.St, Sa, wv, li, lg);
@@ -572,7 +576,7 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
                                                  d, dv);
     __syncthreads();
 
-    tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, wv, li, lg);
+    tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, decay, wv, li, lg);
     __syncthreads();
 
     // dphi(q) = gamma^(t+1) dN S'_in^T + dA phi(K), then phi'(q)
@@ -590,8 +594,10 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
         frag_rk(b, sm.St, BC::LDV, 16 * fb, 32 * ks, li, lg);
         mma(acc, a, b);
       }
+      if (decay) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[16 * tt + 4 * lg + r + 1];
+        for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[16 * tt + 4 * lg + r + 1];
+      }
       const int kend = (16 * tt + 16 + 31) / 32;
 #pragma unroll
       for (int ks = 0; ks < BC::C / 32; ++ks) {
@@ -609,7 +615,7 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
       out_tile<BC>(sm.Os, BC::LDK, rdq, acc, c0, 16 * tt, 16 * fb + li, Lc, d, lg);
     }
     // forward state across the chunk
-    state_update<BC>(Sa, sm.KW, sm.Vp, sm.pw[Lc], wv, li, lg);
+    state_update<BC>(Sa, decay ? sm.KW : sm.Fk, sm.Vp, sm.pw[Lc], wv, li, lg);
     __syncthreads();
     if constexpr (kStageOut) store_rows<BC, VK>(rdq, sm.Os, BC::LDK, BC::QCB, c0, Lc, d);
   }
@@ -636,6 +642,7 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
   const __amdgpu_buffer_rsrc_t rdk = head_rsrc<T>(p.dk, bh, N, d),
                                rdv = head_rsrc<T>(p.dv_, bh, N, dv);
   const float lg2 = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
+  const bool decay = p.gamma != nullptr;  // uniform: no decay skips its factors
   for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
   zero_tail_columns<BC>(sm.Sh);
 
@@ -653,7 +660,8 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
 
   for (int c0 = last; c0 >= t_begin; c0 -= BC::C) {
     const int Lc = min(BC::C, N - c0);
-    commit_feat<BC>(sm.Fq, sm.QW, sm.pw + 1, R.q, Lc, d, p.fmap);
+    // without decay the weighted queries are phi(q) itself
+    commit_feat<BC>(sm.Fq, decay ? sm.QW : nullptr, sm.pw + 1, R.q, Lc, d, p.fmap);
     commit_feat<BC>(sm.Fk, nullptr, nullptr, R.k, Lc, d, p.fmap);
     commit_values<BC>(sm.Vp, R, Lc);
     commit_dn<BC>(sm.dN, R, Lc);
@@ -662,8 +670,8 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
       load_chunk<BC, VK, true, true, true, true>(R, hr, c0 - BC::C, BC::C, d, dv);
     __syncthreads();
 
-    tri_tiles<BC, BC::DK / 32, BC::LDK>(sm.Ad, sm.Fq, sm.Fk, sm.pw, wv, li, lg);
-    tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, wv, li, lg);
+    tri_tiles<BC, BC::DK / 32, BC::LDK>(sm.Ad, sm.Fq, sm.Fk, sm.pw, decay, wv, li, lg);
+    tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, decay, wv, li, lg);
     __syncthreads();
     // dphi(k) = gamma^(L-1-j) V' Sh^T + dA^T phi(Q), then phi'(k)
     constexpr int NKT = BC::NTB * BC::NFB;
@@ -680,8 +688,10 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
         frag_rk(b, sm.Sh, BC::LDV, 16 * fb, 32 * ks, li, lg);
         mma(acc, a, b);
       }
+      if (decay) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
+        for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
+      }
 #pragma unroll
       for (int ks = 0; ks < BC::C / 32; ++ks) {
         if (ks < (16 * jt) / 32) continue;
@@ -712,8 +722,10 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
         frag_kr(b, sm.Sh, BC::LDV, 16 * vb, 32 * ks, li, lg);
         mma(acc, a, b);
       }
+      if (decay) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
+        for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
+      }
 #pragma unroll
       for (int ks = 0; ks < BC::C / 32; ++ks) {
         if (ks < (16 * jt) / 32) continue;
@@ -725,7 +737,7 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
       out_tile<BC>(sm.Ov, BC::LDO, rdv, acc, c0, 16 * jt, 16 * vb + li, Lc, dv, lg);
     }
     // adjoint across the chunk: Sh <- gamma^L Sh + (gamma^(t+1) phi(Q))^T dN
-    state_update<BC>(Sa, sm.QW, sm.dN, sm.pw[Lc], wv, li, lg);
+    state_update<BC>(Sa, decay ? sm.QW : sm.Fq, sm.dN, sm.pw[Lc], wv, li, lg);
     __syncthreads();
     if constexpr (kStageOut) {
       store_rows<BC, VK>(rdk, sm.Ok, BC::LDK, BC::QCB, c0, Lc, d);
