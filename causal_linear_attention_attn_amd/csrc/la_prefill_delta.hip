@@ -37,7 +37,8 @@
 //   accuracy before the final rounding.  Stored in the input precision:
 //   per chunk [Wt: DK x C][R: C x C], each in operand-fragment order
 //   (frag_off), so a wave's fragment is one contiguous 1 KiB block.
-// seq_kernel, one workgroup (4 waves) per (head, slice of W value columns):
+// seq_kernel, one workgroup (4 waves) per (head, slice of W value columns;
+// bf16 runs seq2_kernel below, the same pass with eight waves split by role):
 //   per chunk, wave (row block rb, column group): X^T = S'^T K^T and
 //   Z^T = S'^T Q^T from a T-precision copy S' of the fp32 state; Y = V - X
 //   into LDS; O^T = Z^T + Y^T R^T, stored straight from registers; the
@@ -769,6 +770,296 @@ __global__ void __launch_bounds__(kThreads) seq_kernel(PrefillParams p, int nsli
   }
 }
 
+// ---------------------------------------------------------------------------
+// seq2_kernel (bf16): the sequential pass with the work split by role.
+// Eight waves: four chain waves (row block rb = wave) compute X = K S-,
+// Y = V - X and the state update of their state rows, loading only k, Wt
+// and v; four output waves (row block rb = wave - 4) compute Q S- and
+// O = Q S- + R Y, loading only q and R.  Both read S' before the first
+// barrier and Y after it; the chain waves write S' and the next chunk's k
+// tile, the output waves its q tile, before the second.  The loads per
+// chunk are those of seq_kernel; the chain waves issue less than half of
+// them, and two waves share each SIMD.
+// ---------------------------------------------------------------------------
+constexpr int kThreads2 = 512;
+
+template <class CF>
+struct alignas(16) SmemSeq2 {
+  using T = typename CF::type;
+  T K[CF::NSET][CF::C * CF::QLD];  // k rows of the chunk of register set u
+  T Q[CF::NSET][CF::C * CF::QLD];  // q rows
+  T Ys[CF::C * CF::YLD];
+  T St[CF::W * CF::QLD];
+};
+
+// A role's share of one chunk's operands (256 threads stage its k or q).
+template <class CF>
+struct ChainOps {
+  static constexpr int NB = CF::C * CF::QCB / kThreads;
+  static_assert(NB * kThreads == CF::C * CF::QCB, "k blocks per thread");
+  typename CF::vec kb[NB];
+  Frag<typename CF::type> w[CF::FPW][CF::KSC];
+  typename Vec4<typename CF::type>::type v;
+  float b_tok, b_last;
+};
+template <class CF>
+struct OutOps {
+  static constexpr int NB = CF::C * CF::QCB / kThreads;
+  typename CF::vec qb[NB];
+  Frag<typename CF::type> r[CF::KSC];
+  float b_tok;
+};
+
+// Whole-line 16-byte blocks of rows of q or k (thread rt of the role's 256).
+template <class CF, bool VK, int NB>
+__device__ __forceinline__ void load_rows(typename CF::vec (&x)[NB], __amdgpu_buffer_rsrc_t r,
+                                          const PrefillParams &p, int chunk, int rt) {
+  using T = typename CF::type;
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    const int b = rt + m * kThreads;
+    const int row = chunk * CF::C + b / CF::QCB, col0 = (b % CF::QCB) * CF::VEC;
+    if constexpr (VK) {
+      x[m] = buf_load16<T>(r, (row < p.N && col0 < p.d)
+                                  ? (uint32_t)(((size_t)row * p.d + col0) * sizeof(T)) : kOOB);
+    } else {
+#pragma unroll
+      for (int e = 0; e < CF::VEC; ++e)
+        x[m][e] = buf_load1(r, (row < p.N && col0 + e < p.d)
+                                   ? (uint32_t)(((size_t)row * p.d + col0 + e) * sizeof(T))
+                                   : kOOB, (T *)nullptr);
+    }
+  }
+}
+template <class CF, int NB>
+__device__ __forceinline__ void stage_rows(const typename CF::vec (&x)[NB],
+                                           typename CF::type *tile, int rt) {
+#pragma unroll
+  for (int m = 0; m < NB; ++m) {
+    const int b = rt + m * kThreads;
+    *reinterpret_cast<typename CF::vec *>(tile + (b / CF::QCB) * CF::QLD +
+                                          (b % CF::QCB) * CF::VEC) = x[m];
+  }
+}
+
+template <class CF, bool VK, bool DECAY>
+__global__ void __launch_bounds__(kThreads2) seq2_kernel(PrefillParams p, int nslices,
+                                                         int xcd_map) {
+  using T = typename CF::type;
+  constexpr int C = CF::C, W = CF::W, NS = CF::NSET, FPW = CF::FPW, KSC = CF::KSC;
+  static_assert(CF::NRB == 4 && CF::NCT == 1 && FPW * 4 == CF::NFT, "role split tiling");
+  __shared__ SmemSeq2<CF> sm;
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool chain = wv < 4;
+  const int rb = chain ? wv : wv - 4;  // row block; chain waves also own state rows
+  const int rt = chain ? tid : tid - kThreads;  // thread index within the role
+  const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
+
+  const int b = blockIdx.x;
+  int bh, slice;
+  if (xcd_map) {
+    const int j = b / kXcds;
+    slice = j % nslices;
+    bh = (j / nslices) * kXcds + b % kXcds;
+  } else {
+    bh = b / nslices;
+    slice = b % nslices;
+  }
+  const int n0 = slice * W;
+  const int N = p.N, d = p.d, dv = p.dv;
+  const int nch = (N + C - 1) / C;
+  __amdgpu_buffer_rsrc_t rs[5];
+  {
+    const size_t qk = (size_t)N * d, vo = (size_t)N * dv;
+    rs[0] = buf_rsrc(reinterpret_cast<const T *>(p.q) + (size_t)bh * qk, (uint32_t)(qk * sizeof(T)));
+    rs[1] = buf_rsrc(reinterpret_cast<const T *>(p.k) + (size_t)bh * qk, (uint32_t)(qk * sizeof(T)));
+    const size_t tr = (size_t)nch * CF::REC;
+    rs[2] = buf_rsrc(reinterpret_cast<const T *>(p.ws) + (size_t)bh * tr, (uint32_t)(tr * sizeof(T)));
+    rs[3] = buf_rsrc(reinterpret_cast<const T *>(p.v) + (size_t)bh * vo, (uint32_t)(vo * sizeof(T)));
+    rs[4] = buf_rsrc(reinterpret_cast<const T *>(p.o) + (size_t)bh * vo, (uint32_t)(vo * sizeof(T)));
+  }
+  const __amdgpu_buffer_rsrc_t rdec = buf_rsrc(
+      reinterpret_cast<const float *>(reinterpret_cast<const T *>(p.ws) +
+                                      (size_t)p.BH * nch * CF::REC) + (size_t)bh * nch * C,
+      (uint32_t)((size_t)nch * C * sizeof(float)));
+  const int col = n0 + 4 * lg;  // this lane's four value columns
+
+  if (chain) {
+    auto fetch = [&](ChainOps<CF> &o, int chunk) {
+      load_rows<CF, VK>(o.kb, rs[1], p, chunk, rt);
+      const uint32_t base = (uint32_t)((size_t)chunk * CF::REC * sizeof(T));
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+        for (int a = 0; a < FPW; ++a)
+          load_rec_frag(o.w[a][ks], rs[2],
+                        base + (uint32_t)((((size_t)((rb * FPW + a) * KSC + ks) * 64 + lane) * 8) *
+                                          sizeof(T)));
+      const int t = chunk * C + 16 * rb + li;
+      const bool ok = t < N;
+      if constexpr (VK) {
+        o.v = buf_load4_raw(rs[3], ok && col < dv ? (uint32_t)(((size_t)t * dv + col) * sizeof(T))
+                                                  : kOOB, (T *)nullptr);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o.v[e] = buf_load1(rs[3], ok && col + e < dv
+                                        ? (uint32_t)(((size_t)t * dv + col + e) * sizeof(T))
+                                        : kOOB, (T *)nullptr);
+      }
+      if constexpr (DECAY) {
+        o.b_tok = buf_load1(rdec, (uint32_t)((chunk * C + 16 * rb + li) * 4), (float *)nullptr);
+        o.b_last = buf_load1(rdec, (uint32_t)((chunk * C + C - 1) * 4), (float *)nullptr);
+      } else {
+        o.b_tok = o.b_last = 1.f;
+      }
+    };
+    ChainOps<CF> set[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) fetch(set[u], u);
+    f32x4 Sacc[FPW];
+    const float *S0 = p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr;
+#pragma unroll
+    for (int a = 0; a < FPW; ++a) {
+      const int n = n0 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int f = 16 * (rb * FPW + a) + 4 * lg + r;
+        Sacc[a][r] = (S0 && f < d && n < dv) ? S0[(size_t)f * dv + n] : 0.f;
+      }
+      lds_store4(sm.St + li * CF::QLD + 16 * (rb * FPW + a) + 4 * lg, Sacc[a][0], Sacc[a][1],
+                 Sacc[a][2], Sacc[a][3]);
+    }
+    stage_rows<CF>(set[0].kb, sm.K[0], rt);
+    __syncthreads();
+
+    auto step = [&](ChainOps<CF> &op, const ChainOps<CF> &opn, const T *Kt, T *Kn, int c) {
+      f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < CF::KSD; ++ks) {
+        Frag<T> sf, kf;
+        lds_frag(kf, Kt + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
+        lds_frag(sf, sm.St + li * CF::QLD + 32 * ks + 8 * lg);
+        mma(X, sf, kf);
+      }
+      if (DECAY) X *= op.b_tok;
+      lds_store4(sm.Ys + (16 * rb + li) * CF::YLD + 4 * lg, to_f32(op.v[0]) - X[0],
+                 to_f32(op.v[1]) - X[1], to_f32(op.v[2]) - X[2], to_f32(op.v[3]) - X[3]);
+      __syncthreads();
+      if (DECAY) {
+#pragma unroll
+        for (int a = 0; a < FPW; ++a) Sacc[a] *= op.b_last;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks) {
+        Frag<T> yf;
+        lds_frag_tr(yf, sm.Ys, CF::YLD, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 0, li);
+#pragma unroll
+        for (int a = 0; a < FPW; ++a) mma(Sacc[a], op.w[a][ks], yf);
+      }
+#pragma unroll
+      for (int a = 0; a < FPW; ++a)
+        lds_store4(sm.St + li * CF::QLD + 16 * (rb * FPW + a) + 4 * lg, Sacc[a][0], Sacc[a][1],
+                   Sacc[a][2], Sacc[a][3]);
+      stage_rows<CF>(opn.kb, Kn, rt);
+      fetch(op, c + NS);
+      __syncthreads();
+    };
+    int cb = 0;
+    for (; cb + NS <= nch; cb += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int u1 = (u + 1) % NS;
+        step(set[u], set[u1], sm.K[u], sm.K[u1], cb + u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) {
+      const int u1 = (u + 1) % NS;
+      if (cb + u < nch) step(set[u], set[u1], sm.K[u], sm.K[u1], cb + u);
+    }
+    if (p.S_out) {
+      float *So = p.S_out + (size_t)bh * d * dv;
+#pragma unroll
+      for (int a = 0; a < FPW; ++a) {
+        const int n = n0 + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int f = 16 * (rb * FPW + a) + 4 * lg + r;
+          if (f < d && n < dv) So[(size_t)f * dv + n] = Sacc[a][r];
+        }
+      }
+    }
+  } else {
+    auto fetch = [&](OutOps<CF> &o, int chunk) {
+      load_rows<CF, VK>(o.qb, rs[0], p, chunk, rt);
+      const uint32_t base = (uint32_t)((size_t)chunk * CF::REC * sizeof(T));
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks)  // (blocks past the row block are zero)
+        load_rec_frag(o.r[ks], rs[2],
+                      base + (uint32_t)((CF::WT + ((size_t)(rb * KSC + ks) * 64 + lane) * 8) *
+                                        sizeof(T)));
+      if constexpr (DECAY)
+        o.b_tok = buf_load1(rdec, (uint32_t)((chunk * C + 16 * rb + li) * 4), (float *)nullptr);
+      else
+        o.b_tok = 1.f;
+    };
+    OutOps<CF> set[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) fetch(set[u], u);
+    stage_rows<CF>(set[0].qb, sm.Q[0], rt);
+    __syncthreads();
+
+    auto step = [&](OutOps<CF> &op, const OutOps<CF> &opn, const T *Qt, T *Qn, int c) {
+      const int t = c * C + 16 * rb + li;
+      f32x4 Z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < CF::KSD; ++ks) {
+        Frag<T> sf, qf;
+        lds_frag(qf, Qt + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
+        lds_frag(sf, sm.St + li * CF::QLD + 32 * ks + 8 * lg);
+        mma(Z, sf, qf);
+      }
+      if (DECAY) Z *= op.b_tok;
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks) {
+        if (32 * ks > 16 * rb + 15) continue;
+        Frag<T> yf;
+        lds_frag_tr(yf, sm.Ys, CF::YLD, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 0, li);
+        mma(Z, yf, op.r[ks]);
+      }
+      if constexpr (VK) {
+        buf_store4_nt(rs[4], t < N && col < dv ? (uint32_t)(((size_t)t * dv + col) * sizeof(T))
+                                               : kOOB, Z, (T *)nullptr);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          buf_store1(rs[4], t < N && col + e < dv
+                                ? (uint32_t)(((size_t)t * dv + col + e) * sizeof(T)) : kOOB,
+                     from_f32<T>(Z[e]));
+      }
+      stage_rows<CF>(opn.qb, Qn, rt);
+      fetch(op, c + NS);
+      __syncthreads();
+    };
+    int cb = 0;
+    for (; cb + NS <= nch; cb += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int u1 = (u + 1) % NS;
+        step(set[u], set[u1], sm.Q[u], sm.Q[u1], cb + u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) {
+      const int u1 = (u + 1) % NS;
+      if (cb + u < nch) step(set[u], set[u1], sm.Q[u], sm.Q[u1], cb + u);
+    }
+  }
+}
+
 template <class CF, bool VK, bool DECAY>
 hipError_t run_vkd(const PrefillParams &p, hipStream_t s) {
   static_assert(sizeof(SmemPrep<CF>) <= 64 * 1024, "LDS budget (prep)");
@@ -779,8 +1070,14 @@ hipError_t run_vkd(const PrefillParams &p, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int nsl = (p.dv + CF::W - 1) / CF::W;
   const int xcd_map = (p.BH % kXcds) == 0;
-  return launch_kernel("delta_seq", seq_kernel<CF, VK, DECAY>, dim3(p.BH * nsl),
-                       dim3(kThreads), s, p, nsl, xcd_map);
+  if constexpr (CF::NRB == 4 && CF::NCT == 1) {  // bf16: waves split by role
+    static_assert(sizeof(SmemSeq2<CF>) <= 160 * 1024, "LDS budget (seq2)");
+    return launch_kernel("delta_seq", seq2_kernel<CF, VK, DECAY>, dim3(p.BH * nsl),
+                         dim3(kThreads2), s, p, nsl, xcd_map);
+  } else {
+    return launch_kernel("delta_seq", seq_kernel<CF, VK, DECAY>, dim3(p.BH * nsl),
+                         dim3(kThreads), s, p, nsl, xcd_map);
+  }
 }
 
 // the decay-free rule gets its own instantiation (no decay work compiled in)
