@@ -145,7 +145,7 @@ def library_kernel_name(raw):
         return "linear_bwd_dkv"
     for fn, name in (("chunk_kernel", "linear_chunk"), ("summary_kernel", "linear_summary"),
                      ("scan_kernel", "linear_scan"), ("prep_kernel", "delta_prep"),
-                     ("seq_kernel", "delta_seq")):
+                     ("seq_kernel", "delta_seq"), ("seq2_kernel", "delta_seq")):
         if fn in raw:
             return name
     if "decode_kernel" in raw:
