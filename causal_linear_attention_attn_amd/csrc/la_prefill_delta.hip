@@ -790,6 +790,7 @@ struct alignas(16) SmemSeq2 {
   T Q[CF::NSET][CF::C * CF::QLD];  // q rows
   T Ys[CF::C * CF::YLD];
   T St[CF::W * CF::QLD];
+  float bs[CF::NSET][CF::C];       // decay products b_j of the chunk (with a decay)
 };
 
 // A role's share of one chunk's operands (256 threads stage its k or q).
@@ -800,14 +801,16 @@ struct ChainOps {
   typename CF::vec kb[NB];
   Frag<typename CF::type> w[CF::FPW][CF::KSC];
   typename Vec4<typename CF::type>::type v;
-  float b_tok, b_last;
 };
+// (with a decay, output wave 0 also loads the chunk's C decay products, one
+// per lane, and stages them into LDS with the q tile: one load per chunk
+// instead of one per wave and product)
 template <class CF>
 struct OutOps {
   static constexpr int NB = CF::C * CF::QCB / kThreads;
   typename CF::vec qb[NB];
   Frag<typename CF::type> r[CF::KSC];
-  float b_tok;
+  float bv;
 };
 
 // Whole-line 16-byte blocks of rows of q or k (thread rt of the role's 256).
@@ -848,6 +851,7 @@ __global__ void __launch_bounds__(kThreads2) seq2_kernel(PrefillParams p, int ns
   using T = typename CF::type;
   constexpr int C = CF::C, W = CF::W, NS = CF::NSET, FPW = CF::FPW, KSC = CF::KSC;
   static_assert(CF::NRB == 4 && CF::NCT == 1 && FPW * 4 == CF::NFT, "role split tiling");
+  static_assert(C == kWave, "one decay product per lane of a wave");
   __shared__ SmemSeq2<CF> sm;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -908,12 +912,6 @@ __global__ void __launch_bounds__(kThreads2) seq2_kernel(PrefillParams p, int ns
                                         ? (uint32_t)(((size_t)t * dv + col + e) * sizeof(T))
                                         : kOOB, (T *)nullptr);
       }
-      if constexpr (DECAY) {
-        o.b_tok = buf_load1(rdec, (uint32_t)((chunk * C + 16 * rb + li) * 4), (float *)nullptr);
-        o.b_last = buf_load1(rdec, (uint32_t)((chunk * C + C - 1) * 4), (float *)nullptr);
-      } else {
-        o.b_tok = o.b_last = 1.f;
-      }
     };
     ChainOps<CF> set[NS];
 #pragma unroll
@@ -934,7 +932,8 @@ __global__ void __launch_bounds__(kThreads2) seq2_kernel(PrefillParams p, int ns
     stage_rows<CF>(set[0].kb, sm.K[0], rt);
     __syncthreads();
 
-    auto step = [&](ChainOps<CF> &op, const ChainOps<CF> &opn, const T *Kt, T *Kn, int c) {
+    auto step = [&](ChainOps<CF> &op, const ChainOps<CF> &opn, const T *Kt, T *Kn,
+                    const float *bt, int c) {
       f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < CF::KSD; ++ks) {
@@ -943,13 +942,17 @@ __global__ void __launch_bounds__(kThreads2) seq2_kernel(PrefillParams p, int ns
         lds_frag(sf, sm.St + li * CF::QLD + 32 * ks + 8 * lg);
         mma(X, sf, kf);
       }
-      if (DECAY) X *= op.b_tok;
+      float b_last = 1.f;
+      if (DECAY) {
+        X *= bt[16 * rb + li];
+        b_last = bt[C - 1];
+      }
       lds_store4(sm.Ys + (16 * rb + li) * CF::YLD + 4 * lg, to_f32(op.v[0]) - X[0],
                  to_f32(op.v[1]) - X[1], to_f32(op.v[2]) - X[2], to_f32(op.v[3]) - X[3]);
       __syncthreads();
       if (DECAY) {
 #pragma unroll
-        for (int a = 0; a < FPW; ++a) Sacc[a] *= op.b_last;
+        for (int a = 0; a < FPW; ++a) Sacc[a] *= b_last;
       }
 #pragma unroll
       for (int ks = 0; ks < KSC; ++ks) {
@@ -971,13 +974,13 @@ __global__ void __launch_bounds__(kThreads2) seq2_kernel(PrefillParams p, int ns
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int u1 = (u + 1) % NS;
-        step(set[u], set[u1], sm.K[u], sm.K[u1], cb + u);
+        step(set[u], set[u1], sm.K[u], sm.K[u1], sm.bs[u], cb + u);
       }
     }
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u) {
       const int u1 = (u + 1) % NS;
-      if (cb + u < nch) step(set[u], set[u1], sm.K[u], sm.K[u1], cb + u);
+      if (cb + u < nch) step(set[u], set[u1], sm.K[u], sm.K[u1], sm.bs[u], cb + u);
     }
     if (p.S_out) {
       float *So = p.S_out + (size_t)bh * d * dv;
@@ -1000,18 +1003,21 @@ __global__ void __launch_bounds__(kThreads2) seq2_kernel(PrefillParams p, int ns
         load_rec_frag(o.r[ks], rs[2],
                       base + (uint32_t)((CF::WT + ((size_t)(rb * KSC + ks) * 64 + lane) * 8) *
                                         sizeof(T)));
-      if constexpr (DECAY)
-        o.b_tok = buf_load1(rdec, (uint32_t)((chunk * C + 16 * rb + li) * 4), (float *)nullptr);
-      else
-        o.b_tok = 1.f;
+      if (DECAY && rb == 0)  // past the last chunk: zeros (never used)
+        o.bv = buf_load1(rdec, (uint32_t)((chunk * C + lane) * 4), (float *)nullptr);
+    };
+    auto stage_b = [&](const OutOps<CF> &o, float *dst) {
+      if (DECAY && rb == 0) dst[lane] = o.bv;
     };
     OutOps<CF> set[NS];
 #pragma unroll
     for (int u = 0; u < NS; ++u) fetch(set[u], u);
     stage_rows<CF>(set[0].qb, sm.Q[0], rt);
+    stage_b(set[0], sm.bs[0]);
     __syncthreads();
 
-    auto step = [&](OutOps<CF> &op, const OutOps<CF> &opn, const T *Qt, T *Qn, int c) {
+    auto step = [&](OutOps<CF> &op, const OutOps<CF> &opn, const T *Qt, T *Qn, const float *bt,
+                    float *bn, int c) {
       const int t = c * C + 16 * rb + li;
       f32x4 Z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1021,7 +1027,7 @@ __global__ void __launch_bounds__(kThreads2) seq2_kernel(PrefillParams p, int ns
         lds_frag(sf, sm.St + li * CF::QLD + 32 * ks + 8 * lg);
         mma(Z, sf, qf);
       }
-      if (DECAY) Z *= op.b_tok;
+      if (DECAY) Z *= bt[16 * rb + li];
       __syncthreads();
 #pragma unroll
       for (int ks = 0; ks < KSC; ++ks) {
@@ -1041,6 +1047,7 @@ __global__ void __launch_bounds__(kThreads2) seq2_kernel(PrefillParams p, int ns
                      from_f32<T>(Z[e]));
       }
       stage_rows<CF>(opn.qb, Qn, rt);
+      stage_b(opn, bn);
       fetch(op, c + NS);
       __syncthreads();
     };
@@ -1049,13 +1056,13 @@ __global__ void __launch_bounds__(kThreads2) seq2_kernel(PrefillParams p, int ns
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int u1 = (u + 1) % NS;
-        step(set[u], set[u1], sm.Q[u], sm.Q[u1], cb + u);
+        step(set[u], set[u1], sm.Q[u], sm.Q[u1], sm.bs[u], sm.bs[u1], cb + u);
       }
     }
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u) {
       const int u1 = (u + 1) % NS;
-      if (cb + u < nch) step(set[u], set[u1], sm.Q[u], sm.Q[u1], cb + u);
+      if (cb + u < nch) step(set[u], set[u1], sm.Q[u], sm.Q[u1], sm.bs[u], sm.bs[u1], cb + u);
     }
   }
 }
