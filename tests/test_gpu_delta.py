@@ -124,17 +124,22 @@ def test_delta_prefill_then_decode_handoff():
     assert_close(S, rS, 2e-2, "S", axes=(-2, -1))
 
 
-def test_delta_workload_full_size_sampled():
-    """The gated-delta workload at full size (B=2 H=16 N=8192 d=dv=128, bf16),
-    launched as the benchmark launches it; two whole heads are checked
-    against the oracle token by token."""
-    w = inputs.WORKLOADS[5]
+@pytest.mark.parametrize("wid", [5, 6], ids=["plain", "alpha"])
+def test_delta_workload_full_size_sampled(wid):
+    """The gated-delta workloads at full size (B=2 H=16 N=8192 d=dv=128,
+    bf16; without and with the state decay alpha), launched as the benchmark
+    launches them; two whole heads are checked against the oracle token by
+    token."""
+    w = inputs.WORKLOADS[wid]
     x = inputs.make_prefill(w, DEV)
-    o, S, _ = la.prefill(x["q"], x["k"], x["v"], rule="delta", g=x["g"])
+    al = x.get("alpha")
+    o, S, _ = la.prefill(x["q"], x["k"], x["v"], rule="delta", g=x["g"], alpha=al)
     torch.cuda.synchronize()
     for b, h in ((0, 0), (1, 13)):
         sl = (slice(b, b + 1), slice(h, h + 1))
-        ro, rS = _oracle(x["q"][sl], x["k"][sl], x["v"][sl], x["g"][sl])
+        ro, rS = oracle.delta_prefill(cpu(x["q"][sl]), cpu(x["k"][sl]), cpu(x["v"][sl]),
+                                      cpu(x["g"][sl]),
+                                      alpha=None if al is None else cpu(al[sl]))
         assert_close(o[sl], ro, 2e-2, f"o head ({b},{h})")
         assert_close(S[sl], rS, 2e-2, f"S head ({b},{h})", axes=(-2, -1))
 
