@@ -525,7 +525,9 @@ __device__ __forceinline__ void store_rows(__amdgpu_buffer_rsrc_t r, const typen
 }
 
 // ---- dq: chunks left to right, forward state --------------------------------
-template <class BC, bool VK>
+// DEC: per-head decay (p.gamma set); without it every decay factor is 1 and
+// the weighted copies of phi(q), phi(k) are the unweighted ones
+template <class BC, bool VK, bool DEC>
 __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p) {
   using T = typename BC::type;
   __shared__ SmemDq<BC> sm;
@@ -543,8 +545,8 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
   hr.g = head_rsrc<T>(p.dout, bh, N, dv);
   hr.den = head_rsrc<float>(p.den, bh, N, 1);
   const __amdgpu_buffer_rsrc_t rdq = head_rsrc<T>(p.dq, bh, N, d);
-  const float lg2 = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
-  const bool decay = p.gamma != nullptr;  // uniform: no decay skips its factors
+  const float lg2 = DEC ? log2f(p.gamma[bh % p.H]) : 0.f;
+  constexpr bool decay = DEC;
   for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
   zero_tail_columns<BC>(sm.St);
 
@@ -561,7 +563,7 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
 
   for (int c0 = t_begin; c0 < t_end; c0 += BC::C) {
     const int Lc = min(BC::C, N - c0);
-    if (decay) {
+    if constexpr (decay) {
       for (int j = threadIdx.x; j < BC::C; j += BC::NT) sm.kw[j] = j < Lc ? sm.pw[Lc - 1 - j] : 0.f;
       __syncthreads();
     }
@@ -594,7 +596,7 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
         frag_rk(b, sm.St, BC::LDV, 16 * fb, 32 * ks, li, lg);
         mma(acc, a, b);
       }
-      if (decay) {
+      if constexpr (decay) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[16 * tt + 4 * lg + r + 1];
       }
@@ -615,14 +617,14 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
       out_tile<BC>(sm.Os, BC::LDK, rdq, acc, c0, 16 * tt, 16 * fb + li, Lc, d, lg);
     }
     // forward state across the chunk
-    state_update<BC>(Sa, decay ? sm.KW : sm.Fk, sm.Vp, sm.pw[Lc], wv, li, lg);
+    state_update<BC>(Sa, decay ? sm.KW : sm.Fk, sm.Vp, decay ? sm.pw[Lc] : 1.f, wv, li, lg);
     __syncthreads();
     if constexpr (kStageOut) store_rows<BC, VK>(rdq, sm.Os, BC::LDK, BC::QCB, c0, Lc, d);
   }
 }
 
 // ---- dk, dv: chunks right to left, adjoint state ------------------------------
-template <class BC, bool VK>
+template <class BC, bool VK, bool DEC>
 __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
   using T = typename BC::type;
   __shared__ SmemDkv<BC> sm;
@@ -641,8 +643,8 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
   hr.den = head_rsrc<float>(p.den, bh, N, 1);
   const __amdgpu_buffer_rsrc_t rdk = head_rsrc<T>(p.dk, bh, N, d),
                                rdv = head_rsrc<T>(p.dv_, bh, N, dv);
-  const float lg2 = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
-  const bool decay = p.gamma != nullptr;  // uniform: no decay skips its factors
+  const float lg2 = DEC ? log2f(p.gamma[bh % p.H]) : 0.f;
+  constexpr bool decay = DEC;
   for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
   zero_tail_columns<BC>(sm.Sh);
 
@@ -688,7 +690,7 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
         frag_rk(b, sm.Sh, BC::LDV, 16 * fb, 32 * ks, li, lg);
         mma(acc, a, b);
       }
-      if (decay) {
+      if constexpr (decay) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
       }
@@ -722,7 +724,7 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
         frag_kr(b, sm.Sh, BC::LDV, 16 * vb, 32 * ks, li, lg);
         mma(acc, a, b);
       }
-      if (decay) {
+      if constexpr (decay) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] *= sm.pw[max(Lc - 1 - (16 * jt + 4 * lg + r), 0)];
       }
@@ -737,7 +739,7 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
       out_tile<BC>(sm.Ov, BC::LDO, rdv, acc, c0, 16 * jt, 16 * vb + li, Lc, dv, lg);
     }
     // adjoint across the chunk: Sh <- gamma^L Sh + (gamma^(t+1) phi(Q))^T dN
-    state_update<BC>(Sa, decay ? sm.QW : sm.Fq, sm.dN, sm.pw[Lc], wv, li, lg);
+    state_update<BC>(Sa, decay ? sm.QW : sm.Fq, sm.dN, decay ? sm.pw[Lc] : 1.f, wv, li, lg);
     __syncthreads();
     if constexpr (kStageOut) {
       store_rows<BC, VK>(rdk, sm.Ok, BC::LDK, BC::QCB, c0, Lc, d);
@@ -838,11 +840,16 @@ hipError_t run_bwd(const BwdParams &p, hipStream_t s) {
                       dim3((unsigned)((rec + 255) / 256), p.BH), dim3(256), s, p);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_kernel("linear_bwd_dq", bwd_dq_kernel<BC, VK>, dim3(p.nseg, p.BH),
-                               dim3(BC::NT), s, p);
+  const dim3 grid(p.nseg, p.BH);
+  hipError_t e = p.gamma ? launch_kernel("linear_bwd_dq", bwd_dq_kernel<BC, VK, true>, grid,
+                                         dim3(BC::NT), s, p)
+                         : launch_kernel("linear_bwd_dq", bwd_dq_kernel<BC, VK, false>, grid,
+                                         dim3(BC::NT), s, p);
   if (e != hipSuccess) return e;
-  return launch_kernel("linear_bwd_dkv", bwd_dkv_kernel<BC, VK>, dim3(p.nseg, p.BH),
-                       dim3(BC::NT), s, p);
+  return p.gamma ? launch_kernel("linear_bwd_dkv", bwd_dkv_kernel<BC, VK, true>, grid,
+                                 dim3(BC::NT), s, p)
+                 : launch_kernel("linear_bwd_dkv", bwd_dkv_kernel<BC, VK, false>, grid,
+                                 dim3(BC::NT), s, p);
 }
 
 template <class BC>
