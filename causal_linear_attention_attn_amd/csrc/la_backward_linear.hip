@@ -60,7 +60,12 @@ struct BCfg {
   static constexpr int LDK = DK + PAD;     // row strides of the LDS tiles
   static constexpr int LDV = DVK + PAD;
   static constexpr int LDO = DV + PAD;
-  static constexpr int LDC = C + PAD;
+  // C x C tiles and the gradient staging tiles: rows of 80 or 144 bytes
+  // (bf16), so the 16-byte fragment reads of 16 consecutive rows and the
+  // staging writes of rows 4 apart fall in distinct banks
+  static constexpr int PADS = sizeof(T) == 2 ? 8 : 4;
+  static constexpr int LDC = C + PADS;
+  static constexpr int LDKS = DK + PADS, LDOS = DV + PADS;
   static constexpr int NTB = C / 16;   // token blocks
   static constexpr int NFB = DK / 16;  // feature blocks
   static constexpr int NST = NFB * NVP;               // state tiles
@@ -70,6 +75,9 @@ struct BCfg {
   // resident waves per SIMD the dq kernel's registers must allow (what its
   // LDS admits)
   static constexpr int WPE_DQ = WPE_DQ_;
+  // ... and the dk/dv kernel's without a decay (four-wave bf16 workgroups:
+  // its LDS then admits three per CU)
+  static constexpr int WPE_DKV = (NW == 4 && sizeof(T) == 2) ? 3 : 1;
   static_assert(C % 32 == 0 && DK % 32 == 0 && DV % 16 == 0, "tile sizes");
   // row loops run whole waves (the dn row reduction shuffles within a wave)
   static_assert((C * QCB) % kWave == 0 && (C * VCB) % kWave == 0, "whole-wave row loops");
@@ -88,23 +96,25 @@ struct alignas(16) SmemDq {
   T St[BC::DK * BC::LDV]; // the forward state [S | z | 0], rows = features
   float pw[BC::C + 4];    // gamma^m
   float kw[BC::C];        // gamma^(L-1-j), 0 past the chunk
-  T Os[kStageOut ? BC::C * BC::LDK : 1];  // dq staging
+  T Os[kStageOut ? BC::C * BC::LDKS : 1];  // dq staging
 };
 
-template <class BC>
+// Without a decay (DEC false) the weighted queries are phi(q) itself and
+// there is no power table.
+template <class BC, bool DEC>
 struct alignas(16) SmemDkv {
   using T = typename BC::type;
   T Fq[BC::C * BC::LDK];
-  T QW[BC::C * BC::LDK];  // gamma^(t+1) phi(q_t)
+  T QW[DEC ? BC::C * BC::LDK : 8];  // gamma^(t+1) phi(q_t)
   T Fk[BC::C * BC::LDK];
   T Vp[BC::C * BC::LDV];
   T dN[BC::C * BC::LDV];
   T Ad[BC::C * BC::LDC];  // A . D
   T dA[BC::C * BC::LDC];  // dA . D
   T Sh[BC::DK * BC::LDV]; // the adjoint [Sh | zh | 0], rows = features
-  float pw[BC::C + 4];
-  T Ok[kStageOut ? BC::C * BC::LDK : 1];  // dk staging
-  T Ov[kStageOut ? BC::C * BC::LDO : 1];  // dv staging
+  float pw[DEC ? BC::C + 4 : 4];
+  T Ok[kStageOut ? BC::C * BC::LDKS : 1];  // dk staging
+  T Ov[kStageOut ? BC::C * BC::LDOS : 1];  // dv staging
 };
 
 // The reverse summary needs the weighted queries and dN only.
@@ -614,20 +624,20 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
         const int t = 16 * tt + 4 * lg + r, f = 16 * fb + li;
         acc[r] *= p.fmap ? fminf(to_f32(sm.Fq[t * BC::LDK + f]), 1.f) : 1.f;
       }
-      out_tile<BC>(sm.Os, BC::LDK, rdq, acc, c0, 16 * tt, 16 * fb + li, Lc, d, lg);
+      out_tile<BC>(sm.Os, BC::LDKS, rdq, acc, c0, 16 * tt, 16 * fb + li, Lc, d, lg);
     }
     // forward state across the chunk
     state_update<BC>(Sa, decay ? sm.KW : sm.Fk, sm.Vp, decay ? sm.pw[Lc] : 1.f, wv, li, lg);
     __syncthreads();
-    if constexpr (kStageOut) store_rows<BC, VK>(rdq, sm.Os, BC::LDK, BC::QCB, c0, Lc, d);
+    if constexpr (kStageOut) store_rows<BC, VK>(rdq, sm.Os, BC::LDKS, BC::QCB, c0, Lc, d);
   }
 }
 
 // ---- dk, dv: chunks right to left, adjoint state ------------------------------
 template <class BC, bool VK, bool DEC>
-__global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(BC::NT, DEC ? 1 : BC::WPE_DKV) bwd_dkv_kernel(BwdParams p) {
   using T = typename BC::type;
-  __shared__ SmemDkv<BC> sm;
+  __shared__ SmemDkv<BC, DEC> sm;
   const int seg = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -645,7 +655,8 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
                                rdv = head_rsrc<T>(p.dv_, bh, N, dv);
   const float lg2 = DEC ? log2f(p.gamma[bh % p.H]) : 0.f;
   constexpr bool decay = DEC;
-  for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
+  if constexpr (DEC)
+    for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
   zero_tail_columns<BC>(sm.Sh);
 
   f32x4 Sa[BC::SPW];
@@ -707,7 +718,7 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
         const int j = 16 * jt + 4 * lg + r, f = 16 * fb + li;
         acc[r] *= p.fmap ? fminf(to_f32(sm.Fk[j * BC::LDK + f]), 1.f) : 1.f;
       }
-      out_tile<BC>(sm.Ok, BC::LDK, rdk, acc, c0, 16 * jt, 16 * fb + li, Lc, d, lg);
+      out_tile<BC>(sm.Ok, BC::LDKS, rdk, acc, c0, 16 * jt, 16 * fb + li, Lc, d, lg);
     }
     // dv' = gamma^(L-1-j) phi(K) Sh + (A . D)^T dN  (value columns only)
     constexpr int NVT = BC::NTB * (BC::NVP - 1);
@@ -736,14 +747,14 @@ __global__ void __launch_bounds__(BC::NT) bwd_dkv_kernel(BwdParams p) {
         frag_kr(b, sm.dN, BC::LDV, 16 * vb, 32 * ks, li, lg);
         mma(acc, a, b);
       }
-      out_tile<BC>(sm.Ov, BC::LDO, rdv, acc, c0, 16 * jt, 16 * vb + li, Lc, dv, lg);
+      out_tile<BC>(sm.Ov, BC::LDOS, rdv, acc, c0, 16 * jt, 16 * vb + li, Lc, dv, lg);
     }
     // adjoint across the chunk: Sh <- gamma^L Sh + (gamma^(t+1) phi(Q))^T dN
     state_update<BC>(Sa, decay ? sm.QW : sm.Fq, sm.dN, decay ? sm.pw[Lc] : 1.f, wv, li, lg);
     __syncthreads();
     if constexpr (kStageOut) {
-      store_rows<BC, VK>(rdk, sm.Ok, BC::LDK, BC::QCB, c0, Lc, d);
-      store_rows<BC, VK>(rdv, sm.Ov, BC::LDO, BC::VCB, c0, Lc, dv);
+      store_rows<BC, VK>(rdk, sm.Ok, BC::LDKS, BC::QCB, c0, Lc, d);
+      store_rows<BC, VK>(rdv, sm.Ov, BC::LDOS, BC::VCB, c0, Lc, dv);
     }
   }
 
@@ -829,7 +840,7 @@ __global__ void __launch_bounds__(256) bwd_rscan_kernel(BwdParams p) {
 
 template <class BC, bool VK>
 hipError_t run_bwd(const BwdParams &p, hipStream_t s) {
-  static_assert(sizeof(SmemDq<BC>) <= 160 * 1024 && sizeof(SmemDkv<BC>) <= 160 * 1024,
+  static_assert(sizeof(SmemDq<BC>) <= 160 * 1024 && sizeof(SmemDkv<BC, true>) <= 160 * 1024,
                 "LDS budget");
   if (p.nseg > 1) {
     hipError_t e = launch_kernel("linear_bwd_rsummary", bwd_rsum_kernel<BC, VK>,
