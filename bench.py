@@ -478,8 +478,9 @@ def bench_train(la, lib, torch, w, steps, warmup):
         la.prefill(q, k, v, gamma=gamma, eps=w.eps, o=o, den_out=den, workspace=wsf,
                    return_state=False)
 
-    def bwd():
-        return la.backward(q, k, v, o, den, do, gamma=gamma, state_grad=False)
+    def bwd():  # the forward's segment states are reused from its workspace
+        return la.backward(q, k, v, o, den, do, gamma=gamma, state_grad=False,
+                           fwd_workspace=wsf)
 
     def step():
         fwd()

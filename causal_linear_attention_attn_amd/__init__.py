@@ -171,14 +171,17 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
 
 
 def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=None,
-             dS_out=None, dz_out=None, state_grad=True, workspace=None):
+             dS_out=None, dz_out=None, state_grad=True, workspace=None,
+             fwd_workspace=None):
     """Gradients of a LINEAR prefill (see la_backward): q, k [B,H,N,d], v, o,
     do [B,H,N,dv] (dtype of q), den [B,H,N] fp32 from prefill(den_out=...);
     gamma, S_in, z_in as in the forward; dS_out [B,H,d,dv], dz_out [B,H,d]
     the gradient with respect to the final state, or None.
+    fwd_workspace: the workspace the forward prefill ran with (prefill's
+    workspace=, same inputs), whose segment states are then reused.
     Returns (dq, dk, dv, dS_in, dz_in); the last two are None unless
     state_grad."""
-    _need_gpu(q, k, v, o, den, do, gamma, S_in, z_in, dS_out, dz_out, workspace)
+    _need_gpu(q, k, v, o, den, do, gamma, S_in, z_in, dS_out, dz_out, workspace, fwd_workspace)
     _need_f32(den, gamma, S_in, z_in, dS_out, dz_out)
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,H,N,d] and v [B,H,N,dv]")
@@ -211,6 +214,9 @@ def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=No
     if workspace is not None:
         a.workspace = _ptr(workspace)
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if fwd_workspace is not None:
+        a.fwd_workspace = _ptr(fwd_workspace)
+        a.fwd_workspace_bytes = fwd_workspace.numel() * fwd_workspace.element_size()
     _lib.check(lib.la_backward(ctypes.byref(a), _stream()), "la_backward")
     return dq, dk, dvv, dS_in, dz_in
 

@@ -44,6 +44,7 @@ class BackwardArgs(ctypes.Structure):
         ("grad_q", _ptr), ("grad_k", _ptr), ("grad_v", _ptr),
         ("grad_S_in", _ptr), ("grad_z_in", _ptr),
         ("workspace", _ptr), ("workspace_bytes", _size),
+        ("fwd_workspace", _ptr), ("fwd_workspace_bytes", _size),
     ]
 
 

@@ -327,9 +327,17 @@ int la_backward(const la_backward_args *a, void *stream) {
                       aligned16(a->k) && aligned16(a->v) && aligned16(a->o) &&
                       aligned16(a->grad_o) && aligned16(a->grad_q) && aligned16(a->grad_k) &&
                       aligned16(a->grad_v);
-  float *ws_f = reinterpret_cast<float *>(a->workspace);
-  float *ws_r = ws_f ? ws_f + plan.ws_bytes / sizeof(float) : nullptr;
-  if (plan.nseg > 1) {  // the forward state entering each segment
+  if (plan.nseg > 1 && a->fwd_workspace) {
+    if (a->fwd_workspace_bytes < plan.ws_bytes) return LA_EWORKSPACE;
+    if (reinterpret_cast<uintptr_t>(a->fwd_workspace) & 3u) return LA_EINVAL;
+  }
+  float *ws_own = reinterpret_cast<float *>(a->workspace);
+  float *ws_r = ws_own ? ws_own + plan.ws_bytes / sizeof(float) : nullptr;
+  // the forward's own records, when given (same plan, same slots); else
+  // this call's workspace, filled below
+  const bool reuse = plan.nseg > 1 && a->fwd_workspace != nullptr;
+  const float *ws_f = reuse ? reinterpret_cast<const float *>(a->fwd_workspace) : ws_own;
+  if (plan.nseg > 1 && !reuse) {  // the forward state entering each segment
     la::PrefillParams fp{};
     fp.BH = BH;
     fp.H = a->H;
@@ -344,11 +352,11 @@ int la_backward(const la_backward_args *a, void *stream) {
     fp.gamma = a->gamma;
     fp.S_in = a->S_in;
     fp.z_in = a->z_in;
-    fp.ws = ws_f;
+    fp.ws = ws_own;
     fp.nseg = plan.nseg;
     fp.nsplit = plan.nsplit;
     fp.split_len = plan.split_len;
-    fp.slot_vec = (a->d % 4 == 0) && aligned16(ws_f);
+    fp.slot_vec = (a->d % 4 == 0) && aligned16(ws_own);
     fp.seg_len = plan.seg_len;
     const hipError_t e = la::launch_linear_state_prefix(fp, plan, bf16_io, s);
     if (e != hipSuccess) return LA_EHIP;
@@ -377,12 +385,12 @@ int la_backward(const la_backward_args *a, void *stream) {
   p.dv_ = a->grad_v;
   p.dS_in = a->grad_S_in;
   p.dz_in = a->grad_z_in;
-  p.ws_f = ws_f;
+  p.ws_f = const_cast<float *>(ws_f);  // read only by the backward kernels
   p.ws_r = ws_r;
   p.wrec = plan.nseg > 1 ? plan.wrec : 0;
   p.nseg = plan.nseg;
   p.seg_len = plan.seg_len;
-  p.slot_vec = (a->d % 4 == 0) && aligned16(ws_f);
+  p.slot_vec = (a->d % 4 == 0) && aligned16(ws_f) && aligned16(ws_r);
   return to_status(la::launch_linear_backward(p, bf16_io, s));
 }
 

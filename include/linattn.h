@@ -193,6 +193,16 @@ typedef struct la_backward_args {
   float *grad_z_in;  /* [B,H,d]; NULL = not written */
   void *workspace;   /* device scratch of workspace_bytes, caller-owned */
   size_t workspace_bytes;
+  /* Optional (NULL = not used): the workspace of the la_prefill call that
+   * produced o and den, left as that call wrote it, with this call's q, k,
+   * v, gamma, S_in, z_in, fmap and no alpha or convolution; it holds the
+   * state entering each segment of the forward, which la_backward then
+   * reads (not written) instead of recomputing it.  fwd_workspace_bytes
+   * below la_prefill_workspace_size of those arguments: LA_EWORKSPACE; not
+   * 4-byte aligned: LA_EINVAL.  Any other contents give wrong gradients
+   * (not detected).  Ignored when the forward needs no workspace. */
+  const void *fwd_workspace;
+  size_t fwd_workspace_bytes;
 } la_backward_args;
 
 /* Workspace bytes la_backward needs (0 when none); (size_t)-1 for invalid

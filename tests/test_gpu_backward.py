@@ -119,6 +119,31 @@ def test_backward_identity_map_bf16_128():
     _check(q, k, v, do, None, "identity", TOL[torch.bfloat16])
 
 
+@pytest.mark.parametrize("decay", [False, True], ids=["nodecay", "decay"])
+def test_backward_reuses_forward_workspace(decay):
+    """With the forward's workspace passed in, the backward reads the
+    segment-entering states the forward computed instead of recomputing
+    them: the same kernels on the same inputs, so the gradients agree bit
+    for bit; a workspace below the forward's size is refused."""
+    B, H, N, d, dv = 1, 4, 4099, 64, 64
+    q, k, v, do, gamma = _case(B, H, N, d, dv, torch.bfloat16, 1770 + decay, decay)
+    S0 = _rand((B, H, d, dv), torch.float32, 1772, 0.3)
+    z0 = _rand((B, H, d), torch.float32, 1773, 0.3).abs() + 1.0
+    need = la.workspace_size(q, k, v, gamma=gamma)
+    assert need > 0  # several segments
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    den = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    o, _, _ = la.prefill(q, k, v, gamma=gamma, S_in=S0, z_in=z0, den_out=den, workspace=ws,
+                         return_state=False)
+    ref = la.backward(q, k, v, o, den, do, gamma=gamma, S_in=S0, z_in=z0)
+    got = la.backward(q, k, v, o, den, do, gamma=gamma, S_in=S0, z_in=z0, fwd_workspace=ws)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dS_in", "dz_in"), got, ref):
+        assert torch.equal(a, b), name
+    with pytest.raises(RuntimeError):
+        la.backward(q, k, v, o, den, do, gamma=gamma, S_in=S0, z_in=z0, fwd_workspace=ws[:-4])
+
+
 def test_backward_no_tokens_passes_state_gradient():
     B, H, d, dv = 2, 3, 64, 64
     q = torch.empty((B, H, 0, d), dtype=torch.bfloat16, device=DEV)
