@@ -75,8 +75,8 @@ struct BCfg {
   // resident waves per SIMD the dq kernel's registers must allow (what its
   // LDS admits)
   static constexpr int WPE_DQ = WPE_DQ_;
-  // ... and the dk/dv kernel's without a decay (four-wave bf16 workgroups:
-  // its LDS then admits three per CU)
+  // ... and the dk/dv kernel's (four-wave bf16 workgroups: its LDS admits
+  // three per CU)
   static constexpr int WPE_DKV = (NW == 4 && sizeof(T) == 2) ? 3 : 1;
   static_assert(C % 32 == 0 && DK % 32 == 0 && DV % 16 == 0, "tile sizes");
   // row loops run whole waves (the dn row reduction shuffles within a wave)
@@ -99,13 +99,13 @@ struct alignas(16) SmemDq {
   T Os[kStageOut ? BC::C * BC::LDKS : 1];  // dq staging
 };
 
-// Without a decay (DEC false) the weighted queries are phi(q) itself and
-// there is no power table.
+// The weighted queries gamma^(t+1) phi(q_t) of the adjoint's update are
+// formed from phi(q) in registers; without a decay (DEC false) there is no
+// power table.
 template <class BC, bool DEC>
 struct alignas(16) SmemDkv {
   using T = typename BC::type;
   T Fq[BC::C * BC::LDK];
-  T QW[DEC ? BC::C * BC::LDK : 8];  // gamma^(t+1) phi(q_t)
   T Fk[BC::C * BC::LDK];
   T Vp[BC::C * BC::LDV];
   T dN[BC::C * BC::LDV];
@@ -456,7 +456,7 @@ __device__ __forceinline__ void zero_tail_columns(typename BC::type *M) {
 template <class BC>
 __device__ __forceinline__ void state_update(f32x4 (&Sa)[BC::SPW], const typename BC::type *X,
                                              const typename BC::type *Y, float scale, int wv,
-                                             int li, int lg) {
+                                             int li, int lg, const float *wt = nullptr) {
   using T = typename BC::type;
 #pragma unroll
   for (int i = 0; i < BC::SPW; ++i) {
@@ -469,6 +469,11 @@ __device__ __forceinline__ void state_update(f32x4 (&Sa)[BC::SPW], const typenam
     for (int ks = 0; ks < BC::C / 32; ++ks) {
       Frag<T> a, b;
       frag_kr(a, X, BC::LDK, 16 * fb, 32 * ks, li, lg);
+      if (wt) {  // per-token weights on X's rows (this lane's k slots)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          a.v[e] = from_f32<T>(to_f32(a.v[e]) * wt[32 * ks + 8 * lg + e]);
+      }
       frag_kr(b, Y, BC::LDV, 16 * vb, 32 * ks, li, lg);
       mma(Sa[i], a, b);
     }
@@ -635,7 +640,7 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
 
 // ---- dk, dv: chunks right to left, adjoint state ------------------------------
 template <class BC, bool VK, bool DEC>
-__global__ void __launch_bounds__(BC::NT, DEC ? 1 : BC::WPE_DKV) bwd_dkv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(BC::NT, BC::WPE_DKV) bwd_dkv_kernel(BwdParams p) {
   using T = typename BC::type;
   __shared__ SmemDkv<BC, DEC> sm;
   const int seg = blockIdx.x, bh = blockIdx.y;
@@ -673,8 +678,7 @@ __global__ void __launch_bounds__(BC::NT, DEC ? 1 : BC::WPE_DKV) bwd_dkv_kernel(
 
   for (int c0 = last; c0 >= t_begin; c0 -= BC::C) {
     const int Lc = min(BC::C, N - c0);
-    // without decay the weighted queries are phi(q) itself
-    commit_feat<BC>(sm.Fq, decay ? sm.QW : nullptr, sm.pw + 1, R.q, Lc, d, p.fmap);
+    commit_feat<BC>(sm.Fq, nullptr, nullptr, R.q, Lc, d, p.fmap);
     commit_feat<BC>(sm.Fk, nullptr, nullptr, R.k, Lc, d, p.fmap);
     commit_values<BC>(sm.Vp, R, Lc);
     commit_dn<BC>(sm.dN, R, Lc);
@@ -750,7 +754,8 @@ __global__ void __launch_bounds__(BC::NT, DEC ? 1 : BC::WPE_DKV) bwd_dkv_kernel(
       out_tile<BC>(sm.Ov, BC::LDOS, rdv, acc, c0, 16 * jt, 16 * vb + li, Lc, dv, lg);
     }
     // adjoint across the chunk: Sh <- gamma^L Sh + (gamma^(t+1) phi(Q))^T dN
-    state_update<BC>(Sa, decay ? sm.QW : sm.Fq, sm.dN, decay ? sm.pw[Lc] : 1.f, wv, li, lg);
+    state_update<BC>(Sa, sm.Fq, sm.dN, decay ? sm.pw[Lc] : 1.f, wv, li, lg,
+                     decay ? sm.pw + 1 : nullptr);
     __syncthreads();
     if constexpr (kStageOut) {
       store_rows<BC, VK>(rdk, sm.Ok, BC::LDKS, BC::QCB, c0, Lc, d);
