@@ -90,16 +90,19 @@ def test_decode_workload_full_shape_sampled():
 
 def test_training_step_full_size_sampled():
     """The benchmark's training step (B4 H16 N4096 d64 bf16): prefill with
-    denominators, backward for the seeded dL/do; dq, dk, dv of two heads
+    denominators into a kept workspace, backward for the seeded dL/do
+    reading the forward's segment states from it; dq, dk, dv of two heads
     against the oracle's backward."""
     w = inputs.WORKLOADS[2]
     x = inputs.make_prefill(w, DEV)
     do = inputs.make_grad_out(w, DEV)
     den = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(la.workspace_size(x["q"], x["k"], x["v"], gamma=x["gamma"], eps=w.eps),
+                         1), dtype=torch.uint8, device=DEV)
     o, _, _ = la.prefill(x["q"], x["k"], x["v"], gamma=x["gamma"], eps=w.eps, den_out=den,
-                         return_state=False)
+                         workspace=ws, return_state=False)
     dq, dk, dv, _, _ = la.backward(x["q"], x["k"], x["v"], o, den, do, gamma=x["gamma"],
-                                   state_grad=False)
+                                   state_grad=False, fwd_workspace=ws)
     torch.cuda.synchronize()
     for b, h in ((0, 0), (3, 13)):
         q, k, v, g = (cpu(_head(t, b, h)) for t in (x["q"], x["k"], x["v"], do))
