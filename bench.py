@@ -113,8 +113,7 @@ KERNEL_SRC = {
     "linear_scan": "la_prefill_linear.hip", "delta_prep": "la_prefill_delta.hip",
     "delta_seq": "la_prefill_delta.hip", "linear_decode": "la_decode.hip",
     "delta_decode": "la_decode.hip", "linear_bwd_dq": "la_backward_linear.hip",
-    "linear_bwd_dkv": "la_backward_linear.hip", "linear_bwd_rsummary": "la_backward_linear.hip",
-    "linear_bwd_rscan": "la_backward_linear.hip",
+    "linear_bwd_dkv": "la_backward_linear.hip", "linear_bwd_rscan": "la_backward_linear.hip",
 }
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_MIB = 256
@@ -139,8 +138,6 @@ def library_kernel_name(raw):
         return "linear_bwd_rscan"
     if "bwd_dq_kernel" in raw:
         return "linear_bwd_dq"
-    if "bwd_rsum_kernel" in raw:
-        return "linear_bwd_rsummary"
     if "bwd_dkv_kernel" in raw:
         return "linear_bwd_dkv"
     for fn, name in (("chunk_kernel", "linear_chunk"), ("summary_kernel", "linear_summary"),

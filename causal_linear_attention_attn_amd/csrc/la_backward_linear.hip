@@ -26,9 +26,12 @@
 //
 // Kernels (per (segment, head); segments as in the forward):
 //   the forward's summary and scan kernels   forward state entering each segment
-//   bwd_rsum_kernel                          each segment's own adjoint, from zero
+//                                            (or the forward's own, left in its workspace)
+//   bwd_dq_kernel                            dq, chunks left to right, forward state; also
+//                                            each segment's own adjoint, from zero at its
+//                                            end (the terms are summed in any order:
+//                                            sum_t gamma^(t - t_begin + 1) phi(q_t) dn_t^T)
 //   bwd_rscan_kernel                         adjoint entering each segment from the right
-//   bwd_dq_kernel                            dq, chunks left to right, forward state
 //   bwd_dkv_kernel                           dk, dv, chunks right to left, adjoint state;
 //                                            segment 0 writes the initial-state gradient
 // Every product runs on the matrix cores from LDS tiles (bf16 operands,
@@ -115,15 +118,6 @@ struct alignas(16) SmemDkv {
   float pw[DEC ? BC::C + 4 : 4];
   T Ok[kStageOut ? BC::C * BC::LDKS : 1];  // dk staging
   T Ov[kStageOut ? BC::C * BC::LDOS : 1];  // dv staging
-};
-
-// The reverse summary needs the weighted queries and dN only.
-template <class BC>
-struct alignas(16) SmemRsum {
-  using T = typename BC::type;
-  T QW[BC::C * BC::LDK];
-  T dN[BC::C * BC::LDV];
-  float pw[BC::C + 4];
 };
 
 // ---- operands -------------------------------------------------------------
@@ -456,7 +450,8 @@ __device__ __forceinline__ void zero_tail_columns(typename BC::type *M) {
 template <class BC>
 __device__ __forceinline__ void state_update(f32x4 (&Sa)[BC::SPW], const typename BC::type *X,
                                              const typename BC::type *Y, float scale, int wv,
-                                             int li, int lg, const float *wt = nullptr) {
+                                             int li, int lg, const float *wt = nullptr,
+                                             float wsc = 1.f) {
   using T = typename BC::type;
 #pragma unroll
   for (int i = 0; i < BC::SPW; ++i) {
@@ -469,10 +464,10 @@ __device__ __forceinline__ void state_update(f32x4 (&Sa)[BC::SPW], const typenam
     for (int ks = 0; ks < BC::C / 32; ++ks) {
       Frag<T> a, b;
       frag_kr(a, X, BC::LDK, 16 * fb, 32 * ks, li, lg);
-      if (wt) {  // per-token weights on X's rows (this lane's k slots)
+      if (wt) {  // per-token weights wsc * wt[t] on X's rows (this lane's k slots)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          a.v[e] = from_f32<T>(to_f32(a.v[e]) * wt[32 * ks + 8 * lg + e]);
+          a.v[e] = from_f32<T>(to_f32(a.v[e]) * (wt[32 * ks + 8 * lg + e] * wsc));
       }
       frag_kr(b, Y, BC::LDV, 16 * vb, 32 * ks, li, lg);
       mma(Sa[i], a, b);
@@ -572,6 +567,10 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
   else
     state_load<BC>(Sa, p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr,
                    p.z_in ? p.z_in + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
+  // this segment's own adjoint (segments after the first), for the reverse scan
+  f32x4 Ra[BC::SPW];
+#pragma unroll
+  for (int i = 0; i < BC::SPW; ++i) Ra[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   BRegs<BC> R;
   load_chunk<BC, VK, true, true, true, true>(R, hr, t_begin, min(BC::C, N - t_begin), d, dv);
   __syncthreads();
@@ -633,9 +632,16 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
     }
     // forward state across the chunk
     state_update<BC>(Sa, decay ? sm.KW : sm.Fk, sm.Vp, decay ? sm.pw[Lc] : 1.f, wv, li, lg);
+    // the segment's adjoint: += sum_t gamma^(c0 - t_begin + t + 1) phi(q_t) dn_t^T
+    if (seg > 0)
+      state_update<BC>(Ra, sm.Fq, sm.dN, 1.f, wv, li, lg, decay ? sm.pw + 1 : nullptr,
+                       decay ? exp2f((float)(c0 - t_begin) * lg2) : 1.f);
     __syncthreads();
     if constexpr (kStageOut) store_rows<BC, VK>(rdq, sm.Os, BC::LDKS, BC::QCB, c0, Lc, d);
   }
+  if (seg > 0)  // into reverse slot seg - 1
+    slot_store<BC>(Ra, p.ws_r + ((size_t)(seg - 1) * p.BH + bh) * p.wrec, d, dv, p.slot_vec, wv,
+                   li, lg);
 }
 
 // ---- dk, dv: chunks right to left, adjoint state ------------------------------
@@ -768,47 +774,6 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DKV) bwd_dkv_kernel(BwdParams 
                     p.dz_in ? p.dz_in + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
 }
 
-// Reverse summary: the adjoint, from zero at its end, of segment
-// blockIdx.x + 1 (every segment but the first), into reverse slot blockIdx.x.
-template <class BC, bool VK>
-__global__ void __launch_bounds__(BC::NT) bwd_rsum_kernel(BwdParams p) {
-  using T = typename BC::type;
-  __shared__ SmemRsum<BC> sm;
-  const int seg = blockIdx.x + 1, bh = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int li = lane & 15, lg = lane >> 4;
-  const int d = p.d, dv = p.dv, N = p.N;
-  const int t_begin = seg * p.seg_len, t_end = min(N, t_begin + p.seg_len);
-  HeadRsrc hr;
-  hr.q = head_rsrc<T>(p.q, bh, N, d);
-  hr.k = hr.q;
-  hr.v = head_rsrc<T>(p.v, bh, N, dv);
-  hr.o = head_rsrc<T>(p.o, bh, N, dv);
-  hr.g = head_rsrc<T>(p.dout, bh, N, dv);
-  hr.den = head_rsrc<float>(p.den, bh, N, 1);
-  const float lg2 = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
-  for (int m = threadIdx.x; m <= BC::C; m += BC::NT) sm.pw[m] = exp2f((float)m * lg2);
-  f32x4 Sa[BC::SPW];
-  state_load<BC>(Sa, nullptr, nullptr, d, dv, wv, li, lg);
-  const int last = t_begin + ((t_end - t_begin - 1) / BC::C) * BC::C;
-  BRegs<BC> R;
-  load_chunk<BC, VK, true, false, false, true>(R, hr, last, min(BC::C, N - last), d, dv);
-  __syncthreads();
-  for (int c0 = last; c0 >= t_begin; c0 -= BC::C) {
-    const int Lc = min(BC::C, N - c0);
-    commit_feat<BC>(nullptr, sm.QW, sm.pw + 1, R.q, Lc, d, p.fmap);
-    commit_dn<BC>(sm.dN, R, Lc);
-    if (c0 > t_begin)
-      load_chunk<BC, VK, true, false, false, true>(R, hr, c0 - BC::C, BC::C, d, dv);
-    __syncthreads();
-    state_update<BC>(Sa, sm.QW, sm.dN, sm.pw[Lc], wv, li, lg);
-    __syncthreads();
-  }
-  slot_store<BC>(Sa, p.ws_r + ((size_t)(seg - 1) * p.BH + bh) * p.wrec, d, dv, p.slot_vec, wv,
-                 li, lg);
-}
-
 // Adjoint entering each segment from the right, in place: slot nseg-1 <-
 // (dS_out, dz_out); slot s <- gamma^len(s+1) slot (s+1) + dSh_(s+1) (which the
 // reverse summary left in slot s).  One thread per record element; every
@@ -847,21 +812,20 @@ template <class BC, bool VK>
 hipError_t run_bwd(const BwdParams &p, hipStream_t s) {
   static_assert(sizeof(SmemDq<BC>) <= 160 * 1024 && sizeof(SmemDkv<BC, true>) <= 160 * 1024,
                 "LDS budget");
-  if (p.nseg > 1) {
-    hipError_t e = launch_kernel("linear_bwd_rsummary", bwd_rsum_kernel<BC, VK>,
-                                 dim3(p.nseg - 1, p.BH), dim3(BC::NT), s, p);
-    if (e != hipSuccess) return e;
-    const size_t rec = (size_t)p.d * p.dv + p.d;
-    e = launch_kernel("linear_bwd_rscan", bwd_rscan_kernel,
-                      dim3((unsigned)((rec + 255) / 256), p.BH), dim3(256), s, p);
-    if (e != hipSuccess) return e;
-  }
+  // dq also leaves each segment's own adjoint in the reverse slots; the
+  // reverse scan then turns them into the adjoint entering each segment
   const dim3 grid(p.nseg, p.BH);
   hipError_t e = p.gamma ? launch_kernel("linear_bwd_dq", bwd_dq_kernel<BC, VK, true>, grid,
                                          dim3(BC::NT), s, p)
                          : launch_kernel("linear_bwd_dq", bwd_dq_kernel<BC, VK, false>, grid,
                                          dim3(BC::NT), s, p);
   if (e != hipSuccess) return e;
+  if (p.nseg > 1) {
+    const size_t rec = (size_t)p.d * p.dv + p.d;
+    e = launch_kernel("linear_bwd_rscan", bwd_rscan_kernel,
+                      dim3((unsigned)((rec + 255) / 256), p.BH), dim3(256), s, p);
+    if (e != hipSuccess) return e;
+  }
   return p.gamma ? launch_kernel("linear_bwd_dkv", bwd_dkv_kernel<BC, VK, true>, grid,
                                  dim3(BC::NT), s, p)
                  : launch_kernel("linear_bwd_dkv", bwd_dkv_kernel<BC, VK, false>, grid,
