@@ -77,6 +77,7 @@ namespace la {
 namespace {
 
 constexpr int kLdsBytes = 160 * 1024;
+constexpr size_t kStreamBytes = (size_t)256 << 20;  // last-level (MALL) cache size
 constexpr int kMaxSeg = 32;  // most segments per sequence
 
 // fp32 elements of one workspace slot record: S (d x dv), z (d), and the
@@ -201,15 +202,21 @@ __device__ __forceinline__ HeadBufs head_bufs(const PrefillParams &p, int bh) {
 
 // One 16-byte column block of row `tok` of a [N, ncols] tensor (zero where
 // the row or a column is outside it).  VK: ncols is a multiple of the vector
-// width, so a block is either wholly inside or wholly outside.
-template <typename T, bool VK>
+// width, so a block is either wholly inside or wholly outside.  NT: a
+// non-temporal (streaming) load, for data no later kernel can find in cache.
+template <typename T, bool VK, bool NT = false>
 __device__ __forceinline__ typename Vec16<T>::type load_block(
     __amdgpu_buffer_rsrc_t r, int tok, int col0, int ncols, bool row_ok) {
   constexpr int VEC = 16 / (int)sizeof(T);
   if constexpr (VK) {
     const bool ok = row_ok && col0 < ncols;
-    return buf_load16<T>(r, ok ? (uint32_t)(((size_t)tok * ncols + col0) * sizeof(T))
-                               : kOOB);
+    const uint32_t off = ok ? (uint32_t)(((size_t)tok * ncols + col0) * sizeof(T)) : kOOB;
+    if constexpr (NT) {
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      return __builtin_bit_cast(typename Vec16<T>::type,
+                                __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+    }
+    return buf_load16<T>(r, off);
   } else {
     typename Vec16<T>::type x;
 #pragma unroll
@@ -522,7 +529,7 @@ __device__ void conv_final(const PrefillParams &p, int bh) {
   }
 }
 
-template <class CF, bool WITH_Q, bool VK>
+template <class CF, bool WITH_Q, bool VK, bool NT = false>
 __device__ __forceinline__ void prefetch(ChunkRegs<CF> &R, const PrefillParams &p,
                                          const HeadBufs &hb, int c0, int Lc) {
   using T = typename CF::type;
@@ -531,14 +538,14 @@ __device__ __forceinline__ void prefetch(ChunkRegs<CF> &R, const PrefillParams &
   for (int r = 0; r < CF::RQ; ++r) {
     const int row = qrg * CF::RQ + r;
     if constexpr (WITH_Q)
-      R.q[r] = load_block<T, VK>(hb.q, c0 + row, qcb * CF::VEC, p.d, row < Lc);
-    R.k[r] = load_block<T, VK>(hb.k, c0 + row, qcb * CF::VEC, p.d, row < Lc);
+      R.q[r] = load_block<T, VK, NT>(hb.q, c0 + row, qcb * CF::VEC, p.d, row < Lc);
+    R.k[r] = load_block<T, VK, NT>(hb.k, c0 + row, qcb * CF::VEC, p.d, row < Lc);
   }
   const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
 #pragma unroll
   for (int r = 0; r < CF::RV; ++r) {
     const int row = vrg * CF::RV + r;
-    R.v[r] = load_block<T, VK>(hb.v, c0 + row, vcb * CF::VEC, p.dv, row < Lc);
+    R.v[r] = load_block<T, VK, NT>(hb.v, c0 + row, vcb * CF::VEC, p.dv, row < Lc);
   }
 }
 
@@ -1081,7 +1088,9 @@ __global__ void __launch_bounds__(CF::NT, (CH || CV) ? wpe_at_most_2<CF>() : CF:
 
 // Phase 1: each segment's own contribution, from a zero state (all but the
 // last segment; those are whole multiples of the chunk length).
-template <class CF, bool VK, bool CH, bool CV>
+// NT: streaming loads of k and v (the launch's k and v exceed the last-level
+// cache, so the chunk kernel will not find them there).
+template <class CF, bool VK, bool CH, bool CV, bool NT = false>
 __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF::WPE)
     summary_kernel(PrefillParams p) {
   using T = typename CF::type;
@@ -1107,7 +1116,7 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
 #pragma unroll
   for (int u = 0; u < PD; ++u)
     if (t_begin + u * CF::C < t_end)
-      prefetch<CF, false, VK>(R[u], p, hb, t_begin + u * CF::C, CF::C);
+      prefetch<CF, false, VK, NT>(R[u], p, hb, t_begin + u * CF::C, CF::C);
   [[maybe_unused]] ChanRegs<CF> A;
   [[maybe_unused]] const __amdgpu_buffer_rsrc_t ra =
       CH ? buf_rsrc(p.alpha + (size_t)bh * p.N * d, (uint32_t)((size_t)p.N * d * 4)) : hb.q;
@@ -1148,7 +1157,7 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
         if (cc + CF::C < t_end) chan_prefetch<CF, VK>(A, ra, p, cc + CF::C, CF::C);
       }
       if (cc + PD * CF::C < t_end)
-        prefetch<CF, false, VK>(R[u], p, hb, cc + PD * CF::C, CF::C);
+        prefetch<CF, false, VK, NT>(R[u], p, hb, cc + PD * CF::C, CF::C);
       __syncthreads();
       state_update<CF>(Sacc, sm.Ks, sm.Vs, gC, decay, wv, li, lg);
       if constexpr (CH) chan_scale<CF>(Sacc, sc.bl, wv, lg);
@@ -1252,8 +1261,19 @@ hipError_t run_vkcc(const PrefillParams &p, hipStream_t s) {
     return hipErrorNotSupported;  // refused on the host before any launch
   } else {
   if (p.nseg > 1) {
-    hipError_t e = launch_kernel("linear_summary", summary_kernel<CF, VK, CH, CV>,
-                                 dim3((p.nseg - 1) * p.nsplit, p.BH), dim3(CF::NT), s, p);
+    const dim3 grid((p.nseg - 1) * p.nsplit, p.BH);
+    // k and v beyond the last-level cache (256 MB): streaming loads
+    const bool stream = (size_t)p.BH * p.N * (p.d + p.dv) * sizeof(typename CF::type) >
+                        kStreamBytes;
+    hipError_t e;
+    if constexpr (!CH && !CV && VK)
+      e = stream ? launch_kernel("linear_summary", summary_kernel<CF, VK, false, false, true>,
+                                 grid, dim3(CF::NT), s, p)
+                 : launch_kernel("linear_summary", summary_kernel<CF, VK, CH, CV>, grid,
+                                 dim3(CF::NT), s, p);
+    else
+      e = launch_kernel("linear_summary", summary_kernel<CF, VK, CH, CV>, grid, dim3(CF::NT), s,
+                        p);
     if (e != hipSuccess) return e;
     e = launch_scan<CH>(p, s);
     if (e != hipSuccess) return e;
