@@ -140,8 +140,12 @@ def test_backward_reuses_forward_workspace(decay):
     torch.cuda.synchronize()
     for name, a, b in zip(("dq", "dk", "dv", "dS_in", "dz_in"), got, ref):
         assert torch.equal(a, b), name
-    with pytest.raises(RuntimeError):
+    with pytest.raises(RuntimeError):  # below the forward's workspace size
         la.backward(q, k, v, o, den, do, gamma=gamma, S_in=S0, z_in=z0, fwd_workspace=ws[:-4])
+    big = torch.empty(need + 8, dtype=torch.uint8, device=DEV)
+    with pytest.raises(RuntimeError):  # not 4-byte aligned
+        la.backward(q, k, v, o, den, do, gamma=gamma, S_in=S0, z_in=z0,
+                    fwd_workspace=big[1:1 + need])
 
 
 def test_backward_no_tokens_passes_state_gradient():
