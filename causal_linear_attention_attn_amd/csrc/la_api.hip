@@ -165,7 +165,7 @@ size_t la_prefill_workspace_size(const la_prefill_args *a) {
   if (BH == 0 || a->N == 0) return 0;
   if (a->rule == LA_RULE_LINEAR)
     return la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16,
-                           a->conv_weight ? a->conv_width : 0)
+                           a->conv_weight ? a->conv_width : 0, a->alpha != nullptr)
         .ws_bytes;
   return la::delta_workspace_bytes(BH, a->N, a->d, a->dtype == LA_BF16);
 }
@@ -213,7 +213,7 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   la::LinearPlan plan{};
   size_t ws_need;
   if (linear) {
-    plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io, cw);
+    plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io, cw, a->alpha != nullptr);
     ws_need = plan.ws_bytes;
   } else {
     ws_need = la::delta_workspace_bytes(BH, a->N, a->d, bf16_io);

@@ -111,8 +111,10 @@ hipError_t launch_kernel(const char *name, F kernel, dim3 grid, dim3 block, hipS
   return e;
 }
 
-// conv_width > 0: a short convolution runs in front of q, k, v
-LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16, int conv_width);
+// conv_width > 0: a short convolution runs in front of q, k, v; chan: a
+// per-key-channel decay (its kernels' occupancy sets the segment count)
+LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16, int conv_width,
+                       bool chan = false);
 bool linear_combo_supported(int d, int dv, bool bf16, bool chan_decay, bool conv);
 // The forward's summary and scan kernels only: the state entering each
 // segment, in the workspace slots (nothing to do with one segment).

@@ -1318,21 +1318,26 @@ hipError_t run_prefix(const PrefillParams &p, hipStream_t s) {
   return launch_scan<false>(p, s);
 }
 
-// Workgroups of chunk_kernel<CF> that fit on one CU (queried once).
-template <class CF, bool CV>
+// Workgroups of chunk_kernel<CF> that fit on one CU (queried once per
+// instantiation).
+template <class CF, bool CH, bool CV>
 int resident_per_cu() {
-  static std::atomic<int> cached{0};
-  int v = cached.load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<CF, true, false, CV>,
-                                                   CF::NT, 0) != hipSuccess ||
-      n < 1) {
-    (void)hipGetLastError();
-    n = 1;
+  if constexpr (chunk_lds<CF, CH, CV>() > kLdsBytes) {
+    return 1;  // refused at launch anyway
+  } else {
+    static std::atomic<int> cached{0};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<CF, true, CH, CV>,
+                                                     CF::NT, 0) != hipSuccess ||
+        n < 1) {
+      (void)hipGetLastError();
+      n = 1;
+    }
+    cached.store(n, std::memory_order_relaxed);
+    return n;
   }
-  cached.store(n, std::memory_order_relaxed);
-  return n;
 }
 
 // Instantiations: bf16 uses 64-token chunks; fp32 uses 32-token chunks
@@ -1347,25 +1352,28 @@ using F128x64 = Cfg<float, 128, 64, 32, 8>;
 using F128x128 = Cfg<float, 128, 128, 32, 8>;
 
 template <class CF>
-void fill_plan(LinearPlan &pl, bool conv) {
+void fill_plan(LinearPlan &pl, bool conv, bool chan) {
   pl.chunk = CF::C;
   pl.threads = CF::NT;
-  pl.per_cu = conv ? resident_per_cu<CF, true>() : resident_per_cu<CF, false>();
+  if (chan)
+    pl.per_cu = conv ? resident_per_cu<CF, true, true>() : resident_per_cu<CF, true, false>();
+  else
+    pl.per_cu = conv ? resident_per_cu<CF, false, true>() : resident_per_cu<CF, false, false>();
 }
 
 }  // namespace
 
-LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io, int conv_width) {
+LinearPlan plan_linear(int BH, int N, int d, int dv, bool bf16_io, int conv_width, bool chan) {
   LinearPlan pl{};
   pl.dk = d <= 64 ? 64 : 128;
   pl.dv_pad = dv <= 64 ? 64 : 128;
   const bool cv = conv_width > 0;
   if (bf16_io) {
-    if (pl.dk == 64) pl.dv_pad == 64 ? fill_plan<B64x64>(pl, cv) : fill_plan<B64x128>(pl, cv);
-    else pl.dv_pad == 64 ? fill_plan<B128x64>(pl, cv) : fill_plan<B128x128>(pl, cv);
+    if (pl.dk == 64) pl.dv_pad == 64 ? fill_plan<B64x64>(pl, cv, chan) : fill_plan<B64x128>(pl, cv, chan);
+    else pl.dv_pad == 64 ? fill_plan<B128x64>(pl, cv, chan) : fill_plan<B128x128>(pl, cv, chan);
   } else {
-    if (pl.dk == 64) pl.dv_pad == 64 ? fill_plan<F64x64>(pl, cv) : fill_plan<F64x128>(pl, cv);
-    else pl.dv_pad == 64 ? fill_plan<F128x64>(pl, cv) : fill_plan<F128x128>(pl, cv);
+    if (pl.dk == 64) pl.dv_pad == 64 ? fill_plan<F64x64>(pl, cv, chan) : fill_plan<F64x128>(pl, cv, chan);
+    else pl.dv_pad == 64 ? fill_plan<F128x64>(pl, cv, chan) : fill_plan<F128x128>(pl, cv, chan);
   }
   const long chunks = N > 0 ? ((long)N + pl.chunk - 1) / pl.chunk : 0;
   long nseg = 1;
