@@ -95,7 +95,8 @@ void prof_commit(const char *name, ProfSlot ps, hipError_t launch_status) {
 
 namespace {
 
-constexpr int kMaxGridY = 65535;
+// A dispatch's grid is at most 2^32 - 1 work-items along each axis.
+constexpr unsigned long long kMaxGridItems = 0xffffffffull;
 constexpr size_t kMaxHeadBytes = 0x7fff0000u;
 constexpr int kMaxConvWidth = 4;
 
@@ -111,11 +112,16 @@ int to_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_EHIP; }
 int check_prefill_shape(const la_prefill_args *a) {
   if (!a) return LA_EINVAL;
   if (a->B < 0 || a->H < 0 || a->N < 0 || !dims_ok(a->d, a->dv)) return LA_EINVAL;
+  if ((long long)a->B * a->H > 0x7fffffffLL) return LA_EUNSUPPORTED;
   if (a->dtype != LA_F32 && a->dtype != LA_BF16) return LA_EINVAL;
   if (a->rule != LA_RULE_LINEAR && a->rule != LA_RULE_DELTA) return LA_EINVAL;
   if (a->fmap != LA_FMAP_IDENTITY && a->fmap != LA_FMAP_ELU1) return LA_EINVAL;
   if (a->rule == LA_RULE_DELTA && a->fmap != LA_FMAP_IDENTITY) return LA_EINVAL;
-  if ((long long)a->B * a->H > kMaxGridY) return LA_EUNSUPPORTED;
+  // the delta rule's sequential pass runs 512 threads per (head, 16 value
+  // columns) along one grid axis; every other grid puts heads on y and z
+  if (a->rule == LA_RULE_DELTA &&
+      (unsigned long long)a->B * a->H * ((a->dv + 15) / 16) * 512 > kMaxGridItems)
+    return LA_EUNSUPPORTED;
   // one head's q/k/v/o must be addressable with 32-bit byte offsets
   const size_t esz = a->dtype == LA_BF16 ? 2 : 4;
   const size_t dmax = a->d > a->dv ? a->d : a->dv;
@@ -275,9 +281,9 @@ namespace {
 int check_backward_shape(const la_backward_args *a) {
   if (!a) return LA_EINVAL;
   if (a->B < 0 || a->H < 0 || a->N < 0 || !dims_ok(a->d, a->dv)) return LA_EINVAL;
+  if ((long long)a->B * a->H > 0x7fffffffLL) return LA_EUNSUPPORTED;
   if (a->dtype != LA_F32 && a->dtype != LA_BF16) return LA_EINVAL;
   if (a->fmap != LA_FMAP_IDENTITY && a->fmap != LA_FMAP_ELU1) return LA_EINVAL;
-  if ((long long)a->B * a->H > kMaxGridY) return LA_EUNSUPPORTED;
   const size_t esz = a->dtype == LA_BF16 ? 2 : 4;
   const size_t dmax = a->d > a->dv ? a->d : a->dv;
   if ((size_t)a->N * dmax * esz > kMaxHeadBytes) return LA_EUNSUPPORTED;
@@ -402,7 +408,8 @@ int la_decode_step(const la_decode_args *a, void *stream) {
   if (a->fmap != LA_FMAP_IDENTITY && a->fmap != LA_FMAP_ELU1) return LA_EINVAL;
   const bool delta = a->rule == LA_RULE_DELTA;
   const long long BH = (long long)a->B * a->H;
-  if (BH > 0x7fffffffLL) return LA_EUNSUPPORTED;
+  // one 256-thread workgroup per (b, h) along one grid axis
+  if ((unsigned long long)BH * 256 > kMaxGridItems) return LA_EUNSUPPORTED;
   if (delta) {
     if (a->fmap != LA_FMAP_IDENTITY || a->gamma || a->z) return LA_EINVAL;
     if (BH > 0 && !a->g) return LA_EINVAL;

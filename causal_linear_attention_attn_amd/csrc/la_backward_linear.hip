@@ -541,7 +541,8 @@ template <class BC, bool VK, bool DEC>
 __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p) {
   using T = typename BC::type;
   __shared__ SmemDq<BC> sm;
-  const int seg = blockIdx.x, bh = blockIdx.y;
+  const int seg = blockIdx.x, bh = grid_head();
+  if (bh >= p.BH) return;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
@@ -649,7 +650,8 @@ template <class BC, bool VK, bool DEC>
 __global__ void __launch_bounds__(BC::NT, BC::WPE_DKV) bwd_dkv_kernel(BwdParams p) {
   using T = typename BC::type;
   __shared__ SmemDkv<BC, DEC> sm;
-  const int seg = blockIdx.x, bh = blockIdx.y;
+  const int seg = blockIdx.x, bh = grid_head();
+  if (bh >= p.BH) return;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
@@ -779,7 +781,8 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DKV) bwd_dkv_kernel(BwdParams 
 // reverse summary left in slot s).  One thread per record element; every
 // record is loaded before the chain.
 __global__ void __launch_bounds__(256) bwd_rscan_kernel(BwdParams p) {
-  const int bh = blockIdx.y;
+  const int bh = grid_head();
+  if (bh >= p.BH) return;
   const size_t dd = (size_t)p.d * p.dv;
   const size_t rec = dd + p.d;
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -814,7 +817,7 @@ hipError_t run_bwd(const BwdParams &p, hipStream_t s) {
                 "LDS budget");
   // dq also leaves each segment's own adjoint in the reverse slots; the
   // reverse scan then turns them into the adjoint entering each segment
-  const dim3 grid(p.nseg, p.BH);
+  const dim3 grid = head_grid(p.nseg, p.BH);
   hipError_t e = p.gamma ? launch_kernel("linear_bwd_dq", bwd_dq_kernel<BC, VK, true>, grid,
                                          dim3(BC::NT), s, p)
                          : launch_kernel("linear_bwd_dq", bwd_dq_kernel<BC, VK, false>, grid,
@@ -823,7 +826,7 @@ hipError_t run_bwd(const BwdParams &p, hipStream_t s) {
   if (p.nseg > 1) {
     const size_t rec = (size_t)p.d * p.dv + p.d;
     e = launch_kernel("linear_bwd_rscan", bwd_rscan_kernel,
-                      dim3((unsigned)((rec + 255) / 256), p.BH), dim3(256), s, p);
+                      head_grid((unsigned)((rec + 255) / 256), p.BH), dim3(256), s, p);
     if (e != hipSuccess) return e;
   }
   return p.gamma ? launch_kernel("linear_bwd_dkv", bwd_dkv_kernel<BC, VK, true>, grid,

@@ -13,6 +13,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
+
+// Head of a workgroup in a grid built by head_grid (la_internal.hpp).
+__device__ __forceinline__ int grid_head() {
+  return (int)(blockIdx.y + 65535u * blockIdx.z);
+}
 constexpr int LA_MAXD = 128;  // largest d and dv
 
 // ---------------------------------------------------------------------------

@@ -86,6 +86,15 @@ struct DecodeParams {
 
 int device_cu_count();  // cached per device
 
+// Grids with one row of workgroups per head put the head on y and, past the
+// y limit, on z: head = blockIdx.y + kGridY * blockIdx.z (workgroups with a
+// head index past B*H return at once).
+constexpr int kGridY = 65535;
+inline dim3 head_grid(unsigned nx, int BH) {
+  const unsigned y = BH < kGridY ? (unsigned)BH : (unsigned)kGridY;
+  return dim3(nx, y, (unsigned)((BH + kGridY - 1) / kGridY));
+}
+
 // Kernel timing (off unless la_profile_enable turned it on).  A launch
 // through launch_kernel takes a pair of events from prof_slot and hands them
 // to the dispatch itself (hipExtLaunchKernel stamps them when the kernel

@@ -170,7 +170,8 @@ __global__ void __launch_bounds__(kThreads) prep_kernel(PrefillParams p) {
   using T = typename CF::type;
   constexpr int C = CF::C, FLD = CF::FLD, TLD = CF::TLD, NRB = CF::NRB;
   __shared__ SmemPrep<CF> sm;
-  const int chunk = blockIdx.x, bh = blockIdx.y;
+  const int chunk = blockIdx.x, bh = grid_head();
+  if (bh >= p.BH) return;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
@@ -1072,7 +1073,7 @@ hipError_t run_vkd(const PrefillParams &p, hipStream_t s) {
   static_assert(sizeof(SmemPrep<CF>) <= 64 * 1024, "LDS budget (prep)");
   static_assert(sizeof(SmemSeq<CF>) <= 160 * 1024, "LDS budget (seq)");
   const int nch = (p.N + CF::C - 1) / CF::C;
-  hipError_t e = launch_kernel("delta_prep", prep_kernel<CF, VK, DECAY>, dim3(nch, p.BH),
+  hipError_t e = launch_kernel("delta_prep", prep_kernel<CF, VK, DECAY>, head_grid(nch, p.BH),
                                dim3(kThreads), s, p);
   if (e != hipSuccess) return e;
   const int nsl = (p.dv + CF::W - 1) / CF::W;

@@ -10,15 +10,18 @@
 //     num_i = gamma^(i+1) phi(q_i) S-  +  sum_{j<=i} gamma^(i-j) (phi(q_i).phi(k_j)) v_j
 //     den_i = gamma^(i+1) phi(q_i).z- +  sum_{j<=i} gamma^(i-j) (phi(q_i).phi(k_j))  + eps
 //     S+    = gamma^L S- + sum_j gamma^(L-1-j) phi(k_j) v_j^T   (z+ likewise)
-// With the weighted keys kw_j = gamma^(L-1-j) phi(k_j) the decay factor
-// gamma^(i-j) = gamma^(i+1-L) gamma^(L-1-j) splits into a row factor and the
-// key weight, and multiplying num_i and den_i by gamma^(L-1-i) leaves
-//     num'_i = phi(q_i) (gamma^L S-)  +  sum_{j<=i} (phi(q_i).kw_j) v_j
-//     den'_i = phi(q_i).(gamma^L z-)  +  sum_{j<=i} (phi(q_i).kw_j)  +  eps gamma^(L-1-i)
-//     S+     = gamma^L S- + KW^T V,   z+ = gamma^L z- + KW^T 1
-// so no decay factor is applied per score, and every factor is at most 1.
-// The weights underflow for gamma^(L-1) below the fp32 range, so gamma must
-// be at least 1/2 (documented in linattn.h).
+// and o_i = num_i / den_i.  Every decay factor there is a power gamma^m with
+// m >= 0, and each is applied where it occurs: the scores take gamma^(i-j)
+// after their product (one exponential per four scores of a lane, gamma^e
+// times the constants gamma^-r, r < 4), the state read gamma^(i+1) per query
+// row (one value per lane: each lane holds one token), and the key fragments
+// of the state update gamma^(L-1-j) per token.  No factor exceeds 1, so
+// nothing overflows for any gamma in (0, 1]; a factor that underflows stands
+// for a contribution far below fp32 resolution next to the token's own.
+// log2 gamma is clamped at -40, which keeps gamma^-3 finite (below
+// gamma = 2^-40 every earlier token then weighs under 2^-40 of its own).
+// The segment summaries only accumulate the state, with weighted keys
+// kw_j = gamma^(L-1-j) phi(k_j): S+ = gamma^L S- + KW^T V.
 //
 // The normaliser rides along as one more 16-column tile of the value side:
 // the state is kept as [S | z z ... z] (z replicated over 16 columns) and V
@@ -27,15 +30,16 @@
 // + V'^T A^T), which gives each lane four consecutive output columns of one
 // token and the denominator of that same token.
 //
-// LDS tiles are all row-major: Phi_q, KW and V rows as loaded (16-byte
-// stores), the scaled state copy S'^T (value columns + normaliser rows by
+// LDS tiles are all row-major: Phi_q, Phi_k and V rows as loaded (16-byte
+// stores), the state copy S'^T (value columns + normaliser rows by
 // features), and an output staging tile.  Token contractions (A V and
-// KW^T V) read transposed fragments with the gfx950 LDS transpose load, so no
-// tile is ever written transposed.  Scores are computed transposed (KW as the
-// A operand, Phi_q as B), which leaves in each lane one query row and four
-// consecutive keys: two such tiles form the A^T operand of the next product
-// straight from registers.  The fp32 state lives in matrix-core accumulators
-// and is never rounded; the scaled bf16 copy feeds the next chunk's read.
+// Phi_k^T V) read transposed fragments with the gfx950 LDS transpose load, so
+// no tile is ever written transposed.  Scores are computed transposed (Phi_k
+// as the A operand, Phi_q as B), which leaves in each lane one query row and
+// four consecutive keys: two such tiles form the A^T operand of the next
+// product straight from registers.  The fp32 state lives in matrix-core
+// accumulators and is never rounded; its bf16 copy feeds the next chunk's
+// read.
 //
 // Long sequences are split into segments processed in parallel (a two-level
 // scan, "Transformers Are RNNs": the recurrence is a prefix sum):
@@ -136,7 +140,7 @@ struct alignas(16) SmemChunk {
   T Vs[CF::C * CF::VTLD];     // v rows
   T St[CF::SROWS * CF::QLD];  // gamma^L [S | z]^T for the next state read
   T Os[CF::C * CF::VLD];      // output staging
-  float pw[CF::C + 4];        // gamma^m, m = 0..C
+  float pw[CF::C + 4];        // gamma^m, m = 0..C (decay folded into key weights)
 };
 
 template <class CF>
@@ -549,13 +553,15 @@ __device__ __forceinline__ void prefetch(ChunkRegs<CF> &R, const PrefillParams &
   }
 }
 
-// Registers -> LDS: phi(q) rows, weighted phi(k) rows, v rows.  Keys past
-// the chunk get weight 0 and feature columns past d are zeroed (phi(0) = 1
-// would otherwise count them); queries need no mask (their padded features
-// meet zero keys and zero state rows).  The feature map and the column mask
-// are uniform per launch and taken as branches, so the common case carries
-// no per-element selects; key weights are 1 for a full chunk without decay.
-template <class CF, bool WITH_Q, bool ELU, bool CH, bool CV>
+// Registers -> LDS: phi(q) rows, phi(k) rows, v rows.  Keys past the chunk
+// get weight 0 and feature columns past d are zeroed (phi(0) = 1 would
+// otherwise count them); queries need no mask (their padded features meet
+// zero keys and zero state rows).  The feature map and the column mask are
+// uniform per launch and taken as branches, so the common case carries no
+// per-element selects.  The segment summary (no queries) weights its keys by
+// gamma^(Lc-1-j); the chunk kernel's keys stay unweighted (it applies the
+// decay to its scores and key fragments).
+template <class CF, bool WITH_Q, bool ELU, bool CH, bool CV, bool KW>
 __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R,
                                             const ConvOut<CF, WITH_Q> *Y,
                                             ConvRows<CF, WITH_Q> *P,
@@ -565,7 +571,7 @@ __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R,
                                             const SmemChan<CF> *sc) {
   using T = typename CF::type;
   constexpr int VEC = CF::VEC;
-  const bool weighted = p.gamma != nullptr || Lc < CF::C;
+  const bool weighted = (KW && p.gamma != nullptr) || Lc < CF::C;
   const bool colmask = p.d < CF::DK;  // feature columns past d
   const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
   const int col0 = qcb * VEC;
@@ -597,8 +603,9 @@ __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R,
       x[e] = ELU ? phi_elu1(xk) : xk;
       if constexpr (CH) x[e] *= __expf(lbm[e] - lbr[e]);
     }
-    // key weights gamma^(Lc-1-j), 0 past the chunk
-    const float w = !weighted ? 1.f : row < Lc ? pw[Lc - 1 - row] : 0.f;
+    // key weights: 0 past the chunk; gamma^(Lc-1-j) where the decay is
+    // folded into the keys (KW)
+    const float w = !weighted ? 1.f : row >= Lc ? 0.f : KW ? pw[Lc - 1 - row] : 1.f;
     if (__builtin_expect(colmask, 0)) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) x[e] = col0 + e < p.d ? x[e] * w : 0.f;
@@ -613,7 +620,7 @@ __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R,
   }
 }
 
-template <class CF, bool WITH_Q, bool CH = false, bool CV = false>
+template <class CF, bool WITH_Q, bool CH, bool CV, bool KW>
 __device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type *Qs,
                                        typename CF::type *Ks, typename CF::type *Vs,
                                        const float *pw, const PrefillParams &p, int Lc,
@@ -629,9 +636,9 @@ __device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type
       ConvOut<CF, WITH_Q> Y;
       conv_gather<CF, WITH_Q>(Y, R, Qs, Ks, Vs, *cs);
       if (p.fmap != 0)
-        commit_rows<CF, WITH_Q, true, CH, true>(R, &Y, &P, Qs, Ks, pw, p, Lc, sc);
+        commit_rows<CF, WITH_Q, true, CH, true, KW>(R, &Y, &P, Qs, Ks, pw, p, Lc, sc);
       else
-        commit_rows<CF, WITH_Q, false, CH, true>(R, &Y, &P, Qs, Ks, pw, p, Lc, sc);
+        commit_rows<CF, WITH_Q, false, CH, true, KW>(R, &Y, &P, Qs, Ks, pw, p, Lc, sc);
 #pragma unroll
       for (int r = 0; r < CF::RV; ++r) P.v[r] = pack_vec<CF>(Y.v[r]);
     }
@@ -651,9 +658,9 @@ __device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type
     }
   } else {
     if (p.fmap != 0)
-      commit_rows<CF, WITH_Q, true, CH, false>(R, nullptr, nullptr, Qs, Ks, pw, p, Lc, sc);
+      commit_rows<CF, WITH_Q, true, CH, false, KW>(R, nullptr, nullptr, Qs, Ks, pw, p, Lc, sc);
     else
-      commit_rows<CF, WITH_Q, false, CH, false>(R, nullptr, nullptr, Qs, Ks, pw, p, Lc, sc);
+      commit_rows<CF, WITH_Q, false, CH, false, KW>(R, nullptr, nullptr, Qs, Ks, pw, p, Lc, sc);
 #pragma unroll
     for (int r = 0; r < CF::RV; ++r) {
       const int row = vrg * CF::RV + r;
@@ -711,9 +718,75 @@ __device__ __forceinline__ void state_update(f32x4 (&Sacc)[CF::FPW][CF::TPW],
   }
 }
 
-// Scale the state by gamma^L of the chunk about to be read (decay only) and
-// write its T-precision copy, transposed: St[n][f] = S[f][n].  Scaling the
-// accumulator itself means the chunk's state update then only adds KW^T V.
+// gamma^-1, gamma^-2, gamma^-3 from the clamped log2 gamma (finite).
+struct InvPow {
+  float c1, c2, c3;
+};
+__device__ __forceinline__ InvPow inv_pows(float lg2) {
+  InvPow c;
+  c.c1 = exp2f(-lg2);
+  c.c2 = exp2f(-2.f * lg2);
+  c.c3 = exp2f(-3.f * lg2);
+  return c;
+}
+
+// log2 of a per-head decay, clamped at -40 (see the file header).
+__device__ __forceinline__ float decay_log2(const float *gamma, int h) {
+  return gamma ? fmaxf(log2f(gamma[h]), -40.f) : 0.f;
+}
+
+// [S | z] <- gamma^Lc [S | z] + Phi_k^T diag(w) [V | 1] for this wave's
+// tiles, w_j = gamma^(Lc-1-j): the chunk kernel's keys are unweighted in LDS,
+// so the weights go onto the key fragments in registers (a lane's eight
+// slots are tokens t0..t0+3 and t0+16..t0+19).  Rows past the chunk are
+// zero in LDS, so their (finite) weights do not matter.
+template <class CF>
+__device__ __forceinline__ void state_update_decay(f32x4 (&Sacc)[CF::FPW][CF::TPW],
+                                                   const typename CF::type *Ks,
+                                                   const typename CF::type *Vs, int Lc,
+                                                   float lg2, int wv, int li, int lg) {
+  using T = typename CF::type;
+  const float gL = exp2f((float)Lc * lg2);
+#pragma unroll
+  for (int a = 0; a < CF::FPW; ++a)
+#pragma unroll
+    for (int b = 0; b < CF::TPW; ++b) Sacc[a][b] *= gL;
+  const InvPow c = inv_pows(lg2);
+  Frag<T> ones;
+  frag_fill(ones, 1.f);
+#pragma unroll
+  for (int ks = 0; ks < CF::KSC; ++ks) {
+    const int t0 = 32 * ks + 4 * lg;
+    float w[8];
+    {
+      const float blo = exp2f((float)max(Lc - 1 - t0, 0) * lg2);
+      const float bhi = exp2f((float)max(Lc - 1 - (t0 + 16), 0) * lg2);
+      w[0] = blo; w[1] = blo * c.c1; w[2] = blo * c.c2; w[3] = blo * c.c3;
+      w[4] = bhi; w[5] = bhi * c.c1; w[6] = bhi * c.c2; w[7] = bhi * c.c3;
+    }
+#pragma unroll
+    for (int a = 0; a < CF::FPW; ++a) {
+      Frag<T> kf;
+      lds_frag_tr(kf, Ks, CF::QLD, t0, t0 + 16, 16 * srow<CF>(wv, a), li);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) frag_set(kf, e, frag_elem(kf, e) * w[e]);
+#pragma unroll
+      for (int b = 0; b < CF::TPW; ++b) {
+        const int tn = scol<CF>(wv, b);
+        if (tn < CF::NVT) {
+          Frag<T> vf;
+          lds_frag_tr(vf, Vs, CF::VTLD, t0, t0 + 16, 16 * tn, li);
+          mma(Sacc[a][b], kf, vf);
+        } else if (tn == CF::NVT) {
+          mma(Sacc[a][b], kf, ones);
+        }
+      }
+    }
+  }
+}
+
+// Scale the state (decay only) and write its T-precision copy, transposed:
+// St[n][f] = S[f][n].
 template <class CF>
 __device__ __forceinline__ void rescale_and_copy_state(typename CF::type *St,
                                                        f32x4 (&Sacc)[CF::FPW][CF::TPW],
@@ -865,16 +938,24 @@ __device__ __forceinline__ void fill_powers(float *pw, float log2g) {
   for (int m = threadIdx.x; m <= CF::C; m += CF::NT) pw[m] = exp2f((float)m * log2g);
 }
 
+// How a per-head decay enters the chunk kernel (see the file header):
+// none; folded into the key weights and the state copy (gamma >= 1/2); or
+// each factor applied where it occurs (faster decays).
+enum DecayMode : int { kDecNone = 0, kDecKeys = 1, kDecElem = 2 };
+
 // Outputs of one chunk for one output role: query row block RB (compile-time,
 // so the causal structure of the score tiles costs no branches or selects)
 // and column group cg of the value tiles; normalised rows go to the staging
-// tile Os.
-template <class CF, int RB, bool DN>
+// tile Os.  MODE kDecElem: the scores take gamma^(i-j) and the state read
+// gamma^(i+1) (lg2 = log2 gamma); kDecKeys: numerator and denominator carry
+// gamma^(L-1-i), so eps does too.
+template <class CF, int RB, bool DN, int MODE>
 __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillParams &p, int Lc,
-                                              int cg, int li, int lg, float *den_row) {
+                                              int cg, int li, int lg, float *den_row,
+                                              float lg2) {
   using T = typename CF::type;
   const int irow = 16 * RB + li;  // this lane's query row
-  // ---- scores, transposed: at[tj][r] = phi(q_i) . kw_j, i = irow,
+  // ---- scores, transposed: at[tj][r] = phi(q_i) . phi(k_j), i = irow,
   //      j = 16 tj + 4 lg + r (lower triangle only) ----
   Frag<T> qf[CF::KSD];
 #pragma unroll
@@ -893,10 +974,24 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillPa
       }
     }
   }
+  if constexpr (MODE == kDecElem) {  // gamma^(i-j) = gamma^e gamma^-r, e = i - 16 tj - 4 lg
+    const InvPow c = inv_pows(lg2);
+#pragma unroll
+    for (int tj = 0; tj <= RB; ++tj) {
+      // e < 0 only where all four keys are masked below (then any finite factor)
+      const float f = exp2f((float)max(irow - 16 * tj - 4 * lg, 0) * lg2);
+      at[tj][0] *= f;
+      at[tj][1] *= f * c.c1;
+      at[tj][2] *= f * c.c2;
+      at[tj][3] *= f * c.c3;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) at[RB][r] = 4 * lg + r <= li ? at[RB][r] : 0.f;
 
-  // ---- O'^T = (gamma^L [S | z])^T Phi_q^T + [V | 1]^T A^T ----
+  // ---- O^T = [S' | z']^T Phi_q^T + [V | 1]^T A^T, with the state copy
+  //      S' = S- (row factor gamma^(i+1) applied after the product, kDecElem)
+  //      or S' = gamma^L S- (kDecKeys) ----
   f32x4 acc[CF::NPW], accd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int a = 0; a < CF::NPW; ++a) acc[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -911,6 +1006,12 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillPa
     Frag<T> zf;
     lds_frag(zf, sm.St + (CF::DV + li) * CF::QLD + 32 * ks + 8 * lg);
     mma(accd, zf, qf[ks]);
+  }
+  if constexpr (MODE == kDecElem) {
+    const float gq = exp2f((float)(irow + 1) * lg2);
+#pragma unroll
+    for (int a = 0; a < CF::NPW; ++a) acc[a] *= gq;
+    accd *= gq;
   }
   Frag<T> ones;
   frag_fill(ones, 1.f);
@@ -937,11 +1038,14 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillPa
 
   // ---- normalise: lane holds columns 16 tn + 4 lg + r of token irow ----
   {
-    const float den = accd[0] + p.eps * sm.pw[max(Lc - 1 - irow, 0)];
+    const float den =
+        accd[0] + (MODE == kDecKeys ? p.eps * sm.pw[max(Lc - 1 - irow, 0)] : p.eps);
     const float rd = __builtin_amdgcn_rcpf(den);
-    // the token's own denominator phi(q).z + eps (den carries gamma^(L-1-i))
+    // the token's own denominator phi(q).z + eps (kDecKeys: den carries
+    // gamma^(L-1-i))
     if constexpr (DN) {
-      if (cg == 0 && lg == 0 && irow < Lc) den_row[irow] = accd[0] / sm.pw[Lc - 1 - irow] + p.eps;
+      if (cg == 0 && lg == 0 && irow < Lc)
+        den_row[irow] = MODE == kDecKeys ? accd[0] / sm.pw[Lc - 1 - irow] + p.eps : den;
     }
 #pragma unroll
     for (int a = 0; a < CF::NPW; ++a)
@@ -949,6 +1053,99 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillPa
                  acc[a][0] * rd, acc[a][1] * rd, acc[a][2] * rd, acc[a][3] * rd);
   }
 
+}
+
+// The chunk loop of one segment (chunk_kernel), for one way of applying a
+// per-head decay (MODE).
+template <class CF, bool VK, bool CH, bool CV, bool DN, int MODE>
+__device__ __forceinline__ void chunk_loop(SmemChunk<CF> &sm, ChanSmem<CF, CH> &sc,
+                                           ConvSmem<CF, CV> &cs, const PrefillParams &p,
+                                           const HeadBufs &hb,
+                                           f32x4 (&Sacc)[CF::FPW][CF::TPW], ChunkRegs<CF> &R,
+                                           ChanRegs<CF> &A, __amdgpu_buffer_rsrc_t ra, int bh,
+                                           int t_begin, int t_end, float lg2, int wv, int li,
+                                           int lg) {
+  using T = typename CF::type;
+  using V = typename CF::vec;
+  const int d = p.d, dv = p.dv, N = p.N;
+  constexpr bool KEYS = MODE == kDecKeys;
+  if constexpr (!CH)
+    rescale_and_copy_state<CF>(sm.St, Sacc, KEYS ? sm.pw[min(CF::C, N - t_begin)] : 1.f, KEYS,
+                               wv, li, lg);
+
+  const int rb = wv % CF::NRB, cg = wv / CF::NRB;  // output role
+  for (int c0 = t_begin; c0 < t_end; c0 += CF::C) {
+    const int Lc = min(CF::C, N - c0);
+    if constexpr (CH) {  // the chunk's per-channel decay prefix sums
+      chan_logs<CF>(A, sc, d, Lc);
+      __syncthreads();
+      chan_prefix<CF>(sc, Lc, false);
+      __syncthreads();
+    }
+    commit<CF, true, CH, CV, KEYS>(R, sm.Qs, sm.Ks, sm.Vs, sm.pw, p, Lc, chan_ptr<CF>(sc),
+                                   conv_ptr<CF>(cs));
+    if constexpr (CH) {  // state read from diag(exp(lb_m)) S-
+      chan_scale<CF>(Sacc, sc.bm, wv, lg);
+      rescale_and_copy_state<CF>(sm.St, Sacc, 1.f, false, wv, li, lg);
+      if (c0 + CF::C < t_end)
+        chan_prefetch<CF, VK>(A, ra, p, c0 + CF::C, min(CF::C, N - c0 - CF::C));
+    }
+    if (c0 + CF::C < t_end)
+      prefetch<CF, true, VK>(R, p, hb, c0 + CF::C, min(CF::C, N - c0 - CF::C));
+    __syncthreads();
+
+    float *dno = DN ? p.den_out + (size_t)bh * N + c0 : nullptr;
+    if constexpr (CF::NRB == 2) {
+      if (rb == 0) chunk_outputs<CF, 0, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2);
+      else chunk_outputs<CF, 1, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2);
+    } else {
+      static_assert(CF::NRB == 4, "row blocks per chunk");
+      switch (rb) {
+        case 0: chunk_outputs<CF, 0, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2); break;
+        case 1: chunk_outputs<CF, 1, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2); break;
+        case 2: chunk_outputs<CF, 2, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2); break;
+        default: chunk_outputs<CF, 3, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2); break;
+      }
+    }
+
+    // ---- carry the state across the chunk ----
+    // (the accumulator already carries gamma^Lc with the decay folded into
+    // the keys, or diag(exp(lb_m)) with a per-channel decay: scaled before
+    // the copy)
+    if constexpr (MODE == kDecElem)
+      state_update_decay<CF>(Sacc, sm.Ks, sm.Vs, Lc, lg2, wv, li, lg);
+    else
+      state_update<CF>(Sacc, sm.Ks, sm.Vs, 1.f, false, wv, li, lg);
+    if constexpr (CH) chan_scale<CF>(Sacc, sc.bl, wv, lg);
+    __syncthreads();
+    if constexpr (!CH) {
+      if (c0 + CF::C < t_end)
+        rescale_and_copy_state<CF>(sm.St, Sacc,
+                                   KEYS ? sm.pw[min(CF::C, N - c0 - CF::C)] : 1.f, KEYS, wv,
+                                   li, lg);
+    }
+    // 16-byte row stores of the output tile
+    {
+      const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
+      const int col0 = vcb * CF::VEC;
+#pragma unroll
+      for (int r = 0; r < CF::RV; ++r) {
+        const int row = vrg * CF::RV + r;
+        const V val = *reinterpret_cast<const V *>(sm.Os + row * CF::VLD + col0);
+        const size_t el = (size_t)(c0 + row) * dv + col0;
+        if constexpr (VK) {
+          const bool ok = row < Lc && col0 < dv;
+          buf_store16_nt<T>(hb.o, ok ? (uint32_t)(el * sizeof(T)) : kOOB, val);
+        } else {
+#pragma unroll
+          for (int e = 0; e < CF::VEC; ++e) {
+            const bool ok = row < Lc && col0 + e < dv;
+            buf_store1(hb.o, ok ? (uint32_t)((el + e) * sizeof(T)) : kOOB, val[e]);
+          }
+        }
+      }
+    }
+  }
 }
 
 // Resident waves per SIMD the register allocation must allow: the
@@ -959,8 +1156,9 @@ constexpr int wpe_at_most_2() {
   return CF::WPE < 2 ? CF::WPE : 2;
 }
 
-// DN: also write each token's denominator (den_out; no decay variants)
-template <class CF, bool VK, bool CH, bool CV, bool DN = false>
+// DN: also write each token's denominator (den_out; no per-channel decay or
+// convolution); DEC: per-head decay gamma (compiled in only where given)
+template <class CF, bool VK, bool CH, bool CV, bool DN, bool DEC>
 __global__ void __launch_bounds__(CF::NT, (CH || CV) ? wpe_at_most_2<CF>() : CF::WPE)
     chunk_kernel(PrefillParams p) {
   using T = typename CF::type;
@@ -969,7 +1167,8 @@ __global__ void __launch_bounds__(CF::NT, (CH || CV) ? wpe_at_most_2<CF>() : CF:
   __shared__ ChanSmem<CF, CH> sc;  // per-channel decay (CH) only
   __shared__ ConvSmem<CF, CV> cs;  // short convolution (CV) only
 
-  const int seg = blockIdx.x, bh = blockIdx.y;
+  const int seg = blockIdx.x, bh = grid_head();
+  if (bh >= p.BH) return;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
@@ -977,7 +1176,6 @@ __global__ void __launch_bounds__(CF::NT, (CH || CV) ? wpe_at_most_2<CF>() : CF:
   const HeadBufs hb = head_bufs<T>(p, bh);
   const int t_begin = seg * p.seg_len;
   const int t_end = min(N, t_begin + p.seg_len);
-  const bool decay = p.gamma != nullptr;
 
   // state entering this segment: slot seg of the scanned workspace, or
   // (S_in, z_in) with a single segment
@@ -1002,79 +1200,22 @@ __global__ void __launch_bounds__(CF::NT, (CH || CV) ? wpe_at_most_2<CF>() : CF:
                                    (size_t)bh * (p.conv_width - 1) * (2 * d + dv)
                              : nullptr,
                   nullptr);
-  fill_powers<CF>(sm.pw, decay ? log2f(p.gamma[bh % p.H]) : 0.f);
+  const float lg2 = DEC ? decay_log2(p.gamma, bh % p.H) : 0.f;
+  if constexpr (DEC) fill_powers<CF>(sm.pw, lg2);
   __syncthreads();
-  if constexpr (!CH)
-    rescale_and_copy_state<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - t_begin)], decay, wv, li,
-                               lg);
-
-  const int rb = wv % CF::NRB, cg = wv / CF::NRB;  // output role
-  for (int c0 = t_begin; c0 < t_end; c0 += CF::C) {
-    const int Lc = min(CF::C, N - c0);
-    if constexpr (CH) {  // the chunk's per-channel decay prefix sums
-      chan_logs<CF>(A, sc, d, Lc);
-      __syncthreads();
-      chan_prefix<CF>(sc, Lc, false);
-      __syncthreads();
-    }
-    commit<CF, true, CH, CV>(R, sm.Qs, sm.Ks, sm.Vs, sm.pw, p, Lc, chan_ptr<CF>(sc),
-                             conv_ptr<CF>(cs));
-    if constexpr (CH) {  // state read from diag(exp(lb_m)) S-
-      chan_scale<CF>(Sacc, sc.bm, wv, lg);
-      rescale_and_copy_state<CF>(sm.St, Sacc, 1.f, false, wv, li, lg);
-      if (c0 + CF::C < t_end)
-        chan_prefetch<CF, VK>(A, ra, p, c0 + CF::C, min(CF::C, N - c0 - CF::C));
-    }
-    if (c0 + CF::C < t_end)
-      prefetch<CF, true, VK>(R, p, hb, c0 + CF::C, min(CF::C, N - c0 - CF::C));
-    __syncthreads();
-
-    float *dno = DN ? p.den_out + (size_t)bh * N + c0 : nullptr;
-    if constexpr (CF::NRB == 2) {
-      if (rb == 0) chunk_outputs<CF, 0, DN>(sm, p, Lc, cg, li, lg, dno);
-      else chunk_outputs<CF, 1, DN>(sm, p, Lc, cg, li, lg, dno);
-    } else {
-      static_assert(CF::NRB == 4, "row blocks per chunk");
-      switch (rb) {
-        case 0: chunk_outputs<CF, 0, DN>(sm, p, Lc, cg, li, lg, dno); break;
-        case 1: chunk_outputs<CF, 1, DN>(sm, p, Lc, cg, li, lg, dno); break;
-        case 2: chunk_outputs<CF, 2, DN>(sm, p, Lc, cg, li, lg, dno); break;
-        default: chunk_outputs<CF, 3, DN>(sm, p, Lc, cg, li, lg, dno); break;
-      }
-    }
-
-    // ---- carry the state across the chunk ----
-    // (the accumulator already carries gamma^Lc, or diag(exp(lb_m)) with a
-    // per-channel decay: scaled before the copy)
-    state_update<CF>(Sacc, sm.Ks, sm.Vs, 1.f, false, wv, li, lg);
-    if constexpr (CH) chan_scale<CF>(Sacc, sc.bl, wv, lg);
-    __syncthreads();
-    if constexpr (!CH) {
-      if (c0 + CF::C < t_end)
-        rescale_and_copy_state<CF>(sm.St, Sacc, sm.pw[min(CF::C, N - c0 - CF::C)], decay,
-                                   wv, li, lg);
-    }
-    // 16-byte row stores of the output tile
-    {
-      const int vcb = threadIdx.x % CF::VCB, vrg = threadIdx.x / CF::VCB;
-      const int col0 = vcb * CF::VEC;
-#pragma unroll
-      for (int r = 0; r < CF::RV; ++r) {
-        const int row = vrg * CF::RV + r;
-        const V val = *reinterpret_cast<const V *>(sm.Os + row * CF::VLD + col0);
-        const size_t el = (size_t)(c0 + row) * dv + col0;
-        if constexpr (VK) {
-          const bool ok = row < Lc && col0 < dv;
-          buf_store16_nt<T>(hb.o, ok ? (uint32_t)(el * sizeof(T)) : kOOB, val);
-        } else {
-#pragma unroll
-          for (int e = 0; e < CF::VEC; ++e) {
-            const bool ok = row < Lc && col0 + e < dv;
-            buf_store1(hb.o, ok ? (uint32_t)((el + e) * sizeof(T)) : kOOB, val[e]);
-          }
-        }
-      }
-    }
+  if constexpr (DEC) {
+    // gamma >= 1/2: decay folded into the key weights and the state copy
+    // (factors within gamma^C of 1); faster decays: every factor where it
+    // occurs (uniform per workgroup)
+    if (lg2 >= -1.f)
+      chunk_loop<CF, VK, CH, CV, DN, kDecKeys>(sm, sc, cs, p, hb, Sacc, R, A, ra, bh,
+                                               t_begin, t_end, lg2, wv, li, lg);
+    else
+      chunk_loop<CF, VK, CH, CV, DN, kDecElem>(sm, sc, cs, p, hb, Sacc, R, A, ra, bh,
+                                               t_begin, t_end, lg2, wv, li, lg);
+  } else {
+    chunk_loop<CF, VK, CH, CV, DN, kDecNone>(sm, sc, cs, p, hb, Sacc, R, A, ra, bh, t_begin,
+                                             t_end, lg2, wv, li, lg);
   }
 
   if (seg == p.nseg - 1) {
@@ -1099,7 +1240,8 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
   __shared__ ConvSmem<CF, CV> cs;  // short convolution (CV) only
   // part `part` of segment `seg`: with two parts per segment the first
   // covers split_len tokens, the second the rest (whole chunks both)
-  const int seg = blockIdx.x / p.nsplit, part = blockIdx.x % p.nsplit, bh = blockIdx.y;
+  const int seg = blockIdx.x / p.nsplit, part = blockIdx.x % p.nsplit, bh = grid_head();
+  if (bh >= p.BH) return;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, lg = lane >> 4;
@@ -1130,7 +1272,7 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
                   p.conv_in ? reinterpret_cast<const T *>(p.conv_in) + crow : nullptr,
                   p.conv_copy ? reinterpret_cast<T *>(p.conv_copy) + crow : nullptr);
   }
-  fill_powers<CF>(sm.pw, decay ? log2f(p.gamma[bh % p.H]) : 0.f);
+  fill_powers<CF>(sm.pw, decay_log2(p.gamma, bh % p.H));
 
   f32x4 Sacc[CF::FPW][CF::TPW];
 #pragma unroll
@@ -1150,7 +1292,7 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
         chan_prefix<CF>(sc, CF::C, true);
         __syncthreads();
       }
-      commit<CF, false, CH, CV>(R[u], nullptr, sm.Ks, sm.Vs, sm.pw, p, CF::C,
+      commit<CF, false, CH, CV, true>(R[u], nullptr, sm.Ks, sm.Vs, sm.pw, p, CF::C,
                                 chan_ptr<CF>(sc), conv_ptr<CF>(cs));
       if constexpr (CH) {
         chan_scale<CF>(Sacc, sc.bm, wv, lg);
@@ -1182,14 +1324,15 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
 // per record element; every record is loaded before the dependent chain.
 template <bool CH, bool TWO>
 __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
-  const int bh = blockIdx.y;
+  const int bh = grid_head();
+  if (bh >= p.BH) return;
   const size_t dd = (size_t)p.d * p.dv;
   const size_t rec = dd + p.d;               // scanned elements: S then z
   const size_t wr = ws_rec(p.d, p.dv);       // slot record stride
   const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= rec) return;
   constexpr bool two = TWO;  // two summary parts per segment (nsplit 2)
-  const float lgam = p.gamma ? log2f(p.gamma[bh % p.H]) : 0.f;
+  const float lgam = decay_log2(p.gamma, bh % p.H);
   const float gL = exp2f((float)p.seg_len * lgam);
   const float gB = exp2f((float)(p.seg_len - p.split_len) * lgam);
   float *base = p.ws + (size_t)bh * wr + e;
@@ -1243,7 +1386,7 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
 template <bool CH>
 hipError_t launch_scan(const PrefillParams &p, hipStream_t s) {
   const size_t rec = (size_t)p.d * p.dv + p.d;
-  const dim3 grid((unsigned)((rec + 255) / 256), p.BH);
+  const dim3 grid = head_grid((unsigned)((rec + 255) / 256), p.BH);
   return p.nsplit == 2 ? launch_kernel("linear_scan", scan_kernel<CH, true>, grid, dim3(256), s, p)
                        : launch_kernel("linear_scan", scan_kernel<CH, false>, grid, dim3(256), s, p);
 }
@@ -1261,7 +1404,7 @@ hipError_t run_vkcc(const PrefillParams &p, hipStream_t s) {
     return hipErrorNotSupported;  // refused on the host before any launch
   } else {
   if (p.nseg > 1) {
-    const dim3 grid((p.nseg - 1) * p.nsplit, p.BH);
+    const dim3 grid = head_grid((p.nseg - 1) * p.nsplit, p.BH);
     // k and v beyond the last-level cache (256 MB): streaming loads
     const bool stream = (size_t)p.BH * p.N * (p.d + p.dv) * sizeof(typename CF::type) >
                         kStreamBytes;
@@ -1278,13 +1421,24 @@ hipError_t run_vkcc(const PrefillParams &p, hipStream_t s) {
     e = launch_scan<CH>(p, s);
     if (e != hipSuccess) return e;
   }
-  if constexpr (!CH && !CV) {
-    if (p.den_out)
-      return launch_kernel("linear_chunk", chunk_kernel<CF, VK, false, false, true>,
-                           dim3(p.nseg, p.BH), dim3(CF::NT), s, p);
+  const dim3 grid = head_grid(p.nseg, p.BH);
+  if constexpr (CH) {  // (a per-channel decay excludes gamma)
+    return launch_kernel("linear_chunk", chunk_kernel<CF, VK, CH, CV, false, false>, grid,
+                         dim3(CF::NT), s, p);
+  } else {
+    const bool dec = p.gamma != nullptr;
+    if constexpr (!CV) {
+      if (p.den_out)
+        return dec ? launch_kernel("linear_chunk", chunk_kernel<CF, VK, false, false, true, true>,
+                                   grid, dim3(CF::NT), s, p)
+                   : launch_kernel("linear_chunk", chunk_kernel<CF, VK, false, false, true, false>,
+                                   grid, dim3(CF::NT), s, p);
+    }
+    return dec ? launch_kernel("linear_chunk", chunk_kernel<CF, VK, CH, CV, false, true>, grid,
+                               dim3(CF::NT), s, p)
+               : launch_kernel("linear_chunk", chunk_kernel<CF, VK, CH, CV, false, false>, grid,
+                               dim3(CF::NT), s, p);
   }
-  return launch_kernel("linear_chunk", chunk_kernel<CF, VK, CH, CV>, dim3(p.nseg, p.BH),
-                       dim3(CF::NT), s, p);
   }
 }
 
@@ -1309,7 +1463,7 @@ hipError_t run(const PrefillParams &p, hipStream_t s) {
 template <class CF>
 hipError_t run_prefix(const PrefillParams &p, hipStream_t s) {
   if (p.nseg <= 1) return hipSuccess;
-  const dim3 grid((p.nseg - 1) * p.nsplit, p.BH);
+  const dim3 grid = head_grid((p.nseg - 1) * p.nsplit, p.BH);
   hipError_t e = p.vec_ok ? launch_kernel("linear_summary", summary_kernel<CF, true, false, false>,
                                           grid, dim3(CF::NT), s, p)
                           : launch_kernel("linear_summary", summary_kernel<CF, false, false, false>,
@@ -1329,7 +1483,8 @@ int resident_per_cu() {
     int v = cached.load(std::memory_order_relaxed);
     if (v > 0) return v;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_kernel<CF, true, CH, CV>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n,
+                                                     chunk_kernel<CF, true, CH, CV, false, false>,
                                                      CF::NT, 0) != hipSuccess ||
         n < 1) {
       (void)hipGetLastError();

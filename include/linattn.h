@@ -99,11 +99,13 @@ typedef struct la_prefill_args {
   const void *q;     /* [B,H,N,d]  */
   const void *k;     /* [B,H,N,d]  */
   const void *v;     /* [B,H,N,dv] */
-  const float *gamma;/* LINEAR: [H] decay per head, each in [1/2, 1]; NULL = 1.
+  const float *gamma;/* LINEAR: [H] decay per head, each in (0, 1]; NULL = 1.
                         DELTA: must be NULL.  Values are the caller's
-                        contract (not read on the host); the chunked prefill
-                        folds gamma^(chunk-1) into the key weights, which
-                        stays far inside the fp32 range on that interval. */
+                        contract (not read on the host).  Every decay factor
+                        the kernels apply is a power gamma^m with m >= 0;
+                        below gamma = 2^-40 the earlier tokens' weights are
+                        taken as powers of 2^-40 (under 2^-40 of the
+                        token's own, below fp32 resolution). */
   const float *g;    /* DELTA: [B,H,N] write gate per token (required).
                         LINEAR: must be NULL. */
   const float *alpha;/* State decay per token, or NULL (= 1, no decay).

@@ -116,7 +116,12 @@ def test_prefill_rejects_invalid_arguments(lib, bad):
 
 def test_prefill_null_args_and_unsupported_grid(lib):
     assert lib.la_prefill(None, None) == _lib.LA_EINVAL
-    a = _args(B=70000, H=1)
+    a = _args(B=70000, H=40000)  # B*H past the int32 range
+    assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+    # the delta rule's sequential pass: 512 threads per (head, 16 value
+    # columns) along one grid axis of at most 2^32 - 1 work-items
+    a = _args(B=1 << 21, H=1, dv=128, rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY,
+              g=ctypes.c_void_p(0x2000))
     assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
     fake = ctypes.c_void_p(0x2000)
     # the short convolution is built for the LINEAR rule only
@@ -209,6 +214,8 @@ def test_backward_unsupported_and_sizes(lib):
     a = _bargs(dtype=_lib.LA_F32, d=128)  # fp32 backward takes d, dv <= 64
     assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
     assert lib.la_backward_workspace_size(ctypes.byref(a)) == ctypes.c_size_t(-1).value
+    a = _bargs(B=70000, H=40000)  # B*H past the int32 range
+    assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
     a = _bargs(B=0)
     assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_OK
     assert lib.la_backward_workspace_size(ctypes.byref(a)) == 0

@@ -158,3 +158,18 @@ def test_backward_no_tokens_passes_state_gradient():
     _, _, _, dS0, dz0 = la.backward(q, q, v, v, den, v, dS_out=dS, dz_out=dz)
     torch.cuda.synchronize()
     assert torch.equal(dS0, dS) and torch.equal(dz0, dz)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_backward_fast_decay(dtype):
+    """Per-head decays 0.05, 0.25, 0.45 over several segments, with an
+    initial state and a final-state gradient."""
+    B, H, N, d, dv = 1, 3, 2000 + 5, 64, 64
+    seed = 1790 + (dtype == torch.bfloat16)
+    q, k, v, do, _ = _case(B, H, N, d, dv, dtype, seed, False)
+    gamma = torch.tensor([0.05, 0.25, 0.45], device=DEV)
+    S0 = _rand((B, H, d, dv), torch.float32, seed + 4, 0.3)
+    z0 = _rand((B, H, d), torch.float32, seed + 5, 0.3).abs() + 1.0
+    dS = _rand((B, H, d, dv), torch.float32, seed + 6, 0.01)
+    dz = _rand((B, H, d), torch.float32, seed + 7, 0.01)
+    _check(q, k, v, do, gamma, "elu1", TOL[dtype], S0=S0, z0=z0, dS=dS, dz=dz)

@@ -362,3 +362,61 @@ def test_gla_prefill_then_decode_handoff():
     torch.cuda.synchronize()
     ro, _, _ = _oracle_gla(q, k, v, al)
     assert_close(o, ro[:, :, N], TOL[torch.bfloat16], "o")
+
+
+# --- fast decays ---------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_prefill_fast_decay_segments_then_decode(dtype):
+    """Per-head decays across (0, 1]: 0.05, 0.25, 0.45 and 1e-3 forget within a
+    few tokens ("What Is Linear Attention?" 5.1: smaller gamma forgets
+    faster), 0.9 and 1 for contrast.  Long enough for several segments, an
+    initial state, a ragged last chunk; then decode steps continue from the
+    final state."""
+    B, H, N, d, dv = 1, 6, 3000 + 17, 64, 64
+    seed = 2100 + (dtype == torch.bfloat16)
+    q = _rand((B, H, N, d), dtype, seed, 0.5)
+    k = _rand((B, H, N, d), dtype, seed + 1, 0.5)
+    v = _rand((B, H, N, dv), dtype, seed + 2)
+    gamma = torch.tensor([0.05, 0.25, 0.45, 1e-3, 0.9, 1.0], device=DEV)
+    S0 = _rand((B, H, d, dv), torch.float32, seed + 3, 0.3)
+    z0 = _rand((B, H, d), torch.float32, seed + 4, 0.3).abs() + 1.0
+    assert la.workspace_size(q, k, v, gamma=gamma) > 0  # several segments
+    o, S, z = la.prefill(q, k, v, gamma=gamma, eps=1e-6, S_in=S0, z_in=z0)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_prefill(q, k, v, gamma, 1e-6, "elu1", S0, z0)
+    tol = TOL[dtype]
+    assert_close(o, ro, tol, "o")
+    assert_close(S, rS, tol, "S", axes=(-2, -1))
+    assert_close(z, rz, tol, "z")
+    for t in range(3):
+        q1 = _rand((B, H, d), dtype, seed + 10 + 3 * t, 0.5)
+        k1 = _rand((B, H, d), dtype, seed + 11 + 3 * t, 0.5)
+        v1 = _rand((B, H, dv), dtype, seed + 12 + 3 * t)
+        o1 = la.decode_step(q1, k1, v1, S, z, gamma=gamma, eps=1e-6)
+        torch.cuda.synchronize()
+        r1, rS, rz = oracle.linear_decode_step(cpu(q1), cpu(k1), cpu(v1), rS, rz,
+                                               gamma=cpu(gamma), eps=1e-6)
+        assert_close(o1, r1, tol, f"decode step {t}")
+    assert_close(S, rS, tol, "S after decode", axes=(-2, -1))
+
+
+@pytest.mark.parametrize("shape", [(1, 3, 200, 128, 128), (2, 2, 97, 24, 40)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_prefill_fast_decay_identity_map(shape):
+    """Fast decays with the identity map (features given directly, many of
+    them zero) and one segment: scores, state read and state update all take
+    their own decay factors."""
+    B, H, N, d, dv = shape
+    q = _rand((B, H, N, d), torch.bfloat16, 2150, 0.5).abs()
+    k = _rand((B, H, N, d), torch.bfloat16, 2151, 0.5).abs()
+    v = _rand((B, H, N, dv), torch.bfloat16, 2152)
+    gamma = torch.tensor([0.05, 0.3, 0.45][:H], device=DEV)
+    S0 = _rand((B, H, d, dv), torch.float32, 2153, 0.3).abs()
+    z0 = _rand((B, H, d), torch.float32, 2154, 0.3).abs() + 1.0
+    o, S, z = la.prefill(q, k, v, fmap="identity", gamma=gamma, eps=1e-3, S_in=S0, z_in=z0)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_prefill(q, k, v, gamma, 1e-3, "identity", S0, z0)
+    assert_close(o, ro, 2e-2, "o")
+    assert_close(S, rS, 2e-2, "S", axes=(-2, -1))
+    assert_close(z, rz, 2e-2, "z")

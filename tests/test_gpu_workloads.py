@@ -67,25 +67,58 @@ def test_long_context_workload_full_size_sampled():
     assert_close(_head(S, 0, h), rS, BF16, f"S head (0,{h})", axes=(-2, -1))
 
 
-def test_decode_workload_full_shape_sampled():
-    """B256 H32 d128: the 1024-token prefill that builds the state, then
-    decode steps over every sequence; two heads against the oracle."""
+def test_config1_fp32_prefill_as_stated():
+    """B1 H1 N256 d=dv=64, fp32 q, k, v ~ N(0,1) unscaled from the seed,
+    elu+1, gamma = 1, eps = 1e-6, full-sequence prefill: o, S and z against
+    the oracle at 1e-4 on the plain row metric (no floor on row scales).
+    (The workload's three-token hand-worked example runs in
+    test_gpu_linear.test_handworked_example_on_gpu.)"""
+    w = inputs.WORKLOADS[1]
+    x = inputs.make_prefill(w, DEV)
+    assert x["q"].dtype == torch.float32 and tuple(x["q"].shape) == (1, 1, 256, 64)
+    assert x["gamma"] is None and w.scale == 1.0 and w.eps == 1e-6
+    o, S, z = la.prefill(x["q"], x["k"], x["v"], eps=w.eps)
+    torch.cuda.synchronize()
+    ro, rS, rz = oracle.linear_prefill(cpu(x["q"]), cpu(x["k"]), cpu(x["v"]), eps=w.eps)
+    tol = TOL[torch.float32]
+    assert_close(o, ro, tol, "o", floor=False)
+    assert_close(S, rS, tol, "S", axes=(-2, -1), floor=False)
+    assert_close(z, rz, tol, "z", floor=False)
+
+
+def test_decode_workload_full_loop_sampled():
+    """B256 H32 d128: the 1024-token prefill that builds the state, then all
+    1024 decode steps over every sequence, launched as the benchmark launches
+    them; two heads against the oracle at every step (o), and their final
+    state."""
     w = inputs.WORKLOADS[3]
     x = inputs.make_prefill(w, DEV)
-    dec = inputs.make_decode(w, DEV, steps=16)
     _, S, z = la.prefill(x["q"], x["k"], x["v"], eps=w.eps)
-    outs = []
-    for t in range(16):
-        outs.append(la.decode_step(dec["q"][t], dec["k"][t], dec["v"][t], S, z, eps=w.eps))
+    heads = ((0, 0), (255, 31))
+    ref = {}
+    for b, h in heads:
+        ref[b, h] = oracle.linear_prefill(*(cpu(_head(x[n], b, h)) for n in ("q", "k", "v")),
+                                          eps=w.eps)[1:]
+    del x
+    dec = inputs.make_decode(w, DEV, steps=w.decode_steps)
+    o = torch.empty((w.B, w.H, w.dv), dtype=w.dtype, device=DEV)
+    outs = {bh: [] for bh in heads}
+    for t in range(w.decode_steps):
+        la.decode_step(dec["q"][t], dec["k"][t], dec["v"][t], S, z, eps=w.eps, o=o)
+        for b, h in heads:
+            outs[b, h].append(o[b, h].clone())
     torch.cuda.synchronize()
-    for b, h in ((0, 0), (255, 31)):
-        _, rS, rz = oracle.linear_prefill(*(cpu(_head(x[n], b, h)) for n in ("q", "k", "v")),
-                                          eps=w.eps)
-        for t in range(16):
+    for b, h in heads:
+        rS, rz = ref[b, h]
+        got = torch.stack(outs[b, h]).cpu()
+        want = []
+        for t in range(w.decode_steps):
             ro, rS, rz = oracle.linear_decode_step(
                 *(cpu(dec[n][t][b:b + 1, h:h + 1]) for n in ("q", "k", "v")), rS, rz, eps=w.eps)
-            assert_close(outs[t][b:b + 1, h:h + 1], ro, BF16, f"o step {t} head ({b},{h})")
+            want.append(ro[0, 0])
+        assert_close(got, np.stack(want), BF16, f"o, 1024 steps, head ({b},{h})")
         assert_close(_head(S, b, h), rS, BF16, f"S head ({b},{h})", axes=(-2, -1))
+        assert_close(_head(z, b, h), rz, BF16, f"z head ({b},{h})")
 
 
 def test_training_step_full_size_sampled():
