@@ -108,7 +108,7 @@ def workspace_size(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None,
 def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
             S_in=None, z_in=None, S_out=None, z_out=None, return_state=True,
             o=None, workspace=None, alpha=None, conv_weight=None, conv_cache=None,
-            conv_cache_out=None, den_out=None):
+            conv_cache_out=None, den_out=None, noalloc=False):
     """Chunked prefill over [B,H,N,*] sequences (see la_prefill).
 
     rule "linear": fmap defaults to "elu1"; gamma [H] fp32 or None; eps >= 0;
@@ -123,6 +123,9 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
                    (the input of backward()).
     rule "delta":  fmap "identity"; g [B,H,N] fp32 required; alpha [B,H,N]
                    fp32 state decay in (0, 1] or None.
+    noalloc=True calls la_prefill_noalloc: the library's static device
+    scratch replaces the workspace (none may be passed), so the call itself
+    allocates nothing beyond the outputs made here when not given.
     Returns (o, S_out, z_out); the states are None unless requested
     (return_state) or passed in.  z_out is always None for "delta".
     """
@@ -158,6 +161,11 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
     a.S_out, a.z_out = _ptr(S_out), _ptr(z_out)
     a.q, a.k, a.v, a.o = _ptr(q), _ptr(k), _ptr(v), _ptr(o)
     a.den_out = _ptr(den_out)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        _lib.check(lib.la_prefill_noalloc(ctypes.byref(a), _stream()), "la_prefill_noalloc")
+        return o, S_out, z_out
     need = lib.la_prefill_workspace_size(ctypes.byref(a))
     if need == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes")

@@ -7,14 +7,15 @@ import threading
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinattn.so")
 
-LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP, LA_EWORKSPACE = 0, 1, 2, 3, 4
+LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP, LA_EWORKSPACE, LA_ESCRATCH = 0, 1, 2, 3, 4, 5
+NOALLOC_SCRATCH_BYTES = 128 << 20  # LA_NOALLOC_SCRATCH_BYTES
 LA_F32, LA_BF16 = 0, 1
 LA_FMAP_IDENTITY, LA_FMAP_ELU1 = 0, 1
 LA_RULE_LINEAR, LA_RULE_DELTA = 0, 1
 ABI_VERSION = 4
 
 # Every symbol include/linattn.h declares.
-EXPORTS = ("la_prefill_workspace_size", "la_prefill", "la_decode_step",
+EXPORTS = ("la_prefill_workspace_size", "la_prefill", "la_prefill_noalloc", "la_decode_step",
            "la_backward_workspace_size", "la_backward",
            "la_state_init", "la_status_str", "la_abi_version",
            "la_profile_enable", "la_profile_collect")
@@ -87,6 +88,8 @@ def load(path: str | None = None):
         lib.la_prefill_workspace_size.restype = _size
         lib.la_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _ptr]
         lib.la_prefill.restype = ctypes.c_int
+        lib.la_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), _ptr]
+        lib.la_prefill_noalloc.restype = ctypes.c_int
         lib.la_backward_workspace_size.argtypes = [ctypes.POINTER(BackwardArgs)]
         lib.la_backward_workspace_size.restype = _size
         lib.la_backward.argtypes = [ctypes.POINTER(BackwardArgs), _ptr]

@@ -161,6 +161,7 @@ const char *la_status_str(int s) {
     case LA_EUNSUPPORTED: return "unsupported configuration";
     case LA_EHIP: return "HIP launch or runtime error";
     case LA_EWORKSPACE: return "workspace missing or too small";
+    case LA_ESCRATCH: return "request needs more than the static scratch of la_prefill_noalloc";
     default: return "unknown status";
   }
 }

@@ -52,8 +52,10 @@ typedef enum {
                           or an argument the rule does not take */
   LA_EUNSUPPORTED = 2, /* valid request the library does not implement */
   LA_EHIP = 3,         /* a HIP call or kernel launch failed */
-  LA_EWORKSPACE = 4    /* workspace NULL or smaller than
+  LA_EWORKSPACE = 4,   /* workspace NULL or smaller than
                           la_prefill_workspace_size() */
+  LA_ESCRATCH = 5      /* la_prefill_noalloc: the call needs more workspace
+                          than LA_NOALLOC_SCRATCH_BYTES */
 } la_status;
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype; /* dtype of q, k, v, o */
@@ -157,6 +159,23 @@ size_t la_prefill_workspace_size(const la_prefill_args *args);
  * given, the final state.  Equivalent (up to fp rounding order) to running
  * the per-token recurrence of `rule` from (S_in, z_in). */
 int la_prefill(const la_prefill_args *args, void *stream);
+
+/* la_prefill for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same computation and kernels as la_prefill (bit-identical results),
+ * with the workspace taken from a static device array of
+ * LA_NOALLOC_SCRATCH_BYTES that each GPU holds until the process ends (its
+ * device address is looked up once per device, on the first call there,
+ * with that device current).  The call allocates and frees nothing.
+ * args->workspace must be NULL and workspace_bytes 0 (LA_EINVAL otherwise).
+ * A call whose la_prefill_workspace_size() exceeds the array returns
+ * LA_ESCRATCH and enqueues nothing; LA_EHIP if the array's address cannot be
+ * obtained.  Every call on one GPU uses the same array: calls that overlap
+ * on a GPU (other streams or threads) race, so the caller serialises them;
+ * nothing needs clearing between calls (every element a call reads it has
+ * written first). */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20) /* 128 MiB */
+int la_prefill_noalloc(const la_prefill_args *args, void *stream);
 
 /* Backward of a LINEAR-rule prefill (training).  The pages motivate
  * parallel training ([WILA] section 8; [EAV] sections 8 and 10) but give no
