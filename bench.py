@@ -35,9 +35,14 @@ per step.  Alongside:
                 backward kernels' times, and the dominant backward kernel
                 against HBM peak (its algorithmic bytes: q, k, v, o, dL/do
                 and the denominators read once, its gradients written once);
-  cpu_baseline  the fp64 oracle on the host (one thread) over the same
-                inputs of the main workload (a reported baseline, not a
-                target), with its parity error against the GPU output.
+  cpu_baseline  the fp64 oracle on the host cores for the main workload and
+                (in `decode` and `workloads`) the decode loop, the
+                long-context prefill and the gated delta prefill: a
+                process pool over (b, h) shards with one BLAS thread each,
+                on a bounded sample of each workload (same shapes, recipe
+                and seeds, drawn on the CPU generator), run in a child
+                process before this one touches the GPU; a reported
+                baseline, not a target (parity is the tests' job).
 --gpus N with N > 1 exits with a message: the benchmark runs on one GPU.
 """
 from __future__ import annotations
@@ -78,6 +83,8 @@ def parse():
                     help="only summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs "
                          "kept under DIR/{fetch,write,copy_fetch,copy_write} for "
                          "--workload as markdown (no GPU needed)")
+    ap.add_argument("--cpu-baseline-child", metavar="WIDS", default=None,
+                    help=argparse.SUPPRESS)  # internal: the CPU baseline's child process
     ap.add_argument("--stats-summary", metavar="DIR", default=None,
                     help="only summarise a rocprofv3 --kernel-trace --stats run "
                          "kept under DIR as markdown (no GPU needed)")
@@ -553,45 +560,146 @@ def bench_decode(la, lib, torch, nsteps, warmup=8):
     }
 
 
-def cpu_baseline(w, x, o_gpu):
-    """The fp64 oracle (one thread) over every head of the main workload's
-    inputs; tokens/s = B*N / wall time.  Also its parity error against the
-    GPU output of the same inputs."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the host cores, per workload, on a bounded
+# sample of the workload (same shapes and input recipe).  It runs in a child
+# process started before this process touches the GPU; the child never uses
+# the GPU, so it can fork a pool of workers over (b, h) shards, each with one
+# BLAS thread, that inherit the sample arrays.
+CPU_MAX_WORKERS = 16  # the host's CPU share per GPU
+CPU_BASELINE_WORKLOADS = (2, 3, 4, 5)
+_CPU = {}             # the current sample (fp64, heads flattened to [1, BH, ...])
+
+
+def _cpu_sample(w):
+    """Fill _CPU with a bounded sample of workload w; returns (description,
+    work units covered, unit name, units of the whole workload).  Inputs are
+    drawn with the workload's recipe and seeds on the CPU generator."""
     import numpy as np
 
+    from causal_linear_attention_attn_amd import inputs
+
+    def flat(t):
+        t = t.double().numpy()
+        return t.reshape(1, t.shape[0] * t.shape[1], *t.shape[2:])
+
+    _CPU.clear()
+    _CPU["wid"] = w.wid
+    if w.wid == 3:  # decode loop: 16 of the 256 sequences, all heads
+        nb = 16
+        x = inputs.make_prefill(w, "cpu", B=nb)
+        dec = inputs.make_decode(w, "cpu", B=nb)
+        for n in ("q", "k", "v"):
+            _CPU[n] = flat(x[n])
+            d = dec[n].double().numpy()  # [steps, B, H, dim]
+            _CPU["dec_" + n] = d.reshape(d.shape[0], 1, nb * w.H, d.shape[-1])
+        heads = nb * w.H
+        desc = (f"{nb} of {w.B} sequences x {w.H} heads ({heads} of {w.B * w.H} states): "
+                f"the {w.N}-token prefill recurrence, its check against the closed form "
+                f"phi(K)^T V, sum phi(k) (gamma = 1), then {w.decode_steps} decode steps")
+        return desc, heads, "head-states", w.B * w.H
+    N = 16384 if w.wid == 4 else w.N  # the long-context workload: its first 16384 tokens
+    x = inputs.make_prefill(w, "cpu", N=N)
+    for n in ("q", "k", "v", "g", "alpha"):
+        if x.get(n) is not None:
+            _CPU[n] = flat(x[n])
+    if x.get("gamma") is not None:
+        _CPU["gamma"] = np.tile(x["gamma"].double().numpy(), w.B)
+    heads = w.B * w.H
+    desc = f"all {heads} heads x {N} of {w.N} tokens" if N < w.N else \
+        f"the whole workload ({heads} heads x {N} tokens)"
+    return desc, heads * N, "head-tokens", w.B * w.H * w.N
+
+
+def _cpu_shard(job):
+    """Oracle over heads [lo, hi) of the current sample, one BLAS thread.
+    Returns (seconds, largest closed-form error of the decode prefill)."""
+    lo, hi = job
     from threadpoolctl import threadpool_limits
+
+    import numpy as np
 
     import oracle
 
-    q, k, v = (x[n].cpu() for n in ("q", "k", "v"))
-    gamma = None if x["gamma"] is None else x["gamma"].cpu()
+    x = _CPU
+    sl = lambda n: x[n][:, lo:hi]  # noqa: E731
+    err = 0.0
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        if w.rule == "delta":
-            al = x.get("alpha")
-            ro, _ = oracle.delta_prefill(q, k, v, x["g"].cpu(),
-                                         alpha=None if al is None else al.cpu())
-        elif x.get("conv_weight") is not None:
-            al = x.get("alpha")
-            ro = oracle.linear_prefill_conv(q, k, v, x["conv_weight"].cpu(),
-                                            conv_cache=x["conv_cache"].cpu(), eps=w.eps,
-                                            gamma=gamma,
-                                            alpha=None if al is None else al.cpu())[0]
+        if x["wid"] == 3:
+            q, k, v = sl("q"), sl("k"), sl("v")
+            _, S, z = oracle.linear_prefill(q, k, v, eps=1e-6)
+            fk = oracle.phi_elu1(k)
+            S_cf = np.einsum("bhnr,bhnd->bhrd", fk, v)
+            err = max(float(np.abs(S - S_cf).max() / np.abs(S_cf).max()),
+                      float(np.abs(z - fk.sum(2)).max() / np.abs(fk.sum(2)).max()))
+            t0 = time.perf_counter()  # the decode steps alone are the measured unit
+            for t in range(x["dec_q"].shape[0]):
+                _, S, z = oracle.linear_decode_step(x["dec_q"][t][:, lo:hi],
+                                                    x["dec_k"][t][:, lo:hi],
+                                                    x["dec_v"][t][:, lo:hi], S, z, eps=1e-6)
+        elif "g" in x:
+            oracle.delta_prefill(sl("q"), sl("k"), sl("v"), sl("g"),
+                                 alpha=sl("alpha") if "alpha" in x else None)
         else:
-            al = x.get("alpha")
-            ro, _, _ = oracle.linear_prefill(q, k, v, eps=w.eps, gamma=gamma,
-                                             alpha=None if al is None else al.cpu())
-        el = time.perf_counter() - t0
-    got = o_gpu.detach().cpu().double().numpy()
-    diff = np.abs(got - ro).max(axis=-1)
-    scale = np.abs(ro).max(axis=-1)
-    err = float((diff / np.where(scale > 0, scale, 1.0)).max())
-    return {
-        "value": w.B * w.N / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-        "sample": f"the whole workload ({w.B}x{w.H} heads x {w.N} tokens, "
-                  f"{w.B * w.H * w.N} head-tokens) in {el:.1f} s on one thread",
-        "parity_max_row_rel_err": err,
-    }
+            gamma = x["gamma"][lo:hi] if "gamma" in x else None
+            oracle.linear_prefill(sl("q"), sl("k"), sl("v"), gamma=gamma, eps=1e-6)
+        return time.perf_counter() - t0, err
+
+
+def _cpu_ready(_):
+    return os.getpid()
+
+
+def cpu_baseline_child(wids):
+    """Runs in the child: the oracle over a bounded sample of each workload
+    in a fork pool; prints one JSON dict {workload name: cpu_baseline}."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import torch
+
+    from causal_linear_attention_attn_amd import inputs
+
+    torch.set_num_threads(1)
+    cores = min(len(os.sched_getaffinity(0)), CPU_MAX_WORKERS)
+    res = {}
+    for wid in wids:
+        w = inputs.WORKLOADS[wid]
+        desc, units, uname, total = _cpu_sample(w)
+        nheads = _CPU["q"].shape[1]
+        nw = min(cores, nheads)
+        bounds = np.linspace(0, nheads, nw + 1).astype(int)
+        with mp.get_context("fork").Pool(nw) as pool:
+            pool.map(_cpu_ready, range(nw))
+            t0 = time.perf_counter()
+            out = pool.map(_cpu_shard, list(zip(bounds[:-1].tolist(), bounds[1:].tolist())))
+            wall = time.perf_counter() - t0
+        r = {"kind": "oracle", "cores": nw, "wall_s": wall,
+             "sample": f"{desc}; {nw} worker processes over (b,h) shards, one BLAS thread "
+                       f"each, on {len(os.sched_getaffinity(0))} host cores"}
+        if wid == 3:  # decode steps of the whole batch per second (the decode
+            # loops alone: the slowest worker's)
+            dt = max(t for t, _ in out)
+            r.update(value=w.decode_steps * units / total / dt, unit="steps/s",
+                     decode_s=dt, closed_form_rel_err=max(e for _, e in out))
+        else:
+            r.update(value=units // w.H / wall, unit="tokens/s")  # B * N tokens
+        res[w.name] = r
+    print(json.dumps(res), flush=True)
+
+
+def run_cpu_baseline(wids):
+    """The CPU baseline of workloads `wids` from a child process (call before
+    anything touches the GPU); {workload name: record}."""
+    import subprocess
+
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child",
+                        ",".join(str(i) for i in wids)], capture_output=True, text=True,
+                       timeout=900)
+    if r.returncode != 0:
+        raise RuntimeError(f"cpu baseline child failed:\n{r.stderr[-2000:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def main():
@@ -607,6 +715,20 @@ def main():
     if args.stats_summary:
         stats_summary(args.stats_summary)
         return
+    if args.cpu_baseline_child:
+        cpu_baseline_child([int(i) for i in args.cpu_baseline_child.split(",")])
+        return
+    # the CPU baseline runs first, in a child process, before this process
+    # touches the GPU (rank 0 at N = 1: the only rank here)
+    cpu = None
+    if not args.no_cpu_baseline and not args.copy_probe:
+        wids = [args.workload]
+        if args.workload != 3:
+            if not args.no_decode:
+                wids.append(3)
+            if not args.no_extra:
+                wids += [i for i in (4, 5) if i != args.workload]
+        cpu = run_cpu_baseline([i for i in wids if i in CPU_BASELINE_WORKLOADS])
     import torch
 
     import causal_linear_attention_attn_amd as la
@@ -628,7 +750,8 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic (seeded normal draws; see inputs.py)",
             "config": {"workload": dec["workload"]}, "roofline": dec["roofline"],
-            "decode": dec}), flush=True)
+            "decode": dec, "cpu_baseline": None if cpu is None else cpu.get(dec["workload"])}),
+            flush=True)
         return
     w = inputs.WORKLOADS[args.workload]
     res, x, o = bench_workload(la, lib, torch, w, args.steps, args.warmup)
@@ -647,11 +770,13 @@ def main():
         "step_hbm_frac": res["step_hbm_frac"], "kernels_ms": res["kernels_ms"],
         "workspace_bytes": res["workspace_bytes"],
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, x, o)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu[w.name]
     del x, o
     if not args.no_decode:
         line["decode"] = bench_decode(la, lib, torch, args.decode_steps)
+        if cpu is not None:
+            line["decode"]["cpu_baseline"] = cpu.get(line["decode"]["workload"])
     if not args.no_train and w.rule == "linear" and w.decay in ("none", "per_head") \
             and not w.conv:
         line["train"] = bench_train(la, lib, torch, w, max(10, args.steps // 4), 5)
@@ -663,7 +788,10 @@ def main():
             r, xx, oo = bench_workload(la, lib, torch, inputs.WORKLOADS[wid],
                                        max(5, args.steps // 10), 3)
             del xx, oo
-            extra[r.pop("workload")] = r
+            name = r.pop("workload")
+            if cpu is not None and name in cpu:
+                r["cpu_baseline"] = cpu[name]
+            extra[name] = r
         line["workloads"] = extra
     print(json.dumps(line), flush=True)
 
