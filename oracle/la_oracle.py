@@ -418,3 +418,64 @@ def delta_decode_step(q, k, v, g, S, alpha=None):
     """
     return delta_step(_f64(S), _f64(q), _f64(k), _f64(v), _f64(g),
                       None if alpha is None else _f64(alpha))
+
+
+def delta_backward(q, k, v, g, do, *, alpha=None, S0=None, dS_N=None):
+    """Gradients of the gated delta rule's prefill, token by token in reverse.
+
+    The pages motivate parallel training ([WILA] 8, [EAV] 8 and 10) but give
+    no gradient formulas; this is reverse-mode differentiation of delta_step,
+    written out.  With a = alpha_t (1 without a decay), the forward step is
+        S_t = a (I - g_t k_t k_t^T) S_{t-1} + g_t k_t v_t^T,   o_t = S_t^T q_t.
+    With the adjoint Sh_t = dL/dS_t (all later tokens and the final-state
+    gradient included), the residual u_t = v_t - a S_{t-1}^T k_t and
+    w_t = Sh_t^T k_t:
+        Sh_t   = q_t do_t^T + a_(t+1) (I - g_(t+1) k_(t+1) k_(t+1)^T) Sh_(t+1)
+        dq_t   = S_t do_t
+        dv_t   = g_t w_t
+        dg_t   = w_t . u_t
+        dk_t   = g_t Sh_t u_t - a g_t S_{t-1} w_t
+        dalpha_t = <Sh_t, S_{t-1}> - g_t (S_{t-1}^T k_t) . w_t
+    and the initial-state gradient is what the adjoint becomes before token
+    0, a_0 (I - g_0 k_0 k_0^T) Sh_0.
+
+    q, k: [B, H, N, d]; v, do: [B, H, N, dv]; g: [B, H, N]; alpha: [B, H, N]
+    or None; S0: [B, H, d, dv] or None (zeros); dS_N: [B, H, d, dv] (the
+    gradient with respect to the final state) or None (zero).
+    Returns (dq, dk, dv, dg, dalpha, dS_0) in float64; dalpha is None
+    without a decay.
+    """
+    q, k, v, g, do = _f64(q), _f64(k), _f64(v), _f64(g), _f64(do)
+    al = None if alpha is None else _f64(alpha)
+    B, H, N, d = q.shape
+    dv_ = v.shape[-1]
+    S = np.zeros((B, H, d, dv_)) if S0 is None else _f64(S0).copy()
+    states = [S]  # states[t] = S_{t-1}, the state token t starts from
+    for t in range(N):
+        _, S = delta_step(S, q[:, :, t], k[:, :, t], v[:, :, t], g[:, :, t],
+                          None if al is None else al[:, :, t])
+        states.append(S)
+    Sh = np.zeros((B, H, d, dv_)) if dS_N is None else _f64(dS_N).copy()
+    dq = np.empty((B, H, N, d))
+    dk = np.empty((B, H, N, d))
+    dvv = np.empty((B, H, N, dv_))
+    dg = np.empty((B, H, N))
+    da = None if al is None else np.empty((B, H, N))
+    for t in range(N - 1, -1, -1):
+        qt, kt, vt, gt = q[:, :, t], k[:, :, t], v[:, :, t], g[:, :, t]
+        a = np.ones((B, H)) if al is None else al[:, :, t]
+        S_prev, S_t = states[t], states[t + 1]
+        Sh = Sh + qt[..., :, None] * do[:, :, t][..., None, :]
+        dq[:, :, t] = np.einsum("...rd,...d->...r", S_t, do[:, :, t])
+        pred = np.einsum("...rd,...r->...d", S_prev, kt)  # S_{t-1}^T k_t
+        u = vt - a[..., None] * pred
+        w = np.einsum("...rd,...r->...d", Sh, kt)
+        dvv[:, :, t] = gt[..., None] * w
+        dg[:, :, t] = np.einsum("...d,...d->...", w, u)
+        dk[:, :, t] = (gt[..., None] * np.einsum("...rd,...d->...r", Sh, u)
+                       - (a * gt)[..., None] * np.einsum("...rd,...d->...r", S_prev, w))
+        if da is not None:
+            da[:, :, t] = (np.einsum("...rd,...rd->...", Sh, S_prev)
+                           - gt * np.einsum("...d,...d->...", pred, w))
+        Sh = a[..., None, None] * (Sh - gt[..., None, None] * kt[..., :, None] * w[..., None, :])
+    return dq, dk, dvv, dg, da, Sh

@@ -755,4 +755,105 @@ def pin_denominators_brute_force(orc):
         np.testing.assert_allclose(o[0, 0, t] * den0[t], num, rtol=1e-12, atol=1e-14)
 
 
+# --- backward of the gated DELTA rule (derived; the pages give no formulas) --
+
+def _torch_delta_loss(q, k, v, g, al, S0, do, dS):
+    """Loss sum(o * do) + sum(S_N * dS) of the gated delta recurrence written
+    with explicit matrices, S_t = a (I - g k k^T) S_{t-1} + g k v^T,
+    o_t = S_t^T q_t, in torch ops so that autograd differentiates it."""
+    import torch
+    H, N, d = q.shape
+    eye = torch.eye(d, dtype=torch.float64)
+    S, loss = S0, 0.0
+    for t in range(N):
+        kt = k[:, t]
+        A = al[:, t, None, None] * (eye - g[:, t, None, None] * kt[:, :, None] * kt[:, None, :])
+        S = A @ S + g[:, t, None, None] * kt[:, :, None] * v[:, t, None, :]
+        loss = loss + (torch.einsum("hrd,hr->hd", S, q[:, t]) * do[:, t]).sum()
+    return loss + (S * dS).sum()
+
+
+def pin_delta_backward_matches_autograd(orc):
+    """dq, dk, dv, dg, dalpha and the initial-state gradient of the gated
+    delta rule equal torch autograd's through the explicit-matrix recurrence,
+    with and without the decay, an initial state, a final-state gradient and
+    d != dv."""
+    import torch
+    rng = np.random.default_rng(61)
+    H, N, d, dv = 2, 8, 3, 4
+    for decay in (False, True):
+        q = rng.normal(size=(H, N, d))
+        k = rng.normal(size=(H, N, d)) * 0.6
+        v = rng.normal(size=(H, N, dv))
+        g = rng.uniform(0.1, 0.9, size=(H, N))
+        al = rng.uniform(0.6, 1.0, size=(H, N)) if decay else np.ones((H, N))
+        do = rng.normal(size=(H, N, dv))
+        S0 = rng.normal(size=(H, d, dv)) * 0.5
+        dS = rng.normal(size=(H, d, dv))
+        T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)  # noqa: E731
+        tq, tk, tv, tg, ta, tS0 = T(q), T(k), T(v), T(g), T(al), T(S0)
+        _torch_delta_loss(tq, tk, tv, tg, ta, tS0, torch.tensor(do), torch.tensor(dS)).backward()
+        got = orc.delta_backward(q[None], k[None], v[None], g[None], do[None],
+                                 alpha=al[None] if decay else None, S0=S0[None],
+                                 dS_N=dS[None])
+        want = [tq, tk, tv, tg, ta if decay else None, tS0]
+        for name, x, t in zip(("dq", "dk", "dv", "dg", "dalpha", "dS0"), got, want):
+            if t is None:
+                assert x is None, name
+                continue
+            np.testing.assert_allclose(x[0], t.grad.numpy(), rtol=1e-10, atol=1e-12,
+                                       err_msg=name)
+
+
+def pin_delta_backward_finite_differences(orc):
+    """Central differences of the oracle's own forward (loss sum(o * do) +
+    sum(S_N * dS)) agree with the backward on every entry of q, k, v, g,
+    alpha and the initial state."""
+    rng = np.random.default_rng(62)
+    B, H, N, d, dv, h = 1, 1, 5, 3, 2, 1e-6
+    x = {"q": rng.normal(size=(B, H, N, d)), "k": rng.normal(size=(B, H, N, d)) * 0.6,
+         "v": rng.normal(size=(B, H, N, dv)), "g": rng.uniform(0.1, 0.9, size=(B, H, N)),
+         "alpha": rng.uniform(0.6, 1.0, size=(B, H, N)),
+         "S0": rng.normal(size=(B, H, d, dv)) * 0.5}
+    do = rng.normal(size=(B, H, N, dv))
+    dS = rng.normal(size=(B, H, d, dv))
+    grads = dict(zip(("q", "k", "v", "g", "alpha", "S0"),
+                     orc.delta_backward(x["q"], x["k"], x["v"], x["g"], do, alpha=x["alpha"],
+                                        S0=x["S0"], dS_N=dS)))
+
+    def loss(y):
+        o, S = orc.delta_prefill(y["q"], y["k"], y["v"], y["g"], S0=y["S0"], alpha=y["alpha"])
+        return float(np.sum(o * do) + np.sum(S * dS))
+    for name in x:
+        fd = np.empty_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            yp, ym = dict(x), dict(x)
+            yp[name], ym[name] = x[name].copy(), x[name].copy()
+            yp[name][idx] += h
+            ym[name][idx] -= h
+            fd[idx] = (loss(yp) - loss(ym)) / (2 * h)
+        np.testing.assert_allclose(grads[name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def pin_delta_backward_gate_zero(orc):
+    """With g = 0 the state never changes (S_t = S0, no decay), so
+    o_t = S0^T q_t: dq_t = S0 do_t, dk = dv = 0, dS0 = sum_t q_t do_t^T, and
+    dg_t = (Sh_t^T k_t) . (v_t - S0^T k_t) with Sh_t = sum_(s>=t) q_s do_s^T."""
+    rng = np.random.default_rng(63)
+    N, d, dv = 6, 3, 4
+    q, k, v = rng.normal(size=(N, d)), rng.normal(size=(N, d)), rng.normal(size=(N, dv))
+    do = rng.normal(size=(N, dv))
+    S0 = rng.normal(size=(d, dv))
+    dq, dk, dvv, dg, da, dS0 = orc.delta_backward(_bh(q), _bh(k), _bh(v), _bh(np.zeros(N)),
+                                                   _bh(do), S0=_bh(S0))
+    assert da is None
+    np.testing.assert_allclose(dq[0, 0], do @ S0.T, rtol=1e-12, atol=1e-14)
+    assert not dk.any() and not dvv.any()
+    np.testing.assert_allclose(dS0[0, 0], q.T @ do, rtol=1e-12, atol=1e-14)
+    for t in range(N):
+        Sh = q[t:].T @ do[t:]
+        want = (Sh.T @ k[t]) @ (v[t] - S0.T @ k[t])
+        np.testing.assert_allclose(dg[0, 0, t], want, rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [v for n, v in sorted(globals().items()) if n.startswith("pin_")]

@@ -264,6 +264,27 @@ for _n in ("_bwd_dden_dropped", "_bwd_dden_sign", "_bwd_phi_grad_one",
     globals()[_n].__name__ = _n
 
 
+_dbwd_dk_no_state_term = _patched(
+    """                       - (a * gt)[..., None] * np.einsum("...rd,...d->...r", S_prev, w))""",
+    """                       - 0.0 * np.einsum("...rd,...d->...r", S_prev, w))""")
+_dbwd_adjoint_not_decayed = _patched(
+    "Sh = a[..., None, None] * (Sh - gt", "Sh = (Sh - gt")
+_dbwd_adjoint_no_projection = _patched(
+    "(Sh - gt[..., None, None] * kt[..., :, None] * w[..., None, :])", "(Sh)")
+_dbwd_dv_without_gate = _patched("dvv[:, :, t] = gt[..., None] * w", "dvv[:, :, t] = w")
+_dbwd_dq_from_previous_state = _patched(
+    'dq[:, :, t] = np.einsum("...rd,...d->...r", S_t, do[:, :, t])',
+    'dq[:, :, t] = np.einsum("...rd,...d->...r", S_prev, do[:, :, t])')
+_dbwd_residual_undecayed = _patched("u = vt - a[..., None] * pred", "u = vt - pred")
+_dbwd_dalpha_no_gate_term = _patched(
+    "                           - gt * np.einsum(\"...d,...d->...\", pred, w))",
+    "                           - 0.0 * gt)")
+for _n in ("_dbwd_dk_no_state_term", "_dbwd_adjoint_not_decayed", "_dbwd_adjoint_no_projection",
+           "_dbwd_dv_without_gate", "_dbwd_dq_from_previous_state", "_dbwd_residual_undecayed",
+           "_dbwd_dalpha_no_gate_term"):
+    globals()[_n].__name__ = _n
+
+
 MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _exp_everywhere, _decay_off_by_one, _outer_transposed,
            _quadratic_strict_mask, _delta_not_transposed, _delta_wrong_sign,
@@ -273,7 +294,9 @@ MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _gla_decay_after_write, _conv_taps_reversed, _conv_cache_newest_first,
            _conv_cache_ignored, _conv_excludes_current_token, _conv_qk_filters_swapped,
            _bwd_dden_dropped, _bwd_dden_sign, _bwd_phi_grad_one, _bwd_adjoint_not_decayed,
-           _bwd_dv_from_query, _bwd_dk_without_z]
+           _bwd_dv_from_query, _bwd_dk_without_z, _dbwd_dk_no_state_term,
+           _dbwd_adjoint_not_decayed, _dbwd_adjoint_no_projection, _dbwd_dv_without_gate,
+           _dbwd_dq_from_previous_state, _dbwd_residual_undecayed, _dbwd_dalpha_no_gate_term]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
