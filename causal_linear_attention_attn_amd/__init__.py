@@ -14,6 +14,7 @@ a tensor is not on a GPU, the call raises.
     o = decode_step(q1, k1, v1, S, z, conv_weight=W, conv_cache=C)
     o, S, z = prefill(q, k, v, den_out=den)                   # keep den for training
     dq, dk, dv, dS0, dz0 = backward(q, k, v, o, den, do)      # gradients
+    dq, dk, dv, dg, da, dS0 = delta_backward(q, k, v, g, do, alpha=a)
 """
 from __future__ import annotations
 
@@ -24,7 +25,8 @@ import torch
 from . import _lib
 from ._lib import LinattnError, LibraryMissing  # noqa: F401
 
-__all__ = ["prefill", "decode_step", "backward", "state_init", "workspace_size",
+__all__ = ["prefill", "decode_step", "backward", "delta_backward", "state_init",
+           "workspace_size",
            "LinattnError", "LibraryMissing"]
 
 _RULES = {"linear": _lib.LA_RULE_LINEAR, "delta": _lib.LA_RULE_DELTA}
@@ -227,6 +229,51 @@ def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=No
         a.fwd_workspace_bytes = fwd_workspace.numel() * fwd_workspace.element_size()
     _lib.check(lib.la_backward(ctypes.byref(a), _stream()), "la_backward")
     return dq, dk, dvv, dS_in, dz_in
+
+
+def delta_backward(q, k, v, g, do, *, alpha=None, S_in=None, dS_out=None, state_grad=True,
+                   workspace=None):
+    """Gradients of a gated-delta prefill (see la_delta_backward): q, k
+    [B,H,N,d], v, do [B,H,N,dv] (bf16), g and alpha [B,H,N] fp32 (alpha
+    None: no decay), S_in [B,H,d,dv] the forward's initial state, dS_out
+    the gradient with respect to the final state (or None).
+    Returns (dq, dk, dv, dg, dalpha, dS_in); dalpha is None without a decay,
+    dS_in None unless state_grad."""
+    _need_gpu(q, k, v, g, do, alpha, S_in, dS_out, workspace)
+    _need_f32(g, alpha, S_in, dS_out)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,N,d] and v [B,H,N,dv]")
+    if do.shape != v.shape or tuple(g.shape) != tuple(q.shape[:3]):
+        raise ValueError("do must be [B,H,N,dv] and g [B,H,N]")
+    if alpha is not None and tuple(alpha.shape) != tuple(q.shape[:3]):
+        raise ValueError("alpha must be [B,H,N]")
+    if not (q.dtype == k.dtype == v.dtype == do.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v, do must share dtype float32 or bfloat16")
+    B, H, N, d = q.shape
+    dv = v.shape[3]
+    a = _lib.DeltaBackwardArgs()
+    a.B, a.H, a.N, a.d, a.dv = B, H, N, d, dv
+    a.dtype = _DTYPES[q.dtype]
+    dq, dk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    da = None if alpha is None else torch.empty_like(dg)
+    dS_in = torch.empty((B, H, d, dv), dtype=torch.float32, device=q.device) if state_grad \
+        else None
+    a.q, a.k, a.v, a.g, a.alpha, a.S_in = (_ptr(t) for t in (q, k, v, g, alpha, S_in))
+    a.grad_o, a.grad_S_out = _ptr(do), _ptr(dS_out)
+    a.grad_q, a.grad_k, a.grad_v, a.grad_g = _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(dg)
+    a.grad_alpha, a.grad_S_in = _ptr(da), _ptr(dS_in)
+    lib = _lib.load()
+    need = lib.la_delta_backward_workspace_size(ctypes.byref(a))
+    if need == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes")
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _lib.check(lib.la_delta_backward(ctypes.byref(a), _stream()), "la_delta_backward")
+    return dq, dk, dvv, dg, da, dS_in
 
 
 def decode_step(q, k, v, S, z=None, *, rule="linear", fmap=None, gamma=None,

@@ -12,11 +12,12 @@ NOALLOC_SCRATCH_BYTES = 128 << 20  # LA_NOALLOC_SCRATCH_BYTES
 LA_F32, LA_BF16 = 0, 1
 LA_FMAP_IDENTITY, LA_FMAP_ELU1 = 0, 1
 LA_RULE_LINEAR, LA_RULE_DELTA = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 # Every symbol include/linattn.h declares.
 EXPORTS = ("la_prefill_workspace_size", "la_prefill", "la_prefill_noalloc", "la_decode_step",
            "la_backward_workspace_size", "la_backward",
+           "la_delta_backward_workspace_size", "la_delta_backward",
            "la_state_init", "la_status_str", "la_abi_version",
            "la_profile_enable", "la_profile_collect")
 
@@ -46,6 +47,17 @@ class BackwardArgs(ctypes.Structure):
         ("grad_S_in", _ptr), ("grad_z_in", _ptr),
         ("workspace", _ptr), ("workspace_bytes", _size),
         ("fwd_workspace", _ptr), ("fwd_workspace_bytes", _size),
+    ]
+
+
+class DeltaBackwardArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", _i32), ("H", _i32), ("N", _i32), ("d", _i32), ("dv", _i32), ("dtype", _i32),
+        ("q", _ptr), ("k", _ptr), ("v", _ptr), ("g", _ptr), ("alpha", _ptr), ("S_in", _ptr),
+        ("grad_o", _ptr), ("grad_S_out", _ptr),
+        ("grad_q", _ptr), ("grad_k", _ptr), ("grad_v", _ptr), ("grad_g", _ptr),
+        ("grad_alpha", _ptr), ("grad_S_in", _ptr),
+        ("workspace", _ptr), ("workspace_bytes", _size),
     ]
 
 
@@ -94,6 +106,10 @@ def load(path: str | None = None):
         lib.la_backward_workspace_size.restype = _size
         lib.la_backward.argtypes = [ctypes.POINTER(BackwardArgs), _ptr]
         lib.la_backward.restype = ctypes.c_int
+        lib.la_delta_backward_workspace_size.argtypes = [ctypes.POINTER(DeltaBackwardArgs)]
+        lib.la_delta_backward_workspace_size.restype = _size
+        lib.la_delta_backward.argtypes = [ctypes.POINTER(DeltaBackwardArgs), _ptr]
+        lib.la_delta_backward.restype = ctypes.c_int
         lib.la_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _ptr]
         lib.la_decode_step.restype = ctypes.c_int
         lib.la_state_init.argtypes = [_ptr, _ptr, _i32, _i32, _i32, _i32, _ptr]

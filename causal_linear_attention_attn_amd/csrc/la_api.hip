@@ -152,7 +152,7 @@ bool overlap(const void *a, const void *b, size_t n) {
 
 extern "C" {
 
-int32_t la_abi_version(void) { return 4; }
+int32_t la_abi_version(void) { return 5; }
 
 const char *la_status_str(int s) {
   switch (s) {
@@ -399,6 +399,92 @@ int la_backward(const la_backward_args *a, void *stream) {
   p.seg_len = plan.seg_len;
   p.slot_vec = (a->d % 4 == 0) && aligned16(ws_f) && aligned16(ws_r);
   return to_status(la::launch_linear_backward(p, bf16_io, s));
+}
+
+namespace {
+
+int check_delta_backward_shape(const la_delta_backward_args *a) {
+  if (!a) return LA_EINVAL;
+  if (a->B < 0 || a->H < 0 || a->N < 0 || !dims_ok(a->d, a->dv)) return LA_EINVAL;
+  if ((long long)a->B * a->H > 0x7fffffffLL) return LA_EUNSUPPORTED;
+  if (a->dtype != LA_F32 && a->dtype != LA_BF16) return LA_EINVAL;
+  if (a->dtype != LA_BF16) return LA_EUNSUPPORTED;
+  // the state and reverse passes run 256 threads per (head, 16 value
+  // columns) along one grid axis
+  if ((unsigned long long)a->B * a->H * ((a->dv + 15) / 16) * 256 > kMaxGridItems)
+    return LA_EUNSUPPORTED;
+  const size_t dmax = a->d > a->dv ? a->d : a->dv;
+  if ((size_t)a->N * dmax * 2 > kMaxHeadBytes) return LA_EUNSUPPORTED;
+  // one head's preparation records must be addressable with 32-bit offsets
+  const size_t nch = ((size_t)a->N + 63) / 64, dk = a->d <= 64 ? 64 : 128;
+  if (nch * (2 * dk * 64 + 64 * 64) * 2 > kMaxHeadBytes) return LA_EUNSUPPORTED;
+  return LA_OK;
+}
+
+}  // namespace
+
+size_t la_delta_backward_workspace_size(const la_delta_backward_args *a) {
+  if (check_delta_backward_shape(a) != LA_OK) return (size_t)-1;
+  const int BH = a->B * a->H;
+  if (BH == 0 || a->N == 0) return 0;
+  return la::delta_backward_sizes(BH, a->N, a->d, a->dv).bytes;
+}
+
+int la_delta_backward(const la_delta_backward_args *a, void *stream) {
+  int st = check_delta_backward_shape(a);
+  if (st != LA_OK) return st;
+  const int BH = a->B * a->H;
+  if ((a->alpha != nullptr) != (a->grad_alpha != nullptr) && BH > 0 && a->N > 0)
+    return LA_EINVAL;
+  if (BH > 0 && a->N > 0 &&
+      (!a->q || !a->k || !a->v || !a->g || !a->grad_o || !a->grad_q || !a->grad_k ||
+       !a->grad_v || !a->grad_g))
+    return LA_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (BH == 0) return LA_OK;
+  const size_t nS = (size_t)BH * a->d * a->dv;
+  if (a->N == 0) {  // no tokens: the final state is the initial state
+    hipError_t e = hipSuccess;
+    if (a->grad_S_in)
+      e = a->grad_S_out ? la::launch_copy(a->grad_S_in, a->grad_S_out, nS, s)
+                        : la::launch_fill(a->grad_S_in, nS, 0.f, s);
+    return to_status(e);
+  }
+  const la::BwdDeltaSizes z = la::delta_backward_sizes(BH, a->N, a->d, a->dv);
+  if (!a->workspace || a->workspace_bytes < z.bytes) return LA_EWORKSPACE;
+  if (!aligned16(a->workspace)) return LA_EINVAL;
+  la::BwdDeltaParams p{};
+  p.BH = BH;
+  p.H = a->H;
+  p.N = a->N;
+  p.d = a->d;
+  p.dv = a->dv;
+  p.dvp = z.dvp;
+  p.nch = z.nch;
+  p.vec_ok = (a->d % 8 == 0) && (a->dv % 8 == 0) && aligned16(a->q) && aligned16(a->k) &&
+             aligned16(a->v) && aligned16(a->grad_o) && aligned16(a->grad_q) &&
+             aligned16(a->grad_k) && aligned16(a->grad_v);
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.dout = a->grad_o;
+  p.g = a->g;
+  p.alpha = a->alpha;
+  p.S_in = a->S_in;
+  p.dS_out = a->grad_S_out;
+  p.dq = a->grad_q;
+  p.dk = a->grad_k;
+  p.dv_ = a->grad_v;
+  p.dg = a->grad_g;
+  p.dalpha = a->grad_alpha;
+  p.dS_in = a->grad_S_in;
+  p.ws = a->workspace;
+  p.lay_dec = z.dec;
+  p.lay_states = z.states;
+  p.lay_adj = z.adj;
+  p.lay_y = z.y;
+  p.lay_dd = z.dd;
+  return to_status(la::launch_delta_backward(p, s));
 }
 
 int la_decode_step(const la_decode_args *a, void *stream) {

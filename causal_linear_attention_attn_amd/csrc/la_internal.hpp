@@ -84,6 +84,28 @@ struct DecodeParams {
   void *conv_cache;     // [BH, w-1, 2d+dv], dtype T, updated in place
 };
 
+// Backward of the gated delta rule (bf16).
+struct BwdDeltaParams {
+  int BH, H, N, d, dv;
+  int dvp;       // value width of the state records (64 or 128)
+  int nch;       // chunks per sequence
+  int vec_ok;    // 16-byte loads of q, k rows and 8-byte ones of v, dL/do rows
+  const void *q, *k, *v, *dout;      // forward inputs, dL/do
+  const float *g, *alpha;            // [BH, N]; alpha nullptr = no decay
+  const float *S_in, *dS_out;        // forward initial state, dL/d(final state)
+  void *dq, *dk, *dv_;               // outputs (dtype of q)
+  float *dg, *dalpha, *dS_in;        // [BH, N], [BH, N] (with a decay), [BH, d, dv]
+  void *ws;                          // workspace, sections below
+  size_t lay_dec, lay_states, lay_adj, lay_y, lay_dd;  // element offsets
+};
+struct BwdDeltaSizes {
+  size_t bytes;
+  int dvp, nch;
+  size_t dec, states, adj, y, dd;
+};
+BwdDeltaSizes delta_backward_sizes(int BH, int N, int d, int dv);
+hipError_t launch_delta_backward(const BwdDeltaParams &p, hipStream_t s);
+
 int device_cu_count();  // cached per device
 
 // Grids with one row of workgroups per head put the head on y and, past the

@@ -233,6 +233,54 @@ size_t la_backward_workspace_size(const la_backward_args *args);
 /* dq, dk, dv (and the initial-state gradient) of one LINEAR prefill. */
 int la_backward(const la_backward_args *args, void *stream);
 
+/* Backward of a gated-DELTA-rule prefill (training).  The pages motivate
+ * parallel training ([WILA] section 8; [EAV] sections 8 and 10) but give no
+ * gradient formulas; these are the reverse-mode derivatives of the rule
+ * above, S_t = a_t (I - g_t k_t k_t^T) S_{t-1} + g_t k_t v_t^T,
+ * o_t = S_t^T q_t (a_t = alpha_t, or 1 without a decay).  With the adjoint
+ * Sh_t = dL/dS_t, the residual u_t = v_t - a_t S_{t-1}^T k_t and
+ * w_t = Sh_t^T k_t:
+ *   Sh_t = q_t do_t^T + a_(t+1) (I - g_(t+1) k_(t+1) k_(t+1)^T) Sh_(t+1)
+ *   dq_t = S_t do_t,  dv_t = g_t w_t,  dg_t = w_t . u_t,
+ *   dk_t = g_t Sh_t u_t - a_t g_t S_{t-1} w_t,
+ *   dalpha_t = <Sh_t, S_{t-1}> - g_t (S_{t-1}^T k_t) . w_t,
+ * and dL/d(initial state) = a_0 (I - g_0 k_0 k_0^T) Sh_0; computed chunk by
+ * chunk (a forward pass over chunks for the states, a reverse pass for the
+ * adjoint, then every chunk's gradients in parallel).  Inputs are the
+ * forward's q, k, v, g, alpha and initial state, and dL/do (and optionally
+ * dL/d(final state)); the forward's output is not needed.  bf16 only
+ * (fp32: LA_EUNSUPPORTED). */
+typedef struct la_delta_backward_args {
+  int32_t B, H, N;   /* as the forward (each >= 0) */
+  int32_t d, dv;     /* 1..128 */
+  int32_t dtype;     /* la_dtype of q, k, v, grad_o and their gradients */
+  const void *q;     /* [B,H,N,d]  forward inputs */
+  const void *k;     /* [B,H,N,d]  */
+  const void *v;     /* [B,H,N,dv] */
+  const float *g;    /* [B,H,N] write gate */
+  const float *alpha;/* [B,H,N] state decay, or NULL (none) */
+  const float *S_in; /* [B,H,d,dv] forward initial state; NULL = zeros */
+  const void *grad_o;/* [B,H,N,dv] dL/do */
+  const float *grad_S_out; /* [B,H,d,dv] dL/d(final state); NULL = zero */
+  void *grad_q;      /* [B,H,N,d]  outputs, dtype as q (required if N > 0) */
+  void *grad_k;      /* [B,H,N,d]  */
+  void *grad_v;      /* [B,H,N,dv] */
+  float *grad_g;     /* [B,H,N] (required if N > 0) */
+  float *grad_alpha; /* [B,H,N]: required with alpha, must be NULL without */
+  float *grad_S_in;  /* [B,H,d,dv] dL/d(initial state); NULL = not written */
+  void *workspace;   /* device scratch of workspace_bytes, caller-owned,
+                        16-byte aligned (else LA_EINVAL) */
+  size_t workspace_bytes;
+} la_delta_backward_args;
+
+/* Workspace bytes la_delta_backward needs (0 when none); (size_t)-1 for
+ * invalid sizes.  Reads only the sizes and dtype. */
+size_t la_delta_backward_workspace_size(const la_delta_backward_args *args);
+
+/* dq, dk, dv, dg (and dalpha, the initial-state gradient) of one gated
+ * delta prefill. */
+int la_delta_backward(const la_delta_backward_args *args, void *stream);
+
 /* One token per sequence against a persistent state updated in place. */
 typedef struct la_decode_args {
   int32_t B, H;      /* sequences and heads (each >= 0) */

@@ -43,6 +43,7 @@ def test_struct_layout_matches_header(tmp_path):
     fields_p = [f for f, _ in _lib.PrefillArgs._fields_]
     fields_d = [f for f, _ in _lib.DecodeArgs._fields_]
     fields_b = [f for f, _ in _lib.BackwardArgs._fields_]
+    fields_x = [f for f, _ in _lib.DeltaBackwardArgs._fields_]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "linattn.h"',
              "int main(void){"]
     lines.append('printf("%zu\\n", sizeof(la_prefill_args));')
@@ -54,6 +55,9 @@ def test_struct_layout_matches_header(tmp_path):
     lines.append('printf("%zu\\n", sizeof(la_backward_args));')
     for f in fields_b:
         lines.append(f'printf("%zu\\n", offsetof(la_backward_args, {f}));')
+    lines.append('printf("%zu\\n", sizeof(la_delta_backward_args));')
+    for f in fields_x:
+        lines.append(f'printf("%zu\\n", offsetof(la_delta_backward_args, {f}));')
     lines.append("return 0;}")
     src.write_text("\n".join(lines))
     exe = tmp_path / "layout"
@@ -67,12 +71,14 @@ def test_struct_layout_matches_header(tmp_path):
     want += [getattr(_lib.DecodeArgs, f).offset for f in fields_d]
     want += [ctypes.sizeof(_lib.BackwardArgs)]
     want += [getattr(_lib.BackwardArgs, f).offset for f in fields_b]
+    want += [ctypes.sizeof(_lib.DeltaBackwardArgs)]
+    want += [getattr(_lib.DeltaBackwardArgs, f).offset for f in fields_x]
     assert got == want
 
 
 def test_status_strings(lib):
-    for s in range(5):
-        assert lib.la_status_str(s)
+    for s in range(6):
+        assert lib.la_status_str(s) != b"unknown status"
     assert lib.la_status_str(99) == b"unknown status"
     assert lib.la_abi_version() == _lib.ABI_VERSION
 
@@ -236,3 +242,43 @@ def test_state_init_rejects_invalid_arguments(lib):
     assert lib.la_state_init(ctypes.c_void_p(0x1000), None, 1, 1, 0, 8, None) == \
         _lib.LA_EINVAL
     assert lib.la_state_init(None, None, 0, 4, 8, 8, None) == _lib.LA_OK
+
+
+def _xargs(**kw):
+    a = _lib.DeltaBackwardArgs()
+    a.B, a.H, a.N, a.d, a.dv = 1, 2, 4, 8, 8
+    a.dtype = _lib.LA_BF16
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    a.q = a.k = a.v = a.g = a.grad_o = a.grad_q = a.grad_k = a.grad_v = a.grad_g = fake
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("bad", [
+    dict(B=-1), dict(N=-1), dict(d=0), dict(dv=129), dict(dtype=5),
+    dict(q=None), dict(g=None), dict(grad_o=None), dict(grad_g=None),
+    dict(alpha=ctypes.c_void_p(0x2000)),        # decay without its gradient
+    dict(grad_alpha=ctypes.c_void_p(0x2000)),   # gradient without a decay
+])
+def test_delta_backward_rejects_invalid_arguments(lib, bad):
+    a = _xargs(**bad)
+    assert lib.la_delta_backward(ctypes.byref(a), None) == _lib.LA_EINVAL
+
+
+def test_delta_backward_unsupported_and_workspace(lib):
+    assert lib.la_delta_backward(None, None) == _lib.LA_EINVAL
+    a = _xargs(dtype=_lib.LA_F32)  # bf16 only
+    assert lib.la_delta_backward(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+    assert lib.la_delta_backward_workspace_size(ctypes.byref(a)) == ctypes.c_size_t(-1).value
+    a = _xargs(B=70000, H=40000)
+    assert lib.la_delta_backward(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+    a = _xargs()
+    need = lib.la_delta_backward_workspace_size(ctypes.byref(a))
+    assert 0 < need < 1 << 30
+    assert lib.la_delta_backward(ctypes.byref(a), None) == _lib.LA_EWORKSPACE
+    a.workspace, a.workspace_bytes = ctypes.c_void_p(0x4004), need
+    assert lib.la_delta_backward(ctypes.byref(a), None) == _lib.LA_EINVAL
+    a = _xargs(B=0)
+    assert lib.la_delta_backward(ctypes.byref(a), None) == _lib.LA_OK
+    assert lib.la_delta_backward_workspace_size(ctypes.byref(a)) == 0
