@@ -119,6 +119,8 @@ KERNEL_SRC = {
     "linear_chunk": "la_prefill_linear.hip", "linear_summary": "la_prefill_linear.hip",
     "linear_scan": "la_prefill_linear.hip", "delta_prep": "la_prefill_delta.hip",
     "delta_seq": "la_prefill_delta.hip", "linear_decode": "la_decode.hip",
+    "delta_bwd_prep": "la_backward_delta.hip", "delta_bwd_state": "la_backward_delta.hip",
+    "delta_bwd_rev": "la_backward_delta.hip", "delta_bwd_grad": "la_backward_delta.hip",
     "delta_decode": "la_decode.hip", "linear_bwd_dq": "la_backward_linear.hip",
     "linear_bwd_dkv": "la_backward_linear.hip", "linear_bwd_rscan": "la_backward_linear.hip",
 }
@@ -147,9 +149,17 @@ def library_kernel_name(raw):
         return "linear_bwd_dq"
     if "bwd_dkv_kernel" in raw:
         return "linear_bwd_dkv"
+    if "prep_kernel" in raw:  # its last template flag: the backward's records
+        import re
+
+        m = re.search(r"Lb([01])ELb([01])ELb([01])EEEv", raw) or \
+            re.search(r", (true|false), (true|false), (true|false)>", raw)
+        bwd = m is not None and m.group(3) in ("1", "true")
+        return "delta_bwd_prep" if bwd else "delta_prep"
     for fn, name in (("chunk_kernel", "linear_chunk"), ("summary_kernel", "linear_summary"),
-                     ("scan_kernel", "linear_scan"), ("prep_kernel", "delta_prep"),
-                     ("seq_kernel", "delta_seq"), ("seq2_kernel", "delta_seq")):
+                     ("scan_kernel", "linear_scan"), ("seq_kernel", "delta_seq"),
+                     ("seq2_kernel", "delta_seq"), ("bstate_kernel", "delta_bwd_state"),
+                     ("brev_kernel", "delta_bwd_rev"), ("bgrad_kernel", "delta_bwd_grad")):
         if fn in raw:
             return name
     if "decode_kernel" in raw:
@@ -512,6 +522,74 @@ def bench_train(la, lib, torch, w, steps, warmup):
     }
 
 
+def delta_bwd_bytes_per_head_token(w, kname):
+    """Algorithmic bytes of one delta-rule backward kernel per head-token:
+    the inputs and gradients it reads or writes (q, k, v, dL/do rows, the
+    gate and decay; workspace records excluded)."""
+    e, d, dv = w.dtype.itemsize, w.d, w.dv
+    gd = 4 + (4 if w.decay == "alpha" else 0)  # g (and alpha), fp32
+    return {"delta_bwd_prep": 2 * d * e + gd,
+            "delta_bwd_state": (d + dv) * e,
+            "delta_bwd_rev": (2 * d + dv) * e + dv * e,
+            "delta_bwd_grad": (2 * d + 2 * dv) * e + gd + 2 * d * e + gd}[kname]
+
+
+def delta_train_bytes_per_head_token(w):
+    """The training step's algorithmic bytes: the forward's (q, k, v, g, alpha
+    read, o written) and the backward's (q, k, v, g, alpha, dL/do read; dq,
+    dk, dv, dg, dalpha written)."""
+    e, d, dv = w.dtype.itemsize, w.d, w.dv
+    gd = 4 + (4 if w.decay == "alpha" else 0)
+    return bytes_per_head_token(w) + (2 * d + 2 * dv) * e + gd + (2 * d + dv) * e + gd
+
+
+def bench_train_delta(la, lib, torch, w, steps, warmup):
+    """Training step of a gated-delta workload: the prefill, then
+    la_delta_backward for a seeded dL/do."""
+    from causal_linear_attention_attn_amd import inputs
+
+    x = inputs.make_prefill(w, "cuda")
+    do = inputs.make_grad_out(w, "cuda")
+    q, k, v, g, al = x["q"], x["k"], x["v"], x["g"], x.get("alpha")
+    o = torch.empty((w.B, w.H, w.N, w.dv), dtype=w.dtype, device="cuda")
+    wsf = torch.empty(max(la.workspace_size(q, k, v, rule="delta", g=g), 1), dtype=torch.uint8,
+                      device="cuda")
+    wsb = torch.empty(max(la.delta_backward_workspace_size(q, k, v), 1), dtype=torch.uint8,
+                      device="cuda")
+
+    def fwd():
+        la.prefill(q, k, v, rule="delta", g=g, alpha=al, o=o, workspace=wsf, return_state=False)
+
+    def bwd():
+        return la.delta_backward(q, k, v, g, do, alpha=al, state_grad=False, workspace=wsb)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(max(1, warmup // 4)):
+        step()
+    torch.cuda.synchronize()
+    kern = time_kernels(lib, torch, bwd, max(3, steps // 4))
+    dt = time_graph(torch, step, steps, warmup)
+    head_tokens = w.B * w.H * w.N
+    kname, kms = dominant(kern)
+    bpl = head_tokens * delta_bwd_bytes_per_head_token(w, kname)
+    achieved = bpl / (kms * 1e-3) / 1e9
+    traffic, tsrc = traffic_record(w.name, kname)
+    step_bytes = head_tokens * delta_train_bytes_per_head_token(w)
+    return {
+        "workload": w.name + "_forward_backward", "tokens_per_s": w.B * w.N / dt,
+        "ms_per_step": dt * 1e3, "backward_kernels_ms": kern,
+        "backward_ms": sum(kern.values()),
+        "step_hbm_frac": step_bytes / dt / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"kernel": kname, "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "traffic_profile": tsrc, "bytes_per_launch": bpl,
+                     "kernel_ms": kms},
+    }
+
+
 def decode_step_bytes(w):
     """Algorithmic bytes of one decode step: state S and z read and written
     once; q, k, v read and o written once."""
@@ -780,6 +858,9 @@ def main():
     if not args.no_train and w.rule == "linear" and w.decay in ("none", "per_head") \
             and not w.conv:
         line["train"] = bench_train(la, lib, torch, w, max(10, args.steps // 4), 5)
+    if not args.no_train:
+        wd = inputs.WORKLOADS[5]
+        line["train_delta"] = bench_train_delta(la, lib, torch, wd, max(10, args.steps // 10), 3)
     if not args.no_extra:
         extra = {}
         for wid in (4, 5, 6, 7, 8):

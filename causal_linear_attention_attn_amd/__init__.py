@@ -25,7 +25,8 @@ import torch
 from . import _lib
 from ._lib import LinattnError, LibraryMissing  # noqa: F401
 
-__all__ = ["prefill", "decode_step", "backward", "delta_backward", "state_init",
+__all__ = ["prefill", "decode_step", "backward", "delta_backward",
+           "delta_backward_workspace_size", "state_init",
            "workspace_size",
            "LinattnError", "LibraryMissing"]
 
@@ -229,6 +230,18 @@ def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=No
         a.fwd_workspace_bytes = fwd_workspace.numel() * fwd_workspace.element_size()
     _lib.check(lib.la_backward(ctypes.byref(a), _stream()), "la_backward")
     return dq, dk, dvv, dS_in, dz_in
+
+
+def delta_backward_workspace_size(q, k, v):
+    """Workspace bytes la_delta_backward needs for these tensors."""
+    B, H, N, d = q.shape
+    a = _lib.DeltaBackwardArgs()
+    a.B, a.H, a.N, a.d, a.dv = B, H, N, d, v.shape[3]
+    a.dtype = _DTYPES[q.dtype]
+    n = _lib.load().la_delta_backward_workspace_size(ctypes.byref(a))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes")
+    return int(n)
 
 
 def delta_backward(q, k, v, g, do, *, alpha=None, S_in=None, dS_out=None, state_grad=True,

@@ -541,6 +541,20 @@ __device__ __forceinline__ void tile_load(bf16 *tile, int ld, int cols, __amdgpu
   }
 }
 
+// Rows r0 .. r0 + nrows - 1 of a bf16 [DK][dvp] record into an LDS tile of
+// DV columns (stride ld), columns past dv zero; every thread takes 16-byte
+// blocks.
+__device__ __forceinline__ void stage_rec(bf16 *tile, int ld, __amdgpu_buffer_rsrc_t r, int r0,
+                                          int nrows, int DV, int dvp, int dv) {
+  const int cb = DV / 8;
+  for (int b = threadIdx.x; b < nrows * cb; b += kThreads) {
+    const int row = b / cb, n = (b % cb) * 8;
+    Frag<bf16> f;
+    rec_row_frag(f, r, r0 + row, n, dvp, dv);
+    *reinterpret_cast<bf16x8 *>(tile + row * ld + n) = f.v;
+  }
+}
+
 __device__ __forceinline__ float sum16(float x) {  // over the 16 lanes li of a slot group
   x += __shfl_xor(x, 1);
   x += __shfl_xor(x, 2);
@@ -686,15 +700,32 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
   }
 
   // ---- U = X^(-1) diag(g) Y (fp32 matrix cores): rows of this wave's block ----
-  for (int ct = 0; ct < G::NVT; ++ct) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < 16 * rb + 16; k0 += 4) {
-      const float a = sm.Xi[(16 * rb + li) * LDX + k0 + lg];
-      const float b = sm.gs[k0 + lg] * (float)sm.Ys[(k0 + lg) * LDV + 16 * ct + li];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+  // (per 16-wide k block: the lane's four consecutive k of its row of X^(-1)
+  // in one 16-byte read, k = 16 bm + 4 lg + kk in product kk)
+  // (every value-column tile advances together: independent accumulators)
+  {
+    f32x4 acc[G::NVT];
+#pragma unroll
+    for (int ct = 0; ct < G::NVT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int bm = 0; bm <= rb; ++bm) {
+      const f32x4 a =
+          *reinterpret_cast<const f32x4 *>(sm.Xi + (16 * rb + li) * LDX + 16 * bm + 4 * lg);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k = 16 * bm + 4 * lg + kk;
+        const float gk = sm.gs[k];
+#pragma unroll
+        for (int ct = 0; ct < G::NVT; ++ct) {
+          const float b = gk * (float)sm.Ys[k * LDV + 16 * ct + li];
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk], b, acc[ct], 0, 0, 0);
+        }
+      }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sm.Us[(16 * rb + 4 * lg + r) * LDV + 16 * ct + li] = (bf16)acc[r];
+    for (int ct = 0; ct < G::NVT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sm.Us[(16 * rb + 4 * lg + r) * LDV + 16 * ct + li] = (bf16)acc[ct][r];
   }
   __syncthreads();
 
@@ -710,14 +741,17 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
   }
   f32x4 du[G::NVT];
 #pragma unroll
-  for (int ct = 0; ct < G::NVT; ++ct) {
+  for (int ct = 0; ct < G::NVT; ++ct)
 #pragma unroll
     for (int r = 0; r < 4; ++r) du[ct][r] = (float)sm.Ds[(16 * rb + 4 * lg + r) * LDV + 16 * ct + li];
 #pragma unroll
-    for (int ks = 0; ks < C / 32; ++ks) {
-      if (32 * ks + 31 < 16 * rb) continue;  // P[j][i] = 0 for j < i
-      Frag<bf16> pf, of;
-      lds_frag_tr(pf, sm.Pb, LDC, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * rb, li);
+  for (int ks = 0; ks < C / 32; ++ks) {
+    if (32 * ks + 31 < 16 * rb) continue;  // P[j][i] = 0 for j < i
+    Frag<bf16> pf;
+    lds_frag_tr(pf, sm.Pb, LDC, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * rb, li);
+#pragma unroll
+    for (int ct = 0; ct < G::NVT; ++ct) {
+      Frag<bf16> of;
       lds_frag_tr(of, sm.dOs, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * ct, li);
       mma(du[ct], pf, of);
     }
@@ -732,29 +766,41 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
 
   // ---- lam = X^(-T) dU and r = Y - L U (same tiles); dg_j = lam_j . r_j ----
   {
-    float dgp[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int ct = 0; ct < G::NVT; ++ct) {
-      f32x4 lam = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 16 * rb; k0 < C; k0 += 4) {
-        const float a = sm.Xi[(k0 + lg) * LDX + 16 * rb + li];
-        const float b = (float)sm.Ds[(k0 + lg) * LDV + 16 * ct + li];
-        lam = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, lam, 0, 0, 0);
-      }
-      f32x4 lu = {0.f, 0.f, 0.f, 0.f};
+    f32x4 lam[G::NVT];
 #pragma unroll
-      for (int ks = 0; ks < C / 32; ++ks) {
-        if (32 * ks > 16 * rb + 15) continue;  // L[i][j] = 0 for j >= i
-        Frag<bf16> lf, uf;
-        lds_frag(lf, sm.Lb + (16 * rb + li) * LDC + 32 * ks + 8 * lg);
-        lds_frag_tr(uf, sm.Us, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * ct, li);
-        mma(lu, lf, uf);
+    for (int ct = 0; ct < G::NVT; ++ct) lam[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int k0 = 16 * rb; k0 < C; k0 += 4) {
+      const float a = sm.Xi[(k0 + lg) * LDX + 16 * rb + li];
+#pragma unroll
+      for (int ct = 0; ct < G::NVT; ++ct) {
+        const float b = (float)sm.Ds[(k0 + lg) * LDV + 16 * ct + li];
+        lam[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, lam[ct], 0, 0, 0);
       }
+    }
+    float dgp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C / 32; ++ks) {
+      if (32 * ks > 16 * rb + 15) continue;  // L[i][j] = 0 for j >= i
+      Frag<bf16> lf;
+      lds_frag(lf, sm.Lb + (16 * rb + li) * LDC + 32 * ks + 8 * lg);
+#pragma unroll
+      for (int ct = 0; ct < G::NVT; ++ct) {
+        Frag<bf16> uf;
+        lds_frag_tr(uf, sm.Us, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * ct, li);
+        f32x4 lu = {0.f, 0.f, 0.f, 0.f};
+        mma(lu, lf, uf);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dgp[r] = fmaf(-lam[ct][r], lu[r], dgp[r]);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < G::NVT; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float y = (float)sm.Ys[(16 * rb + 4 * lg + r) * LDV + 16 * ct + li];
-        dgp[r] = fmaf(lam[r], y - lu[r], dgp[r]);
+        dgp[r] = fmaf(lam[ct][r], y, dgp[r]);
       }
-    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float s = sum16(dgp[r]);
@@ -765,7 +811,11 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
   __syncthreads();
 
   // ---- dP = dO U^T, -dY U^T (lower tiles): P's and L's gradients, the
-  //      decay's row/column sums; Pb <- dP (.) Mb, Lb <- G + G^T ----
+  //      decay's row/column sums; Pb <- dP (.) Mb, Lb <- G + G^T.  The
+  //      chunk's S- goes to the Ys / Ds tiles meanwhile (no longer read) ----
+  bf16 *const Sm = sm.Ys;  // S- [DK][DV], stride LDV, over Ys and then Ds
+  static_assert(DK <= 2 * C, "S- fits the Y and D tiles");
+  stage_rec(Sm, LDV, rS, 0, DK, DV, dvp, dv);
   {
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
     for (int tj = 0; tj <= rb; ++tj) {
@@ -824,22 +874,28 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
   // ---- dQ = diag(b) dO S-^T + (dP (.) Mb) K; d log b_i += b_i q_i . (dO S-^T)_i ----
   {
     float da[4] = {0.f, 0.f, 0.f, 0.f};
+    Frag<bf16> ofr[DV / 32], pfr[C / 32];  // this wave's rows of dO and of dP (.) Mb
+#pragma unroll
+    for (int ks = 0; ks < DV / 32; ++ks)
+      lds_frag(ofr[ks], sm.dOs + (16 * rb + li) * LDV + 32 * ks + 8 * lg);
+#pragma unroll
+    for (int ks = 0; ks < C / 32; ++ks)
+      lds_frag(pfr[ks], sm.Pb + (16 * rb + li) * LDC + 32 * ks + 8 * lg);
+#pragma unroll 2
     for (int tf = 0; tf < G::NFT; ++tf) {
       f32x4 t1 = {0.f, 0.f, 0.f, 0.f}, t2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DV / 32; ++ks) {
-        Frag<bf16> of, sf;
-        lds_frag(of, sm.dOs + (16 * rb + li) * LDV + 32 * ks + 8 * lg);
-        rec_row_frag(sf, rS, 16 * tf + li, 32 * ks + 8 * lg, dvp, dv);
-        mma(t1, of, sf);
+        Frag<bf16> sf;
+        lds_frag(sf, Sm + (16 * tf + li) * LDV + 32 * ks + 8 * lg);
+        mma(t1, ofr[ks], sf);
       }
 #pragma unroll
       for (int ks = 0; ks < C / 32; ++ks) {
         if (32 * ks > 16 * rb + 15) continue;
-        Frag<bf16> pf, kf;
-        lds_frag(pf, sm.Pb + (16 * rb + li) * LDC + 32 * ks + 8 * lg);
+        Frag<bf16> kf;
         lds_frag_tr(kf, sm.Ks, LDK, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * tf, li);
-        mma(t2, pf, kf);
+        mma(t2, pfr[ks], kf);
       }
       const int f = 16 * tf + li;
 #pragma unroll
@@ -859,34 +915,58 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
     }
   }
   // ---- dK = (dP (.) Mb)^T Q - diag(b) dY S-^T + diag(beta / b) U Sh+^T + (G + G^T) K;
-  //      d log b_j -= b_j k_j . (dY S-^T)_j ----
+  //      d log b_j -= b_j k_j . (dY S-^T)_j.  Sh+ goes to the dO tile (no
+  //      longer read), 64 rows at a time; beta <Sh+, S-> alongside ----
+  bf16 *const Shs = sm.dOs;
+  float shs = 0.f;  // this thread's part of <Sh+, S->
   {
     float da[4] = {0.f, 0.f, 0.f, 0.f};
+    // this wave's rows j of (G + G^T), of (dP (.) Mb)^T, of dY and of U
+    Frag<bf16> gfr[C / 32], ptr_[C / 32], yfr[DV / 32], ufr[DV / 32];
+#pragma unroll
+    for (int ks = 0; ks < C / 32; ++ks) {
+      lds_frag(gfr[ks], sm.Lb + (16 * rb + li) * LDC + 32 * ks + 8 * lg);
+      lds_frag_tr(ptr_[ks], sm.Pb, LDC, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * rb, li);
+    }
+#pragma unroll
+    for (int ks = 0; ks < DV / 32; ++ks) {
+      lds_frag(yfr[ks], sm.dYs + (16 * rb + li) * LDV + 32 * ks + 8 * lg);
+      lds_frag(ufr[ks], sm.Us + (16 * rb + li) * LDV + 32 * ks + 8 * lg);
+    }
     for (int tf = 0; tf < G::NFT; ++tf) {
+      if (tf % 4 == 0) {  // the next 64 rows of Sh+
+        __syncthreads();
+        stage_rec(Shs, LDV, rA, 16 * tf, 64, DV, dvp, dv);
+        __syncthreads();
+        if constexpr (DECAY) {
+          for (int e = tid; e < 64 * (DV / 8); e += kThreads) {
+            const int row = e / (DV / 8), n = (e % (DV / 8)) * 8;
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Shs + row * LDV + n);
+            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(Sm + (16 * tf + row) * LDV + n);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) shs = fmaf((float)a[m], (float)b[m], shs);
+          }
+        }
+      }
       f32x4 t1 = {0.f, 0.f, 0.f, 0.f}, t2 = {0.f, 0.f, 0.f, 0.f}, t3 = {0.f, 0.f, 0.f, 0.f},
             t4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < C / 32; ++ks) {
         Frag<bf16> kf;
         lds_frag_tr(kf, sm.Ks, LDK, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * tf, li);
-        Frag<bf16> gf;
-        lds_frag(gf, sm.Lb + (16 * rb + li) * LDC + 32 * ks + 8 * lg);
-        mma(t4, gf, kf);
+        mma(t4, gfr[ks], kf);
         if (32 * ks + 31 < 16 * rb) continue;  // dP (.) Mb [i][j] = 0 for i < j
-        Frag<bf16> pf, qf;
-        lds_frag_tr(pf, sm.Pb, LDC, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * rb, li);
+        Frag<bf16> qf;
         lds_frag_tr(qf, sm.Qs, LDK, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * tf, li);
-        mma(t1, pf, qf);
+        mma(t1, ptr_[ks], qf);
       }
 #pragma unroll
       for (int ks = 0; ks < DV / 32; ++ks) {
-        Frag<bf16> yf, uf, sf, hf;
-        lds_frag(yf, sm.dYs + (16 * rb + li) * LDV + 32 * ks + 8 * lg);
-        lds_frag(uf, sm.Us + (16 * rb + li) * LDV + 32 * ks + 8 * lg);
-        rec_row_frag(sf, rS, 16 * tf + li, 32 * ks + 8 * lg, dvp, dv);
-        rec_row_frag(hf, rA, 16 * tf + li, 32 * ks + 8 * lg, dvp, dv);
-        mma(t2, yf, sf);
-        mma(t3, uf, hf);
+        Frag<bf16> sf, hf;
+        lds_frag(sf, Sm + (16 * tf + li) * LDV + 32 * ks + 8 * lg);
+        lds_frag(hf, Shs + (16 * (tf % 4) + li) * LDV + 32 * ks + 8 * lg);
+        mma(t2, yfr[ks], sf);
+        mma(t3, ufr[ks], hf);
       }
       const int f = 16 * tf + li;
 #pragma unroll
@@ -908,16 +988,7 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
     }
   }
   if constexpr (DECAY) {
-    // beta <Sh+, S-> over the chunk's records
-    float s = 0.f;
-    for (int e = tid; e < DK * (DV / 8); e += kThreads) {
-      const int f = e / (DV / 8), n = (e % (DV / 8)) * 8;
-      Frag<bf16> a, b;
-      rec_row_frag(a, rS, f, n, dvp, dv);
-      rec_row_frag(b, rA, f, n, dvp, dv);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) s = fmaf((float)a.v[m], (float)b.v[m], s);
-    }
+    float s = shs;  // beta <Sh+, S-> over the chunk's records
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) s += __shfl_xor(s, o);
     if (lane == 0) sm.red[wv] = s;

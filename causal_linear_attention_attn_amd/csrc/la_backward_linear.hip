@@ -841,21 +841,28 @@ hipError_t run_bwd_vk(const BwdParams &p, hipStream_t s) {
 }
 
 // bf16: 64-token chunks at d = dv = 64, 32-token chunks (and eight waves)
-// with 128-wide tiles; fp32 up to 64-wide tiles, 32-token chunks.
+// with 128-wide tiles; fp32: 32-token chunks, feature and value tiles of
+// 64 and 64, 64 and 128, or 128 and 64 (128 and 128 exceed the LDS: the
+// fp32 state tile alone takes 84 KB).
 using BB64x64 = BCfg<bf16, 64, 64, 32, 4, 3>;
 using BB64x128 = BCfg<bf16, 64, 128, 32, 8, 2>;
 using BB128x64 = BCfg<bf16, 128, 64, 32, 8, 2>;
 using BB128x128 = BCfg<bf16, 128, 128, 32, 8, 2>;
 using BF64x64 = BCfg<float, 64, 64, 32, 4, 1>;
+using BF64x128 = BCfg<float, 64, 128, 32, 4, 1>;
+using BF128x64 = BCfg<float, 128, 64, 32, 4, 1>;
 
 }  // namespace
 
 bool linear_backward_supported(int d, int dv, bool bf16_io) {
-  return bf16_io || (d <= 64 && dv <= 64);
+  return bf16_io || d <= 64 || dv <= 64;
 }
 
 hipError_t launch_linear_backward(const BwdParams &p, bool bf16_io, hipStream_t s) {
-  if (!bf16_io) return run_bwd_vk<BF64x64>(p, s);
+  if (!bf16_io) {
+    if (p.d <= 64) return p.dv <= 64 ? run_bwd_vk<BF64x64>(p, s) : run_bwd_vk<BF64x128>(p, s);
+    return run_bwd_vk<BF128x64>(p, s);
+  }
   if (p.d <= 64) return p.dv <= 64 ? run_bwd_vk<BB64x64>(p, s) : run_bwd_vk<BB64x128>(p, s);
   return p.dv <= 64 ? run_bwd_vk<BB128x64>(p, s) : run_bwd_vk<BB128x128>(p, s);
 }

@@ -189,8 +189,9 @@ int la_prefill_noalloc(const la_prefill_args *args, void *stream);
  *   dq = dphi(q) phi'(q), dk = dphi(k) phi'(k); dL/d(initial state) = gamma Sh_0.
  * Inputs are the forward's q, k, v, gamma, initial state, its output o and
  * its denominators den (la_prefill's den_out); no per-key-channel decay
- * (alpha) or convolution.  fp32 inputs take d, dv <= 64 (LA_EUNSUPPORTED
- * above); bf16 any d, dv up to 128. */
+ * (alpha) or convolution.  fp32 inputs take d or dv up to 64 (both above
+ * 64: LA_EUNSUPPORTED, the fp32 state tile of the 128 x 128 kernels would
+ * not fit the LDS); bf16 any d, dv up to 128. */
 typedef struct la_backward_args {
   int32_t B, H, N;   /* as the forward */
   int32_t d, dv;

@@ -217,7 +217,7 @@ def test_backward_rejects_invalid_arguments(lib, bad):
 
 def test_backward_unsupported_and_sizes(lib):
     assert lib.la_backward(None, None) == _lib.LA_EINVAL
-    a = _bargs(dtype=_lib.LA_F32, d=128)  # fp32 backward takes d, dv <= 64
+    a = _bargs(dtype=_lib.LA_F32, d=128, dv=100)  # fp32 backward: d or dv <= 64
     assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
     assert lib.la_backward_workspace_size(ctypes.byref(a)) == ctypes.c_size_t(-1).value
     a = _bargs(B=70000, H=40000)  # B*H past the int32 range
