@@ -216,6 +216,9 @@ def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=No
     a.grad_S_out, a.grad_z_out = _ptr(dS_out), _ptr(dz_out)
     a.grad_q, a.grad_k, a.grad_v = _ptr(dq), _ptr(dk), _ptr(dvv)
     a.grad_S_in, a.grad_z_in = _ptr(dS_in), _ptr(dz_in)
+    if fwd_workspace is not None:
+        a.fwd_workspace = _ptr(fwd_workspace)
+        a.fwd_workspace_bytes = fwd_workspace.numel() * fwd_workspace.element_size()
     lib = _lib.load()
     need = lib.la_backward_workspace_size(ctypes.byref(a))
     if need == ctypes.c_size_t(-1).value:
@@ -225,9 +228,6 @@ def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=No
     if workspace is not None:
         a.workspace = _ptr(workspace)
         a.workspace_bytes = workspace.numel() * workspace.element_size()
-    if fwd_workspace is not None:
-        a.fwd_workspace = _ptr(fwd_workspace)
-        a.fwd_workspace_bytes = fwd_workspace.numel() * fwd_workspace.element_size()
     _lib.check(lib.la_backward(ctypes.byref(a), _stream()), "la_backward")
     return dq, dk, dvv, dS_in, dz_in
 

@@ -292,8 +292,11 @@ int check_backward_shape(const la_backward_args *a) {
   return LA_OK;
 }
 
-// Forward-state and adjoint slots: two copies of the forward's segment slots.
-size_t backward_ws_bytes(const la::LinearPlan &pl) { return 2 * pl.ws_bytes; }
+// Adjoint slots (one copy of the forward's segment slots), and in front of
+// them the forward-state slots unless the forward's workspace is reused.
+size_t backward_ws_bytes(const la::LinearPlan &pl, bool reuse) {
+  return (reuse ? 1 : 2) * pl.ws_bytes;
+}
 
 }  // namespace
 
@@ -301,7 +304,8 @@ size_t la_backward_workspace_size(const la_backward_args *a) {
   if (check_backward_shape(a) != LA_OK) return (size_t)-1;
   const int BH = a->B * a->H;
   if (BH == 0 || a->N == 0) return 0;
-  return backward_ws_bytes(la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16, 0));
+  return backward_ws_bytes(la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16, 0),
+                           a->fwd_workspace != nullptr);
 }
 
 int la_backward(const la_backward_args *a, void *stream) {
@@ -327,7 +331,10 @@ int la_backward(const la_backward_args *a, void *stream) {
   }
   const bool bf16_io = a->dtype == LA_BF16;
   const la::LinearPlan plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io, 0);
-  const size_t need = plan.nseg > 1 ? backward_ws_bytes(plan) : 0;
+  // the forward's own records, when given (same plan, same slots); else
+  // this call's workspace, filled below
+  const bool reuse = plan.nseg > 1 && a->fwd_workspace != nullptr;
+  const size_t need = plan.nseg > 1 ? backward_ws_bytes(plan, reuse) : 0;
   if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return LA_EWORKSPACE;
   const int vec = bf16_io ? 8 : 4;
   const bool vec_ok = (a->d % vec == 0) && (a->dv % vec == 0) && aligned16(a->q) &&
@@ -339,10 +346,7 @@ int la_backward(const la_backward_args *a, void *stream) {
     if (reinterpret_cast<uintptr_t>(a->fwd_workspace) & 3u) return LA_EINVAL;
   }
   float *ws_own = reinterpret_cast<float *>(a->workspace);
-  float *ws_r = ws_own ? ws_own + plan.ws_bytes / sizeof(float) : nullptr;
-  // the forward's own records, when given (same plan, same slots); else
-  // this call's workspace, filled below
-  const bool reuse = plan.nseg > 1 && a->fwd_workspace != nullptr;
+  float *ws_r = ws_own ? ws_own + (reuse ? 0 : plan.ws_bytes / sizeof(float)) : nullptr;
   const float *ws_f = reuse ? reinterpret_cast<const float *>(a->fwd_workspace) : ws_own;
   if (plan.nseg > 1 && !reuse) {  // the forward state entering each segment
     la::PrefillParams fp{};

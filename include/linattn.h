@@ -228,7 +228,9 @@ typedef struct la_backward_args {
 } la_backward_args;
 
 /* Workspace bytes la_backward needs (0 when none); (size_t)-1 for invalid
- * sizes.  Reads only the sizes and dtype. */
+ * sizes.  Reads only the sizes, the dtype and whether fwd_workspace is NULL:
+ * with the forward's workspace given, half as many bytes (the adjoint slots
+ * only; the forward's states are read from fwd_workspace). */
 size_t la_backward_workspace_size(const la_backward_args *args);
 
 /* dq, dk, dv (and the initial-state gradient) of one LINEAR prefill. */

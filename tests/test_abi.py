@@ -227,6 +227,18 @@ def test_backward_unsupported_and_sizes(lib):
     assert lib.la_backward_workspace_size(ctypes.byref(a)) == 0
 
 
+def test_backward_workspace_halves_with_forward_workspace(lib):
+    """With the forward's workspace given, only the adjoint slots are needed:
+    one forward workspace's worth, half of what recomputing the states takes."""
+    a = _bargs(B=4, H=16, N=4096, d=64, dv=64)
+    own = lib.la_backward_workspace_size(ctypes.byref(a))
+    f = _args(B=4, H=16, N=4096, d=64, dv=64)
+    fwd = lib.la_prefill_workspace_size(ctypes.byref(f))
+    assert fwd > 0 and own == 2 * fwd
+    a.fwd_workspace = ctypes.c_void_p(0x10000)
+    assert lib.la_backward_workspace_size(ctypes.byref(a)) == fwd
+
+
 def test_prefill_den_out_only_for_linear(lib):
     a = _args(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY, g=ctypes.c_void_p(0x2000),
               den_out=ctypes.c_void_p(0x3000))
