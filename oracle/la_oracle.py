@@ -420,6 +420,44 @@ def delta_decode_step(q, k, v, g, S, alpha=None):
                       None if alpha is None else _f64(alpha))
 
 
+def delta_prefill_conv(q, k, v, g, conv_weight, *, conv_cache=None, S0=None, alpha=None):
+    """Short convolution of q, k and v ([WILA] 5.4, which adds it in front of
+    the linear layer beside Gamma, Delta and Gate), then delta_prefill on the
+    convolved q, k, v.  The pages give no normalisation after the
+    convolution, so none is applied: the rule sees the filters' outputs.
+
+    conv_weight: [H, w, 2d + dv], channels [q | k | v]; conv_cache:
+    [B, H, w-1, 2d + dv] raw tokens before the sequence, or None (zeros).
+    Returns (o, S_N, conv cache after the last token [B, H, w-1, 2d + dv]).
+    """
+    d = q.shape[-1]
+    wq, wk, wv = _conv_split(conv_weight, d)
+    cq = ck = cv = None
+    if conv_cache is not None:
+        cq, ck, cv = _conv_split(conv_cache, d)
+    yq, hq = short_conv(q, wq, cq)
+    yk, hk = short_conv(k, wk, ck)
+    yv, hv = short_conv(v, wv, cv)
+    o, S = delta_prefill(yq, yk, yv, g, S0=S0, alpha=alpha)
+    return o, S, np.concatenate([hq, hk, hv], axis=-1)
+
+
+def delta_decode_step_conv(q, k, v, g, S, conv_weight, conv_cache, alpha=None):
+    """One decode step of the gated delta rule behind the short convolution:
+    the token joins the conv cache's window, the convolved q, k, v go through
+    delta_decode_step.  q, k: [B, H, d]; v: [B, H, dv]; g, alpha: [B, H];
+    conv_cache: [B, H, w-1, 2d + dv].  Returns (o, S_new, conv cache after
+    the token); the inputs are not modified."""
+    d = q.shape[-1]
+    wq, wk, wv = _conv_split(conv_weight, d)
+    cq, ck, cv = _conv_split(conv_cache, d)
+    yq, hq = short_conv(_f64(q)[:, :, None], wq, cq)
+    yk, hk = short_conv(_f64(k)[:, :, None], wk, ck)
+    yv, hv = short_conv(_f64(v)[:, :, None], wv, cv)
+    o, S_new = delta_decode_step(yq[:, :, 0], yk[:, :, 0], yv[:, :, 0], g, S, alpha=alpha)
+    return o, S_new, np.concatenate([hq, hk, hv], axis=-1)
+
+
 def delta_backward(q, k, v, g, do, *, alpha=None, S0=None, dS_N=None):
     """Gradients of the gated delta rule's prefill, token by token in reverse.
 

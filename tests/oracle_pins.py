@@ -653,6 +653,73 @@ def pin_conv_split_and_decode(orc):
     np.testing.assert_array_equal(C1, C)
 
 
+def pin_conv_then_delta_brute_force(orc):
+    """delta_prefill_conv (distinct filters, d != dv, with a decay) equals
+    explicit matrix products S <- alpha (I - g k k^T) S + g k v^T, o = S^T q
+    on inputs convolved by numpy's correlation, and returns the raw last
+    tokens as the cache."""
+    rng = np.random.default_rng(45)
+    H, N, d, dv, w = 2, 9, 3, 4, 3
+    q = rng.normal(size=(1, H, N, d))
+    k = rng.normal(size=(1, H, N, d))
+    v = rng.normal(size=(1, H, N, dv))
+    g = rng.uniform(0.1, 0.9, size=(1, H, N))
+    al = rng.uniform(0.6, 1.0, size=(1, H, N))
+    W = rng.normal(size=(H, w, 2 * d + dv)) * 0.6
+    cache = rng.normal(size=(1, H, w - 1, 2 * d + dv))
+    S0 = rng.normal(size=(1, H, d, dv))
+    o, S, hist = orc.delta_prefill_conv(q, k, v, g, W, conv_cache=cache, S0=S0, alpha=al)
+    cq, _ = _correlate_conv(q[0], W[..., :d], cache[0][..., :d])
+    ck, _ = _correlate_conv(k[0], W[..., d:2 * d], cache[0][..., d:2 * d])
+    cv, _ = _correlate_conv(v[0], W[..., 2 * d:], cache[0][..., 2 * d:])
+    eye = np.eye(d)
+    for h in range(H):
+        Sh = S0[0, h].copy()
+        for t in range(N):
+            kk = ck[h, t]
+            Sh = al[0, h, t] * (eye - g[0, h, t] * np.outer(kk, kk)) @ Sh + \
+                g[0, h, t] * np.outer(kk, cv[h, t])
+            np.testing.assert_allclose(o[0, h, t], Sh.T @ cq[h, t], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(S[0, h], Sh, rtol=1e-11, atol=1e-12)
+    raw = np.concatenate([q, k, v], axis=-1)[0]
+    np.testing.assert_array_equal(hist[0], raw[:, N - (w - 1):])
+
+
+def pin_conv_delta_identity_split_and_decode(orc):
+    """The unit filter on the current token gives delta_prefill itself; with
+    a general filter, prefill in pieces (one shorter than the conv window)
+    carrying S and the conv cache, then decode steps, equals one prefill."""
+    rng = np.random.default_rng(46)
+    B, H, N, d, dv, w = 2, 1, 12, 3, 2, 4
+    q = rng.normal(size=(B, H, N, d))
+    k = rng.normal(size=(B, H, N, d))
+    v = rng.normal(size=(B, H, N, dv))
+    g = rng.uniform(size=(B, H, N))
+    al = rng.uniform(0.5, 1.0, size=(B, H, N))
+    ident = np.zeros((H, w, 2 * d + dv))
+    ident[:, w - 1] = 1.0
+    cache = rng.normal(size=(B, H, w - 1, 2 * d + dv))
+    o, S, _ = orc.delta_prefill_conv(q, k, v, g, ident, conv_cache=cache, alpha=al)
+    o0, S0 = orc.delta_prefill(q, k, v, g, alpha=al)
+    np.testing.assert_allclose(o, o0, rtol=1e-14)
+    np.testing.assert_allclose(S, S0, rtol=1e-14)
+    W = rng.normal(size=(H, w, 2 * d + dv)) * 0.5
+    o, S, C = orc.delta_prefill_conv(q, k, v, g, W, alpha=al)
+    parts, S1, C1 = [], None, None
+    for a, b in ((0, 5), (5, 7), (7, 10)):
+        oi, S1, C1 = orc.delta_prefill_conv(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b],
+                                            g[:, :, a:b], W, conv_cache=C1, S0=S1,
+                                            alpha=al[:, :, a:b])
+        parts.append(oi)
+    np.testing.assert_allclose(np.concatenate(parts, axis=2), o[:, :, :10], rtol=1e-12)
+    for t in (10, 11):
+        od, S1, C1 = orc.delta_decode_step_conv(q[:, :, t], k[:, :, t], v[:, :, t], g[:, :, t],
+                                                S1, W, C1, alpha=al[:, :, t])
+        np.testing.assert_allclose(od, o[:, :, t], rtol=1e-12)
+    np.testing.assert_allclose(S1, S, rtol=1e-12)
+    np.testing.assert_array_equal(C1, C)
+
+
 # --- backward of the LINEAR rule (derived; the pages give no formulas) ------
 
 def _torch_linear_loss(q, k, v, do, gamma, eps, S0, z0, dS, dz, elu):

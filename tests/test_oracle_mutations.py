@@ -285,6 +285,16 @@ for _n in ("_dbwd_dk_no_state_term", "_dbwd_adjoint_not_decayed", "_dbwd_adjoint
     globals()[_n].__name__ = _n
 
 
+_dconv_raw_values = _patched("o, S = delta_prefill(yq, yk, yv, g, S0=S0, alpha=alpha)",
+                             "o, S = delta_prefill(yq, yk, _f64(v), g, S0=S0, alpha=alpha)")
+_dconv_decode_raw_query = _patched("o, S_new = delta_decode_step(yq[:, :, 0],",
+                                   "o, S_new = delta_decode_step(_f64(q),")
+_dconv_decode_cache_kept = _patched("return o, S_new, np.concatenate([hq, hk, hv], axis=-1)",
+                                    "return o, S_new, _f64(conv_cache)")
+for _n in ("_dconv_raw_values", "_dconv_decode_raw_query", "_dconv_decode_cache_kept"):
+    globals()[_n].__name__ = _n
+
+
 MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _exp_everywhere, _decay_off_by_one, _outer_transposed,
            _quadratic_strict_mask, _delta_not_transposed, _delta_wrong_sign,
@@ -296,7 +306,8 @@ MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _bwd_dden_dropped, _bwd_dden_sign, _bwd_phi_grad_one, _bwd_adjoint_not_decayed,
            _bwd_dv_from_query, _bwd_dk_without_z, _dbwd_dk_no_state_term,
            _dbwd_adjoint_not_decayed, _dbwd_adjoint_no_projection, _dbwd_dv_without_gate,
-           _dbwd_dq_from_previous_state, _dbwd_residual_undecayed, _dbwd_dalpha_no_gate_term]
+           _dbwd_dq_from_previous_state, _dbwd_residual_undecayed, _dbwd_dalpha_no_gate_term,
+           _dconv_raw_values, _dconv_decode_raw_query, _dconv_decode_cache_kept]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
