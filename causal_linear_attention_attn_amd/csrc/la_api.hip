@@ -128,8 +128,8 @@ int check_prefill_shape(const la_prefill_args *a) {
   if ((size_t)a->N * dmax * esz > kMaxHeadBytes) return LA_EUNSUPPORTED;
   if (a->conv_weight) {
     if (a->conv_width < 1 || a->conv_width > kMaxConvWidth) return LA_EINVAL;
-    if (a->rule != LA_RULE_LINEAR) return LA_EUNSUPPORTED;
-    if (!la::linear_combo_supported(a->d, a->dv, a->dtype == LA_BF16, a->alpha != nullptr,
+    if (a->rule == LA_RULE_LINEAR &&
+        !la::linear_combo_supported(a->d, a->dv, a->dtype == LA_BF16, a->alpha != nullptr,
                                     true))
       return LA_EUNSUPPORTED;
   } else if (a->conv_width != 0 || a->conv_in || a->conv_out) {
@@ -141,6 +141,16 @@ int check_prefill_shape(const la_prefill_args *a) {
 // Bytes of one conv cache [B,H,w-1,2d+dv] (0 without a convolution).
 size_t conv_cache_bytes(size_t BH, int d, int dv, int width, bool bf16_io) {
   return width > 1 ? BH * (size_t)(width - 1) * (2 * (size_t)d + dv) * (bf16_io ? 2 : 4) : 0;
+}
+
+// The delta rule behind a convolution runs on convolved copies of q, k, v
+// at the start of the workspace (each region 256-byte aligned); the rule's
+// own workspace follows.
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+size_t delta_conv_bytes(const la_prefill_args *a) {
+  if (!a->conv_weight || a->rule != LA_RULE_DELTA) return 0;
+  const size_t esz = a->dtype == LA_BF16 ? 2 : 4, rows = (size_t)a->B * a->H * a->N;
+  return 2 * round256(rows * a->d * esz) + round256(rows * a->dv * esz);
 }
 
 bool overlap(const void *a, const void *b, size_t n) {
@@ -174,7 +184,7 @@ size_t la_prefill_workspace_size(const la_prefill_args *a) {
     return la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16,
                            a->conv_weight ? a->conv_width : 0, a->alpha != nullptr)
         .ws_bytes;
-  return la::delta_workspace_bytes(BH, a->N, a->d, a->dtype == LA_BF16);
+  return delta_conv_bytes(a) + la::delta_workspace_bytes(BH, a->N, a->d, a->dtype == LA_BF16);
 }
 
 int la_prefill(const la_prefill_args *a, void *stream) {
@@ -226,6 +236,7 @@ int la_prefill(const la_prefill_args *a, void *stream) {
     ws_need = la::delta_workspace_bytes(BH, a->N, a->d, bf16_io);
     // one head's T and R tiles must be addressable with 32-bit byte offsets
     if (ws_need / (size_t)BH > kMaxHeadBytes) return LA_EUNSUPPORTED;
+    ws_need += delta_conv_bytes(a);
   }
   if (ws_need > 0 && (!a->workspace || a->workspace_bytes < ws_need))
     return LA_EWORKSPACE;
@@ -256,7 +267,39 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   p.o = a->o;
   p.den_out = a->den_out;
   p.ws = reinterpret_cast<float *>(a->workspace);
-  if (!linear) return to_status(la::launch_delta_prefill(p, bf16_io, s));
+  if (!linear) {
+    if (cw > 0) {  // the rule runs on convolved copies of q, k, v
+      const size_t esz = bf16_io ? 2 : 4, rows = (size_t)BH * a->N;
+      char *base = static_cast<char *>(a->workspace);
+      la::ConvParams c{};
+      c.BH = BH;
+      c.H = a->H;
+      c.N = a->N;
+      c.d = a->d;
+      c.dv = a->dv;
+      c.width = cw;
+      c.w = a->conv_weight;
+      c.q = a->q;
+      c.k = a->k;
+      c.v = a->v;
+      c.cache_in = a->conv_in;
+      c.cache_out = a->conv_out;
+      c.yq = base;
+      c.yk = base + round256(rows * a->d * esz);
+      c.yv = base + 2 * round256(rows * a->d * esz);
+      const bool vec16 = (a->d * esz) % 16 == 0 && (a->dv * esz) % 16 == 0 &&
+                         aligned16(a->q) && aligned16(a->k) && aligned16(a->v) &&
+                         (!a->conv_in || aligned16(a->conv_in));
+      hipError_t e = la::launch_conv_qkv(c, bf16_io, vec16, s);
+      if (e != hipSuccess) return LA_EHIP;
+      p.q = c.yq;
+      p.k = c.yk;
+      p.v = c.yv;
+      p.vec_ok = (a->d % vec == 0) && (a->dv % vec == 0) && aligned16(a->o);
+      p.ws = reinterpret_cast<float *>(base + delta_conv_bytes(a));
+    }
+    return to_status(la::launch_delta_prefill(p, bf16_io, s));
+  }
   p.nseg = plan.nseg;
   p.seg_len = plan.seg_len;
   p.nsplit = plan.nsplit;
@@ -511,7 +554,6 @@ int la_decode_step(const la_decode_args *a, void *stream) {
   }
   if (a->conv_weight) {
     if (a->conv_width < 1 || a->conv_width > kMaxConvWidth) return LA_EINVAL;
-    if (delta) return LA_EUNSUPPORTED;
     if (BH > 0 && a->conv_width > 1 && !a->conv_cache) return LA_EINVAL;
   } else if (a->conv_width != 0 || a->conv_cache) {
     return LA_EINVAL;

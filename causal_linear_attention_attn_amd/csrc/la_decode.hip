@@ -12,7 +12,7 @@
 //     b = S^T k,  u = v - alpha b,  S <- alpha S + g k u^T,
 //     o = S_new^T q = alpha S_old^T q + g (k . q) u
 //
-// With a short causal convolution ("What Is Linear Attention?" 5.4; LINEAR
+// With a short causal convolution ("What Is Linear Attention?" 5.4; either
 // rule, the CV instantiations) q, k and v are first convolved with the w-1
 // raw tokens of the conv cache, which then shifts by one token: thread t
 // owns channel t of q, k and v in every cache row, so the in-place update
@@ -261,11 +261,9 @@ __global__ void copy_kernel(float *dst, const float *src, size_t n) {
 
 template <typename T, int VEC, bool DELTA>
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t s) {
-  if constexpr (!DELTA) {
-    if (p.conv_w)
-      return launch_kernel("linear_decode", decode_kernel<T, VEC, false, true>, dim3(p.BH),
-                           dim3(kDecThreads), s, p);
-  }
+  if (p.conv_w)
+    return launch_kernel(DELTA ? "delta_decode" : "linear_decode",
+                         decode_kernel<T, VEC, DELTA, true>, dim3(p.BH), dim3(kDecThreads), s, p);
   return launch_kernel(DELTA ? "delta_decode" : "linear_decode",
                        decode_kernel<T, VEC, DELTA, false>, dim3(p.BH), dim3(kDecThreads), s, p);
 }

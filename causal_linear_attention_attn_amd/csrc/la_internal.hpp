@@ -52,6 +52,20 @@ struct PrefillParams {
   float *den_out;        // [BH, N] per-token denominators, or nullptr
 };
 
+// Short causal convolution of q, k, v into workspace copies (ahead of the
+// delta rule's prefill), and the conv cache after the sequence.
+struct ConvParams {
+  int BH, H, N, d, dv, width;
+  const float *w;         // [H, width, 2d+dv] filters
+  const void *q, *k, *v;  // [BH, N, d], [BH, N, d], [BH, N, dv]
+  const void *cache_in;   // [BH, width-1, 2d+dv] or nullptr (zeros)
+  void *yq, *yk, *yv;     // convolved copies, layouts as q, k, v
+  void *cache_out;        // [BH, width-1, 2d+dv] or nullptr (not written)
+};
+// vec: d and dv multiples of 16 bytes of elements and every buffer 16-byte
+// aligned
+hipError_t launch_conv_qkv(const ConvParams &p, bool bf16_io, bool vec, hipStream_t s);
+
 // Backward of the LINEAR rule's prefill.
 struct BwdParams {
   int BH, H, N, d, dv;

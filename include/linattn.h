@@ -80,15 +80,18 @@ typedef enum { LA_FMAP_IDENTITY = 0, LA_FMAP_ELU1 = 1 } la_fmap;
  *   error is taken on the decayed state):
  *     S_t = alpha_t S_{t-1} + g_t k_t (v_t - alpha_t S_{t-1}^T k_t)^T
  *
- * Short causal convolution (LINEAR rule only; [WILA] section 5.4: a short
+ * Short causal convolution (either rule; [WILA] section 5.4: a short
  * convolution over the most recent tokens in front of the state, with a
  * conv cache of those tokens kept beside the state for decoding): with
  * filters W [H, w, 2d+dv] (fp32, channels [q | k | v]) each raw q, k and v
- * channel is replaced, before the feature map, by
+ * channel is replaced, before the feature map (LINEAR) or the delta rule, by
  *     x'_t[c] = sum_{j=0..w-1} W[h, j, c] * x_{t-(w-1)+j}[c]
- * (tap w-1 on the current token; depthwise, no bias, no activation).  The
+ * (tap w-1 on the current token; depthwise, no bias, no activation, and for
+ * DELTA no normalisation of the convolved keys: the pages give none).  The
  * conv cache [B, H, w-1, 2d+dv] (dtype of q, rows oldest first) holds the
- * raw tokens before the current one: [q | k | v] of each token. */
+ * raw tokens before the current one: [q | k | v] of each token.  The DELTA
+ * prefill convolves into copies of q, k, v in the workspace (rounded to
+ * the dtype of q) and runs the rule on them. */
 typedef enum { LA_RULE_LINEAR = 0, LA_RULE_DELTA = 1 } la_rule;
 
 /* One call processes B*H independent sequences of N tokens. */
@@ -117,10 +120,9 @@ typedef struct la_prefill_args {
                         Values are the caller's contract (not read on the
                         host); values outside the range make the chunk's
                         decay products inaccurate or undefined. */
-  const float *conv_weight; /* LINEAR: [H, w, 2d+dv] short-convolution
-                        filters (see above), or NULL (no convolution; then
-                        conv_width is 0 and conv_in, conv_out are NULL).
-                        DELTA: must be NULL (LA_EUNSUPPORTED). */
+  const float *conv_weight; /* [H, w, 2d+dv] short-convolution filters
+                        (see above), or NULL (no convolution; then
+                        conv_width is 0 and conv_in, conv_out are NULL). */
   int32_t conv_width;/* w, 1..4 with conv_weight */
   const void *conv_in;/* [B,H,w-1,2d+dv] conv cache before the sequence,
                         dtype as q; NULL = zeros */
@@ -298,8 +300,8 @@ typedef struct la_decode_args {
   const float *g;    /* DELTA: [B,H] write gate (required). LINEAR: NULL. */
   const float *alpha;/* State decay, or NULL (= 1).  DELTA: [B,H].
                         LINEAR: [B,H,d] per key channel (not with gamma). */
-  const float *conv_weight; /* LINEAR: [H, w, 2d+dv] short-convolution
-                        filters, or NULL.  DELTA: must be NULL. */
+  const float *conv_weight; /* [H, w, 2d+dv] short-convolution filters,
+                        or NULL (either rule). */
   int32_t conv_width;/* w, 1..4 with conv_weight; 0 without */
   void *conv_cache;  /* [B,H,w-1,2d+dv] conv cache, dtype as q, read and
                         shifted in place by one token (required for w > 1) */

@@ -130,10 +130,6 @@ def test_prefill_null_args_and_unsupported_grid(lib):
               g=ctypes.c_void_p(0x2000))
     assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
     fake = ctypes.c_void_p(0x2000)
-    # the short convolution is built for the LINEAR rule only
-    a = _args(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY, g=fake,
-              conv_weight=fake, conv_width=4)
-    assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
     # fp32, d = dv = 128: convolution and per-channel decay exceed the LDS together
     a = _args(dtype=_lib.LA_F32, d=128, dv=128, alpha=fake, conv_weight=fake, conv_width=4)
     assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
@@ -185,14 +181,30 @@ def test_decode_rejects_invalid_arguments(lib, bad):
     assert lib.la_decode_step(ctypes.byref(a), None) == _lib.LA_EINVAL
 
 
-def test_decode_conv_on_delta_is_unsupported(lib):
+def test_decode_conv_on_delta_needs_its_cache(lib):
     a = _lib.DecodeArgs()
     a.B, a.H, a.d, a.dv = 2, 2, 8, 8
     a.dtype, a.rule, a.fmap = _lib.LA_BF16, _lib.LA_RULE_DELTA, _lib.LA_FMAP_IDENTITY
     fake = ctypes.c_void_p(0x1000)
     a.q = a.k = a.v = a.o = a.S = a.g = fake
-    a.conv_weight, a.conv_width, a.conv_cache = fake, 4, fake
-    assert lib.la_decode_step(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+    a.conv_weight, a.conv_width = fake, 4  # width 4 without a conv cache
+    assert lib.la_decode_step(ctypes.byref(a), None) == _lib.LA_EINVAL
+
+
+@pytest.mark.parametrize("dtype,esz", [(_lib.LA_BF16, 2), (_lib.LA_F32, 4)])
+def test_delta_conv_workspace_holds_the_convolved_inputs(lib, dtype, esz):
+    """Behind a convolution the delta rule runs on convolved copies of q, k
+    and v at the start of the workspace, each region rounded up to 256
+    bytes; the rule's own workspace follows."""
+    fake = ctypes.c_void_p(0x2000)
+    kw = dict(B=2, H=3, N=37, d=24, dv=40, dtype=dtype, rule=_lib.LA_RULE_DELTA,
+              fmap=_lib.LA_FMAP_IDENTITY, g=fake)
+    plain = lib.la_prefill_workspace_size(ctypes.byref(_args(**kw)))
+    conv = lib.la_prefill_workspace_size(ctypes.byref(_args(conv_weight=fake, conv_width=3,
+                                                            **kw)))
+    r256 = lambda n: (n + 255) // 256 * 256
+    rows = 2 * 3 * 37
+    assert conv - plain == 2 * r256(rows * 24 * esz) + r256(rows * 40 * esz)
 
 
 def _bargs(**kw):
