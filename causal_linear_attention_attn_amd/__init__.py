@@ -116,7 +116,7 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
 
     rule "linear": fmap defaults to "elu1"; gamma [H] fp32 or None; eps >= 0;
                    or, instead of gamma, alpha [B,H,N,d] fp32: a decay per key
-                   channel and token in [0.1, 1].  Optionally a short causal
+                   channel and token in (0, 1] (taken as 2^-15 below it).  Optionally a short causal
                    convolution of q, k, v: conv_weight [H, w, 2d+dv] fp32
                    (w <= 4) and conv_cache [B,H,w-1,2d+dv] (dtype of q), read
                    as the tokens before the sequence and overwritten in place

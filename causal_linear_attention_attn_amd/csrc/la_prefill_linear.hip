@@ -54,21 +54,34 @@
 //
 // Per-key-channel decay (GLA, "Efficient attention variants" 7.2; the CH
 // instantiations): S_t = diag(alpha_t) S_{t-1} + phi(k_t) v_t^T, z alike.
-// With lb_j = sum_{t<=j} log alpha_t (chunk-local, per channel) and a
-// reference token m in the middle of the chunk, the score of query j and key
-// i <= j is sum_f phi(q_j)_f phi(k_i)_f exp(lb_j - lb_i)_f = q^_j . k^_i with
-//     q^_j = phi(q_j) (.) exp(lb_j - lb_m),   k^_i = phi(k_i) (.) exp(lb_m - lb_i)
-// (every factor within alpha^(-C/2) of 1, so alpha >= 0.1 keeps them inside
-// the fp32/bf16 range), the state read is q^_j . (diag(exp(lb_m)) S-), and
-//     S+ = diag(exp(lb_L - lb_m)) (diag(exp(lb_m)) S- + K^^T V)   (z alike).
-// The prefix sums are taken per chunk in LDS (one thread per channel); a
-// segment summary also carries the segment's total log decay per channel,
-// which the scan applies row by row.
+// With lb_j = sum_{t<=j} log2 alpha_t (chunk-local, per channel), the score
+// of query j and key i <= j is sum_f phi(q_j)_f phi(k_i)_f 2^(lb_j - lb_i)_f.
+// Each 16-token block b of the chunk has references R_b = lb before it (0
+// for the first), M_b = lb at its eighth token and E_b = lb at its last, and
+// the tiles hold
+//     q^_j = phi(q_j) (.) 2^(lb_j - M_b(j)),   k^_i = phi(k_i) (.) 2^(M_b(i) - lb_i),
+// every factor within alpha^(-8).  A diagonal score tile is q^ . k^ as it
+// stands.  Elsewhere every product is taken as a chain of factors that each
+// stay in range, so that a factor can underflow only where the weight it
+// belongs to is negligible: the query side of a tile of query block r
+// against key block b < r is (q^ (.) 2^(M_r - R_r)) (.) 2^(R_r - E_b) (the
+// second factor only for b < r-1: R_r = E_(r-1)), the key side k^ (.)
+// 2^(E_b - M_b); the state read takes (q^ (.) 2^(M_r - R_r)) (.) 2^R_r against
+// the plain state copy; and the state update is S+ = diag(2^lb_L) S- +
+// sum_i ((k^_i (.) 2^(E_b - M_b)) (.) 2^(lb_L - E_b)) v_i^T (z alike).  The
+// range argument needs alpha^(-8) finite: log2 alpha is clamped at -15
+// (alpha at least 2^-15; below it an earlier token already weighs under
+// 2^-15 of the current one).  The prefix sums are taken per chunk in fp64
+// (one thread per channel) and stored relative to each row's reference, so
+// the exponents keep fp32 accuracy however long the decay has run; a
+// segment summary weights its keys by 2^(lb_L - lb_i) (reference L for every
+// row) and also carries the segment's total log2 decay per channel, which
+// the scan applies row by row.
 //
 // Data layout: q, k [BH, N, d], v, o [BH, N, dv] (row-major, dtype T);
 // alpha [BH, N, d] fp32 (CH); workspace slots [nseg][BH][d*dv + 2d] fp32
 // (state transposed, element (f, n) at n d + f; normaliser; then the
-// segment's log decay per channel for CH).
+// segment's log2 decay per channel for CH).
 // Global traffic goes through buffer resources (bounds by offset, no
 // branches between a load and its use), issued one chunk ahead.
 #include <atomic>
@@ -85,7 +98,7 @@ constexpr size_t kStreamBytes = (size_t)256 << 20;  // last-level (MALL) cache s
 constexpr int kMaxSeg = 32;  // most segments per sequence
 
 // fp32 elements of one workspace slot record: S (d x dv), z (d), and the
-// segment's log decay per channel (d; used with a per-channel decay).
+// segment's log2 decay per channel (d; used with a per-channel decay).
 __host__ __device__ inline size_t ws_rec(int d, int dv) {
   return (size_t)d * dv + 2 * (size_t)d;
 }
@@ -117,7 +130,7 @@ struct Cfg {
   static constexpr int VCB = DV / VEC;  // ... per v/o row
   static constexpr int RQ = C * DK / (VEC * NT);  // q/k rows per thread
   static constexpr int RV = C * DV / (VEC * NT);  // v/o rows per thread
-  static constexpr int SROWS = DV + 16;           // rows of the S'^T copy
+  static constexpr int SROWS = DV + 1;  // rows of the S'^T copy (z once: row DV)
   // resident waves per SIMD the register allocation must allow
   static constexpr int WPE = sizeof(T) == 4 ? 1 : (NW <= 4 ? 3 : 2);
   // chunks whose k, v rows summary_kernel keeps in flight: eight-wave bf16
@@ -167,11 +180,26 @@ struct ChanRegs {
 template <class CF>
 struct alignas(16) SmemChan {
   static constexpr int LDL = CF::DK + 4;  // row stride of lb
-  float lb[CF::C * LDL];  // lb[j][f] = sum_{t<=j} log alpha_t,f within the chunk
-  float bm[CF::DK];       // exp(lb[m][f]) for the reference token m
-  float bl[CF::DK];       // exp(lb[L-1][f] - lb[m][f])
-  float tot[CF::DK];      // segment summaries: log decay of the segment so far
+  static constexpr int NRB = CF::NRB;
+  static constexpr int NP = (NRB - 1) * (NRB - 2) / 2;  // block pairs b <= r - 2
+  // log2 alpha as loaded, then each row's exponent lb_j - ref_j (ref_j =
+  // M_b(j) in the chunk kernel, lb_L in the segment summaries)
+  float lb[CF::C * LDL];
+  float th[NRB][CF::DK], tl[NRB][CF::DK];  // block sums of log2 alpha (fp64 as hi + lo)
+  float el[CF::DK];  // 2^lb_L: the chunk's decay of the state
+  union {
+    struct {  // chunk kernel (the factors of 1 are not stored)
+      float qa[NRB][CF::DK];               // 2^(M_r - R_r)
+      float cp[NP > 0 ? NP : 1][CF::DK];   // 2^(R_r - E_b), b <= r-2: (r-2)(r-1)/2 + b
+      float kb[NRB][CF::DK];               // 2^(E_b - M_b)
+      float kf[NRB > 1 ? NRB - 1 : 1][CF::DK];  // 2^(lb_L - E_b), b < NRB-1
+      float sf[NRB > 1 ? NRB - 1 : 1][CF::DK];  // 2^R_r, r >= 1: row r - 1
+    };
+    float tot[CF::DK];  // segment summaries: log2 decay of the segment so far
+  };
 };
+// log2 alpha below this is clamped (alpha >= 2^-15; see the file header)
+constexpr float kLog2AlphaMin = -15.f;
 struct NoChan {};
 template <class CF>
 __device__ __forceinline__ const SmemChan<CF> *chan_ptr(const SmemChan<CF> &s) {
@@ -260,8 +288,8 @@ __device__ __forceinline__ void chan_prefetch(ChanRegs<CF> &A, __amdgpu_buffer_r
   }
 }
 
-// log alpha of this thread's elements into lb (0 for rows past the chunk and
-// columns past d, i.e. a factor of 1).
+// log2 alpha of this thread's elements into lb (0 for rows past the chunk
+// and columns past d, i.e. a factor of 1).
 template <class CF>
 __device__ __forceinline__ void chan_logs(const ChanRegs<CF> &A, SmemChan<CF> &sc, int d,
                                           int Lc) {
@@ -275,34 +303,91 @@ __device__ __forceinline__ void chan_logs(const ChanRegs<CF> &A, SmemChan<CF> &s
       f32x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        x[e] = row < Lc && col + e < d ? __logf(A.a[r][h][e]) : 0.f;
+        x[e] = row < Lc && col + e < d ? fmaxf(__log2f(A.a[r][h][e]), kLog2AlphaMin) : 0.f;
       *reinterpret_cast<f32x4 *>(sc.lb + row * SmemChan<CF>::LDL + col) = x;
     }
   }
 }
 
-// Prefix sums of lb down each column (one thread per channel), the state
-// factors bm and bl, and (segment summaries) the running total.
+// Prefix sums of log2 alpha down each column in fp64, one thread per
+// (channel, 16-row block): the block's own sums first, then, with every
+// block's total at hand, each row's exponent relative to its reference
+// written back in place, the state decay el and the factor tables of the
+// chunk kernel, or (segment summaries, total) the running log2 decay of the
+// segment.  Rows past Lc add factors of 1.  Two barriers: one inside, one
+// for the caller after it.
 template <class CF>
-__device__ __forceinline__ int chan_ref(int Lc) {
-  return min(CF::C / 2, Lc) - 1;
-}
-template <class CF>
-__device__ __forceinline__ void chan_prefix(SmemChan<CF> &sc, int Lc, bool total) {
-  constexpr int LDL = SmemChan<CF>::LDL;
-  const int t = threadIdx.x;
-  if (t < CF::DK) {
-    float x = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < CF::C; ++j) {
-      x += sc.lb[j * LDL + t];
-      sc.lb[j * LDL + t] = x;
+__device__ __forceinline__ void chan_prefix(SmemChan<CF> &sc, bool total) {
+  constexpr int LDL = SmemChan<CF>::LDL, NRB = CF::NRB;
+  static_assert(NRB * CF::DK <= CF::NT, "one thread per channel and block");
+  const int t = threadIdx.x, f = t % CF::DK, b = t / CF::DK;
+  const bool act = b < NRB;
+  double loc7 = 0.0;
+  if (act) {
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      acc += (double)sc.lb[(16 * b + j) * LDL + f];
+      if (j == 7) loc7 = acc;
     }
-    const float lm = sc.lb[chan_ref<CF>(Lc) * LDL + t];
-    sc.bm[t] = __expf(lm);
-    sc.bl[t] = __expf(x - lm);  // x = lb[C-1] = lb[Lc-1] (factors of 1 past Lc)
-    if (total) sc.tot[t] += x;
+    const float hi = (float)acc;
+    sc.th[b][f] = hi;
+    sc.tl[b][f] = (float)(acc - (double)hi);
   }
+  __syncthreads();
+  if (act) {
+    double off = 0.0, x = 0.0, offs[NRB];
+#pragma unroll
+    for (int c = 0; c < NRB; ++c) {
+      const double T = (double)sc.th[c][f] + (double)sc.tl[c][f];
+      offs[c] = x;  // R_c: the sum of the blocks before c
+      x += T;
+      if (c < b) off += T;
+    }
+    // exponent of row j: lb_j - M_b = (own sums to j) - loc7 in the chunk
+    // kernel; lb_j - lb_L = off + (own sums to j) - x in the summaries
+    const double ref = total ? x - off : loc7;
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float *cell = sc.lb + (16 * b + j) * LDL + f;
+      acc += (double)*cell;
+      *cell = (float)(acc - ref);
+    }
+    if (b == 0) {
+      sc.el[f] = exp2f((float)x);  // x = lb[C-1] = lb[Lc-1]
+      if (total) sc.tot[f] += (float)x;
+    }
+    if (!total) {
+      const double E = off + (double)sc.th[b][f] + (double)sc.tl[b][f];
+      sc.qa[b][f] = exp2f((float)loc7);              // M_b - R_b
+      sc.kb[b][f] = exp2f((float)(E - off - loc7));  // E_b - M_b
+      if (b + 1 < NRB) sc.kf[b][f] = exp2f((float)(x - E));
+      if (b >= 1) sc.sf[b - 1][f] = exp2f((float)off);
+#pragma unroll
+      for (int c = 0; c + 2 <= NRB - 1; ++c) {  // pairs (b, c), c <= b - 2: R_b - E_c
+        if (c + 2 <= b) {
+          const double Ec = offs[c] + (double)sc.th[c][f] + (double)sc.tl[c][f];
+          sc.cp[(b - 2) * (b - 1) / 2 + c][f] = exp2f((float)(off - Ec));
+        }
+      }
+    }
+  }
+}
+
+// A fragment's eight values times eight per-channel factors (fp32 product,
+// rounded back to the fragment's type).
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_scaled(const Frag<T> &f, const float *fac) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(fac);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(fac + 4);
+  Frag<T> o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o.v[e] = from_f32<T>(to_f32(f.v[e]) * a[e]);
+    o.v[4 + e] = from_f32<T>(to_f32(f.v[4 + e]) * b[e]);
+  }
+  return o;
 }
 
 // ---- short causal convolution of q, k, v (the CV instantiations) ----------
@@ -575,9 +660,10 @@ __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R,
   const bool colmask = p.d < CF::DK;  // feature columns past d
   const int qcb = threadIdx.x % CF::QCB, qrg = threadIdx.x / CF::QCB;
   const int col0 = qcb * VEC;
-  // per-channel decay: q^ = phi(q) exp(lb_row - lb_m), k^ = phi(k) exp(lb_m - lb_row)
+  // per-channel decay: q^ = phi(q) 2^D, k^ = phi(k) 2^-D with D = lb_row -
+  // ref_row as chan_prefix leaves it (ref: the row's block reference in the
+  // chunk kernel, lb_L in the segment summaries)
   constexpr int LDL = SmemChan<CF>::LDL;
-  const float *lbm = CH ? sc->lb + chan_ref<CF>(Lc) * LDL + col0 : nullptr;
 #pragma unroll
   for (int r = 0; r < CF::RQ; ++r) {
     const int row = qrg * CF::RQ + r;
@@ -590,7 +676,7 @@ __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R,
         if constexpr (CV) xq = Y->q[r][e];
         else xq = to_f32(R.q[r][e]);
         x[e] = ELU ? phi_elu1(xq) : xq;
-        if constexpr (CH) x[e] *= __expf(lbr[e] - lbm[e]);
+        if constexpr (CH) x[e] *= exp2f(lbr[e]);
       }
       if constexpr (CV) P->q[r] = pack_vec<CF>(x);
       else lds_store_n<T, VEC>(Qs + row * CF::QLD + col0, x);
@@ -601,7 +687,7 @@ __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R,
       if constexpr (CV) xk = Y->k[r][e];
       else xk = to_f32(R.k[r][e]);
       x[e] = ELU ? phi_elu1(xk) : xk;
-      if constexpr (CH) x[e] *= __expf(lbm[e] - lbr[e]);
+      if constexpr (CH) x[e] *= exp2f(-lbr[e]);
     }
     // key weights: 0 past the chunk; gamma^(Lc-1-j) where the decay is
     // folded into the keys (KW)
@@ -718,6 +804,51 @@ __device__ __forceinline__ void state_update(f32x4 (&Sacc)[CF::FPW][CF::TPW],
   }
 }
 
+// The state update with a per-channel decay (chunk kernel): each key
+// fragment row (channel f) takes 2^(E_b - M_b), then 2^(lb_L - E_b), of its
+// token block b; a fragment's slots 0..3 hold tokens of block 2 ks, slots
+// 4..7 of 2 ks + 1.
+template <class CF>
+__device__ __forceinline__ void state_update_chan(f32x4 (&Sacc)[CF::FPW][CF::TPW],
+                                                  const typename CF::type *Ks,
+                                                  const typename CF::type *Vs,
+                                                  const SmemChan<CF> &sc, int wv, int li,
+                                                  int lg) {
+  using T = typename CF::type;
+  Frag<T> ones;
+  frag_fill(ones, 1.f);
+#pragma unroll
+  for (int ks = 0; ks < CF::KSC; ++ks) {
+    const int t0 = 32 * ks + 4 * lg;
+#pragma unroll
+    for (int a = 0; a < CF::FPW; ++a) {
+      const int f = 16 * srow<CF>(wv, a) + li;
+      Frag<T> kf;
+      lds_frag_tr(kf, Ks, CF::QLD, t0, t0 + 16, 16 * srow<CF>(wv, a), li);
+      const int b0 = 2 * ks, b1 = 2 * ks + 1;
+      const float a0 = sc.kb[b0][f], a1 = sc.kb[b1][f];
+      const float c0 = b0 + 1 < CF::NRB ? sc.kf[b0][f] : 1.f;
+      const float c1 = b1 + 1 < CF::NRB ? sc.kf[b1 < CF::NRB - 1 ? b1 : 0][f] : 1.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf.v[e] = from_f32<T>((to_f32(kf.v[e]) * a0) * c0);
+        kf.v[4 + e] = from_f32<T>((to_f32(kf.v[4 + e]) * a1) * c1);
+      }
+#pragma unroll
+      for (int b = 0; b < CF::TPW; ++b) {
+        const int tn = scol<CF>(wv, b);
+        if (tn < CF::NVT) {
+          Frag<T> vf;
+          lds_frag_tr(vf, Vs, CF::VTLD, t0, t0 + 16, 16 * tn, li);
+          mma(Sacc[a][b], kf, vf);
+        } else if (tn == CF::NVT) {
+          mma(Sacc[a][b], kf, ones);
+        }
+      }
+    }
+  }
+}
+
 // gamma^-1, gamma^-2, gamma^-3 from the clamped log2 gamma (finite).
 struct InvPow {
   float c1, c2, c3;
@@ -804,9 +935,10 @@ __device__ __forceinline__ void rescale_and_copy_state(typename CF::type *St,
 #pragma unroll
     for (int b = 0; b < CF::TPW; ++b) {
       const int tn = scol<CF>(wv, b);
-      if (tn < CF::NCT)
-        lds_store4(St + (16 * tn + li) * CF::QLD + 16 * tf + 4 * lg, Sacc[a][b][0],
-                   Sacc[a][b][1], Sacc[a][b][2], Sacc[a][b][3]);
+      // (the normaliser tile holds z in all 16 columns: one row of it)
+      if (tn < CF::NVT || (tn == CF::NVT && li == 0))
+        lds_store4(St + (tn < CF::NVT ? 16 * tn + li : CF::DV) * CF::QLD + 16 * tf + 4 * lg,
+                   Sacc[a][b][0], Sacc[a][b][1], Sacc[a][b][2], Sacc[a][b][3]);
     }
   }
 }
@@ -949,10 +1081,11 @@ enum DecayMode : int { kDecNone = 0, kDecKeys = 1, kDecElem = 2 };
 // tile Os.  MODE kDecElem: the scores take gamma^(i-j) and the state read
 // gamma^(i+1) (lg2 = log2 gamma); kDecKeys: numerator and denominator carry
 // gamma^(L-1-i), so eps does too.
-template <class CF, int RB, bool DN, int MODE>
-__device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillParams &p, int Lc,
-                                              int cg, int li, int lg, float *den_row,
-                                              float lg2) {
+// CH: per-channel decay, factors from the tables of sc (see the file header).
+template <class CF, int RB, bool DN, int MODE, bool CH>
+__device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const SmemChan<CF> *sc,
+                                              const PrefillParams &p, int Lc, int cg, int li,
+                                              int lg, float *den_row, float lg2) {
   using T = typename CF::type;
   const int irow = 16 * RB + li;  // this lane's query row
   // ---- scores, transposed: at[tj][r] = phi(q_i) . phi(k_j), i = irow,
@@ -961,6 +1094,13 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillPa
 #pragma unroll
   for (int ks = 0; ks < CF::KSD; ++ks)
     lds_frag(qf[ks], sm.Qs + irow * CF::QLD + 32 * ks + 8 * lg);
+  // per-channel decay: the queries against the block boundary, q^ 2^(M_RB - R_RB)
+  [[maybe_unused]] Frag<T> qt[CH ? CF::KSD : 1];
+  if constexpr (CH) {
+#pragma unroll
+    for (int ks = 0; ks < CF::KSD; ++ks)
+      qt[ks] = frag_scaled(qf[ks], sc->qa[RB] + 32 * ks + 8 * lg);
+  }
   f32x4 at[CF::NRB];
 #pragma unroll
   for (int tj = 0; tj < CF::NRB; ++tj) {
@@ -970,7 +1110,16 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillPa
       for (int ks = 0; ks < CF::KSD; ++ks) {
         Frag<T> kf;
         lds_frag(kf, sm.Ks + (16 * tj + li) * CF::QLD + 32 * ks + 8 * lg);
-        mma(at[tj], kf, qf[ks]);
+        if (CH && tj < RB) {  // key block tj before the query block (see the header)
+          const int c0 = 32 * ks + 8 * lg;
+          kf = frag_scaled(kf, sc->kb[tj] + c0);
+          if (tj + 1 < RB)
+            mma(at[tj], kf, frag_scaled(qt[ks], sc->cp[(RB - 2) * (RB - 1) / 2 + tj] + c0));
+          else
+            mma(at[tj], kf, qt[ks]);
+        } else {
+          mma(at[tj], kf, qf[ks]);
+        }
       }
     }
   }
@@ -997,15 +1146,19 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const PrefillPa
   for (int a = 0; a < CF::NPW; ++a) acc[a] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < CF::KSD; ++ks) {
+    // (per-channel decay: the state read takes (q^ 2^(M_RB - R_RB)) 2^R_RB)
+    Frag<T> qs = qf[ks];
+    if constexpr (CH) qs = RB ? frag_scaled(qt[ks], sc->sf[RB ? RB - 1 : 0] + 32 * ks + 8 * lg)
+                              : qt[ks];
 #pragma unroll
     for (int a = 0; a < CF::NPW; ++a) {
       Frag<T> sf;
       lds_frag(sf, sm.St + (16 * (cg * CF::NPW + a) + li) * CF::QLD + 32 * ks + 8 * lg);
-      mma(acc[a], sf, qf[ks]);
+      mma(acc[a], sf, qs);
     }
     Frag<T> zf;
-    lds_frag(zf, sm.St + (CF::DV + li) * CF::QLD + 32 * ks + 8 * lg);
-    mma(accd, zf, qf[ks]);
+    lds_frag(zf, sm.St + CF::DV * CF::QLD + 32 * ks + 8 * lg);  // z, every lane
+    mma(accd, zf, qs);
   }
   if constexpr (MODE == kDecElem) {
     const float gq = exp2f((float)(irow + 1) * lg2);
@@ -1079,13 +1232,12 @@ __device__ __forceinline__ void chunk_loop(SmemChunk<CF> &sm, ChanSmem<CF, CH> &
     if constexpr (CH) {  // the chunk's per-channel decay prefix sums
       chan_logs<CF>(A, sc, d, Lc);
       __syncthreads();
-      chan_prefix<CF>(sc, Lc, false);
+      chan_prefix<CF>(sc, false);
       __syncthreads();
     }
     commit<CF, true, CH, CV, KEYS>(R, sm.Qs, sm.Ks, sm.Vs, sm.pw, p, Lc, chan_ptr<CF>(sc),
                                    conv_ptr<CF>(cs));
-    if constexpr (CH) {  // state read from diag(exp(lb_m)) S-
-      chan_scale<CF>(Sacc, sc.bm, wv, lg);
+    if constexpr (CH) {  // the state copy as it stands (factors on the queries)
       rescale_and_copy_state<CF>(sm.St, Sacc, 1.f, false, wv, li, lg);
       if (c0 + CF::C < t_end)
         chan_prefetch<CF, VK>(A, ra, p, c0 + CF::C, min(CF::C, N - c0 - CF::C));
@@ -1096,15 +1248,15 @@ __device__ __forceinline__ void chunk_loop(SmemChunk<CF> &sm, ChanSmem<CF, CH> &
 
     float *dno = DN ? p.den_out + (size_t)bh * N + c0 : nullptr;
     if constexpr (CF::NRB == 2) {
-      if (rb == 0) chunk_outputs<CF, 0, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2);
-      else chunk_outputs<CF, 1, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2);
+      if (rb == 0) chunk_outputs<CF, 0, DN, MODE, CH>(sm, chan_ptr<CF>(sc), p, Lc, cg, li, lg, dno, lg2);
+      else chunk_outputs<CF, 1, DN, MODE, CH>(sm, chan_ptr<CF>(sc), p, Lc, cg, li, lg, dno, lg2);
     } else {
       static_assert(CF::NRB == 4, "row blocks per chunk");
       switch (rb) {
-        case 0: chunk_outputs<CF, 0, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2); break;
-        case 1: chunk_outputs<CF, 1, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2); break;
-        case 2: chunk_outputs<CF, 2, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2); break;
-        default: chunk_outputs<CF, 3, DN, MODE>(sm, p, Lc, cg, li, lg, dno, lg2); break;
+        case 0: chunk_outputs<CF, 0, DN, MODE, CH>(sm, chan_ptr<CF>(sc), p, Lc, cg, li, lg, dno, lg2); break;
+        case 1: chunk_outputs<CF, 1, DN, MODE, CH>(sm, chan_ptr<CF>(sc), p, Lc, cg, li, lg, dno, lg2); break;
+        case 2: chunk_outputs<CF, 2, DN, MODE, CH>(sm, chan_ptr<CF>(sc), p, Lc, cg, li, lg, dno, lg2); break;
+        default: chunk_outputs<CF, 3, DN, MODE, CH>(sm, chan_ptr<CF>(sc), p, Lc, cg, li, lg, dno, lg2); break;
       }
     }
 
@@ -1112,11 +1264,14 @@ __device__ __forceinline__ void chunk_loop(SmemChunk<CF> &sm, ChanSmem<CF, CH> &
     // (the accumulator already carries gamma^Lc with the decay folded into
     // the keys, or diag(exp(lb_m)) with a per-channel decay: scaled before
     // the copy)
-    if constexpr (MODE == kDecElem)
+    if constexpr (CH) {  // S+ = diag(2^lb_L) S- + sum_i (keys to the chunk end) v_i^T
+      chan_scale<CF>(Sacc, sc.el, wv, lg);
+      state_update_chan<CF>(Sacc, sm.Ks, sm.Vs, sc, wv, li, lg);
+    } else if constexpr (MODE == kDecElem) {
       state_update_decay<CF>(Sacc, sm.Ks, sm.Vs, Lc, lg2, wv, li, lg);
-    else
+    } else {
       state_update<CF>(Sacc, sm.Ks, sm.Vs, 1.f, false, wv, li, lg);
-    if constexpr (CH) chan_scale<CF>(Sacc, sc.bl, wv, lg);
+    }
     __syncthreads();
     if constexpr (!CH) {
       if (c0 + CF::C < t_end)
@@ -1289,20 +1444,19 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
       if constexpr (CH) {
         chan_logs<CF>(A, sc, d, CF::C);
         __syncthreads();
-        chan_prefix<CF>(sc, CF::C, true);
+        chan_prefix<CF>(sc, true);
         __syncthreads();
       }
       commit<CF, false, CH, CV, true>(R[u], nullptr, sm.Ks, sm.Vs, sm.pw, p, CF::C,
                                 chan_ptr<CF>(sc), conv_ptr<CF>(cs));
-      if constexpr (CH) {
-        chan_scale<CF>(Sacc, sc.bm, wv, lg);
+      if constexpr (CH) {  // S+ = diag(2^lb_L) S- + K^^T V, keys weighted 2^(lb_L - lb_i)
+        chan_scale<CF>(Sacc, sc.el, wv, lg);
         if (cc + CF::C < t_end) chan_prefetch<CF, VK>(A, ra, p, cc + CF::C, CF::C);
       }
       if (cc + PD * CF::C < t_end)
         prefetch<CF, false, VK, NT>(R[u], p, hb, cc + PD * CF::C, CF::C);
       __syncthreads();
       state_update<CF>(Sacc, sm.Ks, sm.Vs, gC, decay, wv, li, lg);
-      if constexpr (CH) chan_scale<CF>(Sacc, sc.bl, wv, lg);
       __syncthreads();
     }
   }
@@ -1310,7 +1464,7 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
   const int slot = part == 0 ? seg + 1 : p.nseg + seg;
   float *dst = p.ws + ((size_t)slot * p.BH + bh) * ws_rec(d, dv);
   store_slot<CF>(Sacc, dst, d, dv, p.slot_vec, wv, li, lg);
-  if constexpr (CH) {  // the segment's log decay per channel (own thread's sum)
+  if constexpr (CH) {  // the segment's log2 decay per channel (own thread's sum)
     if (threadIdx.x < d) dst[(size_t)d * dv + d + threadIdx.x] = sc.tot[threadIdx.x];
   }
 }
@@ -1319,8 +1473,8 @@ __global__ void __launch_bounds__(CF::NT, (CH && CV) ? wpe_at_most_2<CF>() : CF:
 // slot s <- gamma^Lseg slot (s-1) + dS_(s-1) for s >= 1, where dS_(s-1) is
 // the contribution of segment s-1: its summary record (slot s), or with two
 // summary parts gamma^Lb A + B (A in slot s, B, the last Lb tokens, in slot
-// nseg + s - 1).  With a per-channel decay the factors of row f are exp of
-// the parts' log decays of channel f, stored with the records.  One thread
+// nseg + s - 1).  With a per-channel decay the factors of row f are 2 to
+// the parts' log2 decays of channel f, stored with the records.  One thread
 // per record element; every record is loaded before the dependent chain.
 template <bool CH, bool TWO>
 __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
@@ -1370,12 +1524,12 @@ __global__ void __launch_bounds__(256) scan_kernel(PrefillParams p) {
       if constexpr (TWO) {
         float gb = gB;
         if constexpr (CH) {
-          g = __expf(lgd[s] + lgb[s]);
-          gb = __expf(lgb[s]);
+          g = exp2f(lgd[s] + lgb[s]);
+          gb = exp2f(lgb[s]);
         }
         seg_part = fmaf(gb, seg_part, dB[s]);
       } else if constexpr (CH) {
-        g = __expf(lgd[s]);
+        g = exp2f(lgd[s]);
       }
       acc = fmaf(g, acc, seg_part);
       base[s * stride] = acc;

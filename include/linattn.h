@@ -116,7 +116,9 @@ typedef struct la_prefill_args {
   const float *alpha;/* State decay per token, or NULL (= 1, no decay).
                         DELTA: [B,H,N], each in (0, 1].
                         LINEAR: [B,H,N,d], one factor per key channel, each
-                        in [0.1, 1]; not together with gamma.
+                        in (0, 1]; not together with gamma.  Factors below
+                        2^-15 are taken as 2^-15 (an earlier token then
+                        weighs under 3.1e-5 of the current one).
                         Values are the caller's contract (not read on the
                         host); values outside the range make the chunk's
                         decay products inaccurate or undefined. */

@@ -310,6 +310,65 @@ def test_gla_prefill_segments_and_initial_state(dtype, lo):
     assert_close(z, rz, TOL[dtype], "z")
 
 
+def _alpha_log(shape, seed, lo):
+    """Decay per key channel log-uniform in (lo, 1): lo^u, u ~ U(0, 1)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.exp(torch.rand(shape, generator=g, dtype=torch.float64) * np.log(lo)) \
+        .to(torch.float32).to(DEV)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("lo", [1e-2, 1e-3, 2.0 ** -15, 1e-6],
+                         ids=["1e-2", "1e-3", "2^-15", "1e-6"])
+@pytest.mark.parametrize("N", [150, 4099])
+def test_gla_fast_decay(dtype, lo, N):
+    """Decays log-uniform down to lo per channel and token ("Efficient
+    attention variants" 7.2 lets the gate forget quickly): the block
+    references keep every factor inside the fp32/bf16 range.  Below 2^-15 a
+    token's decay is clamped there, where an earlier token weighs under
+    3.1e-5 of the current one, inside the fp32 bound.  One segment (N = 150)
+    and several (summary, scan, chunk kernels; N = 4099), with an initial
+    state."""
+    B, H, d, dv = 1, 4, 64, 64
+    seed = 990 + int(-np.log2(lo)) + 7 * (dtype == torch.bfloat16) + N % 7
+    q = _rand((B, H, N, d), dtype, seed, 0.125)
+    k = _rand((B, H, N, d), dtype, seed + 1, 0.125)
+    v = _rand((B, H, N, dv), dtype, seed + 2)
+    al = _alpha_log((B, H, N, d), seed + 3, lo)
+    S = _rand((B, H, d, dv), torch.float32, seed + 4, 0.3)
+    z = _rand((B, H, d), torch.float32, seed + 5, 0.3).abs() + 1.0
+    o, S1, z1 = la.prefill(q, k, v, alpha=al, eps=1e-6, S_in=S, z_in=z)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_gla(q, k, v, al, S0=S, z0=z)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S1).all()
+    assert_close(o, ro, TOL[dtype], "o")
+    assert_close(S1, rS, TOL[dtype], "S", axes=(-2, -1))
+    assert_close(z1, rz, TOL[dtype], "z")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("dims", [(128, 128), (64, 128), (24, 40)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gla_mixed_channel_decays(dtype, dims):
+    """Half the key channels barely decay (alpha ~ 0.999), half forget almost
+    at once (alpha ~ 1e-4): factors of both extremes in one tile."""
+    d, dv = dims
+    B, H, N = 2, 2, 300
+    seed = 1010 + d + dv + (dtype == torch.bfloat16)
+    q = _rand((B, H, N, d), dtype, seed, d ** -0.5)
+    k = _rand((B, H, N, d), dtype, seed + 1, d ** -0.5)
+    v = _rand((B, H, N, dv), dtype, seed + 2)
+    slow = _alpha((B, H, N, d), seed + 3, 0.998)
+    fast = _alpha_log((B, H, N, d), seed + 4, 1e-4) * 1e-2
+    al = torch.where(torch.arange(d, device=DEV) % 2 == 0, slow, fast.clamp_min(1e-6))
+    o, S, z = la.prefill(q, k, v, alpha=al, eps=1e-6)
+    torch.cuda.synchronize()
+    ro, rS, rz = _oracle_gla(q, k, v, al)
+    assert_close(o, ro, TOL[dtype], "o")
+    assert_close(S, rS, TOL[dtype], "S", axes=(-2, -1))
+    assert_close(z, rz, TOL[dtype], "z")
+
+
 def test_gla_uniform_alpha_matches_gamma():
     """alpha = gamma_h on every channel and token reproduces the per-head decay
     path (to bf16 resolution: different kernel instantiations)."""
