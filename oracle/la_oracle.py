@@ -364,6 +364,67 @@ def linear_decode_step_conv(q, k, v, S, z, conv_weight, conv_cache, **kw):
     return o, S_new, z_new, np.concatenate([hq, hk, hv], axis=-1)
 
 
+def short_conv_backward(x, weight, dy, cache=None, dcache_out=None):
+    """Gradients of short_conv: reverse mode of its two results, the outputs
+    y_t[c] = sum_j weight[h, j, c] x~_(t+j)[c] over the sequence x~ = [cache |
+    x] (cache rows oldest first, zeros without one) and the returned cache,
+    the last w-1 rows of x~.  The pages give the convolution but no gradient
+    formulas ([WILA] 5.4); this is the chain rule written out.
+
+    dy: dL/dy [B, H, N, c]; dcache_out: dL/d(returned cache) [B, H, w-1, c]
+    or None.  Returns (dx [B, H, N, c], dweight [H, w, c] (summed over the
+    batch), dcache [B, H, w-1, c]) in float64.
+    """
+    x, W, dy = _f64(x), _f64(weight), _f64(dy)
+    B, H, N, c = x.shape
+    w = W.shape[1]
+    hist = np.zeros((B, H, w - 1, c)) if cache is None else _f64(cache)
+    full = np.concatenate([hist, x], axis=2)  # row r is token r - (w-1)
+    dfull = np.zeros_like(full)
+    dW = np.zeros((H, w, c))
+    for t in range(N):
+        for j in range(w):  # y_t reads full row t + j with tap j
+            dfull[:, :, t + j] += W[None, :, j] * dy[:, :, t]
+            dW[:, j] += np.sum(dy[:, :, t] * full[:, :, t + j], axis=0)
+    if dcache_out is not None and w > 1:
+        dfull[:, :, full.shape[2] - (w - 1):] += _f64(dcache_out)
+    return dfull[:, :, w - 1:], dW, dfull[:, :, :w - 1]
+
+
+def _conv_backward_qkv(q, k, v, W, cache, dy, dcache_out):
+    """short_conv_backward on the channels [q | k | v]: (dq, dk, dv, dW, dcache)."""
+    d = q.shape[-1]
+    ws = _conv_split(W, d)
+    cs = (None,) * 3 if cache is None else _conv_split(cache, d)
+    dco = (None,) * 3 if dcache_out is None else _conv_split(dcache_out, d)
+    out = [short_conv_backward(x, wx, g, cx, gx)
+           for x, wx, g, cx, gx in zip((q, k, v), ws, dy, cs, dco)]
+    return (out[0][0], out[1][0], out[2][0],
+            np.concatenate([o[1] for o in out], axis=-1),
+            np.concatenate([o[2] for o in out], axis=-1))
+
+
+def linear_backward_conv(q, k, v, do, conv_weight, *, conv_cache=None, dconv_cache_out=None,
+                         **kw):
+    """Gradients of linear_prefill_conv: linear_backward on the convolved q,
+    k, v, then the convolution's chain rule.  dconv_cache_out: dL/d(the conv
+    cache it returns) or None.  Other keywords as linear_backward.  Returns
+    (dq, dk, dv, dconv_weight [H, w, 2d+dv], dconv_cache [B, H, w-1, 2d+dv],
+    dS_0, dz_0) in float64."""
+    d = q.shape[-1]
+    wq, wk, wv = _conv_split(conv_weight, d)
+    cq = ck = cv = None
+    if conv_cache is not None:
+        cq, ck, cv = _conv_split(conv_cache, d)
+    yq, _ = short_conv(q, wq, cq)
+    yk, _ = short_conv(k, wk, ck)
+    yv, _ = short_conv(v, wv, cv)
+    gq, gk, gv, dS0, dz0 = linear_backward(yq, yk, yv, do, **kw)
+    dq, dk, dv, dW, dC = _conv_backward_qkv(q, k, v, conv_weight, conv_cache, (gq, gk, gv),
+                                            dconv_cache_out)
+    return dq, dk, dv, dW, dC, dS0, dz0
+
+
 # ---------------------------------------------------------------------------
 # Gated DELTA rule (raw q, k; no normaliser)
 # ---------------------------------------------------------------------------
@@ -517,3 +578,22 @@ def delta_backward(q, k, v, g, do, *, alpha=None, S0=None, dS_N=None):
                            - gt * np.einsum("...d,...d->...", pred, w))
         Sh = a[..., None, None] * (Sh - gt[..., None, None] * kt[..., :, None] * w[..., None, :])
     return dq, dk, dvv, dg, da, Sh
+
+
+def delta_backward_conv(q, k, v, g, do, conv_weight, *, conv_cache=None, dconv_cache_out=None,
+                        alpha=None, S0=None, dS_N=None):
+    """Gradients of delta_prefill_conv: delta_backward on the convolved q, k,
+    v, then the convolution's chain rule.  Returns (dq, dk, dv, dg, dalpha,
+    dconv_weight [H, w, 2d+dv], dconv_cache [B, H, w-1, 2d+dv], dS_0)."""
+    d = q.shape[-1]
+    wq, wk, wv = _conv_split(conv_weight, d)
+    cq = ck = cv = None
+    if conv_cache is not None:
+        cq, ck, cv = _conv_split(conv_cache, d)
+    yq, _ = short_conv(q, wq, cq)
+    yk, _ = short_conv(k, wk, ck)
+    yv, _ = short_conv(v, wv, cv)
+    gq, gk, gv, dg, dal, dS0 = delta_backward(yq, yk, yv, g, do, alpha=alpha, S0=S0, dS_N=dS_N)
+    dq, dk, dv, dW, dC = _conv_backward_qkv(q, k, v, conv_weight, conv_cache, (gq, gk, gv),
+                                            dconv_cache_out)
+    return dq, dk, dv, dg, dal, dW, dC, dS0

@@ -902,6 +902,106 @@ def pin_delta_backward_finite_differences(orc):
         np.testing.assert_allclose(grads[name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
 
 
+def _torch_conv(x, W, cache):
+    """The short convolution as explicit tap sums over [cache | x] in torch
+    ops (x [H, N, c], W [H, w, c], cache [H, w-1, c]); returns (y, the last
+    w-1 rows of [cache | x])."""
+    import torch
+    full = torch.cat([cache, x], dim=1)
+    w, N = W.shape[1], x.shape[1]
+    y = sum(W[:, j, None, :] * full[:, j:j + N, :] for j in range(w))
+    return y, full[:, full.shape[1] - (w - 1):]
+
+
+def _conv_grads_case(rng, H, N, d, dv, w):
+    q = rng.normal(size=(H, N, d))
+    k = rng.normal(size=(H, N, d)) * 0.6
+    v = rng.normal(size=(H, N, dv))
+    W = rng.normal(size=(H, w, 2 * d + dv)) * 0.5
+    W[:, w - 1] += 1.0
+    C = rng.normal(size=(H, w - 1, 2 * d + dv)) * 0.5
+    dC = rng.normal(size=(H, w - 1, 2 * d + dv))
+    do = rng.normal(size=(H, N, dv))
+    return q, k, v, W, C, dC, do
+
+
+def pin_conv_backward_matches_autograd(orc):
+    """linear_backward_conv and delta_backward_conv equal torch autograd's
+    gradients through explicit tap sums and the recurrences (inputs, filters,
+    conv cache, initial state; with a final-state gradient and a gradient on
+    the returned conv cache), widths 1..4."""
+    import torch
+    rng = np.random.default_rng(71)
+    H, N, d, dv = 2, 7, 3, 4
+    T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)  # noqa: E731
+    for w in (1, 2, 4):
+        q, k, v, W, C, dC, do = _conv_grads_case(rng, H, N, d, dv, w)
+        # LINEAR (elu+1, decay, eps)
+        S0 = rng.normal(size=(H, d, dv)) * 0.3
+        z0 = rng.uniform(0.5, 1.0, size=(H, d))
+        dS, dz = rng.normal(size=(H, d, dv)), rng.normal(size=(H, d))
+        gamma, eps = np.array([0.9, 0.7]), 1e-2
+        tq, tk, tv, tW, tC, tS0, tz0 = T(q), T(k), T(v), T(W), T(C), T(S0), T(z0)
+        x = torch.cat([tq, tk, tv], dim=-1)
+        y, cout = _torch_conv(x, tW, tC)
+        loss = _torch_linear_loss(y[..., :d], y[..., d:2 * d], y[..., 2 * d:], torch.tensor(do),
+                                  torch.tensor(gamma), eps, tS0, tz0, torch.tensor(dS),
+                                  torch.tensor(dz), True)
+        (loss + (cout * torch.tensor(dC)).sum()).backward()
+        got = orc.linear_backward_conv(q[None], k[None], v[None], do[None], W,
+                                       conv_cache=C[None], dconv_cache_out=dC[None],
+                                       gamma=gamma, eps=eps, S0=S0[None], z0=z0[None],
+                                       dS_N=dS[None], dz_N=dz[None])
+        want = (tq.grad, tk.grad, tv.grad, tW.grad, tC.grad, tS0.grad, tz0.grad)
+        for name, gx, t in zip(("dq", "dk", "dv", "dW", "dC", "dS0", "dz0"), got, want):
+            gx = gx if name == "dW" else gx[0]
+            np.testing.assert_allclose(gx, t.numpy(), rtol=1e-10, atol=1e-12,
+                                       err_msg=f"linear w={w} {name}")
+        # DELTA with a decay
+        g = rng.uniform(0.1, 0.9, size=(H, N))
+        al = rng.uniform(0.6, 1.0, size=(H, N))
+        tq, tk, tv, tW, tC, tS0 = T(q), T(k * 0.5), T(v), T(W), T(C), T(S0)
+        x = torch.cat([tq, tk, tv], dim=-1)
+        y, cout = _torch_conv(x, tW, tC)
+        loss = _torch_delta_loss(y[..., :d], y[..., d:2 * d], y[..., 2 * d:], torch.tensor(g),
+                                 torch.tensor(al), tS0, torch.tensor(do), torch.tensor(dS))
+        (loss + (cout * torch.tensor(dC)).sum()).backward()
+        got = orc.delta_backward_conv(q[None], (k * 0.5)[None], v[None], g[None], do[None], W,
+                                      conv_cache=C[None], dconv_cache_out=dC[None],
+                                      alpha=al[None], S0=S0[None], dS_N=dS[None])
+        want = (tq.grad, tk.grad, tv.grad, None, None, tW.grad, tC.grad, tS0.grad)
+        for name, gx, t in zip(("dq", "dk", "dv", "dg", "dal", "dW", "dC", "dS0"), got, want):
+            if t is None:
+                continue
+            gx = gx if name == "dW" else gx[0]
+            np.testing.assert_allclose(gx, t.numpy(), rtol=1e-10, atol=1e-12,
+                                       err_msg=f"delta w={w} {name}")
+
+
+def pin_conv_backward_finite_differences(orc):
+    """The filter and conv-cache gradients of linear_backward_conv against
+    central differences of linear_prefill_conv's loss sum(o * do)."""
+    rng = np.random.default_rng(72)
+    H, N, d, dv, w = 1, 6, 2, 3, 3
+    q, k, v, W, C, _, do = _conv_grads_case(rng, H, N, d, dv, w)
+    q, k, v, C, do = q[None], k[None], v[None], C[None], do[None]
+    loss = lambda W_, C_: np.sum(orc.linear_prefill_conv(q, k, v, W_, conv_cache=C_)[0] * do)  # noqa: E731
+    _, _, _, dW, dC, _, _ = orc.linear_backward_conv(q, k, v, do, W, conv_cache=C)
+    h = 1e-6
+    for idx in ((0, 0, 0), (0, 1, 2), (0, 2, 5), (0, 2, 6)):
+        Wp, Wm = W.copy(), W.copy()
+        Wp[idx] += h
+        Wm[idx] -= h
+        np.testing.assert_allclose(dW[idx], (loss(Wp, C) - loss(Wm, C)) / (2 * h), rtol=1e-6,
+                                   atol=1e-8)
+    for idx in ((0, 0, 0, 1), (0, 0, 1, 4), (0, 0, 1, 6)):
+        Cp, Cm = C.copy(), C.copy()
+        Cp[idx] += h
+        Cm[idx] -= h
+        np.testing.assert_allclose(dC[idx], (loss(W, Cp) - loss(W, Cm)) / (2 * h), rtol=1e-6,
+                                   atol=1e-8)
+
+
 def pin_delta_backward_gate_zero(orc):
     """With g = 0 the state never changes (S_t = S0, no decay), so
     o_t = S0^T q_t: dq_t = S0 do_t, dk = dv = 0, dS0 = sum_t q_t do_t^T, and

@@ -295,6 +295,18 @@ for _n in ("_dconv_raw_values", "_dconv_decode_raw_query", "_dconv_decode_cache_
     globals()[_n].__name__ = _n
 
 
+_cbwd_tap_mirrored = _patched("dfull[:, :, t + j] += W[None, :, j] * dy[:, :, t]",
+                              "dfull[:, :, t + j] += W[None, :, w - 1 - j] * dy[:, :, t]")
+_cbwd_weight_from_output = _patched(
+    "dW[:, j] += np.sum(dy[:, :, t] * full[:, :, t + j], axis=0)",
+    "dW[:, j] += np.sum(dy[:, :, t] * full[:, :, t + w - 1], axis=0)")
+_cbwd_cache_grad_dropped = _patched(
+    "        dfull[:, :, full.shape[2] - (w - 1):] += _f64(dcache_out)\n",
+    "        pass\n")
+for _n in ("_cbwd_tap_mirrored", "_cbwd_weight_from_output", "_cbwd_cache_grad_dropped"):
+    globals()[_n].__name__ = _n
+
+
 MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _exp_everywhere, _decay_off_by_one, _outer_transposed,
            _quadratic_strict_mask, _delta_not_transposed, _delta_wrong_sign,
@@ -307,7 +319,8 @@ MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _bwd_dv_from_query, _bwd_dk_without_z, _dbwd_dk_no_state_term,
            _dbwd_adjoint_not_decayed, _dbwd_adjoint_no_projection, _dbwd_dv_without_gate,
            _dbwd_dq_from_previous_state, _dbwd_residual_undecayed, _dbwd_dalpha_no_gate_term,
-           _dconv_raw_values, _dconv_decode_raw_query, _dconv_decode_cache_kept]
+           _dconv_raw_values, _dconv_decode_raw_query, _dconv_decode_cache_kept,
+           _cbwd_tap_mirrored, _cbwd_weight_from_output, _cbwd_cache_grad_dropped]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
