@@ -95,13 +95,15 @@ def _prefill_args(q, k, v, rule, fmap, gamma, g, eps, alpha=None):
 
 
 def workspace_size(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None,
-                   eps=1e-6, alpha=None, conv_weight=None):
-    """Workspace bytes la_prefill needs for these tensors (current device)."""
+                   eps=1e-6, alpha=None, conv_weight=None, den_out=None):
+    """Workspace bytes la_prefill needs for these tensors (current device);
+    den_out: the denominators tensor the call will write, if any."""
     if fmap is None:
         fmap = "elu1" if rule == "linear" else "identity"
     a = _prefill_args(q, k, v, rule, fmap, gamma, g, eps, alpha)
     if conv_weight is not None:
         a.conv_weight, a.conv_width = _ptr(conv_weight), conv_weight.shape[1]
+    a.den_out = _ptr(den_out)
     n = _lib.load().la_prefill_workspace_size(ctypes.byref(a))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes")
@@ -181,19 +183,42 @@ def prefill(q, k, v, *, rule="linear", fmap=None, gamma=None, g=None, eps=1e-6,
     return o, S_out, z_out
 
 
+def _conv_grads(a, conv_weight, conv_cache, dconv_cache_out, conv_cache_grad, q, H, d, dv,
+                lead):
+    """Fill the convolution fields of backward arguments; returns (dW, dC)."""
+    w = _conv_check(conv_weight, conv_cache, q, H, d, dv, lead)
+    if dconv_cache_out is not None:
+        _conv_check(conv_weight, dconv_cache_out, q, H, d, dv, lead)
+    if not w:
+        return None, None
+    dW = torch.empty_like(conv_weight)
+    dC = None
+    if conv_cache_grad and w > 1:
+        dC = torch.empty((*lead, w - 1, 2 * d + dv), dtype=q.dtype, device=q.device)
+    a.conv_weight, a.conv_width, a.conv_in = _ptr(conv_weight), w, _ptr(conv_cache)
+    a.grad_conv_out, a.grad_conv_weight, a.grad_conv_in = _ptr(dconv_cache_out), _ptr(dW), \
+        _ptr(dC)
+    return dW, dC
+
+
 def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=None,
              dS_out=None, dz_out=None, state_grad=True, workspace=None,
-             fwd_workspace=None):
+             fwd_workspace=None, conv_weight=None, conv_cache=None, dconv_cache_out=None,
+             conv_cache_grad=True):
     """Gradients of a LINEAR prefill (see la_backward): q, k [B,H,N,d], v, o,
     do [B,H,N,dv] (dtype of q), den [B,H,N] fp32 from prefill(den_out=...);
     gamma, S_in, z_in as in the forward; dS_out [B,H,d,dv], dz_out [B,H,d]
     the gradient with respect to the final state, or None.
     fwd_workspace: the workspace the forward prefill ran with (prefill's
     workspace=, same inputs), whose segment states are then reused.
+    conv_weight, conv_cache: the forward's short convolution (q, k, v raw);
+    dconv_cache_out: dL/d(the conv cache it returned), or None.
     Returns (dq, dk, dv, dS_in, dz_in); the last two are None unless
-    state_grad."""
-    _need_gpu(q, k, v, o, den, do, gamma, S_in, z_in, dS_out, dz_out, workspace, fwd_workspace)
-    _need_f32(den, gamma, S_in, z_in, dS_out, dz_out)
+    state_grad; with a convolution also (dconv_weight, dconv_cache) (the
+    latter None unless conv_cache_grad and w > 1)."""
+    _need_gpu(q, k, v, o, den, do, gamma, S_in, z_in, dS_out, dz_out, workspace, fwd_workspace,
+              conv_weight, conv_cache, dconv_cache_out)
+    _need_f32(den, gamma, S_in, z_in, dS_out, dz_out, conv_weight)
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,H,N,d] and v [B,H,N,dv]")
     if o.shape != v.shape or do.shape != v.shape or tuple(den.shape) != tuple(q.shape[:3]):
@@ -216,6 +241,8 @@ def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=No
     a.grad_S_out, a.grad_z_out = _ptr(dS_out), _ptr(dz_out)
     a.grad_q, a.grad_k, a.grad_v = _ptr(dq), _ptr(dk), _ptr(dvv)
     a.grad_S_in, a.grad_z_in = _ptr(dS_in), _ptr(dz_in)
+    dW, dC = _conv_grads(a, conv_weight, conv_cache, dconv_cache_out, conv_cache_grad, q, H, d,
+                         dv, (B, H))
     if fwd_workspace is not None:
         a.fwd_workspace = _ptr(fwd_workspace)
         a.fwd_workspace_bytes = fwd_workspace.numel() * fwd_workspace.element_size()
@@ -229,15 +256,20 @@ def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=No
         a.workspace = _ptr(workspace)
         a.workspace_bytes = workspace.numel() * workspace.element_size()
     _lib.check(lib.la_backward(ctypes.byref(a), _stream()), "la_backward")
+    if conv_weight is not None:
+        return dq, dk, dvv, dS_in, dz_in, dW, dC
     return dq, dk, dvv, dS_in, dz_in
 
 
-def delta_backward_workspace_size(q, k, v):
+def delta_backward_workspace_size(q, k, v, conv_weight=None):
     """Workspace bytes la_delta_backward needs for these tensors."""
     B, H, N, d = q.shape
     a = _lib.DeltaBackwardArgs()
     a.B, a.H, a.N, a.d, a.dv = B, H, N, d, v.shape[3]
     a.dtype = _DTYPES[q.dtype]
+    if conv_weight is not None:
+        a.conv_weight, a.conv_width = _ptr(conv_weight), conv_weight.shape[1]
+        a.grad_conv_weight = a.conv_weight  # (only whether it is set is read)
     n = _lib.load().la_delta_backward_workspace_size(ctypes.byref(a))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes")
@@ -245,15 +277,19 @@ def delta_backward_workspace_size(q, k, v):
 
 
 def delta_backward(q, k, v, g, do, *, alpha=None, S_in=None, dS_out=None, state_grad=True,
-                   workspace=None):
+                   workspace=None, conv_weight=None, conv_cache=None, dconv_cache_out=None,
+                   conv_cache_grad=True):
     """Gradients of a gated-delta prefill (see la_delta_backward): q, k
     [B,H,N,d], v, do [B,H,N,dv] (bf16), g and alpha [B,H,N] fp32 (alpha
     None: no decay), S_in [B,H,d,dv] the forward's initial state, dS_out
-    the gradient with respect to the final state (or None).
+    the gradient with respect to the final state (or None); conv_weight,
+    conv_cache, dconv_cache_out as in backward().
     Returns (dq, dk, dv, dg, dalpha, dS_in); dalpha is None without a decay,
-    dS_in None unless state_grad."""
-    _need_gpu(q, k, v, g, do, alpha, S_in, dS_out, workspace)
-    _need_f32(g, alpha, S_in, dS_out)
+    dS_in None unless state_grad; with a convolution also (dconv_weight,
+    dconv_cache)."""
+    _need_gpu(q, k, v, g, do, alpha, S_in, dS_out, workspace, conv_weight, conv_cache,
+              dconv_cache_out)
+    _need_f32(g, alpha, S_in, dS_out, conv_weight)
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,H,N,d] and v [B,H,N,dv]")
     if do.shape != v.shape or tuple(g.shape) != tuple(q.shape[:3]):
@@ -276,6 +312,8 @@ def delta_backward(q, k, v, g, do, *, alpha=None, S_in=None, dS_out=None, state_
     a.grad_o, a.grad_S_out = _ptr(do), _ptr(dS_out)
     a.grad_q, a.grad_k, a.grad_v, a.grad_g = _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(dg)
     a.grad_alpha, a.grad_S_in = _ptr(da), _ptr(dS_in)
+    dW, dC = _conv_grads(a, conv_weight, conv_cache, dconv_cache_out, conv_cache_grad, q, H, d,
+                         dv, (B, H))
     lib = _lib.load()
     need = lib.la_delta_backward_workspace_size(ctypes.byref(a))
     if need == ctypes.c_size_t(-1).value:
@@ -286,6 +324,8 @@ def delta_backward(q, k, v, g, do, *, alpha=None, S_in=None, dS_out=None, state_
         a.workspace = _ptr(workspace)
         a.workspace_bytes = workspace.numel() * workspace.element_size()
     _lib.check(lib.la_delta_backward(ctypes.byref(a), _stream()), "la_delta_backward")
+    if conv_weight is not None:
+        return dq, dk, dvv, dg, da, dS_in, dW, dC
     return dq, dk, dvv, dg, da, dS_in
 
 

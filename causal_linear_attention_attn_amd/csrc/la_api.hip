@@ -147,10 +147,51 @@ size_t conv_cache_bytes(size_t BH, int d, int dv, int width, bool bf16_io) {
 // at the start of the workspace (each region 256-byte aligned); the rule's
 // own workspace follows.
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
-size_t delta_conv_bytes(const la_prefill_args *a) {
-  if (!a->conv_weight || a->rule != LA_RULE_DELTA) return 0;
-  const size_t esz = a->dtype == LA_BF16 ? 2 : 4, rows = (size_t)a->B * a->H * a->N;
-  return 2 * round256(rows * a->d * esz) + round256(rows * a->dv * esz);
+// Bytes of three [B,H,N,*] copies of q, k, v (or of their gradients), each
+// region 256-byte aligned.
+size_t qkv_copy_bytes(size_t rows, int d, int dv, size_t esz) {
+  return 2 * round256(rows * d * esz) + round256(rows * dv * esz);
+}
+// The prefills that run the convolution as a pass of its own: the delta
+// rule, and the LINEAR rule with denominators (a training forward).
+bool conv_pass(const la_prefill_args *a) {
+  return a->conv_weight && (a->rule == LA_RULE_DELTA || a->den_out);
+}
+size_t conv_copy_bytes(const la_prefill_args *a) {
+  if (!conv_pass(a)) return 0;
+  return qkv_copy_bytes((size_t)a->B * a->H * a->N, a->d, a->dv, a->dtype == LA_BF16 ? 2 : 4);
+}
+
+// Convolution pass into the three copies at `base` (the conv cache after
+// the sequence to cache_out, when given).
+hipError_t run_conv_pass(int BH, int H, int N, int d, int dv, bool bf16_io, const float *w,
+                         int width, const void *q, const void *k, const void *v,
+                         const void *cache_in, void *cache_out, char *base, hipStream_t s,
+                         const void **yq, const void **yk, const void **yv) {
+  const size_t esz = bf16_io ? 2 : 4, rows = (size_t)BH * N;
+  la::ConvParams c{};
+  c.BH = BH;
+  c.H = H;
+  c.N = N;
+  c.d = d;
+  c.dv = dv;
+  c.width = width;
+  c.w = w;
+  c.q = q;
+  c.k = k;
+  c.v = v;
+  c.cache_in = cache_in;
+  c.cache_out = cache_out;
+  c.yq = base;
+  c.yk = base + round256(rows * d * esz);
+  c.yv = base + 2 * round256(rows * d * esz);
+  *yq = c.yq;
+  *yk = c.yk;
+  *yv = c.yv;
+  const bool vec16 = ((size_t)d * esz) % 16 == 0 && ((size_t)dv * esz) % 16 == 0 &&
+                     aligned16(q) && aligned16(k) && aligned16(v) && aligned16(base) &&
+                     (!cache_in || aligned16(cache_in));
+  return la::launch_conv_qkv(c, bf16_io, vec16, s);
 }
 
 bool overlap(const void *a, const void *b, size_t n) {
@@ -162,7 +203,7 @@ bool overlap(const void *a, const void *b, size_t n) {
 
 extern "C" {
 
-int32_t la_abi_version(void) { return 5; }
+int32_t la_abi_version(void) { return 6; }
 
 const char *la_status_str(int s) {
   switch (s) {
@@ -181,10 +222,12 @@ size_t la_prefill_workspace_size(const la_prefill_args *a) {
   const int BH = a->B * a->H;
   if (BH == 0 || a->N == 0) return 0;
   if (a->rule == LA_RULE_LINEAR)
-    return la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16,
-                           a->conv_weight ? a->conv_width : 0, a->alpha != nullptr)
-        .ws_bytes;
-  return delta_conv_bytes(a) + la::delta_workspace_bytes(BH, a->N, a->d, a->dtype == LA_BF16);
+    return conv_copy_bytes(a) +
+           la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16,
+                           a->conv_weight && !conv_pass(a) ? a->conv_width : 0,
+                           a->alpha != nullptr)
+               .ws_bytes;
+  return conv_copy_bytes(a) + la::delta_workspace_bytes(BH, a->N, a->d, a->dtype == LA_BF16);
 }
 
 int la_prefill(const la_prefill_args *a, void *stream) {
@@ -198,7 +241,7 @@ int la_prefill(const la_prefill_args *a, void *stream) {
     // one head's per-channel decay (fp32) must be addressable with 32-bit offsets
     if (a->alpha && (size_t)a->N * a->d * 4 > kMaxHeadBytes) return LA_EUNSUPPORTED;
     // denominators are written for the rule the backward covers
-    if (a->den_out && (a->alpha || a->conv_weight)) return LA_EUNSUPPORTED;
+    if (a->den_out && a->alpha) return LA_EUNSUPPORTED;
   } else {
     if (!a->g && BH > 0 && a->N > 0) return LA_EINVAL;
     if (a->gamma || a->z_in || a->z_out || a->den_out) return LA_EINVAL;
@@ -230,13 +273,15 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   la::LinearPlan plan{};
   size_t ws_need;
   if (linear) {
-    plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io, cw, a->alpha != nullptr);
-    ws_need = plan.ws_bytes;
+    plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io, conv_pass(a) ? 0 : cw,
+                           a->alpha != nullptr);
+    ws_need = conv_copy_bytes(a) + plan.ws_bytes;
+    if (conv_pass(a) && !aligned16(a->workspace)) return LA_EINVAL;
   } else {
     ws_need = la::delta_workspace_bytes(BH, a->N, a->d, bf16_io);
     // one head's T and R tiles must be addressable with 32-bit byte offsets
     if (ws_need / (size_t)BH > kMaxHeadBytes) return LA_EUNSUPPORTED;
-    ws_need += delta_conv_bytes(a);
+    ws_need += conv_copy_bytes(a);
   }
   if (ws_need > 0 && (!a->workspace || a->workspace_bytes < ws_need))
     return LA_EWORKSPACE;
@@ -267,44 +312,22 @@ int la_prefill(const la_prefill_args *a, void *stream) {
   p.o = a->o;
   p.den_out = a->den_out;
   p.ws = reinterpret_cast<float *>(a->workspace);
-  if (!linear) {
-    if (cw > 0) {  // the rule runs on convolved copies of q, k, v
-      const size_t esz = bf16_io ? 2 : 4, rows = (size_t)BH * a->N;
-      char *base = static_cast<char *>(a->workspace);
-      la::ConvParams c{};
-      c.BH = BH;
-      c.H = a->H;
-      c.N = a->N;
-      c.d = a->d;
-      c.dv = a->dv;
-      c.width = cw;
-      c.w = a->conv_weight;
-      c.q = a->q;
-      c.k = a->k;
-      c.v = a->v;
-      c.cache_in = a->conv_in;
-      c.cache_out = a->conv_out;
-      c.yq = base;
-      c.yk = base + round256(rows * a->d * esz);
-      c.yv = base + 2 * round256(rows * a->d * esz);
-      const bool vec16 = (a->d * esz) % 16 == 0 && (a->dv * esz) % 16 == 0 &&
-                         aligned16(a->q) && aligned16(a->k) && aligned16(a->v) &&
-                         (!a->conv_in || aligned16(a->conv_in));
-      hipError_t e = la::launch_conv_qkv(c, bf16_io, vec16, s);
-      if (e != hipSuccess) return LA_EHIP;
-      p.q = c.yq;
-      p.k = c.yk;
-      p.v = c.yv;
-      p.vec_ok = (a->d % vec == 0) && (a->dv % vec == 0) && aligned16(a->o);
-      p.ws = reinterpret_cast<float *>(base + delta_conv_bytes(a));
-    }
-    return to_status(la::launch_delta_prefill(p, bf16_io, s));
+  if (conv_pass(a)) {  // the rule runs on convolved copies of q, k, v
+    char *base = static_cast<char *>(a->workspace);
+    const hipError_t e =
+        run_conv_pass(BH, a->H, a->N, a->d, a->dv, bf16_io, a->conv_weight, cw, a->q, a->k,
+                      a->v, a->conv_in, a->conv_out, base, s, &p.q, &p.k, &p.v);
+    if (e != hipSuccess) return LA_EHIP;
+    p.vec_ok = (a->d % vec == 0) && (a->dv % vec == 0) && aligned16(a->o);
+    p.ws = reinterpret_cast<float *>(base + conv_copy_bytes(a));
   }
+  if (!linear) return to_status(la::launch_delta_prefill(p, bf16_io, s));
   p.nseg = plan.nseg;
   p.seg_len = plan.seg_len;
   p.nsplit = plan.nsplit;
   p.split_len = plan.split_len;
-  p.slot_vec = (a->d % 4 == 0) && aligned16(a->workspace);
+  p.slot_vec = (a->d % 4 == 0) && aligned16(p.ws);
+  if (conv_pass(a)) return to_status(la::launch_linear_prefill(p, plan, bf16_io, s));
   p.conv_w = a->conv_weight;
   p.conv_width = cw;
   if (cw > 1) {
@@ -322,6 +345,95 @@ int la_prefill(const la_prefill_args *a, void *stream) {
 
 namespace {
 
+// The convolution fields of the backward arguments.
+int check_conv_grads(const float *w, int width, const void *cin, const void *gout,
+                     const float *gw, const void *gin) {
+  if (w) {
+    if (width < 1 || width > kMaxConvWidth || !gw) return LA_EINVAL;
+  } else if (width != 0 || cin || gout || gw || gin) {
+    return LA_EINVAL;
+  }
+  return LA_OK;
+}
+
+// Backward gradients with no tokens for the convolution's parameters: the
+// filters get none, the cache before the sequence passes straight through
+// to the cache after it.
+hipError_t conv_grads_no_tokens(int BH, int H, int d, int dv, int width, bool bf16_io,
+                                const void *gout, float *gw, void *gin, hipStream_t s) {
+  hipError_t e = la::launch_fill(gw, (size_t)H * width * (2 * (size_t)d + dv), 0.f, s);
+  const size_t n = conv_cache_bytes((size_t)BH, d, dv, width, bf16_io);
+  if (e == hipSuccess && gin && n)
+    e = gout ? la::launch_copy_bytes(gin, gout, n, s) : la::launch_zero_bytes(gin, n, s);
+  return e;
+}
+
+// Workspace of a backward call with the forward's short convolution:
+// dL/d(convolved q, k, v), the filter gradient's partial sums, and (unless
+// the forward's workspace is given) the convolved q, k, v themselves; then
+// the rule's own state slots.
+struct BwdLayout {
+  size_t grads, part, copies, slots, total;
+};
+BwdLayout conv_bwd_layout(int BH, int N, int d, int dv, size_t esz, int width, bool conv,
+                          bool fwd, size_t slot_bytes) {
+  BwdLayout L{};
+  const size_t rows = (size_t)BH * N;
+  size_t off = 0;
+  if (conv) {
+    L.grads = off;
+    off += qkv_copy_bytes(rows, d, dv, esz);
+    L.part = off;
+    off += round256(la::conv_dw_partial_floats(BH, N, d, dv, width) * sizeof(float));
+    if (!fwd) {
+      L.copies = off;
+      off += qkv_copy_bytes(rows, d, dv, esz);
+    }
+  }
+  L.slots = off;
+  L.total = off + slot_bytes;
+  return L;
+}
+
+// The convolution's chain rule after a rule's backward (dy: dL/d(convolved
+// q, k, v)).
+hipError_t conv_backward(int BH, int H, int N, int d, int dv, bool bf16_io, const float *w,
+                         int width, const void *q, const void *k, const void *v,
+                         const void *cin, const void *dyq, const void *dyk, const void *dyv,
+                         const void *gout, void *dq, void *dk, void *dv_, void *gin, float *gw,
+                         char *part, hipStream_t s) {
+  la::ConvBwdParams c{};
+  c.BH = BH;
+  c.H = H;
+  c.N = N;
+  c.d = d;
+  c.dv = dv;
+  c.width = width;
+  c.w = w;
+  c.q = q;
+  c.k = k;
+  c.v = v;
+  c.cache_in = cin;
+  c.dyq = dyq;
+  c.dyk = dyk;
+  c.dyv = dyv;
+  c.dcache_out = width > 1 ? gout : nullptr;
+  c.dq = dq;
+  c.dk = dk;
+  c.dv_ = dv_;
+  c.dcache_in = width > 1 ? gin : nullptr;
+  c.dw = gw;
+  c.dw_part = reinterpret_cast<float *>(part);
+  return la::launch_conv_backward(c, bf16_io, s);
+}
+
+// The three regions of a q, k, v copy starting at base.
+void qkv_regions(char *base, size_t rows, int d, size_t esz, void **q, void **k, void **v) {
+  *q = base;
+  *k = base + round256(rows * d * esz);
+  *v = base + 2 * round256(rows * d * esz);
+}
+
 int check_backward_shape(const la_backward_args *a) {
   if (!a) return LA_EINVAL;
   if (a->B < 0 || a->H < 0 || a->N < 0 || !dims_ok(a->d, a->dv)) return LA_EINVAL;
@@ -332,7 +444,8 @@ int check_backward_shape(const la_backward_args *a) {
   const size_t dmax = a->d > a->dv ? a->d : a->dv;
   if ((size_t)a->N * dmax * esz > kMaxHeadBytes) return LA_EUNSUPPORTED;
   if (!la::linear_backward_supported(a->d, a->dv, a->dtype == LA_BF16)) return LA_EUNSUPPORTED;
-  return LA_OK;
+  return check_conv_grads(a->conv_weight, a->conv_width, a->conv_in, a->grad_conv_out,
+                          a->grad_conv_weight, a->grad_conv_in);
 }
 
 // Adjoint slots (one copy of the forward's segment slots), and in front of
@@ -347,8 +460,12 @@ size_t la_backward_workspace_size(const la_backward_args *a) {
   if (check_backward_shape(a) != LA_OK) return (size_t)-1;
   const int BH = a->B * a->H;
   if (BH == 0 || a->N == 0) return 0;
-  return backward_ws_bytes(la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16, 0),
-                           a->fwd_workspace != nullptr);
+  const la::LinearPlan plan = la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16, 0);
+  const bool fwd = a->fwd_workspace != nullptr;
+  return conv_bwd_layout(BH, a->N, a->d, a->dv, a->dtype == LA_BF16 ? 2 : 4, a->conv_width,
+                         a->conv_weight != nullptr, fwd,
+                         plan.nseg > 1 ? backward_ws_bytes(plan, fwd) : 0)
+      .total;
 }
 
 int la_backward(const la_backward_args *a, void *stream) {
@@ -370,27 +487,63 @@ int la_backward(const la_backward_args *a, void *stream) {
     if (e == hipSuccess && a->grad_z_in)
       e = a->grad_z_out ? la::launch_copy(a->grad_z_in, a->grad_z_out, nz, s)
                         : la::launch_fill(a->grad_z_in, nz, 0.f, s);
+    if (e == hipSuccess && a->conv_weight)
+      e = conv_grads_no_tokens(BH, a->H, a->d, a->dv, a->conv_width, a->dtype == LA_BF16,
+                               a->grad_conv_out, a->grad_conv_weight, a->grad_conv_in, s);
     return to_status(e);
   }
   const bool bf16_io = a->dtype == LA_BF16;
+  const size_t esz = bf16_io ? 2 : 4, rows = (size_t)BH * a->N;
+  const bool conv = a->conv_weight != nullptr;
   const la::LinearPlan plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io, 0);
   // the forward's own records, when given (same plan, same slots); else
   // this call's workspace, filled below
   const bool reuse = plan.nseg > 1 && a->fwd_workspace != nullptr;
-  const size_t need = plan.nseg > 1 ? backward_ws_bytes(plan, reuse) : 0;
-  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return LA_EWORKSPACE;
-  const int vec = bf16_io ? 8 : 4;
-  const bool vec_ok = (a->d % vec == 0) && (a->dv % vec == 0) && aligned16(a->q) &&
-                      aligned16(a->k) && aligned16(a->v) && aligned16(a->o) &&
-                      aligned16(a->grad_o) && aligned16(a->grad_q) && aligned16(a->grad_k) &&
-                      aligned16(a->grad_v);
-  if (plan.nseg > 1 && a->fwd_workspace) {
-    if (a->fwd_workspace_bytes < plan.ws_bytes) return LA_EWORKSPACE;
-    if (reinterpret_cast<uintptr_t>(a->fwd_workspace) & 3u) return LA_EINVAL;
+  const BwdLayout L =
+      conv_bwd_layout(BH, a->N, a->d, a->dv, esz, a->conv_width, conv,
+                      a->fwd_workspace != nullptr, plan.nseg > 1 ? backward_ws_bytes(plan, reuse) : 0);
+  if (L.total > 0 && (!a->workspace || a->workspace_bytes < L.total)) return LA_EWORKSPACE;
+  if (conv && !aligned16(a->workspace)) return LA_EINVAL;
+  // the forward's workspace: [convolved q, k, v (with a convolution) | state slots]
+  const size_t fwd_copies = conv ? qkv_copy_bytes(rows, a->d, a->dv, esz) : 0;
+  if (a->fwd_workspace && (conv || plan.nseg > 1)) {
+    if (a->fwd_workspace_bytes < fwd_copies + (plan.nseg > 1 ? plan.ws_bytes : 0))
+      return LA_EWORKSPACE;
+    if (conv ? !aligned16(a->fwd_workspace)
+             : (reinterpret_cast<uintptr_t>(a->fwd_workspace) & 3u) != 0)
+      return LA_EINVAL;
   }
-  float *ws_own = reinterpret_cast<float *>(a->workspace);
+  char *base = static_cast<char *>(a->workspace);
+  // the rule's inputs and gradients: q, k, v themselves, or with a
+  // convolution the convolved copies and dL/d(those copies)
+  const void *q = a->q, *k = a->k, *v = a->v;
+  void *gq = a->grad_q, *gk = a->grad_k, *gv = a->grad_v;
+  if (conv) {
+    if (a->fwd_workspace) {
+      void *fq, *fk, *fv;
+      qkv_regions(const_cast<char *>(static_cast<const char *>(a->fwd_workspace)), rows, a->d,
+                  esz, &fq, &fk, &fv);
+      q = fq;
+      k = fk;
+      v = fv;
+    } else {
+      const hipError_t e =
+          run_conv_pass(BH, a->H, a->N, a->d, a->dv, bf16_io, a->conv_weight, a->conv_width,
+                        a->q, a->k, a->v, a->conv_in, nullptr, base + L.copies, s, &q, &k, &v);
+      if (e != hipSuccess) return LA_EHIP;
+    }
+    qkv_regions(base + L.grads, rows, a->d, esz, &gq, &gk, &gv);
+  }
+  const int vec = bf16_io ? 8 : 4;
+  const bool vec_ok = (a->d % vec == 0) && (a->dv % vec == 0) && aligned16(q) &&
+                      aligned16(k) && aligned16(v) && aligned16(a->o) &&
+                      aligned16(a->grad_o) && aligned16(gq) && aligned16(gk) && aligned16(gv);
+  float *ws_own = base ? reinterpret_cast<float *>(base + L.slots) : nullptr;
   float *ws_r = ws_own ? ws_own + (reuse ? 0 : plan.ws_bytes / sizeof(float)) : nullptr;
-  const float *ws_f = reuse ? reinterpret_cast<const float *>(a->fwd_workspace) : ws_own;
+  const float *ws_f =
+      reuse ? reinterpret_cast<const float *>(static_cast<const char *>(a->fwd_workspace) +
+                                              fwd_copies)
+            : ws_own;
   if (plan.nseg > 1 && !reuse) {  // the forward state entering each segment
     la::PrefillParams fp{};
     fp.BH = BH;
@@ -400,9 +553,9 @@ int la_backward(const la_backward_args *a, void *stream) {
     fp.dv = a->dv;
     fp.fmap = a->fmap == LA_FMAP_ELU1;
     fp.vec_ok = vec_ok;
-    fp.q = a->q;
-    fp.k = a->k;
-    fp.v = a->v;
+    fp.q = q;
+    fp.k = k;
+    fp.v = v;
     fp.gamma = a->gamma;
     fp.S_in = a->S_in;
     fp.z_in = a->z_in;
@@ -423,9 +576,9 @@ int la_backward(const la_backward_args *a, void *stream) {
   p.dv = a->dv;
   p.fmap = a->fmap == LA_FMAP_ELU1;
   p.vec_ok = vec_ok;
-  p.q = a->q;
-  p.k = a->k;
-  p.v = a->v;
+  p.q = q;
+  p.k = k;
+  p.v = v;
   p.o = a->o;
   p.dout = a->grad_o;
   p.den = a->den;
@@ -434,9 +587,9 @@ int la_backward(const la_backward_args *a, void *stream) {
   p.z_in = a->z_in;
   p.dS_out = a->grad_S_out;
   p.dz_out = a->grad_z_out;
-  p.dq = a->grad_q;
-  p.dk = a->grad_k;
-  p.dv_ = a->grad_v;
+  p.dq = gq;
+  p.dk = gk;
+  p.dv_ = gv;
   p.dS_in = a->grad_S_in;
   p.dz_in = a->grad_z_in;
   p.ws_f = const_cast<float *>(ws_f);  // read only by the backward kernels
@@ -445,7 +598,12 @@ int la_backward(const la_backward_args *a, void *stream) {
   p.nseg = plan.nseg;
   p.seg_len = plan.seg_len;
   p.slot_vec = (a->d % 4 == 0) && aligned16(ws_f) && aligned16(ws_r);
-  return to_status(la::launch_linear_backward(p, bf16_io, s));
+  hipError_t e = la::launch_linear_backward(p, bf16_io, s);
+  if (e != hipSuccess || !conv) return to_status(e);
+  return to_status(conv_backward(BH, a->H, a->N, a->d, a->dv, bf16_io, a->conv_weight,
+                                 a->conv_width, a->q, a->k, a->v, a->conv_in, gq, gk, gv,
+                                 a->grad_conv_out, a->grad_q, a->grad_k, a->grad_v,
+                                 a->grad_conv_in, a->grad_conv_weight, base + L.part, s));
 }
 
 namespace {
@@ -465,7 +623,8 @@ int check_delta_backward_shape(const la_delta_backward_args *a) {
   // one head's preparation records must be addressable with 32-bit offsets
   const size_t nch = ((size_t)a->N + 63) / 64, dk = a->d <= 64 ? 64 : 128;
   if (nch * (2 * dk * 64 + 64 * 64) * 2 > kMaxHeadBytes) return LA_EUNSUPPORTED;
-  return LA_OK;
+  return check_conv_grads(a->conv_weight, a->conv_width, a->conv_in, a->grad_conv_out,
+                          a->grad_conv_weight, a->grad_conv_in);
 }
 
 }  // namespace
@@ -474,7 +633,9 @@ size_t la_delta_backward_workspace_size(const la_delta_backward_args *a) {
   if (check_delta_backward_shape(a) != LA_OK) return (size_t)-1;
   const int BH = a->B * a->H;
   if (BH == 0 || a->N == 0) return 0;
-  return la::delta_backward_sizes(BH, a->N, a->d, a->dv).bytes;
+  return conv_bwd_layout(BH, a->N, a->d, a->dv, 2, a->conv_width, a->conv_weight != nullptr,
+                         false, la::delta_backward_sizes(BH, a->N, a->d, a->dv).bytes)
+      .total;
 }
 
 int la_delta_backward(const la_delta_backward_args *a, void *stream) {
@@ -495,11 +656,29 @@ int la_delta_backward(const la_delta_backward_args *a, void *stream) {
     if (a->grad_S_in)
       e = a->grad_S_out ? la::launch_copy(a->grad_S_in, a->grad_S_out, nS, s)
                         : la::launch_fill(a->grad_S_in, nS, 0.f, s);
+    if (e == hipSuccess && a->conv_weight)
+      e = conv_grads_no_tokens(BH, a->H, a->d, a->dv, a->conv_width, true, a->grad_conv_out,
+                               a->grad_conv_weight, a->grad_conv_in, s);
     return to_status(e);
   }
   const la::BwdDeltaSizes z = la::delta_backward_sizes(BH, a->N, a->d, a->dv);
-  if (!a->workspace || a->workspace_bytes < z.bytes) return LA_EWORKSPACE;
+  const bool conv = a->conv_weight != nullptr;
+  const size_t rows = (size_t)BH * a->N;
+  const BwdLayout L = conv_bwd_layout(BH, a->N, a->d, a->dv, 2, a->conv_width, conv, false, z.bytes);
+  if (!a->workspace || a->workspace_bytes < L.total) return LA_EWORKSPACE;
   if (!aligned16(a->workspace)) return LA_EINVAL;
+  char *base = static_cast<char *>(a->workspace);
+  // the rule's inputs and gradients: q, k, v themselves, or with a
+  // convolution the convolved copies and dL/d(those copies)
+  const void *q = a->q, *k = a->k, *v = a->v;
+  void *gq = a->grad_q, *gk = a->grad_k, *gv = a->grad_v;
+  if (conv) {
+    const hipError_t e =
+        run_conv_pass(BH, a->H, a->N, a->d, a->dv, true, a->conv_weight, a->conv_width, a->q,
+                      a->k, a->v, a->conv_in, nullptr, base + L.copies, s, &q, &k, &v);
+    if (e != hipSuccess) return LA_EHIP;
+    qkv_regions(base + L.grads, rows, a->d, 2, &gq, &gk, &gv);
+  }
   la::BwdDeltaParams p{};
   p.BH = BH;
   p.H = a->H;
@@ -508,30 +687,35 @@ int la_delta_backward(const la_delta_backward_args *a, void *stream) {
   p.dv = a->dv;
   p.dvp = z.dvp;
   p.nch = z.nch;
-  p.vec_ok = (a->d % 8 == 0) && (a->dv % 8 == 0) && aligned16(a->q) && aligned16(a->k) &&
-             aligned16(a->v) && aligned16(a->grad_o) && aligned16(a->grad_q) &&
-             aligned16(a->grad_k) && aligned16(a->grad_v);
-  p.q = a->q;
-  p.k = a->k;
-  p.v = a->v;
+  p.vec_ok = (a->d % 8 == 0) && (a->dv % 8 == 0) && aligned16(q) && aligned16(k) &&
+             aligned16(v) && aligned16(a->grad_o) && aligned16(gq) && aligned16(gk) &&
+             aligned16(gv);
+  p.q = q;
+  p.k = k;
+  p.v = v;
   p.dout = a->grad_o;
   p.g = a->g;
   p.alpha = a->alpha;
   p.S_in = a->S_in;
   p.dS_out = a->grad_S_out;
-  p.dq = a->grad_q;
-  p.dk = a->grad_k;
-  p.dv_ = a->grad_v;
+  p.dq = gq;
+  p.dk = gk;
+  p.dv_ = gv;
   p.dg = a->grad_g;
   p.dalpha = a->grad_alpha;
   p.dS_in = a->grad_S_in;
-  p.ws = a->workspace;
+  p.ws = base + L.slots;
   p.lay_dec = z.dec;
   p.lay_states = z.states;
   p.lay_adj = z.adj;
   p.lay_y = z.y;
   p.lay_dd = z.dd;
-  return to_status(la::launch_delta_backward(p, s));
+  hipError_t e = la::launch_delta_backward(p, s);
+  if (e != hipSuccess || !conv) return to_status(e);
+  return to_status(conv_backward(BH, a->H, a->N, a->d, a->dv, true, a->conv_weight,
+                                 a->conv_width, a->q, a->k, a->v, a->conv_in, gq, gk, gv,
+                                 a->grad_conv_out, a->grad_q, a->grad_k, a->grad_v,
+                                 a->grad_conv_in, a->grad_conv_weight, base + L.part, s));
 }
 
 int la_decode_step(const la_decode_args *a, void *stream) {

@@ -65,6 +65,22 @@ struct ConvParams {
 // vec: d and dv multiples of 16 bytes of elements and every buffer 16-byte
 // aligned
 hipError_t launch_conv_qkv(const ConvParams &p, bool bf16_io, bool vec, hipStream_t s);
+// Backward of the convolution: from dL/dy (the convolved q, k, v), dL/dx,
+// dL/d(filters) and dL/d(cache before the sequence).
+struct ConvBwdParams {
+  int BH, H, N, d, dv, width;
+  const float *w;            // [H, width, 2d+dv]
+  const void *q, *k, *v;     // raw inputs
+  const void *cache_in;      // or nullptr (zeros)
+  const void *dyq, *dyk, *dyv;  // dL/d(convolved q, k, v)
+  const void *dcache_out;    // dL/d(returned cache) or nullptr (zero)
+  void *dq, *dk, *dv_;       // dL/d(raw q, k, v)
+  void *dcache_in;           // or nullptr (not written)
+  float *dw;                 // [H, width, 2d+dv]
+  float *dw_part;            // workspace: conv_dw_partial_floats floats
+};
+size_t conv_dw_partial_floats(int BH, int N, int d, int dv, int width);
+hipError_t launch_conv_backward(const ConvBwdParams &p, bool bf16_io, hipStream_t s);
 
 // Backward of the LINEAR rule's prefill.
 struct BwdParams {

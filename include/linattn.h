@@ -143,8 +143,11 @@ typedef struct la_prefill_args {
   void *o;           /* [B,H,N,dv] output, dtype as q (required if N > 0) */
   float *den_out;    /* LINEAR: [B,H,N] each token's denominator
                         phi(q_t).z_t + eps (what la_backward needs), or NULL
-                        (not written).  Not with alpha or conv_weight
-                        (LA_EUNSUPPORTED).  DELTA: must be NULL. */
+                        (not written).  Not with alpha (LA_EUNSUPPORTED).
+                        With conv_weight the convolution then runs as a pass
+                        of its own, into convolved copies of q, k, v at the
+                        start of the workspace (la_backward's fwd_workspace
+                        reads them).  DELTA: must be NULL. */
   void *workspace;   /* device scratch of workspace_bytes, caller-owned;
                         may be NULL when la_prefill_workspace_size() is 0.
                         DELTA: 16-byte aligned (else LA_EINVAL).  LINEAR:
@@ -155,7 +158,7 @@ typedef struct la_prefill_args {
 
 /* Bytes of device workspace la_prefill needs for these arguments on the
  * current device (0 when none).  Reads only the sizes, dtype, rule,
- * conv_width and whether conv_weight and alpha are set.
+ * conv_width and whether conv_weight, alpha and den_out are set.
  * Returns (size_t)-1 when the sizes are invalid. */
 size_t la_prefill_workspace_size(const la_prefill_args *args);
 
@@ -193,7 +196,8 @@ int la_prefill_noalloc(const la_prefill_args *args, void *stream);
  *   dq = dphi(q) phi'(q), dk = dphi(k) phi'(k); dL/d(initial state) = gamma Sh_0.
  * Inputs are the forward's q, k, v, gamma, initial state, its output o and
  * its denominators den (la_prefill's den_out); no per-key-channel decay
- * (alpha) or convolution.  fp32 inputs take d or dv up to 64 (both above
+ * (alpha); with the forward's convolution (conv_weight below) the
+ * gradients are taken through it too.  fp32 inputs take d or dv up to 64 (both above
  * 64: LA_EUNSUPPORTED, the fp32 state tile of the 128 x 128 kernels would
  * not fit the LDS); bf16 any d, dv up to 128. */
 typedef struct la_backward_args {
@@ -221,20 +225,37 @@ typedef struct la_backward_args {
   size_t workspace_bytes;
   /* Optional (NULL = not used): the workspace of the la_prefill call that
    * produced o and den, left as that call wrote it, with this call's q, k,
-   * v, gamma, S_in, z_in, fmap and no alpha or convolution; it holds the
-   * state entering each segment of the forward, which la_backward then
-   * reads (not written) instead of recomputing it.  fwd_workspace_bytes
+   * v, gamma, S_in, z_in, fmap, convolution and no alpha; it holds the
+   * state entering each segment of the forward (and with a convolution the
+   * convolved q, k, v), which la_backward then reads (not written) instead
+   * of recomputing it.  fwd_workspace_bytes
    * below la_prefill_workspace_size of those arguments: LA_EWORKSPACE; not
    * 4-byte aligned: LA_EINVAL.  Any other contents give wrong gradients
    * (not detected).  Ignored when the forward needs no workspace. */
   const void *fwd_workspace;
   size_t fwd_workspace_bytes;
+  /* The forward's short convolution (see la_prefill_args), or NULL: then
+   * q, k, v are the raw inputs and the gradients are taken through the
+   * convolution as well (the pages give no gradient formulas; the chain
+   * rule: dL/dx_t = sum_j W_j dL/dy_(t+(w-1)-j), dL/dW_j = the sum over the
+   * sequences and tokens of dL/dy_t times the input w-1-j tokens back). */
+  const float *conv_weight;  /* [H, w, 2d+dv] filters */
+  int32_t conv_width;        /* w, 1..4 with conv_weight; 0 without */
+  const void *conv_in;       /* [B,H,w-1,2d+dv] the forward's conv cache before
+                                the sequence (dtype of q), NULL = zeros */
+  const void *grad_conv_out; /* [B,H,w-1,2d+dv] dL/d(the conv cache the forward
+                                returned), dtype of q; NULL = zero */
+  float *grad_conv_weight;   /* [H, w, 2d+dv] output (required with
+                                conv_weight): summed over the batch */
+  void *grad_conv_in;        /* [B,H,w-1,2d+dv] dL/d(conv_in), dtype of q;
+                                NULL = not written */
 } la_backward_args;
 
 /* Workspace bytes la_backward needs (0 when none); (size_t)-1 for invalid
- * sizes.  Reads only the sizes, the dtype and whether fwd_workspace is NULL:
- * with the forward's workspace given, half as many bytes (the adjoint slots
- * only; the forward's states are read from fwd_workspace). */
+ * sizes.  Reads only the sizes, the dtype, conv_width (with conv_weight set)
+ * and whether fwd_workspace is NULL: with the forward's workspace given, the
+ * forward's segment states (and convolved inputs) are read from it, so half
+ * the state slots (and no copies of the inputs) are needed. */
 size_t la_backward_workspace_size(const la_backward_args *args);
 
 /* dq, dk, dv (and the initial-state gradient) of one LINEAR prefill. */
@@ -278,10 +299,26 @@ typedef struct la_delta_backward_args {
   void *workspace;   /* device scratch of workspace_bytes, caller-owned,
                         16-byte aligned (else LA_EINVAL) */
   size_t workspace_bytes;
+  /* The forward's short convolution (see la_prefill_args), or NULL: then
+   * q, k, v are the raw inputs and the gradients are taken through the
+   * convolution as well (the pages give no gradient formulas; the chain
+   * rule: dL/dx_t = sum_j W_j dL/dy_(t+(w-1)-j), dL/dW_j = the sum over the
+   * sequences and tokens of dL/dy_t times the input w-1-j tokens back). */
+  const float *conv_weight;  /* [H, w, 2d+dv] filters */
+  int32_t conv_width;        /* w, 1..4 with conv_weight; 0 without */
+  const void *conv_in;       /* [B,H,w-1,2d+dv] the forward's conv cache before
+                                the sequence (dtype of q), NULL = zeros */
+  const void *grad_conv_out; /* [B,H,w-1,2d+dv] dL/d(the conv cache the forward
+                                returned), dtype of q; NULL = zero */
+  float *grad_conv_weight;   /* [H, w, 2d+dv] output (required with
+                                conv_weight): summed over the batch */
+  void *grad_conv_in;        /* [B,H,w-1,2d+dv] dL/d(conv_in), dtype of q;
+                                NULL = not written */
 } la_delta_backward_args;
 
 /* Workspace bytes la_delta_backward needs (0 when none); (size_t)-1 for
- * invalid sizes.  Reads only the sizes and dtype. */
+ * invalid sizes.  Reads only the sizes, the dtype and conv_width (with
+ * conv_weight set). */
 size_t la_delta_backward_workspace_size(const la_delta_backward_args *args);
 
 /* dq, dk, dv, dg (and dalpha, the initial-state gradient) of one gated

@@ -255,10 +255,42 @@ def test_prefill_den_out_only_for_linear(lib):
     a = _args(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY, g=ctypes.c_void_p(0x2000),
               den_out=ctypes.c_void_p(0x3000))
     assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EINVAL
-    for extra in (dict(alpha=ctypes.c_void_p(0x2000)),
-                  dict(conv_weight=ctypes.c_void_p(0x2000), conv_width=4)):
-        a = _args(den_out=ctypes.c_void_p(0x3000), **extra)
-        assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+    a = _args(den_out=ctypes.c_void_p(0x3000), alpha=ctypes.c_void_p(0x2000))
+    assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype,esz", [(_lib.LA_BF16, 2), (_lib.LA_F32, 4)])
+def test_training_forward_with_conv_keeps_the_convolved_inputs(lib, dtype, esz):
+    """With denominators and a convolution the prefill convolves into copies
+    of q, k, v at the start of its workspace, ahead of the plain rule's."""
+    fake = ctypes.c_void_p(0x2000)
+    kw = dict(B=2, H=3, N=4100, d=64, dv=40, dtype=dtype)
+    plain = lib.la_prefill_workspace_size(ctypes.byref(_args(den_out=fake, **kw)))
+    conv = lib.la_prefill_workspace_size(ctypes.byref(_args(den_out=fake, conv_weight=fake,
+                                                            conv_width=4, **kw)))
+    r256 = lambda n: (n + 255) // 256 * 256
+    rows = 2 * 3 * 4100
+    assert conv - plain == 2 * r256(rows * 64 * esz) + r256(rows * 40 * esz)
+
+
+@pytest.mark.parametrize("maker", ["_bargs", "_xargs"])
+def test_backward_conv_fields_validated(lib, maker):
+    fake = ctypes.c_void_p(0x2000)
+    mk = globals()[maker]
+    entry = lib.la_backward if maker == "_bargs" else lib.la_delta_backward
+    size = lib.la_backward_workspace_size if maker == "_bargs" else \
+        lib.la_delta_backward_workspace_size
+    for bad in (dict(conv_weight=fake, conv_width=4),                     # no dW output
+                dict(conv_weight=fake, conv_width=5, grad_conv_weight=fake),
+                dict(conv_width=2), dict(conv_in=fake), dict(grad_conv_out=fake),
+                dict(grad_conv_weight=fake), dict(grad_conv_in=fake)):
+        a = mk(**bad)
+        assert entry(ctypes.byref(a), None) == _lib.LA_EINVAL, bad
+        assert size(ctypes.byref(a)) == ctypes.c_size_t(-1).value, bad
+    a = mk(N=300)
+    plain = size(ctypes.byref(a))
+    a = mk(N=300, conv_weight=fake, conv_width=3, grad_conv_weight=fake)
+    assert size(ctypes.byref(a)) > plain
 
 
 def test_state_init_rejects_invalid_arguments(lib):
