@@ -69,11 +69,9 @@ def _check(q, k, v, do, gamma, fmap, tol, S0=None, z0=None, dS=None, dz=None, ep
     assert_grad_close(dS0, rS0, sS, tol, "dS_in")
     assert_grad_close(dz0[..., None], rz0[..., None], sz[..., None], tol, "dz_in")
     if q.dtype == torch.float32 and N > 1:
-        # fp32 also meets the plain row-relative metric (N = 1 is the exception:
-        # there the output does not depend on q or k but through eps, and dq,
-        # dk are O(eps) residues of O(1) terms)
-        assert_close(dq, rq, tol, "dq rows")
-        assert_close(dk, rk, tol, "dk rows")
+        # fp32 dv and dS_in also meet the plain row-relative metric (dq and dk
+        # rows cancel exactly in places: the first token's o_0 = v_0 makes
+        # dphi(q_0) a difference of equal terms)
         assert_close(dv, rv, tol, "dv rows")
         assert_close(dS0, rS0, tol, "dS_in", axes=(-2, -1))
 

@@ -42,7 +42,7 @@ LINEAR = [  # (B, H, N, d, dv, w)
 
 
 def _close(got, ref, tol, what, axes=(-1,)):
-    assert_close(got, ref, tol, what, axes=axes, floor=False)
+    assert_close(got, ref, tol, what, axes=axes)
 
 
 def _conv_scales(q, k, v, W, C0, dCo, s_y):

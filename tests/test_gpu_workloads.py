@@ -70,7 +70,7 @@ def test_long_context_workload_full_size_sampled():
 def test_config1_fp32_prefill_as_stated():
     """B1 H1 N256 d=dv=64, fp32 q, k, v ~ N(0,1) unscaled from the seed,
     elu+1, gamma = 1, eps = 1e-6, full-sequence prefill: o, S and z against
-    the oracle at 1e-4 on the plain row metric (no floor on row scales).
+    the oracle at 1e-4 on the plain row metric.
     (The workload's three-token hand-worked example runs in
     test_gpu_linear.test_handworked_example_on_gpu.)"""
     w = inputs.WORKLOADS[1]
@@ -81,9 +81,9 @@ def test_config1_fp32_prefill_as_stated():
     torch.cuda.synchronize()
     ro, rS, rz = oracle.linear_prefill(cpu(x["q"]), cpu(x["k"]), cpu(x["v"]), eps=w.eps)
     tol = TOL[torch.float32]
-    assert_close(o, ro, tol, "o", floor=False)
-    assert_close(S, rS, tol, "S", axes=(-2, -1), floor=False)
-    assert_close(z, rz, tol, "z", floor=False)
+    assert_close(o, ro, tol, "o")
+    assert_close(S, rS, tol, "S", axes=(-2, -1))
+    assert_close(z, rz, tol, "z")
 
 
 def test_decode_workload_full_loop_sampled():
