@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--no-train-delta", action="store_true",
+                    help="skip only the gated-delta training leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -88,6 +90,9 @@ def parse():
                          "--workload as markdown (no GPU needed)")
     ap.add_argument("--cpu-baseline-child", metavar="WIDS", default=None,
                     help=argparse.SUPPRESS)  # internal: the CPU baseline's child process
+    ap.add_argument("--sq-summary", metavar="DIR", default=None,
+                    help="condense rocprofv3 --pmc passes (pass1.. under DIR) of the "
+                         "shader / address-unit counter groups for --workload")
     ap.add_argument("--stats-summary", metavar="DIR", default=None,
                     help="only summarise a rocprofv3 --kernel-trace --stats run "
                          "kept under DIR as markdown (no GPU needed)")
@@ -118,14 +123,18 @@ def copy_probe(torch, mib):
 # benchmark reports a kernel's traffic only while that hash still matches.
 
 CSRC = os.path.join(ROOT, "causal_linear_attention_attn_amd", "csrc")
+_DELTA_SRC = ("la_prefill_delta.hip", "la_delta_common.hpp")
+_DELTA_BWD_SRC = ("la_backward_delta.hip", "la_delta_common.hpp")
 KERNEL_SRC = {
-    "linear_chunk": "la_prefill_linear.hip", "linear_summary": "la_prefill_linear.hip",
-    "linear_scan": "la_prefill_linear.hip", "delta_prep": "la_prefill_delta.hip",
-    "delta_seq": "la_prefill_delta.hip", "linear_decode": "la_decode.hip",
-    "delta_bwd_prep": "la_backward_delta.hip", "delta_bwd_state": "la_backward_delta.hip",
-    "delta_bwd_rev": "la_backward_delta.hip", "delta_bwd_grad": "la_backward_delta.hip",
-    "delta_decode": "la_decode.hip", "linear_bwd_dq": "la_backward_linear.hip",
-    "linear_bwd_dkv": "la_backward_linear.hip", "linear_bwd_rscan": "la_backward_linear.hip",
+    "linear_chunk": ("la_prefill_linear.hip",), "linear_summary": ("la_prefill_linear.hip",),
+    "linear_scan": ("la_prefill_linear.hip",), "delta_prep": _DELTA_SRC,
+    "delta_seq": _DELTA_SRC, "linear_decode": ("la_decode.hip",),
+    "delta_bwd_prep": _DELTA_BWD_SRC, "delta_bwd_state": _DELTA_BWD_SRC,
+    "delta_bwd_rev": _DELTA_BWD_SRC, "delta_bwd_grad": _DELTA_BWD_SRC,
+    "delta_decode": ("la_decode.hip",), "linear_bwd_dq": ("la_backward_linear.hip",),
+    "linear_bwd_dkv": ("la_backward_linear.hip",), "linear_bwd_rscan": ("la_backward_linear.hip",),
+    "conv_qkv": ("la_conv.hip",), "conv_cache": ("la_conv.hip",), "conv_dx": ("la_conv.hip",),
+    "conv_dw": ("la_conv.hip",), "conv_dw_reduce": ("la_conv.hip",),
 }
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_PROBE_MIB = 256
@@ -135,7 +144,7 @@ def kernel_src_hash(kname):
     import hashlib
 
     h = hashlib.sha256()
-    for f in (KERNEL_SRC[kname], "la_common.hpp", "la_internal.hpp"):
+    for f in (*KERNEL_SRC[kname], "la_common.hpp", "la_internal.hpp"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -162,11 +171,18 @@ def library_kernel_name(raw):
     for fn, name in (("chunk_kernel", "linear_chunk"), ("summary_kernel", "linear_summary"),
                      ("scan_kernel", "linear_scan"), ("seq_kernel", "delta_seq"),
                      ("seq2_kernel", "delta_seq"), ("bstate_kernel", "delta_bwd_state"),
-                     ("brev_kernel", "delta_bwd_rev"), ("bgrad_kernel", "delta_bwd_grad")):
+                     ("brev_kernel", "delta_bwd_rev"), ("bgrad_kernel", "delta_bwd_grad"),
+                     ("conv_qkv_kernel", "conv_qkv"), ("conv_cache_kernel", "conv_cache"),
+                     ("conv_dx_kernel", "conv_dx"), ("conv_dw_partial_kernel", "conv_dw"),
+                     ("conv_dw_reduce_kernel", "conv_dw_reduce")):
         if fn in raw:
             return name
-    if "decode_kernel" in raw:
-        delta = "Lb1E" in raw or ", true>" in raw
+    if "decode_kernel" in raw:  # template flags <T, VEC, DELTA, CV>
+        import re
+
+        m = re.search(r"Lb([01])ELb([01])EEEv", raw) or \
+            re.search(r", (true|false), (true|false)>", raw)
+        delta = m is not None and m.group(1) in ("1", "true")
         return "delta_decode" if delta else "linear_decode"
     return None
 
@@ -212,9 +228,14 @@ def pmc_commands(d, wid):
 
 
 def bench_args_for_counters(wid):
+    """The bench.py run a workload's counters come from: its own kernels only
+    (the main workload with its training step, the gated-delta workloads
+    with theirs)."""
     if wid == 3:
-        return "--workload 3 --decode-steps 16"
-    return f"--workload {wid} --steps 5 --warmup 2 --no-decode --no-extra --no-cpu-baseline"
+        return "--workload 3 --decode-steps 16 --no-cpu-baseline"
+    own = {2: " --no-train-delta", 5: ""}.get(wid, " --no-train")
+    return (f"--workload {wid} --steps 5 --warmup 2 --no-decode --no-extra --no-cpu-baseline"
+            + own)
 
 
 def pmc_summary(d, wid):
@@ -266,6 +287,8 @@ def pmc_summary(d, wid):
             a = decode_step_bytes(w)
         if k in ("linear_bwd_dq", "linear_bwd_dkv"):
             a = w.B * w.H * w.N * bwd_bytes_per_head_token(w, k)
+        if k.startswith("delta_bwd_"):
+            a = w.B * w.H * w.N * delta_bwd_bytes_per_head_token(w, k)
         out.append(f"| {k} | {n} | {fk:.0f} | {wk:.0f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
                    f"{(rd + wr) / 1e6:.1f} | {'' if a is None else f'{a / 1e6:.1f}'} |")
         recs.append({"workload": w.name, "kernel": k, "src": kernel_src_hash(k),
@@ -273,6 +296,87 @@ def pmc_summary(d, wid):
     out += ["", "Machine-readable records (bench.py reports `traffic` from these while "
             "the kernel source hash matches):", ""]
     out += [f"<!-- traffic {json.dumps(r)} -->" for r in recs]
+    print("\n".join(out))
+
+
+SQ_PASSES = (
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_MFMA "
+    "SQ_INSTS_SALU SQ_INSTS_VMEM GRBM_GUI_ACTIVE",
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_ANY SQ_WAIT_INST_LDS SQ_WAIT_ANY "
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE",
+    "TA_TA_BUSY_sum TA_BUFFER_READ_WAVEFRONTS_sum TCP_TOTAL_CACHE_ACCESSES_sum "
+    "TCP_TCC_READ_REQ_sum TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
+)
+SIMDS = 1024  # 256 CUs x 4 SIMDs
+XCDS = 8
+
+
+def sq_summary(d, wid):
+    """Markdown table of shader, address-unit and L2 counters per dispatch
+    for the library's kernels of one workload (one rocprofv3 --pmc pass per
+    group of counters, in subdirectories pass1.. of D), with the derived
+    fractions and source-hash records."""
+    from causal_linear_attention_attn_amd import inputs
+
+    w = inputs.WORKLOADS[wid]
+    seen = {}  # (kernel, counter) -> per-dispatch averages of the passes holding it
+    for i in range(1, len(SQ_PASSES) + 1):
+        sub = os.path.join(d, f"pass{i}")
+        if not os.path.isdir(sub):
+            continue
+        rows = _counter_rows(sub)
+        for c in sorted({r["Counter_Name"] for r in rows}):
+            for k, (v, _) in _per_dispatch(rows, c, library_kernel_name).items():
+                seen.setdefault((k, c), []).append(v)
+    names = sorted({c for _, c in seen})
+    vals = {}
+    for (k, c), v in seen.items():
+        vals.setdefault(k, {})[c] = sum(v) / len(v)
+    kernels = sorted(vals)
+    run = f"python3 bench.py {bench_args_for_counters(wid)}"
+    out = [f"# Shader and memory-unit counters per dispatch: {w.name}", "",
+           "Commands (repository root, TMPDIR=/tmp, one pass per counter group):", ""]
+    for i, ctr in enumerate(SQ_PASSES, 1):
+        out.append(f"    rocprofv3 --pmc {ctr} --output-format csv -d {d}/pass{i} -o sq -- {run}")
+    out += [f"    python3 bench.py --sq-summary {d} --workload {wid}", "",
+            "| counter | " + " | ".join(kernels) + " |", "|---|" + "---|" * len(kernels)]
+    for c in names:
+        out.append(f"| {c} | " + " | ".join(f"{vals[k].get(c, float('nan')):.0f}"
+                                            for k in kernels) + " |")
+    out += ["", "Derived (GRBM_GUI_ACTIVE is summed over the 8 XCDs; SQ counters over all "
+            f"{SIMDS} SIMDs):", ""]
+    recs = []
+    for k in kernels:
+        v = vals[k]
+        cyc = v.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+        parts = []
+        if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+            parts.append(f"matrix-core busy {v['SQ_VALU_MFMA_BUSY_CYCLES'] / SIMDS / cyc:.1%} "
+                         "of the kernel's cycles per SIMD")
+        if "SQ_LDS_BANK_CONFLICT" in v and v.get("SQ_LDS_IDX_ACTIVE"):
+            parts.append(f"LDS bank-conflict cycles {v['SQ_LDS_BANK_CONFLICT'] / v['SQ_LDS_IDX_ACTIVE']:.0%}"
+                         " of LDS-busy cycles")
+        if v.get("SQ_WAVE_CYCLES"):
+            wc = v["SQ_WAVE_CYCLES"]
+            if "SQ_WAIT_ANY" in v:
+                parts.append(f"waves waiting {v['SQ_WAIT_ANY'] / wc:.0%}")
+            if "SQ_ACTIVE_INST_ANY" in v:
+                parts.append(f"issuing {v['SQ_ACTIVE_INST_ANY'] / wc:.0%}")
+            if "SQ_ACTIVE_INST_VALU" in v:
+                parts.append(f"VALU {v['SQ_ACTIVE_INST_VALU'] / wc:.0%} of wave cycles")
+        if cyc and "TA_TA_BUSY_sum" in v:
+            parts.append(f"address units busy {v['TA_TA_BUSY_sum'] / 256 / cyc:.0%} of the "
+                         "kernel's cycles per CU")
+        if v.get("TCC_HIT_sum") is not None and v.get("TCC_MISS_sum") is not None:
+            tot = v["TCC_HIT_sum"] + v["TCC_MISS_sum"]
+            if tot:
+                parts.append(f"L2 hit rate {v['TCC_HIT_sum'] / tot:.0%}")
+        if parts:
+            out.append(f"- {k}: " + "; ".join(parts) + ".")
+        recs.append({"workload": w.name, "kernel": k, "src": kernel_src_hash(k),
+                     "counters": {c: v[c] for c in sorted(v)}})
+    out += ["", "Machine-readable records (per dispatch, with the kernel source hash):", ""]
+    out += [f"<!-- counters {json.dumps(r)} -->" for r in recs]
     print("\n".join(out))
 
 
@@ -354,17 +458,18 @@ def bytes_per_head_token(w):
 
 
 def flops_per_head_token(w):
-    """Matrix flops of the chunk form as the kernels compute it, per
-    head-token.  LINEAR (chunk C): state read 2 d dv, state update 2 d dv,
-    scores and weighted sum 2 C (d + dv).  DELTA (chunk C): K S, Q S,
-    K^T U 6 d dv; T Y and R Y 2 C dv (lower halves); K K^T and Q K^T 2 C d
-    (lower halves); R = P T about (2/3) C^2."""
+    """Matrix flops of the chunk form per head-token, as the workload
+    table counts them.  LINEAR (chunk C): state read 2 d dv, state update
+    2 d dv, scores and weighted sum 2 C (d + dv).  DELTA (chunk C): the
+    three state products (K S, Q S, the update) 6 d dv, the chunk-local
+    products 2 C (3 d + 2 dv) and the triangular inverse C^2 / 3 (full
+    tiles counted: 181 589 at d = dv = 128, C = 64)."""
     d, dv = w.d, w.dv
     if w.rule == "linear":
         C = LINEAR_CHUNK
         return 4 * d * dv + 2 * C * (d + dv)
     C = DELTA_CHUNK
-    return 6 * d * dv + 2 * C * dv + 2 * C * d + (2 * C * C) // 3
+    return 6 * d * dv + 2 * C * (3 * d + 2 * dv) + (C * C) // 3
 
 
 def make_step(la, torch, w, x):
@@ -827,6 +932,9 @@ def main():
     if args.stats_summary:
         stats_summary(args.stats_summary)
         return
+    if args.sq_summary:
+        sq_summary(args.sq_summary, args.workload)
+        return
     if args.cpu_baseline_child:
         cpu_baseline_child([int(i) for i in args.cpu_baseline_child.split(",")])
         return
@@ -893,8 +1001,9 @@ def main():
     if not args.no_train and w.rule == "linear" and w.decay in ("none", "per_head") \
             and not w.conv:
         line["train"] = bench_train(la, lib, torch, w, max(10, args.steps // 4), 5)
-    if not args.no_train:
-        wd = inputs.WORKLOADS[5]
+    if not args.no_train and not args.no_train_delta and \
+            (w.rule == "delta" or args.workload == 2):
+        wd = w if w.rule == "delta" else inputs.WORKLOADS[5]
         line["train_delta"] = bench_train_delta(la, lib, torch, wd, max(10, args.steps // 10), 3)
     if not args.no_extra:
         extra = {}
