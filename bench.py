@@ -38,6 +38,10 @@ graph.  Alongside:
                 backward kernels' times, and the dominant backward kernel
                 against HBM peak (its algorithmic bytes: q, k, v, o, dL/do
                 and the denominators read once, its gradients written once);
+  train_delta   a training step of the gated delta-rule workload: the
+                prefill, then la_delta_backward (dq, dk, dv, dg) for a
+                seeded dL/do, with the backward kernels' times and the
+                dominant one against HBM peak;
   cpu_baseline  the fp64 oracle on the host cores for the main workload and
                 (in `decode` and `workloads`) the decode loop, the
                 long-context prefill and the gated delta prefill: a
@@ -538,6 +542,8 @@ def time_graph(torch, step, steps, warmup, latency=False):
     g_rem = _capture(torch, step, rem) if rem else None
     for _ in range(max(1, warmup // n)):
         g.replay()
+    if g_rem is not None:  # a graph's first replay also uploads it
+        g_rem.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps // n):

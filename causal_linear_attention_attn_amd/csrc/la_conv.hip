@@ -1,4 +1,6 @@
-// Short causal convolution of q, k and v ahead of the gated DELTA rule.
+// Short causal convolution of q, k and v as a pass of its own (ahead of the
+// gated DELTA rule, and of the LINEAR rule's training forward), and its
+// backward.
 //
 // "What Is Linear Attention?" section 5.4 puts a short convolution over the
 // most recent tokens in front of the linear layer (beside the decay, the
@@ -7,11 +9,12 @@
 // with filter taps W[h][j][c], tap w-1 on the current token:
 //     y_t[c] = sum_{j=0..w-1} W[h][j][c] x_(t-(w-1)+j)[c]
 // where tokens before the sequence come from the conv cache (rows oldest
-// first) or are zero without one.  The LINEAR rule fuses this into its
+// first) or are zero without one.  The LINEAR prefill fuses this into its
 // chunk loads; the delta rule reads q, k and v in two kernels (the
 // preparation pass and the sequential pass, which stages them differently),
-// so here the convolved q, k, v are written once, in the input precision,
-// to the workspace, and the rule runs on those copies.  The sums are taken
+// and the LINEAR training forward hands the convolved inputs on to its
+// backward, so for those the convolved q, k, v are written once, in the
+// input precision, to the workspace, and the rule runs on those copies.  The sums are taken
 // in fp32 in tap order and rounded once, as the matrix cores would take
 // them.
 //

@@ -150,9 +150,11 @@ typedef struct la_prefill_args {
                         reads them).  DELTA: must be NULL. */
   void *workspace;   /* device scratch of workspace_bytes, caller-owned;
                         may be NULL when la_prefill_workspace_size() is 0.
-                        DELTA: 16-byte aligned (else LA_EINVAL).  LINEAR:
-                        4-byte aligned; 16-byte alignment with d % 4 == 0
-                        lets the kernels move it with vector accesses. */
+                        DELTA, and LINEAR with den_out and conv_weight
+                        together: 16-byte aligned (else LA_EINVAL).  Other
+                        LINEAR calls: 4-byte aligned; 16-byte alignment with
+                        d % 4 == 0 lets the kernels move it with vector
+                        accesses. */
   size_t workspace_bytes;
 } la_prefill_args;
 
@@ -221,7 +223,8 @@ typedef struct la_backward_args {
   void *grad_v;      /* [B,H,N,dv] */
   float *grad_S_in;  /* [B,H,d,dv] dL/d(initial state); NULL = not written */
   float *grad_z_in;  /* [B,H,d]; NULL = not written */
-  void *workspace;   /* device scratch of workspace_bytes, caller-owned */
+  void *workspace;   /* device scratch of workspace_bytes, caller-owned;
+                        16-byte aligned with conv_weight (else LA_EINVAL) */
   size_t workspace_bytes;
   /* Optional (NULL = not used): the workspace of the la_prefill call that
    * produced o and den, left as that call wrote it, with this call's q, k,
@@ -230,7 +233,7 @@ typedef struct la_backward_args {
    * convolved q, k, v), which la_backward then reads (not written) instead
    * of recomputing it.  fwd_workspace_bytes
    * below la_prefill_workspace_size of those arguments: LA_EWORKSPACE; not
-   * 4-byte aligned: LA_EINVAL.  Any other contents give wrong gradients
+   * 4-byte aligned (16-byte with conv_weight): LA_EINVAL.  Any other contents give wrong gradients
    * (not detected).  Ignored when the forward needs no workspace. */
   const void *fwd_workspace;
   size_t fwd_workspace_bytes;
