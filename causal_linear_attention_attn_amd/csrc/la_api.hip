@@ -443,7 +443,6 @@ int check_backward_shape(const la_backward_args *a) {
   const size_t esz = a->dtype == LA_BF16 ? 2 : 4;
   const size_t dmax = a->d > a->dv ? a->d : a->dv;
   if ((size_t)a->N * dmax * esz > kMaxHeadBytes) return LA_EUNSUPPORTED;
-  if (!la::linear_backward_supported(a->d, a->dv, a->dtype == LA_BF16)) return LA_EUNSUPPORTED;
   return check_conv_grads(a->conv_weight, a->conv_width, a->conv_in, a->grad_conv_out,
                           a->grad_conv_weight, a->grad_conv_in);
 }
@@ -454,17 +453,198 @@ size_t backward_ws_bytes(const la::LinearPlan &pl, bool reuse) {
   return (reuse ? 1 : 2) * pl.ws_bytes;
 }
 
+// fp32 with d and dv both above 64 has no tile configuration for the whole
+// value width (the fp32 state tile would not fit the LDS beside the operand
+// tiles), so the rule's backward runs over the value columns [0, 64) and
+// [64, dv) in turn: each half's normaliser column carries that half's share
+// of g.o (the shares add up to the whole), so dq, dk and dL/dz_in are the
+// sums of the halves' results and dv, dL/dS_in their column blocks; the
+// final-normaliser gradient enters the first half only.
+constexpr int kSplitCols = 64;
+bool split_values(int d, int dv, bool bf16) { return !la::linear_backward_supported(d, dv, bf16); }
+
+// Regions (bytes from the start of the rule's part of the workspace) of a
+// split backward: the halves' v, o, dL/do, dv, the second half's dq and dk,
+// S_in, dL/dS_out, dL/dS_in by halves, the second half's dL/dz_in, then
+// state slots for one half at a time.
+struct SplitLayout {
+  size_t v[2], o[2], go[2], gv[2], gq, gk, sin[2], gso[2], gsi[2], gz, slots, total;
+};
+SplitLayout split_layout(int BH, int N, int d, int dv) {
+  SplitLayout L{};
+  const size_t rows = (size_t)BH * N, srows = (size_t)BH * d;
+  const int n[2] = {kSplitCols, dv - kSplitCols};
+  size_t off = 0;
+  auto take = [&](size_t floats) {
+    const size_t at = off;
+    off += round256(floats * sizeof(float));
+    return at;
+  };
+  for (int h = 0; h < 2; ++h) {
+    L.v[h] = take(rows * n[h]);
+    L.o[h] = take(rows * n[h]);
+    L.go[h] = take(rows * n[h]);
+    L.gv[h] = take(rows * n[h]);
+    L.sin[h] = take(srows * n[h]);
+    L.gso[h] = take(srows * n[h]);
+    L.gsi[h] = take(srows * n[h]);
+  }
+  L.gq = take(rows * d);
+  L.gk = take(rows * d);
+  L.gz = take(srows);
+  L.slots = off;
+  size_t slot_bytes = 0;
+  for (int h = 0; h < 2; ++h) {
+    const la::LinearPlan pl = la::plan_linear(BH, N, d, n[h], false, 0);
+    if (pl.nseg > 1 && backward_ws_bytes(pl, false) > slot_bytes)
+      slot_bytes = backward_ws_bytes(pl, false);
+  }
+  L.total = off + slot_bytes;
+  return L;
+}
+
+// Bytes of the rule's part of a backward workspace (state slots, and the
+// halves' buffers when the value columns are split).
+size_t rule_ws_bytes(int BH, int N, int d, int dv, bool bf16, bool fwd) {
+  if (split_values(d, dv, bf16)) return split_layout(BH, N, d, dv).total;
+  const la::LinearPlan plan = la::plan_linear(BH, N, d, dv, bf16, 0);
+  return plan.nseg > 1 ? backward_ws_bytes(plan, plan.nseg > 1 && fwd) : 0;
+}
+
+// One LINEAR-rule backward (no convolution) over tensors of width dv.
+struct RuleBwd {
+  int BH, H, N, d, dv, fmap;
+  bool bf16;
+  const void *q, *k, *v, *o, *dout;
+  const float *den, *gamma, *S_in, *z_in, *dS_out, *dz_out;
+  void *dq, *dk, *dv_;
+  float *dS_in, *dz_in;
+};
+
+// ws: state slots of backward_ws_bytes(plan, fwd_slots given); fwd_slots:
+// the forward's own segment states (same plan), or nullptr to recompute.
+hipError_t rule_backward(const RuleBwd &r, float *ws, const float *fwd_slots, hipStream_t s) {
+  const la::LinearPlan plan = la::plan_linear(r.BH, r.N, r.d, r.dv, r.bf16, 0);
+  const bool reuse = plan.nseg > 1 && fwd_slots != nullptr;
+  const int vec = r.bf16 ? 8 : 4;
+  const bool vec_ok = (r.d % vec == 0) && (r.dv % vec == 0) && aligned16(r.q) &&
+                      aligned16(r.k) && aligned16(r.v) && aligned16(r.o) &&
+                      aligned16(r.dout) && aligned16(r.dq) && aligned16(r.dk) &&
+                      aligned16(r.dv_);
+  float *ws_r = ws ? ws + (reuse ? 0 : plan.ws_bytes / sizeof(float)) : nullptr;
+  const float *ws_f = reuse ? fwd_slots : ws;
+  if (plan.nseg > 1 && !reuse) {  // the forward state entering each segment
+    la::PrefillParams fp{};
+    fp.BH = r.BH;
+    fp.H = r.H;
+    fp.N = r.N;
+    fp.d = r.d;
+    fp.dv = r.dv;
+    fp.fmap = r.fmap;
+    fp.vec_ok = vec_ok;
+    fp.q = r.q;
+    fp.k = r.k;
+    fp.v = r.v;
+    fp.gamma = r.gamma;
+    fp.S_in = r.S_in;
+    fp.z_in = r.z_in;
+    fp.ws = ws;
+    fp.nseg = plan.nseg;
+    fp.nsplit = plan.nsplit;
+    fp.split_len = plan.split_len;
+    fp.slot_vec = (r.d % 4 == 0) && aligned16(ws);
+    fp.seg_len = plan.seg_len;
+    const hipError_t e = la::launch_linear_state_prefix(fp, plan, r.bf16, s);
+    if (e != hipSuccess) return e;
+  }
+  la::BwdParams p{};
+  p.BH = r.BH;
+  p.H = r.H;
+  p.N = r.N;
+  p.d = r.d;
+  p.dv = r.dv;
+  p.fmap = r.fmap;
+  p.vec_ok = vec_ok;
+  p.q = r.q;
+  p.k = r.k;
+  p.v = r.v;
+  p.o = r.o;
+  p.dout = r.dout;
+  p.den = r.den;
+  p.gamma = r.gamma;
+  p.S_in = r.S_in;
+  p.z_in = r.z_in;
+  p.dS_out = r.dS_out;
+  p.dz_out = r.dz_out;
+  p.dq = r.dq;
+  p.dk = r.dk;
+  p.dv_ = r.dv_;
+  p.dS_in = r.dS_in;
+  p.dz_in = r.dz_in;
+  p.ws_f = const_cast<float *>(ws_f);  // read only by the backward kernels
+  p.ws_r = ws_r;
+  p.wrec = plan.nseg > 1 ? plan.wrec : 0;
+  p.nseg = plan.nseg;
+  p.seg_len = plan.seg_len;
+  p.slot_vec = (r.d % 4 == 0) && aligned16(ws_f) && aligned16(ws_r);
+  return la::launch_linear_backward(p, r.bf16, s);
+}
+
+// The fp32 backward over two value halves (see split_values), in the
+// rule's part of the workspace (split_layout).
+hipError_t rule_backward_split(const RuleBwd &r, char *ws, hipStream_t s) {
+  const SplitLayout L = split_layout(r.BH, r.N, r.d, r.dv);
+  const size_t rows = (size_t)r.BH * r.N, srows = (size_t)r.BH * r.d;
+  const int na = kSplitCols;
+  auto at = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
+  hipError_t e = hipSuccess;
+  auto split = [&](const void *src, size_t nrows, const size_t (&dst)[2]) {
+    if (e == hipSuccess)
+      e = la::launch_split_cols(static_cast<const float *>(src), at(dst[0]), at(dst[1]), nrows,
+                                r.dv, na, s);
+  };
+  split(r.v, rows, L.v);
+  split(r.o, rows, L.o);
+  split(r.dout, rows, L.go);
+  if (r.S_in) split(r.S_in, srows, L.sin);
+  if (r.dS_out) split(r.dS_out, srows, L.gso);
+  for (int h = 0; h < 2 && e == hipSuccess; ++h) {
+    RuleBwd x = r;
+    x.dv = h ? r.dv - na : na;
+    x.v = at(L.v[h]);
+    x.o = at(L.o[h]);
+    x.dout = at(L.go[h]);
+    x.S_in = r.S_in ? at(L.sin[h]) : nullptr;
+    x.dS_out = r.dS_out ? at(L.gso[h]) : nullptr;
+    x.dz_out = h ? nullptr : r.dz_out;
+    x.dq = h ? at(L.gq) : r.dq;
+    x.dk = h ? at(L.gk) : r.dk;
+    x.dv_ = at(L.gv[h]);
+    x.dS_in = r.dS_in ? at(L.gsi[h]) : nullptr;
+    x.dz_in = r.dz_in ? (h ? at(L.gz) : r.dz_in) : nullptr;
+    e = rule_backward(x, at(L.slots), nullptr, s);
+  }
+  if (e == hipSuccess) e = la::launch_add_into(static_cast<float *>(r.dq), at(L.gq), rows * r.d, s);
+  if (e == hipSuccess) e = la::launch_add_into(static_cast<float *>(r.dk), at(L.gk), rows * r.d, s);
+  if (e == hipSuccess)
+    e = la::launch_join_cols(static_cast<float *>(r.dv_), at(L.gv[0]), at(L.gv[1]), rows, r.dv,
+                             na, s);
+  if (e == hipSuccess && r.dS_in)
+    e = la::launch_join_cols(r.dS_in, at(L.gsi[0]), at(L.gsi[1]), srows, r.dv, na, s);
+  if (e == hipSuccess && r.dz_in) e = la::launch_add_into(r.dz_in, at(L.gz), srows, s);
+  return e;
+}
+
 }  // namespace
 
 size_t la_backward_workspace_size(const la_backward_args *a) {
   if (check_backward_shape(a) != LA_OK) return (size_t)-1;
   const int BH = a->B * a->H;
   if (BH == 0 || a->N == 0) return 0;
-  const la::LinearPlan plan = la::plan_linear(BH, a->N, a->d, a->dv, a->dtype == LA_BF16, 0);
-  const bool fwd = a->fwd_workspace != nullptr;
-  return conv_bwd_layout(BH, a->N, a->d, a->dv, a->dtype == LA_BF16 ? 2 : 4, a->conv_width,
+  const bool bf16 = a->dtype == LA_BF16, fwd = a->fwd_workspace != nullptr;
+  return conv_bwd_layout(BH, a->N, a->d, a->dv, bf16 ? 2 : 4, a->conv_width,
                          a->conv_weight != nullptr, fwd,
-                         plan.nseg > 1 ? backward_ws_bytes(plan, fwd) : 0)
+                         rule_ws_bytes(BH, a->N, a->d, a->dv, bf16, fwd))
       .total;
 }
 
@@ -496,14 +676,17 @@ int la_backward(const la_backward_args *a, void *stream) {
   const size_t esz = bf16_io ? 2 : 4, rows = (size_t)BH * a->N;
   const bool conv = a->conv_weight != nullptr;
   const la::LinearPlan plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io, 0);
+  const bool split = split_values(a->d, a->dv, bf16_io);
   // the forward's own records, when given (same plan, same slots); else
   // this call's workspace, filled below
-  const bool reuse = plan.nseg > 1 && a->fwd_workspace != nullptr;
+  const bool reuse = !split && plan.nseg > 1 && a->fwd_workspace != nullptr;
   const BwdLayout L =
-      conv_bwd_layout(BH, a->N, a->d, a->dv, esz, a->conv_width, conv,
-                      a->fwd_workspace != nullptr, plan.nseg > 1 ? backward_ws_bytes(plan, reuse) : 0);
+      conv_bwd_layout(BH, a->N, a->d, a->dv, esz, a->conv_width, conv, a->fwd_workspace != nullptr,
+                      rule_ws_bytes(BH, a->N, a->d, a->dv, bf16_io, a->fwd_workspace != nullptr));
   if (L.total > 0 && (!a->workspace || a->workspace_bytes < L.total)) return LA_EWORKSPACE;
-  if (conv && !aligned16(a->workspace)) return LA_EINVAL;
+  if (L.total > 0 && (conv ? !aligned16(a->workspace)
+                           : (reinterpret_cast<uintptr_t>(a->workspace) & 3u) != 0))
+    return LA_EINVAL;
   // the forward's workspace: [convolved q, k, v (with a convolution) | state slots]
   const size_t fwd_copies = conv ? qkv_copy_bytes(rows, a->d, a->dv, esz) : 0;
   if (a->fwd_workspace && (conv || plan.nseg > 1)) {
@@ -534,71 +717,41 @@ int la_backward(const la_backward_args *a, void *stream) {
     }
     qkv_regions(base + L.grads, rows, a->d, esz, &gq, &gk, &gv);
   }
-  const int vec = bf16_io ? 8 : 4;
-  const bool vec_ok = (a->d % vec == 0) && (a->dv % vec == 0) && aligned16(q) &&
-                      aligned16(k) && aligned16(v) && aligned16(a->o) &&
-                      aligned16(a->grad_o) && aligned16(gq) && aligned16(gk) && aligned16(gv);
-  float *ws_own = base ? reinterpret_cast<float *>(base + L.slots) : nullptr;
-  float *ws_r = ws_own ? ws_own + (reuse ? 0 : plan.ws_bytes / sizeof(float)) : nullptr;
-  const float *ws_f =
-      reuse ? reinterpret_cast<const float *>(static_cast<const char *>(a->fwd_workspace) +
-                                              fwd_copies)
-            : ws_own;
-  if (plan.nseg > 1 && !reuse) {  // the forward state entering each segment
-    la::PrefillParams fp{};
-    fp.BH = BH;
-    fp.H = a->H;
-    fp.N = a->N;
-    fp.d = a->d;
-    fp.dv = a->dv;
-    fp.fmap = a->fmap == LA_FMAP_ELU1;
-    fp.vec_ok = vec_ok;
-    fp.q = q;
-    fp.k = k;
-    fp.v = v;
-    fp.gamma = a->gamma;
-    fp.S_in = a->S_in;
-    fp.z_in = a->z_in;
-    fp.ws = ws_own;
-    fp.nseg = plan.nseg;
-    fp.nsplit = plan.nsplit;
-    fp.split_len = plan.split_len;
-    fp.slot_vec = (a->d % 4 == 0) && aligned16(ws_own);
-    fp.seg_len = plan.seg_len;
-    const hipError_t e = la::launch_linear_state_prefix(fp, plan, bf16_io, s);
-    if (e != hipSuccess) return LA_EHIP;
+  RuleBwd r{};
+  r.BH = BH;
+  r.H = a->H;
+  r.N = a->N;
+  r.d = a->d;
+  r.dv = a->dv;
+  r.fmap = a->fmap == LA_FMAP_ELU1;
+  r.bf16 = bf16_io;
+  r.q = q;
+  r.k = k;
+  r.v = v;
+  r.o = a->o;
+  r.dout = a->grad_o;
+  r.den = a->den;
+  r.gamma = a->gamma;
+  r.S_in = a->S_in;
+  r.z_in = a->z_in;
+  r.dS_out = a->grad_S_out;
+  r.dz_out = a->grad_z_out;
+  r.dq = gq;
+  r.dk = gk;
+  r.dv_ = gv;
+  r.dS_in = a->grad_S_in;
+  r.dz_in = a->grad_z_in;
+  hipError_t e;
+  if (split) {
+    e = rule_backward_split(r, base + L.slots, s);
+  } else {
+    float *ws_own = base ? reinterpret_cast<float *>(base + L.slots) : nullptr;
+    const float *fwd_slots =
+        reuse ? reinterpret_cast<const float *>(static_cast<const char *>(a->fwd_workspace) +
+                                                fwd_copies)
+              : nullptr;
+    e = rule_backward(r, ws_own, fwd_slots, s);
   }
-  la::BwdParams p{};
-  p.BH = BH;
-  p.H = a->H;
-  p.N = a->N;
-  p.d = a->d;
-  p.dv = a->dv;
-  p.fmap = a->fmap == LA_FMAP_ELU1;
-  p.vec_ok = vec_ok;
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = a->o;
-  p.dout = a->grad_o;
-  p.den = a->den;
-  p.gamma = a->gamma;
-  p.S_in = a->S_in;
-  p.z_in = a->z_in;
-  p.dS_out = a->grad_S_out;
-  p.dz_out = a->grad_z_out;
-  p.dq = gq;
-  p.dk = gk;
-  p.dv_ = gv;
-  p.dS_in = a->grad_S_in;
-  p.dz_in = a->grad_z_in;
-  p.ws_f = const_cast<float *>(ws_f);  // read only by the backward kernels
-  p.ws_r = ws_r;
-  p.wrec = plan.nseg > 1 ? plan.wrec : 0;
-  p.nseg = plan.nseg;
-  p.seg_len = plan.seg_len;
-  p.slot_vec = (a->d % 4 == 0) && aligned16(ws_f) && aligned16(ws_r);
-  hipError_t e = la::launch_linear_backward(p, bf16_io, s);
   if (e != hipSuccess || !conv) return to_status(e);
   return to_status(conv_backward(BH, a->H, a->N, a->d, a->dv, bf16_io, a->conv_weight,
                                  a->conv_width, a->q, a->k, a->v, a->conv_in, gq, gk, gv,

@@ -852,13 +852,82 @@ using BF64x64 = BCfg<float, 64, 64, 32, 4, 1>;
 using BF64x128 = BCfg<float, 64, 128, 32, 4, 1>;
 using BF128x64 = BCfg<float, 128, 64, 32, 4, 1>;
 
+// ---- fp32 with d and dv both above 64: value-column halves ------------------
+// Every gradient is linear in the value columns: splitting them into two
+// halves (each with its own normaliser column carrying that half's share of
+// g.o, which add up to the whole), dq and dk (and dL/dz_in) are the sums of
+// the halves' results, dv and dL/dS_in their column blocks.  These kernels
+// move fp32 rows between the whole width n and the halves [0, na), [na, n).
+__global__ void __launch_bounds__(256) split_cols_kernel(const float *src, float *a, float *b,
+                                                         size_t rows, int n, int na) {
+  const size_t total = rows * (size_t)n;
+  const int nb = n - na;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / (size_t)n;
+    const int c = (int)(i - r * (size_t)n);
+    const float x = src[i];
+    if (c < na)
+      a[r * na + c] = x;
+    else
+      b[r * nb + (c - na)] = x;
+  }
+}
+
+__global__ void __launch_bounds__(256) join_cols_kernel(float *dst, const float *a,
+                                                        const float *b, size_t rows, int n,
+                                                        int na) {
+  const size_t total = rows * (size_t)n;
+  const int nb = n - na;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / (size_t)n;
+    const int c = (int)(i - r * (size_t)n);
+    dst[i] = c < na ? a[r * na + c] : b[r * nb + (c - na)];
+  }
+}
+
+__global__ void __launch_bounds__(256) add_into_kernel(float *dst, const float *src, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] += src[i];
+}
+
+unsigned glue_blocks(size_t n) {
+  const size_t b = (n + 255) / 256;
+  return (unsigned)(b < 4096 ? (b ? b : 1) : 4096);
+}
+
 }  // namespace
+
+hipError_t launch_split_cols(const float *src, float *a, float *b, size_t rows, int n, int na,
+                             hipStream_t s) {
+  if (rows == 0 || n <= na || na <= 0) return hipErrorInvalidValue;
+  return launch_kernel("linear_bwd_split", split_cols_kernel,
+                       dim3(glue_blocks(rows * (size_t)n)), dim3(256), s, src, a, b, rows, n,
+                       na);
+}
+
+hipError_t launch_join_cols(float *dst, const float *a, const float *b, size_t rows, int n,
+                            int na, hipStream_t s) {
+  if (rows == 0 || n <= na || na <= 0) return hipErrorInvalidValue;
+  return launch_kernel("linear_bwd_join", join_cols_kernel,
+                       dim3(glue_blocks(rows * (size_t)n)), dim3(256), s, dst, a, b, rows, n,
+                       na);
+}
+
+hipError_t launch_add_into(float *dst, const float *src, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  return launch_kernel("linear_bwd_add", add_into_kernel, dim3(glue_blocks(n)), dim3(256), s,
+                       dst, src, n);
+}
 
 bool linear_backward_supported(int d, int dv, bool bf16_io) {
   return bf16_io || d <= 64 || dv <= 64;
 }
 
 hipError_t launch_linear_backward(const BwdParams &p, bool bf16_io, hipStream_t s) {
+  if (!linear_backward_supported(p.d, p.dv, bf16_io)) return hipErrorInvalidValue;
   if (!bf16_io) {
     if (p.d <= 64) return p.dv <= 64 ? run_bwd_vk<BF64x64>(p, s) : run_bwd_vk<BF64x128>(p, s);
     return run_bwd_vk<BF128x64>(p, s);

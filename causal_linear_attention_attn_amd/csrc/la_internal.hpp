@@ -181,8 +181,16 @@ bool linear_combo_supported(int d, int dv, bool bf16, bool chan_decay, bool conv
 // segment, in the workspace slots (nothing to do with one segment).
 hipError_t launch_linear_state_prefix(const PrefillParams &p, const LinearPlan &plan,
                                       bool bf16, hipStream_t s);
+// Tile configurations the backward kernels have for these widths (fp32 with
+// d and dv both above 64 has none: the API runs it over value halves).
 bool linear_backward_supported(int d, int dv, bool bf16);
 hipError_t launch_linear_backward(const BwdParams &p, bool bf16, hipStream_t s);
+// fp32 rows [rows, n] <-> column blocks [rows, na] and [rows, n - na]; dst += src.
+hipError_t launch_split_cols(const float *src, float *a, float *b, size_t rows, int n, int na,
+                             hipStream_t s);
+hipError_t launch_join_cols(float *dst, const float *a, const float *b, size_t rows, int n,
+                            int na, hipStream_t s);
+hipError_t launch_add_into(float *dst, const float *src, size_t n, hipStream_t s);
 hipError_t launch_linear_prefill(const PrefillParams &p, const LinearPlan &plan,
                                  bool bf16, hipStream_t s);
 // Gated delta rule: workspace (per-chunk Wt and R tiles) and the two-kernel

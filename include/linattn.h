@@ -199,9 +199,11 @@ int la_prefill_noalloc(const la_prefill_args *args, void *stream);
  * Inputs are the forward's q, k, v, gamma, initial state, its output o and
  * its denominators den (la_prefill's den_out); no per-key-channel decay
  * (alpha); with the forward's convolution (conv_weight below) the
- * gradients are taken through it too.  fp32 inputs take d or dv up to 64 (both above
- * 64: LA_EUNSUPPORTED, the fp32 state tile of the 128 x 128 kernels would
- * not fit the LDS); bf16 any d, dv up to 128. */
+ * gradients are taken through it too.  Any d, dv up to 128 for both
+ * dtypes; fp32 with d and dv both above 64 runs over the value columns
+ * [0, 64) and [64, dv) in turn (the fp32 tiles of the whole width do not
+ * fit the LDS; the gradients are linear in the value columns, so dq, dk and
+ * dL/dz_in are sums over the halves) and then needs a workspace at any N. */
 typedef struct la_backward_args {
   int32_t B, H, N;   /* as the forward */
   int32_t d, dv;
@@ -224,17 +226,20 @@ typedef struct la_backward_args {
   float *grad_S_in;  /* [B,H,d,dv] dL/d(initial state); NULL = not written */
   float *grad_z_in;  /* [B,H,d]; NULL = not written */
   void *workspace;   /* device scratch of workspace_bytes, caller-owned;
-                        16-byte aligned with conv_weight (else LA_EINVAL) */
+                        4-byte aligned, 16-byte with conv_weight (else
+                        LA_EINVAL) */
   size_t workspace_bytes;
   /* Optional (NULL = not used): the workspace of the la_prefill call that
    * produced o and den, left as that call wrote it, with this call's q, k,
    * v, gamma, S_in, z_in, fmap, convolution and no alpha; it holds the
    * state entering each segment of the forward (and with a convolution the
    * convolved q, k, v), which la_backward then reads (not written) instead
-   * of recomputing it.  fwd_workspace_bytes
-   * below la_prefill_workspace_size of those arguments: LA_EWORKSPACE; not
-   * 4-byte aligned (16-byte with conv_weight): LA_EINVAL.  Any other contents give wrong gradients
-   * (not detected).  Ignored when the forward needs no workspace. */
+   * of recomputing it (the fp32 value-half passes recompute their own
+   * segment states and read only the convolved inputs).
+   * fwd_workspace_bytes below la_prefill_workspace_size of those
+   * arguments: LA_EWORKSPACE; not 4-byte aligned (16-byte with
+   * conv_weight): LA_EINVAL.  Any other contents give wrong gradients (not
+   * detected).  Ignored when the forward needs no workspace. */
   const void *fwd_workspace;
   size_t fwd_workspace_bytes;
   /* The forward's short convolution (see la_prefill_args), or NULL: then

@@ -89,9 +89,6 @@ SHAPES = [  # (B, H, N, d, dv)
 @pytest.mark.parametrize("decay", [False, True], ids=["nodecay", "decay"])
 def test_backward_small(shape, dtype, decay):
     B, H, N, d, dv = shape
-    if dtype == torch.float32 and d > 64 and dv > 64:
-        pytest.skip("the fp32 backward takes d or dv <= 64: its 128 x 128 fp32 tiles exceed "
-                    "the LDS (EUNSUPPORTED, tested in test_abi)")
     seed = 1600 + B * 7 + H * 11 + N * 13 + d * 17 + dv * 19 + 3 * (dtype == torch.bfloat16) \
         + 5 * decay
     q, k, v, do, gamma = _case(B, H, N, d, dv, dtype, seed, decay)
@@ -172,3 +169,33 @@ def test_backward_fast_decay(dtype):
     dS = _rand((B, H, d, dv), torch.float32, seed + 6, 0.01)
     dz = _rand((B, H, d), torch.float32, seed + 7, 0.01)
     _check(q, k, v, do, gamma, "elu1", TOL[dtype], S0=S0, z0=z0, dS=dS, dz=dz)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 3000, 128, 128), (1, 1, 2500, 96, 72)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_backward_fp32_wide_value_halves(shape):
+    """fp32 with d and dv both above 64 runs over the value columns [0, 64)
+    and [64, dv): several segments per half, a per-head decay, an initial
+    state and both final-state gradients (the normaliser's only in the
+    first half), against the oracle; with the forward's workspace given the
+    gradients are the same bit for bit (the halves recompute their own
+    segment states)."""
+    B, H, N, d, dv = shape
+    seed = 1800 + d + dv
+    q, k, v, do, gamma = _case(B, H, N, d, dv, torch.float32, seed, True)
+    S0 = _rand((B, H, d, dv), torch.float32, seed + 4, 0.3)
+    z0 = _rand((B, H, d), torch.float32, seed + 5, 0.3).abs() + 1.0
+    dS = _rand((B, H, d, dv), torch.float32, seed + 6, 0.01)
+    dz = _rand((B, H, d), torch.float32, seed + 7, 0.01)
+    _check(q, k, v, do, gamma, "elu1", TOL[torch.float32], S0=S0, z0=z0, dS=dS, dz=dz)
+    ws = torch.empty(max(1, la.workspace_size(q, k, v, gamma=gamma)), dtype=torch.uint8,
+                     device=DEV)
+    den = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    o, _, _ = la.prefill(q, k, v, gamma=gamma, S_in=S0, z_in=z0, den_out=den, workspace=ws,
+                         return_state=False)
+    ref = la.backward(q, k, v, o, den, do, gamma=gamma, S_in=S0, z_in=z0, dS_out=dS, dz_out=dz)
+    got = la.backward(q, k, v, o, den, do, gamma=gamma, S_in=S0, z_in=z0, dS_out=dS, dz_out=dz,
+                      fwd_workspace=ws)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dS_in", "dz_in"), got, ref):
+        assert torch.equal(a, b), name

@@ -67,8 +67,6 @@ def _conv_scales(q, k, v, W, C0, dCo, s_y):
 @pytest.mark.parametrize("reuse", [True, False], ids=["fwd_ws", "recompute"])
 def test_linear_training_through_conv(shape, dtype, reuse):
     B, H, N, d, dv, w = shape
-    if dtype == torch.float32 and d > 64 and dv > 64:
-        pytest.skip("the fp32 backward takes d or dv <= 64")
     wid = 1300 + (B * 7 + H * 11 + N * 13 + d * 17 + dv * 19 + w * 23) % 89 \
         + 3 * (dtype == torch.bfloat16)
     sc = d ** -0.5
