@@ -217,24 +217,29 @@ def feature_map_grad(x, fmap):
     raise ValueError(f"unknown feature map {fmap!r}")
 
 
-def linear_denominators(q, k, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1, z0=None):
+def linear_denominators(q, k, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1, z0=None, alpha=None):
     """den_t = phi(q_t) . z_t + eps of every token (what the output of the
-    LINEAR rule divides by), with z_t = gamma z_(t-1) + phi(k_t).
-    q, k: [B, H, N, d].  Returns [B, H, N] in float64."""
+    LINEAR rule divides by), with z_t = gamma z_(t-1) + phi(k_t), or with a
+    per-channel decay z_t = alpha_t * z_(t-1) + phi(k_t).
+    q, k: [B, H, N, d]; alpha [B, H, N, d] or None.  Returns [B, H, N] in
+    float64."""
+    if alpha is not None and gamma is not None:
+        raise ValueError("gamma and alpha are alternatives")
     q, k = _f64(q), _f64(k)
     B, H, N, d = q.shape
     fq, fk = feature_map(q, fmap), feature_map(k, fmap)
     gam = np.broadcast_to(_gamma_heads(gamma, H)[None, :], (B, H))
+    al = None if alpha is None else _f64(alpha)
     z = np.zeros((B, H, d)) if z0 is None else _f64(z0).copy()
     den = np.empty((B, H, N))
     for t in range(N):
-        z = gam[..., None] * z + fk[:, :, t]
+        z = (gam[..., None] if al is None else al[:, :, t]) * z + fk[:, :, t]
         den[:, :, t] = np.einsum("...r,...r->...", fq[:, :, t], z) + eps
     return den
 
 
 def linear_backward(q, k, v, do, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1,
-                    S0=None, z0=None, dS_N=None, dz_N=None):
+                    S0=None, z0=None, dS_N=None, dz_N=None, alpha=None):
     """Gradients of the LINEAR rule's prefill, token by token in reverse.
 
     The pages motivate parallel training ([WILA] 8, [EAV] 8 and 10) but give
@@ -249,23 +254,34 @@ def linear_backward(q, k, v, do, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1,
         dphi(k_t) = Sh_t v_t + zh_t,   dv_t = Sh_t^T phi(k_t)
         dS_in = gamma Sh_0 (the gradient of the initial state; tokens count
         from 0), dz_in likewise,
-    then dq = dphi(q) * phi'(q), dk = dphi(k) * phi'(k).
+    then dq = dphi(q) * phi'(q), dk = dphi(k) * phi'(k).  With a per-channel
+    decay alpha_t ([EAV] 7.2, GLA) in place of gamma, S_t = diag(alpha_t)
+    S_(t-1) + phi(k_t) v_t^T: the adjoint is carried back through
+    diag(alpha_t) instead of gamma, and
+        dalpha_t[f] = sum_c Sh_t[f, c] S_(t-1)[f, c] + zh_t[f] z_(t-1)[f]
+    (S_(-1) = S0: the state the decay multiplies).
 
-    q, k: [B, H, N, d]; v, do: [B, H, N, dv]; gamma [H] or None; S0, z0 the
-    initial state or None; dS_N [B, H, d, dv], dz_N [B, H, d] the gradient of
-    the loss with respect to the final state, or None.
-    Returns (dq, dk, dv, dS_0, dz_0) in float64.
+    q, k: [B, H, N, d]; v, do: [B, H, N, dv]; gamma [H] or None; alpha [B, H,
+    N, d] or None (not together with gamma); S0, z0 the initial state or
+    None; dS_N [B, H, d, dv], dz_N [B, H, d] the gradient of the loss with
+    respect to the final state, or None.
+    Returns (dq, dk, dv, dS_0, dz_0), and dalpha [B, H, N, d] after them when
+    alpha is given, in float64.
     """
+    if alpha is not None and gamma is not None:
+        raise ValueError("gamma and alpha are alternatives")
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, N, d = q.shape
     dv_ = v.shape[-1]
     fq, fk = feature_map(q, fmap), feature_map(k, fmap)
     gam = np.broadcast_to(_gamma_heads(gamma, H)[None, :], (B, H))
+    al = None if alpha is None else _f64(alpha)
     S = np.zeros((B, H, d, dv_)) if S0 is None else _f64(S0).copy()
     z = np.zeros((B, H, d)) if z0 is None else _f64(z0).copy()
-    Ss, zs = [], []
+    Ss, zs = [S], [z]  # the state before token 0, then after every token
     for t in range(N):  # forward pass, keeping every state
-        _, S, z = linear_step(S, z, fq[:, :, t], fk[:, :, t], v[:, :, t], gam, eps)
+        _, S, z = linear_step(S, z, fq[:, :, t], fk[:, :, t], v[:, :, t],
+                              gam if al is None else al[:, :, t], eps)
         Ss.append(S)
         zs.append(z)
     Sh = np.zeros((B, H, d, dv_)) if dS_N is None else _f64(dS_N).copy()
@@ -273,8 +289,9 @@ def linear_backward(q, k, v, do, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1,
     dfq = np.empty((B, H, N, d))
     dfk = np.empty((B, H, N, d))
     dvv = np.empty((B, H, N, dv_))
+    dal = None if al is None else np.empty((B, H, N, d))
     for t in range(N - 1, -1, -1):
-        St, zt, fqt = Ss[t], zs[t], fq[:, :, t]
+        St, zt, fqt = Ss[t + 1], zs[t + 1], fq[:, :, t]
         num = np.einsum("...r,...rd->...d", fqt, St)
         den = np.einsum("...r,...r->...", fqt, zt) + eps
         g = do[:, :, t]
@@ -285,9 +302,15 @@ def linear_backward(q, k, v, do, *, gamma=None, eps=1e-6, fmap=FMAP_ELU1,
         zh = zh + fqt * dden[..., None]
         dfk[:, :, t] = np.einsum("...rd,...d->...r", Sh, v[:, :, t]) + zh
         dvv[:, :, t] = np.einsum("...rd,...r->...d", Sh, fk[:, :, t])
-        Sh = gam[..., None, None] * Sh
-        zh = gam[..., None] * zh
-    return (dfq * feature_map_grad(q, fmap), dfk * feature_map_grad(k, fmap), dvv, Sh, zh)
+        if al is None:
+            Sh = gam[..., None, None] * Sh
+            zh = gam[..., None] * zh
+        else:
+            dal[:, :, t] = np.einsum("...rd,...rd->...r", Sh, Ss[t]) + zh * zs[t]
+            Sh = al[:, :, t][..., None] * Sh
+            zh = al[:, :, t] * zh
+    out = (dfq * feature_map_grad(q, fmap), dfk * feature_map_grad(k, fmap), dvv, Sh, zh)
+    return out if al is None else out + (dal,)
 
 
 # ---------------------------------------------------------------------------
@@ -410,7 +433,8 @@ def linear_backward_conv(q, k, v, do, conv_weight, *, conv_cache=None, dconv_cac
     k, v, then the convolution's chain rule.  dconv_cache_out: dL/d(the conv
     cache it returns) or None.  Other keywords as linear_backward.  Returns
     (dq, dk, dv, dconv_weight [H, w, 2d+dv], dconv_cache [B, H, w-1, 2d+dv],
-    dS_0, dz_0) in float64."""
+    dS_0, dz_0), and dalpha after them with a per-channel decay, in
+    float64."""
     d = q.shape[-1]
     wq, wk, wv = _conv_split(conv_weight, d)
     cq = ck = cv = None
@@ -419,10 +443,10 @@ def linear_backward_conv(q, k, v, do, conv_weight, *, conv_cache=None, dconv_cac
     yq, _ = short_conv(q, wq, cq)
     yk, _ = short_conv(k, wk, ck)
     yv, _ = short_conv(v, wv, cv)
-    gq, gk, gv, dS0, dz0 = linear_backward(yq, yk, yv, do, **kw)
+    gq, gk, gv, dS0, dz0, *dal = linear_backward(yq, yk, yv, do, **kw)
     dq, dk, dv, dW, dC = _conv_backward_qkv(q, k, v, conv_weight, conv_cache, (gq, gk, gv),
                                             dconv_cache_out)
-    return dq, dk, dv, dW, dC, dS0, dz0
+    return (dq, dk, dv, dW, dC, dS0, dz0, *dal)
 
 
 # ---------------------------------------------------------------------------

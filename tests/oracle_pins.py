@@ -798,6 +798,139 @@ def pin_backward_finite_differences(orc):
         np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
 
 
+def _torch_gla_loss(q, k, v, do, alpha, eps, S0, z0, dS, dz, elu):
+    """As _torch_linear_loss with a per-channel decay alpha [H, N, d]:
+    S_t = diag(alpha_t) S_(t-1) + phi(k_t) v_t^T, z_t = alpha_t z_(t-1) + phi(k_t)."""
+    import torch
+    phi = (lambda x: torch.nn.functional.elu(x) + 1.0) if elu else (lambda x: x)
+    fq, fk = phi(q), phi(k)
+    S, z = S0, z0
+    loss = 0.0
+    for t in range(q.shape[-2]):
+        S = alpha[:, t, :, None] * S + fk[:, t, :, None] * v[:, t, None, :]
+        z = alpha[:, t] * z + fk[:, t]
+        num = torch.einsum("hr,hrd->hd", fq[:, t], S)
+        den = (fq[:, t] * z).sum(-1) + eps
+        loss = loss + ((num / den[:, None]) * do[:, t]).sum()
+    return loss + (S * dS).sum() + (z * dz).sum()
+
+
+def pin_gla_backward_matches_autograd(orc):
+    """With a per-channel decay: dq, dk, dv, the initial-state gradients and
+    dalpha equal torch autograd's through the recurrence (both feature maps,
+    an initial state, a final-state gradient, d != dv)."""
+    import torch
+    rng = np.random.default_rng(54)
+    H, N, d, dv, eps = 2, 8, 3, 4, 1e-2
+    for elu in (True, False):
+        if elu:
+            q, k = rng.normal(size=(H, N, d)), rng.normal(size=(H, N, d))
+        else:
+            q, k = rng.uniform(0.1, 1.0, size=(H, N, d)), rng.uniform(0.1, 1.0, size=(H, N, d))
+        v = rng.normal(size=(H, N, dv))
+        do = rng.normal(size=(H, N, dv))
+        al = rng.uniform(0.3, 1.0, size=(H, N, d))
+        S0 = rng.normal(size=(H, d, dv)) * 0.3
+        z0 = rng.uniform(0.5, 1.0, size=(H, d))
+        dS = rng.normal(size=(H, d, dv))
+        dz = rng.normal(size=(H, d))
+        T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)  # noqa: E731
+        tq, tk, tv, tal, tS0, tz0 = T(q), T(k), T(v), T(al), T(S0), T(z0)
+        loss = _torch_gla_loss(tq, tk, tv, torch.tensor(do), tal, eps, tS0, tz0,
+                               torch.tensor(dS), torch.tensor(dz), elu)
+        loss.backward()
+        fmap = orc.FMAP_ELU1 if elu else orc.FMAP_IDENTITY
+        got = orc.linear_backward(q[None], k[None], v[None], do[None], alpha=al[None], eps=eps,
+                                  fmap=fmap, S0=S0[None], z0=z0[None], dS_N=dS[None],
+                                  dz_N=dz[None])
+        assert len(got) == 6
+        for g, t in zip(got, (tq, tk, tv, tS0, tz0, tal)):
+            np.testing.assert_allclose(g[0], t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def pin_gla_backward_finite_differences(orc):
+    """Central differences of the oracle's own forward with a per-channel
+    decay (loss sum(o * do) + final-state terms) agree with the backward on
+    every entry of alpha, q, k and v."""
+    rng = np.random.default_rng(55)
+    B, H, N, d, dv, eps, h = 1, 1, 5, 3, 2, 1e-3, 1e-6
+    q = rng.normal(size=(B, H, N, d))
+    k = rng.normal(size=(B, H, N, d))
+    v = rng.normal(size=(B, H, N, dv))
+    do = rng.normal(size=(B, H, N, dv))
+    al = rng.uniform(0.2, 1.0, size=(B, H, N, d))
+    dS = rng.normal(size=(B, H, d, dv))
+    dz = rng.normal(size=(B, H, d))
+    dq, dk, dvv, _, _, dal = orc.linear_backward(q, k, v, do, alpha=al, eps=eps, dS_N=dS,
+                                                 dz_N=dz)
+
+    def loss(q_, k_, v_, a_):
+        o, S, z = orc.linear_prefill(q_, k_, v_, alpha=a_, eps=eps)
+        return float(np.sum(o * do) + np.sum(S * dS) + np.sum(z * dz))
+    args = (q, k, v, al)
+    for i, g in enumerate((dq, dk, dvv, dal)):
+        x = args[i]
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            fd[idx] = (loss(*[xp if j == i else a for j, a in enumerate(args)])
+                       - loss(*[xm if j == i else a for j, a in enumerate(args)])) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
+
+
+def pin_gla_backward_uniform_is_gamma(orc):
+    """alpha_t = gamma (every token and channel) gives the per-head rule's
+    gradients, and the sum of dalpha over tokens and channels is dL/dgamma
+    (a central difference of the per-head forward in gamma)."""
+    rng = np.random.default_rng(56)
+    B, H, N, d, dv, eps, h = 1, 2, 7, 3, 4, 1e-2, 1e-6
+    q = rng.normal(size=(B, H, N, d))
+    k = rng.normal(size=(B, H, N, d))
+    v = rng.normal(size=(B, H, N, dv))
+    do = rng.normal(size=(B, H, N, dv))
+    S0 = rng.normal(size=(B, H, d, dv)) * 0.3
+    z0 = rng.uniform(0.5, 1.0, size=(B, H, d))
+    gamma = np.array([0.85, 0.6])
+    al = np.broadcast_to(gamma[None, :, None, None], (B, H, N, d)).copy()
+    kw = dict(eps=eps, S0=S0, z0=z0)
+    want = orc.linear_backward(q, k, v, do, gamma=gamma, **kw)
+    got = orc.linear_backward(q, k, v, do, alpha=al, **kw)
+    for g, w in zip(got[:5], want):
+        np.testing.assert_allclose(g, w, rtol=1e-12, atol=1e-14)
+    for hh in range(H):
+        def loss(gv):
+            gg = gamma.copy()
+            gg[hh] = gv
+            o, _, _ = orc.linear_prefill(q, k, v, gamma=gg, **kw)
+            return float(np.sum(o * do))
+        fd = (loss(gamma[hh] + h) - loss(gamma[hh] - h)) / (2 * h)
+        np.testing.assert_allclose(got[5][0, hh].sum(), fd, rtol=1e-6, atol=1e-9)
+
+
+def pin_gla_denominators_brute_force(orc):
+    """With a per-channel decay: den_t = sum_f phi(q_t)_f (sum_{j<=t}
+    prod_{j<s<=t} alpha_s[f] phi(k_j)_f + prod_{s<=t} alpha_s[f] z0_f) + eps,
+    by explicit loops over tokens and channels."""
+    rng = np.random.default_rng(57)
+    N, d, eps = 6, 3, 1e-2
+    q = rng.normal(size=(N, d))
+    k = rng.normal(size=(N, d))
+    al = rng.uniform(0.3, 1.0, size=(N, d))
+    z0 = rng.uniform(0.1, 1.0, size=d)
+    fq, fk = orc.phi_elu1(q), orc.phi_elu1(k)
+    den = orc.linear_denominators(_bh(q), _bh(k), alpha=_bh(al), eps=eps, z0=_bh(z0))[0, 0]
+    for t in range(N):
+        want = eps
+        for f in range(d):
+            zf = z0[f] * np.prod(al[:t + 1, f])
+            for j in range(t + 1):
+                zf += np.prod(al[j + 1:t + 1, f]) * fk[j, f]
+            want += fq[t, f] * zf
+        assert abs(den[t] - want) < 1e-12 * want
+
+
 def pin_denominators_brute_force(orc):
     """den_t = sum_{j<=t} gamma^(t-j) phi(q_t).phi(k_j) + gamma^(t+1) phi(q_t).z0
     + eps, by explicit double loop; and den_t o_t equals the numerator of

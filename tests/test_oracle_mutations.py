@@ -306,6 +306,22 @@ _cbwd_cache_grad_dropped = _patched(
 for _n in ("_cbwd_tap_mirrored", "_cbwd_weight_from_output", "_cbwd_cache_grad_dropped"):
     globals()[_n].__name__ = _n
 
+# backward with a per-channel decay
+_gbwd_dalpha_after_state = _patched(
+    'dal[:, :, t] = np.einsum("...rd,...rd->...r", Sh, Ss[t]) + zh * zs[t]',
+    'dal[:, :, t] = np.einsum("...rd,...rd->...r", Sh, Ss[t + 1]) + zh * zs[t + 1]')
+_gbwd_dalpha_no_z = _patched(
+    'dal[:, :, t] = np.einsum("...rd,...rd->...r", Sh, Ss[t]) + zh * zs[t]',
+    'dal[:, :, t] = np.einsum("...rd,...rd->...r", Sh, Ss[t])')
+_gbwd_adjoint_next_decay = _patched(
+    "Sh = al[:, :, t][..., None] * Sh", "Sh = al[:, :, min(t + 1, N - 1)][..., None] * Sh")
+_gbwd_den_undecayed = _patched(
+    "z = (gam[..., None] if al is None else al[:, :, t]) * z + fk[:, :, t]",
+    "z = (gam[..., None] if al is None else 1.0) * z + fk[:, :, t]")
+for _n in ("_gbwd_dalpha_after_state", "_gbwd_dalpha_no_z", "_gbwd_adjoint_next_decay",
+           "_gbwd_den_undecayed"):
+    globals()[_n].__name__ = _n
+
 
 MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _exp_everywhere, _decay_off_by_one, _outer_transposed,
@@ -320,7 +336,9 @@ MUTANTS = [_read_before_write, _z_not_decayed, _eps_outside, _no_plus_one,
            _dbwd_adjoint_not_decayed, _dbwd_adjoint_no_projection, _dbwd_dv_without_gate,
            _dbwd_dq_from_previous_state, _dbwd_residual_undecayed, _dbwd_dalpha_no_gate_term,
            _dconv_raw_values, _dconv_decode_raw_query, _dconv_decode_cache_kept,
-           _cbwd_tap_mirrored, _cbwd_weight_from_output, _cbwd_cache_grad_dropped]
+           _cbwd_tap_mirrored, _cbwd_weight_from_output, _cbwd_cache_grad_dropped,
+           _gbwd_dalpha_after_state, _gbwd_dalpha_no_z, _gbwd_adjoint_next_decay,
+           _gbwd_den_undecayed]
 
 
 @pytest.mark.parametrize("mutate", MUTANTS, ids=lambda f: f.__name__.strip("_"))
