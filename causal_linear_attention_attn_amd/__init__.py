@@ -204,7 +204,7 @@ def _conv_grads(a, conv_weight, conv_cache, dconv_cache_out, conv_cache_grad, q,
 def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=None,
              dS_out=None, dz_out=None, state_grad=True, workspace=None,
              fwd_workspace=None, conv_weight=None, conv_cache=None, dconv_cache_out=None,
-             conv_cache_grad=True):
+             conv_cache_grad=True, alpha=None):
     """Gradients of a LINEAR prefill (see la_backward): q, k [B,H,N,d], v, o,
     do [B,H,N,dv] (dtype of q), den [B,H,N] fp32 from prefill(den_out=...);
     gamma, S_in, z_in as in the forward; dS_out [B,H,d,dv], dz_out [B,H,d]
@@ -213,12 +213,15 @@ def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=No
     workspace=, same inputs), whose segment states are then reused.
     conv_weight, conv_cache: the forward's short convolution (q, k, v raw);
     dconv_cache_out: dL/d(the conv cache it returned), or None.
+    alpha: the forward's per-key-channel decay [B,H,N,d] fp32 (instead of
+    gamma), or None.
     Returns (dq, dk, dv, dS_in, dz_in); the last two are None unless
     state_grad; with a convolution also (dconv_weight, dconv_cache) (the
-    latter None unless conv_cache_grad and w > 1)."""
+    latter None unless conv_cache_grad and w > 1); with alpha, dalpha
+    [B,H,N,d] fp32 last."""
     _need_gpu(q, k, v, o, den, do, gamma, S_in, z_in, dS_out, dz_out, workspace, fwd_workspace,
-              conv_weight, conv_cache, dconv_cache_out)
-    _need_f32(den, gamma, S_in, z_in, dS_out, dz_out, conv_weight)
+              conv_weight, conv_cache, dconv_cache_out, alpha)
+    _need_f32(den, gamma, S_in, z_in, dS_out, dz_out, conv_weight, alpha)
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,H,N,d] and v [B,H,N,dv]")
     if o.shape != v.shape or do.shape != v.shape or tuple(den.shape) != tuple(q.shape[:3]):
@@ -241,6 +244,12 @@ def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=No
     a.grad_S_out, a.grad_z_out = _ptr(dS_out), _ptr(dz_out)
     a.grad_q, a.grad_k, a.grad_v = _ptr(dq), _ptr(dk), _ptr(dvv)
     a.grad_S_in, a.grad_z_in = _ptr(dS_in), _ptr(dz_in)
+    dal = None
+    if alpha is not None:
+        if tuple(alpha.shape) != tuple(q.shape):
+            raise ValueError("alpha must be [B,H,N,d]")
+        dal = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        a.alpha, a.grad_alpha = _ptr(alpha), _ptr(dal)
     dW, dC = _conv_grads(a, conv_weight, conv_cache, dconv_cache_out, conv_cache_grad, q, H, d,
                          dv, (B, H))
     if fwd_workspace is not None:
@@ -256,9 +265,10 @@ def backward(q, k, v, o, den, do, *, fmap="elu1", gamma=None, S_in=None, z_in=No
         a.workspace = _ptr(workspace)
         a.workspace_bytes = workspace.numel() * workspace.element_size()
     _lib.check(lib.la_backward(ctypes.byref(a), _stream()), "la_backward")
+    out = (dq, dk, dvv, dS_in, dz_in)
     if conv_weight is not None:
-        return dq, dk, dvv, dS_in, dz_in, dW, dC
-    return dq, dk, dvv, dS_in, dz_in
+        out += (dW, dC)
+    return out + (dal,) if alpha is not None else out
 
 
 def delta_backward_workspace_size(q, k, v, conv_weight=None):

@@ -12,7 +12,7 @@ NOALLOC_SCRATCH_BYTES = 128 << 20  # LA_NOALLOC_SCRATCH_BYTES
 LA_F32, LA_BF16 = 0, 1
 LA_FMAP_IDENTITY, LA_FMAP_ELU1 = 0, 1
 LA_RULE_LINEAR, LA_RULE_DELTA = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 # Every symbol include/linattn.h declares.
 EXPORTS = ("la_prefill_workspace_size", "la_prefill", "la_prefill_noalloc", "la_decode_step",
@@ -49,6 +49,7 @@ class BackwardArgs(ctypes.Structure):
         ("fwd_workspace", _ptr), ("fwd_workspace_bytes", _size),
         ("conv_weight", _ptr), ("conv_width", _i32), ("conv_in", _ptr), ("grad_conv_out", _ptr),
         ("grad_conv_weight", _ptr), ("grad_conv_in", _ptr),
+        ("alpha", _ptr), ("grad_alpha", _ptr),
     ]
 
 

@@ -203,7 +203,7 @@ bool overlap(const void *a, const void *b, size_t n) {
 
 extern "C" {
 
-int32_t la_abi_version(void) { return 6; }
+int32_t la_abi_version(void) { return 7; }
 
 const char *la_status_str(int s) {
   switch (s) {
@@ -240,8 +240,6 @@ int la_prefill(const la_prefill_args *a, void *stream) {
       return LA_EINVAL;
     // one head's per-channel decay (fp32) must be addressable with 32-bit offsets
     if (a->alpha && (size_t)a->N * a->d * 4 > kMaxHeadBytes) return LA_EUNSUPPORTED;
-    // denominators are written for the rule the backward covers
-    if (a->den_out && a->alpha) return LA_EUNSUPPORTED;
   } else {
     if (!a->g && BH > 0 && a->N > 0) return LA_EINVAL;
     if (a->gamma || a->z_in || a->z_out || a->den_out) return LA_EINVAL;
@@ -443,6 +441,14 @@ int check_backward_shape(const la_backward_args *a) {
   const size_t esz = a->dtype == LA_BF16 ? 2 : 4;
   const size_t dmax = a->d > a->dv ? a->d : a->dv;
   if ((size_t)a->N * dmax * esz > kMaxHeadBytes) return LA_EUNSUPPORTED;
+  if (a->alpha) {  // per-key-channel decay (GLA)
+    if (a->gamma) return LA_EINVAL;
+    if (!la::linear_backward_channel_supported(a->d, a->dv, a->dtype == LA_BF16))
+      return LA_EUNSUPPORTED;
+    if ((size_t)a->N * a->d * 4 > kMaxHeadBytes) return LA_EUNSUPPORTED;
+  } else if (a->grad_alpha) {
+    return LA_EINVAL;
+  }
   return check_conv_grads(a->conv_weight, a->conv_width, a->conv_in, a->grad_conv_out,
                           a->grad_conv_weight, a->grad_conv_in);
 }
@@ -495,7 +501,7 @@ SplitLayout split_layout(int BH, int N, int d, int dv) {
   L.slots = off;
   size_t slot_bytes = 0;
   for (int h = 0; h < 2; ++h) {
-    const la::LinearPlan pl = la::plan_linear(BH, N, d, n[h], false, 0);
+    const la::LinearPlan pl = la::plan_linear(BH, N, d, n[h], false, 0);  // (no decay: fp32)
     if (pl.nseg > 1 && backward_ws_bytes(pl, false) > slot_bytes)
       slot_bytes = backward_ws_bytes(pl, false);
   }
@@ -503,12 +509,30 @@ SplitLayout split_layout(int BH, int N, int d, int dv) {
   return L;
 }
 
-// Bytes of the rule's part of a backward workspace (state slots, and the
-// halves' buffers when the value columns are split).
-size_t rule_ws_bytes(int BH, int N, int d, int dv, bool bf16, bool fwd) {
+// With a per-channel decay, after the state slots: phi(q) . dphi(q) per
+// token and channel (fp32 [BH, N, d]) and the forward state after every
+// chunk (slot records, [BH, nchunks]).
+struct ChanBwdLayout {
+  size_t ux, chs, total;
+};
+ChanBwdLayout chan_bwd_layout(int BH, int N, int d, int dv) {
+  ChanBwdLayout L{};
+  const size_t nch = ((size_t)N + la::kChanBwdChunk - 1) / la::kChanBwdChunk;
+  const size_t wrec = (size_t)d * dv + 2 * (size_t)d;
+  L.ux = 0;
+  L.chs = round256((size_t)BH * N * d * sizeof(float));
+  L.total = L.chs + round256((size_t)BH * nch * wrec * sizeof(float));
+  return L;
+}
+
+// Bytes of the rule's part of a backward workspace (state slots, the
+// per-channel decay's buffers, and the halves' buffers when the value
+// columns are split).
+size_t rule_ws_bytes(int BH, int N, int d, int dv, bool bf16, bool fwd, bool chan) {
   if (split_values(d, dv, bf16)) return split_layout(BH, N, d, dv).total;
-  const la::LinearPlan plan = la::plan_linear(BH, N, d, dv, bf16, 0);
-  return plan.nseg > 1 ? backward_ws_bytes(plan, plan.nseg > 1 && fwd) : 0;
+  const la::LinearPlan plan = la::plan_linear(BH, N, d, dv, bf16, 0, chan);
+  const size_t slots = plan.nseg > 1 ? backward_ws_bytes(plan, fwd) : 0;
+  return chan ? round256(slots) + chan_bwd_layout(BH, N, d, dv).total : slots;
 }
 
 // One LINEAR-rule backward (no convolution) over tensors of width dv.
@@ -516,16 +540,20 @@ struct RuleBwd {
   int BH, H, N, d, dv, fmap;
   bool bf16;
   const void *q, *k, *v, *o, *dout;
-  const float *den, *gamma, *S_in, *z_in, *dS_out, *dz_out;
+  const float *den, *gamma, *S_in, *z_in, *dS_out, *dz_out, *alpha;
   void *dq, *dk, *dv_;
-  float *dS_in, *dz_in;
+  float *dS_in, *dz_in, *dalpha;
 };
 
-// ws: state slots of backward_ws_bytes(plan, fwd_slots given); fwd_slots:
-// the forward's own segment states (same plan), or nullptr to recompute.
-hipError_t rule_backward(const RuleBwd &r, float *ws, const float *fwd_slots, hipStream_t s) {
-  const la::LinearPlan plan = la::plan_linear(r.BH, r.N, r.d, r.dv, r.bf16, 0);
+// wsb: the rule's part of the workspace (rule_ws_bytes: state slots of
+// backward_ws_bytes(plan, fwd_slots given), then the per-channel decay's
+// buffers); fwd_slots: the forward's own segment states (same plan), or
+// nullptr to recompute.
+hipError_t rule_backward(const RuleBwd &r, char *wsb, const float *fwd_slots, hipStream_t s) {
+  const bool chan = r.alpha != nullptr;
+  const la::LinearPlan plan = la::plan_linear(r.BH, r.N, r.d, r.dv, r.bf16, 0, chan);
   const bool reuse = plan.nseg > 1 && fwd_slots != nullptr;
+  float *ws = plan.nseg > 1 ? reinterpret_cast<float *>(wsb) : nullptr;
   const int vec = r.bf16 ? 8 : 4;
   const bool vec_ok = (r.d % vec == 0) && (r.dv % vec == 0) && aligned16(r.q) &&
                       aligned16(r.k) && aligned16(r.v) && aligned16(r.o) &&
@@ -546,6 +574,7 @@ hipError_t rule_backward(const RuleBwd &r, float *ws, const float *fwd_slots, hi
     fp.k = r.k;
     fp.v = r.v;
     fp.gamma = r.gamma;
+    fp.alpha = r.alpha;
     fp.S_in = r.S_in;
     fp.z_in = r.z_in;
     fp.ws = ws;
@@ -583,10 +612,19 @@ hipError_t rule_backward(const RuleBwd &r, float *ws, const float *fwd_slots, hi
   p.dz_in = r.dz_in;
   p.ws_f = const_cast<float *>(ws_f);  // read only by the backward kernels
   p.ws_r = ws_r;
-  p.wrec = plan.nseg > 1 ? plan.wrec : 0;
+  p.wrec = plan.wrec;  // (slot records; also the per-chunk states with alpha)
   p.nseg = plan.nseg;
   p.seg_len = plan.seg_len;
   p.slot_vec = (r.d % 4 == 0) && aligned16(ws_f) && aligned16(ws_r);
+  if (chan) {
+    const size_t slots = plan.nseg > 1 ? backward_ws_bytes(plan, reuse) : 0;
+    char *cw = wsb + round256(slots);
+    const ChanBwdLayout C = chan_bwd_layout(r.BH, r.N, r.d, r.dv);
+    p.alpha = r.alpha;
+    p.dalpha = r.dalpha;
+    p.ux = reinterpret_cast<float *>(cw + C.ux);
+    p.chs = reinterpret_cast<float *>(cw + C.chs);
+  }
   return la::launch_linear_backward(p, r.bf16, s);
 }
 
@@ -622,7 +660,7 @@ hipError_t rule_backward_split(const RuleBwd &r, char *ws, hipStream_t s) {
     x.dv_ = at(L.gv[h]);
     x.dS_in = r.dS_in ? at(L.gsi[h]) : nullptr;
     x.dz_in = r.dz_in ? (h ? at(L.gz) : r.dz_in) : nullptr;
-    e = rule_backward(x, at(L.slots), nullptr, s);
+    e = rule_backward(x, ws + L.slots, nullptr, s);
   }
   if (e == hipSuccess) e = la::launch_add_into(static_cast<float *>(r.dq), at(L.gq), rows * r.d, s);
   if (e == hipSuccess) e = la::launch_add_into(static_cast<float *>(r.dk), at(L.gk), rows * r.d, s);
@@ -644,7 +682,7 @@ size_t la_backward_workspace_size(const la_backward_args *a) {
   const bool bf16 = a->dtype == LA_BF16, fwd = a->fwd_workspace != nullptr;
   return conv_bwd_layout(BH, a->N, a->d, a->dv, bf16 ? 2 : 4, a->conv_width,
                          a->conv_weight != nullptr, fwd,
-                         rule_ws_bytes(BH, a->N, a->d, a->dv, bf16, fwd))
+                         rule_ws_bytes(BH, a->N, a->d, a->dv, bf16, fwd, a->alpha != nullptr))
       .total;
 }
 
@@ -654,7 +692,7 @@ int la_backward(const la_backward_args *a, void *stream) {
   const int BH = a->B * a->H;
   if (BH > 0 && a->N > 0 &&
       (!a->q || !a->k || !a->v || !a->o || !a->den || !a->grad_o || !a->grad_q ||
-       !a->grad_k || !a->grad_v))
+       !a->grad_k || !a->grad_v || (a->alpha && !a->grad_alpha)))
     return LA_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (BH == 0) return LA_OK;
@@ -675,17 +713,19 @@ int la_backward(const la_backward_args *a, void *stream) {
   const bool bf16_io = a->dtype == LA_BF16;
   const size_t esz = bf16_io ? 2 : 4, rows = (size_t)BH * a->N;
   const bool conv = a->conv_weight != nullptr;
-  const la::LinearPlan plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io, 0);
+  const bool chan = a->alpha != nullptr;
+  const la::LinearPlan plan = la::plan_linear(BH, a->N, a->d, a->dv, bf16_io, 0, chan);
   const bool split = split_values(a->d, a->dv, bf16_io);
   // the forward's own records, when given (same plan, same slots); else
   // this call's workspace, filled below
   const bool reuse = !split && plan.nseg > 1 && a->fwd_workspace != nullptr;
   const BwdLayout L =
       conv_bwd_layout(BH, a->N, a->d, a->dv, esz, a->conv_width, conv, a->fwd_workspace != nullptr,
-                      rule_ws_bytes(BH, a->N, a->d, a->dv, bf16_io, a->fwd_workspace != nullptr));
+                      rule_ws_bytes(BH, a->N, a->d, a->dv, bf16_io, a->fwd_workspace != nullptr,
+                                    chan));
   if (L.total > 0 && (!a->workspace || a->workspace_bytes < L.total)) return LA_EWORKSPACE;
-  if (L.total > 0 && (conv ? !aligned16(a->workspace)
-                           : (reinterpret_cast<uintptr_t>(a->workspace) & 3u) != 0))
+  if (L.total > 0 && ((conv || chan) ? !aligned16(a->workspace)
+                                    : (reinterpret_cast<uintptr_t>(a->workspace) & 3u) != 0))
     return LA_EINVAL;
   // the forward's workspace: [convolved q, k, v (with a convolution) | state slots]
   const size_t fwd_copies = conv ? qkv_copy_bytes(rows, a->d, a->dv, esz) : 0;
@@ -741,16 +781,17 @@ int la_backward(const la_backward_args *a, void *stream) {
   r.dv_ = gv;
   r.dS_in = a->grad_S_in;
   r.dz_in = a->grad_z_in;
+  r.alpha = a->alpha;
+  r.dalpha = a->grad_alpha;
   hipError_t e;
   if (split) {
     e = rule_backward_split(r, base + L.slots, s);
   } else {
-    float *ws_own = base ? reinterpret_cast<float *>(base + L.slots) : nullptr;
     const float *fwd_slots =
         reuse ? reinterpret_cast<const float *>(static_cast<const char *>(a->fwd_workspace) +
                                                 fwd_copies)
               : nullptr;
-    e = rule_backward(r, ws_own, fwd_slots, s);
+    e = rule_backward(r, base ? base + L.slots : nullptr, fwd_slots, s);
   }
   if (e != hipSuccess || !conv) return to_status(e);
   return to_status(conv_backward(BH, a->H, a->N, a->d, a->dv, bf16_io, a->conv_weight,

@@ -780,6 +780,9 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DKV) bwd_dkv_kernel(BwdParams 
 // (dS_out, dz_out); slot s <- gamma^len(s+1) slot (s+1) + dSh_(s+1) (which the
 // reverse summary left in slot s).  One thread per record element; every
 // record is loaded before the chain.
+// CH: per-channel segment decays, from the third part of each reverse slot
+// (dq of segment s + 1 left it in slot s).
+template <bool CH>
 __global__ void __launch_bounds__(256) bwd_rscan_kernel(BwdParams p) {
   const int bh = grid_head();
   if (bh >= p.BH) return;
@@ -796,6 +799,13 @@ __global__ void __launch_bounds__(256) bwd_rscan_kernel(BwdParams p) {
   float dS[kMaxSegB];
 #pragma unroll
   for (int s = 0; s < kMaxSegB - 1; ++s) dS[s] = s < nseg - 1 ? base[s * stride] : 0.f;
+  [[maybe_unused]] float lgd[CH ? kMaxSegB : 1];
+  if constexpr (CH) {
+    const size_t f = e < dd ? e % p.d : e - dd;  // the element's state row
+    const float *ld = p.ws_r + (size_t)bh * p.wrec + dd + p.d + f;
+#pragma unroll
+    for (int s = 0; s < kMaxSegB - 1; ++s) lgd[s] = s < nseg - 1 ? ld[s * stride] : 0.f;
+  }
   float acc;
   if (e < dd)  // slot element e is S[f][n] with n = e / d, f = e % d
     acc = p.dS_out ? p.dS_out[(size_t)bh * dd + (e % p.d) * p.dv + e / p.d] : 0.f;
@@ -805,10 +815,588 @@ __global__ void __launch_bounds__(256) bwd_rscan_kernel(BwdParams p) {
 #pragma unroll
   for (int s = kMaxSegB - 2; s >= 0; --s) {
     if (s < nseg - 1) {
-      acc = fmaf(s + 1 == nseg - 1 ? glast : gfull, acc, dS[s]);
+      float g = s + 1 == nseg - 1 ? glast : gfull;
+      if constexpr (CH) g = exp2f(lgd[s]);
+      acc = fmaf(g, acc, dS[s]);
       base[s * stride] = acc;
     }
   }
+}
+
+// ---- per-key-channel decay (GLA; a separate instantiation) -----------------
+// With S_t = diag(alpha_t) S_(t-1) + phi(k_t) v'_t^T, inside a chunk (local
+// t, j; lb_t = sum_(s<=t) log2 alpha_s per channel, from the chunk start)
+// every decayed product is a plain one of q~_t = phi(q_t) 2^lb_t and
+// k~_j = phi(k_j) 2^-lb_j, so the gradients are those of the undecayed rule
+// with those features and the mask in place of D:
+//     dphi(q_t) = 2^lb_t (S'_in dn_t + sum_(j<=t) dA_tj k~_j)
+//     dphi(k_j) = 2^-lb_j (sum_(t>=j) dA_tj q~_t + 2^lb_L Sh v'_j)
+//     dv'_j     = sum_(t>=j) A_tj dn_t + Sh^T (phi(k_j) 2^(lb_L - lb_j))
+//     Sh       <- 2^lb_L Sh + sum_t (phi(q_t) 2^lb_t) dn_t^T      (rows scaled per channel)
+// (dA_tj = dn_t . v'_j, A the decayed scores).  The decay's own gradient,
+// d log alpha_s = alpha_s sum_c Sh_s S_(s-1) (per channel; [S | z]), is,
+// for s in a chunk entered with S- and left with the adjoint Sh+ of the
+// later tokens, the sum of every product that spans token s:
+//     2^lb_L <Sh+, S->                                  (the whole chunk)
+//   + sum_(j<s)  phi(k_j) 2^(lb_L - lb_j) (Sh+ v'_j)    (keys before s, later tokens)
+//   + sum_(t>=s) phi(q_t) 2^lb_t (S- dn_t)              (queries from s, earlier tokens)
+//   + sum_(t>=s) sum_(j<s) phi(q_t) phi(k_j) 2^(lb_t - lb_j) dA_tj
+// Every term carries alpha_s, so dalpha_s = that / alpha_s keeps its
+// relative precision however small alpha_s is (a telescoped form, summing
+// phi(q) dphi(q) - phi(k) dphi(k), cancels terms without alpha_s and would
+// lose it).  The dq kernel leaves the third sum's terms per token and the
+// state entering every chunk; the dk/dv kernel forms the rest.
+// The factors are kept in range as in the forward: each 16-token block b
+// has references R_b (lb before it), M_b (at its eighth token) and E_b (at
+// its last); the tiles hold phi(q) 2^(lb_t - M_b) and phi(k) 2^(M_b - lb_t)
+// (within alpha^-8 of phi, log2 alpha clamped at -15), and every other
+// factor is a chain of terms that are each at most 1 (see each use).
+constexpr float kLog2AlphaMinB = -15.f;
+
+template <class BC>
+struct alignas(16) ChanB {
+  static constexpr int LDL = BC::DK + 4;
+  float lbr[BC::C * LDL];      // lb_t - M_b(t) (rows past the chunk: lb stays)
+  float mr[2][BC::DK];         // M_b - R_b (R_0 = 0, R_1 = E_0)
+  float rf[2][BC::DK];         // 2^R_b
+  float fm[2][BC::DK];         // 2^M_b
+  float fl[2][BC::DK];         // 2^(lb_L - M_b)
+  float em[2][BC::DK];         // E_b - M_b
+  float le[2][BC::DK];         // 2^(lb_L - E_b)
+  float qf[2][BC::DK];         // dq: 2^(R_b + log2 decay of the segment before the chunk)
+  float mm[BC::DK];            // 2^(M_1 - M_0)
+  float dl[BC::DK];            // 2^lb_L
+  float anc[BC::DK];           // dk/dv: sum_c Sh+ S+ per channel
+  double tot[BC::DK];          // dq: log2 decay of the segment up to the chunk
+};
+
+// The chunk's prefix sums (fp64, one thread per channel; channels past d
+// get alpha = 1) and the tables above.  TOT: also the running segment decay.
+template <class BC, bool TOT>
+__device__ __forceinline__ void chan_tables(ChanB<BC> &cb, const float *al, int c0, int Lc,
+                                            int d) {
+  static_assert(BC::C == 32, "two 16-token blocks per chunk");
+  constexpr int LDL = ChanB<BC>::LDL;
+  const int f = threadIdx.x;
+  if (f >= BC::DK) return;
+  double lb = 0.0, M[2], E[2], R[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float l[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = 16 * b + i;
+      const float a = (t < Lc && f < d) ? al[(size_t)(c0 + t) * d + f] : 1.f;
+      l[i] = fmaxf(log2f(a), kLog2AlphaMinB);
+    }
+    R[b] = lb;
+    double m = lb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m += (double)l[i];
+    double e = m;
+#pragma unroll
+    for (int i = 8; i < 16; ++i) e += (double)l[i];
+    M[b] = m;
+    E[b] = e;
+    // lb_i - M_b: minus the terms after i up to the reference, or the terms
+    // after the reference up to i
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      cb.lbr[(16 * b + i) * LDL + f] = (float)(-acc);
+      acc += (double)l[i];
+    }
+    acc = 0.0;
+#pragma unroll
+    for (int i = 8; i < 16; ++i) {
+      acc += (double)l[i];
+      cb.lbr[(16 * b + i) * LDL + f] = (float)acc;
+    }
+    cb.mr[b][f] = (float)(M[b] - R[b]);
+    cb.rf[b][f] = exp2f((float)R[b]);
+    cb.fm[b][f] = exp2f((float)M[b]);
+    cb.em[b][f] = (float)(E[b] - M[b]);
+    lb = e;
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    cb.fl[b][f] = exp2f((float)(lb - M[b]));
+    cb.le[b][f] = exp2f((float)(lb - E[b]));
+  }
+  cb.mm[f] = exp2f((float)(M[1] - M[0]));
+  cb.dl[f] = exp2f((float)lb);
+  if constexpr (TOT) {
+    const double before = cb.tot[f];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) cb.qf[b][f] = exp2f((float)(before + R[b]));
+    cb.tot[f] = before + lb;
+  }
+}
+
+// phi rows times 2^(sgn lbr) into F (zero past the chunk and past d).
+template <class BC>
+__device__ __forceinline__ void commit_feat_ch(typename BC::type *F, const ChanB<BC> &cb,
+                                               float sgn,
+                                               const typename BC::vec (&X)[BRegs<BC>::NQ],
+                                               int Lc, int d, int fmap) {
+  using T = typename BC::type;
+  using V = typename BC::vec;
+#pragma unroll
+  for (int n = 0; n < BRegs<BC>::NQ; ++n) {
+    const int i = threadIdx.x + n * BC::NT;
+    if (i >= BC::C * BC::QCB) break;
+    const int row = i / BC::QCB, col0 = (i % BC::QCB) * BC::VEC;
+    V f;
+#pragma unroll
+    for (int e = 0; e < BC::VEC; ++e) {
+      const float y = (row < Lc && col0 + e < d) ? feat(to_f32(X[n][e]), fmap) : 0.f;
+      f[e] = from_f32<T>(y * exp2f(sgn * cb.lbr[row * ChanB<BC>::LDL + col0 + e]));
+    }
+    *reinterpret_cast<V *>(F + row * BC::LDK + col0) = f;
+  }
+}
+
+// S <- diag(rs) S + sum_t (X[t][f] op[b(t)][f]) Y[t][c]: X token-major with
+// channels as rows of S, op one factor per 16-token block and channel (a
+// lane's eight k slots are tokens 8 lg .. 8 lg + 7, all in block lg / 2).
+template <class BC>
+__device__ __forceinline__ void state_update_ch(f32x4 (&Sa)[BC::SPW],
+                                                const typename BC::type *X,
+                                                const typename BC::type *Y, const float *rs,
+                                                const float (*op)[BC::DK], int wv, int li,
+                                                int lg) {
+  using T = typename BC::type;
+#pragma unroll
+  for (int i = 0; i < BC::SPW; ++i) {
+    const int st = wv + BC::NW * i;
+    if (st >= BC::NST) continue;
+    const int fb = st / BC::NVP, vb = st % BC::NVP;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Sa[i][r] *= rs[16 * fb + 4 * lg + r];
+    Frag<T> a, b;
+    frag_kr(a, X, BC::LDK, 16 * fb, 0, li, lg);
+    const float w = op[lg >> 1][16 * fb + li];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a.v[e] = from_f32<T>(to_f32(a.v[e]) * w);
+    frag_kr(b, Y, BC::LDV, 16 * vb, 0, li, lg);
+    mma(Sa[i], a, b);
+  }
+}
+
+// Decayed scores A[t][j] = sum_f Qh[t][f] Kh[j][f] (2^(M_1 - M_0))_f for the
+// key block before the query block (the tiles are block-relative), zero
+// above the diagonal.
+template <class BC>
+__device__ __forceinline__ void tri_tiles_ch(typename BC::type *M, const typename BC::type *X,
+                                             const typename BC::type *Y, const float *mm,
+                                             int wv, int li, int lg) {
+  using T = typename BC::type;
+  constexpr int NTI = BC::NTB * BC::NTB;
+#pragma unroll
+  for (int n = 0; n < (NTI + BC::NW - 1) / BC::NW; ++n) {
+    const int ti = wv + BC::NW * n;
+    if (ti >= NTI) break;
+    const int tt = ti / BC::NTB, jt = ti % BC::NTB;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (jt <= tt) {
+#pragma unroll
+      for (int ks = 0; ks < BC::DK / 32; ++ks) {
+        Frag<T> a, b;
+        frag_rk(a, X, BC::LDK, 16 * tt, 32 * ks, li, lg);
+        frag_rk(b, Y, BC::LDK, 16 * jt, 32 * ks, li, lg);
+        if (jt < tt) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            b.v[e] = from_f32<T>(to_f32(b.v[e]) * mm[32 * ks + 8 * lg + e]);
+        }
+        mma(acc, a, b);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * tt + 4 * lg + r, j = 16 * jt + li;
+      M[t * BC::LDC + j] = from_f32<T>(j <= t ? acc[r] : 0.f);
+    }
+  }
+}
+
+template <class BC>
+constexpr int ch_waves_per_simd(size_t lds) {
+  const int wg = (int)((160 * 1024) / lds);
+  const int w = wg * BC::NW / 4;
+  return w < 1 ? 1 : (w > 2 ? 2 : w);
+}
+
+// ---- dq with a per-channel decay: chunks left to right, forward state ------
+template <class BC>
+struct alignas(16) SmemDqCh {
+  SmemDq<BC> m;  // Fk holds phi(k) 2^(M_b - lb_j); KW, pw, kw unused
+  ChanB<BC> c;
+};
+
+template <class BC, bool VK>
+__global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDqCh<BC>)))
+    bwd_dq_ch_kernel(BwdParams p) {
+  using T = typename BC::type;
+  __shared__ SmemDqCh<BC> smc;
+  SmemDq<BC> &sm = smc.m;
+  ChanB<BC> &cb = smc.c;
+  const int seg = blockIdx.x, bh = grid_head();
+  if (bh >= p.BH) return;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int d = p.d, dv = p.dv, N = p.N;
+  const int t_begin = seg * p.seg_len, t_end = min(N, t_begin + p.seg_len);
+  constexpr int LDL = ChanB<BC>::LDL;
+  HeadRsrc hr;
+  hr.q = head_rsrc<T>(p.q, bh, N, d);
+  hr.k = head_rsrc<T>(p.k, bh, N, d);
+  hr.v = head_rsrc<T>(p.v, bh, N, dv);
+  hr.o = head_rsrc<T>(p.o, bh, N, dv);
+  hr.g = head_rsrc<T>(p.dout, bh, N, dv);
+  hr.den = head_rsrc<float>(p.den, bh, N, 1);
+  const __amdgpu_buffer_rsrc_t rdq = head_rsrc<T>(p.dq, bh, N, d);
+  const float *al = p.alpha + (size_t)bh * N * d;
+  float *ux = p.ux + (size_t)bh * N * d;
+  const int nch = (N + BC::C - 1) / BC::C;
+  zero_tail_columns<BC>(sm.St);
+  for (int f = threadIdx.x; f < BC::DK; f += BC::NT) cb.tot[f] = 0.0;
+
+  f32x4 Sa[BC::SPW];
+  if (p.nseg > 1)
+    slot_load<BC>(Sa, p.ws_f + ((size_t)seg * p.BH + bh) * p.wrec, d, dv, p.slot_vec, wv, li,
+                  lg);
+  else
+    state_load<BC>(Sa, p.S_in ? p.S_in + (size_t)bh * d * dv : nullptr,
+                   p.z_in ? p.z_in + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
+  f32x4 Ra[BC::SPW];  // this segment's own adjoint (segments after the first)
+#pragma unroll
+  for (int i = 0; i < BC::SPW; ++i) Ra[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  BRegs<BC> R;
+  load_chunk<BC, VK, true, true, true, true>(R, hr, t_begin, min(BC::C, N - t_begin), d, dv);
+  __syncthreads();
+
+  for (int c0 = t_begin; c0 < t_end; c0 += BC::C) {
+    const int Lc = min(BC::C, N - c0);
+    chan_tables<BC, true>(cb, al, c0, Lc, d);
+    __syncthreads();
+    commit_feat<BC>(sm.Fq, nullptr, nullptr, R.q, Lc, d, p.fmap);
+    commit_feat_ch<BC>(sm.Fk, cb, -1.f, R.k, Lc, d, p.fmap);
+    commit_values<BC>(sm.Vp, R, Lc);
+    commit_dn<BC>(sm.dN, R, Lc);
+    state_copy<BC>(sm.St, Sa, wv, li, lg);
+    // the state entering the chunk, for the dk/dv kernel's dalpha
+    slot_store<BC>(Sa, p.chs + ((size_t)bh * nch + c0 / BC::C) * p.wrec, d, dv, p.slot_vec, wv,
+                   li, lg);
+    if (c0 + BC::C < t_end)
+      load_chunk<BC, VK, true, true, true, true>(R, hr, c0 + BC::C, min(BC::C, N - c0 - BC::C),
+                                                 d, dv);
+    __syncthreads();
+
+    tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, false, wv, li, lg);
+    __syncthreads();
+
+    // dphi(q_t) = 2^lb_t S'_in dn_t (as 2^(lb_t - R_b) 2^R_b, both <= 1)
+    //           + 2^(lb_t - M_b) sum_j dA_tj phi(k_j) 2^(M_b - lb_j)
+    // (keys of the block before: 2^(M_1 - M_0) <= 1 on their tile entries)
+    constexpr int NQT = BC::NTB * BC::NFB;
+#pragma unroll
+    for (int n = 0; n < (NQT + BC::NW - 1) / BC::NW; ++n) {
+      const int ti = wv + BC::NW * n;
+      if (ti >= NQT) break;
+      const int tt = ti / BC::NFB, fb = ti % BC::NFB;
+      f32x4 acs = {0.f, 0.f, 0.f, 0.f}, acd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < BC::DVK / 32; ++ks) {
+        Frag<T> a, b;
+        frag_rk(a, sm.dN, BC::LDV, 16 * tt, 32 * ks, li, lg);
+        frag_rk(b, sm.St, BC::LDV, 16 * fb, 32 * ks, li, lg);
+        mma(acs, a, b);
+      }
+      {
+        Frag<T> a, b;
+        frag_rk(a, sm.dA, BC::LDC, 16 * tt, 0, li, lg);
+        frag_kr(b, sm.Fk, BC::LDK, 16 * fb, 0, li, lg);
+        if (tt == 1 && (lg >> 1) == 0) {
+          const float w = cb.mm[16 * fb + li];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) b.v[e] = from_f32<T>(to_f32(b.v[e]) * w);
+        }
+        mma(acd, a, b);
+      }
+      f32x4 acc;
+      const int f = 16 * fb + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * tt + 4 * lg + r;
+        const float lr = cb.lbr[t * LDL + f];
+        const float sp = acs[r] * (exp2f(lr + cb.mr[tt][f]) * cb.rf[tt][f]);
+        const float dphi = sp + acd[r] * exp2f(lr);
+        const float fq = to_f32(sm.Fq[t * BC::LDK + f]);
+        if (t < Lc && f < d) ux[(size_t)(c0 + t) * d + f] = fq * sp;  // dalpha's third sum
+        acc[r] = dphi * (p.fmap ? fminf(fq, 1.f) : 1.f);
+      }
+      out_tile<BC>(sm.Os, BC::LDKS, rdq, acc, c0, 16 * tt, f, Lc, d, lg);
+    }
+    // forward state across the chunk: S <- 2^lb_L S + sum_j (phi(k_j) 2^(lb_L - lb_j)) v'_j^T
+    state_update_ch<BC>(Sa, sm.Fk, sm.Vp, cb.dl, cb.fl, wv, li, lg);
+    // the segment's adjoint: += sum_t (phi(q_t) 2^(seg decay before t, incl. t)) dn_t^T
+    if (seg > 0) {
+#pragma unroll
+      for (int i = 0; i < BC::SPW; ++i) {
+        const int st = wv + BC::NW * i;
+        if (st >= BC::NST) continue;
+        const int fb = st / BC::NVP, vb = st % BC::NVP;
+        const int f = 16 * fb + li, b = lg >> 1;
+        Frag<T> a, bb;
+        frag_kr(a, sm.Fq, BC::LDK, 16 * fb, 0, li, lg);
+        const float w0 = cb.qf[b][f], mrb = cb.mr[b][f];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          a.v[e] = from_f32<T>(to_f32(a.v[e]) *
+                               (exp2f(cb.lbr[(8 * lg + e) * LDL + f] + mrb) * w0));
+        frag_kr(bb, sm.dN, BC::LDV, 16 * vb, 0, li, lg);
+        mma(Ra[i], a, bb);
+      }
+    }
+    __syncthreads();
+    store_rows<BC, VK>(rdq, sm.Os, BC::LDKS, BC::QCB, c0, Lc, d);
+  }
+  if (seg > 0) {  // into reverse slot seg - 1, with the segment's log2 decay per channel
+    float *slot = p.ws_r + ((size_t)(seg - 1) * p.BH + bh) * p.wrec;
+    slot_store<BC>(Ra, slot, d, dv, p.slot_vec, wv, li, lg);
+    for (int f = threadIdx.x; f < d; f += BC::NT)
+      slot[(size_t)d * dv + d + f] = (float)cb.tot[f];
+  }
+}
+
+// ---- dk, dv with a per-channel decay: chunks right to left, adjoint state ---
+template <class BC>
+struct alignas(16) SmemDkvCh {
+  static_assert(sizeof(SmemDkv<BC, false>::Ok) >= BC::NVP * BC::DK * sizeof(float),
+                "the anchor partials fit the dk staging tile");
+  SmemDkv<BC, false> m;  // Fq holds phi(q) 2^(lb_t - M_b), Fk phi(k)
+  typename BC::type Kh[BC::C * BC::LDK];  // phi(k) 2^(M_b - lb_j)
+  ChanB<BC> c;
+};
+
+template <class BC, bool VK>
+__global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh<BC>)))
+    bwd_dkv_ch_kernel(BwdParams p) {
+  using T = typename BC::type;
+  __shared__ SmemDkvCh<BC> smc;
+  SmemDkv<BC, false> &sm = smc.m;
+  ChanB<BC> &cb = smc.c;
+  T *Kh = smc.Kh;
+  const int seg = blockIdx.x, bh = grid_head();
+  if (bh >= p.BH) return;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int d = p.d, dv = p.dv, N = p.N;
+  const int t_begin = seg * p.seg_len, t_end = min(N, t_begin + p.seg_len);
+  constexpr int LDL = ChanB<BC>::LDL;
+  HeadRsrc hr;
+  hr.q = head_rsrc<T>(p.q, bh, N, d);
+  hr.k = head_rsrc<T>(p.k, bh, N, d);
+  hr.v = head_rsrc<T>(p.v, bh, N, dv);
+  hr.o = head_rsrc<T>(p.o, bh, N, dv);
+  hr.g = head_rsrc<T>(p.dout, bh, N, dv);
+  hr.den = head_rsrc<float>(p.den, bh, N, 1);
+  const __amdgpu_buffer_rsrc_t rdk = head_rsrc<T>(p.dk, bh, N, d),
+                               rdv = head_rsrc<T>(p.dv_, bh, N, dv);
+  const float *al = p.alpha + (size_t)bh * N * d;
+  const float *ux = p.ux + (size_t)bh * N * d;
+  float *dal = p.dalpha + (size_t)bh * N * d;
+  const int nch = (N + BC::C - 1) / BC::C;
+  zero_tail_columns<BC>(sm.Sh);
+
+  f32x4 Sa[BC::SPW];
+  if (p.nseg > 1)
+    slot_load<BC>(Sa, p.ws_r + ((size_t)seg * p.BH + bh) * p.wrec, d, dv, p.slot_vec, wv, li,
+                  lg);
+  else
+    state_load<BC>(Sa, p.dS_out ? p.dS_out + (size_t)bh * d * dv : nullptr,
+                   p.dz_out ? p.dz_out + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
+  const int last = t_begin + ((t_end - t_begin - 1) / BC::C) * BC::C;
+  BRegs<BC> R;
+  load_chunk<BC, VK, true, true, true, true>(R, hr, last, min(BC::C, N - last), d, dv);
+  __syncthreads();
+
+  constexpr int NKT = BC::NTB * BC::NFB;
+  constexpr int KPW = (NKT + BC::NW - 1) / BC::NW;  // dk tiles per wave
+  const float amin = exp2f(kLog2AlphaMinB);
+  for (int c0 = last; c0 >= t_begin; c0 -= BC::C) {
+    const int Lc = min(BC::C, N - c0);
+    chan_tables<BC, false>(cb, al, c0, Lc, d);
+    __syncthreads();
+    // <Sh+, S-> per channel (Sh+: this wave's adjoint tiles as they enter
+    // the chunk; S-: the forward state entering it, left by dq): one partial
+    // per channel and value tile, in the dk staging tile (free until the dk
+    // tiles), summed in a fixed order below
+    float *partv = reinterpret_cast<float *>(sm.Ok);
+    {
+      const float *sp = p.chs + ((size_t)bh * nch + c0 / BC::C) * p.wrec;
+#pragma unroll
+      for (int i = 0; i < BC::SPW; ++i) {
+        const int st = wv + BC::NW * i;
+        const int fb = st / BC::NVP, vb = st % BC::NVP;
+        const int c = 16 * vb + li;
+        const bool val = vb < BC::NVP - 1;
+        const bool ok = st < BC::NST && (val ? c < dv : li == 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int f = 16 * fb + 4 * lg + r;
+          float part = 0.f;
+          if (ok && f < d) part = Sa[i][r] * sp[val ? (size_t)c * d + f : (size_t)d * dv + f];
+#pragma unroll
+          for (int m = 1; m < 16; m <<= 1) part += __shfl_xor(part, m);
+          if (li == 0 && st < BC::NST) partv[vb * BC::DK + f] = part;
+        }
+      }
+    }
+    commit_feat_ch<BC>(sm.Fq, cb, 1.f, R.q, Lc, d, p.fmap);
+    commit_feat<BC>(sm.Fk, nullptr, nullptr, R.k, Lc, d, p.fmap);
+    commit_feat_ch<BC>(Kh, cb, -1.f, R.k, Lc, d, p.fmap);
+    commit_values<BC>(sm.Vp, R, Lc);
+    commit_dn<BC>(sm.dN, R, Lc);
+    state_copy<BC>(sm.Sh, Sa, wv, li, lg);
+    if (c0 > t_begin)
+      load_chunk<BC, VK, true, true, true, true>(R, hr, c0 - BC::C, BC::C, d, dv);
+    __syncthreads();
+
+    tri_tiles_ch<BC>(sm.Ad, sm.Fq, Kh, cb.mm, wv, li, lg);
+    tri_tiles<BC, BC::DVK / 32, BC::LDV>(sm.dA, sm.dN, sm.Vp, sm.pw, false, wv, li, lg);
+    for (int f = threadIdx.x; f < d; f += BC::NT) {
+      float a = 0.f;
+      for (int vb = 0; vb < BC::NVP; ++vb) a += partv[vb * BC::DK + f];
+      cb.anc[f] = a;
+    }
+    __syncthreads();
+    // dphi(k_j) = 2^(lb_L - lb_j) V' Sh^T (as 2^(E_b - lb_j) 2^(lb_L - E_b))
+    //           + 2^(M_b - lb_j) sum_t dA_tj phi(q_t) 2^(lb_t - M_b)
+    // (queries of the block after: 2^(M_1 - M_0) <= 1 on their tile entries);
+    // dalpha's second sum's terms phi(k_j) (state part) kept in registers
+    float xr[KPW][4];
+#pragma unroll
+    for (int n = 0; n < KPW; ++n) {
+      const int ti = wv + BC::NW * n;
+      if (ti >= NKT) break;
+      const int jt = ti / BC::NFB, fb = ti % BC::NFB;
+      f32x4 acs = {0.f, 0.f, 0.f, 0.f}, aci = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < BC::DVK / 32; ++ks) {
+        Frag<T> a, b;
+        frag_rk(a, sm.Vp, BC::LDV, 16 * jt, 32 * ks, li, lg);
+        frag_rk(b, sm.Sh, BC::LDV, 16 * fb, 32 * ks, li, lg);
+        mma(acs, a, b);
+      }
+      {
+        Frag<T> a, b;
+        frag_kr(a, sm.dA, BC::LDC, 16 * jt, 0, li, lg);
+        frag_kr(b, sm.Fq, BC::LDK, 16 * fb, 0, li, lg);
+        if (jt == 0 && (lg >> 1) == 1) {
+          const float w = cb.mm[16 * fb + li];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) b.v[e] = from_f32<T>(to_f32(b.v[e]) * w);
+        }
+        mma(aci, a, b);
+      }
+      f32x4 acc;
+      const int f = 16 * fb + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * jt + 4 * lg + r;
+        const float lr = cb.lbr[j * LDL + f];
+        const float sp = acs[r] * (exp2f(cb.em[jt][f] - lr) * cb.le[jt][f]);
+        const float dphi = sp + aci[r] * exp2f(-lr);
+        const float fk = to_f32(sm.Fk[j * BC::LDK + f]);
+        xr[n][r] = fk * sp;
+        acc[r] = dphi * (p.fmap ? fminf(fk, 1.f) : 1.f);
+      }
+      out_tile<BC>(sm.Ok, BC::LDKS, rdk, acc, c0, 16 * jt, f, Lc, d, lg);
+    }
+    // dv' = (phi(k_j) 2^(lb_L - lb_j)) Sh + A^T dN  (value columns only)
+    constexpr int NVT = BC::NTB * (BC::NVP - 1);
+#pragma unroll
+    for (int n = 0; n < (NVT + BC::NW - 1) / BC::NW; ++n) {
+      const int ti = wv + BC::NW * n;
+      if (ti >= NVT) break;
+      const int jt = ti / (BC::NVP - 1), vb = ti % (BC::NVP - 1);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < BC::DK / 32; ++ks) {
+        Frag<T> a, b;
+        frag_rk(a, Kh, BC::LDK, 16 * jt, 32 * ks, li, lg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          a.v[e] = from_f32<T>(to_f32(a.v[e]) * cb.fl[jt][32 * ks + 8 * lg + e]);
+        frag_kr(b, sm.Sh, BC::LDV, 16 * vb, 32 * ks, li, lg);
+        mma(acc, a, b);
+      }
+      {
+        Frag<T> a, b;
+        frag_kr(a, sm.Ad, BC::LDC, 16 * jt, 0, li, lg);
+        frag_kr(b, sm.dN, BC::LDV, 16 * vb, 0, li, lg);
+        mma(acc, a, b);
+      }
+      out_tile<BC>(sm.Ov, BC::LDOS, rdv, acc, c0, 16 * jt, 16 * vb + li, Lc, dv, lg);
+    }
+    // adjoint across the chunk: Sh <- 2^lb_L Sh + sum_t (phi(q_t) 2^lb_t) dn_t^T
+    state_update_ch<BC>(Sa, sm.Fq, sm.dN, cb.dl, cb.fm, wv, li, lg);
+    __syncthreads();
+    store_rows<BC, VK>(rdk, sm.Ok, BC::LDKS, BC::QCB, c0, Lc, d);
+    store_rows<BC, VK>(rdv, sm.Ov, BC::LDOS, BC::VCB, c0, Lc, dv);
+    // dalpha: the second sum's terms into the (now unused) exponent tile, then
+    // one thread per channel: their prefix over the keys before s, the
+    // third sum's suffix from dq's terms, and the fourth as a running
+    // G_j = sum_(t>=s) phi(q_t) 2^(lb_t - M) dA_tj over the keys j < s
+#pragma unroll
+    for (int n = 0; n < KPW; ++n) {
+      const int ti = wv + BC::NW * n;
+      if (ti >= NKT) break;
+      const int jt = ti / BC::NFB, fb = ti % BC::NFB;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        cb.lbr[(16 * jt + 4 * lg + r) * LDL + 16 * fb + li] = xr[n][r];
+    }
+    __syncthreads();
+    for (int f = threadIdx.x; f < d; f += BC::NT) {
+      float run = 0.f;  // exclusive prefix of the second sum's terms, in place
+      for (int j = 0; j < Lc; ++j) {
+        const float y = cb.lbr[j * LDL + f];
+        cb.lbr[j * LDL + f] = run;
+        run += y;
+      }
+      float G[BC::C];
+#pragma unroll
+      for (int j = 0; j < BC::C; ++j) G[j] = 0.f;
+      const float a1 = cb.anc[f] * cb.dl[f], mmf = cb.mm[f];
+      float a3 = 0.f;
+      for (int s = Lc - 1; s >= 0; --s) {
+        const float qs = to_f32(sm.Fq[s * BC::LDK + f]);
+        const float qx = s >= 16 ? qs * mmf : qs;  // keys of block 0 under a block-1 query
+        float a4 = 0.f;
+#pragma unroll
+        for (int j = 0; j < BC::C; ++j) {
+          if (j < s) {
+            G[j] = fmaf(j < 16 ? qx : qs, to_f32(sm.dA[s * BC::LDC + j]), G[j]);
+            a4 = fmaf(to_f32(Kh[j * BC::LDK + f]), G[j], a4);
+          }
+        }
+        const size_t at = (size_t)(c0 + s) * d + f;
+        a3 += ux[at];
+        const float a = al[at];
+        dal[at] = a >= amin ? (a1 + cb.lbr[s * LDL + f] + a3 + a4) / a : 0.f;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (seg == 0)
+    state_store<BC>(Sa, p.dS_in ? p.dS_in + (size_t)bh * d * dv : nullptr,
+                    p.dz_in ? p.dz_in + (size_t)bh * d : nullptr, d, dv, wv, li, lg);
 }
 
 template <class BC, bool VK>
@@ -825,7 +1413,7 @@ hipError_t run_bwd(const BwdParams &p, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (p.nseg > 1) {
     const size_t rec = (size_t)p.d * p.dv + p.d;
-    e = launch_kernel("linear_bwd_rscan", bwd_rscan_kernel,
+    e = launch_kernel("linear_bwd_rscan", bwd_rscan_kernel<false>,
                       head_grid((unsigned)((rec + 255) / 256), p.BH), dim3(256), s, p);
     if (e != hipSuccess) return e;
   }
@@ -835,8 +1423,31 @@ hipError_t run_bwd(const BwdParams &p, hipStream_t s) {
                                  dim3(BC::NT), s, p);
 }
 
+template <class BC, bool VK>
+hipError_t run_bwd_ch(const BwdParams &p, hipStream_t s) {
+  static_assert(sizeof(SmemDqCh<BC>) <= 160 * 1024 && sizeof(SmemDkvCh<BC>) <= 160 * 1024,
+                "LDS budget");
+  static_assert(BC::C == kChanBwdChunk, "chunk of the per-channel kernels");
+  const dim3 grid = head_grid(p.nseg, p.BH);
+  hipError_t e = launch_kernel("linear_bwd_dq", bwd_dq_ch_kernel<BC, VK>, grid, dim3(BC::NT), s, p);
+  if (e != hipSuccess) return e;
+  if (p.nseg > 1) {
+    const size_t rec = (size_t)p.d * p.dv + p.d;
+    e = launch_kernel("linear_bwd_rscan", bwd_rscan_kernel<true>,
+                      head_grid((unsigned)((rec + 255) / 256), p.BH), dim3(256), s, p);
+    if (e != hipSuccess) return e;
+  }
+  return launch_kernel("linear_bwd_dkv", bwd_dkv_ch_kernel<BC, VK>, grid, dim3(BC::NT), s, p);
+}
+
 template <class BC>
 hipError_t run_bwd_vk(const BwdParams &p, hipStream_t s) {
+  if (p.alpha) {
+    if constexpr (sizeof(SmemDqCh<BC>) <= 160 * 1024 && sizeof(SmemDkvCh<BC>) <= 160 * 1024)
+      return p.vec_ok ? run_bwd_ch<BC, true>(p, s) : run_bwd_ch<BC, false>(p, s);
+    else
+      return hipErrorInvalidValue;
+  }
   return p.vec_ok ? run_bwd<BC, true>(p, s) : run_bwd<BC, false>(p, s);
 }
 
@@ -926,8 +1537,15 @@ bool linear_backward_supported(int d, int dv, bool bf16_io) {
   return bf16_io || d <= 64 || dv <= 64;
 }
 
+bool linear_backward_channel_supported(int d, int dv, bool bf16_io) {
+  // the fp32 128-feature tiles of the per-channel kernels exceed the LDS
+  return linear_backward_supported(d, dv, bf16_io) && (bf16_io || d <= 64);
+}
+
 hipError_t launch_linear_backward(const BwdParams &p, bool bf16_io, hipStream_t s) {
   if (!linear_backward_supported(p.d, p.dv, bf16_io)) return hipErrorInvalidValue;
+  if (p.alpha && (p.gamma || !linear_backward_channel_supported(p.d, p.dv, bf16_io)))
+    return hipErrorInvalidValue;
   if (!bf16_io) {
     if (p.d <= 64) return p.dv <= 64 ? run_bwd_vk<BF64x64>(p, s) : run_bwd_vk<BF64x128>(p, s);
     return run_bwd_vk<BF128x64>(p, s);

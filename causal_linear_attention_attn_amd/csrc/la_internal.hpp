@@ -98,6 +98,12 @@ struct BwdParams {
   size_t wrec;                       // floats per slot record
   int nseg, seg_len;
   int slot_vec;                      // forward slots take 16-byte accesses
+  // per-key-channel decay (GLA): alpha [BH, N, d] fp32 or nullptr; then
+  // ux [BH, N, d] fp32 (phi(q) . dphi(q) per token and channel), chs
+  // [BH, nchunks] slot records of wrec floats (the forward state after each
+  // chunk) and the output dalpha [BH, N, d]
+  const float *alpha;
+  float *ux, *chs, *dalpha;
 };
 
 struct DecodeParams {
@@ -184,6 +190,7 @@ hipError_t launch_linear_state_prefix(const PrefillParams &p, const LinearPlan &
 // Tile configurations the backward kernels have for these widths (fp32 with
 // d and dv both above 64 has none: the API runs it over value halves).
 bool linear_backward_supported(int d, int dv, bool bf16);
+bool linear_backward_channel_supported(int d, int dv, bool bf16);  // with alpha
 hipError_t launch_linear_backward(const BwdParams &p, bool bf16, hipStream_t s);
 // fp32 rows [rows, n] <-> column blocks [rows, na] and [rows, n - na]; dst += src.
 hipError_t launch_split_cols(const float *src, float *a, float *b, size_t rows, int n, int na,
@@ -191,6 +198,8 @@ hipError_t launch_split_cols(const float *src, float *a, float *b, size_t rows, 
 hipError_t launch_join_cols(float *dst, const float *a, const float *b, size_t rows, int n,
                             int na, hipStream_t s);
 hipError_t launch_add_into(float *dst, const float *src, size_t n, hipStream_t s);
+// tokens per chunk of the backward kernels with a per-channel decay
+constexpr int kChanBwdChunk = 32;
 hipError_t launch_linear_prefill(const PrefillParams &p, const LinearPlan &plan,
                                  bool bf16, hipStream_t s);
 // Gated delta rule: workspace (per-chunk Wt and R tiles) and the two-kernel

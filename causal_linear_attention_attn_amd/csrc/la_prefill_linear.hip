@@ -1311,7 +1311,7 @@ constexpr int wpe_at_most_2() {
   return CF::WPE < 2 ? CF::WPE : 2;
 }
 
-// DN: also write each token's denominator (den_out; no per-channel decay or
+// DN: also write each token's denominator (den_out; not with the fused
 // convolution); DEC: per-head decay gamma (compiled in only where given)
 template <class CF, bool VK, bool CH, bool CV, bool DN, bool DEC>
 __global__ void __launch_bounds__(CF::NT, (CH || CV) ? wpe_at_most_2<CF>() : CF::WPE)
@@ -1577,6 +1577,11 @@ hipError_t run_vkcc(const PrefillParams &p, hipStream_t s) {
   }
   const dim3 grid = head_grid(p.nseg, p.BH);
   if constexpr (CH) {  // (a per-channel decay excludes gamma)
+    if constexpr (!CV) {  // (with den_out a convolution runs as a pass of its own)
+      if (p.den_out)
+        return launch_kernel("linear_chunk", chunk_kernel<CF, VK, true, false, true, false>,
+                             grid, dim3(CF::NT), s, p);
+    }
     return launch_kernel("linear_chunk", chunk_kernel<CF, VK, CH, CV, false, false>, grid,
                          dim3(CF::NT), s, p);
   } else {
@@ -1613,17 +1618,25 @@ hipError_t run(const PrefillParams &p, hipStream_t s) {
   return p.vec_ok ? run_vk<CF, true>(p, s) : run_vk<CF, false>(p, s);
 }
 
-// summary + scan only (the segment-entering states), no decay variants
+// summary + scan only (the segment-entering states); the per-head decay
+// is read by the plain instantiation, a per-channel decay has its own
 template <class CF>
 hipError_t run_prefix(const PrefillParams &p, hipStream_t s) {
   if (p.nseg <= 1) return hipSuccess;
   const dim3 grid = head_grid((p.nseg - 1) * p.nsplit, p.BH);
-  hipError_t e = p.vec_ok ? launch_kernel("linear_summary", summary_kernel<CF, true, false, false>,
-                                          grid, dim3(CF::NT), s, p)
-                          : launch_kernel("linear_summary", summary_kernel<CF, false, false, false>,
-                                          grid, dim3(CF::NT), s, p);
+  hipError_t e;
+  if (p.alpha)
+    e = p.vec_ok ? launch_kernel("linear_summary", summary_kernel<CF, true, true, false>, grid,
+                                 dim3(CF::NT), s, p)
+                 : launch_kernel("linear_summary", summary_kernel<CF, false, true, false>, grid,
+                                 dim3(CF::NT), s, p);
+  else
+    e = p.vec_ok ? launch_kernel("linear_summary", summary_kernel<CF, true, false, false>, grid,
+                                 dim3(CF::NT), s, p)
+                 : launch_kernel("linear_summary", summary_kernel<CF, false, false, false>, grid,
+                                 dim3(CF::NT), s, p);
   if (e != hipSuccess) return e;
-  return launch_scan<false>(p, s);
+  return p.alpha ? launch_scan<true>(p, s) : launch_scan<false>(p, s);
 }
 
 // Workgroups of chunk_kernel<CF> that fit on one CU (queried once per

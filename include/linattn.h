@@ -143,7 +143,7 @@ typedef struct la_prefill_args {
   void *o;           /* [B,H,N,dv] output, dtype as q (required if N > 0) */
   float *den_out;    /* LINEAR: [B,H,N] each token's denominator
                         phi(q_t).z_t + eps (what la_backward needs), or NULL
-                        (not written).  Not with alpha (LA_EUNSUPPORTED).
+                        (not written); with gamma or alpha alike.
                         With conv_weight the convolution then runs as a pass
                         of its own, into convolved copies of q, k, v at the
                         start of the workspace (la_backward's fwd_workspace
@@ -196,14 +196,23 @@ int la_prefill_noalloc(const la_prefill_args *args, void *stream);
  *   dphi(q_t) = [S_t | z_t] dn_t,  dphi(k_t) = Sh_t [v_t | 1],
  *   dv_t = (Sh_t^T phi(k_t)) without its last entry,
  *   dq = dphi(q) phi'(q), dk = dphi(k) phi'(k); dL/d(initial state) = gamma Sh_0.
- * Inputs are the forward's q, k, v, gamma, initial state, its output o and
- * its denominators den (la_prefill's den_out); no per-key-channel decay
- * (alpha); with the forward's convolution (conv_weight below) the
- * gradients are taken through it too.  Any d, dv up to 128 for both
+ * With a per-key-channel decay alpha (GLA) in place of gamma the adjoint is
+ * carried through diag(alpha_t), and
+ *   dalpha_t[f] = sum_c Sh_t[f, c] S_(t-1)[f, c] + zh_t[f] z_(t-1)[f]
+ * (S_(-1) the initial state), computed as (C0 + sum_(s>=t) (phi(q_s)
+ * dphi(q_s) - phi(k_s) dphi(k_s))[f]) / alpha_t[f] with C0 = sum_c dS_out
+ * S_N + dz_out z_N (the same sum, telescoped along the recurrence); alpha
+ * below 2^-15, which the forward takes as 2^-15, gets dalpha 0.
+ * Inputs are the forward's q, k, v, gamma or alpha, initial state, its
+ * output o and its denominators den (la_prefill's den_out); with the
+ * forward's convolution (conv_weight below) the gradients are taken
+ * through it too.  Any d, dv up to 128 for both
  * dtypes; fp32 with d and dv both above 64 runs over the value columns
  * [0, 64) and [64, dv) in turn (the fp32 tiles of the whole width do not
  * fit the LDS; the gradients are linear in the value columns, so dq, dk and
- * dL/dz_in are sums over the halves) and then needs a workspace at any N. */
+ * dL/dz_in are sums over the halves) and then needs a workspace at any N;
+ * with alpha, fp32 takes d up to 64 (LA_EUNSUPPORTED above: the fp32
+ * tiles of the per-channel kernels exceed the LDS). */
 typedef struct la_backward_args {
   int32_t B, H, N;   /* as the forward */
   int32_t d, dv;
@@ -226,8 +235,8 @@ typedef struct la_backward_args {
   float *grad_S_in;  /* [B,H,d,dv] dL/d(initial state); NULL = not written */
   float *grad_z_in;  /* [B,H,d]; NULL = not written */
   void *workspace;   /* device scratch of workspace_bytes, caller-owned;
-                        4-byte aligned, 16-byte with conv_weight (else
-                        LA_EINVAL) */
+                        4-byte aligned, 16-byte with conv_weight or alpha
+                        (else LA_EINVAL) */
   size_t workspace_bytes;
   /* Optional (NULL = not used): the workspace of the la_prefill call that
    * produced o and den, left as that call wrote it, with this call's q, k,
@@ -257,11 +266,15 @@ typedef struct la_backward_args {
                                 conv_weight): summed over the batch */
   void *grad_conv_in;        /* [B,H,w-1,2d+dv] dL/d(conv_in), dtype of q;
                                 NULL = not written */
+  const float *alpha;        /* [B,H,N,d] the forward's per-key-channel decay,
+                                or NULL; not with gamma (LA_EINVAL) */
+  float *grad_alpha;         /* [B,H,N,d] dL/dalpha: required with alpha (if
+                                N > 0), must be NULL without */
 } la_backward_args;
 
 /* Workspace bytes la_backward needs (0 when none); (size_t)-1 for invalid
  * sizes.  Reads only the sizes, the dtype, conv_width (with conv_weight set)
- * and whether fwd_workspace is NULL: with the forward's workspace given, the
+ * and whether alpha and fwd_workspace are NULL: with the forward's workspace given, the
  * forward's segment states (and convolved inputs) are read from it, so half
  * the state slots (and no copies of the inputs) are needed. */
 size_t la_backward_workspace_size(const la_backward_args *args);

@@ -163,6 +163,52 @@ def linear_grad_scales(q, k, v, do, o, den, *, gamma=None, fmap="elu1", S0=None,
     return sq, sk, sv, sS, sz
 
 
+def gla_grad_scales(q, k, v, do, o, den, alpha, *, fmap="elu1", S0=None, z0=None, dS_N=None,
+                    dz_N=None):
+    """Per-element sums of |terms| of dq, dk, dv, dS_in, dz_in and dalpha
+    for the LINEAR rule with a per-channel decay alpha (fp64, from the
+    oracle's o and den): every gradient is a sum of products of nonnegative
+    magnitudes, so the same recurrences run on magnitudes give those sums:
+        |S|_t = alpha_t |S|_(t-1) + |phi(k_t)| [|v_t| | 1]^T   ([S | z], from |S0|, |z0|)
+        |Sh|_t = phi(q_t) |dn_t|^T + alpha_(t+1) |Sh|_(t+1)     (from |dS_N|, |dz_N|)
+    with |dn_t| = [|g_t| | |g_t . o_t|] / den_t; then dq_t ~ |S|_t |dn_t|,
+    dk_t ~ |Sh|_t [|v_t| | 1], dv_t ~ |Sh|_t^T |phi(k_t)|, d(S, z)_in ~
+    alpha_0 |Sh|_0, dalpha_t ~ sum_c |Sh|_t |S|_(t-1)."""
+    import oracle
+    q, k, v, do, o, den, al = (f64(x) for x in (q, k, v, do, o, den, alpha))
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    fq, fk = np.abs(oracle.feature_map(q, fmap)), np.abs(oracle.feature_map(k, fmap))
+    vp = np.concatenate([np.abs(v), np.ones((B, H, N, 1))], -1)
+    dn = np.concatenate([np.abs(do), np.abs(np.sum(do * o, -1, keepdims=True))], -1) / \
+        den[..., None]
+    S = np.zeros((B, H, d, dv + 1))
+    if S0 is not None:
+        S[..., :dv] = np.abs(f64(S0))
+    if z0 is not None:
+        S[..., dv] = np.abs(f64(z0))
+    Ss = [S]
+    sq = np.empty((B, H, N, d))
+    for t in range(N):
+        S = al[:, :, t, :, None] * S + fk[:, :, t, :, None] * vp[:, :, t, None, :]
+        Ss.append(S)
+        sq[:, :, t] = np.einsum("bhfc,bhc->bhf", S, dn[:, :, t])
+    Sh = np.zeros((B, H, d, dv + 1))
+    if dS_N is not None:
+        Sh[..., :dv] = np.abs(f64(dS_N))
+    if dz_N is not None:
+        Sh[..., dv] = np.abs(f64(dz_N))
+    sk, sa = np.empty((B, H, N, d)), np.empty((B, H, N, d))
+    sv = np.empty((B, H, N, dv))
+    for t in range(N - 1, -1, -1):
+        Sh = Sh + fq[:, :, t, :, None] * dn[:, :, t, None, :]
+        sk[:, :, t] = np.einsum("bhfc,bhc->bhf", Sh, vp[:, :, t])
+        sv[:, :, t] = np.einsum("bhfc,bhf->bhc", Sh[..., :dv], fk[:, :, t])
+        sa[:, :, t] = np.sum(Sh * Ss[t], -1)
+        Sh = al[:, :, t, :, None] * Sh
+    return sq, sk, sv, Sh[..., :dv], Sh[..., dv], sa
+
+
 def _delta_states(q, k, v, g, alpha, S0):
     """The states of the gated delta rule before every token and after the
     last (fp64, from the oracle's step), [B, H, N + 1, d, dv]."""

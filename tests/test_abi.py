@@ -227,6 +227,31 @@ def test_backward_rejects_invalid_arguments(lib, bad):
     assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EINVAL
 
 
+def test_backward_per_channel_decay_arguments(lib):
+    """alpha (GLA's decay) excludes gamma, needs grad_alpha, and fp32 takes
+    it only up to d = 64; with alpha the workspace holds the per-token and
+    per-chunk buffers even at one segment, and must be 16-byte aligned."""
+    fake = ctypes.c_void_p(0x1000)
+    a = _bargs(alpha=fake, grad_alpha=fake, gamma=fake)
+    assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EINVAL
+    a = _bargs(grad_alpha=fake)  # no alpha
+    assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EINVAL
+    a = _bargs(alpha=fake)  # no grad_alpha with tokens
+    assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EINVAL
+    a = _bargs(dtype=_lib.LA_F32, d=128, dv=16, alpha=fake, grad_alpha=fake)
+    assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+    assert lib.la_backward_workspace_size(ctypes.byref(a)) == ctypes.c_size_t(-1).value
+    a = _bargs(alpha=fake, grad_alpha=fake)
+    n = lib.la_backward_workspace_size(ctypes.byref(a))
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    B, H, N, d, dv = 1, 2, 4, 8, 8
+    nch = (N + 31) // 32
+    assert n == r256(B * H * N * d * 4) + r256(B * H * nch * (d * dv + 2 * d) * 4)
+    assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EWORKSPACE
+    a.workspace, a.workspace_bytes = ctypes.c_void_p(0x1004), n
+    assert lib.la_backward(ctypes.byref(a), None) == _lib.LA_EINVAL
+
+
 def test_backward_unsupported_and_sizes(lib):
     assert lib.la_backward(None, None) == _lib.LA_EINVAL
     # fp32 with d and dv above 64 runs over two value halves: it needs a
@@ -259,8 +284,9 @@ def test_prefill_den_out_only_for_linear(lib):
     a = _args(rule=_lib.LA_RULE_DELTA, fmap=_lib.LA_FMAP_IDENTITY, g=ctypes.c_void_p(0x2000),
               den_out=ctypes.c_void_p(0x3000))
     assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EINVAL
+    # with GLA's per-channel decay too (the backward takes alpha): a valid size
     a = _args(den_out=ctypes.c_void_p(0x3000), alpha=ctypes.c_void_p(0x2000))
-    assert lib.la_prefill(ctypes.byref(a), None) == _lib.LA_EUNSUPPORTED
+    assert lib.la_prefill_workspace_size(ctypes.byref(a)) != ctypes.c_size_t(-1).value
 
 
 @pytest.mark.parametrize("dtype,esz", [(_lib.LA_BF16, 2), (_lib.LA_F32, 4)])
