@@ -38,6 +38,8 @@ graph.  Alongside:
                 backward kernels' times, and the dominant backward kernel
                 against HBM peak (its algorithmic bytes: q, k, v, o, dL/do
                 and the denominators read once, its gradients written once);
+  train_gla     the same training step with GLA's per-channel decay (the
+                B=4 H=16 N=4096 d=64 workload with alpha), dalpha included;
   train_delta   a training step of the gated delta-rule workload: the
                 prefill, then la_delta_backward (dq, dk, dv, dg) for a
                 seeded dL/do, with the backward kernels' times and the
@@ -81,6 +83,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--no-train-gla", action="store_true",
+                    help="skip the training step with GLA's per-channel decay")
     ap.add_argument("--no-train-delta", action="store_true",
                     help="skip only the gated-delta training leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -161,9 +165,9 @@ def library_kernel_name(raw):
         return None
     if "bwd_rscan_kernel" in raw:
         return "linear_bwd_rscan"
-    if "bwd_dq_kernel" in raw:
+    if "bwd_dq_kernel" in raw or "bwd_dq_ch_kernel" in raw:
         return "linear_bwd_dq"
-    if "bwd_dkv_kernel" in raw:
+    if "bwd_dkv_kernel" in raw or "bwd_dkv_ch_kernel" in raw:
         return "linear_bwd_dkv"
     if "prep_kernel" in raw:  # its last template flag: the backward's records
         import re
@@ -237,7 +241,8 @@ def bench_args_for_counters(wid):
     with theirs)."""
     if wid == 3:
         return "--workload 3 --decode-steps 16 --no-cpu-baseline"
-    own = {2: " --no-train-delta", 5: ""}.get(wid, " --no-train")
+    own = {2: " --no-train-delta --no-train-gla", 5: "", 7: " --no-train-delta"}.get(
+        wid, " --no-train")
     return (f"--workload {wid} --steps 5 --warmup 2 --no-decode --no-extra --no-cpu-baseline"
             + own)
 
@@ -613,10 +618,14 @@ def bench_workload(la, lib, torch, w, steps, warmup):
 
 def bwd_bytes_per_head_token(w, kname):
     """Algorithmic bytes of one backward kernel per head-token: q, k, v, o,
-    dL/do and den read once; its gradients written once."""
+    dL/do and den read once; its gradients written once (with GLA's
+    per-channel decay also alpha read, and dalpha written by dk/dv; fp32)."""
     e = w.dtype.itemsize
     rd = (2 * w.d + 3 * w.dv) * e + 4
-    return rd + (w.d * e if kname == "linear_bwd_dq" else (w.d + w.dv) * e)
+    b = rd + (w.d * e if kname == "linear_bwd_dq" else (w.d + w.dv) * e)
+    if w.decay == "channel":
+        b += 4 * w.d * (1 if kname == "linear_bwd_dq" else 2)
+    return b
 
 
 def bench_train(la, lib, torch, w, steps, warmup):
@@ -626,19 +635,20 @@ def bench_train(la, lib, torch, w, steps, warmup):
 
     x = inputs.make_prefill(w, "cuda")
     do = inputs.make_grad_out(w, "cuda")
-    q, k, v, gamma = x["q"], x["k"], x["v"], x["gamma"]
+    q, k, v, gamma, al = x["q"], x["k"], x["v"], x["gamma"], x.get("alpha")
     B, H, N, d, dv = w.B, w.H, w.N, w.d, w.dv
     o = torch.empty((B, H, N, dv), dtype=w.dtype, device="cuda")
     den = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    wsf = torch.empty(max(la.workspace_size(q, k, v, gamma=gamma, eps=w.eps), 1),
+    wsf = torch.empty(max(la.workspace_size(q, k, v, gamma=gamma, alpha=al, eps=w.eps,
+                                            den_out=den), 1),
                       dtype=torch.uint8, device="cuda")
 
     def fwd():
-        la.prefill(q, k, v, gamma=gamma, eps=w.eps, o=o, den_out=den, workspace=wsf,
+        la.prefill(q, k, v, gamma=gamma, alpha=al, eps=w.eps, o=o, den_out=den, workspace=wsf,
                    return_state=False)
 
     def bwd():  # the forward's segment states are reused from its workspace
-        return la.backward(q, k, v, o, den, do, gamma=gamma, state_grad=False,
+        return la.backward(q, k, v, o, den, do, gamma=gamma, alpha=al, state_grad=False,
                            fwd_workspace=wsf)
 
     def step():
@@ -1007,6 +1017,10 @@ def main():
     if not args.no_train and w.rule == "linear" and w.decay in ("none", "per_head") \
             and not w.conv:
         line["train"] = bench_train(la, lib, torch, w, max(10, args.steps // 4), 5)
+    if not args.no_train and not args.no_train_gla and \
+            (w.decay == "channel" or args.workload == 2):
+        wg = w if w.decay == "channel" else inputs.WORKLOADS[7]
+        line["train_gla"] = bench_train(la, lib, torch, wg, max(10, args.steps // 4), 5)
     if not args.no_train and not args.no_train_delta and \
             (w.rule == "delta" or args.workload == 2):
         wd = w if w.rule == "delta" else inputs.WORKLOADS[5]

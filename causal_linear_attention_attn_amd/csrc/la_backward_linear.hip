@@ -870,71 +870,113 @@ struct alignas(16) ChanB {
   double tot[BC::DK];          // dq: log2 decay of the segment up to the chunk
 };
 
-// The chunk's prefix sums (fp64, one thread per channel; channels past d
-// get alpha = 1) and the tables above.  TOT: also the running segment decay.
-template <class BC, bool TOT>
-__device__ __forceinline__ void chan_tables(ChanB<BC> &cb, const float *al, int c0, int Lc,
-                                            int d) {
-  static_assert(BC::C == 32, "two 16-token blocks per chunk");
-  constexpr int LDL = ChanB<BC>::LDL;
-  const int f = threadIdx.x;
-  if (f >= BC::DK) return;
-  double lb = 0.0, M[2], E[2], R[2];
+// The chunk's alpha rows, loaded a chunk ahead (element i of the C x DK
+// block, row-major, i = thread + n NT), then staged in the exponent tile.
+template <class BC>
+struct ARegs {
+  static_assert((BC::C * BC::DK) % BC::NT == 0, "whole steps");
+  static constexpr int NA = BC::C * BC::DK / BC::NT;
+  float a[NA];
+};
+
+template <class BC>
+__device__ __forceinline__ void load_alpha(ARegs<BC> &A, __amdgpu_buffer_rsrc_t ra, int c0,
+                                           int Lc, int d) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    float l[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = 16 * b + i;
-      const float a = (t < Lc && f < d) ? al[(size_t)(c0 + t) * d + f] : 1.f;
-      l[i] = fmaxf(log2f(a), kLog2AlphaMinB);
-    }
-    R[b] = lb;
-    double m = lb;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m += (double)l[i];
-    double e = m;
-#pragma unroll
-    for (int i = 8; i < 16; ++i) e += (double)l[i];
-    M[b] = m;
-    E[b] = e;
-    // lb_i - M_b: minus the terms after i up to the reference, or the terms
-    // after the reference up to i
-    double acc = 0.0;
-#pragma unroll
-    for (int i = 7; i >= 0; --i) {
-      cb.lbr[(16 * b + i) * LDL + f] = (float)(-acc);
-      acc += (double)l[i];
-    }
-    acc = 0.0;
-#pragma unroll
-    for (int i = 8; i < 16; ++i) {
-      acc += (double)l[i];
-      cb.lbr[(16 * b + i) * LDL + f] = (float)acc;
-    }
-    cb.mr[b][f] = (float)(M[b] - R[b]);
-    cb.rf[b][f] = exp2f((float)R[b]);
-    cb.fm[b][f] = exp2f((float)M[b]);
-    cb.em[b][f] = (float)(E[b] - M[b]);
-    lb = e;
-  }
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    cb.fl[b][f] = exp2f((float)(lb - M[b]));
-    cb.le[b][f] = exp2f((float)(lb - E[b]));
-  }
-  cb.mm[f] = exp2f((float)(M[1] - M[0]));
-  cb.dl[f] = exp2f((float)lb);
-  if constexpr (TOT) {
-    const double before = cb.tot[f];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) cb.qf[b][f] = exp2f((float)(before + R[b]));
-    cb.tot[f] = before + lb;
+  for (int n = 0; n < ARegs<BC>::NA; ++n) {
+    const int i = threadIdx.x + n * BC::NT;
+    const int row = i / BC::DK, col = i % BC::DK;
+    const bool ok = row < Lc && col < d;
+    A.a[n] = buf_load1(ra, ok ? (uint32_t)(((size_t)(c0 + row) * d + col) * 4) : kOOB,
+                       (float *)nullptr);
   }
 }
 
-// phi rows times 2^(sgn lbr) into F (zero past the chunk and past d).
 template <class BC>
+__device__ __forceinline__ void stage_alpha(ChanB<BC> &cb, const ARegs<BC> &A) {
+#pragma unroll
+  for (int n = 0; n < ARegs<BC>::NA; ++n) {
+    const int i = threadIdx.x + n * BC::NT;
+    cb.lbr[(i / BC::DK) * ChanB<BC>::LDL + i % BC::DK] = A.a[n];
+  }
+}
+
+// Threads per channel of the per-channel passes (lanes next to each other),
+// each with JP consecutive tokens of the chunk.
+template <class BC>
+struct ChanSplit {
+  static constexpr int P = BC::NT / BC::DK, JP = BC::C / P;
+  static_assert(P * BC::DK == BC::NT && JP * P == BC::C && (P & (P - 1)) == 0 && P <= 16,
+                "threads per channel");
+};
+
+// The value v of the lane `owner` threads further in this channel's group.
+__device__ __forceinline__ double shfl_group(double v, int base, int owner) {
+  return __shfl(v, base + owner);
+}
+
+// The chunk's prefix sums (fp64; P threads per channel, each over its JP
+// tokens of the staged alpha column, replaced in place by the exponents;
+// channels past d and rows past the chunk take alpha = 1) and the tables
+// above.  TOT: also the running segment decay.
+template <class BC, bool TOT>
+__device__ __forceinline__ void chan_tables(ChanB<BC> &cb, int Lc, int d) {
+  static_assert(BC::C == 32, "two 16-token blocks per chunk");
+  constexpr int LDL = ChanB<BC>::LDL, P = ChanSplit<BC>::P, JP = ChanSplit<BC>::JP;
+  const int f = threadIdx.x / P, pp = threadIdx.x % P;
+  const int base = (threadIdx.x & 63) - pp;
+  double lb[JP];
+  double part = 0.0;
+#pragma unroll
+  for (int jj = 0; jj < JP; ++jj) {
+    const int t = pp * JP + jj;
+    const float a = (t < Lc && f < d) ? cb.lbr[t * LDL + f] : 1.f;
+    part += (double)fmaxf(log2f(a), kLog2AlphaMinB);
+    lb[jj] = part;
+  }
+  double before = 0.0;  // the earlier threads' parts
+#pragma unroll
+  for (int m = 0; m < P - 1; ++m) {
+    const double x = shfl_group(part, base, m);
+    if (m < pp) before += x;
+  }
+#pragma unroll
+  for (int jj = 0; jj < JP; ++jj) lb[jj] += before;
+  // block references: M_b at token 16 b + 7, E_b at 16 b + 15 (E_1 = lb_L)
+  const double M0 = shfl_group(lb[7 % JP], base, 7 / JP);
+  const double E0 = shfl_group(lb[15 % JP], base, 15 / JP);
+  const double M1 = shfl_group(lb[23 % JP], base, 23 / JP);
+  const double L = shfl_group(lb[31 % JP], base, 31 / JP);
+#pragma unroll
+  for (int jj = 0; jj < JP; ++jj) {
+    const int t = pp * JP + jj;
+    cb.lbr[t * LDL + f] = (float)(lb[jj] - (t < 16 ? M0 : M1));
+  }
+  if (pp == 0) {
+    const double M[2] = {M0, M1}, E[2] = {E0, L}, R[2] = {0.0, E0};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      cb.mr[b][f] = (float)(M[b] - R[b]);
+      cb.rf[b][f] = exp2f((float)R[b]);
+      cb.fm[b][f] = exp2f((float)M[b]);
+      cb.em[b][f] = (float)(E[b] - M[b]);
+      cb.fl[b][f] = exp2f((float)(L - M[b]));
+      cb.le[b][f] = exp2f((float)(L - E[b]));
+    }
+    cb.mm[f] = exp2f((float)(M1 - M0));
+    cb.dl[f] = exp2f((float)L);
+    if constexpr (TOT) {
+      const double seg = cb.tot[f];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) cb.qf[b][f] = exp2f((float)(seg + R[b]));
+      cb.tot[f] = seg + L;
+    }
+  }
+}
+
+// phi rows times 2^(sgn lbr) into F (zero past the chunk and past d); RB:
+// times 2^(lbr + M_b - R_b) = 2^(lb_t - R_b) instead (at most 1).
+template <class BC, bool RB = false>
 __device__ __forceinline__ void commit_feat_ch(typename BC::type *F, const ChanB<BC> &cb,
                                                float sgn,
                                                const typename BC::vec (&X)[BRegs<BC>::NQ],
@@ -950,7 +992,8 @@ __device__ __forceinline__ void commit_feat_ch(typename BC::type *F, const ChanB
 #pragma unroll
     for (int e = 0; e < BC::VEC; ++e) {
       const float y = (row < Lc && col0 + e < d) ? feat(to_f32(X[n][e]), fmap) : 0.f;
-      f[e] = from_f32<T>(y * exp2f(sgn * cb.lbr[row * ChanB<BC>::LDL + col0 + e]));
+      const float x = cb.lbr[row * ChanB<BC>::LDL + col0 + e];
+      f[e] = from_f32<T>(y * exp2f(RB ? x + cb.mr[row >> 4][col0 + e] : sgn * x));
     }
     *reinterpret_cast<V *>(F + row * BC::LDK + col0) = f;
   }
@@ -1057,7 +1100,7 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDqCh<
   hr.g = head_rsrc<T>(p.dout, bh, N, dv);
   hr.den = head_rsrc<float>(p.den, bh, N, 1);
   const __amdgpu_buffer_rsrc_t rdq = head_rsrc<T>(p.dq, bh, N, d);
-  const float *al = p.alpha + (size_t)bh * N * d;
+  const __amdgpu_buffer_rsrc_t ra = head_rsrc<float>(p.alpha, bh, N, d);
   float *ux = p.ux + (size_t)bh * N * d;
   const int nch = (N + BC::C - 1) / BC::C;
   zero_tail_columns<BC>(sm.St);
@@ -1075,14 +1118,20 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDqCh<
   for (int i = 0; i < BC::SPW; ++i) Ra[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   BRegs<BC> R;
   load_chunk<BC, VK, true, true, true, true>(R, hr, t_begin, min(BC::C, N - t_begin), d, dv);
+  ARegs<BC> A;
+  load_alpha<BC>(A, ra, t_begin, min(BC::C, N - t_begin), d);
   __syncthreads();
 
   for (int c0 = t_begin; c0 < t_end; c0 += BC::C) {
     const int Lc = min(BC::C, N - c0);
-    chan_tables<BC, true>(cb, al, c0, Lc, d);
+    stage_alpha<BC>(cb, A);
+    __syncthreads();
+    chan_tables<BC, true>(cb, Lc, d);
+    if (c0 + BC::C < t_end) load_alpha<BC>(A, ra, c0 + BC::C, min(BC::C, N - c0 - BC::C), d);
     __syncthreads();
     commit_feat<BC>(sm.Fq, nullptr, nullptr, R.q, Lc, d, p.fmap);
     commit_feat_ch<BC>(sm.Fk, cb, -1.f, R.k, Lc, d, p.fmap);
+    if (seg > 0) commit_feat_ch<BC, true>(sm.KW, cb, 1.f, R.q, Lc, d, p.fmap);
     commit_values<BC>(sm.Vp, R, Lc);
     commit_dn<BC>(sm.dN, R, Lc);
     state_copy<BC>(sm.St, Sa, wv, li, lg);
@@ -1148,14 +1197,12 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDqCh<
         const int st = wv + BC::NW * i;
         if (st >= BC::NST) continue;
         const int fb = st / BC::NVP, vb = st % BC::NVP;
-        const int f = 16 * fb + li, b = lg >> 1;
+        const int f = 16 * fb + li;
         Frag<T> a, bb;
-        frag_kr(a, sm.Fq, BC::LDK, 16 * fb, 0, li, lg);
-        const float w0 = cb.qf[b][f], mrb = cb.mr[b][f];
+        frag_kr(a, sm.KW, BC::LDK, 16 * fb, 0, li, lg);  // phi(q) 2^(lb_t - R_b)
+        const float w0 = cb.qf[lg >> 1][f];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          a.v[e] = from_f32<T>(to_f32(a.v[e]) *
-                               (exp2f(cb.lbr[(8 * lg + e) * LDL + f] + mrb) * w0));
+        for (int e = 0; e < 8; ++e) a.v[e] = from_f32<T>(to_f32(a.v[e]) * w0);
         frag_kr(bb, sm.dN, BC::LDV, 16 * vb, 0, li, lg);
         mma(Ra[i], a, bb);
       }
@@ -1174,8 +1221,9 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDqCh<
 // ---- dk, dv with a per-channel decay: chunks right to left, adjoint state ---
 template <class BC>
 struct alignas(16) SmemDkvCh {
-  static_assert(sizeof(SmemDkv<BC, false>::Ok) >= BC::NVP * BC::DK * sizeof(float),
-                "the anchor partials fit the dk staging tile");
+  static_assert(sizeof(SmemDkv<BC, false>::Ok) >= BC::NVP * BC::DK * sizeof(float) &&
+                    sizeof(SmemDkv<BC, false>::Ok) >= 2 * BC::NW * 64 * sizeof(float),
+                "the anchor partials and the dalpha range totals fit the dk staging tile");
   SmemDkv<BC, false> m;  // Fq holds phi(q) 2^(lb_t - M_b), Fk phi(k)
   typename BC::type Kh[BC::C * BC::LDK];  // phi(k) 2^(M_b - lb_j)
   ChanB<BC> c;
@@ -1206,6 +1254,7 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
   hr.den = head_rsrc<float>(p.den, bh, N, 1);
   const __amdgpu_buffer_rsrc_t rdk = head_rsrc<T>(p.dk, bh, N, d),
                                rdv = head_rsrc<T>(p.dv_, bh, N, dv);
+  const __amdgpu_buffer_rsrc_t ra = head_rsrc<float>(p.alpha, bh, N, d);
   const float *al = p.alpha + (size_t)bh * N * d;
   const float *ux = p.ux + (size_t)bh * N * d;
   float *dal = p.dalpha + (size_t)bh * N * d;
@@ -1222,6 +1271,8 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
   const int last = t_begin + ((t_end - t_begin - 1) / BC::C) * BC::C;
   BRegs<BC> R;
   load_chunk<BC, VK, true, true, true, true>(R, hr, last, min(BC::C, N - last), d, dv);
+  ARegs<BC> A;
+  load_alpha<BC>(A, ra, last, min(BC::C, N - last), d);
   __syncthreads();
 
   constexpr int NKT = BC::NTB * BC::NFB;
@@ -1229,7 +1280,9 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
   const float amin = exp2f(kLog2AlphaMinB);
   for (int c0 = last; c0 >= t_begin; c0 -= BC::C) {
     const int Lc = min(BC::C, N - c0);
-    chan_tables<BC, false>(cb, al, c0, Lc, d);
+    stage_alpha<BC>(cb, A);
+    __syncthreads();
+    chan_tables<BC, false>(cb, Lc, d);
     __syncthreads();
     // <Sh+, S-> per channel (Sh+: this wave's adjoint tiles as they enter
     // the chunk; S-: the forward state entering it, left by dq): one partial
@@ -1237,19 +1290,17 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
     // tiles), summed in a fixed order below
     float *partv = reinterpret_cast<float *>(sm.Ok);
     {
-      const float *sp = p.chs + ((size_t)bh * nch + c0 / BC::C) * p.wrec;
+      f32x4 Sm[BC::SPW];  // loaded together, in the adjoint tiles' layout
+      slot_load<BC>(Sm, p.chs + ((size_t)bh * nch + c0 / BC::C) * p.wrec, d, dv, p.slot_vec, wv,
+                    li, lg);
 #pragma unroll
       for (int i = 0; i < BC::SPW; ++i) {
         const int st = wv + BC::NW * i;
         const int fb = st / BC::NVP, vb = st % BC::NVP;
-        const int c = 16 * vb + li;
-        const bool val = vb < BC::NVP - 1;
-        const bool ok = st < BC::NST && (val ? c < dv : li == 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int f = 16 * fb + 4 * lg + r;
-          float part = 0.f;
-          if (ok && f < d) part = Sa[i][r] * sp[val ? (size_t)c * d + f : (size_t)d * dv + f];
+          float part = Sa[i][r] * Sm[i][r];
 #pragma unroll
           for (int m = 1; m < 16; m <<= 1) part += __shfl_xor(part, m);
           if (li == 0 && st < BC::NST) partv[vb * BC::DK + f] = part;
@@ -1262,8 +1313,6 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
     commit_values<BC>(sm.Vp, R, Lc);
     commit_dn<BC>(sm.dN, R, Lc);
     state_copy<BC>(sm.Sh, Sa, wv, li, lg);
-    if (c0 > t_begin)
-      load_chunk<BC, VK, true, true, true, true>(R, hr, c0 - BC::C, BC::C, d, dv);
     __syncthreads();
 
     tri_tiles_ch<BC>(sm.Ad, sm.Fq, Kh, cb.mm, wv, li, lg);
@@ -1349,9 +1398,9 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
     store_rows<BC, VK>(rdk, sm.Ok, BC::LDKS, BC::QCB, c0, Lc, d);
     store_rows<BC, VK>(rdv, sm.Ov, BC::LDOS, BC::VCB, c0, Lc, dv);
     // dalpha: the second sum's terms into the (now unused) exponent tile, then
-    // one thread per channel: their prefix over the keys before s, the
-    // third sum's suffix from dq's terms, and the fourth as a running
-    // G_j = sum_(t>=s) phi(q_t) 2^(lb_t - M) dA_tj over the keys j < s
+    // per channel their prefix over the keys before s, the third sum's suffix
+    // from dq's terms, and the fourth as a running G_j = sum_(t>=s) phi(q_t)
+    // 2^(lb_t - M) dA_tj over the keys j < s
 #pragma unroll
     for (int n = 0; n < KPW; ++n) {
       const int ti = wv + BC::NW * n;
@@ -1362,34 +1411,93 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
         cb.lbr[(16 * jt + 4 * lg + r) * LDL + 16 * fb + li] = xr[n][r];
     }
     __syncthreads();
-    for (int f = threadIdx.x; f < d; f += BC::NT) {
-      float run = 0.f;  // exclusive prefix of the second sum's terms, in place
-      for (int j = 0; j < Lc; ++j) {
-        const float y = cb.lbr[j * LDL + f];
-        cb.lbr[j * LDL + f] = run;
-        run += y;
+    {
+      // wave wv takes the JP tokens pp JP .. of channels 64 fg + lane
+      // (pp = wv % P, fg = wv / P): every lane sums its own channel, no
+      // exchange inside the walk
+      constexpr int FG = BC::DK / 64, P = BC::NW / FG, JP = BC::C / P;
+      static_assert(FG * 64 == BC::DK && P * FG == BC::NW && JP * P == BC::C, "token ranges");
+      const int pp = wv % P, f = 64 * (wv / P) + lane;
+      const int s0 = pp * JP;
+      const bool fok = f < d;
+      float* ytot = partv;                // [P][DK] the ranges' totals (staging tile,
+      float* utot = partv + P * BC::DK;   // free again after the dk/dv rows went out)
+      float base[JP], alr[JP];
+      float yt = 0.f, ut = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < JP; ++jj) {
+        const int t = s0 + jj;
+        const bool ok = fok && t < Lc;
+        const size_t at = (size_t)(c0 + t) * d + f;
+        base[jj] = ok ? cb.lbr[t * LDL + f] : 0.f;  // the second sum's term of key t
+        alr[jj] = ok ? al[at] : 1.f;
+        yt += base[jj];
+        ut += ok ? ux[at] : 0.f;
       }
-      float G[BC::C];
+      ytot[pp * BC::DK + f] = yt;
+      utot[pp * BC::DK + f] = ut;
+      __syncthreads();
+      float run = cb.anc[f] * cb.dl[f], suf = 0.f;  // the first sum, then the others' parts
+      for (int m = 0; m < P; ++m) {
+        if (m < pp) run += ytot[m * BC::DK + f];
+        if (m > pp) suf += utot[m * BC::DK + f];
+      }
+      // prefix of the second sum over the keys before s (exclusive), suffix of
+      // the third from s (inclusive); sums only, every term kept carries alpha_s
+      float pre[JP];
 #pragma unroll
-      for (int j = 0; j < BC::C; ++j) G[j] = 0.f;
-      const float a1 = cb.anc[f] * cb.dl[f], mmf = cb.mm[f];
-      float a3 = 0.f;
-      for (int s = Lc - 1; s >= 0; --s) {
-        const float qs = to_f32(sm.Fq[s * BC::LDK + f]);
-        const float qx = s >= 16 ? qs * mmf : qs;  // keys of block 0 under a block-1 query
-        float a4 = 0.f;
+      for (int jj = 0; jj < JP; ++jj) {
+        pre[jj] = run;
+        run += base[jj];
+      }
 #pragma unroll
-        for (int j = 0; j < BC::C; ++j) {
-          if (j < s) {
-            G[j] = fmaf(j < 16 ? qx : qs, to_f32(sm.dA[s * BC::LDC + j]), G[j]);
-            a4 = fmaf(to_f32(Kh[j * BC::LDK + f]), G[j], a4);
+      for (int jj = JP - 1; jj >= 0; --jj) {
+        const int t = s0 + jj;
+        suf += (fok && t < Lc) ? ux[(size_t)(c0 + t) * d + f] : 0.f;
+        base[jj] = pre[jj] + suf;
+      }
+      // the fourth sum: G_j = sum_(t>=s) phi(q_t) 2^(lb_t - M) dA_tj for the keys
+      // j < s, walking t down from the chunk's end to this range's first
+      // token, eight keys at a time (only the groups below the range's last
+      // token).  Branch-free: the row's entries past the diagonal are zero, and
+      // a key j >= t enters G_j only with terms of queries at or after j,
+      // which an output s <= j never reads; the output masks its keys.
+      using T = typename BC::type;
+      const float mmf = cb.mm[f];
+      for (int j0 = 0; j0 < s0 + JP - 1; j0 += 8) {  // (uniform)
+        float G[8], kq[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          G[jj] = 0.f;
+          kq[jj] = to_f32(Kh[(j0 + jj) * BC::LDK + f]);
+        }
+        for (int t = Lc - 1; t >= s0; --t) {  // (uniform)
+          const float qt = to_f32(sm.Fq[t * BC::LDK + f]);
+          const float qk = j0 < 16 && t >= 16 ? qt * mmf : qt;  // block-0 keys, block-1 query
+          T arow[8];  // row t of dA at these keys (the same for every lane)
+          __builtin_memcpy(arow, sm.dA + t * BC::LDC + j0, sizeof(arow));
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) G[jj] = fmaf(qk, to_f32(arow[jj]), G[jj]);
+          if (t < s0 + JP) {  // an output of this range: add sum_(j<t) k^_j G_j
+            float a4 = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) a4 = fmaf(j0 + jj < t ? kq[jj] : 0.f, G[jj], a4);
+#pragma unroll
+            for (int jj = 0; jj < JP; ++jj) base[jj] += s0 + jj == t ? a4 : 0.f;
           }
         }
-        const size_t at = (size_t)(c0 + s) * d + f;
-        a3 += ux[at];
-        const float a = al[at];
-        dal[at] = a >= amin ? (a1 + cb.lbr[s * LDL + f] + a3 + a4) / a : 0.f;
       }
+#pragma unroll
+      for (int jj = 0; jj < JP; ++jj) {
+        const int t = s0 + jj;
+        if (fok && t < Lc)
+          dal[(size_t)(c0 + t) * d + f] = alr[jj] >= amin ? base[jj] / alr[jj] : 0.f;
+      }
+    }
+    // the previous chunk's rows go out only now (registers the walk needed)
+    if (c0 > t_begin) {
+      load_chunk<BC, VK, true, true, true, true>(R, hr, c0 - BC::C, BC::C, d, dv);
+      load_alpha<BC>(A, ra, c0 - BC::C, BC::C, d);
     }
     __syncthreads();
   }
