@@ -143,3 +143,47 @@ def test_gla_workload_training_sampled():
         assert_grad_close(dk[sl], r[1], sk, tol, f"dk head {b},{h}")
         assert_grad_close(dv[sl], r[2], sv, tol, f"dv head {b},{h}")
         assert_grad_close(dal[sl], r[5], sa, tol, f"dalpha head {b},{h}")
+
+
+@pytest.mark.parametrize("reuse", [True, False], ids=["fwd_ws", "recompute"])
+def test_gla_training_through_conv(reuse):
+    """GLA's decay behind the short convolution: the training forward (the
+    convolution as a pass, then the rule keeping denominators under alpha)
+    and la_backward with both, against the oracle's backward through the
+    convolution; input, filter, cache, state and decay gradients."""
+    B, H, N, d, dv, w = 2, 2, 300, 64, 64, 4
+    wid = 1996
+    q, k, v, do, al = _case(B, H, N, d, dv, torch.bfloat16, wid, 0.5)
+    W = inputs.normal((H, w, 2 * d + dv), wid, 6, "cpu", 0.25 / np.sqrt(w))
+    W[:, w - 1] += 1.0
+    W = W.to(DEV)
+    C0 = inputs.normal((B, H, w - 1, 2 * d + dv), wid, 7, "cpu", 0.1, torch.bfloat16).to(DEV)
+    dCo = inputs.normal((B, H, w - 1, 2 * d + dv), wid, 8, "cpu", 1.0, torch.bfloat16).to(DEV)
+    C = C0.clone()
+    den = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(1, la.workspace_size(q, k, v, alpha=al, conv_weight=W, den_out=den)),
+                     dtype=torch.uint8, device=DEV)
+    o, _, _ = la.prefill(q, k, v, alpha=al, conv_weight=W, conv_cache=C, den_out=den,
+                         workspace=ws, return_state=False)
+    dq, dk, dv_, dS, dz, dW, dC, dal = la.backward(
+        q, k, v, o, den, do, alpha=al, conv_weight=W, conv_cache=C0, dconv_cache_out=dCo,
+        fwd_workspace=ws if reuse else None)
+    torch.cuda.synchronize()
+    r = oracle.linear_backward_conv(cpu(q), cpu(k), cpu(v), cpu(do), cpu(W), conv_cache=cpu(C0),
+                                    dconv_cache_out=cpu(dCo), alpha=cpu(al), eps=1e-6)
+    tol = TOL[torch.bfloat16]
+    # the convolved inputs' gradients' scales, then the chain rule on magnitudes
+    cw, cc = cpu(W).double().numpy(), cpu(C0).double().numpy()
+    ys = [oracle.short_conv(cpu(x), cw[..., sl], cc[..., sl])[0]
+          for x, sl in ((q, slice(0, d)), (k, slice(d, 2 * d)), (v, slice(2 * d, None)))]
+    yo, _, _ = oracle.linear_prefill(*ys, alpha=cpu(al), eps=1e-6)
+    yden = oracle.linear_denominators(ys[0], ys[1], alpha=cpu(al), eps=1e-6)
+    sq, sk, sv, sS, sz, sa = gla_grad_scales(*ys, cpu(do), yo, yden, cpu(al))
+    from test_gpu_conv_backward import _conv_scales
+    sx, sW, sC = _conv_scales(q, k, v, W, C0, dCo, (sq, sk, sv))
+    for name, got, want, sc in zip(("dq", "dk", "dv"), (dq, dk, dv_), r[:3], sx):
+        assert_grad_close(got, want, sc, tol, name)
+    assert_grad_close(dW, r[3], sW, tol, "dconv_weight")
+    assert_grad_close(dC, r[4], sC, tol, "dconv_cache")
+    assert_grad_close(dS, r[5], sS, tol, "dS_in")
+    assert_grad_close(dal, r[7], sa, tol, "dalpha")
