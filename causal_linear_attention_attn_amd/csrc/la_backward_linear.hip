@@ -1219,8 +1219,70 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDqCh<
 }
 
 // ---- dk, dv with a per-channel decay: chunks right to left, adjoint state ---
+// The cross-block terms of dalpha's fourth sum, per token and channel (fp32,
+// row stride LDX), then the token ranges' totals of them ([NW][DK]), in the
+// adjoint copy's tile.
+template <class BC>
+struct CrossB {
+  static constexpr int LDX = BC::DK + 4;
+  static constexpr size_t bytes = ((size_t)BC::C * LDX + (size_t)BC::NW * BC::DK) * sizeof(float);
+  static_assert(BC::C == 32 && BC::NTB == 2, "two 16-token blocks per chunk");
+};
+
+// xc[j][f] = k^_j Y_j (j in block 0) and xc[t][f] = q^_t Z_t (t in block 1),
+// with Y_j = mm sum_(t in block 1) q^_t dA_tj and Z_t = mm sum_(j in block 0)
+// dA_tj k^_j (q^ = Fq, k^ = Kh, mm = 2^(M_1 - M_0) per channel).  Wave w
+// takes the feature tiles w, w + NW, ... of both.
+template <class BC>
+__device__ __forceinline__ void cross_block_terms(float *xc, const typename BC::type *dA,
+                                                  const typename BC::type *Fq,
+                                                  const typename BC::type *Kh, const float *mm,
+                                                  int wv, int li, int lg) {
+  using T = typename BC::type;
+  constexpr int LDX = CrossB<BC>::LDX;
+  const T zero = from_f32<T>(0.f);
+  for (int fb = wv; fb < BC::NFB; fb += BC::NW) {
+    const int f = 16 * fb + li;
+    const float m = mm[f];
+    {  // Y: keys of block 0 (rows 4 lg + r), queries of block 1 only
+      Frag<T> a, b;
+      frag_kr(a, dA, BC::LDC, 0, 0, li, lg);
+      frag_kr(b, Fq, BC::LDK, 16 * fb, 0, li, lg);
+      if (lg < 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b.v[e] = zero;
+      }
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      mma(y, a, b);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * lg + r;
+        xc[j * LDX + f] = to_f32(Kh[j * BC::LDK + f]) * (y[r] * m);
+      }
+    }
+    {  // Z: queries of block 1 (rows 16 + 4 lg + r), keys of block 0 only
+      Frag<T> a, b;
+      frag_rk(a, dA, BC::LDC, 16, 0, li, lg);
+      if (lg >= 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a.v[e] = zero;
+      }
+      frag_kr(b, Kh, BC::LDK, 16 * fb, 0, li, lg);
+      f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      mma(z, a, b);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 + 4 * lg + r;
+        xc[t * LDX + f] = to_f32(Fq[t * BC::LDK + f]) * (z[r] * m);
+      }
+    }
+  }
+}
+
 template <class BC>
 struct alignas(16) SmemDkvCh {
+  static_assert(sizeof(SmemDkv<BC, false>::Sh) >= CrossB<BC>::bytes,
+                "the cross-block terms and their range totals fit the adjoint copy's tile");
   static_assert(sizeof(SmemDkv<BC, false>::Ok) >= BC::NVP * BC::DK * sizeof(float) &&
                     sizeof(SmemDkv<BC, false>::Ok) >= 2 * BC::NW * 64 * sizeof(float),
                 "the anchor partials and the dalpha range totals fit the dk staging tile");
@@ -1277,9 +1339,13 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
 
   constexpr int NKT = BC::NTB * BC::NFB;
   constexpr int KPW = (NKT + BC::NW - 1) / BC::NW;  // dk tiles per wave
+  constexpr int LDX = CrossB<BC>::LDX;
   const float amin = exp2f(kLog2AlphaMinB);
   for (int c0 = last; c0 >= t_begin; c0 -= BC::C) {
     const int Lc = min(BC::C, N - c0);
+    // (the previous chunk's cross-block terms overwrote the adjoint copy's
+    // zero columns)
+    if (c0 != last) zero_tail_columns<BC>(sm.Sh);
     stage_alpha<BC>(cb, A);
     __syncthreads();
     chan_tables<BC, false>(cb, Lc, d);
@@ -1399,8 +1465,10 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
     store_rows<BC, VK>(rdv, sm.Ov, BC::LDOS, BC::VCB, c0, Lc, dv);
     // dalpha: the second sum's terms into the (now unused) exponent tile, then
     // per channel their prefix over the keys before s, the third sum's suffix
-    // from dq's terms, and the fourth as a running G_j = sum_(t>=s) phi(q_t)
-    // 2^(lb_t - M) dA_tj over the keys j < s
+    // from dq's terms, and the fourth split by the chunk's two 16-token
+    // blocks: its pairs across the blocks from two matrix products, its pairs
+    // inside s's block as a running G_j = sum_(t>=s) phi(q_t) 2^(lb_t - M)
+    // dA_tj over the block's keys j < s
 #pragma unroll
     for (int n = 0; n < KPW; ++n) {
       const int ti = wv + BC::NW * n;
@@ -1410,6 +1478,17 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
       for (int r = 0; r < 4; ++r)
         cb.lbr[(16 * jt + 4 * lg + r) * LDL + 16 * fb + li] = xr[n][r];
     }
+    // the fourth sum's pairs across the chunk's two token blocks (query t in
+    // block 1, key j in block 0), per channel, into the adjoint copy's tile
+    // (free now): for a key j, phi(k_j)-side times Y_j = sum_(t in block 1)
+    // phi(q_t)-side dA_tj (it enters every s of block 0 after j); for a query
+    // t, phi(q_t)-side times Z_t = sum_(j in block 0) dA_tj phi(k_j)-side (it
+    // enters every s of block 1 up to t).  Both products are taken on the
+    // matrix cores with the other block's k slots zeroed (lanes lg < 2 hold
+    // the tokens of block 0); the factor 2^(M_1 - M_0) of the pairs is per
+    // channel and goes on after the product.
+    float *xc = reinterpret_cast<float *>(sm.Sh);
+    cross_block_terms<BC>(xc, sm.dA, sm.Fq, Kh, cb.mm, wv, li, lg);
     __syncthreads();
     {
       // wave wv takes the JP tokens pp JP .. of channels 64 fg + lane
@@ -1417,63 +1496,91 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
       // exchange inside the walk
       constexpr int FG = BC::DK / 64, P = BC::NW / FG, JP = BC::C / P;
       static_assert(FG * 64 == BC::DK && P * FG == BC::NW && JP * P == BC::C, "token ranges");
+      static_assert(16 % JP == 0, "a token range lies in one 16-token block");
       const int pp = wv % P, f = 64 * (wv / P) + lane;
-      const int s0 = pp * JP;
+      const int s0 = pp * JP, blk = s0 / 16;
       const bool fok = f < d;
       float* ytot = partv;                // [P][DK] the ranges' totals (staging tile,
       float* utot = partv + P * BC::DK;   // free again after the dk/dv rows went out)
-      float base[JP], alr[JP];
-      float yt = 0.f, ut = 0.f;
+      float* ctot = xc + BC::C * LDX;     // (after the cross terms)
+      float base[JP], alr[JP], cx[JP];
+      float yt = 0.f, ut = 0.f, ct = 0.f;
 #pragma unroll
       for (int jj = 0; jj < JP; ++jj) {
         const int t = s0 + jj;
         const bool ok = fok && t < Lc;
         const size_t at = (size_t)(c0 + t) * d + f;
         base[jj] = ok ? cb.lbr[t * LDL + f] : 0.f;  // the second sum's term of key t
+        cx[jj] = ok ? xc[t * LDX + f] : 0.f;         // the cross-block term of token t
         alr[jj] = ok ? al[at] : 1.f;
         yt += base[jj];
+        ct += cx[jj];
         ut += ok ? ux[at] : 0.f;
       }
       ytot[pp * BC::DK + f] = yt;
       utot[pp * BC::DK + f] = ut;
+      ctot[pp * BC::DK + f] = ct;
       __syncthreads();
-      float run = cb.anc[f] * cb.dl[f], suf = 0.f;  // the first sum, then the others' parts
+      // the first sum, then the other ranges' parts: the second sum's over the
+      // ranges before, the third's over those after; the cross-block terms
+      // over the ranges of the same block before (block 0: keys) or after
+      // (block 1: queries)
+      float run = cb.anc[f] * cb.dl[f], suf = 0.f, cc = 0.f;
       for (int m = 0; m < P; ++m) {
         if (m < pp) run += ytot[m * BC::DK + f];
         if (m > pp) suf += utot[m * BC::DK + f];
+        if (blk == 0 ? m < pp : m > pp) cc += ctot[m * BC::DK + f];
       }
       // prefix of the second sum over the keys before s (exclusive), suffix of
-      // the third from s (inclusive); sums only, every term kept carries alpha_s
+      // the third from s (inclusive); the cross-block terms likewise by block;
+      // sums only, every term kept carries alpha_s
       float pre[JP];
+      if (blk == 0) {  // (uniform)
 #pragma unroll
-      for (int jj = 0; jj < JP; ++jj) {
-        pre[jj] = run;
-        run += base[jj];
-      }
+        for (int jj = 0; jj < JP; ++jj) {
+          pre[jj] = run + cc;
+          run += base[jj];
+          cc += cx[jj];
+        }
 #pragma unroll
-      for (int jj = JP - 1; jj >= 0; --jj) {
-        const int t = s0 + jj;
-        suf += (fok && t < Lc) ? ux[(size_t)(c0 + t) * d + f] : 0.f;
-        base[jj] = pre[jj] + suf;
+        for (int jj = JP - 1; jj >= 0; --jj) {
+          const int t = s0 + jj;
+          suf += (fok && t < Lc) ? ux[(size_t)(c0 + t) * d + f] : 0.f;
+          base[jj] = pre[jj] + suf;
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < JP; ++jj) {
+          pre[jj] = run;
+          run += base[jj];
+        }
+#pragma unroll
+        for (int jj = JP - 1; jj >= 0; --jj) {
+          const int t = s0 + jj;
+          suf += (fok && t < Lc) ? ux[(size_t)(c0 + t) * d + f] : 0.f;
+          cc += cx[jj];
+          base[jj] = pre[jj] + suf + cc;
+        }
       }
-      // the fourth sum: G_j = sum_(t>=s) phi(q_t) 2^(lb_t - M) dA_tj for the keys
-      // j < s, walking t down from the chunk's end to this range's first
-      // token, eight keys at a time (only the groups below the range's last
-      // token).  Branch-free: the row's entries past the diagonal are zero, and
-      // a key j >= t enters G_j only with terms of queries at or after j,
-      // which an output s <= j never reads; the output masks its keys.
+      // the fourth sum's pairs inside the range's block: G_j = sum_(t>=s)
+      // phi(q_t) 2^(lb_t - M) dA_tj for the block's keys j < s, walking t down
+      // from the block's end to this range's first token, eight keys at a
+      // time (only the groups below the range's last token).  Branch-free: the
+      // row's entries past the diagonal are zero, and a key j >= t enters G_j
+      // only with terms of queries at or after j, which an output s <= j never
+      // reads; the output masks its keys.  (Query and key share the block's
+      // reference M, so no factor enters.)
       using T = typename BC::type;
-      const float mmf = cb.mm[f];
-      for (int j0 = 0; j0 < s0 + JP - 1; j0 += 8) {  // (uniform)
+      const int tl = min(Lc, 16 * blk + 16) - 1;
+      for (int j0 = 16 * blk; j0 < s0 + JP - 1; j0 += 8) {  // (uniform)
         float G[8], kq[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           G[jj] = 0.f;
           kq[jj] = to_f32(Kh[(j0 + jj) * BC::LDK + f]);
         }
-        for (int t = Lc - 1; t >= s0; --t) {  // (uniform)
-          const float qt = to_f32(sm.Fq[t * BC::LDK + f]);
-          const float qk = j0 < 16 && t >= 16 ? qt * mmf : qt;  // block-0 keys, block-1 query
+        for (int t = tl; t >= s0; --t) {  // (uniform)
+          const float qk = to_f32(sm.Fq[t * BC::LDK + f]);
           T arow[8];  // row t of dA at these keys (the same for every lane)
           __builtin_memcpy(arow, sm.dA + t * BC::LDC + j0, sizeof(arow));
 #pragma unroll
