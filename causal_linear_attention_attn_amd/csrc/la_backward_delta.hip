@@ -556,11 +556,7 @@ __device__ __forceinline__ void stage_rec(bf16 *tile, int ld, __amdgpu_buffer_rs
 }
 
 __device__ __forceinline__ float sum16(float x) {  // over the 16 lanes li of a slot group
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
-  return x;
+  return lane_sum<16>(x);
 }
 
 template <class G, bool VK, bool DECAY>

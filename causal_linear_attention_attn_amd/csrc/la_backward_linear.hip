@@ -293,8 +293,7 @@ __device__ __forceinline__ void commit_dn(typename BC::type *dN, const BRegs<BC>
       dot = fmaf(ge, to_f32(R.o[n][e]), dot);
       x[e] = from_f32<T>(ge * rd);
     }
-#pragma unroll
-    for (int m = 1; m < BC::VCB; m <<= 1) dot += __shfl_xor(dot, m);
+    dot = lane_sum<BC::VCB>(dot);
     *reinterpret_cast<V *>(dN + row * BC::LDV + col0) = x;
     if (cb < BC::XCB) {
       V y;
@@ -910,9 +909,31 @@ struct ChanSplit {
                 "threads per channel");
 };
 
-// The value v of the lane `owner` threads further in this channel's group.
-__device__ __forceinline__ double shfl_group(double v, int base, int owner) {
-  return __shfl(v, base + owner);
+// The value v of lane OWNER of this thread's group of P adjacent lanes
+// (first lane base): for P = 4 a DPP quad broadcast of both halves, else a
+// lane shuffle.
+template <int P, int OWNER>
+__device__ __forceinline__ double group_lane(double v, int base) {
+  if constexpr (P == 4) {
+    constexpr int ctrl = OWNER * 0x55;  // quad_perm [OWNER, OWNER, OWNER, OWNER]
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    i32x2 w = __builtin_bit_cast(i32x2, v);
+    w.x = __builtin_amdgcn_update_dpp(0, w.x, ctrl, 0xF, 0xF, false);
+    w.y = __builtin_amdgcn_update_dpp(0, w.y, ctrl, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, w);
+  } else {
+    return __shfl(v, base + OWNER);
+  }
+}
+
+// before += the parts of the group's lanes M .. P - 2 that precede lane pp.
+template <int P, int M>
+__device__ __forceinline__ void add_earlier_parts(double &before, double part, int base, int pp) {
+  if constexpr (M < P - 1) {
+    const double x = group_lane<P, M>(part, base);
+    if (M < pp) before += x;
+    add_earlier_parts<P, M + 1>(before, part, base, pp);
+  }
 }
 
 // The chunk's prefix sums (fp64; P threads per channel, each over its JP
@@ -935,18 +956,14 @@ __device__ __forceinline__ void chan_tables(ChanB<BC> &cb, int Lc, int d) {
     lb[jj] = part;
   }
   double before = 0.0;  // the earlier threads' parts
-#pragma unroll
-  for (int m = 0; m < P - 1; ++m) {
-    const double x = shfl_group(part, base, m);
-    if (m < pp) before += x;
-  }
+  add_earlier_parts<P, 0>(before, part, base, pp);
 #pragma unroll
   for (int jj = 0; jj < JP; ++jj) lb[jj] += before;
   // block references: M_b at token 16 b + 7, E_b at 16 b + 15 (E_1 = lb_L)
-  const double M0 = shfl_group(lb[7 % JP], base, 7 / JP);
-  const double E0 = shfl_group(lb[15 % JP], base, 15 / JP);
-  const double M1 = shfl_group(lb[23 % JP], base, 23 / JP);
-  const double L = shfl_group(lb[31 % JP], base, 31 / JP);
+  const double M0 = group_lane<P, 7 / JP>(lb[7 % JP], base);
+  const double E0 = group_lane<P, 15 / JP>(lb[15 % JP], base);
+  const double M1 = group_lane<P, 23 / JP>(lb[23 % JP], base);
+  const double L = group_lane<P, 31 / JP>(lb[31 % JP], base);
 #pragma unroll
   for (int jj = 0; jj < JP; ++jj) {
     const int t = pp * JP + jj;
@@ -1367,8 +1384,7 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
         for (int r = 0; r < 4; ++r) {
           const int f = 16 * fb + 4 * lg + r;
           float part = Sa[i][r] * Sm[i][r];
-#pragma unroll
-          for (int m = 1; m < 16; m <<= 1) part += __shfl_xor(part, m);
+          part = lane_sum<16>(part);
           if (li == 0 && st < BC::NST) partv[vb * BC::DK + f] = part;
         }
       }

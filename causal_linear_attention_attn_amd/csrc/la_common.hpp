@@ -256,6 +256,32 @@ __device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, uint32_t of
   __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, x), r, (int)off, 0, 0);
 }
 
+// One DPP lane move inside 16-lane rows (CTRL: a quad permutation, or the
+// half-row / row mirror), a VALU operand modifier with no trip through the
+// LDS unit.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W consecutive lanes (a power of two up to 64),
+// the same value in every lane of a group: lanes l ^ 1 and l ^ 2 by quad
+// permutations, then the other quad of the half-row and the other half of
+// the row by the mirrors (each step adds a group to its mirror image, so
+// every lane ends with the whole sum), then across rows by lane shuffles.
+template <int W>
+__device__ __forceinline__ float lane_sum(float x) {
+  static_assert(W >= 2 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  x += dpp_move<0xB1>(x);                         // quad_perm [1, 0, 3, 2]
+  if constexpr (W >= 4) x += dpp_move<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  if constexpr (W >= 8) x += dpp_move<0x141>(x);  // row_half_mirror
+  if constexpr (W >= 16) x += dpp_move<0x140>(x); // row_mirror
+  if constexpr (W >= 32) x += __shfl_xor(x, 16);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
 // Sum over the four slot groups (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float sum_groups(float x) {
   x += __shfl_xor(x, 16);
