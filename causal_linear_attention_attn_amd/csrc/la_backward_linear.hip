@@ -623,10 +623,11 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DQ) bwd_dq_kernel(BwdParams p)
         frag_kr(b, sm.Fk, BC::LDK, 16 * fb, 32 * ks, li, lg);
         mma(acc, a, b);
       }
+      if (p.fmap) {
+        float fq[4];
+        lds_col4(fq, sm.Fq, BC::LDK, 16 * tt + 4 * lg, 16 * fb, li);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * tt + 4 * lg + r, f = 16 * fb + li;
-        acc[r] *= p.fmap ? fminf(to_f32(sm.Fq[t * BC::LDK + f]), 1.f) : 1.f;
+        for (int r = 0; r < 4; ++r) acc[r] *= fminf(fq[r], 1.f);
       }
       out_tile<BC>(sm.Os, BC::LDKS, rdq, acc, c0, 16 * tt, 16 * fb + li, Lc, d, lg);
     }
@@ -724,10 +725,11 @@ __global__ void __launch_bounds__(BC::NT, BC::WPE_DKV) bwd_dkv_kernel(BwdParams 
         frag_kr(b, sm.Fq, BC::LDK, 16 * fb, 32 * ks, li, lg);
         mma(acc, a, b);
       }
+      if (p.fmap) {
+        float fk[4];
+        lds_col4(fk, sm.Fk, BC::LDK, 16 * jt + 4 * lg, 16 * fb, li);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * jt + 4 * lg + r, f = 16 * fb + li;
-        acc[r] *= p.fmap ? fminf(to_f32(sm.Fk[j * BC::LDK + f]), 1.f) : 1.f;
+        for (int r = 0; r < 4; ++r) acc[r] *= fminf(fk[r], 1.f);
       }
       out_tile<BC>(sm.Ok, BC::LDKS, rdk, acc, c0, 16 * jt, 16 * fb + li, Lc, d, lg);
     }
@@ -1193,13 +1195,15 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDqCh<
       }
       f32x4 acc;
       const int f = 16 * fb + li;
+      float fq4[4];
+      lds_col4(fq4, sm.Fq, BC::LDK, 16 * tt + 4 * lg, 16 * fb, li);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * tt + 4 * lg + r;
         const float lr = cb.lbr[t * LDL + f];
         const float sp = acs[r] * (exp2f(lr + cb.mr[tt][f]) * cb.rf[tt][f]);
         const float dphi = sp + acd[r] * exp2f(lr);
-        const float fq = to_f32(sm.Fq[t * BC::LDK + f]);
+        const float fq = fq4[r];
         if (t < Lc && f < d) ux[(size_t)(c0 + t) * d + f] = fq * sp;  // dalpha's third sum
         acc[r] = dphi * (p.fmap ? fminf(fq, 1.f) : 1.f);
       }
@@ -1236,9 +1240,9 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDqCh<
 }
 
 // ---- dk, dv with a per-channel decay: chunks right to left, adjoint state ---
-// The cross-block terms of dalpha's fourth sum, per token and channel (fp32,
-// row stride LDX), then the token ranges' totals of them ([NW][DK]), in the
-// adjoint copy's tile.
+// The cross-block sums of dalpha's fourth sum, per token and channel (fp32,
+// row stride LDX), then the token ranges' totals of its terms ([NW][DK]),
+// in the adjoint copy's tile.
 template <class BC>
 struct CrossB {
   static constexpr int LDX = BC::DK + 4;
@@ -1246,10 +1250,11 @@ struct CrossB {
   static_assert(BC::C == 32 && BC::NTB == 2, "two 16-token blocks per chunk");
 };
 
-// xc[j][f] = k^_j Y_j (j in block 0) and xc[t][f] = q^_t Z_t (t in block 1),
-// with Y_j = mm sum_(t in block 1) q^_t dA_tj and Z_t = mm sum_(j in block 0)
-// dA_tj k^_j (q^ = Fq, k^ = Kh, mm = 2^(M_1 - M_0) per channel).  Wave w
-// takes the feature tiles w, w + NW, ... of both.
+// xc[j][f] = Y_j (j in block 0) and xc[t][f] = Z_t (t in block 1), with
+// Y_j = mm sum_(t in block 1) q^_t dA_tj and Z_t = mm sum_(j in block 0)
+// dA_tj k^_j (q^ = Fq, k^ = Kh, mm = 2^(M_1 - M_0) per channel); the final
+// phase multiplies by k^_j or q^_t.  Wave w takes the feature tiles w,
+// w + NW, ... of both.
 template <class BC>
 __device__ __forceinline__ void cross_block_terms(float *xc, const typename BC::type *dA,
                                                   const typename BC::type *Fq,
@@ -1274,7 +1279,7 @@ __device__ __forceinline__ void cross_block_terms(float *xc, const typename BC::
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * lg + r;
-        xc[j * LDX + f] = to_f32(Kh[j * BC::LDK + f]) * (y[r] * m);
+        xc[j * LDX + f] = y[r] * m;
       }
     }
     {  // Z: queries of block 1 (rows 16 + 4 lg + r), keys of block 0 only
@@ -1290,7 +1295,7 @@ __device__ __forceinline__ void cross_block_terms(float *xc, const typename BC::
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 + 4 * lg + r;
-        xc[t * LDX + f] = to_f32(Fq[t * BC::LDK + f]) * (z[r] * m);
+        xc[t * LDX + f] = z[r] * m;
       }
     }
   }
@@ -1436,13 +1441,15 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
       }
       f32x4 acc;
       const int f = 16 * fb + li;
+      float fk4[4];
+      lds_col4(fk4, sm.Fk, BC::LDK, 16 * jt + 4 * lg, 16 * fb, li);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * jt + 4 * lg + r;
         const float lr = cb.lbr[j * LDL + f];
         const float sp = acs[r] * (exp2f(cb.em[jt][f] - lr) * cb.le[jt][f]);
         const float dphi = sp + aci[r] * exp2f(-lr);
-        const float fk = to_f32(sm.Fk[j * BC::LDK + f]);
+        const float fk = fk4[r];
         xr[n][r] = fk * sp;
         acc[r] = dphi * (p.fmap ? fminf(fk, 1.f) : 1.f);
       }
@@ -1527,7 +1534,8 @@ __global__ void __launch_bounds__(BC::NT, ch_waves_per_simd<BC>(sizeof(SmemDkvCh
         const bool ok = fok && t < Lc;
         const size_t at = (size_t)(c0 + t) * d + f;
         base[jj] = ok ? cb.lbr[t * LDL + f] : 0.f;  // the second sum's term of key t
-        cx[jj] = ok ? xc[t * LDX + f] : 0.f;         // the cross-block term of token t
+        // the cross-block term of token t: k^_t Y_t (block 0), q^_t Z_t (block 1)
+        cx[jj] = ok ? xc[t * LDX + f] * to_f32((blk == 0 ? Kh : sm.Fq)[t * BC::LDK + f]) : 0.f;
         alr[jj] = ok ? al[at] : 1.f;
         yt += base[jj];
         ct += cx[jj];

@@ -124,6 +124,26 @@ __device__ __forceinline__ void lds_frag_tr(Frag<float> &f, const float *M, int 
     f.v[4 + e] = M[(t_hi + e) * ld + c0 + li];
   }
 }
+
+// Rows t..t+3 of column c0 + li of a row-major LDS tile, as fp32: the
+// accumulator layout of a 16 x 16 product (lane (li, lg) holds rows 4 lg + r
+// of column li), with t the same for the 16 lanes of a slot group.  bf16:
+// one transpose read (as in lds_frag_tr) instead of four 2-byte reads;
+// fp32: four strided reads.
+__device__ __forceinline__ void lds_col4(float (&x)[4], const bf16 *M, int ld, int t, int c0,
+                                         int li) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lbf16x4;
+  typedef __attribute__((address_space(3))) lbf16x4 lds_bf16x4;
+  const lbf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4 *)(M + t * ld + (li >> 2) * ld + c0 + 4 * (li & 3)));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = (float)a[e];
+}
+__device__ __forceinline__ void lds_col4(float (&x)[4], const float *M, int ld, int t, int c0,
+                                         int li) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = M[(t + e) * ld + c0 + li];
+}
 template <typename T>
 __device__ __forceinline__ void frag_fill(Frag<T> &f, float x) {
 #pragma unroll
