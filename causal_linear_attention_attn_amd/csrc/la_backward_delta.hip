@@ -706,13 +706,16 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
     for (int bm = 0; bm <= rb; ++bm) {
       const f32x4 a =
           *reinterpret_cast<const f32x4 *>(sm.Xi + (16 * rb + li) * LDX + 16 * bm + 4 * lg);
+      float yk[G::NVT][4];  // Y rows 16 bm + 4 lg .. + 3 of column 16 ct + li
+#pragma unroll
+      for (int ct = 0; ct < G::NVT; ++ct) lds_col4(yk[ct], sm.Ys, LDV, 16 * bm + 4 * lg, 16 * ct, li);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int k = 16 * bm + 4 * lg + kk;
         const float gk = sm.gs[k];
 #pragma unroll
         for (int ct = 0; ct < G::NVT; ++ct) {
-          const float b = gk * (float)sm.Ys[k * LDV + 16 * ct + li];
+          const float b = gk * yk[ct][kk];
           acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk], b, acc[ct], 0, 0, 0);
         }
       }
@@ -737,9 +740,12 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
   }
   f32x4 du[G::NVT];
 #pragma unroll
-  for (int ct = 0; ct < G::NVT; ++ct)
+  for (int ct = 0; ct < G::NVT; ++ct) {
+    float x[4];
+    lds_col4(x, sm.Ds, LDV, 16 * rb + 4 * lg, 16 * ct, li);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) du[ct][r] = (float)sm.Ds[(16 * rb + 4 * lg + r) * LDV + 16 * ct + li];
+    for (int r = 0; r < 4; ++r) du[ct][r] = x[r];
+  }
 #pragma unroll
   for (int ks = 0; ks < C / 32; ++ks) {
     if (32 * ks + 31 < 16 * rb) continue;  // P[j][i] = 0 for j < i
@@ -791,12 +797,12 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < G::NVT; ++ct)
+    for (int ct = 0; ct < G::NVT; ++ct) {
+      float y[4];
+      lds_col4(y, sm.Ys, LDV, 16 * rb + 4 * lg, 16 * ct, li);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float y = (float)sm.Ys[(16 * rb + 4 * lg + r) * LDV + 16 * ct + li];
-        dgp[r] = fmaf(lam[ct][r], y, dgp[r]);
-      }
+      for (int r = 0; r < 4; ++r) dgp[r] = fmaf(lam[ct][r], y[r], dgp[r]);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float s = sum16(dgp[r]);
