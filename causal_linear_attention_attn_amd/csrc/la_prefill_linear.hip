@@ -110,7 +110,9 @@ struct Cfg {
   static constexpr int DK = DK_, DV = DV_, C = C_, NW = NW_;
   static constexpr int NT = NW * kWave;
   static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte vector
-  static constexpr int QLD = DK + VEC;  // row stride: Qs, Ks, St
+  static constexpr int QLD = DK + VEC;  // row strides: Qs, Ks, St
+  static constexpr int KLD = DK + VEC;
+  static constexpr int SLD = DK + VEC;
   static constexpr int VLD = DV + VEC;  // row stride: Os
   // row stride of Vs, read only through transpose loads: 8 consecutive rows
   // of 32 bytes then fall in distinct LDS banks
@@ -149,9 +151,9 @@ template <class CF>
 struct alignas(16) SmemChunk {
   using T = typename CF::type;
   T Qs[CF::C * CF::QLD];      // phi(q) rows
-  T Ks[CF::C * CF::QLD];      // weighted phi(k) rows
+  T Ks[CF::C * CF::KLD];      // weighted phi(k) rows
   T Vs[CF::C * CF::VTLD];     // v rows
-  T St[CF::SROWS * CF::QLD];  // gamma^L [S | z]^T for the next state read
+  T St[CF::SROWS * CF::SLD];  // gamma^L [S | z]^T for the next state read
   T Os[CF::C * CF::VLD];      // output staging
   float pw[CF::C + 4];        // gamma^m, m = 0..C (decay folded into key weights)
 };
@@ -159,7 +161,7 @@ struct alignas(16) SmemChunk {
 template <class CF>
 struct alignas(16) SmemSummary {
   using T = typename CF::type;
-  T Ks[CF::C * CF::QLD];
+  T Ks[CF::C * CF::KLD];
   T Vs[CF::C * CF::VTLD];
   float pw[CF::C + 4];
 };
@@ -544,7 +546,7 @@ __device__ __forceinline__ void conv_gather(ConvOut<CF, WITH_Q> &Y, const ChunkR
   for (int r = 0; r < CF::RQ; ++r) {
     const int row = qrg * CF::RQ + r;
     if constexpr (WITH_Q) *reinterpret_cast<V *>(Qs + row * CF::QLD + qc0) = R.q[r];
-    *reinterpret_cast<V *>(Ks + row * CF::QLD + qc0) = R.k[r];
+    *reinterpret_cast<V *>(Ks + row * CF::KLD + qc0) = R.k[r];
   }
 #pragma unroll
   for (int r = 0; r < CF::RV; ++r)
@@ -552,7 +554,7 @@ __device__ __forceinline__ void conv_gather(ConvOut<CF, WITH_Q> &Y, const ChunkR
   __syncthreads();
   if constexpr (WITH_Q)
     conv_rows<CF, CF::RQ>(Y.q, R.q, Qs, CF::QLD, cs.hq, CF::QLD, qrg * CF::RQ, qc0, cs.w);
-  conv_rows<CF, CF::RQ>(Y.k, R.k, Ks, CF::QLD, cs.hk, CF::QLD, qrg * CF::RQ, qc0,
+  conv_rows<CF, CF::RQ>(Y.k, R.k, Ks, CF::KLD, cs.hk, CF::QLD, qrg * CF::RQ, qc0,
                         cs.w + CF::DK);
   conv_rows<CF, CF::RV>(Y.v, R.v, Vs, CF::VTLD, cs.hv, CF::VLD, vrg * CF::RV, vc0,
                         cs.w + 2 * CF::DK);
@@ -696,12 +698,12 @@ __device__ __forceinline__ void commit_rows(const ChunkRegs<CF> &R,
 #pragma unroll
       for (int e = 0; e < VEC; ++e) x[e] = col0 + e < p.d ? x[e] * w : 0.f;
       if constexpr (CV) P->k[r] = pack_vec<CF>(x);
-      else lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
+      else lds_store_n<T, VEC>(Ks + row * CF::KLD + col0, x);
     } else {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) x[e] *= w;
       if constexpr (CV) P->k[r] = pack_vec<CF>(x);
-      else lds_store_n<T, VEC>(Ks + row * CF::QLD + col0, x);
+      else lds_store_n<T, VEC>(Ks + row * CF::KLD + col0, x);
     }
   }
 }
@@ -735,7 +737,7 @@ __device__ __forceinline__ void commit(const ChunkRegs<CF> &R, typename CF::type
     for (int r = 0; r < CF::RQ; ++r) {
       const int row = qrg * CF::RQ + r;
       if constexpr (WITH_Q) *reinterpret_cast<V *>(Qs + row * CF::QLD + qcb * CF::VEC) = P.q[r];
-      *reinterpret_cast<V *>(Ks + row * CF::QLD + qcb * CF::VEC) = P.k[r];
+      *reinterpret_cast<V *>(Ks + row * CF::KLD + qcb * CF::VEC) = P.k[r];
     }
 #pragma unroll
     for (int r = 0; r < CF::RV; ++r) {
@@ -788,7 +790,7 @@ __device__ __forceinline__ void state_update(f32x4 (&Sacc)[CF::FPW][CF::TPW],
 #pragma unroll
     for (int a = 0; a < CF::FPW; ++a) {
       Frag<T> kf;
-      lds_frag_tr(kf, Ks, CF::QLD, t0, t0 + 16, 16 * srow<CF>(wv, a), li);
+      lds_frag_tr(kf, Ks, CF::KLD, t0, t0 + 16, 16 * srow<CF>(wv, a), li);
 #pragma unroll
       for (int b = 0; b < CF::TPW; ++b) {
         const int tn = scol<CF>(wv, b);
@@ -824,7 +826,7 @@ __device__ __forceinline__ void state_update_chan(f32x4 (&Sacc)[CF::FPW][CF::TPW
     for (int a = 0; a < CF::FPW; ++a) {
       const int f = 16 * srow<CF>(wv, a) + li;
       Frag<T> kf;
-      lds_frag_tr(kf, Ks, CF::QLD, t0, t0 + 16, 16 * srow<CF>(wv, a), li);
+      lds_frag_tr(kf, Ks, CF::KLD, t0, t0 + 16, 16 * srow<CF>(wv, a), li);
       const int b0 = 2 * ks, b1 = 2 * ks + 1;
       const float a0 = sc.kb[b0][f], a1 = sc.kb[b1][f];
       const float c0 = b0 + 1 < CF::NRB ? sc.kf[b0][f] : 1.f;
@@ -898,7 +900,7 @@ __device__ __forceinline__ void state_update_decay(f32x4 (&Sacc)[CF::FPW][CF::TP
 #pragma unroll
     for (int a = 0; a < CF::FPW; ++a) {
       Frag<T> kf;
-      lds_frag_tr(kf, Ks, CF::QLD, t0, t0 + 16, 16 * srow<CF>(wv, a), li);
+      lds_frag_tr(kf, Ks, CF::KLD, t0, t0 + 16, 16 * srow<CF>(wv, a), li);
 #pragma unroll
       for (int e = 0; e < 8; ++e) frag_set(kf, e, frag_elem(kf, e) * w[e]);
 #pragma unroll
@@ -937,7 +939,7 @@ __device__ __forceinline__ void rescale_and_copy_state(typename CF::type *St,
       const int tn = scol<CF>(wv, b);
       // (the normaliser tile holds z in all 16 columns: one row of it)
       if (tn < CF::NVT || (tn == CF::NVT && li == 0))
-        lds_store4(St + (tn < CF::NVT ? 16 * tn + li : CF::DV) * CF::QLD + 16 * tf + 4 * lg,
+        lds_store4(St + (tn < CF::NVT ? 16 * tn + li : CF::DV) * CF::SLD + 16 * tf + 4 * lg,
                    Sacc[a][b][0], Sacc[a][b][1], Sacc[a][b][2], Sacc[a][b][3]);
     }
   }
@@ -1109,7 +1111,7 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const SmemChan<
 #pragma unroll
       for (int ks = 0; ks < CF::KSD; ++ks) {
         Frag<T> kf;
-        lds_frag(kf, sm.Ks + (16 * tj + li) * CF::QLD + 32 * ks + 8 * lg);
+        lds_frag(kf, sm.Ks + (16 * tj + li) * CF::KLD + 32 * ks + 8 * lg);
         if (CH && tj < RB) {  // key block tj before the query block (see the header)
           const int c0 = 32 * ks + 8 * lg;
           kf = frag_scaled(kf, sc->kb[tj] + c0);
@@ -1153,11 +1155,11 @@ __device__ __forceinline__ void chunk_outputs(SmemChunk<CF> &sm, const SmemChan<
 #pragma unroll
     for (int a = 0; a < CF::NPW; ++a) {
       Frag<T> sf;
-      lds_frag(sf, sm.St + (16 * (cg * CF::NPW + a) + li) * CF::QLD + 32 * ks + 8 * lg);
+      lds_frag(sf, sm.St + (16 * (cg * CF::NPW + a) + li) * CF::SLD + 32 * ks + 8 * lg);
       mma(acc[a], sf, qs);
     }
     Frag<T> zf;
-    lds_frag(zf, sm.St + CF::DV * CF::QLD + 32 * ks + 8 * lg);  // z, every lane
+    lds_frag(zf, sm.St + CF::DV * CF::SLD + 32 * ks + 8 * lg);  // z, every lane
     mma(accd, zf, qs);
   }
   if constexpr (MODE == kDecElem) {
@@ -1552,8 +1554,24 @@ constexpr size_t chunk_lds() {
          (CV ? sizeof(SmemConv<CF>) : 0);
 }
 
-template <class CF, bool VK, bool CH, bool CV>
+// The chunk kernel's tile strides: at d = 128 (bf16) the plain kernel's
+// Qs, Ks and state-copy rows take 16 more elements, which spreads its
+// output phase's LDS reads over more banks (measured faster at B1 H32
+// N131072); the per-channel-decay and convolution variants keep the
+// tighter rows (with both, that tile size would not fit in the LDS).
+template <class CF>
+struct WideRows : CF {
+  static constexpr int QLD = CF::DK + 2 * CF::VEC;
+  static constexpr int KLD = QLD, SLD = QLD;
+};
+template <class CF, bool CH, bool CV>
+using ChunkCfg =
+    typename std::conditional<!CH && !CV && CF::DK == 128 && sizeof(typename CF::type) == 2,
+                              WideRows<CF>, CF>::type;
+
+template <class CF0, bool VK, bool CH, bool CV>
 hipError_t run_vkcc(const PrefillParams &p, hipStream_t s) {
+  using CF = ChunkCfg<CF0, CH, CV>;  // (the summary keeps CF0)
   if constexpr (chunk_lds<CF, CH, CV>() > kLdsBytes) {
     return hipErrorNotSupported;  // refused on the host before any launch
   } else {
@@ -1564,12 +1582,12 @@ hipError_t run_vkcc(const PrefillParams &p, hipStream_t s) {
                         kStreamBytes;
     hipError_t e;
     if constexpr (!CH && !CV && VK)
-      e = stream ? launch_kernel("linear_summary", summary_kernel<CF, VK, false, false, true>,
+      e = stream ? launch_kernel("linear_summary", summary_kernel<CF0, VK, false, false, true>,
                                  grid, dim3(CF::NT), s, p)
-                 : launch_kernel("linear_summary", summary_kernel<CF, VK, CH, CV>, grid,
+                 : launch_kernel("linear_summary", summary_kernel<CF0, VK, CH, CV>, grid,
                                  dim3(CF::NT), s, p);
     else
-      e = launch_kernel("linear_summary", summary_kernel<CF, VK, CH, CV>, grid, dim3(CF::NT), s,
+      e = launch_kernel("linear_summary", summary_kernel<CF0, VK, CH, CV>, grid, dim3(CF::NT), s,
                         p);
     if (e != hipSuccess) return e;
     e = launch_scan<CH>(p, s);
@@ -1643,16 +1661,16 @@ hipError_t run_prefix(const PrefillParams &p, hipStream_t s) {
 // instantiation).
 template <class CF, bool CH, bool CV>
 int resident_per_cu() {
-  if constexpr (chunk_lds<CF, CH, CV>() > kLdsBytes) {
+  if constexpr (chunk_lds<ChunkCfg<CF, CH, CV>, CH, CV>() > kLdsBytes) {
     return 1;  // refused at launch anyway
   } else {
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
     if (v > 0) return v;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n,
-                                                     chunk_kernel<CF, true, CH, CV, false, false>,
-                                                     CF::NT, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, chunk_kernel<ChunkCfg<CF, CH, CV>, true, CH, CV, false, false>, CF::NT, 0) !=
+            hipSuccess ||
         n < 1) {
       (void)hipGetLastError();
       n = 1;
