@@ -541,6 +541,28 @@ __device__ __forceinline__ void tile_load(bf16 *tile, int ld, int cols, __amdgpu
   }
 }
 
+// The first nrows rows of an LDS tile (cols columns, stride ld) to rows
+// row0 .. of a [N, ncols] bf16 tensor (columns past ncols not written),
+// every thread 16-byte blocks (VK: ncols % 8 == 0 and 16-byte aligned rows).
+template <bool VK>
+__device__ __forceinline__ void tile_store(const bf16 *tile, int ld, int cols, bf16 *out,
+                                           int row0, int nrows, int ncols) {
+  const int cb = cols / 8;
+  for (int b = threadIdx.x; b < 64 * cb; b += kThreads) {
+    const int row = b / cb, c0 = (b % cb) * 8;
+    if (row >= nrows) continue;
+    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(tile + row * ld + c0);
+    bf16 *dst = out + (size_t)(row0 + row) * ncols + c0;
+    if constexpr (VK) {
+      if (c0 < ncols) *reinterpret_cast<bf16x8 *>(dst) = x;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c0 + e < ncols) dst[e] = x[e];
+    }
+  }
+}
+
 // Rows r0 .. r0 + nrows - 1 of a bf16 [DK][dvp] record into an LDS tile of
 // DV columns (stride ld), columns past dv zero; every thread takes 16-byte
 // blocks.
@@ -873,6 +895,10 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
 
   bf16 *dqo = reinterpret_cast<bf16 *>(p.dq) + bh * qk;
   bf16 *dko = reinterpret_cast<bf16 *>(p.dk) + bh * qk;
+  // dQ, then dK rows staged in the X^(-1) tile (no longer read), then
+  // stored as whole rows
+  bf16 *const Gst = reinterpret_cast<bf16 *>(sm.Xi);
+  static_assert(sizeof(sm.Xi) >= sizeof(bf16) * C * LDK, "gradient rows fit the X tile");
   // ---- dQ = diag(b) dO S-^T + (dP (.) Mb) K; d log b_i += b_i q_i . (dO S-^T)_i ----
   {
     float da[4] = {0.f, 0.f, 0.f, 0.f};
@@ -905,7 +931,7 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
         const int i = 16 * rb + 4 * lg + r;
         const float b = DECAY ? __expf(sm.lb[i]) : 1.f;
         if (DECAY) da[r] = fmaf(b * t1[r], (float)sm.Qs[i * LDK + f], da[r]);
-        if (i < Lc && f < d) dqo[(size_t)(c0 + i) * d + f] = (bf16)fmaf(b, t1[r], t2[r]);
+        Gst[i * LDK + f] = (bf16)fmaf(b, t1[r], t2[r]);
       }
     }
     if constexpr (DECAY) {
@@ -915,6 +941,8 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
         if (li == 0) sm.dlb[wv][16 * rb + 4 * lg + r] += s;
       }
     }
+    __syncthreads();
+    tile_store<VK>(Gst, LDK, DK, dqo, c0, Lc, d);
   }
   // ---- dK = (dP (.) Mb)^T Q - diag(b) dY S-^T + diag(beta / b) U Sh+^T + (G + G^T) K;
   //      d log b_j -= b_j k_j . (dY S-^T)_j.  Sh+ goes to the dO tile (no
@@ -978,7 +1006,7 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
         const float wl = DECAY ? __expf(lbeta - sm.lb[j]) : 1.f;
         if (DECAY) da[r] = fmaf(-b * t2[r], (float)sm.Ks[j * LDK + f], da[r]);
         const float g = t1[r] - b * t2[r] + wl * t3[r] + t4[r];
-        if (j < Lc && f < d) dko[(size_t)(c0 + j) * d + f] = (bf16)g;
+        Gst[j * LDK + f] = (bf16)g;
       }
     }
     if constexpr (DECAY) {
@@ -988,6 +1016,8 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
         if (li == 0) sm.dlb[wv][16 * rb + 4 * lg + r] += s;
       }
     }
+    __syncthreads();
+    tile_store<VK>(Gst, LDK, DK, dko, c0, Lc, d);
   }
   if constexpr (DECAY) {
     float s = shs;  // beta <Sh+, S-> over the chunk's records
