@@ -32,7 +32,8 @@ struct DCfg {
   static constexpr int FPW = NFT / kWaves;   // state row tiles per wave
   static constexpr int KSD = DK / 32;   // k-steps over features
   static constexpr int KSC = C / 32;    // k-steps over tokens
-  static constexpr int QLD = DK + VEC;  // row stride: Ks (prep), St (seq)
+  static constexpr int QLD = DK + 2 * VEC;  // row stride: Ks (prep), St (seq); 16 past DK
+                                            // (measured 1.5 % faster than 8 in the pass)
   static constexpr int YLD = W + 16;    // row stride: Ys (transpose reads)
   static constexpr int FLD = C + 8;     // fp32 row stride: Nm (prep)
   static constexpr int TLD = C + VEC;   // row stride: T^T parts (prep)
