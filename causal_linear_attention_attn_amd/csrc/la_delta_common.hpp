@@ -35,7 +35,7 @@ struct DCfg {
   static constexpr int QLD = DK + 2 * VEC;  // row stride: Ks (prep), St (seq); 16 past DK
                                             // (measured 1.5 % faster than 8 in the pass)
   static constexpr int YLD = W + 16;    // row stride: Ys (transpose reads)
-  static constexpr int FLD = C + 8;     // fp32 row stride: Nm (prep)
+  static constexpr int FLD = C + 4;     // fp32 row stride: Nm (prep; + 4 measured faster than + 8)
   static constexpr int TLD = C + VEC;   // row stride: T^T parts (prep)
   static constexpr int QCB = DK / VEC;  // 16-byte blocks per q/k row
   static constexpr size_t WT = (size_t)DK * C;     // Wt elements per chunk
