@@ -483,7 +483,13 @@ __global__ void __launch_bounds__(kThreads) brev_kernel(BwdDeltaParams p, int ns
 }
 
 // ---------------------------------------------------------------------------
-// bgrad_kernel: the per-chunk gradients, every chunk in parallel.
+// bgrad_kernel: the per-chunk gradients, every chunk in parallel.  Its tiles
+// fill the LDS, so one workgroup runs per CU; it has eight waves, two per
+// 16-row block of the chunk, each taking half of the block's output tiles
+// (value column tiles of U, dU and lambda; feature tiles of dQ and dK;
+// alternate column blocks of L, P and dP), so that every SIMD holds two
+// waves to cover each other's LDS and matrix-core latency.
+constexpr int kGWaves = 8, kGThreads = kGWaves * kWave;
 // ---------------------------------------------------------------------------
 template <int DK_, int DV_>
 struct GCfg {
@@ -500,8 +506,9 @@ struct alignas(16) SmemGrad {
   bf16 Lb[G::C * G::LDC], Pb[G::C * G::LDC];  // L then G + G^T; P then dP (.) Mb
   float Xi[G::C * G::LDX];                    // X, then X^(-1)
   float gs[G::C], lb[G::C], al[G::C], Gi[G::C];
-  float dlb[kWaves][G::C];  // per-wave parts of d log b
-  float red[kWaves];
+  float dlb[kGWaves][G::C];  // per-wave parts of d log b
+  float dgp[2][G::C];        // the two halves of dg
+  float red[kGWaves];
 };
 
 // 8 consecutive row elements of a bf16 [DK][dvp] record (columns n .. n+7
@@ -522,7 +529,7 @@ template <bool VK>
 __device__ __forceinline__ void tile_load(bf16 *tile, int ld, int cols, __amdgpu_buffer_rsrc_t r,
                                           int row0, int nrows, int ncols, int rstride) {
   const int cb = cols / 8;
-  for (int b = threadIdx.x; b < 64 * cb; b += kThreads) {
+  for (int b = threadIdx.x; b < 64 * cb; b += kGThreads) {
     const int row = b / cb, c0 = (b % cb) * 8;
     bf16x8 x;
     const bool ok = row < nrows;
@@ -548,7 +555,7 @@ template <bool VK>
 __device__ __forceinline__ void tile_store(const bf16 *tile, int ld, int cols, bf16 *out,
                                            int row0, int nrows, int ncols) {
   const int cb = cols / 8;
-  for (int b = threadIdx.x; b < 64 * cb; b += kThreads) {
+  for (int b = threadIdx.x; b < 64 * cb; b += kGThreads) {
     const int row = b / cb, c0 = (b % cb) * 8;
     if (row >= nrows) continue;
     const bf16x8 x = *reinterpret_cast<const bf16x8 *>(tile + row * ld + c0);
@@ -569,7 +576,7 @@ __device__ __forceinline__ void tile_store(const bf16 *tile, int ld, int cols, b
 __device__ __forceinline__ void stage_rec(bf16 *tile, int ld, __amdgpu_buffer_rsrc_t r, int r0,
                                           int nrows, int DV, int dvp, int dv) {
   const int cb = DV / 8;
-  for (int b = threadIdx.x; b < nrows * cb; b += kThreads) {
+  for (int b = threadIdx.x; b < nrows * cb; b += kGThreads) {
     const int row = b / cb, n = (b % cb) * 8;
     Frag<bf16> f;
     rec_row_frag(f, r, r0 + row, n, dvp, dv);
@@ -582,8 +589,10 @@ __device__ __forceinline__ float sum16(float x) {  // over the 16 lanes li of a 
 }
 
 template <class G, bool VK, bool DECAY>
-__global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
+__global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
   constexpr int C = G::C, DK = G::DK, DV = G::DV, NRB = G::NRB;
+  constexpr int NVH = G::NVT / 2, NFH = G::NFT / 2;  // a wave's value / feature tiles
+  static_assert(2 * NRB == kGWaves && 2 * NVH == G::NVT && 2 * NFH == G::NFT, "wave split");
   constexpr int LDK = G::LDK, LDV = G::LDV, LDC = G::LDC, LDX = G::LDX;
   __shared__ SmemGrad<G> sm;
   const int chunk = blockIdx.x, bh = grid_head();
@@ -591,7 +600,9 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int rb = wv;
+  // half h of row block rb; a SIMD's two waves (w, w + 4) take an early
+  // and a late row block, whose triangular parts differ in length
+  const int h = wv >> 2, rb = h ? NRB - 1 - (wv & 3) : (wv & 3);
   const int N = p.N, d = p.d, dv = p.dv, nch = p.nch, dvp = p.dvp;
   const int c0 = chunk * C, Lc = min(C, N - c0);
   const size_t qk = (size_t)N * d, vo = (size_t)N * dv;
@@ -623,12 +634,12 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
     sm.lb[tid] = DECAY ? ldec[tid] : 0.f;  // log b_j (constant past the chunk)
     sm.al[tid] = (DECAY && tid < Lc) ? p.alpha[(size_t)bh * N + c0 + tid] : 1.f;
   }
-  for (int e = tid; e < kWaves * C; e += kThreads) (&sm.dlb[0][0])[e] = 0.f;
-  for (int e = tid; e < C * LDC; e += kThreads) {
+  for (int e = tid; e < kGWaves * C; e += kGThreads) (&sm.dlb[0][0])[e] = 0.f;
+  for (int e = tid; e < C * LDC; e += kGThreads) {
     sm.Lb[e] = (bf16)0.f;
     sm.Pb[e] = (bf16)0.f;
   }
-  for (int e = tid; e < C * C; e += kThreads) sm.Xi[(e / C) * LDX + e % C] = 0.f;
+  for (int e = tid; e < C * C; e += kGThreads) sm.Xi[(e / C) * LDX + e % C] = 0.f;
   __syncthreads();
   const float lbeta = DECAY ? sm.lb[C - 1] : 0.f;
 
@@ -645,7 +656,7 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
     const float gi = sm.gs[i], lbi = sm.lb[i];
 #pragma unroll
     for (int tj = 0; tj < NRB; ++tj) {
-      if (tj > rb) continue;
+      if (tj > rb || (tj & 1) != h) continue;
       f32x4 kk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) {
@@ -717,41 +728,43 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
     __syncthreads();
   }
 
-  // ---- U = X^(-1) diag(g) Y (fp32 matrix cores): rows of this wave's block ----
+  // ---- U = X^(-1) diag(g) Y (fp32 matrix cores): rows of this wave's block,
+  //      its half of the value tiles (ct = NVH h + c) ----
   // (per 16-wide k block: the lane's four consecutive k of its row of X^(-1)
   // in one 16-byte read, k = 16 bm + 4 lg + kk in product kk)
   // (every value-column tile advances together: independent accumulators)
   {
-    f32x4 acc[G::NVT];
+    f32x4 acc[NVH];
 #pragma unroll
-    for (int ct = 0; ct < G::NVT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NVH; ++c) acc[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
     for (int bm = 0; bm <= rb; ++bm) {
       const f32x4 a =
           *reinterpret_cast<const f32x4 *>(sm.Xi + (16 * rb + li) * LDX + 16 * bm + 4 * lg);
-      float yk[G::NVT][4];  // Y rows 16 bm + 4 lg .. + 3 of column 16 ct + li
+      float yk[NVH][4];  // Y rows 16 bm + 4 lg .. + 3 of column 16 ct + li
 #pragma unroll
-      for (int ct = 0; ct < G::NVT; ++ct) lds_col4(yk[ct], sm.Ys, LDV, 16 * bm + 4 * lg, 16 * ct, li);
+      for (int c = 0; c < NVH; ++c)
+        lds_col4(yk[c], sm.Ys, LDV, 16 * bm + 4 * lg, 16 * (NVH * h + c), li);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int k = 16 * bm + 4 * lg + kk;
         const float gk = sm.gs[k];
 #pragma unroll
-        for (int ct = 0; ct < G::NVT; ++ct) {
-          const float b = gk * yk[ct][kk];
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk], b, acc[ct], 0, 0, 0);
+        for (int c = 0; c < NVH; ++c) {
+          const float b = gk * yk[c][kk];
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk], b, acc[c], 0, 0, 0);
         }
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < G::NVT; ++ct)
+    for (int c = 0; c < NVH; ++c)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        sm.Us[(16 * rb + 4 * lg + r) * LDV + 16 * ct + li] = (bf16)acc[ct][r];
+        sm.Us[(16 * rb + 4 * lg + r) * LDV + 16 * (NVH * h + c) + li] = (bf16)acc[c][r];
   }
   __syncthreads();
 
-  // ---- G_i = u_i . D_i (decay), then dU = P^T dO + D into Ds ----
-  if constexpr (DECAY) {
+  // ---- G_i = u_i . D_i (decay; the first half), then dU = P^T dO + D into Ds ----
+  if (DECAY && h == 0) {
     const int i = 16 * rb + li;
     float s = 0.f;
     for (int n = lg * (DV / 4); n < (lg + 1) * (DV / 4); ++n)
@@ -760,13 +773,13 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
     s += __shfl_xor(s, 32);
     if (lg == 0) sm.Gi[i] = s;
   }
-  f32x4 du[G::NVT];
+  f32x4 du[NVH];
 #pragma unroll
-  for (int ct = 0; ct < G::NVT; ++ct) {
+  for (int c = 0; c < NVH; ++c) {
     float x[4];
-    lds_col4(x, sm.Ds, LDV, 16 * rb + 4 * lg, 16 * ct, li);
+    lds_col4(x, sm.Ds, LDV, 16 * rb + 4 * lg, 16 * (NVH * h + c), li);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) du[ct][r] = x[r];
+    for (int r = 0; r < 4; ++r) du[c][r] = x[r];
   }
 #pragma unroll
   for (int ks = 0; ks < C / 32; ++ks) {
@@ -774,32 +787,33 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
     Frag<bf16> pf;
     lds_frag_tr(pf, sm.Pb, LDC, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * rb, li);
 #pragma unroll
-    for (int ct = 0; ct < G::NVT; ++ct) {
+    for (int c = 0; c < NVH; ++c) {
       Frag<bf16> of;
-      lds_frag_tr(of, sm.dOs, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * ct, li);
-      mma(du[ct], pf, of);
+      lds_frag_tr(of, sm.dOs, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * (NVH * h + c),
+                  li);
+      mma(du[c], pf, of);
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int ct = 0; ct < G::NVT; ++ct)
+  for (int c = 0; c < NVH; ++c)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      sm.Ds[(16 * rb + 4 * lg + r) * LDV + 16 * ct + li] = (bf16)du[ct][r];
+      sm.Ds[(16 * rb + 4 * lg + r) * LDV + 16 * (NVH * h + c) + li] = (bf16)du[c][r];
   __syncthreads();
 
   // ---- lam = X^(-T) dU and r = Y - L U (same tiles); dg_j = lam_j . r_j ----
   {
-    f32x4 lam[G::NVT];
+    f32x4 lam[NVH];
 #pragma unroll
-    for (int ct = 0; ct < G::NVT; ++ct) lam[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NVH; ++c) lam[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
     for (int k0 = 16 * rb; k0 < C; k0 += 4) {
       const float a = sm.Xi[(k0 + lg) * LDX + 16 * rb + li];
 #pragma unroll
-      for (int ct = 0; ct < G::NVT; ++ct) {
-        const float b = (float)sm.Ds[(k0 + lg) * LDV + 16 * ct + li];
-        lam[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, lam[ct], 0, 0, 0);
+      for (int c = 0; c < NVH; ++c) {
+        const float b = (float)sm.Ds[(k0 + lg) * LDV + 16 * (NVH * h + c) + li];
+        lam[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, lam[c], 0, 0, 0);
       }
     }
     float dgp[4] = {0.f, 0.f, 0.f, 0.f};
@@ -809,30 +823,31 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
       Frag<bf16> lf;
       lds_frag(lf, sm.Lb + (16 * rb + li) * LDC + 32 * ks + 8 * lg);
 #pragma unroll
-      for (int ct = 0; ct < G::NVT; ++ct) {
+      for (int c = 0; c < NVH; ++c) {
         Frag<bf16> uf;
-        lds_frag_tr(uf, sm.Us, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * ct, li);
+        lds_frag_tr(uf, sm.Us, LDV, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * (NVH * h + c),
+                    li);
         f32x4 lu = {0.f, 0.f, 0.f, 0.f};
         mma(lu, lf, uf);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dgp[r] = fmaf(-lam[ct][r], lu[r], dgp[r]);
+        for (int r = 0; r < 4; ++r) dgp[r] = fmaf(-lam[c][r], lu[r], dgp[r]);
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < G::NVT; ++ct) {
+    for (int c = 0; c < NVH; ++c) {
       float y[4];
-      lds_col4(y, sm.Ys, LDV, 16 * rb + 4 * lg, 16 * ct, li);
+      lds_col4(y, sm.Ys, LDV, 16 * rb + 4 * lg, 16 * (NVH * h + c), li);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dgp[r] = fmaf(lam[ct][r], y[r], dgp[r]);
+      for (int r = 0; r < 4; ++r) dgp[r] = fmaf(lam[c][r], y[r], dgp[r]);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float s = sum16(dgp[r]);
-      const int j = 16 * rb + 4 * lg + r;
-      if (li == 0 && j < Lc) p.dg[(size_t)bh * N + c0 + j] = s;
+      if (li == 0) sm.dgp[h][16 * rb + 4 * lg + r] = s;
     }
   }
   __syncthreads();
+  if (tid < Lc) p.dg[(size_t)bh * N + c0 + tid] = sm.dgp[0][tid] + sm.dgp[1][tid];
 
   // ---- dP = dO U^T, -dY U^T (lower tiles): P's and L's gradients, the
   //      decay's row/column sums; Pb <- dP (.) Mb, Lb <- G + G^T.  The
@@ -842,7 +857,7 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
   stage_rec(Sm, LDV, rS, 0, DK, DV, dvp, dv);
   {
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int tj = 0; tj <= rb; ++tj) {
+    for (int tj = h; tj <= rb; tj += 2) {
       f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DV / 32; ++ks) {
@@ -910,7 +925,7 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
     for (int ks = 0; ks < C / 32; ++ks)
       lds_frag(pfr[ks], sm.Pb + (16 * rb + li) * LDC + 32 * ks + 8 * lg);
 #pragma unroll 2
-    for (int tf = 0; tf < G::NFT; ++tf) {
+    for (int tf = NFH * h; tf < NFH * (h + 1); ++tf) {
       f32x4 t1 = {0.f, 0.f, 0.f, 0.f}, t2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DV / 32; ++ks) {
@@ -945,9 +960,12 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
     tile_store<VK>(Gst, LDK, DK, dqo, c0, Lc, d);
   }
   // ---- dK = (dP (.) Mb)^T Q - diag(b) dY S-^T + diag(beta / b) U Sh+^T + (G + G^T) K;
-  //      d log b_j -= b_j k_j . (dY S-^T)_j.  Sh+ goes to the dO tile (no
-  //      longer read), 64 rows at a time; beta <Sh+, S-> alongside ----
-  bf16 *const Shs = sm.dOs;
+  //      d log b_j -= b_j k_j . (dY S-^T)_j.  Sh+ goes to the dO and dY
+  //      tiles (no longer read once the dY rows are in registers); beta
+  //      <Sh+, S-> alongside ----
+  bf16 *const Shs = sm.dOs;  // Sh+ [DK][DV], stride LDV, over dOs and then dYs
+  static_assert(offsetof(SmemGrad<G>, dYs) == offsetof(SmemGrad<G>, dOs) + sizeof(sm.dOs),
+                "the dO and dY tiles are adjacent");
   float shs = 0.f;  // this thread's part of <Sh+, S->
   {
     float da[4] = {0.f, 0.f, 0.f, 0.f};
@@ -963,21 +981,19 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
       lds_frag(yfr[ks], sm.dYs + (16 * rb + li) * LDV + 32 * ks + 8 * lg);
       lds_frag(ufr[ks], sm.Us + (16 * rb + li) * LDV + 32 * ks + 8 * lg);
     }
-    for (int tf = 0; tf < G::NFT; ++tf) {
-      if (tf % 4 == 0) {  // the next 64 rows of Sh+
-        __syncthreads();
-        stage_rec(Shs, LDV, rA, 16 * tf, 64, DV, dvp, dv);
-        __syncthreads();
-        if constexpr (DECAY) {
-          for (int e = tid; e < 64 * (DV / 8); e += kThreads) {
-            const int row = e / (DV / 8), n = (e % (DV / 8)) * 8;
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Shs + row * LDV + n);
-            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(Sm + (16 * tf + row) * LDV + n);
+    __syncthreads();  // dQ's rows are out of the X tile, every wave has its dY rows
+    stage_rec(Shs, LDV, rA, 0, DK, DV, dvp, dv);
+    __syncthreads();
+    if constexpr (DECAY) {
+      for (int e = tid; e < DK * (DV / 8); e += kGThreads) {
+        const int row = e / (DV / 8), n = (e % (DV / 8)) * 8;
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Shs + row * LDV + n);
+        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(Sm + row * LDV + n);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) shs = fmaf((float)a[m], (float)b[m], shs);
-          }
-        }
+        for (int m = 0; m < 8; ++m) shs = fmaf((float)a[m], (float)b[m], shs);
       }
+    }
+    for (int tf = NFH * h; tf < NFH * (h + 1); ++tf) {
       f32x4 t1 = {0.f, 0.f, 0.f, 0.f}, t2 = {0.f, 0.f, 0.f, 0.f}, t3 = {0.f, 0.f, 0.f, 0.f},
             t4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -994,7 +1010,7 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
       for (int ks = 0; ks < DV / 32; ++ks) {
         Frag<bf16> sf, hf;
         lds_frag(sf, Sm + (16 * tf + li) * LDV + 32 * ks + 8 * lg);
-        lds_frag(hf, Shs + (16 * (tf % 4) + li) * LDV + 32 * ks + 8 * lg);
+        lds_frag(hf, Shs + (16 * tf + li) * LDV + 32 * ks + 8 * lg);
         mma(t2, yfr[ks], sf);
         mma(t3, ufr[ks], hf);
       }
@@ -1029,11 +1045,16 @@ __global__ void __launch_bounds__(kThreads) bgrad_kernel(BwdDeltaParams p) {
       // d log b_j for the chunk's tokens (lane j), then d log alpha_t as the
       // suffix sums, dalpha = d log alpha / alpha
       const int j = lane;
-      float x = sm.dlb[0][j] + sm.dlb[1][j] + sm.dlb[2][j] + sm.dlb[3][j] - sm.Gi[j];
+      float x = -sm.Gi[j], red = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGWaves; ++w) {
+        x += sm.dlb[w][j];
+        red += sm.red[w];
+      }
       float gsum = sm.Gi[j];
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) gsum += __shfl_xor(gsum, o);
-      const float dlbeta = __expf(lbeta) * (sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]) + gsum;
+      const float dlbeta = __expf(lbeta) * red + gsum;
       if (j == Lc - 1) x += dlbeta;
       if (j >= Lc) x = 0.f;
       // suffix sum: sum over j' >= j
@@ -1064,7 +1085,7 @@ hipError_t run_bwd(const BwdDeltaParams &bp, const PrefillParams &pp, hipStream_
                     dim3(kThreads), s, bp, nsl, xcd_map);
   if (e != hipSuccess) return e;
   return launch_kernel("delta_bwd_grad", bgrad_kernel<G, VK, DECAY>, head_grid(nch, bp.BH),
-                       dim3(kThreads), s, bp);
+                       dim3(kGThreads), s, bp);
 }
 
 template <class CF, int DV>
