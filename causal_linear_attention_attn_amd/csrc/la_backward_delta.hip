@@ -484,12 +484,12 @@ __global__ void __launch_bounds__(kThreads) brev_kernel(BwdDeltaParams p, int ns
 
 // ---------------------------------------------------------------------------
 // bgrad_kernel: the per-chunk gradients, every chunk in parallel.  Its tiles
-// fill the LDS, so one workgroup runs per CU; it has eight waves, two per
-// 16-row block of the chunk, each taking half of the block's output tiles
-// (value column tiles of U, dU and lambda; feature tiles of dQ and dK;
-// alternate column blocks of L, P and dP), so that every SIMD holds two
+// fill the LDS, so one workgroup runs per CU; it has sixteen waves, four per
+// 16-row block of the chunk, each taking a quarter of the block's output
+// tiles (value column tiles of U, dU and lambda; feature tiles of dQ and dK;
+// every fourth column block of L, P and dP), so that every SIMD holds four
 // waves to cover each other's LDS and matrix-core latency.
-constexpr int kGWaves = 8, kGThreads = kGWaves * kWave;
+constexpr int kGSplit = 4, kGWaves = 4 * kGSplit, kGThreads = kGWaves * kWave;
 // ---------------------------------------------------------------------------
 template <int DK_, int DV_>
 struct GCfg {
@@ -507,8 +507,7 @@ struct alignas(16) SmemGrad {
   float Xi[G::C * G::LDX];                    // X, then X^(-1)
   float gs[G::C], lb[G::C], al[G::C], Gi[G::C];
   float dlb[kGWaves][G::C];  // per-wave parts of d log b
-  float dgp[2][G::C];        // the two halves of dg
-  float red[kGWaves];
+  float dgp[kGSplit][G::C];  // the parts of dg; later the waves' parts of <Sh+, S->
 };
 
 // 8 consecutive row elements of a bf16 [DK][dvp] record (columns n .. n+7
@@ -591,8 +590,9 @@ __device__ __forceinline__ float sum16(float x) {  // over the 16 lanes li of a 
 template <class G, bool VK, bool DECAY>
 __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
   constexpr int C = G::C, DK = G::DK, DV = G::DV, NRB = G::NRB;
-  constexpr int NVH = G::NVT / 2, NFH = G::NFT / 2;  // a wave's value / feature tiles
-  static_assert(2 * NRB == kGWaves && 2 * NVH == G::NVT && 2 * NFH == G::NFT, "wave split");
+  constexpr int NVH = G::NVT / kGSplit, NFH = G::NFT / kGSplit;  // a wave's value / feature tiles
+  static_assert(kGSplit * NRB == kGWaves && kGSplit * NVH == G::NVT && kGSplit * NFH == G::NFT,
+                "wave split");
   constexpr int LDK = G::LDK, LDV = G::LDV, LDC = G::LDC, LDX = G::LDX;
   __shared__ SmemGrad<G> sm;
   const int chunk = blockIdx.x, bh = grid_head();
@@ -600,9 +600,10 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  // half h of row block rb; a SIMD's two waves (w, w + 4) take an early
-  // and a late row block, whose triangular parts differ in length
-  const int h = wv >> 2, rb = h ? NRB - 1 - (wv & 3) : (wv & 3);
+  // part h of row block rb; the waves w, w + 4, ... of one SIMD alternate
+  // between an early and a late row block, whose triangular parts differ
+  // in length
+  const int h = wv >> 2, rb = (h & 1) ? NRB - 1 - (wv & 3) : (wv & 3);
   const int N = p.N, d = p.d, dv = p.dv, nch = p.nch, dvp = p.dvp;
   const int c0 = chunk * C, Lc = min(C, N - c0);
   const size_t qk = (size_t)N * d, vo = (size_t)N * dv;
@@ -656,7 +657,7 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
     const float gi = sm.gs[i], lbi = sm.lb[i];
 #pragma unroll
     for (int tj = 0; tj < NRB; ++tj) {
-      if (tj > rb || (tj & 1) != h) continue;
+      if (tj > rb || tj % kGSplit != h) continue;
       f32x4 kk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) {
@@ -729,7 +730,7 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
   }
 
   // ---- U = X^(-1) diag(g) Y (fp32 matrix cores): rows of this wave's block,
-  //      its half of the value tiles (ct = NVH h + c) ----
+  //      its part of the value tiles (ct = NVH h + c) ----
   // (per 16-wide k block: the lane's four consecutive k of its row of X^(-1)
   // in one 16-byte read, k = 16 bm + 4 lg + kk in product kk)
   // (every value-column tile advances together: independent accumulators)
@@ -763,7 +764,7 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
   }
   __syncthreads();
 
-  // ---- G_i = u_i . D_i (decay; the first half), then dU = P^T dO + D into Ds ----
+  // ---- G_i = u_i . D_i (decay; the first part), then dU = P^T dO + D into Ds ----
   if (DECAY && h == 0) {
     const int i = 16 * rb + li;
     float s = 0.f;
@@ -847,7 +848,12 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
     }
   }
   __syncthreads();
-  if (tid < Lc) p.dg[(size_t)bh * N + c0 + tid] = sm.dgp[0][tid] + sm.dgp[1][tid];
+  if (tid < Lc) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kGSplit; ++w) s += sm.dgp[w][tid];
+    p.dg[(size_t)bh * N + c0 + tid] = s;
+  }
 
   // ---- dP = dO U^T, -dY U^T (lower tiles): P's and L's gradients, the
   //      decay's row/column sums; Pb <- dP (.) Mb, Lb <- G + G^T.  The
@@ -857,7 +863,7 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
   stage_rec(Sm, LDV, rS, 0, DK, DV, dvp, dv);
   {
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int tj = h; tj <= rb; tj += 2) {
+    for (int tj = h; tj <= rb; tj += kGSplit) {
       f32x4 dp = {0.f, 0.f, 0.f, 0.f}, dl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DV / 32; ++ks) {
@@ -1039,22 +1045,24 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
     float s = shs;  // beta <Sh+, S-> over the chunk's records
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) s += __shfl_xor(s, o);
-    if (lane == 0) sm.red[wv] = s;
+    float *const red = &sm.dgp[0][0];
+    static_assert(sizeof(sm.dgp) >= kGWaves * sizeof(float), "one slot per wave");
+    if (lane == 0) red[wv] = s;
     __syncthreads();
     if (wv == 0) {
       // d log b_j for the chunk's tokens (lane j), then d log alpha_t as the
       // suffix sums, dalpha = d log alpha / alpha
       const int j = lane;
-      float x = -sm.Gi[j], red = 0.f;
+      float x = -sm.Gi[j], shsum = 0.f;
 #pragma unroll
       for (int w = 0; w < kGWaves; ++w) {
         x += sm.dlb[w][j];
-        red += sm.red[w];
+        shsum += red[w];
       }
       float gsum = sm.Gi[j];
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) gsum += __shfl_xor(gsum, o);
-      const float dlbeta = __expf(lbeta) * red + gsum;
+      const float dlbeta = __expf(lbeta) * shsum + gsum;
       if (j == Lc - 1) x += dlbeta;
       if (j >= Lc) x = 0.f;
       // suffix sum: sum over j' >= j
