@@ -36,7 +36,8 @@
 //                  U, dU, lam from the stored Y, D and the inputs, then dQ,
 //                  dK, dg and dalpha.
 // Workspace: the preparation records, then the states S- and adjoints Sh+
-// of every chunk ([DK][DV] bf16), then Y and D ([C][DV] bf16).
+// of every chunk (transposed, [DV][DK] bf16: a slice workgroup's 16 columns
+// are 16 whole rows), then Y and D ([C][DV] bf16).
 #include "la_delta_common.hpp"
 
 namespace la {
@@ -166,17 +167,20 @@ struct RowBlocks {
   }
 };
 
-// This wave's fp32 state tiles (rows 16 (wv FPW + a) + 4 lg + r, column
-// n0 + li) to a [DK][DV] bf16 record (every row; columns past the head's
-// value width are zero in the state).
+// The state slice of the workgroup as its bf16 LDS copy holds it
+// (Sl[n * QLD + f] = S[f][n0 + n]) to the chunk's transposed record
+// [dvp][DK] (row n: column n of the state over the features), one 16-byte
+// store per thread; feature rows past the head's d are zero in the state.
 template <class CF>
-__device__ __forceinline__ void store_state_rec(bf16 *rec, const f32x4 (&S)[CF::FPW], int dvp,
-                                                int n, int wv, int lg) {
-#pragma unroll
-  for (int a = 0; a < CF::FPW; ++a)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      rec[(size_t)(16 * (wv * CF::FPW + a) + 4 * lg + r) * dvp + n] = (bf16)S[a][r];
+__device__ __forceinline__ void store_state_rec(bf16 *rec, const bf16 *Sl, int n0) {
+  constexpr int FB = CF::DK / 8;  // 16-byte blocks of a record row
+  static_assert(CF::W * FB <= kThreads, "one block per thread");
+  const int t = threadIdx.x;
+  if (t < CF::W * FB) {
+    const int n = t / FB, f0 = (t % FB) * 8;
+    *reinterpret_cast<bf16x8 *>(rec + (size_t)(n0 + n) * CF::DK + f0) =
+        *reinterpret_cast<const bf16x8 *>(Sl + n * CF::QLD + f0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -258,7 +262,7 @@ __global__ void __launch_bounds__(kThreads) bstate_kernel(BwdDeltaParams p, int 
   for (int c = 0; c < nch; ++c) {
     const int u = c & 1;
     // the state entering the chunk
-    store_state_rec<CF>(states + (size_t)c * CF::DK * dvp, Sacc, dvp, n0 + li, wv, lg);
+    store_state_rec<CF>(states + (size_t)c * CF::DK * dvp, sm.St, n0);
     // X^T = S'^T K^T for this wave's 16 tokens; Y = V - b X
     f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -408,7 +412,7 @@ __global__ void __launch_bounds__(kThreads) brev_kernel(BwdDeltaParams p, int ns
     const int u = c & 1;
     const float lbeta = DECAY ? ldec[(size_t)c * C + C - 1] : 0.f;
     const float beta = DECAY ? __expf(lbeta) : 1.f;
-    store_state_rec<CF>(adj + (size_t)c * CF::DK * dvp, Sacc, dvp, n0 + li, wv, lg);
+    store_state_rec<CF>(adj + (size_t)c * CF::DK * dvp, sm.Sh, n0);
     // dY^T = Sh'^T Wt + dO^T R and D^T = Sh'^T K^T for this wave's 16 tokens
     f32x4 dy = {0.f, 0.f, 0.f, 0.f}, dd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -510,18 +514,6 @@ struct alignas(16) SmemGrad {
   float dgp[kGSplit][G::C];  // the parts of dg; later the waves' parts of <Sh+, S->
 };
 
-// 8 consecutive row elements of a bf16 [DK][dvp] record (columns n .. n+7
-// of row f) as an operand fragment, zero at columns past dv.
-__device__ __forceinline__ void rec_row_frag(Frag<bf16> &fr, __amdgpu_buffer_rsrc_t r, int f,
-                                             int n, int dvp, int dv) {
-  fr.v = buf_load16<bf16>(r, (uint32_t)(((size_t)f * dvp + n) * 2));
-  if (n + 8 > dv) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (n + e >= dv) fr.v[e] = (bf16)0.f;
-  }
-}
-
 // Rows of a [tokens, ncols] bf16 tensor (or a chunk record) into an LDS tile
 // of `cols` columns (zero outside rows < nrows, columns < ncols).
 template <bool VK>
@@ -569,17 +561,17 @@ __device__ __forceinline__ void tile_store(const bf16 *tile, int ld, int cols, b
   }
 }
 
-// Rows r0 .. r0 + nrows - 1 of a bf16 [DK][dvp] record into an LDS tile of
-// DV columns (stride ld), columns past dv zero; every thread takes 16-byte
-// blocks.
-__device__ __forceinline__ void stage_rec(bf16 *tile, int ld, __amdgpu_buffer_rsrc_t r, int r0,
-                                          int nrows, int DV, int dvp, int dv) {
-  const int cb = DV / 8;
-  for (int b = threadIdx.x; b < nrows * cb; b += kGThreads) {
-    const int row = b / cb, n = (b % cb) * 8;
-    Frag<bf16> f;
-    rec_row_frag(f, r, r0 + row, n, dvp, dv);
-    *reinterpret_cast<bf16x8 *>(tile + row * ld + n) = f.v;
+// A transposed state record [dvp][DK] (row n: the state's column n) into an
+// LDS tile of DV rows (stride ld), rows past dv zero; every thread takes
+// 16-byte blocks.
+template <int DK>
+__device__ __forceinline__ void stage_rec(bf16 *tile, int ld, __amdgpu_buffer_rsrc_t r, int DV,
+                                          int dv) {
+  constexpr int cb = DK / 8;
+  for (int b = threadIdx.x; b < DV * cb; b += kGThreads) {
+    const int n = b / cb, f0 = (b % cb) * 8;
+    const bf16x8 x = buf_load16<bf16>(r, n < dv ? (uint32_t)(((size_t)n * DK + f0) * 2) : kOOB);
+    *reinterpret_cast<bf16x8 *>(tile + n * ld + f0) = x;
   }
 }
 
@@ -858,9 +850,9 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
   // ---- dP = dO U^T, -dY U^T (lower tiles): P's and L's gradients, the
   //      decay's row/column sums; Pb <- dP (.) Mb, Lb <- G + G^T.  The
   //      chunk's S- goes to the Ys / Ds tiles meanwhile (no longer read) ----
-  bf16 *const Sm = sm.Ys;  // S- [DK][DV], stride LDV, over Ys and then Ds
-  static_assert(DK <= 2 * C, "S- fits the Y and D tiles");
-  stage_rec(Sm, LDV, rS, 0, DK, DV, dvp, dv);
+  bf16 *const Sm = sm.Ys;  // S-^T [DV][DK], stride LDK, over Ys and then Ds
+  static_assert(DV * LDK <= 2 * C * LDV, "S- fits the Y and D tiles");
+  stage_rec<DK>(Sm, LDK, rS, DV, dv);
   {
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
     for (int tj = h; tj <= rb; tj += kGSplit) {
@@ -936,7 +928,7 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
 #pragma unroll
       for (int ks = 0; ks < DV / 32; ++ks) {
         Frag<bf16> sf;
-        lds_frag(sf, Sm + (16 * tf + li) * LDV + 32 * ks + 8 * lg);
+        lds_frag_tr(sf, Sm, LDK, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * tf, li);
         mma(t1, ofr[ks], sf);
       }
 #pragma unroll
@@ -969,7 +961,7 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
   //      d log b_j -= b_j k_j . (dY S-^T)_j.  Sh+ goes to the dO and dY
   //      tiles (no longer read once the dY rows are in registers); beta
   //      <Sh+, S-> alongside ----
-  bf16 *const Shs = sm.dOs;  // Sh+ [DK][DV], stride LDV, over dOs and then dYs
+  bf16 *const Shs = sm.dOs;  // Sh+^T [DV][DK], stride LDK, over dOs and then dYs
   static_assert(offsetof(SmemGrad<G>, dYs) == offsetof(SmemGrad<G>, dOs) + sizeof(sm.dOs),
                 "the dO and dY tiles are adjacent");
   float shs = 0.f;  // this thread's part of <Sh+, S->
@@ -988,13 +980,13 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
       lds_frag(ufr[ks], sm.Us + (16 * rb + li) * LDV + 32 * ks + 8 * lg);
     }
     __syncthreads();  // dQ's rows are out of the X tile, every wave has its dY rows
-    stage_rec(Shs, LDV, rA, 0, DK, DV, dvp, dv);
+    stage_rec<DK>(Shs, LDK, rA, DV, dv);
     __syncthreads();
     if constexpr (DECAY) {
-      for (int e = tid; e < DK * (DV / 8); e += kGThreads) {
-        const int row = e / (DV / 8), n = (e % (DV / 8)) * 8;
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Shs + row * LDV + n);
-        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(Sm + row * LDV + n);
+      for (int e = tid; e < DV * (DK / 8); e += kGThreads) {
+        const int row = e / (DK / 8), f0 = (e % (DK / 8)) * 8;
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Shs + row * LDK + f0);
+        const bf16x8 b = *reinterpret_cast<const bf16x8 *>(Sm + row * LDK + f0);
 #pragma unroll
         for (int m = 0; m < 8; ++m) shs = fmaf((float)a[m], (float)b[m], shs);
       }
@@ -1015,8 +1007,8 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
 #pragma unroll
       for (int ks = 0; ks < DV / 32; ++ks) {
         Frag<bf16> sf, hf;
-        lds_frag(sf, Sm + (16 * tf + li) * LDV + 32 * ks + 8 * lg);
-        lds_frag(hf, Shs + (16 * tf + li) * LDV + 32 * ks + 8 * lg);
+        lds_frag_tr(sf, Sm, LDK, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * tf, li);
+        lds_frag_tr(hf, Shs, LDK, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 16 * tf, li);
         mma(t2, yfr[ks], sf);
         mma(t3, ufr[ks], hf);
       }
