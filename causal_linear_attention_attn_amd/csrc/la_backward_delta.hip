@@ -134,16 +134,16 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, int row, int co
 }
 
 // Whole-line blocks of q or k rows of one chunk (this thread's share of the
-// workgroup's 256) and their staging into an LDS tile.
-template <class CF, bool VK>
+// workgroup's NT) and their staging into an LDS tile.
+template <class CF, bool VK, int NT = kThreads>
 struct RowBlocks {
-  static constexpr int NB = CF::C * CF::QCB / kThreads;
-  static_assert(NB * kThreads == CF::C * CF::QCB, "row blocks per thread");
+  static constexpr int NB = CF::C * CF::QCB / NT;
+  static_assert(NB * NT == CF::C * CF::QCB, "row blocks per thread");
   typename CF::vec x[NB];
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int N, int d, int chunk) {
 #pragma unroll
     for (int m = 0; m < NB; ++m) {
-      const int b = threadIdx.x + m * kThreads;
+      const int b = threadIdx.x + m * NT;
       const int row = chunk * CF::C + b / CF::QCB, col0 = (b % CF::QCB) * CF::VEC;
       if constexpr (VK) {
         x[m] = buf_load16<bf16>(r, (chunk >= 0 && row < N && col0 < d)
@@ -160,7 +160,7 @@ struct RowBlocks {
   __device__ __forceinline__ void stage(bf16 *tile) const {
 #pragma unroll
     for (int m = 0; m < NB; ++m) {
-      const int b = threadIdx.x + m * kThreads;
+      const int b = threadIdx.x + m * NT;
       *reinterpret_cast<typename CF::vec *>(tile + (b / CF::QCB) * CF::QLD +
                                             (b % CF::QCB) * CF::VEC) = x[m];
     }
@@ -309,7 +309,11 @@ __global__ void __launch_bounds__(kThreads) bstate_kernel(BwdDeltaParams p, int 
 }
 
 // ---------------------------------------------------------------------------
-// brev_kernel: the adjoint chain over chunks in reverse.
+// brev_kernel: the adjoint chain over chunks in reverse.  NWR waves: with
+// four, each takes one 16-token row block (dY and D) and a quarter of the
+// state tiles; with eight (d = 128), the two waves of a row block take its
+// dY and its D, and each wave an eighth of the state tiles, so that every
+// SIMD holds two waves of the chain.
 // ---------------------------------------------------------------------------
 template <class CF>
 struct alignas(16) SmemBRev {
@@ -321,16 +325,21 @@ struct alignas(16) SmemBRev {
   bf16 Sh[CF::W * CF::QLD];      // Sh'^T: bf16 copy of the adjoint slice
 };
 
-template <class CF, bool VK, bool DECAY>
-__global__ void __launch_bounds__(kThreads) brev_kernel(BwdDeltaParams p, int nslices,
-                                                        int xcd_map) {
+template <class CF, bool VK, bool DECAY, int NWR>
+__global__ void __launch_bounds__(NWR *kWave) brev_kernel(BwdDeltaParams p, int nslices,
+                                                          int xcd_map) {
   static_assert(CF::W == 16 && CF::NRB == 4 && CF::NCT == 1, "16-column slices, 4 row blocks");
-  constexpr int C = CF::C, FPW = CF::FPW, KSC = CF::KSC, KSD = CF::KSD;
+  constexpr int C = CF::C, KSC = CF::KSC, KSD = CF::KSD;
+  constexpr int FPW = CF::NFT / NWR;  // state row tiles per wave
+  constexpr bool SPLIT = NWR == 2 * CF::NRB;
+  static_assert(FPW >= 1 && FPW * NWR == CF::NFT && (NWR == CF::NRB || SPLIT), "wave split");
   __shared__ SmemBRev<CF> sm;
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int rb = wv;
+  const int rb = wv % CF::NRB;
+  // (wave-uniform) this wave computes its row block's dY, its D, or both
+  const bool do_dy = !SPLIT || wv < CF::NRB, do_dd = !SPLIT || wv >= CF::NRB;
   int bh, slice;
   head_slice(blockIdx.x, nslices, xcd_map, bh, slice);
   const int n0 = slice * 16;
@@ -353,8 +362,8 @@ __global__ void __launch_bounds__(kThreads) brev_kernel(BwdDeltaParams p, int ns
   const int col = n0 + 4 * lg;
 
   struct Ops {
-    RowBlocks<CF, VK> q, k;
-    Frag<bf16> wt[KSD], rt[KSC];  // Wt^T and R^T rows of this wave's 16 tokens
+    RowBlocks<CF, VK, NWR * kWave> q, k;
+    Frag<bf16> wt[KSD], rt[KSC];  // Wt^T and R^T rows of this wave's 16 tokens (dY)
     bf16x4 dout;
     float lb;  // log b of this lane's token
   };
@@ -363,17 +372,20 @@ __global__ void __launch_bounds__(kThreads) brev_kernel(BwdDeltaParams p, int ns
     o.q.load(rq, N, d, ok ? c : -1);
     o.k.load(rk, N, d, ok ? c : -1);
     const uint32_t base = ok ? (uint32_t)((size_t)c * CF::RECB * 2) : 0u;
+    if (do_dy) {
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks)
-      load_rec_frag(o.wt[ks], rw,
-                    ok ? base + (uint32_t)((CF::WT + ((size_t)(rb * KSD + ks) * 64 + lane) * 8) * 2)
-                       : kOOB);
+      for (int ks = 0; ks < KSD; ++ks)
+        load_rec_frag(o.wt[ks], rw,
+                      ok ? base + (uint32_t)((CF::WT + ((size_t)(rb * KSD + ks) * 64 + lane) * 8) *
+                                             2)
+                         : kOOB);
 #pragma unroll
-    for (int ks = 0; ks < KSC; ++ks)
-      load_rec_frag(o.rt[ks], rw,
-                    ok ? base + (uint32_t)((2 * CF::WT + ((size_t)(rb * KSC + ks) * 64 + lane) * 8) *
-                                           2)
-                       : kOOB);
+      for (int ks = 0; ks < KSC; ++ks)
+        load_rec_frag(o.rt[ks], rw,
+                      ok ? base + (uint32_t)((2 * CF::WT +
+                                              ((size_t)(rb * KSC + ks) * 64 + lane) * 8) * 2)
+                         : kOOB);
+    }
     const int t = c * C + 16 * rb + li;
     o.dout = load4<VK>(rdo, t, col, dv, ok && t < N);
     o.lb = (DECAY && ok) ? ldec[(size_t)c * C + 16 * rb + li] : 0.f;
@@ -385,9 +397,10 @@ __global__ void __launch_bounds__(kThreads) brev_kernel(BwdDeltaParams p, int ns
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = (float)o.dout[e];
     const float b = DECAY ? __expf(o.lb) : 1.f;
-    lds_store4(sm.dO[u] + (16 * rb + li) * CF::YLD + 4 * lg, x[0], x[1], x[2], x[3]);
-    lds_store4(sm.dOb[u] + (16 * rb + li) * CF::YLD + 4 * lg, b * x[0], b * x[1], b * x[2],
-               b * x[3]);
+    if (do_dy) lds_store4(sm.dO[u] + (16 * rb + li) * CF::YLD + 4 * lg, x[0], x[1], x[2], x[3]);
+    if (do_dd)
+      lds_store4(sm.dOb[u] + (16 * rb + li) * CF::YLD + 4 * lg, b * x[0], b * x[1], b * x[2],
+                 b * x[3]);
   };
 
   f32x4 Sacc[FPW];
@@ -419,30 +432,32 @@ __global__ void __launch_bounds__(kThreads) brev_kernel(BwdDeltaParams p, int ns
     for (int ks = 0; ks < KSD; ++ks) {
       Frag<bf16> sf, kf;
       lds_frag(sf, sm.Sh + li * CF::QLD + 32 * ks + 8 * lg);
-      lds_frag(kf, sm.K[u] + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
-      mma(dy, sf, cur.wt[ks]);
-      mma(dd, sf, kf);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KSC; ++ks) {
-      if (32 * ks + 31 < 16 * rb) continue;  // R[j][t] = 0 for j < t
-      Frag<bf16> of;
-      lds_frag_tr(of, sm.dO[u], CF::YLD, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 0, li);
-      mma(dy, of, cur.rt[ks]);
+      if (do_dy) mma(dy, sf, cur.wt[ks]);
+      if (do_dd) {
+        lds_frag(kf, sm.K[u] + (16 * rb + li) * CF::QLD + 32 * ks + 8 * lg);
+        mma(dd, sf, kf);
+      }
     }
     const int t = c * C + 16 * rb + li;  // this lane's token; dY[t][col .. col + 3]
-    store4<VK>(rdv, t, col, dv, t < N, dy);
-    {
+    if (do_dy) {
+#pragma unroll
+      for (int ks = 0; ks < KSC; ++ks) {
+        if (32 * ks + 31 < 16 * rb) continue;  // R[j][t] = 0 for j < t
+        Frag<bf16> of;
+        lds_frag_tr(of, sm.dO[u], CF::YLD, 32 * ks + 8 * lg, 32 * ks + 8 * lg + 4, 0, li);
+        mma(dy, of, cur.rt[ks]);
+      }
+      store4<VK>(rdv, t, col, dv, t < N, dy);
+      const float nb = DECAY ? -__expf(cur.lb) : -1.f;
+      lds_store4(sm.dYb + (16 * rb + li) * CF::YLD + 4 * lg, nb * dy[0], nb * dy[1], nb * dy[2],
+                 nb * dy[3]);
+    }
+    if (do_dd) {
       const float wl = DECAY ? __expf(lbeta - cur.lb) : 1.f;  // beta / b_t
       bf16 *dr = dbase + ((size_t)c * C + 16 * rb + li) * dvp + col;
       if (col < dvp)
         *reinterpret_cast<bf16x4 *>(dr) = (bf16x4){(bf16)(wl * dd[0]), (bf16)(wl * dd[1]),
                                                    (bf16)(wl * dd[2]), (bf16)(wl * dd[3])};
-    }
-    {
-      const float nb = DECAY ? -__expf(cur.lb) : -1.f;
-      lds_store4(sm.dYb + (16 * rb + li) * CF::YLD + 4 * lg, nb * dy[0], nb * dy[1], nb * dy[2],
-                 nb * dy[3]);
     }
     __syncthreads();
     // Sh- = beta Sh+ + Q^T (b dO) + K^T (-b dY)
@@ -1081,8 +1096,9 @@ hipError_t run_bwd(const BwdDeltaParams &bp, const PrefillParams &pp, hipStream_
   e = launch_kernel("delta_bwd_state", bstate_kernel<CF, VK, DECAY>, dim3(bp.BH * nsl),
                     dim3(kThreads), s, bp, nsl, xcd_map);
   if (e != hipSuccess) return e;
-  e = launch_kernel("delta_bwd_rev", brev_kernel<CF, VK, DECAY>, dim3(bp.BH * nsl),
-                    dim3(kThreads), s, bp, nsl, xcd_map);
+  constexpr int NWR = CF::NFT >= 8 ? 8 : 4;  // the reverse pass's waves
+  e = launch_kernel("delta_bwd_rev", brev_kernel<CF, VK, DECAY, NWR>, dim3(bp.BH * nsl),
+                    dim3(NWR * kWave), s, bp, nsl, xcd_map);
   if (e != hipSuccess) return e;
   return launch_kernel("delta_bwd_grad", bgrad_kernel<G, VK, DECAY>, head_grid(nch, bp.BH),
                        dim3(kGThreads), s, bp);
