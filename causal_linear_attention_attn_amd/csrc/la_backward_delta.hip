@@ -576,19 +576,30 @@ __device__ __forceinline__ void tile_store(const bf16 *tile, int ld, int cols, b
   }
 }
 
-// A transposed state record [dvp][DK] (row n: the state's column n) into an
-// LDS tile of DV rows (stride ld), rows past dv zero; every thread takes
-// 16-byte blocks.
-template <int DK>
-__device__ __forceinline__ void stage_rec(bf16 *tile, int ld, __amdgpu_buffer_rsrc_t r, int DV,
-                                          int dv) {
-  constexpr int cb = DK / 8;
-  for (int b = threadIdx.x; b < DV * cb; b += kGThreads) {
-    const int n = b / cb, f0 = (b % cb) * 8;
-    const bf16x8 x = buf_load16<bf16>(r, n < dv ? (uint32_t)(((size_t)n * DK + f0) * 2) : kOOB);
-    *reinterpret_cast<bf16x8 *>(tile + n * ld + f0) = x;
+// A transposed state record [dvp][DK] (row n: the state's column n), DV
+// rows of it, in registers: loaded ahead of the phase that stages it into an
+// LDS tile (stride ld), so that its latency overlaps the phases before;
+// rows past dv are zero.  Every thread takes 16-byte blocks.
+template <int DK, int DV>
+struct RecRegs {
+  static constexpr int CB = DK / 8, NB = (DV * CB + kGThreads - 1) / kGThreads;
+  bf16x8 x[NB];
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int dv) {
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+      const int b = threadIdx.x + m * kGThreads, n = b / CB, f0 = (b % CB) * 8;
+      x[m] = buf_load16<bf16>(r, b < DV * CB && n < dv ? (uint32_t)(((size_t)n * DK + f0) * 2)
+                                                        : kOOB);
+    }
   }
-}
+  __device__ __forceinline__ void stage(bf16 *tile, int ld) const {
+#pragma unroll
+    for (int m = 0; m < NB; ++m) {
+      const int b = threadIdx.x + m * kGThreads;
+      if (b < DV * CB) *reinterpret_cast<bf16x8 *>(tile + (b / CB) * ld + (b % CB) * 8) = x[m];
+    }
+  }
+};
 
 __device__ __forceinline__ float sum16(float x) {  // over the 16 lanes li of a slot group
   return lane_sum<16>(x);
@@ -810,6 +821,8 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
       sm.Ds[(16 * rb + 4 * lg + r) * LDV + 16 * (NVH * h + c) + li] = (bf16)du[c][r];
   __syncthreads();
 
+  RecRegs<DK, DV> srec;  // S- of the chunk, staged after this phase
+  srec.load(rS, dv);
   // ---- lam = X^(-T) dU and r = Y - L U (same tiles); dg_j = lam_j . r_j ----
   {
     f32x4 lam[NVH];
@@ -867,7 +880,9 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
   //      chunk's S- goes to the Ys / Ds tiles meanwhile (no longer read) ----
   bf16 *const Sm = sm.Ys;  // S-^T [DV][DK], stride LDK, over Ys and then Ds
   static_assert(DV * LDK <= 2 * C * LDV, "S- fits the Y and D tiles");
-  stage_rec<DK>(Sm, LDK, rS, DV, dv);
+  srec.stage(Sm, LDK);
+  RecRegs<DK, DV> arec;  // Sh+ of the chunk, staged for the dK phase
+  arec.load(rA, dv);
   {
     float rs[4] = {0.f, 0.f, 0.f, 0.f};
     for (int tj = h; tj <= rb; tj += kGSplit) {
@@ -995,7 +1010,7 @@ __global__ void __launch_bounds__(kGThreads) bgrad_kernel(BwdDeltaParams p) {
       lds_frag(ufr[ks], sm.Us + (16 * rb + li) * LDV + 32 * ks + 8 * lg);
     }
     __syncthreads();  // dQ's rows are out of the X tile, every wave has its dY rows
-    stage_rec<DK>(Shs, LDK, rA, DV, dv);
+    arec.stage(Shs, LDK);
     __syncthreads();
     if constexpr (DECAY) {
       for (int e = tid; e < DV * (DK / 8); e += kGThreads) {
